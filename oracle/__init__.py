@@ -1,0 +1,167 @@
+"""fp64 reference ("oracle") for the gated delta-rule operator -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU product path
+(``gated_delta_rule_37_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``gdr_oracle.c`` (plain C, fp64, token by token); this
+module only marshals NumPy arrays through ctypes.  The recurrence it follows is
+the state update of the Kimi Delta Attention blog, section 2.1,
+``S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T`` with
+``o_t = S_t^T q_t``; see the C file's header for the step-by-step statement.
+
+Parity of every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, reductions between gate kinds, brute-force unrolled products,
+finite differences) rather than by comparison with any implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compiles ``liboracle.so`` with the host C compiler (no HIP, no BLAS)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            i64, dbl, ptr, cint = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+            lib.oracle_forward.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 8 + [cint]
+            lib.oracle_backward.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 14 + [cint]
+            lib.oracle_decode.argtypes = [i64] * 4 + [cint, dbl] + [ptr] * 7 + [cint]
+            lib.oracle_clvr_forward.argtypes = [i64] * 4 + [ptr] * 4
+            lib.oracle_clvr_backward.argtypes = [i64] * 4 + [ptr] * 5
+            for f in (lib.oracle_forward, lib.oracle_backward, lib.oracle_decode,
+                      lib.oracle_clvr_forward, lib.oracle_clvr_backward):
+                f.restype = cint
+            _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _threads(nthreads):
+    if nthreads is None or nthreads <= 0:
+        try:
+            return len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            return os.cpu_count() or 1
+    return int(nthreads)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError("%s failed with status %d" % (name, rc))
+
+
+def gate_kind(alpha, q):
+    """NONE when alpha is None, SCALAR for [B,T,H], CHANNEL for [B,T,H,dk]."""
+    if alpha is None:
+        return GATE_NONE
+    return GATE_SCALAR if np.ndim(alpha) == 3 else GATE_CHANNEL
+
+
+def forward(q, k, v, beta, alpha=None, S0=None, scale=1.0, nthreads=None):
+    """Token-by-token forward.  Returns ``(o [B,T,H,dv], S_T [B,H,dk,dv])``."""
+    q, k, v, beta, alpha, S0 = map(_f64, (q, k, v, beta, alpha, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    gate = gate_kind(alpha, q)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    rc = _load().oracle_forward(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
+                                _p(beta), _p(alpha), _p(S0), _p(o), _p(ST), _threads(nthreads))
+    _check(rc, "oracle_forward")
+    return o, ST
+
+
+def backward(q, k, v, beta, alpha, S0, dO, dST=None, scale=1.0, nthreads=None):
+    """Adjoint of :func:`forward`.
+
+    Returns a dict with ``dq, dk, dv, dbeta, dalpha`` (None for DeltaNet) and
+    ``dS0``.  ``dalpha`` is the derivative with respect to alpha itself.
+    """
+    q, k, v, beta, alpha, S0, dO, dST = map(_f64, (q, k, v, beta, alpha, S0, dO, dST))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    gate = gate_kind(alpha, q)
+    dq = np.zeros_like(q)
+    dk_ = np.zeros_like(k)
+    dv_ = np.zeros_like(v)
+    dbeta = np.zeros_like(beta)
+    dalpha = None if alpha is None else np.zeros_like(alpha)
+    dS0 = np.zeros((B, H, dk, dv))
+    rc = _load().oracle_backward(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
+                                 _p(beta), _p(alpha), _p(S0), _p(dO), _p(dST), _p(dq), _p(dk_),
+                                 _p(dv_), _p(dbeta), _p(dalpha), _p(dS0), _threads(nthreads))
+    _check(rc, "oracle_backward")
+    return {"dq": dq, "dk": dk_, "dv": dv_, "dbeta": dbeta, "dalpha": dalpha, "dS0": dS0}
+
+
+def decode(q, k, v, beta, alpha, S, scale=1.0, nthreads=None):
+    """One step for N sequences.  Returns ``(o [N,H,dv], S_new [N,H,dk,dv])``;
+    the input state is not modified."""
+    q, k, v, beta, alpha = map(_f64, (q, k, v, beta, alpha))
+    S = np.array(S, dtype=np.float64, order="C", copy=True)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    gate = GATE_NONE if alpha is None else (GATE_SCALAR if alpha.ndim == 2 else GATE_CHANNEL)
+    o = np.zeros((N, H, dv))
+    rc = _load().oracle_decode(N, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v), _p(beta),
+                               _p(alpha), _p(S), _p(o), _threads(nthreads))
+    _check(rc, "oracle_decode")
+    return o, S
+
+
+def clvr_forward(h, v, lam=None):
+    """``h + lam * v`` routed per hidden channel ``h*dv + j``; h is [B,T,H*dv]."""
+    h, v, lam = map(_f64, (h, v, lam))
+    B, T, H, dv = v.shape
+    out = np.zeros_like(h)
+    rc = _load().oracle_clvr_forward(B, T, H, dv, _p(h), _p(v), _p(lam), _p(out))
+    _check(rc, "oracle_clvr_forward")
+    return out
+
+
+def clvr_backward(dh, v, lam=None):
+    """Returns ``(dv_from_clvr [B,T,H,dv], dlam [H*dv])``."""
+    dh, v, lam = map(_f64, (dh, v, lam))
+    B, T, H, dv = v.shape
+    dv_acc = np.zeros_like(v)
+    dlam = np.zeros(H * dv)
+    rc = _load().oracle_clvr_backward(B, T, H, dv, _p(dh), _p(v), _p(lam), _p(dv_acc), _p(dlam))
+    _check(rc, "oracle_clvr_backward")
+    return dv_acc, dlam
