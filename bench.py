@@ -1,0 +1,250 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = one pass of the whole chunked path over the 32K-token Kimi Delta
+Attention prefill (B=1, H=16, T=32768, dk=dv=128, bf16 inputs, fp32 state):
+gate prep + intra-chunk transform + state pass + output + CLVR epilogue, then
+the chunked backward (when the library provides it).  Inputs are resident in
+HBM before the timed region starts.  The decode step (256 sequences x 16 heads,
+256 MiB fp32 state, rotating over independent state sets so the 256 MB
+Infinity Cache cannot serve it) is timed in the same run and reported beside.
+
+Prints ONE JSON line (see the design doc for every field's definition).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_F16_PEAK_TFS = 2500.0  # dense fp16/bf16 matrix peak, published
+METRIC = "tokens/s of KDA/GDN chunked fwd(+bwd) at T=32K; % MFMA peak; decode % HBM BW"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--decode-steps", type=int, default=30)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    return p.parse_args()
+
+
+class KernelTimer:
+    """Live per-kernel HIP event timing through gdr_profile_begin/end."""
+
+    class Rec(ctypes.Structure):
+        _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                    ("total_ms", ctypes.c_double)]
+
+    def __init__(self, lib):
+        self.lib = lib
+        lib.gdr_profile_begin.restype = ctypes.c_int32
+        lib.gdr_profile_end.restype = ctypes.c_int32
+        lib.gdr_profile_end.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+
+    def begin(self):
+        self.lib.gdr_profile_begin()
+
+    def end(self):
+        buf = (self.Rec * 32)()
+        n = self.lib.gdr_profile_end(ctypes.cast(buf, ctypes.c_void_p), 32)
+        if n < 0:
+            raise RuntimeError("gdr_profile_end failed")
+        return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the operator shards "
+              "over batch and heads with no communication; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_37_amd as gdr
+    import gdr_inputs
+
+    dev = torch.device("cuda:0")
+    lib = gdr.load_library()
+    timer = KernelTimer(lib)
+
+    # ---------------- chunked workload: KDA prefill at 32K tokens ----------------
+    cfg = dict(gdr_inputs.CONFIGS["c5b"])
+    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
+    log("generating inputs B=%d T=%d H=%d d=%d" % (B, T, H, d))
+    inp = gdr_inputs.make(**dict(cfg, bwd=True, clvr=True))
+    bf = torch.bfloat16
+    q = torch.from_numpy(inp["q"]).to(dev).to(bf)
+    k = torch.from_numpy(inp["k"]).to(dev).to(bf)
+    v = torch.from_numpy(inp["v"]).to(dev).to(bf)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    alpha = torch.from_numpy(inp["alpha"]).to(dev)
+    dO = torch.from_numpy(inp["dO"]).to(dev).to(bf)
+    h = torch.from_numpy(inp["h"]).to(dev).to(bf)
+    lam = torch.from_numpy(inp["lam"]).to(dev)
+    ws_f = torch.empty(gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf), dtype=torch.uint8,
+                       device=dev)
+    do_bwd = not args.no_backward
+    ws_b = None
+    if do_bwd:
+        try:
+            nb = gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf, backward=True)
+            ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
+            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam)
+            torch.cuda.synchronize()
+        except gdr.GdrError as e:
+            if e.code != 2:
+                raise
+            log("backward not available in this build: timing the forward only")
+            do_bwd = False
+
+    def step():
+        gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f,
+                    output_final_state=True)
+        if do_bwd:
+            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens = B * T
+    value = tokens / (ms_step / 1e3)
+
+    # per-kernel durations, HIP events on the launch stream
+    timer.begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = timer.end()
+    kernels = {n: {"launches": c, "avg_us": 1e3 * ms / c} for n, (c, ms) in kt.items()}
+    fwd_us = sum(kernels[n]["avg_us"] for n in kernels if n in ("intra_fwd", "state_fwd"))
+    log("step %.3f ms; kernels %s" % (ms_step, json.dumps(kernels)))
+
+    # algorithmic bytes (per token-head, KDA, bf16 inputs): q,k,v 3*256 + beta 4 +
+    # alpha 512 read, o 256 written -> 1540; CLVR reads and writes h (2*256)
+    th = B * T * H
+    fwd_bytes = th * (1540 + 512)
+    fwd_flops = th * (5 * 64 * d + 6 * d * d + 64 * 64 / 3)
+    # dominant kernel and its algorithmic traffic
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    per_kernel_bytes = {
+        # compulsory reads of q,k,v,beta,alpha and the CLVR read+write of h
+        "intra_fwd": th * (3 * 256 + 4 + 512 + 512),
+        # compulsory write of o (bf16)
+        "state_fwd": th * 256,
+    }
+    dom_bytes = per_kernel_bytes.get(dom, fwd_bytes)
+    achieved = dom_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+
+    # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
+    dc = gdr_inputs.DECODE_CONFIG
+    nsets = 3
+    dinp = gdr_inputs.make_decode(N=dc["N"], H=dc["H"], d=dc["d"], seed=dc["seed"], nstates=nsets)
+    dq = torch.from_numpy(dinp["q"]).to(dev).to(bf)
+    dk_ = torch.from_numpy(dinp["k"]).to(dev).to(bf)
+    dv_ = torch.from_numpy(dinp["v"]).to(dev).to(bf)
+    db = torch.from_numpy(dinp["beta"]).to(dev)
+    da = torch.from_numpy(dinp["alpha"]).to(dev)
+    states = [torch.from_numpy(s).to(dev) for s in dinp["S"]]
+    del dinp
+    od = torch.empty((dc["N"], dc["H"], dc["d"]), dtype=bf, device=dev)
+    for i in range(3):
+        gdr.decode_step(dq, dk_, dv_, db, da, states[i % nsets], out=od)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.decode_steps):
+        gdr.decode_step(dq, dk_, dv_, db, da, states[i % nsets], out=od)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_us = 1e3 * e0.elapsed_time(e1) / args.decode_steps
+    slabs = dc["N"] * dc["H"]
+    dec_bytes = slabs * (2 * dc["d"] * dc["d"] * 4 + 3 * dc["d"] * 2 + dc["d"] * 4 + 4 + dc["d"] * 2)
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+    decode = {"workload": "KDA decode step, N=256 H=16 d=128, fp32 state 256 MiB, %d rotating sets" % nsets,
+              "us_per_step": round(dec_us, 2), "tokens_per_s": round(dc["N"] / (dec_us * 1e-6), 1),
+              "achieved_GBs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+
+    # ---------------- CPU baseline: the fp64 oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ts = min(args.cpu_sample_tokens, T)
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        threads = min(cores, B * H)
+        sl = lambda a: np.ascontiguousarray(a[:, :ts])  # noqa: E731
+        t0 = time.perf_counter()
+        oracle.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["alpha"]),
+                       None, nthreads=threads)
+        if do_bwd:
+            oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]),
+                            sl(inp["alpha"]), None, sl(inp["dO"]), nthreads=threads)
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(B * ts / cpu_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": "first %d of %d tokens, all %d heads, %s, fp64 token-by-token" % (
+                   ts, T, H, "forward+backward" if do_bwd else "forward")}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/fp16-mfma/fp32-state",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunked %s + CLVR, B=%d H=%d T=%d dk=dv=%d, chunk 64" % (
+            "fwd+bwd" if do_bwd else "fwd", B, H, T, d), "global_batch": B, "seq_len": T,
+            "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "forward": {"us": round(fwd_us, 2), "tokens_per_s": round(tokens / (fwd_us * 1e-6), 1),
+                    "alg_GBs": round(fwd_bytes / (fwd_us * 1e-6) / 1e9, 1),
+                    "alg_TFLOPs": round(fwd_flops / (fwd_us * 1e-6) / 1e12, 2),
+                    "hbm_frac": round(fwd_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "mfma_frac": round(fwd_flops / (fwd_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4)},
+        "kernels_us": {n: round(kernels[n]["avg_us"], 2) for n in kernels},
+        "decode": decode,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""ctypes marshalling for libgdr.so.  No arithmetic of the operator lives here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
+_BF16, _FP32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdr.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class GdrError(RuntimeError):
+    """A non-OK status from libgdr (``code`` is the gdr_status value)."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(code, "GDR_ERR_%d" % code), msg))
+        self.code = code
+
+
+_STATUS = {0: "GDR_OK", 1: "GDR_ERR_INVALID_ARG", 2: "GDR_ERR_UNSUPPORTED", 3: "GDR_ERR_WORKSPACE",
+           4: "GDR_ERR_DEVICE"}
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``gdr_desc`` in include/gdr.h."""
+
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("gate", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("chunk", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libgdr.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libgdr.so is not built; run `python -m gated_delta_rule_37_amd.build` "
+                              "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32, F32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                ctypes.c_size_t)
+        D = ctypes.POINTER(Desc)
+        lib.gdr_workspace_size.argtypes = [D, ctypes.c_int]
+        lib.gdr_workspace_size.restype = SZ
+        lib.gdr_forward_chunked.argtypes = [D] + [P] * 10 + [P, SZ, P]
+        lib.gdr_forward_chunked.restype = ctypes.c_int
+        lib.gdr_backward.argtypes = [D] + [P] * 17 + [P, SZ, P]
+        lib.gdr_backward.restype = ctypes.c_int
+        lib.gdr_decode_step.argtypes = [I64] * 4 + [I32] * 3 + [F32] + [P] * 7 + [P]
+        lib.gdr_decode_step.restype = ctypes.c_int
+        lib.gdr_status_string.argtypes = [ctypes.c_int]
+        lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_last_error.argtypes = []
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_version.argtypes = []
+        lib.gdr_version.restype = I32
+        _lib = lib
+        return lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise GdrError(code, load_library().gdr_last_error().decode())
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return _BF16
+    if t == torch.float32:
+        return _FP32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _gate_of(alpha, q):
+    if alpha is None:
+        return GATE_NONE
+    return GATE_SCALAR if alpha.dim() == 3 else GATE_CHANNEL
+
+
+def _desc(q, v, alpha, out_dtype, scale):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    return Desc(B, T, H, dk, dv, _gate_of(alpha, q), _dt(q.dtype),
+                _dt(out_dtype if out_dtype is not None else q.dtype), float(scale), 0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(B, T, H, d, gate=GATE_CHANNEL, in_dtype=torch.bfloat16, out_dtype=None,
+                   backward=False) -> int:
+    desc = Desc(B, T, H, d, d, gate, _dt(in_dtype), _dt(out_dtype or in_dtype), 1.0, 0)
+    n = load_library().gdr_workspace_size(ctypes.byref(desc), 1 if backward else 0)
+    if n == 0 and B * H * T > 0:
+        _check(1)
+    return int(n)
+
+
+def _check_inputs(q, k, v, beta, alpha, S0):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, dk))
+    _need(v, "v", q.dtype, (B, T, H, dv))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if alpha is not None:
+        if alpha.dim() == 3:
+            _need(alpha, "alpha", torch.float32, (B, T, H))
+        else:
+            _need(alpha, "alpha", torch.float32, (B, T, H, dk))
+    _need(S0, "S0", torch.float32, (B, H, dk, dv))
+    return B, T, H, dk, dv
+
+
+def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=None,
+            clvr_scale=None, output_final_state=True, workspace=None):
+    """Chunked forward.  Returns ``(o, S_T)`` (``S_T`` None unless requested).
+
+    ``h`` ([B, T, H*dv], q's dtype) is updated in place by the CLVR epilogue
+    ``h += clvr_scale * v`` when given."""
+    B, T, H, dk, dv = _check_inputs(q, k, v, beta, alpha, S0)
+    _need(h, "h", q.dtype, (B, T, H * dv))
+    _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
+    lib = load_library()
+    desc = _desc(q, v, alpha, out_dtype, scale)
+    o = torch.empty((B, T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    need = lib.gdr_workspace_size(ctypes.byref(desc), 0)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.gdr_forward_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(alpha), _ptr(S0), _ptr(o), _ptr(ST), _ptr(h),
+                                   _ptr(clvr_scale), _ptr(workspace), need, _stream(q.device)))
+    return o, ST
+
+
+def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=None, dh=None,
+             clvr_scale=None, want_dclvr_scale=False, workspace=None):
+    """Gradients of :func:`forward`.  Returns a dict with ``dq, dk, dv, dbeta,
+    dalpha`` (None for DeltaNet), ``dS0`` and ``dclvr_scale`` (when asked)."""
+    B, T, H, dk, dv = _check_inputs(q, k, v, beta, alpha, S0)
+    _need(dO, "dO", q.dtype, (B, T, H, dv))
+    _need(dST, "dST", torch.float32, (B, H, dk, dv))
+    _need(dh, "dh", q.dtype, (B, T, H * dv))
+    _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
+    lib = load_library()
+    desc = _desc(q, v, alpha, out_dtype, scale)
+    od = out_dtype or q.dtype
+    dq = torch.empty_like(q, dtype=od)
+    dk_ = torch.empty_like(k, dtype=od)
+    dv_ = torch.empty_like(v, dtype=od)
+    dbeta = torch.empty_like(beta)
+    dalpha = None if alpha is None else torch.empty_like(alpha)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    dlam = torch.empty((H * dv,), dtype=torch.float32, device=q.device) if want_dclvr_scale else None
+    need = lib.gdr_workspace_size(ctypes.byref(desc), 1)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.gdr_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                            _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dh), _ptr(clvr_scale), _ptr(dq),
+                            _ptr(dk_), _ptr(dv_), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), _ptr(dlam),
+                            _ptr(workspace), need, _stream(q.device)))
+    return {"dq": dq, "dk": dk_, "dv": dv_, "dbeta": dbeta, "dalpha": dalpha, "dS0": dS0,
+            "dclvr_scale": dlam}
+
+
+def decode_step(q, k, v, beta, alpha, S, *, scale=1.0, out_dtype=None, out=None):
+    """One recurrence step for N sequences; ``S`` [N,H,dk,dv] fp32 is updated in
+    place.  Returns ``o`` [N,H,dv]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (N, H, dk))
+    _need(v, "v", q.dtype, (N, H, dv))
+    _need(beta, "beta", torch.float32, (N, H))
+    gate = GATE_NONE
+    if alpha is not None:
+        gate = GATE_SCALAR if alpha.dim() == 2 else GATE_CHANNEL
+        _need(alpha, "alpha", torch.float32, (N, H) if gate == GATE_SCALAR else (N, H, dk))
+    _need(S, "S", torch.float32, (N, H, dk, dv))
+    od = out_dtype or q.dtype
+    o = out if out is not None else torch.empty((N, H, dv), dtype=od, device=q.device)
+    _need(o, "out", od, (N, H, dv))
+    lib = load_library()
+    _check(lib.gdr_decode_step(N, H, dk, dv, gate, _dt(q.dtype), _dt(od), float(scale), _ptr(q),
+                               _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
+                               _stream(q.device)))
+    return o

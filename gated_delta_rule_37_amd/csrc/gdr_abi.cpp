@@ -1,0 +1,272 @@
+// gdr_abi.cpp -- the C ABI of libgdr (declared in include/gdr.h).
+//
+// Host code only: argument validation (pure functions of sizes and pointer
+// values, so it runs and is tested without a GPU), workspace sizing and carving,
+// and kernel launches on the caller's stream.  No function here allocates
+// device memory, throws, aborts or synchronises.
+#include "../../include/gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "gdr_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr int kChunk = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p+n) and [q, q+m) share a byte
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+size_t dtype_bytes(int32_t dt) { return dt == GDR_FP32 ? 4 : 2; }
+
+// Checks a descriptor; fills derived sizes.
+gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
+    if (!d) return fail(GDR_ERR_INVALID_ARG, "desc is NULL");
+    if (d->B < 0 || d->T < 0 || d->H < 0)
+        return fail(GDR_ERR_INVALID_ARG, "B, T, H must be >= 0 (got %lld, %lld, %lld)",
+                    (long long)d->B, (long long)d->T, (long long)d->H);
+    if (d->gate < GDR_GATE_NONE || d->gate > GDR_GATE_CHANNEL)
+        return fail(GDR_ERR_INVALID_ARG, "unknown gate kind %d", d->gate);
+    if ((d->in_dtype != GDR_BF16 && d->in_dtype != GDR_FP32) ||
+        (d->out_dtype != GDR_BF16 && d->out_dtype != GDR_FP32))
+        return fail(GDR_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", d->in_dtype, d->out_dtype);
+    if (!std::isfinite(d->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is not finite");
+    if (d->dk != d->dv || (d->dk != 64 && d->dk != 128))
+        return fail(GDR_ERR_UNSUPPORTED, "only dk == dv in {64, 128} is supported (got %lld, %lld)",
+                    (long long)d->dk, (long long)d->dv);
+    if (d->chunk != 0 && d->chunk != kChunk)
+        return fail(GDR_ERR_UNSUPPORTED, "only chunk size 64 is supported (got %d)", d->chunk);
+    // sizes: keep every element index and grid dimension in range
+    const int64_t lim = int64_t(1) << 40;
+    if (d->B > lim || d->T > lim || d->H > (int64_t(1) << 24))
+        return fail(GDR_ERR_INVALID_ARG, "sizes out of range");
+    const double elems = double(d->B) * double(d->T) * double(d->H) * double(d->dk);
+    if (elems > 9.0e15) return fail(GDR_ERR_INVALID_ARG, "tensor too large");
+    const int64_t nc = (d->T + kChunk - 1) / kChunk;
+    const double blocks = double(d->B) * double(d->H) * double(nc > 0 ? nc : 1);
+    const double state_blocks = double(d->B) * double(d->H) * double(d->dk / 16);
+    if (blocks > 2147483647.0 || state_blocks > 2147483647.0)
+        return fail(GDR_ERR_INVALID_ARG, "too many chunks for one launch");
+    if (NC) *NC = nc;
+    return GDR_OK;
+}
+
+}  // namespace
+
+namespace gdr {
+
+// Carves the chunk workspace; returns the bytes needed.  `base` may be NULL
+// (sizing only).
+size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* out, void* base) {
+    ChunkWs w;
+    std::memset(&w, 0, sizeof w);
+    size_t off = 0;
+    char* p = static_cast<char*>(base);
+    auto take = [&](size_t bytes) -> void* {
+        void* r = p ? p + off : nullptr;
+        off += align_up(bytes);
+        return r;
+    };
+    const size_t mat = size_t(nch) * kChunk * D * op_bytes;    // [64][D] per chunk-head
+    const size_t sq = size_t(nch) * kChunk * kChunk * op_bytes;  // [64][64]
+    const size_t st = size_t(nch) * D * D * op_bytes;            // [D][D]
+    w.W = take(mat);
+    w.Ut = take(mat);
+    w.Qt = take(mat);
+    w.KbT = take(mat);
+    w.A = take(sq);
+    w.gam = static_cast<float*>(take(size_t(nch) * D * 4));
+    if (backward) {
+        w.AT = take(sq);
+        w.Kb = take(mat);
+        w.QtT = take(mat);
+        w.WT = take(mat);
+        w.Ssnap = take(st);
+        w.Usave = take(mat);
+        w.dSsnap = take(st);
+        w.dUsave = take(mat);
+    }
+    if (out) *out = w;
+    return off;
+}
+
+}  // namespace gdr
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+    switch (s) {
+        case GDR_OK: return "GDR_OK";
+        case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+        case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+        case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+        case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE";
+    }
+    return "GDR_ERR_UNKNOWN";
+}
+
+const char* gdr_last_error(void) { return g_err; }
+
+int32_t gdr_version(void) { return 100; }
+
+size_t gdr_workspace_size(const gdr_desc* desc, int op) {
+    int64_t NC = 0;
+    if (check_desc(desc, &NC) != GDR_OK) return 0;
+    if (op != 0 && op != 1) {
+        fail(GDR_ERR_INVALID_ARG, "op must be 0 (forward) or 1 (backward)");
+        return 0;
+    }
+    const int64_t nch = desc->B * desc->H * NC;
+    const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
+    return gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, nullptr, nullptr);
+}
+
+gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                               const float* beta, const float* alpha, const float* S0, void* o,
+                               float* ST, void* h_clvr, const float* clvr_scale, void* ws,
+                               size_t ws_bytes, void* stream) {
+    int64_t NC = 0;
+    gdr_status st = check_desc(desc, &NC);
+    if (st != GDR_OK) return st;
+    const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
+    const int64_t ntok = B * T * H;
+    const bool any = ntok > 0;
+    if (any && (!q || !k || !v || !beta || !o))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, beta and o are required");
+    if ((desc->gate == GDR_GATE_NONE) != (alpha == nullptr) && any)
+        return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
+    const void* ptrs[] = {q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    if (clvr_scale && !h_clvr) return fail(GDR_ERR_INVALID_ARG, "clvr_scale given without h_clvr");
+    const size_t ib = dtype_bytes(desc->in_dtype), ob = dtype_bytes(desc->out_dtype);
+    const size_t n_in = size_t(ntok) * D;
+    const size_t o_bytes = n_in * ob;
+    const size_t a_bytes = desc->gate == GDR_GATE_CHANNEL ? n_in * 4 : size_t(ntok) * 4;
+    const size_t s_bytes = size_t(B * H) * D * D * 4;
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{q, n_in * ib}, {k, n_in * ib}, {v, n_in * ib}, {beta, size_t(ntok) * 4},
+               {alpha, a_bytes}, {S0, s_bytes}, {clvr_scale, size_t(H) * D * 4}};
+    for (auto& in : ins) {
+        if (overlap(o, o_bytes, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "o overlaps an input");
+        if (ST && in.p != S0 && overlap(ST, s_bytes, in.p, in.n))
+            return fail(GDR_ERR_INVALID_ARG, "ST overlaps an input other than S0");
+        if (h_clvr && in.p != nullptr && overlap(h_clvr, n_in * ib, in.p, in.n))
+            return fail(GDR_ERR_INVALID_ARG, "h_clvr overlaps an input");
+    }
+    if (ST && overlap(ST, s_bytes, o, o_bytes)) return fail(GDR_ERR_INVALID_ARG, "ST overlaps o");
+    if (h_clvr && overlap(h_clvr, n_in * ib, o, o_bytes))
+        return fail(GDR_ERR_INVALID_ARG, "h_clvr overlaps o");
+    if (S0 && ST && S0 != ST && overlap(S0, s_bytes, ST, s_bytes))
+        return fail(GDR_ERR_INVALID_ARG, "ST partially overlaps S0 (it may only alias it exactly)");
+    const int64_t nch = B * H * NC;
+    const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
+    gdr::ChunkWs w;
+    const size_t need = gdr::chunk_ws_bytes(nch, int(D), opb, false, &w, ws);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+    if (B * H == 0) return GDR_OK;
+    if (ws && overlap(ws, need, o, o_bytes)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps o");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
+    hipError_t e = hipSuccess;
+    if (NC > 0) {
+        gdr::prof_before(s);
+        e = gdr::launch_intra(int(D), desc->gate, in_f32, false, B, T, int(H), NC, q, k, v, beta, alpha,
+                              h_clvr, clvr_scale, w, s);
+        gdr::prof_after("intra_fwd", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
+    }
+    gdr::prof_before(s);
+    e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o,
+                              false, s);
+    gdr::prof_after("state_fwd", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* alpha, const float* S0, const void* dO,
+                        const float* dST, const void* dh_clvr, const float* clvr_scale, void* dq,
+                        void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                        float* dclvr_scale, void* ws, size_t ws_bytes, void* stream) {
+    int64_t NC = 0;
+    gdr_status st = check_desc(desc, &NC);
+    if (st != GDR_OK) return st;
+    (void)q; (void)k; (void)v; (void)beta; (void)alpha; (void)S0; (void)dO; (void)dST;
+    (void)dh_clvr; (void)clvr_scale; (void)dq; (void)dk; (void)dv; (void)dbeta; (void)dalpha;
+    (void)dS0; (void)dclvr_scale; (void)ws; (void)ws_bytes; (void)stream;
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_backward is not available in this build");
+}
+
+gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,
+                           int32_t in_dtype, int32_t out_dtype, float scale, const void* q,
+                           const void* k, const void* v, const float* beta, const float* alpha,
+                           float* S, void* o, void* stream) {
+    gdr_desc d;
+    std::memset(&d, 0, sizeof d);
+    d.B = N; d.T = 1; d.H = H; d.dk = dk; d.dv = dv; d.gate = gate; d.in_dtype = in_dtype;
+    d.out_dtype = out_dtype; d.scale = scale; d.chunk = 0;
+    gdr_status st = check_desc(&d, nullptr);
+    if (st != GDR_OK) return st;
+    const int64_t nslab = N * H;
+    if (nslab == 0) return GDR_OK;
+    if (nslab > 2147483647LL) return fail(GDR_ERR_INVALID_ARG, "N*H too large for one launch");
+    if (!q || !k || !v || !beta || !S || !o)
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, beta, S and o are required");
+    if ((gate == GDR_GATE_NONE) != (alpha == nullptr))
+        return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
+    const void* ptrs[] = {q, k, v, beta, alpha, S, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const size_t n = size_t(nslab) * dk;
+    const size_t s_bytes = size_t(nslab) * dk * dv * 4;
+    const size_t a_bytes = gate == GDR_GATE_CHANNEL ? n * 4 : size_t(nslab) * 4;
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{q, n * ib}, {k, n * ib}, {v, n * ib}, {beta, size_t(nslab) * 4}, {alpha, a_bytes}};
+    for (auto& in : ins) {
+        if (overlap(o, n * ob, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "o overlaps an input");
+        if (overlap(S, s_bytes, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "S overlaps an input");
+    }
+    if (overlap(S, s_bytes, o, n * ob)) return fail(GDR_ERR_INVALID_ARG, "o overlaps S");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    gdr::prof_before(s);
+    hipError_t e = gdr::launch_decode(int(dk), gate, in_dtype == GDR_FP32, out_dtype == GDR_FP32, nslab,
+                                      int(H), scale, q, k, v, beta, alpha, S, o, s);
+    gdr::prof_after("decode", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// gdr_common.hpp -- shared device helpers for the gfx950 kernels of libgdr.
+//
+// Matrix-core (MFMA) fragments.  Every product in the chunked path is tiled
+// into 16x16 output tiles contracted over K in steps of 32:
+//   A fragment (16 x 32, row-major M x K): lane l holds row (l % 16) and the
+//     eight consecutive k = 8*(l/16) .. 8*(l/16)+7.
+//   B fragment (32 x 16, K x N): lane l holds column (l % 16) and the same
+//     eight consecutive k.
+//   C/D tile (16 x 16, fp32): lane l holds column (l % 16) and rows
+//     4*(l/16) .. 4*(l/16)+3.
+// For fp16 operands one v_mfma_f32_16x16x32_f16 consumes a fragment pair.  For
+// fp32 operands the same fragments feed eight v_mfma_f32_16x16x4_f32: the i-th
+// instruction takes element i of every lane, so lane group g contributes
+// k = 8g + i.  A contraction only needs A and B to agree on the k order, so both
+// precisions share one fragment layout and one set of address computations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float8v __attribute__((ext_vector_type(8)));
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+enum Gate { GATE_NONE = 0, GATE_SCALAR = 1, GATE_CHANNEL = 2 };
+
+constexpr int WAVE = 64;
+constexpr int CHUNK = 64;
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Element type of the inputs: bf16 (raw bits) or fp32.
+template <bool F32> struct InType { using T = bf16_t; };
+template <> struct InType<true> { using T = float; };
+
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) {
+    return static_cast<_Float16>(x);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragments
+// ---------------------------------------------------------------------------
+
+template <typename OpT> struct Frag;
+
+template <> struct Frag<_Float16> {
+    half8 v;
+    __device__ __forceinline__ void zero() {
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<_Float16>(0.f);
+    }
+    __device__ __forceinline__ void load(const _Float16* p) { v = *reinterpret_cast<const half8*>(p); }
+};
+
+template <> struct Frag<float> {
+    float8v v;
+    __device__ __forceinline__ void zero() {
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+    __device__ __forceinline__ void load(const float* p) {
+        const float4v a = reinterpret_cast<const float4v*>(p)[0];
+        const float4v b = reinterpret_cast<const float4v*>(p)[1];
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    }
+};
+
+// acc += A(16x32) * B(32x16)
+__device__ __forceinline__ void mma(const Frag<_Float16>& a, const Frag<_Float16>& b, float4v& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(const Frag<float>& a, const Frag<float>& b, float4v& acc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4v zero4() {
+    float4v z;
+    z[0] = 0.f; z[1] = 0.f; z[2] = 0.f; z[3] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
+
+// Fast base-2 exponent and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace gdr

@@ -1,0 +1,528 @@
+// gdr_intra.hip -- intra-chunk transform of the chunked gated delta rule.
+//
+// One workgroup (4 waves) per (batch, head, chunk of 64 tokens).  With S the
+// chunk's start state, G_r the in-chunk inclusive sum of log2(alpha) (kept in
+// log space for range safety, KDA blog section 7.1) and
+//   Kt = K*2^G, Kh = K*2^-G, Qt = Q*2^G, Kb = K*2^(G_last - G)   (row-wise),
+// unrolling the token recurrence over the chunk gives
+//   U = T (V - Kt S),  T = (I + L)^-1 diag(beta),
+//   L = strict_tril(diag(beta) Kt Kh^T),
+//   O = Qt S + A U,    A = tril(Qt Kh^T),
+//   S_next = Diag(2^G_last) S + Kb^T U.
+// This kernel computes everything that does not depend on S -- the rank-1
+// updates of the chunk gathered into one triangular solve plus dense products
+// (the "UT transform" of the KDA blog, section 6.2) -- and writes, per chunk,
+//   W = T Kt, Ut = T V, Qt, Kb^T, A and gamma = 2^G_last
+// for the sequential state pass.  The optional CLVR epilogue (h += lam * v) is
+// fused here because this kernel already reads v.
+//
+// Range handling for the channel gate (Kimi Delta Attention).  The pair factor
+// 2^(G_r - G_i) (r >= i) is <= 1, but Kt Kh^T written naively overflows for
+// strong gates.  The chunk is split into four 16-row blocks; block row R uses
+// the reference value ref(R) = G at the last row before the block, so that
+//   row operand   Kq_r = k_r 2^(G_r - ref(R))   <= 1
+//   column operand Kh_i = k_i 2^(ref(R) - G_i)  <= 1 for i before block R,
+// and only the 16x16 diagonal block has column factors >= 1 (bounded by the
+// block's own decay range rho).  When rho exceeds what the operand precision
+// can carry, that diagonal block is recomputed exactly on the vector ALUs from
+// running products of alpha (no exponentials, no overflow).  For the scalar
+// gate the factor does not depend on the channel, so K K^T and Q K^T are taken
+// on the raw inputs and the decay mask is applied afterwards in fp32.
+#include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+#include <type_traits>
+
+namespace gdr {
+
+template <int D, int GATE, bool IN_F32>
+struct IntraLayout {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    static constexpr int OPB = sizeof(OpT);
+    static constexpr int PAD = 16 / OPB;  // one 16-byte granule per row: conflict-free fragment reads
+    static constexpr int LDR = D + PAD;   // row stride of [64][D] arrays
+    static constexpr int LDC = CHUNK + PAD;  // row stride of [D][64] and [64][64] operand arrays
+    static constexpr int NPART = 256 / D;    // row parts of the element-wise phase
+    static constexpr int RPP = CHUNK / NPART;  // rows per part
+    // phase 1-2: Kq, Qq, Kh  (each [64][LDR])
+    static constexpr int KQ = 0;
+    static constexpr int QQ = KQ + CHUNK * LDR * OPB;
+    static constexpr int KH = QQ + CHUNK * LDR * OPB;
+    static constexpr int END12 = KH + CHUNK * LDR * OPB;
+    // phase 3-4: Kt^T, V^T ([D][LDC]), P/L/T, N
+    static constexpr int KTT = 0;
+    static constexpr int VT = KTT + D * LDC * OPB;
+    static constexpr int PL = VT + D * LDC * OPB;
+    static constexpr int PL_BYTES = (CHUNK * CHUNK * 4 > CHUNK * LDC * OPB) ? CHUNK * CHUNK * 4 : CHUNK * LDC * OPB;
+    // N (and, during phase 2, the fp32 P staging) must not overlap phase 1-2 buffers
+    static constexpr int NM = (PL + PL_BYTES > END12) ? PL + PL_BYTES : END12;
+    static constexpr int END34 = NM + CHUNK * CHUNK * 4;
+    static constexpr int BYTES = END12 > END34 ? END12 : END34;
+    // operand-precision limit on the in-block decay range (log2 units)
+    static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
+};
+
+template <typename OpT, int N>
+__device__ __forceinline__ void store_run(OpT* dst, const float* src) {
+    // N consecutive values, 16-byte aligned destination
+    if constexpr (sizeof(OpT) == 2) {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(src[i + e]);
+            *reinterpret_cast<half8*>(dst + i) = h;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            float4v f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = src[i + e];
+            *reinterpret_cast<float4v*>(dst + i) = f;
+        }
+    }
+}
+
+template <typename OpT>
+__device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
+    if constexpr (sizeof(OpT) == 2) {
+        half4 h;
+        h[0] = static_cast<_Float16>(v[0]); h[1] = static_cast<_Float16>(v[1]);
+        h[2] = static_cast<_Float16>(v[2]); h[3] = static_cast<_Float16>(v[3]);
+        *reinterpret_cast<half4*>(dst) = h;
+    } else {
+        *reinterpret_cast<float4v*>(dst) = v;
+    }
+}
+
+template <int D, int GATE, bool IN_F32, bool BWD>
+__global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC,
+                                                    const void* __restrict__ q_,
+                                                    const void* __restrict__ k_,
+                                                    const void* __restrict__ v_,
+                                                    const float* __restrict__ beta,
+                                                    const float* __restrict__ alpha,
+                                                    void* __restrict__ h_, const float* __restrict__ lam,
+                                                    ChunkWs ws) {
+    using L = IntraLayout<D, GATE, IN_F32>;
+    using OpT = typename L::OpT;
+    using InT = typename InType<IN_F32>::T;
+    constexpr int NPART = L::NPART, RPP = L::RPP, LDR = L::LDR, LDC = L::LDC;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ float s_tot[NPART][D];
+    __shared__ float s_blk[4][D];  // G at the last row of each 16-row block
+    __shared__ float s_gs[CHUNK];  // scalar-gate G per row
+    __shared__ float s_beta[CHUNK];
+    __shared__ float s_rho[4][4];
+
+    OpT* Kq = reinterpret_cast<OpT*>(smem + L::KQ);
+    OpT* Qq = reinterpret_cast<OpT*>(smem + L::QQ);
+    OpT* Kh = reinterpret_cast<OpT*>(smem + L::KH);
+    OpT* KtT = reinterpret_cast<OpT*>(smem + L::KTT);
+    OpT* VT = reinterpret_cast<OpT*>(smem + L::VT);
+    float* Pm = reinterpret_cast<float*>(smem + L::PL);
+    OpT* Tm = reinterpret_cast<OpT*>(smem + L::PL);
+    float* Nm = reinterpret_cast<float*>(smem + L::NM);
+
+    const int64_t ch = blockIdx.x;  // (b*H + h)*NC + c
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t t0 = c * CHUNK;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int cc = tid % D, part = tid / D, r0 = part * RPP;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    const InT* q = reinterpret_cast<const InT*>(q_);
+    const InT* k = reinterpret_cast<const InT*>(k_);
+    const InT* v = reinterpret_cast<const InT*>(v_);
+    const int64_t tokstride = static_cast<int64_t>(H) * D;
+    const int64_t base = ((b * T + t0) * H + h) * D;  // element (row 0, channel 0) of this chunk
+    const int64_t nvalid64 = T - t0;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
+
+    // ---------------- phase 1: load, gate cumsum, element-wise operands ----------------
+    float G[RPP], kk[RPP], vv[RPP], qq[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const int r = r0 + j;
+        const bool ok = r < nvalid;
+        const int64_t e = base + r * tokstride + cc;
+        kk[j] = ok ? to_f32(k[e]) : 0.f;
+        qq[j] = ok ? to_f32(q[e]) : 0.f;
+        vv[j] = ok ? to_f32(v[e]) : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(alpha[e]) : 0.f;
+        else G[j] = 0.f;
+    }
+    if (tid < CHUNK) {
+        const bool ok = tid < nvalid;
+        const int64_t tok = (b * T + t0 + tid) * H + h;
+        s_beta[tid] = ok ? beta[tok] : 0.f;
+        if constexpr (GATE == GATE_SCALAR) {
+            float g = ok ? log2_fast(alpha[tok]) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(g, off);
+                if (lane >= off) g += y;
+            }
+            s_gs[tid] = g;
+        }
+    }
+    if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+        for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
+        s_tot[part][cc] = G[RPP - 1];
+    }
+    __syncthreads();
+    if constexpr (GATE == GATE_CHANNEL) {
+        float carry = 0.f;
+        for (int p = 0; p < part; ++p) carry += s_tot[p][cc];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            G[j] += carry;
+            if (((r0 + j) & 15) == 15) s_blk[(r0 + j) >> 4][cc] = G[j];
+        }
+    } else if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) G[j] = s_gs[r0 + j];
+    }
+    __syncthreads();
+
+    float glast;
+    if constexpr (GATE == GATE_CHANNEL) glast = s_blk[3][cc];
+    else if constexpr (GATE == GATE_SCALAR) glast = s_gs[CHUNK - 1];
+    else glast = 0.f;
+
+    if constexpr (GATE == GATE_CHANNEL) {
+        // decay range of each diagonal block, max over channels
+        if (tid < D) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                float rho = (R ? s_blk[R - 1][tid] : 0.f) - s_blk[R][tid];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
+                if (lane == 0) s_rho[wid][R] = rho;
+            }
+        }
+    }
+
+    // element-wise outputs: Qt, Kb^T, gamma; row operands Kq, Qq
+    {
+        OpT* Qt_g = reinterpret_cast<OpT*>(ws.Qt) + ch * CHUNK * D;
+        OpT* KbT_g = reinterpret_cast<OpT*>(ws.KbT) + ch * D * CHUNK;
+        float kb[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = r0 + j;
+            const float e = exp2_fast(G[j]);
+            Qt_g[r * D + cc] = from_f32<OpT>(qq[j] * e);
+            kb[j] = kk[j] * exp2_fast(glast - G[j]);
+            if constexpr (GATE == GATE_CHANNEL) {
+                const int R = r >> 4;
+                const float ref = R ? s_blk[R - 1][cc] : 0.f;
+                const float f = exp2_fast(G[j] - ref);
+                Kq[r * LDR + cc] = from_f32<OpT>(kk[j] * f);
+                Qq[r * LDR + cc] = from_f32<OpT>(qq[j] * f);
+            } else {
+                Kq[r * LDR + cc] = from_f32<OpT>(kk[j]);
+                Qq[r * LDR + cc] = from_f32<OpT>(qq[j]);
+                Kh[r * LDR + cc] = from_f32<OpT>(kk[j]);
+            }
+        }
+        store_run<OpT, RPP>(KbT_g + cc * CHUNK + r0, kb);
+        if (part == NPART - 1) ws.gam[ch * D + cc] = exp2_fast(glast);
+    }
+
+    // CLVR epilogue: the written value v is routed into the hidden stream
+    if (h_ != nullptr) {
+        InT* hh = reinterpret_cast<InT*>(h_);
+        const float lm = lam ? lam[h * D + cc] : 1.f;
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = r0 + j;
+            if (r < nvalid) {
+                const int64_t e = base + r * tokstride + cc;
+                hh[e] = from_f32<InT>(__builtin_fmaf(lm, vv[j], to_f32(hh[e])));
+            }
+        }
+    }
+
+    int flags = 0;  // bit R: diagonal block R needs the exact path
+    __syncthreads();
+    if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float rho = s_rho[0][R];
+#pragma unroll
+            for (int w = 1; w < D / 64; ++w) rho = fmaxf(rho, s_rho[w][R]);
+            if (!(rho <= L::RHO_MAX)) flags |= 1 << R;  // NaN-safe
+        }
+    }
+
+    // ---------------- phase 2: P = Kt Kh^T and A = Qt Kh^T on the matrix cores ----------------
+    // Tiles are computed transposed (Kh rows as the A operand), so lane l ends up
+    // holding P[16R + l%16][16I + 4(l/16) .. +3]: four consecutive columns of one row.
+    float* Ps = Nm;  // fp32 P staging, outside the phase 1-2 buffers
+    OpT* A_g = reinterpret_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
+    constexpr int NPH = (GATE == GATE_CHANNEL) ? 4 : 1;
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+        if constexpr (GATE == GATE_CHANNEL) {
+            // column operand for block row R = ph: rows 0 .. 16R+15 with reference ref(R)
+            const int R = ph;
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                const int r = r0 + j;
+                if (r <= 16 * R + 15) {
+                    const float ref = R ? s_blk[R - 1][cc] : 0.f;
+                    float val = kk[j] * exp2_fast(ref - G[j]);
+                    if ((r >> 4) == R && ((flags >> R) & 1)) val = 0.f;  // diagonal block redone exactly below
+                    Kh[r * LDR + cc] = from_f32<OpT>(val);
+                }
+            }
+            __syncthreads();
+        }
+        const int Rlo = (GATE == GATE_CHANNEL) ? ph : 0;
+        const int Rhi = (GATE == GATE_CHANNEL) ? ph : 3;
+        int ti = 0;
+        for (int R = Rlo; R <= Rhi; ++R) {
+            for (int I = 0; I <= R; ++I) {
+                for (int isA = 0; isA < 2; ++isA, ++ti) {
+                    if ((ti & 3) != wid) continue;
+                    if (GATE == GATE_CHANNEL && I == R && ((flags >> R) & 1)) continue;
+                    float4v acc = zero4();
+                    const OpT* arow = Kh + (16 * I + l16) * LDR + 8 * g4;
+                    const OpT* brow = (isA ? Qq : Kq) + (16 * R + l16) * LDR + 8 * g4;
+#pragma unroll
+                    for (int kq = 0; kq < D / 32; ++kq) {
+                        Frag<OpT> fa, fb;
+                        fa.load(arow + 32 * kq);
+                        fb.load(brow + 32 * kq);
+                        mma(fa, fb, acc);
+                    }
+                    const int r = 16 * R + l16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * I + 4 * g4 + e;
+                        float f = (i <= r) ? 1.f : 0.f;
+                        if constexpr (GATE == GATE_SCALAR) f = (i <= r) ? exp2_fast(s_gs[r] - s_gs[i]) : 0.f;
+                        acc[e] *= f;
+                    }
+                    if (isA) {
+                        store4<OpT>(A_g + r * CHUNK + 16 * I + 4 * g4, acc);
+                    } else {
+                        *reinterpret_cast<float4v*>(Ps + r * CHUNK + 16 * I + 4 * g4) = acc;
+                    }
+                }
+            }
+        }
+        if (GATE == GATE_CHANNEL && ph < NPH - 1) __syncthreads();  // Kh is rebuilt next phase
+    }
+    // zero the strictly upper tiles of A (never computed)
+    for (int e = tid; e < 6 * 64; e += 256) {
+        const int tile = e / 64, w = e % 64;  // tile: (R, I) with I > R
+        const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+        const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+        const int r = 16 * R + w / 4, i0 = 16 * I + 4 * (w % 4);
+        store4<OpT>(A_g + r * CHUNK + i0, zero4());
+    }
+    __syncthreads();  // all reads of Kq/Qq/Kh done: the region is reused below
+
+    // Kt^T and V^T operands for W and Ut
+    {
+        float kt[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) kt[j] = kk[j] * exp2_fast(G[j]);
+        store_run<OpT, RPP>(KtT + cc * LDC + r0, kt);
+        store_run<OpT, RPP>(VT + cc * LDC + r0, vv);
+    }
+    __syncthreads();
+
+    // exact diagonal blocks for the channel gate when the decay range is too wide:
+    // 2^(G_r - G_i) = prod_{s=i+1..r} alpha_s, accumulated as a running product
+    if constexpr (GATE == GATE_CHANNEL) {
+        constexpr int CPG = D / 16;  // channels per group
+        const int rr = tid >> 4, cg = tid & 15;
+#pragma unroll 1
+        for (int R = 0; R < 4; ++R) {
+            if (!((flags >> R) & 1)) continue;
+            const int r = 16 * R + rr;
+            const bool okr = r < nvalid;
+            float kr[CPG], qr[CPG], f[CPG];
+#pragma unroll
+            for (int m = 0; m < CPG; ++m) {
+                const int64_t e = base + r * tokstride + cg * CPG + m;
+                kr[m] = okr ? to_f32(k[e]) : 0.f;
+                qr[m] = okr ? to_f32(q[e]) : 0.f;
+                f[m] = 1.f;
+            }
+#pragma unroll 1
+            for (int i = 15; i >= 0; --i) {
+                const int ii = 16 * R + i;
+                float ps = 0.f, as = 0.f;
+                if (ii <= r) {
+                    if (ii < r) {  // include alpha_{ii+1}
+                        const int s = ii + 1;
+                        const bool oks = s < nvalid;
+#pragma unroll
+                        for (int m = 0; m < CPG; ++m)
+                            f[m] *= oks ? alpha[base + s * tokstride + cg * CPG + m] : 1.f;
+                    }
+                    const bool oki = ii < nvalid;
+#pragma unroll
+                    for (int m = 0; m < CPG; ++m) {
+                        const float ki = oki ? to_f32(k[base + ii * tokstride + cg * CPG + m]) : 0.f;
+                        ps += kr[m] * ki * f[m];
+                        as += qr[m] * ki * f[m];
+                    }
+                }
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    ps += __shfl_xor(ps, off);
+                    as += __shfl_xor(as, off);
+                }
+                if (cg == 0) {
+                    Ps[r * CHUNK + ii] = ps;
+                    A_g[r * CHUNK + ii] = from_f32<OpT>(as);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---------------- phase 3: T = (I + L)^-1 diag(beta), L = strict_tril(diag(beta) P) ----------------
+    for (int e = tid; e < CHUNK * CHUNK; e += 256) {
+        const int r = e / CHUNK, i = e % CHUNK;
+        Pm[e] = (i < r) ? s_beta[r] * Ps[e] : 0.f;  // Ps aliases Nm: read before the zero
+        Nm[e] = 0.f;
+    }
+    __syncthreads();
+    // diagonal 16x16 blocks by forward substitution, one wave per block, lane = column
+    if (lane < 16) {
+        const int R = wid;
+        const float* Lb = Pm + (16 * R) * CHUNK + 16 * R;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) s += Lb[r * CHUNK + m] * x[m];
+            if (r > lane) x[r] = -s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Nm[(16 * R + r) * CHUNK + 16 * R + lane] = x[r];
+    }
+    __syncthreads();
+    // off-diagonal blocks: N[R, <R] = -N_RR (L[R, <R] N[<R, <R])
+    {
+        const int r = tid >> 4, i0 = tid & 15;
+        float* X = Pm;  // rows 0..15 of L are no longer needed
+#pragma unroll
+        for (int R = 1; R < 4; ++R) {
+            float xs[3];
+#pragma unroll
+            for (int m = 0; m < R; ++m) {
+                const int ii = 16 * m + i0;
+                float s = 0.f;
+                const float* Lr = Pm + (16 * R + r) * CHUNK;
+                for (int j = 16 * m; j < 16 * R; ++j) s += Lr[j] * Nm[j * CHUNK + ii];
+                xs[m] = s;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < R; ++m) X[r * CHUNK + 16 * m + i0] = xs[m];
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < R; ++m) {
+                const int ii = 16 * m + i0;
+                float s = 0.f;
+                const float* Nr = Nm + (16 * R + r) * CHUNK + 16 * R;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s += Nr[j] * X[j * CHUNK + ii];
+                xs[m] = -s;
+            }
+#pragma unroll
+            for (int m = 0; m < R; ++m) Nm[(16 * R + r) * CHUNK + 16 * m + i0] = xs[m];
+            __syncthreads();
+        }
+    }
+    // T = N diag(beta) in operand precision (row-major, padded), in the L region
+    for (int e = tid; e < CHUNK * CHUNK; e += 256) {
+        const int r = e / CHUNK, i = e % CHUNK;
+        Tm[r * LDC + i] = from_f32<OpT>(Nm[e] * s_beta[i]);
+    }
+    __syncthreads();
+
+    // ---------------- phase 4: W = T Kt and Ut = T V (computed transposed) ----------------
+    {
+        OpT* W_g = reinterpret_cast<OpT*>(ws.W) + ch * CHUNK * D;
+        OpT* U_g = reinterpret_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
+        for (int m = wid; m < D / 16; m += 4) {
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                const OpT* arow = (mat ? VT : KtT) + (16 * m + l16) * LDC + 8 * g4;
+                Frag<OpT> fa0, fa1;
+                fa0.load(arow);
+                fa1.load(arow + 32);
+                OpT* dst = mat ? U_g : W_g;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    float4v acc = zero4();
+                    const OpT* brow = Tm + (16 * n + l16) * LDC + 8 * g4;
+                    Frag<OpT> fb;
+                    fb.load(brow);
+                    mma(fa0, fb, acc);
+                    if (n >= 2) {
+                        fb.load(brow + 32);
+                        mma(fa1, fb, acc);
+                    }
+                    store4<OpT>(dst + (16 * n + l16) * D + 16 * m + 4 * g4, acc);
+                }
+            }
+        }
+    }
+    (void)BWD;
+}
+
+template <int D, int GATE, bool IN_F32>
+static hipError_t launch_intra_t(int64_t B, int64_t T, int H, int64_t NC, const void* q,
+                                 const void* k, const void* v, const float* beta,
+                                 const float* alpha, void* h_clvr, const float* lam,
+                                 const ChunkWs& ws, hipStream_t stream) {
+    const int64_t nblk = B * H * NC;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, false>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+    return hipGetLastError();
+}
+
+template <int D, bool IN_F32>
+static hipError_t launch_intra_d(int gate, int64_t B, int64_t T, int H, int64_t NC,
+                                 const void* q, const void* k, const void* v, const float* beta,
+                                 const float* alpha, void* h_clvr, const float* lam,
+                                 const ChunkWs& ws, hipStream_t stream) {
+    switch (gate) {
+        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    }
+}
+
+hipError_t launch_intra(int D, int gate, bool in_f32, bool backward, int64_t B, int64_t T, int H,
+                        int64_t NC, const void* q, const void* k, const void* v,
+                        const float* beta, const float* alpha, void* h_clvr, const float* lam,
+                        const ChunkWs& ws, hipStream_t stream) {
+    (void)backward;
+    if (D == 64) {
+        if (in_f32) return launch_intra_d<64, true>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        return launch_intra_d<64, false>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    }
+    if (in_f32) return launch_intra_d<128, true>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    return launch_intra_d<128, false>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+}
+
+}  // namespace gdr

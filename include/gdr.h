@@ -1,0 +1,175 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) gated delta-rule operator library
+ * (libgdr.so).
+ *
+ * The operator (KDA blog "线性注意力架构演进与Kimi Delta Attention创新实践",
+ * section 2.1, with "=" and "+" restored where the page's extraction lost them):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * S is a dk x dv matrix per (sequence, head); the read-out uses the state after
+ * the token's write.  One family, three gate kinds (linear-attention comparison
+ * explainer "线性注意力架构：机制、权衡与跨层路由", core method 1):
+ *   GDR_GATE_NONE     DeltaNet             alpha == 1
+ *   GDR_GATE_SCALAR   Gated DeltaNet       one alpha per token and head
+ *   GDR_GATE_CHANNEL  Kimi Delta Attention one alpha per token, head, key channel
+ * The normaliser Z_t of the explainer's unified notation is 1 for this family.
+ *
+ * Optional Cross-Layer Value Routing (CLVR) epilogue (explainer, cross-layer
+ * routing section; abstract on the paper page): the layer's written value v_t
+ * is added into the aligned hidden (residual) stream, with a per-channel scale
+ * lam standing in for the paper's zero-initialised routing projection:
+ *     h[b,t,h*dv+j] += lam[h*dv+j] * v[b,t,h,j]
+ *
+ * Conventions shared by every entry point
+ *   - Every function is extern "C", never throws, never aborts, and never
+ *     allocates device memory.  The caller owns every buffer.
+ *   - Pointers are device pointers unless stated otherwise, and must be
+ *     16-byte aligned.  All tensors are dense row-major:
+ *       q, k        [B, T, H, dk]          v, o   [B, T, H, dv]
+ *       beta        [B, T, H]    fp32
+ *       alpha       NONE: NULL; SCALAR: [B, T, H] fp32; CHANNEL: [B, T, H, dk]
+ *                   fp32; every value in (0, 1] (the chunked kernels work with
+ *                   log2(alpha); alpha == 0 is outside the domain)
+ *       S0, ST      [B, H, dk, dv] fp32
+ *       h_clvr      [B, T, H*dv] in the input dtype
+ *       clvr_scale  [H*dv] fp32
+ *   - v1 supports dk == dv in {64, 128} and chunk size 64.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns at once.  Host-side validation runs before any launch;
+ *     on a non-OK status nothing has been launched and no output was touched.
+ *     A launch failure returns GDR_ERR_DEVICE; asynchronous device faults
+ *     surface at the caller's next synchronisation.
+ *   - Precision: fp32 state and fp32 accumulation throughout.  For bf16 inputs
+ *     the matrix-core operands of the chunked path are rounded to fp16 (one
+ *     pass), which requires every intermediate (|v|, |S|, the entries of the
+ *     in-chunk transform) to stay below 65504 in magnitude.  For fp32 inputs
+ *     the operands stay fp32.
+ *   - NaN and Inf propagate; they are not checked.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size, bad enum, aliasing */
+    GDR_ERR_UNSUPPORTED = 2, /* a valid request this version does not implement */
+    GDR_ERR_WORKSPACE = 3,   /* ws_bytes below gdr_workspace_size() or ws NULL */
+    GDR_ERR_DEVICE = 4       /* the HIP runtime reported an error at launch */
+} gdr_status;
+
+typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gdr_gate;
+
+typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
+
+typedef struct {
+    int64_t B, T, H, dk, dv; /* batch, tokens, heads, key and value widths */
+    int32_t gate;            /* gdr_gate */
+    int32_t in_dtype;        /* gdr_dtype of q, k, v, dO and h_clvr */
+    int32_t out_dtype;       /* gdr_dtype of o, dq, dk, dv */
+    float scale;             /* o = scale * S^T q ; 1.0 is the pages' equation */
+    int32_t chunk;           /* 0 selects the default (64); only 64 is supported */
+} gdr_desc;
+
+/* Bytes of device workspace the chunked calls need for `desc`.
+ * op = 0: gdr_forward_chunked, op = 1: gdr_backward.  Returns 0 for an invalid
+ * descriptor (gdr_last_error() then says why).  Host function, no GPU access. */
+size_t gdr_workspace_size(const gdr_desc* desc, int op);
+
+/* Chunked forward over B sequences of T tokens.
+ *
+ * The sequence is cut into chunks of 64 tokens (the chunkwise recurrent form of
+ * the KDA blog, section 6.1: every chunk carries its own start state).  Inside a
+ * chunk the rank-1 updates are gathered into one triangular solve and dense
+ * matrix-core products (the "UT transform" the blog's section 6.2 names), with
+ * the cumulative decay kept in log space (section 7.1); the chunks are then
+ * chained by a sequential state pass.
+ *
+ *   S0        initial state, NULL = zeros.  ST final state, NULL = not written;
+ *             ST may alias S0.
+ *   o         [B,T,H,dv] in out_dtype; must not alias an input.
+ *   h_clvr    NULL = no CLVR; else updated in place (in_dtype).
+ *   clvr_scale NULL = lam == 1.
+ *   ws        device workspace of at least gdr_workspace_size(desc, 0) bytes;
+ *             its contents on entry do not matter.
+ */
+gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k,
+                               const void* v, const float* beta, const float* alpha,
+                               const float* S0, void* o, float* ST, void* h_clvr,
+                               const float* clvr_scale, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Gradients of gdr_forward_chunked (reverse mode, chunked, recomputing the
+ * forward's intermediates):
+ *   dO        [B,T,H,dv] in_dtype, upstream gradient of o.
+ *   dST       NULL = zero gradient on the final state.
+ *   dh_clvr   NULL = no CLVR term; else [B,T,H*dv] in_dtype, the gradient
+ *             arriving at the hidden stream after the CLVR add.
+ *   dq, dk    [B,T,H,dk], dv [B,T,H,dv] in out_dtype.
+ *   dbeta     [B,T,H] fp32.
+ *   dalpha    alpha's shape, fp32, derivative w.r.t. alpha itself; must be NULL
+ *             iff the gate is NONE.
+ *   dS0       [B,H,dk,dv] fp32, NULL = not written.
+ *   dclvr_scale [H*dv] fp32, NULL = not written (requires dh_clvr).
+ *   ws        at least gdr_workspace_size(desc, 1) bytes.
+ */
+gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* alpha, const float* S0,
+                        const void* dO, const float* dST, const void* dh_clvr,
+                        const float* clvr_scale, void* dq, void* dk, void* dv, float* dbeta,
+                        float* dalpha, float* dS0, float* dclvr_scale, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* One decode step for N independent sequences, state updated in place
+ * (inference with a fixed-size state, KDA blog section 6.1):
+ *   p = S^T (alpha*k), r = S^T (alpha*q), u = beta (v - p),
+ *   o = scale (r + u (k.q)),  S <- Diag(alpha) S + k u^T,
+ * which is exactly one step of the recurrence above.
+ *   q, k [N,H,dk] and v [N,H,dv] in in_dtype; beta [N,H] fp32;
+ *   alpha NULL (NONE), [N,H] (SCALAR) or [N,H,dk] (CHANNEL) fp32;
+ *   S [N,H,dk,dv] fp32 in/out; o [N,H,dv] in out_dtype (must not alias S).
+ * No workspace. */
+gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,
+                           int32_t in_dtype, int32_t out_dtype, float scale, const void* q,
+                           const void* k, const void* v, const float* beta,
+                           const float* alpha, float* S, void* o, void* stream);
+
+/* Static text for a status code. */
+const char* gdr_status_string(gdr_status status);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char* gdr_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t gdr_version(void);
+
+/* Per-kernel timing (a measurement aid, off by default).
+ * gdr_profile_begin() makes every later launch on this process record a HIP
+ * event pair on the launch stream around each kernel (at most 65536 launches;
+ * later ones are not recorded).  gdr_profile_end() waits for the recorded
+ * events, fills up to `max` entries of `out` with, per kernel name, the number
+ * of launches and their summed duration in milliseconds, returns the number of
+ * entries, and turns recording off.  Not thread-safe: profile from one thread.
+ * Returns -1 (gdr_last_error() says why) if the HIP runtime fails. */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+} gdr_kernel_time;
+
+int32_t gdr_profile_begin(void);
+int32_t gdr_profile_end(gdr_kernel_time* out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */
