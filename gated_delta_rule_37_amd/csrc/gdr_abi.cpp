@@ -106,6 +106,7 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* 
         w.Kb = take(mat);
         w.QtT = take(mat);
         w.WT = take(mat);
+        w.Nw = static_cast<float*>(take(size_t(nch) * kChunk * kChunk * 4));
         w.Ssnap = take(st);
         w.Usave = take(mat);
         w.dSsnap = take(st);

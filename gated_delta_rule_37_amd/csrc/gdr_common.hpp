@@ -98,6 +98,24 @@ __device__ __forceinline__ void mma(const Frag<float>& a, const Frag<float>& b, 
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
+// Fragment-order storage.  A matrix that a later kernel reads as MFMA A or B
+// operands is written so that every 64-lane fragment is one contiguous block
+// (lane l's eight k-consecutive elements at [frag][l][0..7]); a load
+// instruction then reads 64 x 16 contiguous bytes instead of 16-byte pieces of
+// 16 different rows.  frag_off gives the element offset of (r, k) in an
+// M x K operand; cfrag_off the offset of (r, n) in an M x N matrix stored in
+// accumulator order (lane l holding rows 4(l/16)..+3 of column l%16).
+template <int K>
+__host__ __device__ __forceinline__ int frag_off(int r, int k) {
+    const int rt = r >> 4, l16 = r & 15, kq = k >> 5, g = (k >> 3) & 3, e = k & 7;
+    return ((rt * (K / 32) + kq) * 64 + g * 16 + l16) * 8 + e;
+}
+template <int N>
+__host__ __device__ __forceinline__ int cfrag_off(int r, int n) {
+    const int rt = r >> 4, ct = n >> 4, lane = ((r & 15) >> 2) * 16 + (n & 15), e = r & 3;
+    return ((rt * (N / 16) + ct) * 64 + lane) * 4 + e;
+}
+
 __device__ __forceinline__ float4v zero4() {
     float4v z;
     z[0] = 0.f; z[1] = 0.f; z[2] = 0.f; z[3] = 0.f;

@@ -1,9 +1,9 @@
 // gdr_intra.hip -- intra-chunk transform of the chunked gated delta rule.
 //
-// One workgroup (4 waves) per (batch, head, chunk of 64 tokens).  With S the
-// chunk's start state, G_r the in-chunk inclusive sum of log2(alpha) (kept in
-// log space for range safety, KDA blog section 7.1) and
-//   Kt = K*2^G, Kh = K*2^-G, Qt = Q*2^G, Kb = K*2^(G_last - G)   (row-wise),
+// One workgroup per (batch, head, chunk of 64 tokens).  With S the chunk's start
+// state, G_r the in-chunk inclusive sum of log2(alpha) (kept in log space for
+// range safety, KDA blog section 7.1) and, row-wise,
+//   Kt = K*2^G, Kh = K*2^-G, Qt = Q*2^G, Kb = K*2^(G_last - G),
 // unrolling the token recurrence over the chunk gives
 //   U = T (V - Kt S),  T = (I + L)^-1 diag(beta),
 //   L = strict_tril(diag(beta) Kt Kh^T),
@@ -14,20 +14,30 @@
 // (the "UT transform" of the KDA blog, section 6.2) -- and writes, per chunk,
 //   W = T Kt, Ut = T V, Qt, Kb^T, A and gamma = 2^G_last
 // for the sequential state pass.  The optional CLVR epilogue (h += lam * v) is
-// fused here because this kernel already reads v.
+// fused here because this kernel already reads v.  Every operand of the state
+// pass is written in fragment order (see gdr_common.hpp) so that the
+// sequential kernel reads it with fully coalesced loads.  In backward mode it writes
+// instead the operands the reverse state pass and the gradient kernel need:
+// W, Ut, Kb^T, gamma, A^T, Kb, Qt^T, W^T and N = (I + L)^-1 in fp32.
+//
+// Thread layout: 4*D threads; thread (channel c, part p) owns rows 16p..16p+15
+// of channel c for the element-wise work, i.e. exactly the 16-row block p.
 //
 // Range handling for the channel gate (Kimi Delta Attention).  The pair factor
 // 2^(G_r - G_i) (r >= i) is <= 1, but Kt Kh^T written naively overflows for
-// strong gates.  The chunk is split into four 16-row blocks; block row R uses
-// the reference value ref(R) = G at the last row before the block, so that
-//   row operand   Kq_r = k_r 2^(G_r - ref(R))   <= 1
+// strong gates.  Block row R uses the reference value ref(R) = G at the last
+// row before block R, so that
+//   row operand    Kq_r = k_r 2^(G_r - ref(R))   <= 1
 //   column operand Kh_i = k_i 2^(ref(R) - G_i)  <= 1 for i before block R,
 // and only the 16x16 diagonal block has column factors >= 1 (bounded by the
 // block's own decay range rho).  When rho exceeds what the operand precision
 // can carry, that diagonal block is recomputed exactly on the vector ALUs from
-// running products of alpha (no exponentials, no overflow).  For the scalar
-// gate the factor does not depend on the channel, so K K^T and Q K^T are taken
-// on the raw inputs and the decay mask is applied afterwards in fp32.
+// running products of alpha (no exponentials, no overflow).  The exponentials
+// themselves are formed as 2^G and 2^-G once per element times per-channel
+// scalars when the chunk's total decay fits the fp32 exponent range, and pair
+// by pair otherwise.  For the scalar gate the factor does not depend on the
+// channel, so K K^T and Q K^T are taken on the raw inputs and the decay mask is
+// applied afterwards in fp32.
 #include "gdr_common.hpp"
 #include "gdr_launch.hpp"
 
@@ -42,8 +52,9 @@ struct IntraLayout {
     static constexpr int PAD = 16 / OPB;  // one 16-byte granule per row: conflict-free fragment reads
     static constexpr int LDR = D + PAD;   // row stride of [64][D] arrays
     static constexpr int LDC = CHUNK + PAD;  // row stride of [D][64] and [64][64] operand arrays
-    static constexpr int NPART = 256 / D;    // row parts of the element-wise phase
-    static constexpr int RPP = CHUNK / NPART;  // rows per part
+    static constexpr int NT = 4 * D;         // threads
+    static constexpr int NW = NT / WAVE;     // waves
+    static constexpr int RPP = 16;           // rows per thread (one 16-row block)
     // phase 1-2: Kq, Qq, Kh  (each [64][LDR])
     static constexpr int KQ = 0;
     static constexpr int QQ = KQ + CHUNK * LDR * OPB;
@@ -60,6 +71,8 @@ struct IntraLayout {
     static constexpr int BYTES = END12 > END34 ? END12 : END34;
     // operand-precision limit on the in-block decay range (log2 units)
     static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
+    // chunk decay beyond which 2^G or 2^-G leaves the fp32 range (log2 units)
+    static constexpr float WIDE_MAX = 120.f;
 };
 
 template <typename OpT, int N>
@@ -96,26 +109,31 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
     }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
 template <int D, int GATE, bool IN_F32, bool BWD>
-__global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC,
-                                                    const void* __restrict__ q_,
-                                                    const void* __restrict__ k_,
-                                                    const void* __restrict__ v_,
-                                                    const float* __restrict__ beta,
-                                                    const float* __restrict__ alpha,
-                                                    void* __restrict__ h_, const float* __restrict__ lam,
-                                                    ChunkWs ws) {
+__global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t NC,
+                                                      const void* __restrict__ q_,
+                                                      const void* __restrict__ k_,
+                                                      const void* __restrict__ v_,
+                                                      const float* __restrict__ beta,
+                                                      const float* __restrict__ alpha,
+                                                      void* __restrict__ h_, const float* __restrict__ lam,
+                                                      ChunkWs ws) {
     using L = IntraLayout<D, GATE, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
-    constexpr int NPART = L::NPART, RPP = L::RPP, LDR = L::LDR, LDC = L::LDC;
+    constexpr int NT = L::NT, NW = L::NW, RPP = L::RPP, LDR = L::LDR, LDC = L::LDC;
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-    __shared__ float s_tot[NPART][D];
-    __shared__ float s_blk[4][D];  // G at the last row of each 16-row block
+    __shared__ float s_tot[4][D];  // per-block sums of log2(alpha), then block-end values
     __shared__ float s_gs[CHUNK];  // scalar-gate G per row
     __shared__ float s_beta[CHUNK];
-    __shared__ float s_rho[4][4];
+    __shared__ float s_red[NW][2];
 
     OpT* Kq = reinterpret_cast<OpT*>(smem + L::KQ);
     OpT* Qq = reinterpret_cast<OpT*>(smem + L::QQ);
@@ -138,30 +156,43 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
     const InT* q = reinterpret_cast<const InT*>(q_);
     const InT* k = reinterpret_cast<const InT*>(k_);
     const InT* v = reinterpret_cast<const InT*>(v_);
+    InT* hh = reinterpret_cast<InT*>(h_);
     const int64_t tokstride = static_cast<int64_t>(H) * D;
     const int64_t base = ((b * T + t0) * H + h) * D;  // element (row 0, channel 0) of this chunk
     const int64_t nvalid64 = T - t0;
     const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
 
-    // ---------------- phase 1: load, gate cumsum, element-wise operands ----------------
+    // ---------------- phase 1: loads ----------------
+    // Every global load of the chunk is issued here, back to back.  Rows past the
+    // end of the sequence read the last valid row (always in bounds) and are
+    // zeroed afterwards, so the loads carry no branches.
     float G[RPP], kk[RPP], vv[RPP], qq[RPP];
+    InT hv[RPP];
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
         const int r = r0 + j;
-        const bool ok = r < nvalid;
-        const int64_t e = base + r * tokstride + cc;
-        kk[j] = ok ? to_f32(k[e]) : 0.f;
-        qq[j] = ok ? to_f32(q[e]) : 0.f;
-        vv[j] = ok ? to_f32(v[e]) : 0.f;
-        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(alpha[e]) : 0.f;
+        const int64_t e = base + (r < nvalid ? r : nvalid - 1) * tokstride + cc;
+        kk[j] = to_f32(k[e]);
+        qq[j] = to_f32(q[e]);
+        vv[j] = to_f32(v[e]);
+        if constexpr (GATE == GATE_CHANNEL) G[j] = alpha[e];
         else G[j] = 0.f;
+    }
+    if (hh) {
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = r0 + j;
+            hv[j] = hh[base + (r < nvalid ? r : nvalid - 1) * tokstride + cc];
+        }
     }
     if (tid < CHUNK) {
         const bool ok = tid < nvalid;
-        const int64_t tok = (b * T + t0 + tid) * H + h;
-        s_beta[tid] = ok ? beta[tok] : 0.f;
+        const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
+        const float bt = beta[tok];
+        s_beta[tid] = ok ? bt : 0.f;
         if constexpr (GATE == GATE_SCALAR) {
-            float g = ok ? log2_fast(alpha[tok]) : 0.f;
+            const float at = alpha[tok];
+            float g = ok ? log2_fast(at) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -170,116 +201,150 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
             s_gs[tid] = g;
         }
     }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const bool ok = r0 + j < nvalid;
+        kk[j] = ok ? kk[j] : 0.f;
+        qq[j] = ok ? qq[j] : 0.f;
+        vv[j] = ok ? vv[j] : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(G[j]) : 0.f;
+    }
     if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
     __syncthreads();
+
+    // ---------------- gate totals, block references, range flags ----------------
+    float carry = 0.f, glast = 0.f;  // G before this thread's block, G at the chunk end
     if constexpr (GATE == GATE_CHANNEL) {
-        float carry = 0.f;
-        for (int p = 0; p < part; ++p) carry += s_tot[p][cc];
+        float t[4];
 #pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            G[j] += carry;
-            if (((r0 + j) & 15) == 15) s_blk[(r0 + j) >> 4][cc] = G[j];
+        for (int p = 0; p < 4; ++p) t[p] = s_tot[p][cc];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            carry += (p < part) ? t[p] : 0.f;
+            glast += t[p];
         }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) G[j] += carry;
     } else if constexpr (GATE == GATE_SCALAR) {
 #pragma unroll
         for (int j = 0; j < RPP; ++j) G[j] = s_gs[r0 + j];
+        glast = s_gs[CHUNK - 1];
     }
-    __syncthreads();
-
-    float glast;
-    if constexpr (GATE == GATE_CHANNEL) glast = s_blk[3][cc];
-    else if constexpr (GATE == GATE_SCALAR) glast = s_gs[CHUNK - 1];
-    else glast = 0.f;
-
+    int flags = 0;      // bit R: diagonal block R needs the exact path
+    bool wide = false;  // 2^G or 2^-G would leave the fp32 range somewhere in the chunk
     if constexpr (GATE == GATE_CHANNEL) {
-        // decay range of each diagonal block, max over channels
-        if (tid < D) {
+        // each wave holds one block (part) for 64 channels
+        const float rho = wave_max(carry - G[RPP - 1]);
+        const float span = wave_max(-glast);
+        if (lane == 0) {
+            s_red[wid][0] = rho;
+            s_red[wid][1] = span;
+        }
+    }
+    __syncthreads();  // s_tot is reused below for the block-end values
+    if constexpr (GATE == GATE_CHANNEL) {
+        s_tot[part][cc] = G[RPP - 1];  // G at the last row of block `part`
+        constexpr int WPB = D / WAVE;  // waves per block
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                float rho = (R ? s_blk[R - 1][tid] : 0.f) - s_blk[R][tid];
+        for (int R = 0; R < 4; ++R) {
+            float rho = s_red[R * WPB][0], span = s_red[R * WPB][1];
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
-                if (lane == 0) s_rho[wid][R] = rho;
+            for (int w = 1; w < WPB; ++w) {
+                rho = fmaxf(rho, s_red[R * WPB + w][0]);
+                span = fmaxf(span, s_red[R * WPB + w][1]);
             }
+            if (!(rho <= L::RHO_MAX)) flags |= 1 << R;  // NaN-safe
+            if (!(span <= L::WIDE_MAX)) wide = true;
         }
     }
 
-    // element-wise outputs: Qt, Kb^T, gamma; row operands Kq, Qq
+    // ---------------- element-wise outputs ----------------
+    // Ei[j] = 2^-G (only on the narrow-range path); used again for Kh below
+    float E[RPP], Ei[RPP];
     {
         OpT* Qt_g = reinterpret_cast<OpT*>(ws.Qt) + ch * CHUNK * D;
         OpT* KbT_g = reinterpret_cast<OpT*>(ws.KbT) + ch * D * CHUNK;
         float kb[RPP];
+        const float egl = exp2_fast(glast);
+        const float eref = exp2_fast(-carry);
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = r0 + j;
-            const float e = exp2_fast(G[j]);
-            Qt_g[r * D + cc] = from_f32<OpT>(qq[j] * e);
-            kb[j] = kk[j] * exp2_fast(glast - G[j]);
+            float fq;  // 2^(G_r - ref(R)) for the row operands
+            if (!wide) {
+                E[j] = exp2_fast(G[j]);
+                Ei[j] = exp2_fast(-G[j]);
+                kb[j] = kk[j] * (Ei[j] * egl);
+                fq = E[j] * eref;
+            } else {
+                E[j] = exp2_fast(G[j]);
+                Ei[j] = 0.f;
+                kb[j] = kk[j] * exp2_fast(glast - G[j]);
+                fq = exp2_fast(G[j] - carry);
+            }
+            if constexpr (!BWD) Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
             if constexpr (GATE == GATE_CHANNEL) {
-                const int R = r >> 4;
-                const float ref = R ? s_blk[R - 1][cc] : 0.f;
-                const float f = exp2_fast(G[j] - ref);
-                Kq[r * LDR + cc] = from_f32<OpT>(kk[j] * f);
-                Qq[r * LDR + cc] = from_f32<OpT>(qq[j] * f);
+                Kq[r * LDR + cc] = from_f32<OpT>(kk[j] * fq);
+                Qq[r * LDR + cc] = from_f32<OpT>(qq[j] * fq);
             } else {
                 Kq[r * LDR + cc] = from_f32<OpT>(kk[j]);
                 Qq[r * LDR + cc] = from_f32<OpT>(qq[j]);
                 Kh[r * LDR + cc] = from_f32<OpT>(kk[j]);
             }
+            if constexpr (BWD) {
+                OpT* Kb_g = reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D;
+                Kb_g[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
+            }
         }
-        store_run<OpT, RPP>(KbT_g + cc * CHUNK + r0, kb);
-        if (part == NPART - 1) ws.gam[ch * D + cc] = exp2_fast(glast);
+        // Kb^T is the A operand of Kb^T U (rows d, k = position): two runs of 8
+        store_run<OpT, 8>(KbT_g + frag_off<CHUNK>(cc, r0), kb);
+        store_run<OpT, 8>(KbT_g + frag_off<CHUNK>(cc, r0 + 8), kb + 8);
+        if constexpr (BWD) {
+            float qt[RPP];
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) qt[j] = qq[j] * E[j];
+            OpT* QtT_g = reinterpret_cast<OpT*>(ws.QtT) + ch * D * CHUNK;
+            store_run<OpT, 8>(QtT_g + frag_off<CHUNK>(cc, r0), qt);
+            store_run<OpT, 8>(QtT_g + frag_off<CHUNK>(cc, r0 + 8), qt + 8);
+        }
+        if (tid < D) ws.gam[ch * D + cc] = egl;
     }
 
     // CLVR epilogue: the written value v is routed into the hidden stream
-    if (h_ != nullptr) {
-        InT* hh = reinterpret_cast<InT*>(h_);
+    if (hh) {
         const float lm = lam ? lam[h * D + cc] : 1.f;
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = r0 + j;
-            if (r < nvalid) {
-                const int64_t e = base + r * tokstride + cc;
-                hh[e] = from_f32<InT>(__builtin_fmaf(lm, vv[j], to_f32(hh[e])));
-            }
+            if (r < nvalid) hh[base + r * tokstride + cc] = from_f32<InT>(__builtin_fmaf(lm, vv[j], to_f32(hv[j])));
         }
     }
-
-    int flags = 0;  // bit R: diagonal block R needs the exact path
-    __syncthreads();
-    if constexpr (GATE == GATE_CHANNEL) {
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            float rho = s_rho[0][R];
-#pragma unroll
-            for (int w = 1; w < D / 64; ++w) rho = fmaxf(rho, s_rho[w][R]);
-            if (!(rho <= L::RHO_MAX)) flags |= 1 << R;  // NaN-safe
-        }
-    }
+    __syncthreads();  // Kq, Qq (and Kh for scalar gates), block-end values
 
     // ---------------- phase 2: P = Kt Kh^T and A = Qt Kh^T on the matrix cores ----------------
     // Tiles are computed transposed (Kh rows as the A operand), so lane l ends up
     // holding P[16R + l%16][16I + 4(l/16) .. +3]: four consecutive columns of one row.
     float* Ps = Nm;  // fp32 P staging, outside the phase 1-2 buffers
     OpT* A_g = reinterpret_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
+    OpT* AT_g = reinterpret_cast<OpT*>(ws.AT) + ch * CHUNK * CHUNK;
     constexpr int NPH = (GATE == GATE_CHANNEL) ? 4 : 1;
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph) {
         if constexpr (GATE == GATE_CHANNEL) {
             // column operand for block row R = ph: rows 0 .. 16R+15 with reference ref(R)
             const int R = ph;
+            if (part <= R) {
+                const float ref = R ? s_tot[R - 1][cc] : 0.f;
+                const float eref = exp2_fast(ref);
+                const bool zero = (part == R) && ((flags >> R) & 1);  // redone exactly below
 #pragma unroll
-            for (int j = 0; j < RPP; ++j) {
-                const int r = r0 + j;
-                if (r <= 16 * R + 15) {
-                    const float ref = R ? s_blk[R - 1][cc] : 0.f;
-                    float val = kk[j] * exp2_fast(ref - G[j]);
-                    if ((r >> 4) == R && ((flags >> R) & 1)) val = 0.f;  // diagonal block redone exactly below
-                    Kh[r * LDR + cc] = from_f32<OpT>(val);
+                for (int j = 0; j < RPP; ++j) {
+                    float val = wide ? kk[j] * exp2_fast(ref - G[j]) : kk[j] * (Ei[j] * eref);
+                    Kh[(r0 + j) * LDR + cc] = from_f32<OpT>(zero ? 0.f : val);
                 }
             }
             __syncthreads();
@@ -290,7 +355,7 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
         for (int R = Rlo; R <= Rhi; ++R) {
             for (int I = 0; I <= R; ++I) {
                 for (int isA = 0; isA < 2; ++isA, ++ti) {
-                    if ((ti & 3) != wid) continue;
+                    if ((ti % NW) != wid) continue;
                     if (GATE == GATE_CHANNEL && I == R && ((flags >> R) & 1)) continue;
                     float4v acc = zero4();
                     const OpT* arow = Kh + (16 * I + l16) * LDR + 8 * g4;
@@ -311,7 +376,11 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
                         acc[e] *= f;
                     }
                     if (isA) {
-                        store4<OpT>(A_g + r * CHUNK + 16 * I + 4 * g4, acc);
+                        if constexpr (!BWD) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
+                        if constexpr (BWD) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) AT_g[frag_off<CHUNK>(16 * I + 4 * g4 + e, r)] = from_f32<OpT>(acc[e]);
+                        }
                     } else {
                         *reinterpret_cast<float4v*>(Ps + r * CHUNK + 16 * I + 4 * g4) = acc;
                     }
@@ -321,12 +390,17 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
         if (GATE == GATE_CHANNEL && ph < NPH - 1) __syncthreads();  // Kh is rebuilt next phase
     }
     // zero the strictly upper tiles of A (never computed)
-    for (int e = tid; e < 6 * 64; e += 256) {
+    for (int e = tid; e < 6 * 64; e += NT) {
         const int tile = e / 64, w = e % 64;  // tile: (R, I) with I > R
         const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
         const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
         const int r = 16 * R + w / 4, i0 = 16 * I + 4 * (w % 4);
-        store4<OpT>(A_g + r * CHUNK + i0, zero4());
+        if constexpr (!BWD) {
+            store4<OpT>(A_g + frag_off<CHUNK>(r, i0), zero4());
+        } else {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) AT_g[frag_off<CHUNK>(i0 + e2, r)] = from_f32<OpT>(0.f);
+        }
     }
     __syncthreads();  // all reads of Kq/Qq/Kh done: the region is reused below
 
@@ -334,84 +408,87 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
     {
         float kt[RPP];
 #pragma unroll
-        for (int j = 0; j < RPP; ++j) kt[j] = kk[j] * exp2_fast(G[j]);
+        for (int j = 0; j < RPP; ++j) kt[j] = kk[j] * E[j];
         store_run<OpT, RPP>(KtT + cc * LDC + r0, kt);
         store_run<OpT, RPP>(VT + cc * LDC + r0, vv);
     }
-    __syncthreads();
 
     // exact diagonal blocks for the channel gate when the decay range is too wide:
     // 2^(G_r - G_i) = prod_{s=i+1..r} alpha_s, accumulated as a running product
     if constexpr (GATE == GATE_CHANNEL) {
-        constexpr int CPG = D / 16;  // channels per group
-        const int rr = tid >> 4, cg = tid & 15;
+        if (flags && tid < 256) {
+            constexpr int CPG = D / 16;  // channels per group
+            const int rr = tid >> 4, cg = tid & 15;
 #pragma unroll 1
-        for (int R = 0; R < 4; ++R) {
-            if (!((flags >> R) & 1)) continue;
-            const int r = 16 * R + rr;
-            const bool okr = r < nvalid;
-            float kr[CPG], qr[CPG], f[CPG];
+            for (int R = 0; R < 4; ++R) {
+                if (!((flags >> R) & 1)) continue;
+                const int r = 16 * R + rr;
+                const bool okr = r < nvalid;
+                float kr[CPG], qr[CPG], f[CPG];
 #pragma unroll
-            for (int m = 0; m < CPG; ++m) {
-                const int64_t e = base + r * tokstride + cg * CPG + m;
-                kr[m] = okr ? to_f32(k[e]) : 0.f;
-                qr[m] = okr ? to_f32(q[e]) : 0.f;
-                f[m] = 1.f;
-            }
+                for (int m = 0; m < CPG; ++m) {
+                    const int64_t e = base + r * tokstride + cg * CPG + m;
+                    kr[m] = okr ? to_f32(k[e]) : 0.f;
+                    qr[m] = okr ? to_f32(q[e]) : 0.f;
+                    f[m] = 1.f;
+                }
 #pragma unroll 1
-            for (int i = 15; i >= 0; --i) {
-                const int ii = 16 * R + i;
-                float ps = 0.f, as = 0.f;
-                if (ii <= r) {
-                    if (ii < r) {  // include alpha_{ii+1}
-                        const int s = ii + 1;
-                        const bool oks = s < nvalid;
+                for (int i = 15; i >= 0; --i) {
+                    const int ii = 16 * R + i;
+                    float ps = 0.f, as = 0.f;
+                    if (ii <= r) {
+                        if (ii < r) {  // include alpha_{ii+1}
+                            const int s = ii + 1;
+                            const bool oks = s < nvalid;
 #pragma unroll
-                        for (int m = 0; m < CPG; ++m)
-                            f[m] *= oks ? alpha[base + s * tokstride + cg * CPG + m] : 1.f;
+                            for (int m = 0; m < CPG; ++m)
+                                f[m] *= oks ? alpha[base + s * tokstride + cg * CPG + m] : 1.f;
+                        }
+                        const bool oki = ii < nvalid;
+#pragma unroll
+                        for (int m = 0; m < CPG; ++m) {
+                            const float ki = oki ? to_f32(k[base + ii * tokstride + cg * CPG + m]) : 0.f;
+                            ps += kr[m] * ki * f[m];
+                            as += qr[m] * ki * f[m];
+                        }
                     }
-                    const bool oki = ii < nvalid;
 #pragma unroll
-                    for (int m = 0; m < CPG; ++m) {
-                        const float ki = oki ? to_f32(k[base + ii * tokstride + cg * CPG + m]) : 0.f;
-                        ps += kr[m] * ki * f[m];
-                        as += qr[m] * ki * f[m];
+                    for (int off = 1; off < 16; off <<= 1) {
+                        ps += __shfl_xor(ps, off);
+                        as += __shfl_xor(as, off);
                     }
-                }
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) {
-                    ps += __shfl_xor(ps, off);
-                    as += __shfl_xor(as, off);
-                }
-                if (cg == 0) {
-                    Ps[r * CHUNK + ii] = ps;
-                    A_g[r * CHUNK + ii] = from_f32<OpT>(as);
+                    if (cg == 0) {
+                        Ps[r * CHUNK + ii] = ps;
+                        if constexpr (!BWD) A_g[frag_off<CHUNK>(r, ii)] = from_f32<OpT>(as);
+                        if constexpr (BWD) AT_g[frag_off<CHUNK>(ii, r)] = from_f32<OpT>(as);
+                    }
                 }
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---------------- phase 3: T = (I + L)^-1 diag(beta), L = strict_tril(diag(beta) P) ----------------
-    for (int e = tid; e < CHUNK * CHUNK; e += 256) {
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, i = e % CHUNK;
         Pm[e] = (i < r) ? s_beta[r] * Ps[e] : 0.f;  // Ps aliases Nm: read before the zero
         Nm[e] = 0.f;
     }
     __syncthreads();
-    // diagonal 16x16 blocks by forward substitution, one wave per block, lane = column
-    if (lane < 16) {
+    // diagonal 16x16 blocks, one wave per block, lane j solves column j of
+    // (I + L_RR) x = e_j column by column: once x_m is final it is applied to
+    // every later row, so the 15 updates of each step are independent
+    if (wid < 4 && lane < 16) {
         const int R = wid;
         const float* Lb = Pm + (16 * R) * CHUNK + 16 * R;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float s = 0.f;
+        for (int m = 0; m < 15; ++m) {
+            const float xm = x[m];
 #pragma unroll
-            for (int m = 0; m < r; ++m) s += Lb[r * CHUNK + m] * x[m];
-            if (r > lane) x[r] = -s;
+            for (int r = m + 1; r < 16; ++r) x[r] -= Lb[r * CHUNK + m] * xm;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) Nm[(16 * R + r) * CHUNK + 16 * R + lane] = x[r];
@@ -419,41 +496,71 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
     __syncthreads();
     // off-diagonal blocks: N[R, <R] = -N_RR (L[R, <R] N[<R, <R])
     {
-        const int r = tid >> 4, i0 = tid & 15;
+        constexpr int RSTEP = NT / 32;            // rows of block R handled per pass
+        constexpr int RPT = 16 / RSTEP;           // rows per thread (1 or 2)
+        const int r0t = tid >> 5, cl = tid & 31;  // first row in block R, column lane
         float* X = Pm;  // rows 0..15 of L are no longer needed
 #pragma unroll
         for (int R = 1; R < 4; ++R) {
-            float xs[3];
+            float xs[RPT][2];
 #pragma unroll
-            for (int m = 0; m < R; ++m) {
-                const int ii = 16 * m + i0;
-                float s = 0.f;
-                const float* Lr = Pm + (16 * R + r) * CHUNK;
-                for (int j = 16 * m; j < 16 * R; ++j) s += Lr[j] * Nm[j * CHUNK + ii];
-                xs[m] = s;
+            for (int a = 0; a < RPT; ++a) {
+                const int r = r0t + a * RSTEP;
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int col = cl + 32 * mm;
+                    float s = 0.f;
+                    if (col < 16 * R) {
+                        const float* Lr = Pm + (16 * R + r) * CHUNK;
+                        for (int j = 16 * (col >> 4); j < 16 * R; ++j) s += Lr[j] * Nm[j * CHUNK + col];
+                    }
+                    xs[a][mm] = s;
+                }
             }
             __syncthreads();
 #pragma unroll
-            for (int m = 0; m < R; ++m) X[r * CHUNK + 16 * m + i0] = xs[m];
+            for (int a = 0; a < RPT; ++a) {
+                const int r = r0t + a * RSTEP;
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int col = cl + 32 * mm;
+                    if (col < 16 * R) X[r * CHUNK + col] = xs[a][mm];
+                }
+            }
             __syncthreads();
 #pragma unroll
-            for (int m = 0; m < R; ++m) {
-                const int ii = 16 * m + i0;
-                float s = 0.f;
-                const float* Nr = Nm + (16 * R + r) * CHUNK + 16 * R;
+            for (int a = 0; a < RPT; ++a) {
+                const int r = r0t + a * RSTEP;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s += Nr[j] * X[j * CHUNK + ii];
-                xs[m] = -s;
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int col = cl + 32 * mm;
+                    if (col < 16 * R) {
+                        float s = 0.f;
+                        const float* Nr = Nm + (16 * R + r) * CHUNK + 16 * R;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) s += Nr[j] * X[j * CHUNK + col];
+                        xs[a][mm] = -s;
+                    }
+                }
             }
 #pragma unroll
-            for (int m = 0; m < R; ++m) Nm[(16 * R + r) * CHUNK + 16 * m + i0] = xs[m];
+            for (int a = 0; a < RPT; ++a) {
+                const int r = r0t + a * RSTEP;
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int col = cl + 32 * mm;
+                    if (col < 16 * R) Nm[(16 * R + r) * CHUNK + col] = xs[a][mm];
+                }
+            }
             __syncthreads();
         }
     }
     // T = N diag(beta) in operand precision (row-major, padded), in the L region
-    for (int e = tid; e < CHUNK * CHUNK; e += 256) {
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, i = e % CHUNK;
-        Tm[r * LDC + i] = from_f32<OpT>(Nm[e] * s_beta[i]);
+        const float n = Nm[e];
+        Tm[r * LDC + i] = from_f32<OpT>(n * s_beta[i]);
+        if constexpr (BWD) ws.Nw[ch * CHUNK * CHUNK + e] = n;
     }
     __syncthreads();
 
@@ -461,14 +568,14 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
     {
         OpT* W_g = reinterpret_cast<OpT*>(ws.W) + ch * CHUNK * D;
         OpT* U_g = reinterpret_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
-        for (int m = wid; m < D / 16; m += 4) {
+        OpT* WT_g = reinterpret_cast<OpT*>(ws.WT) + ch * D * CHUNK;
+        for (int m = wid; m < D / 16; m += NW) {
 #pragma unroll
             for (int mat = 0; mat < 2; ++mat) {
                 const OpT* arow = (mat ? VT : KtT) + (16 * m + l16) * LDC + 8 * g4;
                 Frag<OpT> fa0, fa1;
                 fa0.load(arow);
                 fa1.load(arow + 32);
-                OpT* dst = mat ? U_g : W_g;
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
                     float4v acc = zero4();
@@ -480,35 +587,48 @@ __global__ __launch_bounds__(256) void intra_kernel(int64_t T, int H, int64_t NC
                         fb.load(brow + 32);
                         mma(fa1, fb, acc);
                     }
-                    store4<OpT>(dst + (16 * n + l16) * D + 16 * m + 4 * g4, acc);
+                    const int pos = 16 * n + l16, d0 = 16 * m + 4 * g4;
+                    if (mat == 0) {
+                        store4<OpT>(W_g + frag_off<D>(pos, d0), acc);  // A operand of W S
+                        if constexpr (BWD) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) WT_g[frag_off<CHUNK>(d0 + e, pos)] = from_f32<OpT>(acc[e]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) U_g[cfrag_off<D>(pos, d0 + e)] = from_f32<OpT>(acc[e]);
+                    }
                 }
             }
         }
     }
-    (void)BWD;
 }
 
 template <int D, int GATE, bool IN_F32>
-static hipError_t launch_intra_t(int64_t B, int64_t T, int H, int64_t NC, const void* q,
+static hipError_t launch_intra_t(bool bwd, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                                  const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
                                  const ChunkWs& ws, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, false>), dim3((unsigned)nblk), dim3(256), 0,
-                       stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+    if (bwd)
+        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+    else
+        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
     return hipGetLastError();
 }
 
 template <int D, bool IN_F32>
-static hipError_t launch_intra_d(int gate, int64_t B, int64_t T, int H, int64_t NC,
+static hipError_t launch_intra_d(int gate, bool bwd, int64_t B, int64_t T, int H, int64_t NC,
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
                                  const ChunkWs& ws, hipStream_t stream) {
     switch (gate) {
-        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
     }
 }
 
@@ -516,13 +636,12 @@ hipError_t launch_intra(int D, int gate, bool in_f32, bool backward, int64_t B, 
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
                         const ChunkWs& ws, hipStream_t stream) {
-    (void)backward;
     if (D == 64) {
-        if (in_f32) return launch_intra_d<64, true>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        return launch_intra_d<64, false>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        if (in_f32) return launch_intra_d<64, true>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        return launch_intra_d<64, false>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
     }
-    if (in_f32) return launch_intra_d<128, true>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-    return launch_intra_d<128, false>(gate, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    if (in_f32) return launch_intra_d<128, true>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    return launch_intra_d<128, false>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
 }
 
 }  // namespace gdr

@@ -14,13 +14,14 @@ namespace gdr {
 //   W   [64][D]   Ut  [64][D]   Qt  [64][D]   KbT [D][64]   A [64][64]
 //   gam [D] fp32 (per-channel decay over the whole chunk)
 // and, for the backward only,
-//   AT  [64][64]  Kb [64][D]  QtT [D][64]  WT [D][64]
+//   AT  [64][64]  Kb [64][D]  QtT [D][64]  WT [D][64]  Nw [64][64] fp32
 //   Ssnap [D][D] chunk-start state, Usave [64][D] (op elements)
 //   dSsnap [D][D] chunk-end state gradient, dUsave [64][D]
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;
     float* gam;
     void *AT, *Kb, *QtT, *WT;
+    float* Nw;  // N = (I + L)^-1, [64][64] fp32 (backward)
     void *Ssnap, *Usave, *dSsnap, *dUsave;
 };
 

@@ -34,43 +34,47 @@ struct StateCfg {
     static constexpr int SRT = D / 64;         // 16-row state tiles per wave
 };
 
+// Operand fragments of one chunk, held in registers exactly as loaded (no
+// conversion at load time, so issuing a prefetch never waits for it).
 template <int D, bool IN_F32>
 struct ChunkFrags {
     using OpT = typename StateCfg<D, IN_F32>::OpT;
     static constexpr int SRT = StateCfg<D, IN_F32>::SRT;
     Frag<OpT> w[D / 32], q[D / 32], a[2], kb[SRT][2];
-    float ut[4];
+    OpT ut[4];
     float gam[SRT][4];
 };
 
+// All chunk operands are stored in fragment order by the intra-chunk kernel:
+// every fragment below is one contiguous, fully coalesced 1 KiB (fp16) load.
 template <int D, bool IN_F32>
 __device__ __forceinline__ void load_chunk(ChunkFrags<D, IN_F32>& f, const ChunkWs& ws, int64_t ch,
-                                           int j0, int wid, int l16, int g4) {
+                                           int j0, int wid, int lane) {
     using Cfg = StateCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
-    const OpT* W = reinterpret_cast<const OpT*>(ws.W) + ch * CHUNK * D + (16 * wid + l16) * D + 8 * g4;
-    const OpT* Q = reinterpret_cast<const OpT*>(ws.Qt) + ch * CHUNK * D + (16 * wid + l16) * D + 8 * g4;
+    const OpT* W = reinterpret_cast<const OpT*>(ws.W) + ch * CHUNK * D + (wid * (D / 32) * 64 + lane) * 8;
+    const OpT* Q = reinterpret_cast<const OpT*>(ws.Qt) + ch * CHUNK * D + (wid * (D / 32) * 64 + lane) * 8;
 #pragma unroll
     for (int kq = 0; kq < D / 32; ++kq) {
-        f.w[kq].load(W + 32 * kq);
-        f.q[kq].load(Q + 32 * kq);
+        f.w[kq].load(W + kq * 64 * 8);
+        f.q[kq].load(Q + kq * 64 * 8);
     }
-    const OpT* A = reinterpret_cast<const OpT*>(ws.A) + ch * CHUNK * CHUNK + (16 * wid + l16) * CHUNK + 8 * g4;
+    const OpT* A = reinterpret_cast<const OpT*>(ws.A) + ch * CHUNK * CHUNK + (wid * 2 * 64 + lane) * 8;
     f.a[0].load(A);
-    if (wid >= 2) f.a[1].load(A + 32);
-    else f.a[1].zero();
+    f.a[1].load(A + 64 * 8);  // zero for waves 0 and 1 (A is lower triangular)
     const OpT* KbT = reinterpret_cast<const OpT*>(ws.KbT) + ch * D * CHUNK;
 #pragma unroll
     for (int m = 0; m < Cfg::SRT; ++m) {
-        const OpT* row = KbT + (wid * (D / 4) + 16 * m + l16) * CHUNK + 8 * g4;
-        f.kb[m][0].load(row);
-        f.kb[m][1].load(row + 32);
+        const int rt = wid * (D / 64) + m;  // 16-row tile of the state
+        f.kb[m][0].load(KbT + ((rt * 2 + 0) * 64 + lane) * 8);
+        f.kb[m][1].load(KbT + ((rt * 2 + 1) * 64 + lane) * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f.gam[m][e] = ws.gam[ch * D + wid * (D / 4) + 16 * m + 4 * g4 + e];
+        for (int e = 0; e < 4; ++e) f.gam[m][e] = ws.gam[ch * D + 16 * rt + 4 * (lane >> 4) + e];
     }
-    const OpT* Ut = reinterpret_cast<const OpT*>(ws.Ut) + ch * CHUNK * D + j0 + l16;
+    // Ut in accumulator order: this lane's four rows of its column
+    const OpT* Ut = reinterpret_cast<const OpT*>(ws.Ut) + ch * CHUNK * D + ((wid * (D / 16) + j0 / 16) * 64 + lane) * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f.ut[e] = to_f32(Ut[(16 * wid + 4 * g4 + e) * D]);
+    for (int e = 0; e < 4; ++e) f.ut[e] = Ut[e];
 }
 
 template <typename OpT>
@@ -85,8 +89,131 @@ __device__ __forceinline__ void st4(OpT* dst, const float4v& v) {
     }
 }
 
-template <int D, bool IN_F32, bool OUT_F32, bool SAVE>
-__global__ __launch_bounds__(256) void state_fwd_kernel(int64_t T, int H, int64_t NC, float scale,
+template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O>
+__device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int64_t c, int64_t T, int H,
+                                           int64_t b, int h, int64_t bh, int64_t NC, int j0, int wid,
+                                           int l16, int g4, float scale, const ChunkWs& ws,
+                                           float4v (&S)[StateCfg<D, IN_F32>::SRT],
+                                           typename StateCfg<D, IN_F32>::OpT* s_S,
+                                           typename StateCfg<D, IN_F32>::OpT* s_U,
+                                           typename InType<OUT_F32>::T* o) {
+    using Cfg = StateCfg<D, IN_F32>;
+    using OpT = typename Cfg::OpT;
+    using OutT = typename InType<OUT_F32>::T;
+    constexpr int SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
+    const int64_t ch = bh * NC + c;
+
+    if constexpr (SAVE) {
+        // chunk-start state snapshot [D][D] in operand precision
+        OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D;
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) snap[(d0 + e) * D + j0 + l16] = from_f32<OpT>(S[m][e]);
+        }
+    }
+
+    // U = Ut - W S and the inter-chunk part of the output, O = Qt S
+    float4v u = zero4(), oacc = zero4();
+#pragma unroll
+    for (int kq = 0; kq < D / 32; ++kq) {
+        Frag<OpT> fs;
+        fs.load(s_S + l16 * LDS_S + 32 * kq + 8 * g4);
+        mma(cur.w[kq], fs, u);
+        if constexpr (HAS_O) mma(cur.q[kq], fs, oacc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = to_f32(cur.ut[e]) - u[e];
+    st4<OpT>(s_U + l16 * LDS_U + 16 * wid + 4 * g4, u);
+    if constexpr (SAVE) {
+        OpT* us = reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + j0 + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) us[(16 * wid + 4 * g4 + e) * D] = from_f32<OpT>(u[e]);
+    }
+    __syncthreads();
+
+    Frag<OpT> fu0, fu1;
+    fu0.load(s_U + l16 * LDS_U + 8 * g4);
+    fu1.load(s_U + l16 * LDS_U + 32 + 8 * g4);
+    // intra-chunk part of the output, O += A U
+    if constexpr (HAS_O) {
+        mma(cur.a[0], fu0, oacc);
+        if (wid >= 2) mma(cur.a[1], fu1, oacc);
+        const int64_t tbase = c * CHUNK + 16 * wid + 4 * g4;
+        OutT* op = o + ((b * T + tbase) * H + h) * D + j0 + l16;
+        const int64_t tstride = static_cast<int64_t>(H) * D;
+        if (tbase + 3 < T) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) op[e * tstride] = from_f32<OutT>(scale * oacc[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (tbase + e < T) op[e * tstride] = from_f32<OutT>(scale * oacc[e]);
+        }
+    }
+
+    // S <- Diag(gamma) S + Kb^T U
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[m][e] *= cur.gam[m][e];
+        mma(cur.kb[m][0], fu0, S[m]);
+        mma(cur.kb[m][1], fu1, S[m]);
+        st4<OpT>(s_S + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, S[m]);
+    }
+    __syncthreads();
+}
+
+// L2 warm-up for a chunk-head's operands: the eight workgroups of one head
+// (one per dv slice, all on one XCD) each touch their 1/NSL share of every
+// per-chunk array with one dword per 128-byte line.  Returns the loaded dwords
+// XOR-ed together; the caller keeps the value alive so the loads are issued.
+template <int D, bool IN_F32>
+struct L2Touch {
+    using OpT = typename StateCfg<D, IN_F32>::OpT;
+    static constexpr int NSL = StateCfg<D, IN_F32>::NSL;
+    static constexpr int LINE = 128;
+    static constexpr int QL = CHUNK * D * (int)sizeof(OpT) / NSL / LINE;      // lines per slice, [64][D]
+    static constexpr int AL = CHUNK * CHUNK * (int)sizeof(OpT) / NSL / LINE;  // lines per slice, A
+    static constexpr int GL = (D * 4 + LINE - 1) / LINE;                      // gamma lines (slice 0)
+    static constexpr int NL = 4 * QL + AL + GL;
+    static constexpr int NPF = (NL + WAVE - 1) / WAVE;  // loads per lane per chunk
+};
+
+template <int D, bool IN_F32, int NPF>
+__device__ __forceinline__ void touch_chunk(uint32_t (&out)[NPF], const ChunkWs& ws, int64_t ch, int slice,
+                                            int lane) {
+    using P = L2Touch<D, IN_F32>;
+    using OpT = typename P::OpT;
+    const size_t mat = size_t(CHUNK) * D * sizeof(OpT);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+        const int L = lane + WAVE * i;
+        const char* addr;
+        const int reg = L / P::QL;
+        if (L < 4 * P::QL) {
+            const char* base = reg == 0   ? static_cast<const char*>(ws.W)
+                               : reg == 1 ? static_cast<const char*>(ws.Qt)
+                               : reg == 2 ? static_cast<const char*>(ws.KbT)
+                                          : static_cast<const char*>(ws.Ut);
+            addr = base + ch * mat + size_t(slice * P::QL + L % P::QL) * P::LINE;
+        } else if (L < 4 * P::QL + P::AL) {
+            addr = static_cast<const char*>(ws.A) + ch * size_t(CHUNK) * CHUNK * sizeof(OpT) +
+                   size_t(slice * P::AL + (L - 4 * P::QL)) * P::LINE;
+        } else {
+            // gamma: slice 0 only; other slices re-touch their first W line
+            const int gl = L - 4 * P::QL - P::AL;
+            addr = (slice == 0 && gl < P::GL)
+                       ? reinterpret_cast<const char*>(ws.gam + ch * D) + size_t(gl) * P::LINE
+                       : static_cast<const char*>(ws.W) + ch * mat + size_t(slice * P::QL) * P::LINE;
+        }
+        out[i] = *reinterpret_cast<const uint32_t*>(addr);
+    }
+}
+
+template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O>
+__global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_t NC, float scale,
                                                         ChunkWs ws, const float* S0,
                                                         float* ST, void* __restrict__ o_) {
     // S0 and ST may alias: each workgroup reads its slice of S0 before it
@@ -109,7 +236,38 @@ __global__ __launch_bounds__(256) void state_fwd_kernel(int64_t T, int H, int64_
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    OutT* o = reinterpret_cast<OutT*>(o_);
+    OutT* o = reinterpret_cast<OutT*>(o_);  // NULL: state pass only (backward recompute)
+
+    // Waves 0-3 run the state pass.  Wave 4 only warms the L2 with the operands
+    // of chunk c + PF while chunk c computes; it takes part in every barrier.
+    if (wid == 4) {
+        constexpr int PF = 8;
+        constexpr int NPF = L2Touch<D, IN_F32>::NPF;
+        const int slice = j0 / Cfg::NS;
+        uint32_t ring[PF][NPF];
+        uint32_t acc = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < PF; ++s2)
+            touch_chunk<D, IN_F32, NPF>(ring[s2], ws, bh * NC + (s2 < NC ? s2 : 0), slice, lane);
+        __syncthreads();
+#pragma unroll 1
+        for (int64_t c0 = 0; c0 < NC; c0 += PF) {
+#pragma unroll
+            for (int s2 = 0; s2 < PF; ++s2) {
+                const int64_t c = c0 + s2;
+                if (c < NC) {
+#pragma unroll
+                    for (int i = 0; i < NPF; ++i) acc ^= ring[s2][i];  // chunk c is in L2 by now
+                    // unconditional (clamped) so every slot is refilled: no register copies
+                    touch_chunk<D, IN_F32, NPF>(ring[s2], ws, bh * NC + (c + PF < NC ? c + PF : NC - 1), slice, lane);
+                    __syncthreads();
+                    __syncthreads();
+                }
+            }
+        }
+        asm volatile("" ::"v"(acc));
+        return;
+    }
 
     // state tile m of this wave: rows wid*D/4 + 16m + 4*g4 + e, column j0 + l16
     float4v S[SRT];
@@ -123,77 +281,23 @@ __global__ __launch_bounds__(256) void state_fwd_kernel(int64_t T, int H, int64_
     }
     __syncthreads();
 
-    ChunkFrags<D, IN_F32> cur, nxt;
-    if (NC > 0) load_chunk<D, IN_F32>(cur, ws, bh * NC, j0, wid, l16, g4);
-
+    // Chunks are processed in pairs with two register sets used alternately,
+    // so the prefetch of chunk c+1 never has to be copied into place.
+    // The prefetch is unconditional (the chunk index is clamped to the last
+    // chunk) so that the compiler can count outstanding loads exactly and wait
+    // only for the chunk about to be used.
+    ChunkFrags<D, IN_F32> fa, fb;
+    const int64_t last = NC - 1;
+    if (NC > 0) load_chunk<D, IN_F32>(fa, ws, bh * NC, j0, wid, lane);
 #pragma unroll 1
-    for (int64_t c = 0; c < NC; ++c) {
-        const int64_t ch = bh * NC + c;
-        if (c + 1 < NC) load_chunk<D, IN_F32>(nxt, ws, ch + 1, j0, wid, l16, g4);
-
-        if constexpr (SAVE) {
-            // chunk-start state snapshot [D][D] in operand precision
-            OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D;
-#pragma unroll
-            for (int m = 0; m < SRT; ++m) {
-                const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) snap[(d0 + e) * D + j0 + l16] = from_f32<OpT>(S[m][e]);
-            }
-        }
-
-        // U = Ut - W S and the inter-chunk part of the output, O = Qt S
-        float4v u = zero4(), oacc = zero4();
-#pragma unroll
-        for (int kq = 0; kq < D / 32; ++kq) {
-            Frag<OpT> fs;
-            fs.load(s_S + l16 * LDS_S + 32 * kq + 8 * g4);
-            mma(cur.w[kq], fs, u);
-            mma(cur.q[kq], fs, oacc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = cur.ut[e] - u[e];
-        st4<OpT>(s_U + l16 * LDS_U + 16 * wid + 4 * g4, u);
-        if constexpr (SAVE) {
-            OpT* us = reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + j0 + l16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) us[(16 * wid + 4 * g4 + e) * D] = from_f32<OpT>(u[e]);
-        }
-        __syncthreads();
-
-        // intra-chunk part of the output, O += A U
-        {
-            Frag<OpT> fu;
-            fu.load(s_U + l16 * LDS_U + 8 * g4);
-            mma(cur.a[0], fu, oacc);
-            if (wid >= 2) {
-                fu.load(s_U + l16 * LDS_U + 32 + 8 * g4);
-                mma(cur.a[1], fu, oacc);
-            }
-            const int64_t tbase = c * CHUNK + 16 * wid + 4 * g4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t t = tbase + e;
-                if (t < T) o[((b * T + t) * H + h) * D + j0 + l16] = from_f32<OutT>(scale * oacc[e]);
-            }
-        }
-
-        // S <- Diag(gamma) S + Kb^T U
-        {
-            Frag<OpT> fu0, fu1;
-            fu0.load(s_U + l16 * LDS_U + 8 * g4);
-            fu1.load(s_U + l16 * LDS_U + 32 + 8 * g4);
-#pragma unroll
-            for (int m = 0; m < SRT; ++m) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) S[m][e] *= cur.gam[m][e];
-                mma(cur.kb[m][0], fu0, S[m]);
-                mma(cur.kb[m][1], fu1, S[m]);
-                st4<OpT>(s_S + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, S[m]);
-            }
-        }
-        __syncthreads();
-        cur = nxt;
+    for (int64_t c = 0; c < NC; c += 2) {
+        load_chunk<D, IN_F32>(fb, ws, bh * NC + (c + 1 < NC ? c + 1 : last), j0, wid, lane);
+        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O>(fa, c, T, H, b, h, bh, NC, j0, wid, l16, g4, scale, ws,
+                                                    S, s_S, s_U, o);
+        if (c + 1 >= NC) break;
+        load_chunk<D, IN_F32>(fa, ws, bh * NC + (c + 2 < NC ? c + 2 : last), j0, wid, lane);
+        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O>(fb, c + 1, T, H, b, h, bh, NC, j0, wid, l16, g4, scale,
+                                                    ws, S, s_S, s_U, o);
     }
 
     if (ST) {
@@ -212,12 +316,15 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
                                  hipStream_t stream) {
     const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    if (save)
-        hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(256), 0,
-                           stream, T, H, NC, scale, ws, S0, ST, o);
+    if (save && o)
+        hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true, true>), dim3((unsigned)nblk), dim3(320),
+                           0, stream, T, H, NC, scale, ws, S0, ST, o);
+    else if (save)
+        hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true, false>), dim3((unsigned)nblk), dim3(320),
+                           0, stream, T, H, NC, scale, ws, S0, ST, o);
     else
-        hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(256), 0,
-                           stream, T, H, NC, scale, ws, S0, ST, o);
+        hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false, true>), dim3((unsigned)nblk), dim3(320),
+                           0, stream, T, H, NC, scale, ws, S0, ST, o);
     return hipGetLastError();
 }
 
