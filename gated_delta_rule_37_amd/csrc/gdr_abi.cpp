@@ -76,6 +76,15 @@ gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
     return GDR_OK;
 }
 
+// CLVR scale gradient: token segments reduced in two passes
+int64_t dlam_segments(const gdr_desc* d) {
+    const int64_t bt = d->B * d->T;
+    return bt < 1 ? 1 : (bt < 256 ? bt : 256);
+}
+size_t dlam_partial_bytes(const gdr_desc* d) {
+    return size_t(dlam_segments(d)) * size_t(d->H) * size_t(d->dv) * 4;
+}
+
 }  // namespace
 
 namespace gdr {
@@ -102,15 +111,25 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* 
     w.A = take(sq);
     w.gam = static_cast<float*>(take(size_t(nch) * D * 4));
     if (backward) {
+        const size_t sq32 = size_t(nch) * kChunk * kChunk * 4;
+        const size_t mat32 = size_t(nch) * kChunk * D * 4;
         w.AT = take(sq);
         w.Kb = take(mat);
         w.QtT = take(mat);
         w.WT = take(mat);
-        w.Nw = static_cast<float*>(take(size_t(nch) * kChunk * kChunk * 4));
+        w.Nw = static_cast<float*>(take(sq32));
+        w.Pw = static_cast<float*>(take(sq32));
         w.Ssnap = take(st);
         w.Usave = take(mat);
         w.dSsnap = take(st);
         w.dUsave = take(mat);
+        w.dUsaveT = take(mat);
+        w.gQt = static_cast<float*>(take(mat32));
+        w.gKt = static_cast<float*>(take(mat32));
+        w.gKb = static_cast<float*>(take(mat32));
+        w.gA = static_cast<float*>(take(sq32));
+        w.gP = static_cast<float*>(take(sq32));
+        w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
     }
     if (out) *out = w;
     return off;
@@ -144,7 +163,9 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     }
     const int64_t nch = desc->B * desc->H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
-    return gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, nullptr, nullptr);
+    size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, nullptr, nullptr);
+    if (op == 1) n += align_up(dlam_partial_bytes(desc));
+    return n;
 }
 
 gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
@@ -222,10 +243,85 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
     int64_t NC = 0;
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
-    (void)q; (void)k; (void)v; (void)beta; (void)alpha; (void)S0; (void)dO; (void)dST;
-    (void)dh_clvr; (void)clvr_scale; (void)dq; (void)dk; (void)dv; (void)dbeta; (void)dalpha;
-    (void)dS0; (void)dclvr_scale; (void)ws; (void)ws_bytes; (void)stream;
-    return fail(GDR_ERR_UNSUPPORTED, "gdr_backward is not available in this build");
+    const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
+    if (desc->in_dtype == GDR_FP32 && D == 128)
+        return fail(GDR_ERR_UNSUPPORTED, "the backward supports fp32 inputs only at dk = dv = 64");
+    const int64_t ntok = B * T * H;
+    const bool any = ntok > 0;
+    if (any && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, beta, dO, dq, dk, dv and dbeta are required");
+    if ((desc->gate == GDR_GATE_NONE) != (alpha == nullptr) && any)
+        return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
+    if ((desc->gate == GDR_GATE_NONE) != (dalpha == nullptr) && any)
+        return fail(GDR_ERR_INVALID_ARG, "dalpha must be NULL iff the gate is NONE");
+    if ((clvr_scale || dclvr_scale) && !dh_clvr)
+        return fail(GDR_ERR_INVALID_ARG, "clvr_scale / dclvr_scale given without dh_clvr");
+    const void* ptrs[] = {q, k, v, beta, alpha, S0, dO, dST, dh_clvr, clvr_scale, dq, dk, dv, dbeta,
+                          dalpha, dS0, dclvr_scale, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t ib = dtype_bytes(desc->in_dtype), ob = dtype_bytes(desc->out_dtype);
+    const size_t n_in = size_t(ntok) * D;
+    const size_t a_bytes = desc->gate == GDR_GATE_CHANNEL ? n_in * 4 : size_t(ntok) * 4;
+    const size_t s_bytes = size_t(B * H) * D * D * 4;
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{q, n_in * ib}, {k, n_in * ib}, {v, n_in * ib}, {beta, size_t(ntok) * 4}, {alpha, a_bytes},
+               {S0, s_bytes}, {dO, n_in * ib}, {dST, s_bytes}, {dh_clvr, n_in * ib},
+               {clvr_scale, size_t(H) * D * 4}},
+      outs[] = {{dq, n_in * ob}, {dk, n_in * ob}, {dv, n_in * ob}, {dbeta, size_t(ntok) * 4},
+                {dalpha, a_bytes}, {dS0, s_bytes}, {dclvr_scale, size_t(H) * D * 4}};
+    for (auto& o1 : outs) {
+        for (auto& in : ins)
+            if (overlap(o1.p, o1.n, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "an output overlaps an input");
+        for (auto& o2 : outs)
+            if (&o1 != &o2 && overlap(o1.p, o1.n, o2.p, o2.n))
+                return fail(GDR_ERR_INVALID_ARG, "two outputs overlap");
+    }
+    const int64_t nch = B * H * NC;
+    const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
+    gdr::ChunkWs w;
+    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, true, &w, ws);
+    const size_t need = chunk_bytes + align_up(dlam_partial_bytes(desc));
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+    for (auto& o1 : outs)
+        if (ws && overlap(ws, need, o1.p, o1.n)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an output");
+    if (B * H == 0) return GDR_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
+    const int gate = desc->gate;
+    hipError_t e = hipSuccess;
+#define GDR_STEP(name, call)                                                                  \
+    do {                                                                                      \
+        gdr::prof_before(s);                                                                  \
+        e = (call);                                                                           \
+        gdr::prof_after(name, s);                                                             \
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "%s launch: %s", name, hipGetErrorString(e)); \
+    } while (0)
+    if (NC > 0) {
+        GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, true, B, T, int(H), NC, q, k, v, beta,
+                                                alpha, nullptr, nullptr, w, s));
+        GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
+                                                         desc->scale, w, S0, nullptr, nullptr, true, s));
+    }
+    GDR_STEP("state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
+                                                 dS0, s));
+    if (NC > 0) {
+        GDR_STEP("grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
+                                                  q, k, v, beta, alpha, dO, dh_clvr, clvr_scale, dv, dbeta, w, s));
+        GDR_STEP("grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
+                                                    alpha, dq, dk, dalpha, w, s));
+    }
+    if (dclvr_scale) {
+        float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
+        GDR_STEP("clvr_dlam", gdr::launch_clvr_dlam(in_f32, B * T, int(H), int(D), dh_clvr, v, dclvr_scale,
+                                                    partial, dlam_segments(desc), s));
+    }
+#undef GDR_STEP
+    return GDR_OK;
 }
 
 gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,

@@ -1,0 +1,871 @@
+// gdr_bwd_grad.hip -- per-chunk gradients of the chunked gated delta rule.
+//
+// With S the chunk-start state, dS' the chunk-end state gradient and dU, U, dO
+// (scaled by the output scale) of the chunk, the chunk's forward
+//   U = T (V - Kt S),  O = Qt S + A U,  S' = Diag(gamma) S + Kb^T U,
+//   T = N diag(beta),  N = (I + L)^-1,  L = strict_tril(diag(beta) P),
+//   P = Kt Kh^T,  A = tril(Qt Kh^T),  W = T Kt, Ut = T V
+// gives, in reverse mode (every identity below is the derivative of one line):
+//   dQt = dO S^T               dA = tril(dO U^T)        dKb = U dS'^T
+//   dW  = -dU S^T              dgamma = rowsum(dS' . S)
+//   dT  = dU V^T + dW Kt^T     dV = T^T dU              dKt = T^T dW
+//   Y   = N^T dT               dbeta = diag(Y) + rowsum(dL . P)
+//   dL  = -strict_tril(Y T^T)  dP = diag(beta) dL
+// grad_lin_kernel computes all of that.  grad_gate_kernel then takes dA and dP
+// back through the decay-factored products (the same block references as the
+// forward), adds the Qt, Kt, Kb and gamma terms, and turns the gradient with
+// respect to the in-chunk log-decay cumsum into dalpha by a reverse cumsum.
+#include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+#include <type_traits>
+
+namespace gdr {
+
+template <int D, bool IN_F32>
+struct GLinLayout {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    static constexpr int OPB = sizeof(OpT);
+    static constexpr int PAD = 16 / OPB;
+    static constexpr int LDR = D + PAD;
+    static constexpr int LDC = CHUNK + PAD;
+    static constexpr int NT = 4 * D;
+    static constexpr int NW = NT / WAVE;
+    static constexpr int KT = 0;                           // Kt [64][LDR]  (Kt and dW later: Y fp32)
+    static constexpr int DW = KT + CHUNK * LDR * OPB;      // dW [64][LDR]
+    static constexpr int DWT = DW + CHUNK * LDR * OPB;     // dW^T [D][LDC]
+    static constexpr int TT = DWT + D * LDC * OPB;         // T^T [64][LDC]
+    static constexpr int NF = TT + CHUNK * LDC * OPB;      // N [64][64] fp32
+    static constexpr int DTF = NF + CHUNK * CHUNK * 4;     // dT [64][64] fp32
+    static constexpr int BYTES = DTF + CHUNK * CHUNK * 4;
+    static_assert(CHUNK * CHUNK * 4 <= 2 * CHUNK * LDR * OPB, "Y must fit in the Kt and dW regions");
+};
+
+template <typename InT, typename OpT>
+__device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
+    // eight consecutive input elements -> operand precision
+    if constexpr (sizeof(InT) == 2) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f.v[2 * e] = static_cast<OpT>(__uint_as_float(w[e] << 16));
+            f.v[2 * e + 1] = static_cast<OpT>(__uint_as_float(w[e] & 0xffff0000u));
+        }
+    } else {
+        const float4v a = reinterpret_cast<const float4v*>(p)[0];
+        const float4v b = reinterpret_cast<const float4v*>(p)[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f.v[e] = static_cast<OpT>(a[e]);
+            f.v[4 + e] = static_cast<OpT>(b[e]);
+        }
+    }
+}
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64_t NC, float scale,
+                                                         const void* __restrict__ k_, const void* __restrict__ v_,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ alpha,
+                                                         const void* __restrict__ dO_, const void* __restrict__ dh_,
+                                                         const float* __restrict__ lam, void* __restrict__ dv_,
+                                                         float* __restrict__ dbeta, ChunkWs ws) {
+    using L = GLinLayout<D, IN_F32>;
+    using OpT = typename L::OpT;
+    using InT = typename InType<IN_F32>::T;
+    using OutT = typename InType<OUT_F32>::T;
+    constexpr int NT = L::NT, NW = L::NW, LDR = L::LDR, LDC = L::LDC, RPP = 16;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ float s_tot[4][D];
+    __shared__ float s_gs[CHUNK];
+    __shared__ float s_beta[CHUNK];
+    __shared__ float s_db[CHUNK];
+
+    OpT* KT = reinterpret_cast<OpT*>(smem + L::KT);
+    float* YF = reinterpret_cast<float*>(smem + L::KT);
+    OpT* DWs = reinterpret_cast<OpT*>(smem + L::DW);
+    OpT* DWT = reinterpret_cast<OpT*>(smem + L::DWT);
+    OpT* TT = reinterpret_cast<OpT*>(smem + L::TT);
+    float* NF = reinterpret_cast<float*>(smem + L::NF);
+    float* DTF = reinterpret_cast<float*>(smem + L::DTF);
+
+    const int64_t ch = blockIdx.x;
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t t0 = c * CHUNK;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int cc = tid % D, part = tid / D, r0 = part * RPP;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t tokstride = static_cast<int64_t>(H) * D;
+    const int64_t base = ((b * T + t0) * H + h) * D;
+    const int64_t nvalid64 = T - t0;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
+    const InT* k = reinterpret_cast<const InT*>(k_);
+    const InT* v = reinterpret_cast<const InT*>(v_);
+    const InT* dO = reinterpret_cast<const InT*>(dO_);
+
+    // ---------------- phase 0: Kt = K 2^G, N, T^T ----------------
+    float G[RPP], kk[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const int r = r0 + j;
+        const int64_t e = base + (r < nvalid ? r : nvalid - 1) * tokstride + cc;
+        kk[j] = to_f32(k[e]);
+        if constexpr (GATE == GATE_CHANNEL) G[j] = alpha[e];
+        else G[j] = 0.f;
+    }
+    if (tid < CHUNK) {
+        const bool ok = tid < nvalid;
+        const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
+        const float bt = beta[tok];
+        s_beta[tid] = ok ? bt : 0.f;
+        if constexpr (GATE == GATE_SCALAR) {
+            const float at = alpha[tok];
+            float g = ok ? log2_fast(at) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(g, off);
+                if (lane >= off) g += y;
+            }
+            s_gs[tid] = g;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const bool ok = r0 + j < nvalid;
+        kk[j] = ok ? kk[j] : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(G[j]) : 0.f;
+    }
+    if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+        for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
+        s_tot[part][cc] = G[RPP - 1];
+    }
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) NF[e] = ws.Nw[ch * CHUNK * CHUNK + e];
+    __syncthreads();
+    if constexpr (GATE == GATE_CHANNEL) {
+        float carry = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) carry += (p < part) ? s_tot[p][cc] : 0.f;
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) G[j] += carry;
+    } else if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) G[j] = s_gs[r0 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) KT[(r0 + j) * LDR + cc] = from_f32<OpT>(kk[j] * exp2_fast(G[j]));
+    // T^T[i][r] = N[r][i] beta_i
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
+        const int r = e / CHUNK, i = e % CHUNK;
+        TT[i * LDC + r] = from_f32<OpT>(NF[e] * s_beta[i]);
+    }
+    __syncthreads();
+
+    // ---------------- phase 1: products contracting over the value dimension ----------------
+    // jobs: dQt (4 x D/16 tiles), dW (same), dKb (same), dA (10 lower tiles), dT1 (16)
+    {
+        constexpr int NDT = D / 16;
+        constexpr int NJ = 3 * 4 * NDT + 10 + 16;
+        const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
+        const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
+        const OpT* Us = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
+        const OpT* dUs = reinterpret_cast<const OpT*>(ws.dUsave) + ch * CHUNK * D;
+        for (int job = wid; job < NJ; job += NW) {
+            int kind, rt, nt;
+            if (job < 3 * 4 * NDT) {
+                kind = job / (4 * NDT);
+                rt = (job % (4 * NDT)) / NDT;
+                nt = job % NDT;
+            } else if (job < 3 * 4 * NDT + 10) {
+                kind = 3;
+                const int t = job - 3 * 4 * NDT;  // lower tiles (rt, nt <= rt)
+                rt = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+                nt = t - (rt * (rt + 1)) / 2;
+            } else {
+                kind = 4;
+                const int t = job - 3 * 4 * NDT - 10;
+                rt = t / 4;
+                nt = t % 4;
+            }
+            float4v acc = zero4();
+            const int arow = 16 * rt + l16;  // row of the A operand for this lane
+            const int brow = 16 * nt + l16;  // row of the B operand (column of the result)
+            const int64_t arow_g = base + (arow < nvalid ? arow : nvalid - 1) * tokstride;
+            const int64_t brow_g = base + (brow < nvalid ? brow : nvalid - 1) * tokstride;
+            const bool aok = arow < nvalid, bok = brow < nvalid;
+#pragma unroll
+            for (int kq = 0; kq < D / 32; ++kq) {
+                Frag<OpT> fa, fb;
+                const int kofs = 32 * kq + 8 * g4;
+                const int fo_a = ((rt * (D / 32) + kq) * 64 + lane) * 8;
+                const int fo_b = ((nt * (D / 32) + kq) * 64 + lane) * 8;
+                if (kind == 0 || kind == 3) {  // A = dO rows
+                    load_frag_in<InT, OpT>(fa, dO + arow_g + kofs);
+                    if (!aok) fa.zero();
+                } else if (kind == 1 || kind == 4) {  // A = dU rows
+                    fa.load(dUs + fo_a);
+                } else {  // A = U rows
+                    fa.load(Us + fo_a);
+                }
+                if (kind == 0 || kind == 1) fb.load(Ss + fo_b);        // B = S rows (d)
+                else if (kind == 2) fb.load(dSs + fo_b);                // B = dS' rows (d)
+                else if (kind == 3) fb.load(Us + fo_b);                 // B = U rows (i)
+                else {                                                   // B = V rows (i)
+                    load_frag_in<InT, OpT>(fb, v + brow_g + kofs);
+                    if (!bok) fb.zero();
+                }
+                mma(fa, fb, acc);
+            }
+            const int r_ = 16 * rt + 4 * g4;  // result rows r_ + e, column 16 nt + l16
+            const int col = 16 * nt + l16;
+            if (kind == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ws.gQt[ch * CHUNK * D + (r_ + e) * D + col] = scale * acc[e];
+            } else if (kind == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const OpT w = from_f32<OpT>(-acc[e]);
+                    DWs[(r_ + e) * LDR + col] = w;
+                    DWT[col * LDC + r_ + e] = w;
+                }
+            } else if (kind == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ws.gKb[ch * CHUNK * D + (r_ + e) * D + col] = acc[e];
+            } else if (kind == 3) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ws.gA[ch * CHUNK * CHUNK + (r_ + e) * CHUNK + col] = (col <= r_ + e) ? scale * acc[e] : 0.f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) DTF[(r_ + e) * CHUNK + col] = acc[e];
+            }
+        }
+        // dA is lower triangular: zero the six upper tiles
+        for (int e = tid; e < 6 * 256; e += NT) {
+            const int tile = e / 256, w = e % 256;
+            const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+            const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+            ws.gA[ch * CHUNK * CHUNK + (16 * R + w / 16) * CHUNK + 16 * I + w % 16] = 0.f;
+        }
+        // dgamma_d = sum_j dS'[d][j] S[d][j]
+        if (tid < D) {
+            float s = 0.f;
+#pragma unroll 4
+            for (int j8 = 0; j8 < D / 8; ++j8) {
+                Frag<OpT> fs, fd;
+                fs.load(Ss + frag_off<D>(tid, 8 * j8));
+                fd.load(dSs + frag_off<D>(tid, 8 * j8));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s += static_cast<float>(fs.v[e]) * static_cast<float>(fd.v[e]);
+            }
+            ws.gGam[ch * D + tid] = s;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: dT += dW Kt^T, dKt = T^T dW, dV = T^T dU ----------------
+    {
+        constexpr int NDT = D / 16;
+        constexpr int NJ = 16 + 2 * 4 * NDT;
+        const OpT* dUT = reinterpret_cast<const OpT*>(ws.dUsaveT) + ch * D * CHUNK;
+        OutT* dv = reinterpret_cast<OutT*>(dv_);
+        const InT* dh = reinterpret_cast<const InT*>(dh_);
+        for (int job = wid; job < NJ; job += NW) {
+            float4v acc = zero4();
+            int kind, rt, nt;
+            if (job < 16) {
+                kind = 0;
+                rt = job / 4;
+                nt = job % 4;
+#pragma unroll
+                for (int kq = 0; kq < D / 32; ++kq) {
+                    Frag<OpT> fa, fb;
+                    fa.load(DWs + (16 * rt + l16) * LDR + 32 * kq + 8 * g4);
+                    fb.load(KT + (16 * nt + l16) * LDR + 32 * kq + 8 * g4);
+                    mma(fa, fb, acc);
+                }
+            } else {
+                kind = (job - 16) < 4 * NDT ? 1 : 2;
+                const int t = (job - 16) % (4 * NDT);
+                rt = t / NDT;
+                nt = t % NDT;
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    Frag<OpT> fa, fb;
+                    fa.load(TT + (16 * rt + l16) * LDC + 32 * kq + 8 * g4);
+                    if (kind == 1) fb.load(DWT + (16 * nt + l16) * LDC + 32 * kq + 8 * g4);
+                    else fb.load(dUT + ((nt * 2 + kq) * 64 + lane) * 8);
+                    mma(fa, fb, acc);
+                }
+            }
+            const int r_ = 16 * rt + 4 * g4;
+            const int col = 16 * nt + l16;
+            if (kind == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) DTF[(r_ + e) * CHUNK + col] += acc[e];
+            } else if (kind == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = acc[e];
+            } else {
+                const float lm = (dh && lam) ? lam[h * D + col] : 1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r_ + e;
+                    if (r < nvalid) {
+                        const int64_t idx = base + r * tokstride + col;
+                        float g = acc[e];
+                        if (dh) g = __builtin_fmaf(lm, to_f32(dh[idx]), g);  // CLVR: h += lam v
+                        dv[idx] = from_f32<OutT>(g);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase 3: solve adjoint (fp32) ----------------
+    // Y = N^T dT  (N lower triangular: Y[a][x] = sum_{r >= a} N[r][a] dT[r][x])
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
+        const int a = e / CHUNK, x = e % CHUNK;
+        float s = 0.f;
+        for (int r = a; r < CHUNK; ++r) s += NF[r * CHUNK + a] * DTF[r * CHUNK + x];
+        YF[e] = s;
+    }
+    __syncthreads();
+    // dL[a][x] = -sum_{y <= x} Y[a][y] T[x][y] for x < a, T[x][y] = N[x][y] beta_y;
+    // dP = beta_a dL; dbeta_a = Y[a][a] + sum_x dL[a][x] P[a][x]
+    {
+        const float* Pw = ws.Pw + ch * CHUNK * CHUNK;
+        for (int e0 = 0; e0 < CHUNK * CHUNK; e0 += NT) {
+            const int e = e0 + tid;
+            const int a = e / CHUNK, x = e % CHUNK;  // a is uniform across the wave
+            float dl = 0.f;
+            if (x < a) {
+                float s = 0.f;
+                for (int y = 0; y <= x; ++y) s += YF[a * CHUNK + y] * NF[x * CHUNK + y] * s_beta[y];
+                dl = -s;
+            }
+            ws.gP[ch * CHUNK * CHUNK + e] = s_beta[a] * dl;
+            float contrib = dl * Pw[e];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) contrib += __shfl_xor(contrib, off);
+            if (lane == 0) s_db[a] = contrib;  // one wave covers one row a
+        }
+    }
+    __syncthreads();
+    if (tid < nvalid) dbeta[(b * T + t0 + tid) * H + h] = YF[tid * CHUNK + tid] + s_db[tid];
+}
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* k,
+                                    const void* v, const float* beta, const float* alpha, const void* dO,
+                                    const void* dh, const float* lam, void* dv, float* dbeta, const ChunkWs& ws,
+                                    hipStream_t stream) {
+    const int64_t nblk = B * H * NC;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T,
+                       H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws);
+    return hipGetLastError();
+}
+
+template <int D, int GATE>
+static hipError_t launch_grad_lin_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
+                                    float scale, const void* k, const void* v, const float* beta,
+                                    const float* alpha, const void* dO, const void* dh, const float* lam,
+                                    void* dv, float* dbeta, const ChunkWs& ws, hipStream_t stream) {
+    if (in_f32) {
+        if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+        return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+    }
+    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+}
+
+hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
+                           int64_t NC, float scale, const void* q, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* dO,
+                           const void* dh, const float* lam, void* dv, float* dbeta,
+                           const ChunkWs& ws, hipStream_t stream) {
+    (void)q;
+#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream
+    if (D == 64) {
+        if (gate == GATE_NONE) return launch_grad_lin_g<64, GATE_NONE>(GL_ARGS);
+        if (gate == GATE_SCALAR) return launch_grad_lin_g<64, GATE_SCALAR>(GL_ARGS);
+        return launch_grad_lin_g<64, GATE_CHANNEL>(GL_ARGS);
+    }
+    if (gate == GATE_NONE) return launch_grad_lin_g<128, GATE_NONE>(GL_ARGS);
+    if (gate == GATE_SCALAR) return launch_grad_lin_g<128, GATE_SCALAR>(GL_ARGS);
+    return launch_grad_lin_g<128, GATE_CHANNEL>(GL_ARGS);
+#undef GL_ARGS
+}
+
+}  // namespace gdr
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------
+// grad_gate: dA and dP back through the decay-factored products.
+//
+// With E_ri = 2^(G_r - G_i) (r >= i), A_ri = sum_c q_rc k_ic E_ric and
+// P_ri = sum_c k_rc k_ic E_ric.  For block row R and its reference ref(R)
+// (G at the last row before the block), Fq_r = 2^(G_r - ref) <= 1 and
+// Fh_i = 2^(ref - G_i), so that
+//   row side:    dqA_r  = Fq_r . (dA_R Kh)_r      dkP_r  = Fq_r . (dP_R Kh)_r
+//   column side: dkC_i += Fh_i . (dA_R^T Qq_R + dP_R^T Kq_R)_i
+// with Kh = K . Fh, Qq = Q . Fq, Kq = K . Fq.  The log-decay gradient is then
+// elementwise: dG_r += q_r . dqA_r + k_r . dkP_r - k_r . dkC_r.  Adding the Qt,
+// Kt, Kb and gamma terms (Qt = Q 2^G, Kt = K 2^G, Kb = K 2^(G_last - G),
+// gamma = 2^G_last) gives dq, dk and dG; dalpha_s = (sum_{r >= s} dG_r) / alpha_s
+// (G is the cumsum of log alpha).  Diagonal blocks whose decay range is too wide
+// for the operand precision are done exactly in fp32 by the thread that owns
+// the block's rows (pair factors from G differences, always <= 1).
+// ---------------------------------------------------------------------------
+
+template <int D, bool IN_F32>
+struct GGateLayout {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    static constexpr int OPB = sizeof(OpT);
+    static constexpr int PAD = 16 / OPB;
+    static constexpr int LDC = CHUNK + PAD;
+    static constexpr int NT = 4 * D;
+    static constexpr int NW = NT / WAVE;
+    static constexpr int DA = 0;                            // dA  [64][LDC]
+    static constexpr int DP = DA + CHUNK * LDC * OPB;       // dP  [64][LDC]
+    static constexpr int DAT = DP + CHUNK * LDC * OPB;      // dA^T
+    static constexpr int DPT = DAT + CHUNK * LDC * OPB;     // dP^T
+    static constexpr int QQT = DPT + CHUNK * LDC * OPB;     // Qq^T [D][LDC]
+    static constexpr int KQT = QQT + D * LDC * OPB;         // Kq^T
+    static constexpr int KHT = KQT + D * LDC * OPB;         // Kh^T
+    static constexpr int SA = KHT + D * LDC * OPB;          // fp32 [16][D]  dA_R Kh
+    static constexpr int SB = SA + 16 * D * 4;              // fp32 [16][D]  dP_R Kh
+    static constexpr int SC = SB + 16 * D * 4;              // fp32 [64][D]  dA_R^T Qq + dP_R^T Kq
+    static constexpr int BYTES = SC + CHUNK * D * 4;
+    static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
+};
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int64_t NC,
+                                                          const void* __restrict__ q_, const void* __restrict__ k_,
+                                                          const float* __restrict__ alpha, void* __restrict__ dq_,
+                                                          void* __restrict__ dk_, float* __restrict__ dalpha,
+                                                          ChunkWs ws) {
+    using L = GGateLayout<D, IN_F32>;
+    using OpT = typename L::OpT;
+    using InT = typename InType<IN_F32>::T;
+    using OutT = typename InType<OUT_F32>::T;
+    constexpr int NT = L::NT, NW = L::NW, LDC = L::LDC, RPP = 16;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ float s_tot[4][D];
+    __shared__ float s_gs[CHUNK];
+    __shared__ float s_red[NW];
+    __shared__ float s_row[CHUNK];
+
+    OpT* dAs = reinterpret_cast<OpT*>(smem + L::DA);
+    OpT* dPs = reinterpret_cast<OpT*>(smem + L::DP);
+    OpT* dAT = reinterpret_cast<OpT*>(smem + L::DAT);
+    OpT* dPT = reinterpret_cast<OpT*>(smem + L::DPT);
+    OpT* QqT = reinterpret_cast<OpT*>(smem + L::QQT);
+    OpT* KqT = reinterpret_cast<OpT*>(smem + L::KQT);
+    OpT* KhT = reinterpret_cast<OpT*>(smem + L::KHT);
+    float* SAf = reinterpret_cast<float*>(smem + L::SA);
+    float* SBf = reinterpret_cast<float*>(smem + L::SB);
+    float* SCf = reinterpret_cast<float*>(smem + L::SC);
+
+    const int64_t ch = blockIdx.x;
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t t0 = c * CHUNK;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int cc = tid % D, part = tid / D, r0 = part * RPP;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t tokstride = static_cast<int64_t>(H) * D;
+    const int64_t base = ((b * T + t0) * H + h) * D;
+    const int64_t nvalid64 = T - t0;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
+    const InT* q = reinterpret_cast<const InT*>(q_);
+    const InT* k = reinterpret_cast<const InT*>(k_);
+    const float* gA = ws.gA + ch * CHUNK * CHUNK;
+    const float* gP = ws.gP + ch * CHUNK * CHUNK;
+
+    // ---------------- phase 0: G, block references, row operands, dA/dP ----------------
+    float G[RPP], kk[RPP], qq[RPP], al[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const int r = r0 + j;
+        const int64_t e = base + (r < nvalid ? r : nvalid - 1) * tokstride + cc;
+        kk[j] = to_f32(k[e]);
+        qq[j] = to_f32(q[e]);
+        if constexpr (GATE == GATE_CHANNEL) al[j] = alpha[e];
+        else al[j] = 1.f;
+    }
+    if constexpr (GATE == GATE_SCALAR) {
+        if (tid < CHUNK) {
+            const bool ok = tid < nvalid;
+            const float at = alpha[(b * T + t0 + (ok ? tid : nvalid - 1)) * H + h];
+            float g = ok ? log2_fast(at) : 0.f;
+            s_row[tid] = ok ? at : 1.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(g, off);
+                if (lane >= off) g += y;
+            }
+            s_gs[tid] = g;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const bool ok = r0 + j < nvalid;
+        kk[j] = ok ? kk[j] : 0.f;
+        qq[j] = ok ? qq[j] : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) {
+            al[j] = ok ? al[j] : 1.f;
+            G[j] = log2_fast(al[j]);
+        } else {
+            G[j] = 0.f;
+        }
+    }
+    if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+        for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
+        s_tot[part][cc] = G[RPP - 1];
+    }
+    // dA, dP into operand precision, both orientations; Kh^T starts at zero
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
+        const int r = e / CHUNK, i = e % CHUNK;
+        const OpT a = from_f32<OpT>(gA[e]), p = from_f32<OpT>(gP[e]);
+        dAs[r * LDC + i] = a;
+        dPs[r * LDC + i] = p;
+        dAT[i * LDC + r] = a;
+        dPT[i * LDC + r] = p;
+    }
+    for (int e = tid; e < D * LDC; e += NT) KhT[e] = from_f32<OpT>(0.f);
+    __syncthreads();
+
+    float carry = 0.f, glast = 0.f;
+    if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float t = s_tot[p][cc];
+            carry += (p < part) ? t : 0.f;
+            glast += t;
+        }
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) G[j] += carry;
+    } else if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            G[j] = s_gs[r0 + j];
+            al[j] = s_row[r0 + j];
+        }
+        carry = part ? s_gs[r0 - 1] : 0.f;
+        glast = s_gs[CHUNK - 1];
+    }
+    // exact-path flags: decay range of each diagonal block, max over channels
+    int flags = 0;
+    if constexpr (GATE != GATE_NONE) {
+        float rho = carry - G[RPP - 1];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
+        if (lane == 0) s_red[wid] = rho;  // each wave holds one block
+    }
+    __syncthreads();
+    s_tot[part][cc] = G[RPP - 1];  // G at the last row of block `part` (0 without a gate)
+    if constexpr (GATE != GATE_NONE) {
+        constexpr int WPB = D / WAVE;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float rho = s_red[R * WPB];
+#pragma unroll
+            for (int w = 1; w < WPB; ++w) rho = fmaxf(rho, s_red[R * WPB + w]);
+            if (!(rho <= L::RHO_MAX)) flags |= 1 << R;
+        }
+    }
+    {
+        // row operands Qq, Kq (reference = G before this thread's block), transposed
+        float fq[RPP], kq_[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const float f = exp2_fast(G[j] - carry);
+            fq[j] = qq[j] * f;
+            kq_[j] = kk[j] * f;
+        }
+        store_run<OpT, RPP>(QqT + cc * LDC + r0, fq);
+        store_run<OpT, RPP>(KqT + cc * LDC + r0, kq_);
+    }
+    // flagged diagonal blocks are excluded from the matrix-core products
+    if (flags) {
+        for (int e = tid; e < 4 * 256; e += NT) {
+            const int R = e / 256;
+            if (!((flags >> R) & 1)) continue;
+            const int r = 16 * R + (e % 256) / 16, i = 16 * R + e % 16;
+            const OpT z = from_f32<OpT>(0.f);
+            dAs[r * LDC + i] = z;
+            dPs[r * LDC + i] = z;
+            dAT[i * LDC + r] = z;
+            dPT[i * LDC + r] = z;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phases R = 0..3 ----------------
+    float Aq[RPP], Prow[RPP], Ccol[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        Aq[j] = 0.f;
+        Prow[j] = 0.f;
+        Ccol[j] = 0.f;
+    }
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const float ref = R ? s_tot[R - 1][cc] : 0.f;
+        if (part <= R) {
+            float kh[RPP];
+            const bool zero = (part == R) && ((flags >> R) & 1);
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) kh[j] = zero ? 0.f : kk[j] * exp2_fast(ref - G[j]);
+            store_run<OpT, RPP>(KhT + cc * LDC + r0, kh);
+        }
+        __syncthreads();
+        // (a) dA_R Kh, (b) dP_R Kh: 16 x D each, k over 16(R+1) columns
+        // (c) [dA_R^T | dP_R^T] [Qq_R ; Kq_R]: 16(R+1) x D, one 32-wide k step
+        constexpr int NDT = D / 16;
+        const int nj = 2 * NDT + (R + 1) * NDT;
+        for (int job = wid; job < nj; job += NW) {
+            float4v acc = zero4();
+            if (job < 2 * NDT) {
+                const int isP = job / NDT, ct = job % NDT;
+                const OpT* arow = (isP ? dPs : dAs) + (16 * R + l16) * LDC + 8 * g4;
+                const OpT* brow = KhT + (16 * ct + l16) * LDC + 8 * g4;
+                const int nkq = (16 * (R + 1) + 31) / 32;
+                for (int kq = 0; kq < nkq; ++kq) {
+                    Frag<OpT> fa, fb;
+                    fa.load(arow + 32 * kq);
+                    fb.load(brow + 32 * kq);
+                    mma(fa, fb, acc);
+                }
+                float* dst = isP ? SBf : SAf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(4 * g4 + e) * D + 16 * ct + l16] = acc[e];
+            } else {
+                const int t = job - 2 * NDT, it = t / NDT, ct = t % NDT;
+                Frag<OpT> fa, fb;
+                // k < 16: dA^T and Qq; k >= 16: dP^T and Kq (lane groups 0,1 vs 2,3)
+                const int i = 16 * it + l16, kr = 16 * R + 8 * (g4 & 1);
+                fa.load((g4 < 2 ? dAT : dPT) + i * LDC + kr);
+                fb.load((g4 < 2 ? QqT : KqT) + (16 * ct + l16) * LDC + kr);
+                mma(fa, fb, acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) SCf[(16 * it + 4 * g4 + e) * D + 16 * ct + l16] = acc[e];
+            }
+        }
+        __syncthreads();
+        if (part == R) {
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                Aq[j] += SAf[j * D + cc];
+                Prow[j] += SBf[j * D + cc];
+            }
+        }
+        // column side, scaled by Fh = 2^(ref(R) - G) (a flagged diagonal block
+        // contributes nothing here; its exact terms are added below)
+        if (part < R || (part == R && !((flags >> R) & 1))) {
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) Ccol[j] += SCf[(r0 + j) * D + cc] * exp2_fast(ref - G[j]);
+        }
+        __syncthreads();
+    }
+    // row-side factor Fq = 2^(G - ref(own block))
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const float f = exp2_fast(G[j] - carry);
+        Aq[j] *= f;
+        Prow[j] *= f;
+    }
+    // exact diagonal blocks (fp32, pair factors 2^(G_r - G_i) <= 1)
+    if ((flags >> part) & 1) {
+        const float* gAr = gA + r0 * CHUNK + r0;
+        const float* gPr = gP + r0 * CHUNK + r0;
+#pragma unroll
+        for (int jr = 0; jr < RPP; ++jr) {
+#pragma unroll
+            for (int ji = 0; ji <= jr; ++ji) {
+                const float E = exp2_fast(G[jr] - G[ji]);
+                const float da = gAr[jr * CHUNK + ji], dp = (ji < jr) ? gPr[jr * CHUNK + ji] : 0.f;
+                Aq[jr] += da * kk[ji] * E;
+                Prow[jr] += dp * kk[ji] * E;
+                Ccol[ji] += (da * qq[jr] + dp * kk[jr]) * E;
+            }
+        }
+    }
+
+    // ---------------- combine ----------------
+    float dG[RPP];
+    float lastsum = 0.f;  // sum_r k_r . dKb_r . 2^(G_last - G_r): goes to the last row
+    {
+        OutT* dq = reinterpret_cast<OutT*>(dq_);
+        OutT* dk = reinterpret_cast<OutT*>(dk_);
+        const float* gQt = ws.gQt + ch * CHUNK * D;
+        const float* gKt = ws.gKt + ch * CHUNK * D;
+        const float* gKb = ws.gKb + ch * CHUNK * D;
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = r0 + j;
+            const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
+            const float gq = gQt[r * D + cc] * E, gkt = gKt[r * D + cc] * E, gkb = gKb[r * D + cc] * Eb;
+            const float dqv = gq + Aq[j];
+            const float dkv = gkt + gkb + Prow[j] + Ccol[j];
+            dG[j] = qq[j] * dqv + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
+            lastsum += kk[j] * gkb;
+            if (r < nvalid) {
+                dq[base + r * tokstride + cc] = from_f32<OutT>(dqv);
+                dk[base + r * tokstride + cc] = from_f32<OutT>(dkv);
+            }
+        }
+    }
+    if constexpr (GATE != GATE_NONE) {
+        // gradient w.r.t. G (natural-log units) -> reverse cumsum over the chunk -> dalpha
+        // part sums of dG and of the last-row term, for the carries between parts
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) psum += dG[j];
+        __syncthreads();
+        s_tot[part][cc] = psum;
+        __syncthreads();
+        float later = 0.f;  // sum of dG over rows after this thread's block
+#pragma unroll
+        for (int p = 0; p < 4; ++p) later += (p > part) ? s_tot[p][cc] : 0.f;
+        __syncthreads();
+        s_tot[part][cc] = lastsum;
+        __syncthreads();
+        float ltot = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ltot += s_tot[p][cc];
+        // the last row (and so every row, through the reverse cumsum) also gets
+        // d/dG_last of Kb's 2^G_last and of gamma: sum_r k.dKb.2^(Gl-G) + gamma.dgamma
+        const float gl_term = ltot + exp2_fast(glast) * ws.gGam[ch * D + cc];
+        float run = later + gl_term;
+        float dg[RPP];
+#pragma unroll
+        for (int j = RPP - 1; j >= 0; --j) {
+            run += dG[j];
+            dg[j] = run;
+        }
+        if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                const int r = r0 + j;
+                if (r < nvalid) dalpha[base + r * tokstride + cc] = dg[j] / al[j];
+            }
+        } else {
+            // scalar gate: sum over channels
+            __syncthreads();
+            for (int e = tid; e < CHUNK; e += NT) s_row[e] = 0.f;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                float x = dg[j];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+                if (lane == 0) atomicAdd(&s_row[r0 + j], x);
+            }
+            __syncthreads();
+            if (tid < nvalid) {
+                float a1 = alpha[(b * T + t0 + tid) * H + h];
+                dalpha[(b * T + t0 + tid) * H + h] = s_row[tid] / a1;
+            }
+        }
+    }
+}
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
+                                     const float* alpha, void* dq, void* dk, float* dalpha, const ChunkWs& ws,
+                                     hipStream_t stream) {
+    const int64_t nblk = B * H * NC;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream,
+                       T, H, NC, q, k, alpha, dq, dk, dalpha, ws);
+    return hipGetLastError();
+}
+
+template <int D, int GATE>
+static hipError_t launch_grad_gate_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
+                                     const void* q, const void* k, const float* alpha, void* dq, void* dk,
+                                     float* dalpha, const ChunkWs& ws, hipStream_t stream) {
+    if (in_f32) {
+        if constexpr (D == 64) {
+            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+        }
+        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
+    }
+    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+}
+
+hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
+                            int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
+                            void* dk, float* dalpha, const ChunkWs& ws, hipStream_t stream) {
+#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream
+    if (D == 64) {
+        if (gate == GATE_NONE) return launch_grad_gate_g<64, GATE_NONE>(GG_ARGS);
+        if (gate == GATE_SCALAR) return launch_grad_gate_g<64, GATE_SCALAR>(GG_ARGS);
+        return launch_grad_gate_g<64, GATE_CHANNEL>(GG_ARGS);
+    }
+    if (gate == GATE_NONE) return launch_grad_gate_g<128, GATE_NONE>(GG_ARGS);
+    if (gate == GATE_SCALAR) return launch_grad_gate_g<128, GATE_SCALAR>(GG_ARGS);
+    return launch_grad_gate_g<128, GATE_CHANNEL>(GG_ARGS);
+#undef GG_ARGS
+}
+
+// ---------------------------------------------------------------------------
+// CLVR: dlam[c] = sum over tokens of dh[., c] * v[., c]  (c = h*dv + j).
+// Pass 1: nseg token segments, one partial per (segment, channel).
+// Pass 2: sum the partials of each channel in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+template <bool IN_F32>
+__global__ __launch_bounds__(256) void clvr_dlam_partial(int64_t BT, int HD, int64_t nseg, const void* __restrict__ dh_,
+                                                         const void* __restrict__ v_, float* __restrict__ partial) {
+    using InT = typename InType<IN_F32>::T;
+    const InT* dh = reinterpret_cast<const InT*>(dh_);
+    const InT* v = reinterpret_cast<const InT*>(v_);
+    const int64_t c = blockIdx.x * 256 + threadIdx.x;
+    const int64_t seg = blockIdx.y;
+    if (c >= HD) return;
+    const int64_t per = (BT + nseg - 1) / nseg;
+    const int64_t t0 = seg * per, t1 = t0 + per < BT ? t0 + per : BT;
+    float s = 0.f;
+    for (int64_t t = t0; t < t1; ++t) s += to_f32(dh[t * HD + c]) * to_f32(v[t * HD + c]);
+    partial[seg * HD + c] = s;
+}
+
+__global__ __launch_bounds__(256) void clvr_dlam_final(int HD, int64_t nseg, const float* __restrict__ partial,
+                                                       float* __restrict__ dlam) {
+    const int64_t c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= HD) return;
+    float s = 0.f;
+    for (int64_t seg = 0; seg < nseg; ++seg) s += partial[seg * HD + c];
+    dlam[c] = s;
+}
+
+hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
+                            float* dlam, float* partial, int64_t nseg, hipStream_t stream) {
+    const int HD = H * D;
+    const dim3 g1((HD + 255) / 256, (unsigned)nseg);
+    if (in_f32)
+        hipLaunchKernelGGL((clvr_dlam_partial<true>), g1, dim3(256), 0, stream, BT, HD, nseg, dh, v, partial);
+    else
+        hipLaunchKernelGGL((clvr_dlam_partial<false>), g1, dim3(256), 0, stream, BT, HD, nseg, dh, v, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(clvr_dlam_final, dim3((HD + 255) / 256), dim3(256), 0, stream, HD, nseg, partial, dlam);
+    return hipGetLastError();
+}
+
+}  // namespace gdr

@@ -1,0 +1,273 @@
+// gdr_bwd_state.hip -- reverse state pass of the chunked backward.
+//
+// Reverse mode of the chunk recurrence (forward, per chunk c with start state S):
+//   U = Ut - W S,   O = Qt S + A U,   S' = Diag(gamma) S + Kb^T U.
+// Carrying dS' = dL/dS' backwards (dO already multiplied by the output scale):
+//   dU = A^T dO + Kb dS'
+//   dS = Qt^T dO + Diag(gamma) dS' - W^T dU
+// Columns of the state are again independent, so the pass is split into dv
+// slices of 16 columns exactly like the forward pass.  Per chunk it saves the
+// chunk-end gradient dS' and dU (fragment order, for the gradient kernels); the
+// gradient that reaches the initial state is dS0.
+#include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+#include <type_traits>
+
+namespace gdr {
+
+template <int D, bool IN_F32>
+struct BwdCfg {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    using InT = typename InType<IN_F32>::T;
+    static constexpr int NS = 16;
+    static constexpr int NSL = D / NS;
+    static constexpr int PAD = 16 / sizeof(OpT);
+    static constexpr int LDS_S = D + PAD;
+    static constexpr int LDS_U = CHUNK + PAD;
+    static constexpr int SRT = D / 64;
+};
+
+template <int D, bool IN_F32>
+struct BwdFrags {
+    using OpT = typename BwdCfg<D, IN_F32>::OpT;
+    using InT = typename BwdCfg<D, IN_F32>::InT;
+    static constexpr int SRT = BwdCfg<D, IN_F32>::SRT;
+    Frag<OpT> at[2], kb[D / 32], qtt[SRT][2], wt[SRT][2];
+    float gam[SRT][4];
+    InT dO[4];
+};
+
+// Loads the operands of chunk c (fragment order, contiguous per fragment) and
+// this lane's four dO values (rows 16*wid + 4*g4 + e, column j0 + l16).
+template <int D, bool IN_F32>
+__device__ __forceinline__ void load_bwd(BwdFrags<D, IN_F32>& f, const ChunkWs& ws, int64_t ch, int64_t c,
+                                         int64_t b, int64_t T, int H, int h, const void* dO_, int j0, int wid,
+                                         int lane) {
+    using Cfg = BwdCfg<D, IN_F32>;
+    using OpT = typename Cfg::OpT;
+    using InT = typename Cfg::InT;
+    const OpT* AT = reinterpret_cast<const OpT*>(ws.AT) + ch * CHUNK * CHUNK;
+    f.at[0].load(AT + ((wid * 2 + 0) * 64 + lane) * 8);
+    f.at[1].load(AT + ((wid * 2 + 1) * 64 + lane) * 8);
+    const OpT* Kb = reinterpret_cast<const OpT*>(ws.Kb) + ch * CHUNK * D;
+#pragma unroll
+    for (int kq = 0; kq < D / 32; ++kq) f.kb[kq].load(Kb + ((wid * (D / 32) + kq) * 64 + lane) * 8);
+    const OpT* QtT = reinterpret_cast<const OpT*>(ws.QtT) + ch * D * CHUNK;
+    const OpT* WT = reinterpret_cast<const OpT*>(ws.WT) + ch * D * CHUNK;
+#pragma unroll
+    for (int m = 0; m < Cfg::SRT; ++m) {
+        const int rt = wid * (D / 64) + m;
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            f.qtt[m][kq].load(QtT + ((rt * 2 + kq) * 64 + lane) * 8);
+            f.wt[m][kq].load(WT + ((rt * 2 + kq) * 64 + lane) * 8);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.gam[m][e] = ws.gam[ch * D + 16 * rt + 4 * (lane >> 4) + e];
+    }
+    const InT* dO = reinterpret_cast<const InT*>(dO_);
+    const int64_t tb = c * CHUNK + 16 * wid + 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t t = (tb + e < T) ? tb + e : T - 1;  // clamped; zeroed at use
+        f.dO[e] = dO[((b * T + t) * H + h) * D + j0 + (lane & 15)];
+    }
+}
+
+template <typename OpT>
+__device__ __forceinline__ void st4b(OpT* dst, const float4v& v) {
+    if constexpr (sizeof(OpT) == 2) {
+        half4 hv;
+        hv[0] = static_cast<_Float16>(v[0]); hv[1] = static_cast<_Float16>(v[1]);
+        hv[2] = static_cast<_Float16>(v[2]); hv[3] = static_cast<_Float16>(v[3]);
+        *reinterpret_cast<half4*>(dst) = hv;
+    } else {
+        *reinterpret_cast<float4v*>(dst) = v;
+    }
+}
+
+template <typename OpT>
+__device__ __forceinline__ void st8(OpT* dst, const OpT (&v)[8]) {
+    if constexpr (sizeof(OpT) == 2) {
+        half8 hv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = v[e];
+        *reinterpret_cast<half8*>(dst) = hv;
+    } else {
+        float4v a, c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = v[e];
+            c[e] = v[4 + e];
+        }
+        reinterpret_cast<float4v*>(dst)[0] = a;
+        reinterpret_cast<float4v*>(dst)[1] = c;
+    }
+}
+
+template <int D, bool IN_F32>
+__device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t c, int64_t T, int64_t bh,
+                                         int64_t NC, int j0, int wid, int lane, float scale, const ChunkWs& ws,
+                                         float4v (&dS)[BwdCfg<D, IN_F32>::SRT],
+                                         typename BwdCfg<D, IN_F32>::OpT* s_dS,
+                                         typename BwdCfg<D, IN_F32>::OpT* s_dO,
+                                         typename BwdCfg<D, IN_F32>::OpT* s_dU) {
+    using Cfg = BwdCfg<D, IN_F32>;
+    using OpT = typename Cfg::OpT;
+    constexpr int SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
+    const int l16 = lane & 15, g4 = lane >> 4, tid = wid * WAVE + lane;
+    const int64_t ch = bh * NC + c;
+
+    // chunk-end gradient dS' of this chunk, fragment order (rows d, k = column)
+    if (tid < 2 * D) {
+        const int d = tid >> 1, hf = tid & 1;
+        OpT vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = s_dS[(8 * hf + e) * LDS_S + d];
+        st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf), vals);
+    }
+    // scaled dO slice, transposed into LDS (rows past the end are zero)
+    {
+        float4v x;
+        const int64_t tb = c * CHUNK + 16 * wid + 4 * g4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (tb + e < T) ? scale * to_f32(cur.dO[e]) : 0.f;
+        st4b<OpT>(s_dO + l16 * LDS_U + 16 * wid + 4 * g4, x);
+    }
+    __syncthreads();
+
+    // dU = A^T dO + Kb dS'   (A^T is upper triangular: rows 16w.. need k >= 16w)
+    float4v du = zero4();
+    {
+        Frag<OpT> fo;
+        if (wid < 2) {
+            fo.load(s_dO + l16 * LDS_U + 8 * g4);
+            mma(cur.at[0], fo, du);
+        }
+        fo.load(s_dO + l16 * LDS_U + 32 + 8 * g4);
+        mma(cur.at[1], fo, du);
+#pragma unroll
+        for (int kq = 0; kq < D / 32; ++kq) {
+            Frag<OpT> fs;
+            fs.load(s_dS + l16 * LDS_S + 32 * kq + 8 * g4);
+            mma(cur.kb[kq], fs, du);
+        }
+    }
+    st4b<OpT>(s_dU + l16 * LDS_U + 16 * wid + 4 * g4, du);
+    __syncthreads();
+
+    // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
+    if (tid < 2 * CHUNK) {
+        const int pos = tid >> 1, hf = tid & 1;
+        OpT vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = s_dU[(8 * hf + e) * LDS_U + pos];
+        st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
+    } else if (tid < 2 * CHUNK + 128) {
+        const int t2 = tid - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;  // column j, positions 8pg..8pg+7
+        OpT vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = s_dU[j * LDS_U + 8 * pg + e];
+        st8(reinterpret_cast<OpT*>(ws.dUsaveT) + ch * D * CHUNK + frag_off<CHUNK>(j0 + j, 8 * pg), vals);
+    }
+
+    // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
+    Frag<OpT> fo0, fo1, fu0, fu1;
+    fo0.load(s_dO + l16 * LDS_U + 8 * g4);
+    fo1.load(s_dO + l16 * LDS_U + 32 + 8 * g4);
+    fu0.load(s_dU + l16 * LDS_U + 8 * g4);
+    fu1.load(s_dU + l16 * LDS_U + 32 + 8 * g4);
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[m][e] *= cur.gam[m][e];
+        mma(cur.qtt[m][0], fo0, dS[m]);
+        mma(cur.qtt[m][1], fo1, dS[m]);
+        float4v wdu = zero4();
+        mma(cur.wt[m][0], fu0, wdu);
+        mma(cur.wt[m][1], fu1, wdu);
+        dS[m] -= wdu;
+        // s_dS was last read before the previous barrier
+        st4b<OpT>(s_dS + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, dS[m]);
+    }
+    __syncthreads();
+}
+
+template <int D, bool IN_F32>
+__global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
+                                                        const void* __restrict__ dO, const float* __restrict__ dST,
+                                                        float* __restrict__ dS0) {
+    using Cfg = BwdCfg<D, IN_F32>;
+    using OpT = typename Cfg::OpT;
+    constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
+
+    __shared__ __attribute__((aligned(16))) OpT s_dS[Cfg::NS * LDS_S];
+    __shared__ __attribute__((aligned(16))) OpT s_dO[Cfg::NS * LDS_U];
+    __shared__ __attribute__((aligned(16))) OpT s_dU[Cfg::NS * LDS_U];
+
+    const int64_t nblk = gridDim.x;
+    int64_t lid = blockIdx.x;
+    if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+    const int64_t bh = lid / NSL;
+    const int j0 = static_cast<int>(lid % NSL) * Cfg::NS;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    float4v dS[SRT];
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+        const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[m][e] = dST ? dST[(bh * D + d0 + e) * D + j0 + l16] : 0.f;
+        st4b<OpT>(s_dS + l16 * LDS_S + d0, dS[m]);
+    }
+    __syncthreads();
+
+    BwdFrags<D, IN_F32> fa, fb;
+    if (NC > 0) load_bwd<D, IN_F32>(fa, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, wid, lane);
+#pragma unroll 1
+    for (int64_t c = NC - 1; c >= 0; c -= 2) {
+        const int64_t n1 = c - 1 >= 0 ? c - 1 : 0;
+        load_bwd<D, IN_F32>(fb, ws, bh * NC + n1, n1, b, T, H, h, dO, j0, wid, lane);
+        bwd_step<D, IN_F32>(fa, c, T, bh, NC, j0, wid, lane, scale, ws, dS, s_dS, s_dO, s_dU);
+        if (c - 1 < 0) break;
+        const int64_t n2 = c - 2 >= 0 ? c - 2 : 0;
+        load_bwd<D, IN_F32>(fa, ws, bh * NC + n2, n2, b, T, H, h, dO, j0, wid, lane);
+        bwd_step<D, IN_F32>(fb, c - 1, T, bh, NC, j0, wid, lane, scale, ws, dS, s_dS, s_dO, s_dU);
+    }
+
+    if (dS0) {
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS0[(bh * D + d0 + e) * D + j0 + l16] = dS[m][e];
+        }
+    }
+}
+
+template <int D, bool IN_F32>
+static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
+                                     const void* dO, const float* dST, float* dS0, hipStream_t stream) {
+    const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
+                       scale, ws, dO, dST, dS0);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                            const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
+                            hipStream_t stream) {
+    if (D == 64) {
+        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+    }
+    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+}
+
+}  // namespace gdr

@@ -122,6 +122,42 @@ __device__ __forceinline__ float4v zero4() {
     return z;
 }
 
+// Stores N consecutive values (16-byte aligned destination) in operand precision.
+template <typename OpT, int N>
+__device__ __forceinline__ void store_run(OpT* dst, const float* src) {
+    // N consecutive values, 16-byte aligned destination
+    if constexpr (sizeof(OpT) == 2) {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(src[i + e]);
+            *reinterpret_cast<half8*>(dst + i) = h;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            float4v f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = src[i + e];
+            *reinterpret_cast<float4v*>(dst + i) = f;
+        }
+    }
+}
+
+// Stores the four values of an accumulator quad in operand precision.
+template <typename OpT>
+__device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
+    if constexpr (sizeof(OpT) == 2) {
+        half4 h;
+        h[0] = static_cast<_Float16>(v[0]); h[1] = static_cast<_Float16>(v[1]);
+        h[2] = static_cast<_Float16>(v[2]); h[3] = static_cast<_Float16>(v[3]);
+        *reinterpret_cast<half4*>(dst) = h;
+    } else {
+        *reinterpret_cast<float4v*>(dst) = v;
+    }
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 

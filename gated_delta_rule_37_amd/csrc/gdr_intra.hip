@@ -75,40 +75,6 @@ struct IntraLayout {
     static constexpr float WIDE_MAX = 120.f;
 };
 
-template <typename OpT, int N>
-__device__ __forceinline__ void store_run(OpT* dst, const float* src) {
-    // N consecutive values, 16-byte aligned destination
-    if constexpr (sizeof(OpT) == 2) {
-#pragma unroll
-        for (int i = 0; i < N; i += 8) {
-            half8 h;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(src[i + e]);
-            *reinterpret_cast<half8*>(dst + i) = h;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            float4v f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = src[i + e];
-            *reinterpret_cast<float4v*>(dst + i) = f;
-        }
-    }
-}
-
-template <typename OpT>
-__device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
-    if constexpr (sizeof(OpT) == 2) {
-        half4 h;
-        h[0] = static_cast<_Float16>(v[0]); h[1] = static_cast<_Float16>(v[1]);
-        h[2] = static_cast<_Float16>(v[2]); h[3] = static_cast<_Float16>(v[3]);
-        *reinterpret_cast<half4*>(dst) = h;
-    } else {
-        *reinterpret_cast<float4v*>(dst) = v;
-    }
-}
-
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -471,7 +437,9 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     // ---------------- phase 3: T = (I + L)^-1 diag(beta), L = strict_tril(diag(beta) P) ----------------
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, i = e % CHUNK;
-        Pm[e] = (i < r) ? s_beta[r] * Ps[e] : 0.f;  // Ps aliases Nm: read before the zero
+        const float pv = Ps[e];
+        if constexpr (BWD) ws.Pw[ch * CHUNK * CHUNK + e] = (i < r) ? pv : 0.f;
+        Pm[e] = (i < r) ? s_beta[r] * pv : 0.f;  // Ps aliases Nm: read before the zero
         Nm[e] = 0.f;
     }
     __syncthreads();

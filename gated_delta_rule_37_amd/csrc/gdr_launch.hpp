@@ -8,21 +8,27 @@
 
 namespace gdr {
 
-// Per chunk-head intermediates written by the intra-chunk kernel and consumed by
-// the state pass.  `op` is the element size of the matrix-core operands
-// (2 for fp16, 4 for fp32).  Each array is [B*H*NC] chunk-heads of:
-//   W   [64][D]   Ut  [64][D]   Qt  [64][D]   KbT [D][64]   A [64][64]
-//   gam [D] fp32 (per-channel decay over the whole chunk)
-// and, for the backward only,
-//   AT  [64][64]  Kb [64][D]  QtT [D][64]  WT [D][64]  Nw [64][64] fp32
-//   Ssnap [D][D] chunk-start state, Usave [64][D] (op elements)
-//   dSsnap [D][D] chunk-end state gradient, dUsave [64][D]
+// Per chunk-head intermediates, [B*H*NC] chunk-heads each; "op" elements are
+// fp16 for bf16 inputs and fp32 for fp32 inputs.  Operands read by matrix
+// cores are stored in fragment order (frag_off / cfrag_off in gdr_common.hpp).
+//   forward (written by the intra-chunk kernel, read by the state pass):
+//     W [64][D], Ut [64][D] (accumulator order), Qt [64][D], KbT [D][64],
+//     A [64][64] (op); gam [D] fp32
+//   backward, additionally:
+//     AT [64][64], Kb [64][D], QtT [D][64], WT [D][64] (op)   reverse pass
+//     Nw, Pw [64][64] fp32: N = (I + L)^-1 and P = Kt Kh^T     gradient kernels
+//     Ssnap [D][D] chunk-start state, Usave [64][D] (op)        state pass (save)
+//     dSsnap [D][D] chunk-end state gradient, dUsave [64][D],
+//     dUsaveT [D][64] (op)                                      reverse pass
+//     gQt, gKt, gKb [64][D], gA, gP [64][64], gGam [D] (fp32)  gradients w.r.t.
+//       Qt, Kt, Kb, A, P and gamma, passed to the gate-gradient kernel
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;
     float* gam;
     void *AT, *Kb, *QtT, *WT;
-    float* Nw;  // N = (I + L)^-1, [64][64] fp32 (backward)
-    void *Ssnap, *Usave, *dSsnap, *dUsave;
+    float *Nw, *Pw;
+    void *Ssnap, *Usave, *dSsnap, *dUsave, *dUsaveT;
+    float *gQt, *gKt, *gKb, *gA, *gP, *gGam;
 };
 
 // Per-launch event timing (gdr_profile_begin/end); no-ops unless enabled.
@@ -44,5 +50,22 @@ hipError_t launch_intra(int D, int gate, bool in_f32, bool backward, int64_t B, 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
                             float* ST, void* o, bool save_for_backward, hipStream_t stream);
+
+hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                            const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
+                            hipStream_t stream);
+
+hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
+                           int64_t NC, float scale, const void* q, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* dO,
+                           const void* dh, const float* lam, void* dv, float* dbeta,
+                           const ChunkWs& ws, hipStream_t stream);
+
+hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
+                            int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
+                            void* dk, float* dalpha, const ChunkWs& ws, hipStream_t stream);
+
+hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
+                            float* dlam, float* partial, int64_t nseg, hipStream_t stream);
 
 }  // namespace gdr

@@ -78,6 +78,25 @@ __device__ __forceinline__ void load_chunk(ChunkFrags<D, IN_F32>& f, const Chunk
 }
 
 template <typename OpT>
+__device__ __forceinline__ void store8(OpT* dst, const OpT (&v)[8]) {
+    if constexpr (sizeof(OpT) == 2) {
+        half8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = v[e];
+        *reinterpret_cast<half8*>(dst) = h;
+    } else {
+        float4v a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = v[e];
+            b[e] = v[4 + e];
+        }
+        reinterpret_cast<float4v*>(dst)[0] = a;
+        reinterpret_cast<float4v*>(dst)[1] = b;
+    }
+}
+
+template <typename OpT>
 __device__ __forceinline__ void st4(OpT* dst, const float4v& v) {
     if constexpr (sizeof(OpT) == 2) {
         half4 h;
@@ -104,13 +123,17 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
     const int64_t ch = bh * NC + c;
 
     if constexpr (SAVE) {
-        // chunk-start state snapshot [D][D] in operand precision
-        OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D;
+        // chunk-start state snapshot [D][D] in operand precision, fragment order
+        // (rows d, k = value column): eight consecutive columns per thread,
+        // gathered from the transposed LDS copy
+        const int t = wid * WAVE + (l16 + 16 * g4);
+        if (t < 2 * D) {
+            const int d = t >> 1, hf = t & 1;
+            OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf);
+            OpT vals[8];
 #pragma unroll
-        for (int m = 0; m < SRT; ++m) {
-            const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) snap[(d0 + e) * D + j0 + l16] = from_f32<OpT>(S[m][e]);
+            for (int e = 0; e < 8; ++e) vals[e] = s_S[(8 * hf + e) * LDS_S + d];
+            store8(snap, vals);
         }
     }
 
@@ -126,12 +149,19 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[e] = to_f32(cur.ut[e]) - u[e];
     st4<OpT>(s_U + l16 * LDS_U + 16 * wid + 4 * g4, u);
-    if constexpr (SAVE) {
-        OpT* us = reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + j0 + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) us[(16 * wid + 4 * g4 + e) * D] = from_f32<OpT>(u[e]);
-    }
     __syncthreads();
+    if constexpr (SAVE) {
+        // U of this chunk, fragment order (rows position, k = value column)
+        const int t = wid * WAVE + (l16 + 16 * g4);
+        if (t < 2 * CHUNK) {
+            const int pos = t >> 1, hf = t & 1;
+            OpT* us = reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf);
+            OpT vals[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = s_U[(8 * hf + e) * LDS_U + pos];
+            store8(us, vals);
+        }
+    }
 
     Frag<OpT> fu0, fu1;
     fu0.load(s_U + l16 * LDS_U + 8 * g4);

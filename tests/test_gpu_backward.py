@@ -1,0 +1,156 @@
+"""GPU parity of gdr_backward against the fp64 oracle's adjoint.
+
+Gradients are compared per tensor as max|x - y| / max|y| (y the oracle), with
+the tolerances of gpu_util.TOL.  Small cases span several chunks and a ragged
+tail; the 350M-layer workload (B=8, T=4096, H=8, d=128) runs on the GPU in full
+and is checked on sampled (batch, head) slabs, which the oracle recomputes
+completely (slabs are independent)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_37_amd as gdr
+import gdr_inputs
+import oracle
+from gpu_util import TORCH, announce, inputs_to_dev, rel, to_dev, tol
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dalpha", "dS0")
+
+
+def gpu_backward(t, dST=None, scale=1.0, dh=None, lam=None, want_dlam=False):
+    g = gdr.backward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["S0"], t["dO"], dST, scale=scale,
+                     out_dtype=torch.float32, dh=dh, clvr_scale=lam, want_dclvr_scale=want_dlam)
+    torch.cuda.synchronize()
+    return g
+
+
+def compare(inp, g, dST=None, scale=1.0, heads=None):
+    errs = {}
+    if heads is None:
+        ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["alpha"], inp["S0"], inp["dO"],
+                              dST, scale=scale)
+        for n in NAMES:
+            if ref[n] is not None:
+                errs[n] = rel(g[n], ref[n])
+        return errs
+    for (b, h) in heads:
+        sl = lambda a: None if a is None else a[b:b + 1, :, h:h + 1]  # noqa: E731
+        S0 = None if inp["S0"] is None else inp["S0"][b:b + 1, h:h + 1]
+        dS = None if dST is None else dST[b:b + 1, h:h + 1]
+        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["alpha"]), S0,
+                              sl(inp["dO"]), dS, scale=scale)
+        for n in NAMES:
+            if ref[n] is None:
+                continue
+            x = g[n][b:b + 1, h:h + 1] if n == "dS0" else g[n][b:b + 1, :, h:h + 1]
+            errs[n] = max(errs.get(n, 0.0), rel(x, ref[n]))
+    return errs
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("s0", [False, True])
+def test_backward_parity_bf16(gate, d, s0):
+    announce("backward bf16 gate=%s d=%d s0=%s" % (gate, d, s0))
+    inp = gdr_inputs.make(B=2, T=200, H=2, d=d, gate=gate, dtype="bf16", seed=300 + d, s0=s0, bwd=True)
+    dST = (0.1 * np.random.default_rng(301).standard_normal((2, 2, d, d))).astype(np.float32) if s0 else None
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t, None if dST is None else to_dev(dST))
+    errs = compare(inp, g, dST)
+    assert max(errs.values()) < 2e-3, errs
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_backward_parity_fp32(gate):
+    announce("backward fp32 gate=%s" % gate)
+    inp = gdr_inputs.make(B=1, T=150, H=2, d=64, gate=gate, dtype="fp32", seed=310, s0=True, bwd=True)
+    t = inputs_to_dev(inp, "fp32")
+    g = gpu_backward(t, scale=0.8)
+    errs = compare(inp, g, scale=0.8)
+    assert max(errs.values()) < 1e-5, errs
+
+
+def test_backward_deltanet_fp32_config_shape():
+    """The DeltaNet fp32 case (B=1, H=2, T=256, d=64), with upstream gradient."""
+    announce("backward c1")
+    inp, cfg = gdr_inputs.make_config("c1", bwd=True)
+    t = inputs_to_dev(inp, "fp32")
+    g = gpu_backward(t)
+    errs = compare(inp, g)
+    assert max(errs.values()) < 1e-5, errs
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_backward_ragged_lengths(T):
+    announce("backward ragged T=%d" % T)
+    inp = gdr_inputs.make(B=1, T=T, H=2, d=128, gate="channel", dtype="bf16", seed=320 + T, s0=True, bwd=True)
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t)
+    errs = compare(inp, g)
+    assert max(errs.values()) < 2e-3, errs
+
+
+def test_backward_empty_sequence_passes_state_gradient():
+    announce("backward T=0")
+    inp = gdr_inputs.make(B=1, T=0, H=2, d=64, gate="channel", dtype="bf16", seed=330, s0=True, bwd=True)
+    dST = np.random.default_rng(331).standard_normal((1, 2, 64, 64)).astype(np.float32)
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t, to_dev(dST))
+    assert torch.equal(g["dS0"].cpu(), torch.from_numpy(dST))
+
+
+@pytest.mark.parametrize("recipe", ["sigmoid(N(-1,1))", "uniform[1e-6,1e-3]"])
+def test_backward_strong_gates(recipe):
+    announce("backward strong gates %s" % recipe)
+    inp = gdr_inputs.make(B=1, T=512, H=2, d=128, gate="channel", dtype="bf16", seed=340, s0=True, bwd=True,
+                          alpha_recipe=recipe)
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t)
+    errs = compare(inp, g)
+    # The chunked backward reaches dalpha through the gradient with respect to
+    # log(alpha): dalpha = d/dlog(alpha) / alpha.  Where alpha is ~1e-6 the
+    # division amplifies the absolute error of that (well-conditioned) quantity a
+    # million-fold, so the gate gradient is checked as alpha * dalpha.
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["alpha"], inp["S0"], inp["dO"])
+    dlog = g["dalpha"].cpu().double().numpy() * inp["alpha"]
+    errs["alpha*dalpha"] = rel(dlog, ref["dalpha"] * inp["alpha"])
+    del errs["dalpha"]
+    assert max(errs.values()) < 2e-3, errs
+
+
+def test_backward_clvr_terms():
+    """dv gains lam * dh; dlam = sum over tokens of dh * v."""
+    announce("backward clvr")
+    inp = gdr_inputs.make(B=2, T=130, H=2, d=128, gate="channel", dtype="bf16", seed=350, bwd=True, clvr=True)
+    r = np.random.default_rng(351)
+    lam = r.standard_normal(256).astype(np.float32)
+    dh = gdr_inputs.round_bf16(r.standard_normal((2, 130, 256)))
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t, dh=to_dev(dh, torch.bfloat16), lam=to_dev(lam), want_dlam=True)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["alpha"], None, inp["dO"])
+    dv_c, dlam = oracle.clvr_backward(dh, inp["v"], lam)
+    assert rel(g["dv"], ref["dv"] + dv_c) < 2e-3
+    assert rel(g["dclvr_scale"], dlam) < 1e-5
+
+
+def test_backward_is_deterministic():
+    announce("backward determinism")
+    inp = gdr_inputs.make(B=1, T=300, H=2, d=128, gate="channel", dtype="bf16", seed=360, s0=True, bwd=True)
+    t = inputs_to_dev(inp, "bf16")
+    g1 = gpu_backward(t)
+    g2 = gpu_backward(t)
+    for n in NAMES:
+        assert torch.equal(g1[n], g2[n]), n
+
+
+def test_backward_full_layer_sampled_slabs():
+    """350M-layer shape: B=8, T=4096, H=8, d=128, KDA, bf16; the full backward
+    runs on the GPU, two (batch, head) slabs are recomputed by the oracle."""
+    announce("backward full c4")
+    inp, cfg = gdr_inputs.make_config("c4")
+    t = inputs_to_dev({n: a for n, a in inp.items() if n not in ("h", "lam")}, "bf16")
+    g = gpu_backward(t)
+    errs = compare(inp, g, heads=[(0, 0), (7, 5)])
+    assert max(errs.values()) < 2e-3, errs
