@@ -35,10 +35,12 @@ struct GLinLayout {
     static constexpr int DW = KT + CHUNK * LDR * OPB;      // dW [64][LDR]
     static constexpr int DWT = DW + CHUNK * LDR * OPB;     // dW^T [D][LDC]
     static constexpr int TT = DWT + D * LDC * OPB;         // T^T [64][LDC]
-    static constexpr int NF = TT + CHUNK * LDC * OPB;      // N [64][64] fp32
-    static constexpr int DTF = NF + CHUNK * CHUNK * 4;     // dT [64][64] fp32
-    static constexpr int BYTES = DTF + CHUNK * CHUNK * 4;
-    static_assert(CHUNK * CHUNK * 4 <= 2 * CHUNK * LDR * OPB, "Y must fit in the Kt and dW regions");
+    static constexpr int LDF = CHUNK + 4;                  // fp32 row stride (16-byte pad)
+    static constexpr int NF = TT + CHUNK * LDC * OPB;      // N [64][LDF] fp32
+    static constexpr int DTF = NF + CHUNK * LDF * 4;       // dT [64][LDF] fp32, later Y
+    static constexpr int BYTES = DTF + CHUNK * LDF * 4;
+    // phase 3 reuses the Kt..T^T region (dead by then) for N^T and dT^T (fp32)
+    static_assert(2 * CHUNK * LDF * 4 <= NF, "N^T and dT^T must fit below N");
 };
 
 template <typename InT, typename OpT>
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
-    constexpr int NT = L::NT, NW = L::NW, LDR = L::LDR, LDC = L::LDC, RPP = 16;
+    constexpr int NT = L::NT, NW = L::NW, LDR = L::LDR, LDC = L::LDC, LDF = L::LDF, RPP = 16;
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __shared__ float s_tot[4][D];
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     __shared__ float s_db[CHUNK];
 
     OpT* KT = reinterpret_cast<OpT*>(smem + L::KT);
-    float* YF = reinterpret_cast<float*>(smem + L::KT);
+    float* NTF = reinterpret_cast<float*>(smem + L::KT);                    // phase 3: N^T
+    float* DTT = reinterpret_cast<float*>(smem + L::KT + CHUNK * LDF * 4);  // phase 3: dT^T
     OpT* DWs = reinterpret_cast<OpT*>(smem + L::DW);
     OpT* DWT = reinterpret_cast<OpT*>(smem + L::DWT);
     OpT* TT = reinterpret_cast<OpT*>(smem + L::TT);
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    for (int e = tid; e < CHUNK * CHUNK; e += NT) NF[e] = ws.Nw[ch * CHUNK * CHUNK + e];
+    for (int e = tid; e < CHUNK * CHUNK; e += NT) NF[(e / CHUNK) * LDF + e % CHUNK] = ws.Nw[ch * CHUNK * CHUNK + e];
     __syncthreads();
     if constexpr (GATE == GATE_CHANNEL) {
         float carry = 0.f;
@@ -161,100 +164,89 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     // T^T[i][r] = N[r][i] beta_i
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, i = e % CHUNK;
-        TT[i * LDC + r] = from_f32<OpT>(NF[e] * s_beta[i]);
+        TT[i * LDC + r] = from_f32<OpT>(NF[r * LDF + i] * s_beta[i]);
     }
     __syncthreads();
 
     // ---------------- phase 1: products contracting over the value dimension ----------------
-    // jobs: dQt (4 x D/16 tiles), dW (same), dKb (same), dA (10 lower tiles), dT1 (16)
+    // Wave w owns row tile rt = w % 4 (positions 16rt..16rt+15) and every
+    // NHALF-th column tile; its A fragments (dO, dU, U rows) are loaded once.
+    constexpr int NHALF = NW / 4;
+    const int rt = wid & 3, half = wid >> 2;
     {
-        constexpr int NDT = D / 16;
-        constexpr int NJ = 3 * 4 * NDT + 10 + 16;
+        constexpr int KQ = D / 32;
         const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
         const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
         const OpT* Us = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
         const OpT* dUs = reinterpret_cast<const OpT*>(ws.dUsave) + ch * CHUNK * D;
-        for (int job = wid; job < NJ; job += NW) {
-            int kind, rt, nt;
-            if (job < 3 * 4 * NDT) {
-                kind = job / (4 * NDT);
-                rt = (job % (4 * NDT)) / NDT;
-                nt = job % NDT;
-            } else if (job < 3 * 4 * NDT + 10) {
-                kind = 3;
-                const int t = job - 3 * 4 * NDT;  // lower tiles (rt, nt <= rt)
-                rt = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-                nt = t - (rt * (rt + 1)) / 2;
-            } else {
-                kind = 4;
-                const int t = job - 3 * 4 * NDT - 10;
-                rt = t / 4;
-                nt = t % 4;
-            }
-            float4v acc = zero4();
-            const int arow = 16 * rt + l16;  // row of the A operand for this lane
-            const int brow = 16 * nt + l16;  // row of the B operand (column of the result)
-            const int64_t arow_g = base + (arow < nvalid ? arow : nvalid - 1) * tokstride;
-            const int64_t brow_g = base + (brow < nvalid ? brow : nvalid - 1) * tokstride;
-            const bool aok = arow < nvalid, bok = brow < nvalid;
+        const int arow = 16 * rt + l16;
+        const bool aok = arow < nvalid;
+        const int64_t arow_g = base + (aok ? arow : nvalid - 1) * tokstride;
+        Frag<OpT> aO[KQ], aDU[KQ], aU[KQ];
 #pragma unroll
-            for (int kq = 0; kq < D / 32; ++kq) {
-                Frag<OpT> fa, fb;
-                const int kofs = 32 * kq + 8 * g4;
-                const int fo_a = ((rt * (D / 32) + kq) * 64 + lane) * 8;
-                const int fo_b = ((nt * (D / 32) + kq) * 64 + lane) * 8;
-                if (kind == 0 || kind == 3) {  // A = dO rows
-                    load_frag_in<InT, OpT>(fa, dO + arow_g + kofs);
-                    if (!aok) fa.zero();
-                } else if (kind == 1 || kind == 4) {  // A = dU rows
-                    fa.load(dUs + fo_a);
-                } else {  // A = U rows
-                    fa.load(Us + fo_a);
-                }
-                if (kind == 0 || kind == 1) fb.load(Ss + fo_b);        // B = S rows (d)
-                else if (kind == 2) fb.load(dSs + fo_b);                // B = dS' rows (d)
-                else if (kind == 3) fb.load(Us + fo_b);                 // B = U rows (i)
-                else {                                                   // B = V rows (i)
-                    load_frag_in<InT, OpT>(fb, v + brow_g + kofs);
-                    if (!bok) fb.zero();
-                }
-                mma(fa, fb, acc);
+        for (int kq = 0; kq < KQ; ++kq) {
+            load_frag_in<InT, OpT>(aO[kq], dO + arow_g + 32 * kq + 8 * g4);
+            if (!aok) aO[kq].zero();
+            aDU[kq].load(dUs + ((rt * KQ + kq) * 64 + lane) * 8);
+            aU[kq].load(Us + ((rt * KQ + kq) * 64 + lane) * 8);
+        }
+        const int r_ = 16 * rt + 4 * g4;  // result rows r_ + e of this lane
+        // d tiles: dQt = dO S^T, dW = -dU S^T, dKb = U dS'^T
+#pragma unroll
+        for (int nt = half; nt < D / 16; nt += NHALF) {
+            Frag<OpT> bS[KQ], bD[KQ];
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
+                bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
             }
-            const int r_ = 16 * rt + 4 * g4;  // result rows r_ + e, column 16 nt + l16
+            float4v aq = zero4(), aw = zero4(), ak = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                mma(aO[kq], bS[kq], aq);
+                mma(aDU[kq], bS[kq], aw);
+                mma(aU[kq], bD[kq], ak);
+            }
             const int col = 16 * nt + l16;
-            if (kind == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ws.gQt[ch * CHUNK * D + (r_ + e) * D + col] = scale * acc[e];
-            } else if (kind == 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const OpT w = from_f32<OpT>(-acc[e]);
-                    DWs[(r_ + e) * LDR + col] = w;
-                    DWT[col * LDC + r_ + e] = w;
-                }
-            } else if (kind == 2) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ws.gKb[ch * CHUNK * D + (r_ + e) * D + col] = acc[e];
-            } else if (kind == 3) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ws.gA[ch * CHUNK * CHUNK + (r_ + e) * CHUNK + col] = (col <= r_ + e) ? scale * acc[e] : 0.f;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) DTF[(r_ + e) * CHUNK + col] = acc[e];
+            for (int e = 0; e < 4; ++e) {
+                ws.gQt[ch * CHUNK * D + (r_ + e) * D + col] = scale * aq[e];
+                ws.gKb[ch * CHUNK * D + (r_ + e) * D + col] = ak[e];
+                const OpT w = from_f32<OpT>(-aw[e]);
+                DWs[(r_ + e) * LDR + col] = w;
+                DWT[col * LDC + r_ + e] = w;
             }
         }
-        // dA is lower triangular: zero the six upper tiles
-        for (int e = tid; e < 6 * 256; e += NT) {
-            const int tile = e / 256, w = e % 256;
-            const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-            const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-            ws.gA[ch * CHUNK * CHUNK + (16 * R + w / 16) * CHUNK + 16 * I + w % 16] = 0.f;
+        // position tiles: dA = tril(dO U^T) (scaled), dT1 = dU V^T
+#pragma unroll
+        for (int it = half; it < 4; it += NHALF) {
+            const int brow = 16 * it + l16;
+            const bool bok = brow < nvalid;
+            const int64_t brow_g = base + (bok ? brow : nvalid - 1) * tokstride;
+            Frag<OpT> bU[KQ], bV[KQ];
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                bU[kq].load(Us + ((it * KQ + kq) * 64 + lane) * 8);
+                load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
+                if (!bok) bV[kq].zero();
+            }
+            float4v aa = zero4(), at = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                if (it <= rt) mma(aO[kq], bU[kq], aa);
+                mma(aDU[kq], bV[kq], at);
+            }
+            const int col = 16 * it + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ws.gA[ch * CHUNK * CHUNK + (r_ + e) * CHUNK + col] = (col <= r_ + e) ? scale * aa[e] : 0.f;
+                DTF[(r_ + e) * LDF + col] = at[e];
+            }
         }
         // dgamma_d = sum_j dS'[d][j] S[d][j]
         if (tid < D) {
             float s = 0.f;
-#pragma unroll 4
+#pragma unroll
             for (int j8 = 0; j8 < D / 8; ++j8) {
                 Frag<OpT> fs, fd;
                 fs.load(Ss + frag_off<D>(tid, 8 * j8));
@@ -269,95 +261,114 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
 
     // ---------------- phase 2: dT += dW Kt^T, dKt = T^T dW, dV = T^T dU ----------------
     {
-        constexpr int NDT = D / 16;
-        constexpr int NJ = 16 + 2 * 4 * NDT;
         const OpT* dUT = reinterpret_cast<const OpT*>(ws.dUsaveT) + ch * D * CHUNK;
         OutT* dv = reinterpret_cast<OutT*>(dv_);
         const InT* dh = reinterpret_cast<const InT*>(dh_);
-        for (int job = wid; job < NJ; job += NW) {
+        const int r_ = 16 * rt + 4 * g4;
+        Frag<OpT> aT[2];
+        aT[0].load(TT + (16 * rt + l16) * LDC + 8 * g4);
+        aT[1].load(TT + (16 * rt + l16) * LDC + 32 + 8 * g4);
+#pragma unroll
+        for (int ct = half; ct < D / 16; ct += NHALF) {
+            Frag<OpT> bW[2], bU[2];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                bW[kq].load(DWT + (16 * ct + l16) * LDC + 32 * kq + 8 * g4);
+                bU[kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
+            }
+            float4v ak = zero4(), av = zero4();
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                mma(aT[kq], bW[kq], ak);
+                mma(aT[kq], bU[kq], av);
+            }
+            const int col = 16 * ct + l16;
+            const float lm = (dh && lam) ? lam[h * D + col] : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = ak[e];
+                const int r = r_ + e;
+                if (r < nvalid) {
+                    const int64_t idx = base + r * tokstride + col;
+                    float g = av[e];
+                    if (dh) g = __builtin_fmaf(lm, to_f32(dh[idx]), g);  // CLVR: h += lam v
+                    dv[idx] = from_f32<OutT>(g);
+                }
+            }
+        }
+#pragma unroll
+        for (int it = half; it < 4; it += NHALF) {
             float4v acc = zero4();
-            int kind, rt, nt;
-            if (job < 16) {
-                kind = 0;
-                rt = job / 4;
-                nt = job % 4;
 #pragma unroll
-                for (int kq = 0; kq < D / 32; ++kq) {
-                    Frag<OpT> fa, fb;
-                    fa.load(DWs + (16 * rt + l16) * LDR + 32 * kq + 8 * g4);
-                    fb.load(KT + (16 * nt + l16) * LDR + 32 * kq + 8 * g4);
-                    mma(fa, fb, acc);
-                }
-            } else {
-                kind = (job - 16) < 4 * NDT ? 1 : 2;
-                const int t = (job - 16) % (4 * NDT);
-                rt = t / NDT;
-                nt = t % NDT;
-#pragma unroll
-                for (int kq = 0; kq < 2; ++kq) {
-                    Frag<OpT> fa, fb;
-                    fa.load(TT + (16 * rt + l16) * LDC + 32 * kq + 8 * g4);
-                    if (kind == 1) fb.load(DWT + (16 * nt + l16) * LDC + 32 * kq + 8 * g4);
-                    else fb.load(dUT + ((nt * 2 + kq) * 64 + lane) * 8);
-                    mma(fa, fb, acc);
-                }
+            for (int kq = 0; kq < D / 32; ++kq) {
+                Frag<OpT> fa, fb;
+                fa.load(DWs + (16 * rt + l16) * LDR + 32 * kq + 8 * g4);
+                fb.load(KT + (16 * it + l16) * LDR + 32 * kq + 8 * g4);
+                mma(fa, fb, acc);
             }
-            const int r_ = 16 * rt + 4 * g4;
-            const int col = 16 * nt + l16;
-            if (kind == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) DTF[(r_ + e) * CHUNK + col] += acc[e];
-            } else if (kind == 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = acc[e];
-            } else {
-                const float lm = (dh && lam) ? lam[h * D + col] : 1.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = r_ + e;
-                    if (r < nvalid) {
-                        const int64_t idx = base + r * tokstride + col;
-                        float g = acc[e];
-                        if (dh) g = __builtin_fmaf(lm, to_f32(dh[idx]), g);  // CLVR: h += lam v
-                        dv[idx] = from_f32<OutT>(g);
-                    }
-                }
-            }
+            for (int e = 0; e < 4; ++e) DTF[(r_ + e) * LDF + 16 * it + l16] += acc[e];
         }
     }
     __syncthreads();
 
-    // ---------------- phase 3: solve adjoint (fp32) ----------------
-    // Y = N^T dT  (N lower triangular: Y[a][x] = sum_{r >= a} N[r][a] dT[r][x])
+    // ---------------- phase 3: solve adjoint on fp32 matrix cores ----------------
+    // Y = N^T dT and dL = -strict_tril(Y T^T), T = N diag(beta)
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
-        const int a = e / CHUNK, x = e % CHUNK;
-        float s = 0.f;
-        for (int r = a; r < CHUNK; ++r) s += NF[r * CHUNK + a] * DTF[r * CHUNK + x];
-        YF[e] = s;
+        const int r = e / CHUNK, x = e % CHUNK;
+        NTF[x * LDF + r] = NF[r * LDF + x];
+        DTT[x * LDF + r] = DTF[r * LDF + x];
     }
     __syncthreads();
-    // dL[a][x] = -sum_{y <= x} Y[a][y] T[x][y] for x < a, T[x][y] = N[x][y] beta_y;
-    // dP = beta_a dL; dbeta_a = Y[a][a] + sum_x dL[a][x] P[a][x]
+    for (int tile = wid; tile < 16; tile += NW) {  // Y tile (at, xt), k = r
+        const int at = tile / 4, xt = tile % 4;
+        float4v acc = zero4();
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            Frag<float> fa, fb;
+            fa.load(NTF + (16 * at + l16) * LDF + 32 * kq + 8 * g4);
+            fb.load(DTT + (16 * xt + l16) * LDF + 32 * kq + 8 * g4);
+            mma(fa, fb, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DTF[(16 * at + 4 * g4 + e) * LDF + 16 * xt + l16] = acc[e];  // Y
+    }
+    __syncthreads();
+    float* YF = DTF;
+    float* CB = NTF;  // dL . P contributions [64][LDF] (N^T is no longer needed)
     {
         const float* Pw = ws.Pw + ch * CHUNK * CHUNK;
-        for (int e0 = 0; e0 < CHUNK * CHUNK; e0 += NT) {
-            const int e = e0 + tid;
-            const int a = e / CHUNK, x = e % CHUNK;  // a is uniform across the wave
-            float dl = 0.f;
-            if (x < a) {
-                float s = 0.f;
-                for (int y = 0; y <= x; ++y) s += YF[a * CHUNK + y] * NF[x * CHUNK + y] * s_beta[y];
-                dl = -s;
-            }
-            ws.gP[ch * CHUNK * CHUNK + e] = s_beta[a] * dl;
-            float contrib = dl * Pw[e];
+        for (int tile = wid; tile < 16; tile += NW) {  // dL tile (at, xt), k = c
+            const int at = tile / 4, xt = tile % 4;
+            float4v acc = zero4();
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) contrib += __shfl_xor(contrib, off);
-            if (lane == 0) s_db[a] = contrib;  // one wave covers one row a
+            for (int kq = 0; kq < 2; ++kq) {
+                Frag<float> fa, fb;
+                fa.load(YF + (16 * at + l16) * LDF + 32 * kq + 8 * g4);
+                const int c0 = 32 * kq + 8 * g4;
+                fb.load(NF + (16 * xt + l16) * LDF + c0);  // T[x][c] = N[x][c] beta_c
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fb.v[e] *= s_beta[c0 + e];
+                mma(fa, fb, acc);
+            }
+            const int x = 16 * xt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = 16 * at + 4 * g4 + e;
+                const float dl = (x < a) ? -acc[e] : 0.f;
+                ws.gP[ch * CHUNK * CHUNK + a * CHUNK + x] = s_beta[a] * dl;
+                CB[a * LDF + x] = dl * Pw[a * CHUNK + x];
+            }
         }
     }
     __syncthreads();
-    if (tid < nvalid) dbeta[(b * T + t0 + tid) * H + h] = YF[tid * CHUNK + tid] + s_db[tid];
+    if (tid < CHUNK) {  // fixed-order row sums: deterministic
+        float sdb = YF[tid * LDF + tid];
+        for (int x = 0; x < CHUNK; ++x) sdb += CB[tid * LDF + x];
+        s_db[tid] = sdb;
+    }
+    __syncthreads();
+    if (tid < nvalid) dbeta[(b * T + t0 + tid) * H + h] = s_db[tid];
 }
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
