@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="end with three 1 GiB device copies (reference kernel for HBM counters)")
     return p.parse_args()
 
 
@@ -68,6 +70,66 @@ class KernelTimer:
         if n < 0:
             raise RuntimeError("gdr_profile_end failed")
         return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n)}
+
+
+# Path tensors each kernel must touch at least once (bytes per token-head, KDA,
+# bf16 q/k/v/dO/h and bf16 outputs, fp32 beta/alpha and their gradients).  A
+# tensor read by two kernels counts for both; workspace intermediates never count.
+PER_TH_BYTES = {
+    "intra_fwd": 3 * 256 + 4 + 512 + 2 * 256,          # q,k,v,beta,alpha read; h read+write (CLVR)
+    "state_fwd": 256,                                  # o written
+    "intra_bwd": 3 * 256 + 4 + 512,                    # q,k,v,beta,alpha read
+    "state_fwd_save": 0,                               # intermediates only
+    "state_bwd": 256,                                  # dO read
+    "grad_lin": 256 + 4 + 512 + 256 + 256 + 256 + 256 + 4,  # k,beta,alpha,v,dO,dh read; dv,dbeta written
+    "grad_gate": 2 * 256 + 512 + 2 * 256 + 512,        # q,k,alpha read; dq,dk,dalpha written
+    "clvr_dlam": 2 * 256,                              # dh, v read
+}
+# Per (b,h) state tensors (fp32 d x d): S_T written by the forward state pass.
+PER_BH_STATE = {"state_fwd": 1}
+
+# Kernel -> HIP sources whose text defines it (for matching stored counter runs).
+KERNEL_SOURCES = {
+    "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"],
+    "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"],
+    "state_bwd": ["gdr_bwd_state.hip"],
+    "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
+    "decode": ["gdr_decode.hip"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kda_t32k.txt")
+
+
+def kernel_alg_bytes(B, T, H, d):
+    th = B * T * H
+    out = {n: th * b * d // 128 for n, b in PER_TH_BYTES.items()}
+    for n, k in PER_BH_STATE.items():
+        out[n] += k * B * H * d * d * 4
+    return out
+
+
+def kernel_source_digest(name):
+    import hashlib
+    hsh = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_37_amd", "csrc")
+    for f in KERNEL_SOURCES[name] + ["gdr_common.hpp", "gdr_launch.hpp"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    scaled by the same counters' reading for a copy of known size; None when no
+    run is stored or the kernel's source has changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = kernel_source_digest(name)
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) >= 5 and f[0] == "traffic" and f[1] == name:
+                return int(float(f[3]) + float(f[4])) if f[2] == digest else None
+    return None
 
 
 def main():
@@ -109,7 +171,8 @@ def main():
         try:
             nb = gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf, backward=True)
             ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
-            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam)
+            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam,
+                         want_dclvr_scale=True)
             torch.cuda.synchronize()
         except gdr.GdrError as e:
             if e.code != 2:
@@ -121,7 +184,8 @@ def main():
         gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f,
                     output_final_state=True)
         if do_bwd:
-            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam)
+            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam,
+                         want_dclvr_scale=True)
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -149,23 +213,25 @@ def main():
     fwd_us = sum(kernels[n]["avg_us"] for n in kernels if n in ("intra_fwd", "state_fwd"))
     log("step %.3f ms; kernels %s" % (ms_step, json.dumps(kernels)))
 
-    # algorithmic bytes (per token-head, KDA, bf16 inputs): q,k,v 3*256 + beta 4 +
-    # alpha 512 read, o 256 written -> 1540; CLVR reads and writes h (2*256)
+    # Algorithmic bytes per token-head (KDA, bf16 q/k/v/dO/outputs, fp32 beta/alpha):
+    # q,k,v 3*256 + beta 4 + alpha 512 read, o 256 written -> 1540; CLVR reads and
+    # writes h (2*256).
     th = B * T * H
     fwd_bytes = th * (1540 + 512)
     fwd_flops = th * (5 * 64 * d + 6 * d * d + 64 * 64 / 3)
-    # dominant kernel and its algorithmic traffic
+    kbytes = kernel_alg_bytes(B, T, H, d)
+    for n, kr in kernels.items():
+        nb = kbytes.get(n)
+        kr["alg_bytes"] = nb
+        kr["alg_GBs"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9, 1)
+        kr["hbm_frac"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    # dominant kernel: the largest share of the step's time
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
-    per_kernel_bytes = {
-        # compulsory reads of q,k,v,beta,alpha and the CLVR read+write of h
-        "intra_fwd": th * (3 * 256 + 4 + 512 + 512),
-        # compulsory write of o (bf16)
-        "state_fwd": th * 256,
-    }
-    dom_bytes = per_kernel_bytes.get(dom, fwd_bytes)
-    achieved = dom_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    achieved = kernels[dom]["alg_GBs"]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom), "alg_bytes_per_launch": kernels[dom]["alg_bytes"],
+                "avg_us": round(kernels[dom]["avg_us"], 2)}
 
     # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
     dc = gdr_inputs.DECODE_CONFIG
@@ -240,10 +306,20 @@ def main():
                     "alg_TFLOPs": round(fwd_flops / (fwd_us * 1e-6) / 1e12, 2),
                     "hbm_frac": round(fwd_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "mfma_frac": round(fwd_flops / (fwd_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4)},
-        "kernels_us": {n: round(kernels[n]["avg_us"], 2) for n in kernels},
+        "kernels": {n: {"avg_us": round(kr["avg_us"], 2), "alg_GBs": kr["alg_GBs"], "hbm_frac": kr["hbm_frac"]}
+                    for n, kr in kernels.items()},
         "decode": decode,
     }
     print(json.dumps(out), flush=True)
+
+    if args.copy_calibration:
+        # A plain copy of known size: 1 GiB read + 1 GiB written per launch.
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB copies done")
 
 
 if __name__ == "__main__":
