@@ -53,6 +53,11 @@ def rel(x, y):
     return float(np.abs(x - y).max() / (den if den > 0 else 1.0))
 
 
+def report(**errs):
+    """Prints the measured errors of a case (shown with pytest -s)."""
+    print("[gpu-err] " + " ".join("%s=%.3e" % (k, float(v)) for k, v in errs.items()), flush=True)
+
+
 def announce(msg):
     print("[gpu-case] " + msg, flush=True)
 

@@ -12,7 +12,7 @@ import torch
 import gated_delta_rule_37_amd as gdr
 import gdr_inputs
 import oracle
-from gpu_util import TORCH, announce, inputs_to_dev, rel, to_dev, tol
+from gpu_util import TORCH, announce, inputs_to_dev, rel, report, to_dev, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,7 @@ def test_backward_parity_bf16(gate, d, s0):
     t = inputs_to_dev(inp, "bf16")
     g = gpu_backward(t, None if dST is None else to_dev(dST))
     errs = compare(inp, g, dST)
+    report(**errs)
     assert max(errs.values()) < 2e-3, errs
 
 
@@ -69,6 +70,7 @@ def test_backward_parity_fp32(gate):
     t = inputs_to_dev(inp, "fp32")
     g = gpu_backward(t, scale=0.8)
     errs = compare(inp, g, scale=0.8)
+    report(**errs)
     assert max(errs.values()) < 1e-5, errs
 
 
@@ -79,6 +81,7 @@ def test_backward_deltanet_fp32_config_shape():
     t = inputs_to_dev(inp, "fp32")
     g = gpu_backward(t)
     errs = compare(inp, g)
+    report(**errs)
     assert max(errs.values()) < 1e-5, errs
 
 
@@ -89,6 +92,7 @@ def test_backward_ragged_lengths(T):
     t = inputs_to_dev(inp, "bf16")
     g = gpu_backward(t)
     errs = compare(inp, g)
+    report(**errs)
     assert max(errs.values()) < 2e-3, errs
 
 
@@ -117,6 +121,7 @@ def test_backward_strong_gates(recipe):
     dlog = g["dalpha"].cpu().double().numpy() * inp["alpha"]
     errs["alpha*dalpha"] = rel(dlog, ref["dalpha"] * inp["alpha"])
     del errs["dalpha"]
+    report(**errs)
     assert max(errs.values()) < 2e-3, errs
 
 
@@ -153,4 +158,5 @@ def test_backward_full_layer_sampled_slabs():
     t = inputs_to_dev({n: a for n, a in inp.items() if n not in ("h", "lam")}, "bf16")
     g = gpu_backward(t)
     errs = compare(inp, g, heads=[(0, 0), (7, 5)])
+    report(**errs)
     assert max(errs.values()) < 2e-3, errs

@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_37_amd as gdr
 import gdr_inputs
 import oracle
-from gpu_util import TORCH, announce, rel, to_dev
+from gpu_util import TORCH, report, announce, rel, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +32,7 @@ def test_decode_parity(gate, d, in_dt, out_dt):
     eo, es = run(5, 3, d, gate, in_dt, out_dt, seed=40 + d)
     # all arithmetic is fp32 on exact inputs: fp32-level agreement, plus the
     # output rounding when o is stored in bf16
+    report(o=eo, S=es)
     assert es < 1e-5
     assert eo < (1e-5 if out_dt == "fp32" else 2.0 ** -8 + 1e-5)
 
@@ -41,6 +42,7 @@ def test_decode_full_size_256_sequences():
     slab compared."""
     cfg = gdr_inputs.DECODE_CONFIG
     eo, es = run(cfg["N"], cfg["H"], cfg["d"], cfg["gate"], "bf16", "fp32", seed=cfg["seed"])
+    report(o=eo, S=es)
     assert eo < 1e-5 and es < 1e-5
 
 

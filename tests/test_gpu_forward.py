@@ -10,7 +10,7 @@ import torch
 import gated_delta_rule_37_amd as gdr
 import gdr_inputs
 import oracle
-from gpu_util import TORCH, announce, inputs_to_dev, rel, tol
+from gpu_util import TORCH, announce, inputs_to_dev, rel, report, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,7 @@ def test_forward_parity_small(gate, d, in_dt, s0):
     announce("forward small gate=%s d=%d in=%s s0=%s" % (gate, d, in_dt, s0))
     inp = gdr_inputs.make(B=2, T=200, H=2, d=d, gate=gate, dtype=in_dt, seed=100 + d, s0=s0)
     eo, es = check(inp, in_dt)
+    report(o=eo, S=es)
     assert eo < tol(in_dt, "fp32") and es < tol(in_dt, "fp32"), (eo, es)
 
 
@@ -56,6 +57,7 @@ def test_forward_ragged_lengths(T):
     announce("forward ragged T=%d" % T)
     inp = gdr_inputs.make(B=1, T=T, H=3, d=128, gate="channel", dtype="bf16", seed=200 + T, s0=True)
     eo, es = check(inp, "bf16")
+    report(o=eo, S=es)
     assert eo < 2e-3 and es < 2e-3, (eo, es)
 
 
@@ -73,6 +75,7 @@ def test_forward_deltanet_fp32_config():
     announce("forward c1")
     inp, cfg = gdr_inputs.make_config("c1")
     eo, es = check(inp, "fp32")
+    report(o=eo, S=es)
     assert eo < 1e-5 and es < 1e-5, (eo, es)
 
 
@@ -80,6 +83,7 @@ def test_forward_bf16_output():
     announce("forward bf16 out")
     inp = gdr_inputs.make(B=1, T=300, H=2, d=128, gate="channel", dtype="bf16", seed=220, s0=True)
     eo, es = check(inp, "bf16", out_dt="bf16", scale=0.5)
+    report(o=eo, S=es)
     assert eo < tol("bf16", "bf16") and es < 2e-3, (eo, es)
 
 
@@ -91,6 +95,7 @@ def test_forward_strong_gates(recipe):
     inp = gdr_inputs.make(B=1, T=2048, H=2, d=128, gate="channel", dtype="bf16", seed=230,
                           s0=True, alpha_recipe=recipe)
     eo, es = check(inp, "bf16")
+    report(o=eo, S=es)
     assert eo < 2e-3 and es < 2e-3, (eo, es)
 
 
@@ -99,6 +104,7 @@ def test_forward_strong_gates_fp32():
     inp = gdr_inputs.make(B=1, T=300, H=2, d=64, gate="channel", dtype="fp32", seed=231,
                           s0=True, alpha_recipe="uniform[1e-6,1e-3]")
     eo, es = check(inp, "fp32")
+    report(o=eo, S=es)
     assert eo < 1e-5 and es < 1e-5, (eo, es)
 
 
@@ -108,6 +114,7 @@ def test_forward_beta_edge_values(beta):
     inp = gdr_inputs.make(B=1, T=256, H=2, d=128, gate="channel", dtype="bf16", seed=240, s0=True,
                           beta_recipe=beta)
     eo, es = check(inp, "bf16")
+    report(o=eo, S=es)
     assert eo < 2e-3 and es < 2e-3, (eo, es)
 
 
@@ -236,4 +243,5 @@ def test_forward_full_size_sampled_heads(name, heads):
     announce("forward full size %s" % name)
     inp, cfg = gdr_inputs.make_config(name)
     eo, es = check(inp, cfg["dtype"], heads=heads)
+    report(o=eo, S=es)
     assert eo < 2e-3 and es < 2e-3, (eo, es)
