@@ -120,6 +120,9 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
  *   dS0       [B,H,dk,dv] fp32, NULL = not written.
  *   dclvr_scale [H*dv] fp32, NULL = not written (requires dh_clvr).
  *   ws        at least gdr_workspace_size(desc, 1) bytes.
+ * fp32 inputs are supported at dk = dv = 64 only (the fp32 gradient kernels
+ * need more LDS than a workgroup can hold at 128); fp32 inputs with
+ * dk = dv = 128 return GDR_ERR_UNSUPPORTED.
  */
 gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, const float* S0,
