@@ -77,7 +77,9 @@ class KernelTimer:
 # tensor read by two kernels counts for both; workspace intermediates never count.
 PER_TH_BYTES = {
     "intra_fwd": 3 * 256 + 4 + 512 + 2 * 256,          # q,k,v,beta,alpha read; h read+write (CLVR)
+    "intra_train": 3 * 256 + 4 + 512 + 2 * 256,        # the same, training forward
     "state_fwd": 256,                                  # o written
+    "state_train": 256,                                # o written
     "intra_bwd": 3 * 256 + 4 + 512,                    # q,k,v,beta,alpha read
     "state_fwd_save": 0,                               # intermediates only
     "state_bwd": 256,                                  # dO read
@@ -86,12 +88,12 @@ PER_TH_BYTES = {
     "clvr_dlam": 2 * 256,                              # dh, v read
 }
 # Per (b,h) state tensors (fp32 d x d): S_T written by the forward state pass.
-PER_BH_STATE = {"state_fwd": 1}
+PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
 
 # Kernel -> HIP sources whose text defines it (for matching stored counter runs).
 KERNEL_SOURCES = {
-    "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"],
-    "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"],
+    "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"], "intra_train": ["gdr_intra.hip"],
+    "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"], "state_train": ["gdr_state.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
     "decode": ["gdr_decode.hip"],
@@ -172,11 +174,16 @@ def main():
         ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     def step():
-        gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f,
-                    output_final_state=True)
+        # training step: the forward keeps its intermediates in ws_b, the
+        # backward reads them instead of recomputing them
         if do_bwd:
-            gdr.backward(q, k, v, beta, alpha, None, dO, workspace=ws_b, dh=h, clvr_scale=lam,
-                         want_dclvr_scale=True)
+            gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_b,
+                        output_final_state=True, save_for_backward=True)
+            gdr.backward(q, k, v, beta, alpha, None, dO, dh=h, clvr_scale=lam, want_dclvr_scale=True,
+                         saved_workspace=ws_b)
+        else:
+            gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f,
+                        output_final_state=True)
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -201,8 +208,27 @@ def main():
     torch.cuda.synchronize()
     kt = timer.end()
     kernels = {n: {"launches": c, "avg_us": 1e3 * ms / c} for n, (c, ms) in kt.items()}
-    fwd_us = sum(kernels[n]["avg_us"] for n in kernels if n in ("intra_fwd", "state_fwd"))
     log("step %.3f ms; kernels %s" % (ms_step, json.dumps(kernels)))
+
+    # the inference forward alone (no intermediates kept), timed the same way
+    def fwd():
+        gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f, output_final_state=True)
+
+    fwd()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    timer.begin()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    for n, (c, ms) in timer.end().items():
+        kernels.setdefault(n, {"launches": c, "avg_us": 1e3 * ms / c})
+    log("forward %.1f us" % fwd_us)
 
     # Algorithmic bytes per token-head (KDA, bf16 q/k/v/dO/outputs, fp32 beta/alpha):
     # q,k,v 3*256 + beta 4 + alpha 512 read, o 256 written -> 1540; CLVR reads and
@@ -217,7 +243,7 @@ def main():
         kr["alg_GBs"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9, 1)
         kr["hbm_frac"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     # dominant kernel: the largest share of the step's time
-    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dom = max(kt, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
     achieved = kernels[dom]["alg_GBs"]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -60,6 +60,10 @@ def load_library():
         lib.gdr_forward_chunked.restype = ctypes.c_int
         lib.gdr_backward.argtypes = [D] + [P] * 17 + [P, SZ, P]
         lib.gdr_backward.restype = ctypes.c_int
+        lib.gdr_forward_train.argtypes = [D] + [P] * 10 + [P, SZ, P]
+        lib.gdr_forward_train.restype = ctypes.c_int
+        lib.gdr_backward_saved.argtypes = [D] + [P] * 17 + [P, SZ, P]
+        lib.gdr_backward_saved.restype = ctypes.c_int
         lib.gdr_decode_step.argtypes = [I64] * 4 + [I32] * 3 + [F32] + [P] * 7 + [P]
         lib.gdr_decode_step.restype = ctypes.c_int
         lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -149,11 +153,15 @@ def _check_inputs(q, k, v, beta, alpha, S0):
 
 
 def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=None,
-            clvr_scale=None, output_final_state=True, workspace=None):
+            clvr_scale=None, output_final_state=True, workspace=None, save_for_backward=False):
     """Chunked forward.  Returns ``(o, S_T)`` (``S_T`` None unless requested).
 
     ``h`` ([B, T, H*dv], q's dtype) is updated in place by the CLVR epilogue
-    ``h += clvr_scale * v`` when given."""
+    ``h += clvr_scale * v`` when given.
+
+    ``save_for_backward=True`` runs the training forward: ``workspace`` (a uint8
+    tensor of ``workspace_size(..., backward=True)`` bytes, required) then holds
+    the intermediates that ``backward(..., saved_workspace=workspace)`` reuses."""
     B, T, H, dk, dv = _check_inputs(q, k, v, beta, alpha, S0)
     _need(h, "h", q.dtype, (B, T, H * dv))
     _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
@@ -161,19 +169,29 @@ def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=
     desc = _desc(q, v, alpha, out_dtype, scale)
     o = torch.empty((B, T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
     ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
-    need = lib.gdr_workspace_size(ctypes.byref(desc), 0)
-    if workspace is None or workspace.numel() < need:
+    need = lib.gdr_workspace_size(ctypes.byref(desc), 1 if save_for_backward else 0)
+    if save_for_backward:
+        if workspace is None:
+            raise ValueError("save_for_backward needs a workspace tensor that the backward will reuse")
+        _need(workspace, "workspace", torch.uint8)
+        if workspace.numel() < need:
+            raise ValueError("workspace has %d bytes, the training forward needs %d" % (workspace.numel(), need))
+    elif workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.gdr_forward_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                   _ptr(alpha), _ptr(S0), _ptr(o), _ptr(ST), _ptr(h),
-                                   _ptr(clvr_scale), _ptr(workspace), need, _stream(q.device)))
+    fn = lib.gdr_forward_train if save_for_backward else lib.gdr_forward_chunked
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
+              _ptr(ST), _ptr(h), _ptr(clvr_scale), _ptr(workspace), need, _stream(q.device)))
     return o, ST
 
 
 def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=None, dh=None,
-             clvr_scale=None, want_dclvr_scale=False, workspace=None):
+             clvr_scale=None, want_dclvr_scale=False, workspace=None, saved_workspace=None):
     """Gradients of :func:`forward`.  Returns a dict with ``dq, dk, dv, dbeta,
-    dalpha`` (None for DeltaNet), ``dS0`` and ``dclvr_scale`` (when asked)."""
+    dalpha`` (None for DeltaNet), ``dS0`` and ``dclvr_scale`` (when asked).
+
+    ``saved_workspace``: the workspace of a preceding ``forward(...,
+    save_for_backward=True)`` with the same inputs; the forward's intermediates
+    are then read from it instead of being recomputed."""
     B, T, H, dk, dv = _check_inputs(q, k, v, beta, alpha, S0)
     _need(dO, "dO", q.dtype, (B, T, H, dv))
     _need(dST, "dST", torch.float32, (B, H, dk, dv))
@@ -190,12 +208,18 @@ def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=Non
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     dlam = torch.empty((H * dv,), dtype=torch.float32, device=q.device) if want_dclvr_scale else None
     need = lib.gdr_workspace_size(ctypes.byref(desc), 1)
-    if workspace is None or workspace.numel() < need:
+    fn = lib.gdr_backward
+    if saved_workspace is not None:
+        _need(saved_workspace, "saved_workspace", torch.uint8)
+        if saved_workspace.numel() < need:
+            raise ValueError("saved_workspace has %d bytes, needs %d" % (saved_workspace.numel(), need))
+        workspace, fn = saved_workspace, lib.gdr_backward_saved
+    elif workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.gdr_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
-                            _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dh), _ptr(clvr_scale), _ptr(dq),
-                            _ptr(dk_), _ptr(dv_), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), _ptr(dlam),
-                            _ptr(workspace), need, _stream(q.device)))
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+              _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dh), _ptr(clvr_scale), _ptr(dq),
+              _ptr(dk_), _ptr(dv_), _ptr(dbeta), _ptr(dalpha), _ptr(dS0), _ptr(dlam),
+              _ptr(workspace), need, _stream(q.device)))
     return {"dq": dq, "dk": dk_, "dv": dv_, "dbeta": dbeta, "dalpha": dalpha, "dS0": dS0,
             "dclvr_scale": dlam}
 

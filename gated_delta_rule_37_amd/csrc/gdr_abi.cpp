@@ -168,14 +168,21 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     return n;
 }
 
-gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
+}  // extern "C"
+
+// Forward.  train = true also keeps in ws everything the backward needs (the
+// backward layout of the workspace), so that gdr_backward_saved can skip the
+// recomputation.
+static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* k, const void* v,
                                const float* beta, const float* alpha, const float* S0, void* o,
                                float* ST, void* h_clvr, const float* clvr_scale, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               size_t ws_bytes, void* stream, bool train) {
     int64_t NC = 0;
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
     const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
+    if (train && desc->in_dtype == GDR_FP32 && D == 128)
+        return fail(GDR_ERR_UNSUPPORTED, "the backward supports fp32 inputs only at dk = dv = 64");
     const int64_t ntok = B * T * H;
     const bool any = ntok > 0;
     if (any && (!q || !k || !v || !beta || !o))
@@ -211,35 +218,45 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
     const int64_t nch = B * H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
     gdr::ChunkWs w;
-    const size_t need = gdr::chunk_ws_bytes(nch, int(D), opb, false, &w, ws);
+    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, train, &w, ws);
+    const size_t need = train ? chunk_bytes + align_up(dlam_partial_bytes(desc)) : chunk_bytes;
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     if (B * H == 0) return GDR_OK;
-    if (ws && overlap(ws, need, o, o_bytes)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps o");
+    if (ws) {
+        for (auto& in : ins)
+            if (overlap(ws, need, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an input");
+        if (overlap(ws, need, o, o_bytes) || (ST && overlap(ws, need, ST, s_bytes)) ||
+            (h_clvr && overlap(ws, need, h_clvr, n_in * ib)))
+            return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an output");
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
     hipError_t e = hipSuccess;
     if (NC > 0) {
         gdr::prof_before(s);
-        e = gdr::launch_intra(int(D), desc->gate, in_f32, false, B, T, int(H), NC, q, k, v, beta, alpha,
-                              h_clvr, clvr_scale, w, s);
-        gdr::prof_after("intra_fwd", s);
+        e = gdr::launch_intra(int(D), desc->gate, in_f32, train ? 2 : 0, B, T, int(H), NC, q, k, v, beta,
+                              alpha, h_clvr, clvr_scale, w, s);
+        gdr::prof_after(train ? "intra_train" : "intra_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
     }
     gdr::prof_before(s);
     e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o,
-                              false, s);
-    gdr::prof_after("state_fwd", s);
+                              train, s);
+    gdr::prof_after(train ? "state_train" : "state_fwd", s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     return GDR_OK;
 }
 
-gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
-                        const float* beta, const float* alpha, const float* S0, const void* dO,
-                        const float* dST, const void* dh_clvr, const float* clvr_scale, void* dq,
-                        void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
-                        float* dclvr_scale, void* ws, size_t ws_bytes, void* stream) {
+// Backward.  recompute = false takes the forward's intermediates from ws, where
+// a preceding forward_impl(train = true) with the same arguments left them.
+static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                                const float* beta, const float* alpha, const float* S0, const void* dO,
+                                const float* dST, const void* dh_clvr, const float* clvr_scale, void* dq,
+                                void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                                float* dclvr_scale, void* ws, size_t ws_bytes, void* stream,
+                                bool recompute) {
     int64_t NC = 0;
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
@@ -288,6 +305,8 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     for (auto& o1 : outs)
         if (ws && overlap(ws, need, o1.p, o1.n)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an output");
+    for (auto& in : ins)
+        if (ws && overlap(ws, need, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an input");
     if (B * H == 0) return GDR_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -301,8 +320,8 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
         gdr::prof_after(name, s);                                                             \
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "%s launch: %s", name, hipGetErrorString(e)); \
     } while (0)
-    if (NC > 0) {
-        GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, true, B, T, int(H), NC, q, k, v, beta,
+    if (NC > 0 && recompute) {
+        GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, 1, B, T, int(H), NC, q, k, v, beta,
                                                 alpha, nullptr, nullptr, w, s));
         GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
                                                          desc->scale, w, S0, nullptr, nullptr, true, s));
@@ -322,6 +341,40 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
     }
 #undef GDR_STEP
     return GDR_OK;
+}
+
+extern "C" {
+
+gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                               const float* beta, const float* alpha, const float* S0, void* o,
+                               float* ST, void* h_clvr, const float* clvr_scale, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return forward_impl(desc, q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws, ws_bytes, stream, false);
+}
+
+gdr_status gdr_forward_train(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                             const float* beta, const float* alpha, const float* S0, void* o, float* ST,
+                             void* h_clvr, const float* clvr_scale, void* ws, size_t ws_bytes,
+                             void* stream) {
+    return forward_impl(desc, q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws, ws_bytes, stream, true);
+}
+
+gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* alpha, const float* S0, const void* dO,
+                        const float* dST, const void* dh_clvr, const float* clvr_scale, void* dq,
+                        void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                        float* dclvr_scale, void* ws, size_t ws_bytes, void* stream) {
+    return backward_impl(desc, q, k, v, beta, alpha, S0, dO, dST, dh_clvr, clvr_scale, dq, dk, dv, dbeta,
+                         dalpha, dS0, dclvr_scale, ws, ws_bytes, stream, true);
+}
+
+gdr_status gdr_backward_saved(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                              const float* beta, const float* alpha, const float* S0, const void* dO,
+                              const float* dST, const void* dh_clvr, const float* clvr_scale, void* dq,
+                              void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                              float* dclvr_scale, void* ws, size_t ws_bytes, void* stream) {
+    return backward_impl(desc, q, k, v, beta, alpha, S0, dO, dST, dh_clvr, clvr_scale, dq, dk, dv, dbeta,
+                         dalpha, dS0, dclvr_scale, ws, ws_bytes, stream, false);
 }
 
 gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,

@@ -79,8 +79,8 @@ template <typename OpT>
 __device__ __forceinline__ void st4b(OpT* dst, const float4v& v) {
     if constexpr (sizeof(OpT) == 2) {
         half4 hv;
-        hv[0] = static_cast<_Float16>(v[0]); hv[1] = static_cast<_Float16>(v[1]);
-        hv[2] = static_cast<_Float16>(v[2]); hv[3] = static_cast<_Float16>(v[3]);
+        hv[0] = from_f32<_Float16>(v[0]); hv[1] = from_f32<_Float16>(v[1]);
+        hv[2] = from_f32<_Float16>(v[2]); hv[3] = from_f32<_Float16>(v[3]);
         *reinterpret_cast<half4*>(dst) = hv;
     } else {
         *reinterpret_cast<float4v*>(dst) = v;

@@ -58,7 +58,12 @@ __device__ __forceinline__ float to_f32(_Float16 x) { return static_cast<float>(
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+// The empty asm pins x as an fp32 value: without it the compiler may fuse a
+// product feeding the conversion into one mixed-precision FMA (one rounding
+// instead of two), and whether it does depends on the surrounding code, so two
+// kernels computing the same value could round it differently.
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) {
+    asm volatile("" : "+v"(x));
     return static_cast<_Float16>(x);
 }
 
@@ -131,7 +136,7 @@ __device__ __forceinline__ void store_run(OpT* dst, const float* src) {
         for (int i = 0; i < N; i += 8) {
             half8 h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(src[i + e]);
+            for (int e = 0; e < 8; ++e) h[e] = from_f32<_Float16>(src[i + e]);
             *reinterpret_cast<half8*>(dst + i) = h;
         }
     } else {
@@ -150,8 +155,8 @@ template <typename OpT>
 __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
     if constexpr (sizeof(OpT) == 2) {
         half4 h;
-        h[0] = static_cast<_Float16>(v[0]); h[1] = static_cast<_Float16>(v[1]);
-        h[2] = static_cast<_Float16>(v[2]); h[3] = static_cast<_Float16>(v[3]);
+        h[0] = from_f32<_Float16>(v[0]); h[1] = from_f32<_Float16>(v[1]);
+        h[2] = from_f32<_Float16>(v[2]); h[3] = from_f32<_Float16>(v[3]);
         *reinterpret_cast<half4*>(dst) = h;
     } else {
         *reinterpret_cast<float4v*>(dst) = v;

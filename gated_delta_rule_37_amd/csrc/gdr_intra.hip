@@ -81,7 +81,9 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
-template <int D, int GATE, bool IN_F32, bool BWD>
+// MODE 0: the forward's operands (and CLVR); 1: the operands of the recomputing
+// backward; 2: both, so that a training forward leaves everything its backward needs.
+template <int D, int GATE, bool IN_F32, int MODE>
 __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t NC,
                                                       const void* __restrict__ q_,
                                                       const void* __restrict__ k_,
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                                                       const float* __restrict__ alpha,
                                                       void* __restrict__ h_, const float* __restrict__ lam,
                                                       ChunkWs ws) {
+    constexpr bool FO = MODE != 1;  // forward operands: Qt, A
+    constexpr bool BWD = MODE != 0; // backward operands: Kb, Qt^T, A^T, W^T, N, P
     using L = IntraLayout<D, GATE, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 kb[j] = kk[j] * exp2_fast(glast - G[j]);
                 fq = exp2_fast(G[j] - carry);
             }
-            if constexpr (!BWD) Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
+            if constexpr (FO) Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
             if constexpr (GATE == GATE_CHANNEL) {
                 Kq[r * LDR + cc] = from_f32<OpT>(kk[j] * fq);
                 Qq[r * LDR + cc] = from_f32<OpT>(qq[j] * fq);
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                         acc[e] *= f;
                     }
                     if (isA) {
-                        if constexpr (!BWD) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
+                        if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
                         if constexpr (BWD) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e) AT_g[frag_off<CHUNK>(16 * I + 4 * g4 + e, r)] = from_f32<OpT>(acc[e]);
@@ -361,9 +365,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
         const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
         const int r = 16 * R + w / 4, i0 = 16 * I + 4 * (w % 4);
-        if constexpr (!BWD) {
-            store4<OpT>(A_g + frag_off<CHUNK>(r, i0), zero4());
-        } else {
+        if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, i0), zero4());
+        if constexpr (BWD) {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) AT_g[frag_off<CHUNK>(i0 + e2, r)] = from_f32<OpT>(0.f);
         }
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                     }
                     if (cg == 0) {
                         Ps[r * CHUNK + ii] = ps;
-                        if constexpr (!BWD) A_g[frag_off<CHUNK>(r, ii)] = from_f32<OpT>(as);
+                        if constexpr (FO) A_g[frag_off<CHUNK>(r, ii)] = from_f32<OpT>(as);
                         if constexpr (BWD) AT_g[frag_off<CHUNK>(ii, r)] = from_f32<OpT>(as);
                     }
                 }
@@ -573,43 +576,46 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
 }
 
 template <int D, int GATE, bool IN_F32>
-static hipError_t launch_intra_t(bool bwd, int64_t B, int64_t T, int H, int64_t NC, const void* q,
+static hipError_t launch_intra_t(int mode, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                                  const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
                                  const ChunkWs& ws, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
-    if (bwd)
-        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
+    if (mode == 1)
+        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 1>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+    else if (mode == 2)
+        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 2>), dim3((unsigned)nblk), dim3(4 * D), 0,
                            stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
     else
-        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
+        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 0>), dim3((unsigned)nblk), dim3(4 * D), 0,
                            stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
     return hipGetLastError();
 }
 
 template <int D, bool IN_F32>
-static hipError_t launch_intra_d(int gate, bool bwd, int64_t B, int64_t T, int H, int64_t NC,
+static hipError_t launch_intra_d(int gate, int mode, int64_t B, int64_t T, int H, int64_t NC,
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
                                  const ChunkWs& ws, hipStream_t stream) {
     switch (gate) {
-        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(bwd, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
     }
 }
 
-hipError_t launch_intra(int D, int gate, bool in_f32, bool backward, int64_t B, int64_t T, int H,
+hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
                         const ChunkWs& ws, hipStream_t stream) {
     if (D == 64) {
-        if (in_f32) return launch_intra_d<64, true>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        return launch_intra_d<64, false>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        if (in_f32) return launch_intra_d<64, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        return launch_intra_d<64, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
     }
-    if (in_f32) return launch_intra_d<128, true>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-    return launch_intra_d<128, false>(gate, backward, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    if (in_f32) return launch_intra_d<128, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    return launch_intra_d<128, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
 }
 
 }  // namespace gdr

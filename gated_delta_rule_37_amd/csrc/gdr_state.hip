@@ -100,8 +100,8 @@ template <typename OpT>
 __device__ __forceinline__ void st4(OpT* dst, const float4v& v) {
     if constexpr (sizeof(OpT) == 2) {
         half4 h;
-        h[0] = static_cast<_Float16>(v[0]); h[1] = static_cast<_Float16>(v[1]);
-        h[2] = static_cast<_Float16>(v[2]); h[3] = static_cast<_Float16>(v[3]);
+        h[0] = from_f32<_Float16>(v[0]); h[1] = from_f32<_Float16>(v[1]);
+        h[2] = from_f32<_Float16>(v[2]); h[3] = from_f32<_Float16>(v[3]);
         *reinterpret_cast<half4*>(dst) = h;
     } else {
         *reinterpret_cast<float4v*>(dst) = v;
@@ -169,7 +169,7 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
     // intra-chunk part of the output, O += A U
     if constexpr (HAS_O) {
         mma(cur.a[0], fu0, oacc);
-        if (wid >= 2) mma(cur.a[1], fu1, oacc);
+        mma(cur.a[1], fu1, oacc);  // zero block for waves 0 and 1
         const int64_t tbase = c * CHUNK + 16 * wid + 4 * g4;
         OutT* op = o + ((b * T + tbase) * H + h) * D + j0 + l16;
         const int64_t tstride = static_cast<int64_t>(H) * D;

@@ -131,6 +131,35 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
                         float* dalpha, float* dS0, float* dclvr_scale, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Training pair: a forward that keeps its intermediates, and the backward that
+ * uses them instead of recomputing them (the per-chunk operands of the
+ * intra-chunk transform and the chunk-start states and U of the state pass).
+ *
+ * gdr_forward_train computes exactly what gdr_forward_chunked computes (same
+ * arguments, same results bit for bit) and in addition leaves in `ws` the
+ * intermediates gdr_backward_saved reads.  Its workspace has the backward's
+ * size, gdr_workspace_size(desc, 1).
+ *
+ * gdr_backward_saved takes the arguments of gdr_backward and returns the same
+ * gradients bit for bit.  Its `ws` must be the workspace of the preceding
+ * gdr_forward_train call on the same stream, with the same desc, q, k, v, beta,
+ * alpha and S0, none of them modified in between (the library cannot check
+ * this; other contents give wrong gradients, never an out-of-bounds access).
+ * fp32 inputs are supported at dk = dv = 64 only, as for gdr_backward.
+ */
+gdr_status gdr_forward_train(const gdr_desc* desc, const void* q, const void* k,
+                             const void* v, const float* beta, const float* alpha,
+                             const float* S0, void* o, float* ST, void* h_clvr,
+                             const float* clvr_scale, void* ws, size_t ws_bytes,
+                             void* stream);
+
+gdr_status gdr_backward_saved(const gdr_desc* desc, const void* q, const void* k,
+                              const void* v, const float* beta, const float* alpha,
+                              const float* S0, const void* dO, const float* dST,
+                              const void* dh_clvr, const float* clvr_scale, void* dq,
+                              void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
+                              float* dclvr_scale, void* ws, size_t ws_bytes, void* stream);
+
 /* One decode step for N independent sequences, state updated in place
  * (inference with a fixed-size state, KDA blog section 6.1):
  *   p = S^T (alpha*k), r = S^T (alpha*q), u = beta (v - p),
