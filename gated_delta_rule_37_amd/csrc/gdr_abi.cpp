@@ -110,6 +110,10 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* 
     w.KbT = take(mat);
     w.A = take(sq);
     w.gam = static_cast<float*>(take(size_t(nch) * D * 4));
+    // chunk-start states and U: written by the state pass, read by the output
+    // kernel and the gradient kernels
+    w.Ssnap = take(st);
+    w.Usave = take(mat);
     if (backward) {
         const size_t sq32 = size_t(nch) * kChunk * kChunk * 4;
         const size_t mat32 = size_t(nch) * kChunk * D * 4;
@@ -119,8 +123,6 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* 
         w.WT = take(mat);
         w.Nw = static_cast<float*>(take(sq32));
         w.Pw = static_cast<float*>(take(sq32));
-        w.Ssnap = take(st);
-        w.Usave = take(mat);
         w.dSsnap = take(st);
         w.dUsave = take(mat);
         w.dUsaveT = take(mat);
@@ -246,6 +248,12 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
                               train, s);
     gdr::prof_after(train ? "state_train" : "state_fwd", s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
+    if (!in_f32 && NC > 0) {
+        gdr::prof_before(s);
+        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, s);
+        gdr::prof_after("output", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
+    }
     return GDR_OK;
 }
 

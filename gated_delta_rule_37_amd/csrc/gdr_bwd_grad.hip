@@ -840,42 +840,64 @@ hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t 
 // Pass 1: nseg token segments, one partial per (segment, channel).
 // Pass 2: sum the partials of each channel in a fixed order (deterministic).
 // ---------------------------------------------------------------------------
+// CLVR scale gradient, dlam[c] = sum over (b, t) of dh[b,t,c] * v[b,t,c], in two
+// deterministic passes.  Pass 1: segment y of the token range, thread x owns
+// VEC consecutive columns (one 16-byte load per row of each operand).
 template <bool IN_F32>
 __global__ __launch_bounds__(256) void clvr_dlam_partial(int64_t BT, int HD, int64_t nseg, const void* __restrict__ dh_,
                                                          const void* __restrict__ v_, float* __restrict__ partial) {
     using InT = typename InType<IN_F32>::T;
+    constexpr int VEC = 16 / sizeof(InT);
     const InT* dh = reinterpret_cast<const InT*>(dh_);
     const InT* v = reinterpret_cast<const InT*>(v_);
-    const int64_t c = blockIdx.x * 256 + threadIdx.x;
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * VEC;
     const int64_t seg = blockIdx.y;
-    if (c >= HD) return;
+    if (c0 >= HD) return;
     const int64_t per = (BT + nseg - 1) / nseg;
     const int64_t t0 = seg * per, t1 = t0 + per < BT ? t0 + per : BT;
-    float s = 0.f;
-    for (int64_t t = t0; t < t1; ++t) s += to_f32(dh[t * HD + c]) * to_f32(v[t * HD + c]);
-    partial[seg * HD + c] = s;
+    float s[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+        const float4v rd = *reinterpret_cast<const float4v*>(dh + t * HD + c0);
+        const float4v rv = *reinterpret_cast<const float4v*>(v + t * HD + c0);
+        const InT* pd = reinterpret_cast<const InT*>(&rd);
+        const InT* pv = reinterpret_cast<const InT*>(&rv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] = __builtin_fmaf(to_f32(pd[e]), to_f32(pv[e]), s[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) partial[seg * HD + c0 + e] = s[e];
 }
 
+// Pass 2: 64 columns per workgroup; thread (column c, group g) sums segments
+// g, g + 4, ...; the four group sums are added in a fixed order.
 __global__ __launch_bounds__(256) void clvr_dlam_final(int HD, int64_t nseg, const float* __restrict__ partial,
                                                        float* __restrict__ dlam) {
-    const int64_t c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= HD) return;
+    __shared__ float red[4][64];
+    const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
     float s = 0.f;
-    for (int64_t seg = 0; seg < nseg; ++seg) s += partial[seg * HD + c];
-    dlam[c] = s;
+    if (c < HD)
+        for (int64_t seg = g; seg < nseg; seg += 4) s += partial[seg * HD + c];
+    red[g][cl] = s;
+    __syncthreads();
+    if (g == 0 && c < HD) dlam[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
 }
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream) {
     const int HD = H * D;
-    const dim3 g1((HD + 255) / 256, (unsigned)nseg);
+    const int vec = in_f32 ? 4 : 8;
+    const dim3 g1((HD / vec + 255) / 256, (unsigned)nseg);
     if (in_f32)
         hipLaunchKernelGGL((clvr_dlam_partial<true>), g1, dim3(256), 0, stream, BT, HD, nseg, dh, v, partial);
     else
         hipLaunchKernelGGL((clvr_dlam_partial<false>), g1, dim3(256), 0, stream, BT, HD, nseg, dh, v, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(clvr_dlam_final, dim3((HD + 255) / 256), dim3(256), 0, stream, HD, nseg, partial, dlam);
+    hipLaunchKernelGGL(clvr_dlam_final, dim3((HD + 63) / 64), dim3(256), 0, stream, HD, nseg, partial, dlam);
     return hipGetLastError();
 }
 

@@ -163,6 +163,31 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// direct global -> LDS copies (global_load_lds) and explicit vmcnt waits
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Each lane copies 16 bytes from src_lane to lds_base + 16 * lane.  lds_base
+// must be the same for the whole wave.  The copy is counted by vmcnt and the
+// data is in LDS once the wave's vmcnt has dropped past it.
+__device__ __forceinline__ void copy16_to_lds(const void* src_lane, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src_lane, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+// Each lane copies 4 bytes (used to pull lines into the L2).
+__device__ __forceinline__ void copy4_to_lds(const void* src_lane, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src_lane, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 

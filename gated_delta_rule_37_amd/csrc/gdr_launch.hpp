@@ -42,6 +42,11 @@ hipError_t launch_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nsl
                          const float* beta, const float* alpha, float* S, void* o,
                          hipStream_t stream);
 
+// O = scale (Qt S + A U) for every chunk from the saved chunk-start states and U
+// (fp16 operands only).
+hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                         const ChunkWs& ws, void* o, hipStream_t stream);
+
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,

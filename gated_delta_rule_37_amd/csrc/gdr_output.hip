@@ -1,0 +1,148 @@
+// gdr_output.hip -- chunk outputs from the saved chunk-start states.
+//
+// With S the state at the start of chunk c (as the chain pass saved it) and U
+// the chunk's beta-scaled write errors, every output row of the chunk is
+//   O = scale (Qt S + A U)
+// (read-out after each token's write, KDA blog section 2.1, in the chunked form
+// of section 6.1).  None of this is sequential, so it runs over all chunk-heads
+// at once, one workgroup each.
+//
+// The saved S and U are in the fragment order the gradient kernels read (rows
+// d resp. position, k = value column).  Here the contraction runs over d resp.
+// position, so both are transposed through LDS once; Qt and A are copied to LDS
+// as they are.  Wave w owns the value columns 32w..32w+31 of all 64 rows.  The
+// products accumulate in the same order as a fused state pass would (Qt S over
+// d, then A U), in fp32.
+#include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+template <int D>
+struct OutLayout {
+    static constexpr int LDT = D + 8;       // row stride of S^T [D][D]  (fp16)
+    static constexpr int LDU = CHUNK + 8;   // row stride of U^T [D][64] (fp16)
+    static constexpr int ST = 0;
+    static constexpr int UT = ST + D * LDT * 2;
+    static constexpr int QT = UT + D * LDU * 2;  // Qt, fragment order copy
+    static constexpr int A = QT + CHUNK * D * 2;  // A, fragment order copy
+    static constexpr int BYTES = A + CHUNK * CHUNK * 2;
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
+                                                     void* __restrict__ o_) {
+    using L = OutLayout<D>;
+    using OutT = typename InType<OUT_F32>::T;
+    constexpr int LDT = L::LDT, LDU = L::LDU;
+    constexpr int CPW = D / 4 / 16;  // column tiles per wave
+
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+    _Float16* sT = reinterpret_cast<_Float16*>(smem + L::ST);
+    _Float16* uT = reinterpret_cast<_Float16*>(smem + L::UT);
+
+    const int64_t ch = blockIdx.x;
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // Qt and A: straight copies (fragment order), 1 KiB per copy
+    {
+        const char* Qg = static_cast<const char*>(ws.Qt) + ch * CHUNK * D * 2;
+        const char* Ag = static_cast<const char*>(ws.A) + ch * CHUNK * CHUNK * 2;
+        constexpr int NQ = CHUNK * D * 2 / 1024, NA = CHUNK * CHUNK * 2 / 1024;
+        for (int i = wid; i < NQ + NA; i += 4) {
+            if (i < NQ) copy16_to_lds(Qg + i * 1024 + lane * 16, smem + L::QT + i * 1024);
+            else copy16_to_lds(Ag + (i - NQ) * 1024 + lane * 16, smem + L::A + (i - NQ) * 1024);
+        }
+    }
+    // S and U transposed: piece p of a fragment-ordered [M][D] array is lane
+    // (p % 64) of fragment p / 64 = (row tile, 32-column step), eight
+    // consecutive columns of one row
+    {
+        const _Float16* Sg = reinterpret_cast<const _Float16*>(ws.Ssnap) + ch * D * D;
+        const _Float16* Ug = reinterpret_cast<const _Float16*>(ws.Usave) + ch * CHUNK * D;
+#pragma unroll
+        for (int i = 0; i < D * D / 8 / 256; ++i) {
+            const int p = i * 256 + tid, f = p >> 6, l = p & 63;
+            const int d = 16 * (f / (D / 32)) + (l & 15), j = 32 * (f % (D / 32)) + 8 * (l >> 4);
+            const half8 v = *reinterpret_cast<const half8*>(Sg + p * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sT[(j + e) * LDT + d] = v[e];
+        }
+#pragma unroll
+        for (int i = 0; i < CHUNK * D / 8 / 256; ++i) {
+            const int p = i * 256 + tid, f = p >> 6, l = p & 63;
+            const int pos = 16 * (f / (D / 32)) + (l & 15), j = 32 * (f % (D / 32)) + 8 * (l >> 4);
+            const half8 v = *reinterpret_cast<const half8*>(Ug + p * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) uT[(j + e) * LDU + pos] = v[e];
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    const int64_t nvalid64 = T - c * CHUNK;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
+    OutT* o = reinterpret_cast<OutT*>(o_);
+    const int64_t tstride = static_cast<int64_t>(H) * D;
+    const int64_t obase = ((b * T + c * CHUNK) * H + h) * D;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        Frag<_Float16> fq[D / 32], fa[2];
+#pragma unroll
+        for (int kq = 0; kq < D / 32; ++kq)
+            fq[kq].v = *reinterpret_cast<const half8*>(smem + L::QT + ((rt * (D / 32) + kq) * 64 + lane) * 16);
+        fa[0].v = *reinterpret_cast<const half8*>(smem + L::A + ((rt * 2 + 0) * 64 + lane) * 16);
+        fa[1].v = *reinterpret_cast<const half8*>(smem + L::A + ((rt * 2 + 1) * 64 + lane) * 16);
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+            const int ct = wid * CPW + ci;
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < D / 32; ++kq) {
+                Frag<_Float16> fs;
+                fs.v = *reinterpret_cast<const half8*>(sT + (16 * ct + l16) * LDT + 32 * kq + 8 * g4);
+                mma(fq[kq], fs, acc);
+            }
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                Frag<_Float16> fu;
+                fu.v = *reinterpret_cast<const half8*>(uT + (16 * ct + l16) * LDU + 32 * kq + 8 * g4);
+                mma(fa[kq], fu, acc);  // the upper blocks of A are zero
+            }
+            const int col = 16 * ct + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * g4 + e;
+                if (r < nvalid) o[obase + r * tstride + col] = from_f32<OutT>(scale * acc[e]);
+            }
+        }
+    }
+}
+
+hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                         const ChunkWs& ws, void* o, hipStream_t stream) {
+    const int64_t nch = B * H * NC;
+    if (nch == 0) return hipSuccess;
+    if (D == 64) {
+        if (out_f32)
+            hipLaunchKernelGGL((output_kernel<64, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, scale,
+                               ws, o);
+        else
+            hipLaunchKernelGGL((output_kernel<64, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, scale,
+                               ws, o);
+    } else {
+        if (out_f32)
+            hipLaunchKernelGGL((output_kernel<128, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
+                               scale, ws, o);
+        else
+            hipLaunchKernelGGL((output_kernel<128, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
+                               scale, ws, o);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdr

@@ -340,12 +340,195 @@ __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chain-only pass for fp16 operands, staged through LDS.
+//
+// Only U = Ut - W S and S <- Diag(gamma) S + Kb^T U are sequential; the output
+// O = Qt S + A U is computed afterwards for all chunks in parallel from the
+// saved chunk-start states and U (output_kernel).  Every step needs all of W
+// and Kb^T of its chunk in each slice's CU, so the step is bounded by how fast
+// a CU can take them in.  Wave 4 copies chunk c+2 from global memory straight
+// into one of three LDS buffers (global_load_lds: no registers, no waits in
+// the compute waves) and pulls chunk c+PF into the L2; waves 0-3 compute chunk
+// c from its buffer with conflict-free 16-byte LDS reads.
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct ChainStage {
+    static constexpr int MAT = CHUNK * D * 2;  // [64][D] fp16
+    static constexpr int W = 0;
+    static constexpr int KBT = MAT;
+    static constexpr int UT = 2 * MAT;          // this slice's four 16x16 tiles of Ut
+    static constexpr int GAM = UT + 2048;       // D fp32 in a 1 KiB slot
+    static constexpr int BYTES = GAM + 1024;
+    static constexpr int ND = 2 * MAT / 1024 + 2 + 1;  // copies per chunk
+    static constexpr int NSL = D / 16;
+    static constexpr int QL = MAT / NSL / 128;         // 128-byte lines per slice of one array
+    static constexpr int NT = (3 * QL + 1 + 63) / 64;  // touch copies per chunk
+};
+
+// Chunk ch's operands for slice `slice` into `dst`; issued by one wave.
+template <int D>
+__device__ __forceinline__ void stage_chain(char* dst, const ChunkWs& ws, int64_t ch, int slice, int lane) {
+    using L = ChainStage<D>;
+    const char* W = static_cast<const char*>(ws.W) + ch * L::MAT;
+    const char* Kb = static_cast<const char*>(ws.KbT) + ch * L::MAT;
+#pragma unroll
+    for (int i = 0; i < L::MAT / 1024; ++i) {
+        copy16_to_lds(W + i * 1024 + lane * 16, dst + L::W + i * 1024);
+        copy16_to_lds(Kb + i * 1024 + lane * 16, dst + L::KBT + i * 1024);
+    }
+    // Ut tiles (rt, slice), rt = 0..3, 512 bytes each: two tiles per copy
+    const char* U = static_cast<const char*>(ws.Ut) + ch * L::MAT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rt = 2 * i + (lane >> 5);
+        copy16_to_lds(U + (rt * (D / 16) + slice) * 512 + (lane & 31) * 16, dst + L::UT + i * 1024);
+    }
+    // gamma: D floats; lanes past the end re-read the first piece into the slot's tail
+    const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
+    copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+}
+
+// One dword of each 128-byte line of this slice's share of chunk ch.
+template <int D>
+__device__ __forceinline__ void touch_chain(char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
+    using L = ChainStage<D>;
+    constexpr int QL = L::QL;
+#pragma unroll
+    for (int i = 0; i < L::NT; ++i) {
+        const int Lr = lane + 64 * i;
+        const char* addr;
+        if (Lr < QL) addr = static_cast<const char*>(ws.W) + ch * L::MAT + (slice * QL + Lr) * 128;
+        else if (Lr < 2 * QL) addr = static_cast<const char*>(ws.KbT) + ch * L::MAT + (slice * QL + Lr - QL) * 128;
+        else if (Lr < 3 * QL) addr = static_cast<const char*>(ws.Ut) + ch * L::MAT + (slice * QL + Lr - 2 * QL) * 128;
+        else addr = reinterpret_cast<const char*>(ws.gam + ch * D) + (slice % (D * 4 / 128)) * 128;
+        copy4_to_lds(addr, dummy + i * 256);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const char* src, int wid, int lane) {
+    using L = ChainStage<D>;
+    constexpr int SRT = StateCfg<D, false>::SRT;
+#pragma unroll
+    for (int kq = 0; kq < D / 32; ++kq)
+        f.w[kq].v = *reinterpret_cast<const half8*>(src + L::W + ((wid * (D / 32) + kq) * 64 + lane) * 16);
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+        const int rt = wid * (D / 64) + m;
+        f.kb[m][0].v = *reinterpret_cast<const half8*>(src + L::KBT + ((rt * 2 + 0) * 64 + lane) * 16);
+        f.kb[m][1].v = *reinterpret_cast<const half8*>(src + L::KBT + ((rt * 2 + 1) * 64 + lane) * 16);
+        const float4v g = *reinterpret_cast<const float4v*>(src + L::GAM + (16 * rt + 4 * (lane >> 4)) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.gam[m][e] = g[e];
+    }
+    const half4 u = *reinterpret_cast<const half4*>(src + L::UT + (wid * 256 + lane * 4) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.ut[e] = u[e];
+}
+
+// Waits until at most n copies of this wave are outstanding; n is one of
+// 0, NT, 2NT, ND, ND+NT, ND+2NT (chosen at run time, immediates at compile time).
+template <int ND, int NT>
+__device__ __forceinline__ void wait_outstanding(int n) {
+    if (n >= ND + 2 * NT) wait_vmcnt<ND + 2 * NT>();
+    else if (n >= ND + NT) wait_vmcnt<ND + NT>();
+    else if (n >= ND) wait_vmcnt<ND>();
+    else if (n >= 2 * NT) wait_vmcnt<2 * NT>();
+    else if (n >= NT) wait_vmcnt<NT>();
+    else wait_vmcnt<0>();
+}
+
+template <int D>
+__global__ __launch_bounds__(320) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
+                                                          const float* S0, float* ST) {
+    using Cfg = StateCfg<D, false>;
+    using OpT = _Float16;
+    using L = ChainStage<D>;
+    constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S;
+    constexpr int PF = 8;
+
+    __shared__ __attribute__((aligned(16))) OpT s_S[Cfg::NS * LDS_S];
+    __shared__ __attribute__((aligned(16))) OpT s_U[Cfg::NS * Cfg::LDS_U];
+    __shared__ __attribute__((aligned(1024))) char stage[3][L::BYTES];
+    __shared__ __attribute__((aligned(16))) char dummy[L::NT * 256];
+
+    const int64_t nblk = gridDim.x;
+    int64_t lid = blockIdx.x;
+    if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+    const int64_t bh = lid / NSL;
+    const int slice = static_cast<int>(lid % NSL);
+    const int j0 = slice * Cfg::NS;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    if (wid == 4) {
+        // Loader.  Two barriers per step, like the compute waves; it never
+        // fences, so its own copies stay in flight across the first one.
+        if (NC > 0) stage_chain<D>(stage[0], ws, bh * NC, slice, lane);
+        if (NC > 1) stage_chain<D>(stage[1], ws, bh * NC + 1, slice, lane);
+#pragma unroll 1
+        for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(dummy, ws, bh * NC + c, slice, lane);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll 1
+        for (int64_t c = 0; c < NC; ++c) {
+            const bool st2 = c + 2 < NC, tpf = c + PF < NC;
+            if (st2) stage_chain<D>(stage[(c + 2) % 3], ws, bh * NC + c + 2, slice, lane);
+            if (tpf) touch_chain<D>(dummy, ws, bh * NC + c + PF, slice, lane);
+            __builtin_amdgcn_s_barrier();
+            // chunk c+1 must have landed; later copies may stay in flight
+            const int n = ((c >= 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND : 0) + (tpf ? L::NT : 0);
+            wait_outstanding<L::ND, L::NT>(n);
+            __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
+    float4v S[SRT];
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+        const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[m][e] = S0 ? S0[(bh * D + d0 + e) * D + j0 + l16] : 0.f;
+        st4<OpT>(s_S + l16 * LDS_S + d0, S[m]);
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int64_t c = 0; c < NC; ++c) {
+        ChunkFrags<D, false> f;
+        chain_frags<D>(f, stage[c % 3], wid, lane);
+        state_step<D, false, false, true, false>(f, c, T, H, b, h, bh, NC, j0, wid, l16, g4, 1.f, ws, S, s_S,
+                                                 s_U, nullptr);
+    }
+
+    if (ST) {
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ST[(bh * D + d0 + e) * D + j0 + l16] = S[m][e];
+        }
+    }
+}
+
 template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float scale,
                                  const ChunkWs& ws, const float* S0, float* ST, void* o, bool save,
                                  hipStream_t stream) {
     const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
+    if constexpr (!IN_F32) {
+        // fp16 operands: the chain pass always saves the chunk-start states and U;
+        // the output is produced by output_kernel
+        hipLaunchKernelGGL((state_chain_kernel<D>), dim3((unsigned)nblk), dim3(320), 0, stream, T, H, NC, ws, S0,
+                           ST);
+        return hipGetLastError();
+    }
     if (save && o)
         hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true, true>), dim3((unsigned)nblk), dim3(320),
                            0, stream, T, H, NC, scale, ws, S0, ST, o);
