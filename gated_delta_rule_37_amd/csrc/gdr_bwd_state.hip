@@ -249,13 +249,268 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged variant for fp16 operands.  Wave 4 copies chunk c-1's operands
+// (A^T, Kb, Qt^T, W^T, gamma and this slice's dO rows) from global memory
+// straight into the LDS buffer that chunk c+1 used, while waves 0-3 run chunk
+// c from the other buffer; it also pulls chunk c-PF into the L2.  The dO
+// fragments are built directly from the staged rows, so a step needs only two
+// barriers (after dU, after dS).
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct BwdStage {
+    static constexpr int MAT = CHUNK * D * 2;   // [64][D] or [D][64] fp16
+    static constexpr int AT = 0;                // [64][64]
+    static constexpr int KB = AT + CHUNK * CHUNK * 2;
+    static constexpr int QTT = KB + MAT;
+    static constexpr int WT = QTT + MAT;
+    static constexpr int DO = WT + MAT;         // dO rows of this slice: [64][16] in the input dtype (bf16)
+    static constexpr int GAM = DO + 2048;       // D fp32 in a 1 KiB slot
+    static constexpr int BYTES = GAM + 1024;
+    static constexpr int NA = (CHUNK * CHUNK * 2 + MAT) / 1024 + 2 + 1;  // copies before the first barrier
+    static constexpr int NSL = D / 16;
+    static constexpr int NL = (CHUNK * CHUNK * 2 + 3 * MAT) / NSL / 128 + 1;  // lines touched per chunk
+    static constexpr int NT = (NL + 63) / 64;
+};
+
+// PART 0: A^T, Kb, dO rows, gamma; PART 1: Qt^T, W^T.
+template <int D, int PART>
+__device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c, int64_t b,
+                                          int64_t T, int H, int h, const void* dO, int j0, int lane) {
+    using L = BwdStage<D>;
+    if constexpr (PART == 1) {
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.QtT) + ch * L::MAT, dst + L::QTT, lane);
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.WT) + ch * L::MAT, dst + L::WT, lane);
+        return;
+    }
+    copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2,
+                                                dst + L::AT, lane);
+    copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
+    // dO rows: position pos = 32 i + lane / 2, half lane % 2 of its 16 columns
+    // (rows past the end re-read the last token; they are zeroed at use)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
+        const int64_t t = t0 < T ? t0 : T - 1;
+        const char* src = static_cast<const char*>(dO) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
+        copy16_to_lds(src, dst + L::DO + i * 1024);
+    }
+    const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
+    copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+}
+
+template <int D>
+__device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
+    using L = BwdStage<D>;
+    constexpr int AL = CHUNK * CHUNK * 2 / L::NSL / 128, QL = L::MAT / L::NSL / 128;
+#pragma unroll
+    for (int i = 0; i < L::NT; ++i) {
+        const int Lr = lane + 64 * i;
+        const char* addr;
+        if (Lr < AL) addr = static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2 + (slice * AL + Lr) * 128;
+        else if (Lr < AL + QL) addr = static_cast<const char*>(ws.Kb) + ch * L::MAT + (slice * QL + Lr - AL) * 128;
+        else if (Lr < AL + 2 * QL)
+            addr = static_cast<const char*>(ws.QtT) + ch * L::MAT + (slice * QL + Lr - AL - QL) * 128;
+        else if (Lr < AL + 3 * QL)
+            addr = static_cast<const char*>(ws.WT) + ch * L::MAT + (slice * QL + Lr - AL - 2 * QL) * 128;
+        else addr = reinterpret_cast<const char*>(ws.gam + ch * D) + (slice % (D * 4 / 128)) * 128;
+        copy4_to_lds(addr, dummy + i * 256);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(320) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
+                                                            const void* __restrict__ dO,
+                                                            const float* __restrict__ dST,
+                                                            float* __restrict__ dS0) {
+    using Cfg = BwdCfg<D, false>;
+    using OpT = _Float16;
+    using L = BwdStage<D>;
+    constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
+    constexpr int PF = 8;
+
+    __shared__ __attribute__((aligned(16))) OpT s_dS[Cfg::NS * LDS_S];
+    __shared__ __attribute__((aligned(16))) OpT s_dU[Cfg::NS * LDS_U];
+    __shared__ __attribute__((aligned(1024))) char stage[2][L::BYTES];
+    __shared__ __attribute__((aligned(16))) char dummy[L::NT * 256];
+
+    const int64_t nblk = gridDim.x;
+    int64_t lid = blockIdx.x;
+    if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+    const int64_t bh = lid / NSL;
+    const int slice = static_cast<int>(lid % NSL);
+    const int j0 = slice * Cfg::NS;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    lds_char* const sbuf = (lds_char*)&stage[0][0];
+    lds_char* const sdummy = (lds_char*)&dummy[0];
+
+    if (wid == 4) {
+        // Loader: chunk c-1 goes into the buffer chunk c+1 used (free since the
+        // end of that step); copies are split around the first barrier.
+        if (NC > 0) {
+            stage_bwd<D, 0>(sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
+            stage_bwd<D, 1>(sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
+        }
+#pragma unroll 1
+        for (int64_t c = NC - 2; c >= 0 && c > NC - 1 - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        int nb = 1;  // buffer of chunk c-1
+#pragma unroll 1
+        for (int64_t c = NC - 1; c >= 0; --c) {
+            const bool st = c >= 1, tpf = c - PF >= 0;
+            if (st) stage_bwd<D, 0>(sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
+            __builtin_amdgcn_s_barrier();
+            if (st) stage_bwd<D, 1>(sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
+            if (tpf) touch_bwd<D>(sdummy, ws, bh * NC + c - PF, slice, lane);
+            // chunk c-1 must have landed; only this step's touches may stay in flight
+            if (tpf) wait_vmcnt<L::NT>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            nb ^= 1;
+        }
+        return;
+    }
+
+    float4v dS[SRT];
+#pragma unroll
+    for (int m = 0; m < SRT; ++m) {
+        const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[m][e] = dST ? dST[(bh * D + d0 + e) * D + j0 + l16] : 0.f;
+        st4b<OpT>(s_dS + l16 * LDS_S + d0, dS[m]);
+    }
+    __syncthreads();
+
+    int cb = 0;
+#pragma unroll 1
+    for (int64_t c = NC - 1; c >= 0; --c) {
+        const lds_char* src = sbuf + cb * L::BYTES;
+        cb ^= 1;
+        const int64_t ch = bh * NC + c;
+        // operand fragments of this wave
+        Frag<OpT> at[2], kb[D / 32], qtt[SRT][2], wt[SRT][2];
+        float gam[SRT][4];
+        at[0].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::AT + ((wid * 2 + 0) * 64 + lane) * 16);
+        at[1].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::AT + ((wid * 2 + 1) * 64 + lane) * 16);
+#pragma unroll
+        for (int kq = 0; kq < D / 32; ++kq)
+            kb[kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::KB + ((wid * (D / 32) + kq) * 64 + lane) * 16);
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int rt = wid * (D / 64) + m;
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                qtt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::QTT + ((rt * 2 + kq) * 64 + lane) * 16);
+                wt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::WT + ((rt * 2 + kq) * 64 + lane) * 16);
+            }
+            const float4v g = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::GAM + (16 * rt + 4 * g4) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gam[m][e] = g[e];
+        }
+        // dO fragments (B operand, k = position): column j0 + l16, positions
+        // 32 kq + 8 g4 + e, scaled; rows past the end are zero
+        Frag<OpT> fo[2];
+        {
+            const __attribute__((address_space(3))) bf16_t* dos = reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DO);
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int pos = 32 * kq + 8 * g4 + e;
+                    const float x = (c * CHUNK + pos < T) ? scale * bf16_to_f32(dos[pos * 16 + l16]) : 0.f;
+                    fo[kq].v[e] = from_f32<_Float16>(x);
+                }
+            }
+        }
+
+        // dU = A^T dO + Kb dS'   (A^T's lower blocks are zero)
+        float4v du = zero4();
+        mma(at[0], fo[0], du);
+        mma(at[1], fo[1], du);
+#pragma unroll
+        for (int kq = 0; kq < D / 32; ++kq) {
+            Frag<OpT> fs;
+            fs.load(s_dS + l16 * LDS_S + 32 * kq + 8 * g4);
+            mma(kb[kq], fs, du);
+        }
+        st4b<OpT>(s_dU + l16 * LDS_U + 16 * wid + 4 * g4, du);
+        __syncthreads();
+
+        // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
+        {
+            const int t = tid;
+            if (t < 2 * CHUNK) {
+                const int pos = t >> 1, hf = t & 1;
+                OpT vals[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[e] = s_dU[(8 * hf + e) * LDS_U + pos];
+                st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
+            } else if (t < 2 * CHUNK + 128) {
+                const int t2 = t - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;
+                OpT vals[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[e] = s_dU[j * LDS_U + 8 * pg + e];
+                st8(reinterpret_cast<OpT*>(ws.dUsaveT) + ch * D * CHUNK + frag_off<CHUNK>(j0 + j, 8 * pg), vals);
+            }
+        }
+        // chunk-end gradient dS' (rows d, k = column): each wave saves the rows
+        // it owns before it overwrites them below
+        {
+            constexpr int RW = D / 4;
+            if (lane < 2 * RW) {
+                const int d = RW * wid + (lane >> 1), hf = lane & 1;
+                OpT vals[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[e] = s_dS[(8 * hf + e) * LDS_S + d];
+                st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf), vals);
+            }
+        }
+
+        // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
+        Frag<OpT> fu0, fu1;
+        fu0.load(s_dU + l16 * LDS_U + 8 * g4);
+        fu1.load(s_dU + l16 * LDS_U + 32 + 8 * g4);
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS[m][e] *= gam[m][e];
+            mma(qtt[m][0], fo[0], dS[m]);
+            mma(qtt[m][1], fo[1], dS[m]);
+            float4v wdu = zero4();
+            mma(wt[m][0], fu0, wdu);
+            mma(wt[m][1], fu1, wdu);
+            dS[m] -= wdu;
+            st4b<OpT>(s_dS + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, dS[m]);
+        }
+        __syncthreads();
+    }
+
+    if (dS0) {
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS0[(bh * D + d0 + e) * D + j0 + l16] = dS[m][e];
+        }
+    }
+}
+
 template <int D, bool IN_F32>
 static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
                                      const void* dO, const float* dST, float* dS0, hipStream_t stream) {
     const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
-                       scale, ws, dO, dST, dS0);
+    if constexpr (!IN_F32)
+        hipLaunchKernelGGL((state_bwd_lds_kernel<D>), dim3((unsigned)nblk), dim3(320), 0, stream, T, H, NC, scale,
+                           ws, dO, dST, dS0);
+    else
+        hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
+                           scale, ws, dO, dST, dS0);
     return hipGetLastError();
 }
 

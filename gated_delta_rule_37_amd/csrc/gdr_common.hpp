@@ -168,16 +168,32 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
 // direct global -> LDS copies (global_load_lds) and explicit vmcnt waits
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) char lds_char;  // byte pointer into LDS
 
-// Each lane copies 16 bytes from src_lane to lds_base + 16 * lane.  lds_base
-// must be the same for the whole wave.  The copy is counted by vmcnt and the
-// data is in LDS once the wave's vmcnt has dropped past it.
-__device__ __forceinline__ void copy16_to_lds(const void* src_lane, char* lds_base) {
-    __builtin_amdgcn_global_load_lds(src_lane, (lds_ptr_t)lds_base, 16, 0, 0);
+// Each lane copies 16 bytes from src_lane + OFF to lds_base + OFF + 16 * lane
+// (the instruction offset applies to both addresses).  lds_base must be the
+// same for the whole wave.  The copy is counted by vmcnt and the data is in
+// LDS once the wave's vmcnt has dropped past it.
+template <int OFF = 0>
+__device__ __forceinline__ void copy16_to_lds(const void* src_lane, lds_char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src_lane, (lds_ptr_t)lds_base, 16, OFF, 0);
 }
 // Each lane copies 4 bytes (used to pull lines into the L2).
-__device__ __forceinline__ void copy4_to_lds(const void* src_lane, char* lds_base) {
+__device__ __forceinline__ void copy4_to_lds(const void* src_lane, lds_char* lds_base) {
     __builtin_amdgcn_global_load_lds(src_lane, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+// A contiguous block of NKB KiB, one wave: four 1 KiB copies per address.
+template <int NKB>
+__device__ __forceinline__ void copy_block_to_lds(const char* src, lds_char* dst, int lane) {
+#pragma unroll
+    for (int i = 0; i < NKB; i += 4) {
+        const char* s = src + i * 1024 + lane * 16;
+        lds_char* d = dst + i * 1024;
+        copy16_to_lds<0>(s, d);
+        if (i + 1 < NKB) copy16_to_lds<1024>(s, d);
+        if (i + 2 < NKB) copy16_to_lds<2048>(s, d);
+        if (i + 3 < NKB) copy16_to_lds<3072>(s, d);
+    }
 }
 
 // s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding: vmcnt

@@ -54,8 +54,9 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
         const char* Ag = static_cast<const char*>(ws.A) + ch * CHUNK * CHUNK * 2;
         constexpr int NQ = CHUNK * D * 2 / 1024, NA = CHUNK * CHUNK * 2 / 1024;
         for (int i = wid; i < NQ + NA; i += 4) {
-            if (i < NQ) copy16_to_lds(Qg + i * 1024 + lane * 16, smem + L::QT + i * 1024);
-            else copy16_to_lds(Ag + (i - NQ) * 1024 + lane * 16, smem + L::A + (i - NQ) * 1024);
+            lds_char* sm = (lds_char*)&smem[0];
+            if (i < NQ) copy16_to_lds(Qg + i * 1024 + lane * 16, sm + L::QT + i * 1024);
+            else copy16_to_lds(Ag + (i - NQ) * 1024 + lane * 16, sm + L::A + (i - NQ) * 1024);
         }
     }
     // S and U transposed: piece p of a fragment-ordered [M][D] array is lane

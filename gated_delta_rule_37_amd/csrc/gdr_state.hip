@@ -122,21 +122,6 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
     constexpr int SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
     const int64_t ch = bh * NC + c;
 
-    if constexpr (SAVE) {
-        // chunk-start state snapshot [D][D] in operand precision, fragment order
-        // (rows d, k = value column): eight consecutive columns per thread,
-        // gathered from the transposed LDS copy
-        const int t = wid * WAVE + (l16 + 16 * g4);
-        if (t < 2 * D) {
-            const int d = t >> 1, hf = t & 1;
-            OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf);
-            OpT vals[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = s_S[(8 * hf + e) * LDS_S + d];
-            store8(snap, vals);
-        }
-    }
-
     // U = Ut - W S and the inter-chunk part of the output, O = Qt S
     float4v u = zero4(), oacc = zero4();
 #pragma unroll
@@ -180,6 +165,23 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (tbase + e < T) op[e * tstride] = from_f32<OutT>(scale * oacc[e]);
+        }
+    }
+
+    if constexpr (SAVE) {
+        // chunk-start state snapshot [D][D] in operand precision, fragment order
+        // (rows d, k = value column): eight consecutive columns per lane,
+        // gathered from the transposed LDS copy.  Each wave saves the rows it
+        // owns, which no other wave writes, before it overwrites them below.
+        constexpr int RW = D / 4;
+        const int lane = 16 * g4 + l16;
+        if (lane < 2 * RW) {
+            const int d = RW * wid + (lane >> 1), hf = lane & 1;
+            OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf);
+            OpT vals[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = s_S[(8 * hf + e) * LDS_S + d];
+            store8(snap, vals);
         }
     }
 
@@ -367,17 +369,16 @@ struct ChainStage {
     static constexpr int NT = (3 * QL + 1 + 63) / 64;  // touch copies per chunk
 };
 
-// Chunk ch's operands for slice `slice` into `dst`; issued by one wave.
-template <int D>
-__device__ __forceinline__ void stage_chain(char* dst, const ChunkWs& ws, int64_t ch, int slice, int lane) {
+// Chunk ch's operands for slice `slice` into `dst`; issued by one wave in two
+// parts (PART 0: W, Ut, gamma; PART 1: Kb^T).
+template <int D, int PART>
+__device__ __forceinline__ void stage_chain(lds_char* dst, const ChunkWs& ws, int64_t ch, int slice, int lane) {
     using L = ChainStage<D>;
-    const char* W = static_cast<const char*>(ws.W) + ch * L::MAT;
-    const char* Kb = static_cast<const char*>(ws.KbT) + ch * L::MAT;
-#pragma unroll
-    for (int i = 0; i < L::MAT / 1024; ++i) {
-        copy16_to_lds(W + i * 1024 + lane * 16, dst + L::W + i * 1024);
-        copy16_to_lds(Kb + i * 1024 + lane * 16, dst + L::KBT + i * 1024);
+    if constexpr (PART == 1) {
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.KbT) + ch * L::MAT, dst + L::KBT, lane);
+        return;
     }
+    copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT, dst + L::W, lane);
     // Ut tiles (rt, slice), rt = 0..3, 512 bytes each: two tiles per copy
     const char* U = static_cast<const char*>(ws.Ut) + ch * L::MAT;
 #pragma unroll
@@ -392,7 +393,7 @@ __device__ __forceinline__ void stage_chain(char* dst, const ChunkWs& ws, int64_
 
 // One dword of each 128-byte line of this slice's share of chunk ch.
 template <int D>
-__device__ __forceinline__ void touch_chain(char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
+__device__ __forceinline__ void touch_chain(lds_char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
     using L = ChainStage<D>;
     constexpr int QL = L::QL;
 #pragma unroll
@@ -408,22 +409,22 @@ __device__ __forceinline__ void touch_chain(char* dummy, const ChunkWs& ws, int6
 }
 
 template <int D>
-__device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const char* src, int wid, int lane) {
+__device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const lds_char* src, int wid, int lane) {
     using L = ChainStage<D>;
     constexpr int SRT = StateCfg<D, false>::SRT;
 #pragma unroll
     for (int kq = 0; kq < D / 32; ++kq)
-        f.w[kq].v = *reinterpret_cast<const half8*>(src + L::W + ((wid * (D / 32) + kq) * 64 + lane) * 16);
+        f.w[kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::W + ((wid * (D / 32) + kq) * 64 + lane) * 16);
 #pragma unroll
     for (int m = 0; m < SRT; ++m) {
         const int rt = wid * (D / 64) + m;
-        f.kb[m][0].v = *reinterpret_cast<const half8*>(src + L::KBT + ((rt * 2 + 0) * 64 + lane) * 16);
-        f.kb[m][1].v = *reinterpret_cast<const half8*>(src + L::KBT + ((rt * 2 + 1) * 64 + lane) * 16);
-        const float4v g = *reinterpret_cast<const float4v*>(src + L::GAM + (16 * rt + 4 * (lane >> 4)) * 4);
+        f.kb[m][0].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::KBT + ((rt * 2 + 0) * 64 + lane) * 16);
+        f.kb[m][1].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::KBT + ((rt * 2 + 1) * 64 + lane) * 16);
+        const float4v g = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::GAM + (16 * rt + 4 * (lane >> 4)) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) f.gam[m][e] = g[e];
     }
-    const half4 u = *reinterpret_cast<const half4*>(src + L::UT + (wid * 256 + lane * 4) * 2);
+    const half4 u = *reinterpret_cast<const __attribute__((address_space(3))) half4*>(src + L::UT + (wid * 256 + lane * 4) * 2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) f.ut[e] = u[e];
 }
@@ -464,22 +465,35 @@ __global__ __launch_bounds__(320) void state_chain_kernel(int64_t T, int H, int6
     const int h = static_cast<int>(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    lds_char* const sbuf = (lds_char*)&stage[0][0];
+    lds_char* const sdummy = (lds_char*)&dummy[0];
 
     if (wid == 4) {
         // Loader.  Two barriers per step, like the compute waves; it never
         // fences, so its own copies stay in flight across the first one.
-        if (NC > 0) stage_chain<D>(stage[0], ws, bh * NC, slice, lane);
-        if (NC > 1) stage_chain<D>(stage[1], ws, bh * NC + 1, slice, lane);
+        if (NC > 0) {
+            stage_chain<D, 0>(sbuf, ws, bh * NC, slice, lane);
+            stage_chain<D, 1>(sbuf, ws, bh * NC, slice, lane);
+        }
+        if (NC > 1) {
+            stage_chain<D, 0>(sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
+            stage_chain<D, 1>(sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
+        }
 #pragma unroll 1
-        for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(dummy, ws, bh * NC + c, slice, lane);
+        for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
+        int nb = 2;  // buffer of chunk c + 2
 #pragma unroll 1
         for (int64_t c = 0; c < NC; ++c) {
             const bool st2 = c + 2 < NC, tpf = c + PF < NC;
-            if (st2) stage_chain<D>(stage[(c + 2) % 3], ws, bh * NC + c + 2, slice, lane);
-            if (tpf) touch_chain<D>(dummy, ws, bh * NC + c + PF, slice, lane);
+            // the copies are split around the first barrier so that issuing
+            // them never holds the compute waves up
+            if (st2) stage_chain<D, 0>(sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
             __builtin_amdgcn_s_barrier();
+            if (st2) stage_chain<D, 1>(sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
+            if (tpf) touch_chain<D>(sdummy, ws, bh * NC + c + PF, slice, lane);
+            nb = nb == 2 ? 0 : nb + 1;
             // chunk c+1 must have landed; later copies may stay in flight
             const int n = ((c >= 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND : 0) + (tpf ? L::NT : 0);
             wait_outstanding<L::ND, L::NT>(n);
@@ -498,10 +512,12 @@ __global__ __launch_bounds__(320) void state_chain_kernel(int64_t T, int H, int6
     }
     __syncthreads();
 
+    int cb = 0;  // buffer of chunk c
 #pragma unroll 1
     for (int64_t c = 0; c < NC; ++c) {
         ChunkFrags<D, false> f;
-        chain_frags<D>(f, stage[c % 3], wid, lane);
+        chain_frags<D>(f, sbuf + cb * L::BYTES, wid, lane);
+        cb = cb == 2 ? 0 : cb + 1;
         state_step<D, false, false, true, false>(f, c, T, H, b, h, bh, NC, j0, wid, l16, g4, 1.f, ws, S, s_S,
                                                  s_U, nullptr);
     }
