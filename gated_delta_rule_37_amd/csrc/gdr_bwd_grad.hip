@@ -147,7 +147,17 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    for (int e = tid; e < CHUNK * CHUNK; e += NT) NF[(e / CHUNK) * LDF + e % CHUNK] = ws.Nw[ch * CHUNK * CHUNK + e];
+    {
+        constexpr int NE = CHUNK * CHUNK / NT;
+        float nv[NE];
+#pragma unroll
+        for (int k2 = 0; k2 < NE; ++k2) nv[k2] = ws.Nw[ch * CHUNK * CHUNK + k2 * NT + tid];
+#pragma unroll
+        for (int k2 = 0; k2 < NE; ++k2) {
+            const int e = k2 * NT + tid;
+            NF[(e / CHUNK) * LDF + e % CHUNK] = nv[k2];
+        }
+    }
     __syncthreads();
     if constexpr (GATE == GATE_CHANNEL) {
         float carry = 0.f;
@@ -314,6 +324,18 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
 
     // ---------------- phase 3: solve adjoint on fp32 matrix cores ----------------
     // Y = N^T dT and dL = -strict_tril(Y T^T), T = N diag(beta)
+    // this wave's P entries of its dL tiles, fetched now so the loads overlap Y
+    constexpr int NTL = 16 / NW;
+    float pwv[NTL][4];
+    {
+        const float* Pw = ws.Pw + ch * CHUNK * CHUNK;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            const int tile = wid + t * NW, at = tile / 4, xt = tile % 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pwv[t][e] = Pw[(16 * at + 4 * g4 + e) * CHUNK + 16 * xt + l16];
+        }
+    }
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, x = e % CHUNK;
         NTF[x * LDF + r] = NF[r * LDF + x];
@@ -337,9 +359,9 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     float* YF = DTF;
     float* CB = NTF;  // dL . P contributions [64][LDF] (N^T is no longer needed)
     {
-        const float* Pw = ws.Pw + ch * CHUNK * CHUNK;
-        for (int tile = wid; tile < 16; tile += NW) {  // dL tile (at, xt), k = c
-            const int at = tile / 4, xt = tile % 4;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {  // dL tile (at, xt), k = c
+            const int tile = wid + t * NW, at = tile / 4, xt = tile % 4;
             float4v acc = zero4();
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
                 const int a = 16 * at + 4 * g4 + e;
                 const float dl = (x < a) ? -acc[e] : 0.f;
                 ws.gP[ch * CHUNK * CHUNK + a * CHUNK + x] = s_beta[a] * dl;
-                CB[a * LDF + x] = dl * Pw[a * CHUNK + x];
+                CB[a * LDF + x] = dl * pwv[t][e];
             }
         }
     }
@@ -546,14 +568,25 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    // dA, dP into operand precision, both orientations; Kh^T starts at zero
-    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
-        const int r = e / CHUNK, i = e % CHUNK;
-        const OpT a = from_f32<OpT>(gA[e]), p = from_f32<OpT>(gP[e]);
-        dAs[r * LDC + i] = a;
-        dPs[r * LDC + i] = p;
-        dAT[i * LDC + r] = a;
-        dPT[i * LDC + r] = p;
+    // dA, dP into operand precision, both orientations; Kh^T starts at zero.
+    // All loads are issued before the first LDS write.
+    {
+        constexpr int NE = CHUNK * CHUNK / NT;
+        float av[NE], pv[NE];
+#pragma unroll
+        for (int k2 = 0; k2 < NE; ++k2) {
+            av[k2] = gA[k2 * NT + tid];
+            pv[k2] = gP[k2 * NT + tid];
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NE; ++k2) {
+            const int e = k2 * NT + tid, r = e / CHUNK, i = e % CHUNK;
+            const OpT a = from_f32<OpT>(av[k2]), p = from_f32<OpT>(pv[k2]);
+            dAs[r * LDC + i] = a;
+            dPs[r * LDC + i] = p;
+            dAT[i * LDC + r] = a;
+            dPT[i * LDC + r] = p;
+        }
     }
     for (int e = tid; e < D * LDC; e += NT) KhT[e] = from_f32<OpT>(0.f);
     __syncthreads();
@@ -724,11 +757,20 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         const float* gQt = ws.gQt + ch * CHUNK * D;
         const float* gKt = ws.gKt + ch * CHUNK * D;
         const float* gKb = ws.gKb + ch * CHUNK * D;
+        // every partial is loaded before the first store (the stores could
+        // alias them as far as the compiler knows)
+        float pq[RPP], pkt[RPP], pkb[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            pq[j] = gQt[(r0 + j) * D + cc];
+            pkt[j] = gKt[(r0 + j) * D + cc];
+            pkb[j] = gKb[(r0 + j) * D + cc];
+        }
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = r0 + j;
             const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
-            const float gq = gQt[r * D + cc] * E, gkt = gKt[r * D + cc] * E, gkb = gKb[r * D + cc] * Eb;
+            const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
             const float dqv = gq + Aq[j];
             const float dkv = gkt + gkb + Prow[j] + Ccol[j];
             dG[j] = qq[j] * dqv + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
