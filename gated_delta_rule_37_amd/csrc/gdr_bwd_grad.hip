@@ -38,7 +38,11 @@ struct GLinLayout {
     static constexpr int LDF = CHUNK + 4;                  // fp32 row stride (16-byte pad)
     static constexpr int NF = TT + CHUNK * LDC * OPB;      // N [64][LDF] fp32
     static constexpr int DTF = NF + CHUNK * LDF * 4;       // dT [64][LDF] fp32, later Y
-    static constexpr int BYTES = DTF + CHUNK * LDF * 4;
+    static constexpr int RO = DTF + CHUNK * LDF * 4;       // row operands of phase 1, fragment order:
+    static constexpr int RDO = RO;                         //   scaled-free dO [64][D]
+    static constexpr int RDU = RDO + CHUNK * D * OPB;      //   dU [64][D]
+    static constexpr int RU = RDU + CHUNK * D * OPB;       //   U [64][D]
+    static constexpr int BYTES = RU + CHUNK * D * OPB;
     // phase 3 reuses the Kt..T^T region (dead by then) for N^T and dT^T (fp32)
     static_assert(2 * CHUNK * LDF * 4 <= NF, "N^T and dT^T must fit below N");
 };
@@ -179,93 +183,155 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     __syncthreads();
 
     // ---------------- phase 1: products contracting over the value dimension ----------------
-    // Wave w owns row tile rt = w % 4 (positions 16rt..16rt+15) and every
-    // NHALF-th column tile; its A fragments (dO, dU, U rows) are loaded once.
+    // The row operands (dO, dU, U; 16 rows per tile) are staged in LDS once.
+    // Wave w owns value-column tile w (D/16 tiles, one per wave) of dQt = dO S^T,
+    // dW = -dU S^T and dKb = U dS'^T for all four row tiles, so S and dS' are
+    // read from global memory exactly once; dgamma comes from the same
+    // registers.  The position tiles (dA, dT1) are spread four per column of
+    // waves.  Global stores wait until every load of the phase is issued.
     constexpr int NHALF = NW / 4;
     const int rt = wid & 3, half = wid >> 2;
     {
         constexpr int KQ = D / 32;
         const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
         const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
-        const OpT* Us = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
-        const OpT* dUs = reinterpret_cast<const OpT*>(ws.dUsave) + ch * CHUNK * D;
-        const int arow = 16 * rt + l16;
-        const bool aok = arow < nvalid;
-        const int64_t arow_g = base + (aok ? arow : nvalid - 1) * tokstride;
-        Frag<OpT> aO[KQ], aDU[KQ], aU[KQ];
+        OpT* sDO = reinterpret_cast<OpT*>(smem + L::RDO);
+        const OpT* sDU = reinterpret_cast<const OpT*>(smem + L::RDU);
+        const OpT* sU = reinterpret_cast<const OpT*>(smem + L::RU);
+        // stage dU and U (straight copies) and dO (converted; rows past the end zero)
+        {
+            constexpr int NCP = CHUNK * D * L::OPB / 1024;  // 1 KiB copies per array
+            const char* gdu = static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB;
+            const char* gu = static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB;
+            lds_char* sm = (lds_char*)&smem[0];
+            for (int i = wid; i < 2 * NCP; i += NW) {
+                if (i < NCP) copy16_to_lds(gdu + i * 1024 + lane * 16, sm + L::RDU + i * 1024);
+                else copy16_to_lds(gu + (i - NCP) * 1024 + lane * 16, sm + L::RU + (i - NCP) * 1024);
+            }
+            constexpr int NP = CHUNK * D / 8 / NT;  // 8-element pieces per thread
+#pragma unroll
+            for (int k2 = 0; k2 < NP; ++k2) {
+                const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
+                const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
+                Frag<OpT> x;
+                load_frag_in<InT, OpT>(x, dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
+                if (pos >= nvalid) x.zero();
+                if constexpr (sizeof(OpT) == 2) {
+                    *reinterpret_cast<half8*>(sDO + p * 8) = x.v;
+                } else {
+                    float4v lo, hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = x.v[e];
+                        hi[e] = x.v[4 + e];
+                    }
+                    reinterpret_cast<float4v*>(sDO + p * 8)[0] = lo;
+                    reinterpret_cast<float4v*>(sDO + p * 8)[1] = hi;
+                }
+            }
+        }
+        // this wave's column tile of S and dS' (B operands, k = value column)
+        const int nt = wid;
+        Frag<OpT> bS[KQ], bD[KQ];
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
-            load_frag_in<InT, OpT>(aO[kq], dO + arow_g + 32 * kq + 8 * g4);
-            if (!aok) aO[kq].zero();
-            aDU[kq].load(dUs + ((rt * KQ + kq) * 64 + lane) * 8);
-            aU[kq].load(Us + ((rt * KQ + kq) * 64 + lane) * 8);
+            bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
+            bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
         }
-        const int r_ = 16 * rt + 4 * g4;  // result rows r_ + e of this lane
-        // d tiles: dQt = dO S^T, dW = -dU S^T, dKb = U dS'^T
-#pragma unroll
-        for (int nt = half; nt < D / 16; nt += NHALF) {
-            Frag<OpT> bS[KQ], bD[KQ];
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
-                bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
-            }
-            float4v aq = zero4(), aw = zero4(), ak = zero4();
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                mma(aO[kq], bS[kq], aq);
-                mma(aDU[kq], bS[kq], aw);
-                mma(aU[kq], bD[kq], ak);
-            }
-            const int col = 16 * nt + l16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ws.gQt[ch * CHUNK * D + (r_ + e) * D + col] = scale * aq[e];
-                ws.gKb[ch * CHUNK * D + (r_ + e) * D + col] = ak[e];
-                const OpT w = from_f32<OpT>(-aw[e]);
-                DWs[(r_ + e) * LDR + col] = w;
-                DWT[col * LDC + r_ + e] = w;
-            }
-        }
-        // position tiles: dA = tril(dO U^T) (scaled), dT1 = dU V^T
-#pragma unroll
-        for (int it = half; it < 4; it += NHALF) {
-            const int brow = 16 * it + l16;
+        // position tiles of this wave: it = wid % 4, rows tiles wid / 4 + k NHALF
+        constexpr int NPW = 4 / NHALF;
+        const int itp = wid & 3;
+        Frag<OpT> bV[KQ];
+        {
+            const int brow = 16 * itp + l16;
             const bool bok = brow < nvalid;
             const int64_t brow_g = base + (bok ? brow : nvalid - 1) * tokstride;
-            Frag<OpT> bU[KQ], bV[KQ];
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
-                bU[kq].load(Us + ((it * KQ + kq) * 64 + lane) * 8);
                 load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
                 if (!bok) bV[kq].zero();
             }
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        // dgamma_d = sum_j dS'[d][j] S[d][j], d = 16 nt + l16: this lane's 8 KQ
+        // columns, then the four lane groups in a fixed order
+        float sg = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sg += static_cast<float>(bS[kq].v[e]) * static_cast<float>(bD[kq].v[e]);
+        sg += __shfl_xor(sg, 16);
+        sg += __shfl_xor(sg, 32);
+
+        float rq[4][4], rk[4][4], ra[NPW][4];
+        const int col = 16 * nt + l16;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float4v aq = zero4(), aw = zero4(), ak = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const int fo = ((r4 * KQ + kq) * 64 + lane) * 8;
+                Frag<OpT> fo_, fdu, fu;
+                fo_.load(sDO + fo);
+                fdu.load(sDU + fo);
+                fu.load(sU + fo);
+                mma(fo_, bS[kq], aq);
+                mma(fdu, bS[kq], aw);
+                mma(fu, bD[kq], ak);
+            }
+            const int r0_ = 16 * r4 + 4 * g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                rq[r4][e] = scale * aq[e];
+                rk[r4][e] = ak[e];
+                const OpT w = from_f32<OpT>(-aw[e]);
+                DWs[(r0_ + e) * LDR + col] = w;
+                DWT[col * LDC + r0_ + e] = w;
+            }
+        }
+        // position tiles: dA = tril(dO U^T) (scaled), dT1 = dU V^T
+        Frag<OpT> bU[KQ];
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) bU[kq].load(sU + ((itp * KQ + kq) * 64 + lane) * 8);
+#pragma unroll
+        for (int k = 0; k < NPW; ++k) {
+            const int r4 = (wid >> 2) + k * NHALF;
             float4v aa = zero4(), at = zero4();
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
-                if (it <= rt) mma(aO[kq], bU[kq], aa);
-                mma(aDU[kq], bV[kq], at);
+                const int fo = ((r4 * KQ + kq) * 64 + lane) * 8;
+                Frag<OpT> fo_, fdu;
+                fo_.load(sDO + fo);
+                fdu.load(sDU + fo);
+                if (itp <= r4) mma(fo_, bU[kq], aa);
+                mma(fdu, bV[kq], at);
             }
-            const int col = 16 * it + l16;
+            const int r0_ = 16 * r4 + 4 * g4, pc = 16 * itp + l16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ws.gA[ch * CHUNK * CHUNK + (r_ + e) * CHUNK + col] = (col <= r_ + e) ? scale * aa[e] : 0.f;
-                DTF[(r_ + e) * LDF + col] = at[e];
+                ra[k][e] = (pc <= r0_ + e) ? scale * aa[e] : 0.f;
+                DTF[(r0_ + e) * LDF + pc] = at[e];
             }
         }
-        // dgamma_d = sum_j dS'[d][j] S[d][j]
-        if (tid < D) {
-            float s = 0.f;
+        // stores
 #pragma unroll
-            for (int j8 = 0; j8 < D / 8; ++j8) {
-                Frag<OpT> fs, fd;
-                fs.load(Ss + frag_off<D>(tid, 8 * j8));
-                fd.load(dSs + frag_off<D>(tid, 8 * j8));
+        for (int r4 = 0; r4 < 4; ++r4) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s += static_cast<float>(fs.v[e]) * static_cast<float>(fd.v[e]);
+            for (int e = 0; e < 4; ++e) {
+                ws.gQt[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = rq[r4][e];
+                ws.gKb[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = rk[r4][e];
             }
-            ws.gGam[ch * D + tid] = s;
         }
+#pragma unroll
+        for (int k = 0; k < NPW; ++k) {
+            const int r4 = (wid >> 2) + k * NHALF;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ws.gA[ch * CHUNK * CHUNK + (16 * r4 + 4 * g4 + e) * CHUNK + 16 * itp + l16] = ra[k][e];
+        }
+        if (g4 == 0) ws.gGam[ch * D + col] = sg;
     }
     __syncthreads();
 
@@ -278,32 +344,49 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         Frag<OpT> aT[2];
         aT[0].load(TT + (16 * rt + l16) * LDC + 8 * g4);
         aT[1].load(TT + (16 * rt + l16) * LDC + 32 + 8 * g4);
+        // global loads first (dU^T fragments, the CLVR terms), stores last
+        constexpr int NIT = D / 16 / NHALF;
+        Frag<OpT> bU[NIT][2];
+        float dhv[NIT][4], lmv[NIT];
 #pragma unroll
         for (int ct = half; ct < D / 16; ct += NHALF) {
-            Frag<OpT> bW[2], bU[2];
+            const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
 #pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
-                bW[kq].load(DWT + (16 * ct + l16) * LDC + 32 * kq + 8 * g4);
-                bU[kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
+            for (int kq = 0; kq < 2; ++kq) bU[ii][kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
+            lmv[ii] = (dh && lam) ? lam[h * D + col] : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r_ + e < nvalid ? r_ + e : nvalid - 1;  // clamped; not stored past the end
+                dhv[ii][e] = dh ? to_f32(dh[base + r * tokstride + col]) : 0.f;
             }
+        }
+        float rkt[NIT][4], rdv[NIT][4];
+#pragma unroll
+        for (int ct = half; ct < D / 16; ct += NHALF) {
+            const int ii = (ct - half) / NHALF;
+            Frag<OpT> bW[2];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) bW[kq].load(DWT + (16 * ct + l16) * LDC + 32 * kq + 8 * g4);
             float4v ak = zero4(), av = zero4();
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 mma(aT[kq], bW[kq], ak);
-                mma(aT[kq], bU[kq], av);
+                mma(aT[kq], bU[ii][kq], av);
             }
-            const int col = 16 * ct + l16;
-            const float lm = (dh && lam) ? lam[h * D + col] : 1.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = ak[e];
+                rkt[ii][e] = ak[e];
+                rdv[ii][e] = dh ? __builtin_fmaf(lmv[ii], dhv[ii][e], av[e]) : av[e];  // CLVR: h += lam v
+            }
+        }
+#pragma unroll
+        for (int ct = half; ct < D / 16; ct += NHALF) {
+            const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = rkt[ii][e];
                 const int r = r_ + e;
-                if (r < nvalid) {
-                    const int64_t idx = base + r * tokstride + col;
-                    float g = av[e];
-                    if (dh) g = __builtin_fmaf(lm, to_f32(dh[idx]), g);  // CLVR: h += lam v
-                    dv[idx] = from_f32<OutT>(g);
-                }
+                if (r < nvalid) dv[base + r * tokstride + col] = from_f32<OutT>(rdv[ii][e]);
             }
         }
 #pragma unroll
@@ -411,8 +494,11 @@ static hipError_t launch_grad_lin_g(bool in_f32, bool out_f32, int64_t B, int64_
                                     const float* alpha, const void* dO, const void* dh, const float* lam,
                                     void* dv, float* dbeta, const ChunkWs& ws, hipStream_t stream) {
     if (in_f32) {
-        if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
-        return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+        if constexpr (D == 64) {
+            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+        }
+        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
     }
     if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
     return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
