@@ -68,7 +68,14 @@ struct IntraLayout {
     // N (and, during phase 2, the fp32 P staging) must not overlap phase 1-2 buffers
     static constexpr int NM = (PL + PL_BYTES > END12) ? PL + PL_BYTES : END12;
     static constexpr int END34 = NM + CHUNK * CHUNK * 4;
-    static constexpr int BYTES = END12 > END34 ? END12 : END34;
+    static constexpr int BASE_BYTES = END12 > END34 ? END12 : END34;
+    // fp16 operands: Qt and Kb (fragment order) and the updated h rows are
+    // assembled in LDS and written out with full 16-byte stores
+    static constexpr bool STAGE = !IN_F32;
+    static constexpr int QTS = BASE_BYTES;
+    static constexpr int KBS = QTS + (STAGE ? CHUNK * D * OPB : 0);
+    static constexpr int HS = KBS + (STAGE ? CHUNK * D * OPB : 0);
+    static constexpr int BYTES = HS + (STAGE ? CHUNK * D * 2 : 0);
     // operand-precision limit on the in-block decay range (log2 units)
     static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
     // chunk decay beyond which 2^G or 2^-G leaves the fp32 range (log2 units)
@@ -108,6 +115,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     OpT* Kq = reinterpret_cast<OpT*>(smem + L::KQ);
     OpT* Qq = reinterpret_cast<OpT*>(smem + L::QQ);
     OpT* Kh = reinterpret_cast<OpT*>(smem + L::KH);
+    OpT* QtS = reinterpret_cast<OpT*>(smem + L::QTS);  // staged outputs (fp16 operands only)
+    OpT* KbS = reinterpret_cast<OpT*>(smem + L::KBS);
     OpT* KtT = reinterpret_cast<OpT*>(smem + L::KTT);
     OpT* VT = reinterpret_cast<OpT*>(smem + L::VT);
     float* Pm = reinterpret_cast<float*>(smem + L::PL);
@@ -127,6 +136,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     const InT* k = reinterpret_cast<const InT*>(k_);
     const InT* v = reinterpret_cast<const InT*>(v_);
     InT* hh = reinterpret_cast<InT*>(h_);
+    InT* HS = reinterpret_cast<InT*>(smem + L::HS);
     const int64_t tokstride = static_cast<int64_t>(H) * D;
     const int64_t base = ((b * T + t0) * H + h) * D;  // element (row 0, channel 0) of this chunk
     const int64_t nvalid64 = T - t0;
@@ -256,7 +266,10 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 kb[j] = kk[j] * exp2_fast(glast - G[j]);
                 fq = exp2_fast(G[j] - carry);
             }
-            if constexpr (FO) Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
+            if constexpr (FO) {
+                if constexpr (L::STAGE) QtS[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
+                else Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
+            }
             if constexpr (GATE == GATE_CHANNEL) {
                 Kq[r * LDR + cc] = from_f32<OpT>(kk[j] * fq);
                 Qq[r * LDR + cc] = from_f32<OpT>(qq[j] * fq);
@@ -266,8 +279,12 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 Kh[r * LDR + cc] = from_f32<OpT>(kk[j]);
             }
             if constexpr (BWD) {
-                OpT* Kb_g = reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D;
-                Kb_g[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
+                if constexpr (L::STAGE) {
+                    KbS[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
+                } else {
+                    OpT* Kb_g = reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D;
+                    Kb_g[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
+                }
             }
         }
         // Kb^T is the A operand of Kb^T U (rows d, k = position): two runs of 8
@@ -290,10 +307,37 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = r0 + j;
-            if (r < nvalid) hh[base + r * tokstride + cc] = from_f32<InT>(__builtin_fmaf(lm, vv[j], to_f32(hv[j])));
+            const InT nh = from_f32<InT>(__builtin_fmaf(lm, vv[j], to_f32(hv[j])));
+            if constexpr (L::STAGE) HS[r * D + cc] = nh;
+            else if (r < nvalid) hh[base + r * tokstride + cc] = nh;
         }
     }
     __syncthreads();  // Kq, Qq (and Kh for scalar gates), block-end values
+    if constexpr (L::STAGE) {
+        // staged outputs: fragment-order blocks are straight copies; h rows go
+        // back to their tokens (rows past the end are not written)
+        constexpr int NPC = CHUNK * D * 2 / 16 / NT;  // 16-byte pieces per thread
+        if constexpr (FO) {
+            uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<OpT*>(ws.Qt) + ch * CHUNK * D);
+#pragma unroll
+            for (int k2 = 0; k2 < NPC; ++k2) dst[k2 * NT + tid] = reinterpret_cast<const uint4*>(QtS)[k2 * NT + tid];
+        }
+        if constexpr (BWD) {
+            uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D);
+#pragma unroll
+            for (int k2 = 0; k2 < NPC; ++k2) dst[k2 * NT + tid] = reinterpret_cast<const uint4*>(KbS)[k2 * NT + tid];
+        }
+        if (hh) {
+            constexpr int PPR = D * 2 / 16;  // pieces per row
+#pragma unroll
+            for (int k2 = 0; k2 < NPC; ++k2) {
+                const int p = k2 * NT + tid, r = p / PPR, c8 = (p % PPR) * 8;
+                if (r < nvalid)
+                    *reinterpret_cast<uint4*>(hh + base + r * tokstride + c8) =
+                        *reinterpret_cast<const uint4*>(HS + r * D + c8);
+            }
+        }
+    }
 
     // ---------------- phase 2: P = Kt Kh^T and A = Qt Kh^T on the matrix cores ----------------
     // Tiles are computed transposed (Kh rows as the A operand), so lane l ends up
