@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     OutT* o = reinterpret_cast<OutT*>(o_);
     const int64_t tstride = static_cast<int64_t>(H) * D;
     const int64_t obase = ((b * T + c * CHUNK) * H + h) * D;
+    float res[4][CPW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         Frag<_Float16> fq[D / 32], fa[2];
@@ -114,13 +115,31 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
                 fu.v = *reinterpret_cast<const half8*>(uT + (16 * ct + l16) * LDU + 32 * kq + 8 * g4);
                 mma(fa[kq], fu, acc);  // the upper blocks of A are zero
             }
-            const int col = 16 * ct + l16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * g4 + e;
-                if (r < nvalid) o[obase + r * tstride + col] = from_f32<OutT>(scale * acc[e]);
-            }
+            for (int e = 0; e < 4; ++e) res[rt][ci][e] = scale * acc[e];
         }
+    }
+    // assemble the output rows in LDS (over S^T, no longer read) and write them
+    // with 16-byte stores; rows past the end are not written
+    __syncthreads();
+    static_assert(CHUNK * D * sizeof(OutT) <= L::QT, "output rows must fit over S^T and U^T");
+    OutT* so = reinterpret_cast<OutT*>(smem + L::ST);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                so[(16 * rt + 4 * g4 + e) * D + 16 * (wid * CPW + ci) + l16] = from_f32<OutT>(res[rt][ci][e]);
+    __syncthreads();
+    constexpr int EPP = 16 / sizeof(OutT);      // elements per 16-byte piece
+    constexpr int PPR = D / EPP;                // pieces per row
+    constexpr int NPC = CHUNK * PPR / 256;      // pieces per thread
+#pragma unroll
+    for (int k2 = 0; k2 < NPC; ++k2) {
+        const int p = k2 * 256 + tid, r = p / PPR, c0 = (p % PPR) * EPP;
+        if (r < nvalid)
+            *reinterpret_cast<uint4*>(o + obase + r * tstride + c0) = *reinterpret_cast<const uint4*>(so + r * D + c0);
     }
 }
 

@@ -68,14 +68,16 @@ def desc(B=2, T=100, H=3, d=128, gate=2, in_dt=0, out_dt=1, scale=1.0, chunk=0):
 
 def test_workspace_size_formula(lib):
     # per chunk-head: W, Ut, Qt, Kb^T ([64][d] each), A [64][64] in operand
-    # precision, gamma [d] fp32; every region rounded up to 256 bytes
+    # precision, gamma [d] fp32, the chunk-start state [d][d] and U [64][d] in
+    # operand precision; every region rounded up to 256 bytes
     def al(x):
         return (x + 255) // 256 * 256
 
     for d, in_dt, opb in ((128, 0, 2), (64, 1, 4), (64, 0, 2)):
         dd = desc(B=2, T=130, H=3, d=d, in_dt=in_dt)
         nch = 2 * 3 * 3
-        expect = 4 * al(nch * 64 * d * opb) + al(nch * 64 * 64 * opb) + al(nch * d * 4)
+        expect = (5 * al(nch * 64 * d * opb) + al(nch * 64 * 64 * opb) + al(nch * d * 4)
+                  + al(nch * d * d * opb))
         assert lib.gdr_workspace_size(ctypes.byref(dd), 0) == expect
         assert lib.gdr_workspace_size(ctypes.byref(dd), 1) > expect
     assert lib.gdr_workspace_size(ctypes.byref(desc(T=0)), 0) == 0
