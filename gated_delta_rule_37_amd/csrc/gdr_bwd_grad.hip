@@ -114,6 +114,69 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     const InT* v = reinterpret_cast<const InT*>(v_);
     const InT* dO = reinterpret_cast<const InT*>(dO_);
 
+    // ---------------- phase 1 operands, fetched first so that their latency
+    // overlaps phase 0: dU and U copied to LDS, dO converted into LDS, and this
+    // wave's S, dS' and V fragments into registers
+    constexpr int KQ1 = D / 32;
+    OpT* sDO = reinterpret_cast<OpT*>(smem + L::RDO);
+    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
+    const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
+    Frag<OpT> bS[KQ1], bD[KQ1], bV[KQ1];
+    const int itp = wid & 3;
+    {
+        constexpr int KQ = KQ1;
+        // stage dU and U (straight copies) and dO (converted; rows past the end zero)
+        {
+            constexpr int NCP = CHUNK * D * L::OPB / 1024;  // 1 KiB copies per array
+            const char* gdu = static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB;
+            const char* gu = static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB;
+            lds_char* sm = (lds_char*)&smem[0];
+            for (int i = wid; i < 2 * NCP; i += NW) {
+                if (i < NCP) copy16_to_lds(gdu + i * 1024 + lane * 16, sm + L::RDU + i * 1024);
+                else copy16_to_lds(gu + (i - NCP) * 1024 + lane * 16, sm + L::RU + (i - NCP) * 1024);
+            }
+            constexpr int NP = CHUNK * D / 8 / NT;  // 8-element pieces per thread
+#pragma unroll
+            for (int k2 = 0; k2 < NP; ++k2) {
+                const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
+                const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
+                Frag<OpT> x;
+                load_frag_in<InT, OpT>(x, dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
+                if (pos >= nvalid) x.zero();
+                if constexpr (sizeof(OpT) == 2) {
+                    *reinterpret_cast<half8*>(sDO + p * 8) = x.v;
+                } else {
+                    float4v lo, hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = x.v[e];
+                        hi[e] = x.v[4 + e];
+                    }
+                    reinterpret_cast<float4v*>(sDO + p * 8)[0] = lo;
+                    reinterpret_cast<float4v*>(sDO + p * 8)[1] = hi;
+                }
+            }
+        }
+        // this wave's column tile of S and dS' (B operands, k = value column)
+        const int nt = wid;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+            bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
+            bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
+        }
+        // V rows of this wave's position tiles (it = wid % 4)
+        {
+            const int brow = 16 * itp + l16;
+            const bool bok = brow < nvalid;
+            const int64_t brow_g = base + (bok ? brow : nvalid - 1) * tokstride;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
+                if (!bok) bV[kq].zero();
+            }
+        }
+    }
+
     // ---------------- phase 0: Kt = K 2^G, N, T^T ----------------
     float G[RPP], kk[RPP];
 #pragma unroll
@@ -193,66 +256,11 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     const int rt = wid & 3, half = wid >> 2;
     {
         constexpr int KQ = D / 32;
-        const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
-        const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
-        OpT* sDO = reinterpret_cast<OpT*>(smem + L::RDO);
         const OpT* sDU = reinterpret_cast<const OpT*>(smem + L::RDU);
         const OpT* sU = reinterpret_cast<const OpT*>(smem + L::RU);
-        // stage dU and U (straight copies) and dO (converted; rows past the end zero)
-        {
-            constexpr int NCP = CHUNK * D * L::OPB / 1024;  // 1 KiB copies per array
-            const char* gdu = static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB;
-            const char* gu = static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB;
-            lds_char* sm = (lds_char*)&smem[0];
-            for (int i = wid; i < 2 * NCP; i += NW) {
-                if (i < NCP) copy16_to_lds(gdu + i * 1024 + lane * 16, sm + L::RDU + i * 1024);
-                else copy16_to_lds(gu + (i - NCP) * 1024 + lane * 16, sm + L::RU + (i - NCP) * 1024);
-            }
-            constexpr int NP = CHUNK * D / 8 / NT;  // 8-element pieces per thread
-#pragma unroll
-            for (int k2 = 0; k2 < NP; ++k2) {
-                const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
-                const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
-                Frag<OpT> x;
-                load_frag_in<InT, OpT>(x, dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
-                if (pos >= nvalid) x.zero();
-                if constexpr (sizeof(OpT) == 2) {
-                    *reinterpret_cast<half8*>(sDO + p * 8) = x.v;
-                } else {
-                    float4v lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = x.v[e];
-                        hi[e] = x.v[4 + e];
-                    }
-                    reinterpret_cast<float4v*>(sDO + p * 8)[0] = lo;
-                    reinterpret_cast<float4v*>(sDO + p * 8)[1] = hi;
-                }
-            }
-        }
-        // this wave's column tile of S and dS' (B operands, k = value column)
-        const int nt = wid;
-        Frag<OpT> bS[KQ], bD[KQ];
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-            bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
-            bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
-        }
-        // position tiles of this wave: it = wid % 4, rows tiles wid / 4 + k NHALF
-        constexpr int NPW = 4 / NHALF;
-        const int itp = wid & 3;
-        Frag<OpT> bV[KQ];
-        {
-            const int brow = 16 * itp + l16;
-            const bool bok = brow < nvalid;
-            const int64_t brow_g = base + (bok ? brow : nvalid - 1) * tokstride;
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
-                if (!bok) bV[kq].zero();
-            }
-        }
-        wait_vmcnt<0>();
+        constexpr int NPW = 4 / NHALF;  // position tiles per wave
+        const int nt = wid;             // this wave's value-column tile
+        wait_vmcnt<0>();                // the copies into LDS have landed
         __syncthreads();
 
         // dgamma_d = sum_j dS'[d][j] S[d][j], d = 16 nt + l16: this lane's 8 KQ

@@ -268,36 +268,47 @@ struct BwdStage {
     static constexpr int DO = WT + MAT;         // dO rows of this slice: [64][16] in the input dtype (bf16)
     static constexpr int GAM = DO + 2048;       // D fp32 in a 1 KiB slot
     static constexpr int BYTES = GAM + 1024;
-    static constexpr int NA = (CHUNK * CHUNK * 2 + MAT) / 1024 + 2 + 1;  // copies before the first barrier
     static constexpr int NSL = D / 16;
     static constexpr int NL = (CHUNK * CHUNK * 2 + 3 * MAT) / NSL / 128 + 1;  // lines touched per chunk
     static constexpr int NT = (NL + 63) / 64;
 };
 
-// PART 0: A^T, Kb, dO rows, gamma; PART 1: Qt^T, W^T.
+// PART 0: A^T, dO rows, gamma; PART 1: Kb; PART 2: Qt^T; PART 3: W^T.
 template <int D, int PART>
 __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c, int64_t b,
                                           int64_t T, int H, int h, const void* dO, int j0, int lane) {
     using L = BwdStage<D>;
     if constexpr (PART == 1) {
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
+    } else if constexpr (PART == 2) {
         copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.QtT) + ch * L::MAT, dst + L::QTT, lane);
+    } else if constexpr (PART == 3) {
         copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.WT) + ch * L::MAT, dst + L::WT, lane);
-        return;
-    }
-    copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2,
-                                                dst + L::AT, lane);
-    copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
-    // dO rows: position pos = 32 i + lane / 2, half lane % 2 of its 16 columns
-    // (rows past the end re-read the last token; they are zeroed at use)
+    } else {
+        copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2,
+                                                    dst + L::AT, lane);
+        // dO rows: position pos = 32 i + lane / 2, half lane % 2 of its 16 columns
+        // (rows past the end re-read the last token; they are zeroed at use)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
-        const int64_t t = t0 < T ? t0 : T - 1;
-        const char* src = static_cast<const char*>(dO) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
-        copy16_to_lds(src, dst + L::DO + i * 1024);
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
+            const int64_t t = t0 < T ? t0 : T - 1;
+            const char* src = static_cast<const char*>(dO) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
+            copy16_to_lds(src, dst + L::DO + i * 1024);
+        }
+        const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
+        copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
     }
-    const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
-    copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+}
+
+// Loader wave `part` (0..3) copies its share of chunk ch.
+template <int D>
+__device__ __forceinline__ void stage_bwd_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c,
+                                               int64_t b, int64_t T, int H, int h, const void* dO, int j0, int lane) {
+    if (part == 0) stage_bwd<D, 0>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
+    else if (part == 1) stage_bwd<D, 1>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
+    else if (part == 2) stage_bwd<D, 2>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
+    else stage_bwd<D, 3>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
 }
 
 template <int D>
@@ -320,7 +331,7 @@ __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, in
 }
 
 template <int D>
-__global__ __launch_bounds__(320) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
+__global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                             const void* __restrict__ dO,
                                                             const float* __restrict__ dST,
                                                             float* __restrict__ dS0) {
@@ -348,25 +359,27 @@ __global__ __launch_bounds__(320) void state_bwd_lds_kernel(int64_t T, int H, in
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
 
-    if (wid == 4) {
-        // Loader: chunk c-1 goes into the buffer chunk c+1 used (free since the
-        // end of that step); copies are split around the first barrier.
-        if (NC > 0) {
-            stage_bwd<D, 0>(sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
-            stage_bwd<D, 1>(sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
-        }
+    if (wid >= 4) {
+        // Loaders: chunk c-1 goes into the buffer chunk c+1 used (free since the
+        // end of that step).  Four waves each copy one part (A^T, dO and gamma;
+        // Kb; Qt^T; W^T), so four times as many copies are in flight as with
+        // one; wave 4 also warms the L2.
+        const int part = wid - 4;
+        const bool w4 = part == 0;
+        if (NC > 0) stage_bwd_part<D>(part, sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
+        if (w4) {
 #pragma unroll 1
-        for (int64_t c = NC - 2; c >= 0 && c > NC - 1 - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = NC - 2; c >= 0 && c > NC - 1 - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
+        }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         int nb = 1;  // buffer of chunk c-1
 #pragma unroll 1
         for (int64_t c = NC - 1; c >= 0; --c) {
-            const bool st = c >= 1, tpf = c - PF >= 0;
-            if (st) stage_bwd<D, 0>(sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
-            __builtin_amdgcn_s_barrier();
-            if (st) stage_bwd<D, 1>(sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
+            const bool st = c >= 1, tpf = w4 && c - PF >= 0;
+            if (st) stage_bwd_part<D>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
             if (tpf) touch_bwd<D>(sdummy, ws, bh * NC + c - PF, slice, lane);
+            __builtin_amdgcn_s_barrier();
             // chunk c-1 must have landed; only this step's touches may stay in flight
             if (tpf) wait_vmcnt<L::NT>();
             else wait_vmcnt<0>();
@@ -506,7 +519,7 @@ static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, fl
     const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
     if constexpr (!IN_F32)
-        hipLaunchKernelGGL((state_bwd_lds_kernel<D>), dim3((unsigned)nblk), dim3(320), 0, stream, T, H, NC, scale,
+        hipLaunchKernelGGL((state_bwd_lds_kernel<D>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC, scale,
                            ws, dO, dST, dS0);
     else
         hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,

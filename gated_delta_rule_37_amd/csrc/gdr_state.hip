@@ -363,32 +363,49 @@ struct ChainStage {
     static constexpr int UT = 2 * MAT;          // this slice's four 16x16 tiles of Ut
     static constexpr int GAM = UT + 2048;       // D fp32 in a 1 KiB slot
     static constexpr int BYTES = GAM + 1024;
-    static constexpr int ND = 2 * MAT / 1024 + 2 + 1;  // copies per chunk
+    static constexpr int ND0 = MAT / 2048 + 2 + 1;     // copies per chunk of loader wave 0
+    static constexpr int NDP = MAT / 2048;             // copies per chunk of loader waves 1-3
     static constexpr int NSL = D / 16;
     static constexpr int QL = MAT / NSL / 128;         // 128-byte lines per slice of one array
     static constexpr int NT = (3 * QL + 1 + 63) / 64;  // touch copies per chunk
 };
 
-// Chunk ch's operands for slice `slice` into `dst`; issued by one wave in two
-// parts (PART 0: W, Ut, gamma; PART 1: Kb^T).
+// Chunk ch's operands for slice `slice` into `dst`, in four parts, one per
+// loader wave: PART 0 the first half of W, Ut and gamma; PART 1 the second half
+// of W; PARTs 2 and 3 the halves of Kb^T.
 template <int D, int PART>
 __device__ __forceinline__ void stage_chain(lds_char* dst, const ChunkWs& ws, int64_t ch, int slice, int lane) {
     using L = ChainStage<D>;
+    constexpr int HALF = L::MAT / 2;
     if constexpr (PART == 1) {
-        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.KbT) + ch * L::MAT, dst + L::KBT, lane);
-        return;
-    }
-    copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT, dst + L::W, lane);
-    // Ut tiles (rt, slice), rt = 0..3, 512 bytes each: two tiles per copy
-    const char* U = static_cast<const char*>(ws.Ut) + ch * L::MAT;
+        copy_block_to_lds<HALF / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT + HALF, dst + L::W + HALF, lane);
+    } else if constexpr (PART == 2) {
+        copy_block_to_lds<HALF / 1024>(static_cast<const char*>(ws.KbT) + ch * L::MAT, dst + L::KBT, lane);
+    } else if constexpr (PART == 3) {
+        copy_block_to_lds<HALF / 1024>(static_cast<const char*>(ws.KbT) + ch * L::MAT + HALF, dst + L::KBT + HALF,
+                                       lane);
+    } else {
+        copy_block_to_lds<HALF / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT, dst + L::W, lane);
+        // Ut tiles (rt, slice), rt = 0..3, 512 bytes each: two tiles per copy
+        const char* U = static_cast<const char*>(ws.Ut) + ch * L::MAT;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int rt = 2 * i + (lane >> 5);
-        copy16_to_lds(U + (rt * (D / 16) + slice) * 512 + (lane & 31) * 16, dst + L::UT + i * 1024);
+        for (int i = 0; i < 2; ++i) {
+            const int rt = 2 * i + (lane >> 5);
+            copy16_to_lds(U + (rt * (D / 16) + slice) * 512 + (lane & 31) * 16, dst + L::UT + i * 1024);
+        }
+        // gamma: D floats; lanes past the end re-read the first piece into the slot's tail
+        const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
+        copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
     }
-    // gamma: D floats; lanes past the end re-read the first piece into the slot's tail
-    const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
-    copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+}
+
+template <int D>
+__device__ __forceinline__ void stage_chain_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int slice,
+                                                 int lane) {
+    if (part == 0) stage_chain<D, 0>(dst, ws, ch, slice, lane);
+    else if (part == 1) stage_chain<D, 1>(dst, ws, ch, slice, lane);
+    else if (part == 2) stage_chain<D, 2>(dst, ws, ch, slice, lane);
+    else stage_chain<D, 3>(dst, ws, ch, slice, lane);
 }
 
 // One dword of each 128-byte line of this slice's share of chunk ch.
@@ -442,7 +459,7 @@ __device__ __forceinline__ void wait_outstanding(int n) {
 }
 
 template <int D>
-__global__ __launch_bounds__(320) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
+__global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
                                                           const float* S0, float* ST) {
     using Cfg = StateCfg<D, false>;
     using OpT = _Float16;
@@ -468,35 +485,37 @@ __global__ __launch_bounds__(320) void state_chain_kernel(int64_t T, int H, int6
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
 
-    if (wid == 4) {
-        // Loader.  Two barriers per step, like the compute waves; it never
-        // fences, so its own copies stay in flight across the first one.
-        if (NC > 0) {
-            stage_chain<D, 0>(sbuf, ws, bh * NC, slice, lane);
-            stage_chain<D, 1>(sbuf, ws, bh * NC, slice, lane);
-        }
-        if (NC > 1) {
-            stage_chain<D, 0>(sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
-            stage_chain<D, 1>(sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
-        }
+    if (wid >= 4) {
+        // Loaders (waves 4-7, one part each).  Two barriers per step, like the
+        // compute waves; they never fence, so their copies stay in flight
+        // across the first one.  Wave 4 also warms the L2.
+        const int part = wid - 4;
+        const bool w4 = part == 0;
+        if (NC > 0) stage_chain_part<D>(part, sbuf, ws, bh * NC, slice, lane);
+        if (NC > 1) stage_chain_part<D>(part, sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
+        if (w4) {
 #pragma unroll 1
-        for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
+        }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         int nb = 2;  // buffer of chunk c + 2
 #pragma unroll 1
         for (int64_t c = 0; c < NC; ++c) {
-            const bool st2 = c + 2 < NC, tpf = c + PF < NC;
-            // the copies are split around the first barrier so that issuing
-            // them never holds the compute waves up
-            if (st2) stage_chain<D, 0>(sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
-            __builtin_amdgcn_s_barrier();
-            if (st2) stage_chain<D, 1>(sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
+            const bool st2 = c + 2 < NC, tpf = w4 && c + PF < NC;
+            if (st2) stage_chain_part<D>(part, sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
             if (tpf) touch_chain<D>(sdummy, ws, bh * NC + c + PF, slice, lane);
             nb = nb == 2 ? 0 : nb + 1;
-            // chunk c+1 must have landed; later copies may stay in flight
-            const int n = ((c >= 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND : 0) + (tpf ? L::NT : 0);
-            wait_outstanding<L::ND, L::NT>(n);
+            __builtin_amdgcn_s_barrier();
+            // this wave's copies of chunk c+1 must have landed; later ones may stay in flight
+            if (w4) {
+                const int n = ((c >= 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND0 : 0) + (tpf ? L::NT : 0);
+                wait_outstanding<L::ND0, L::NT>(n);
+            } else if (st2) {
+                wait_vmcnt<L::NDP>();
+            } else {
+                wait_vmcnt<0>();
+            }
             __builtin_amdgcn_s_barrier();
         }
         return;
@@ -541,7 +560,7 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
     if constexpr (!IN_F32) {
         // fp16 operands: the chain pass always saves the chunk-start states and U;
         // the output is produced by output_kernel
-        hipLaunchKernelGGL((state_chain_kernel<D>), dim3((unsigned)nblk), dim3(320), 0, stream, T, H, NC, ws, S0,
+        hipLaunchKernelGGL((state_chain_kernel<D>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC, ws, S0,
                            ST);
         return hipGetLastError();
     }
