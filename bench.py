@@ -78,8 +78,9 @@ class KernelTimer:
 PER_TH_BYTES = {
     "intra_fwd": 3 * 256 + 4 + 512 + 2 * 256,          # q,k,v,beta,alpha read; h read+write (CLVR)
     "intra_train": 3 * 256 + 4 + 512 + 2 * 256,        # the same, training forward
-    "state_fwd": 256,                                  # o written
-    "state_train": 256,                                # o written
+    "state_fwd": 0,                                    # intermediates only (+ S_T)
+    "state_train": 0,                                  # intermediates only (+ S_T)
+    "output": 256,                                     # o written
     "intra_bwd": 3 * 256 + 4 + 512,                    # q,k,v,beta,alpha read
     "state_fwd_save": 0,                               # intermediates only
     "state_bwd": 256,                                  # dO read
@@ -94,6 +95,7 @@ PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
 KERNEL_SOURCES = {
     "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"], "intra_train": ["gdr_intra.hip"],
     "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"], "state_train": ["gdr_state.hip"],
+    "output": ["gdr_output.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
     "decode": ["gdr_decode.hip"],
@@ -234,7 +236,7 @@ def main():
     # q,k,v 3*256 + beta 4 + alpha 512 read, o 256 written -> 1540; CLVR reads and
     # writes h (2*256).
     th = B * T * H
-    fwd_bytes = th * (1540 + 512)
+    fwd_bytes = th * (1540 + 512)  # the whole forward: intra + state + output
     fwd_flops = th * (5 * 64 * d + 6 * d * d + 64 * 64 / 3)
     kbytes = kernel_alg_bytes(B, T, H, d)
     for n, kr in kernels.items():
