@@ -56,8 +56,11 @@ def _load():
             lib.oracle_decode.argtypes = [i64] * 4 + [cint, dbl] + [ptr] * 7 + [cint]
             lib.oracle_clvr_forward.argtypes = [i64] * 4 + [ptr] * 4
             lib.oracle_clvr_backward.argtypes = [i64] * 4 + [ptr] * 5
+            lib.oracle_forward_errors.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 9 + [cint]
+            lib.oracle_backward_errors.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 15 + [cint]
             for f in (lib.oracle_forward, lib.oracle_backward, lib.oracle_decode,
-                      lib.oracle_clvr_forward, lib.oracle_clvr_backward):
+                      lib.oracle_clvr_forward, lib.oracle_clvr_backward,
+                      lib.oracle_forward_errors, lib.oracle_backward_errors):
                 f.restype = cint
             _lib = lib
     return _lib
@@ -94,27 +97,38 @@ def gate_kind(alpha, q):
     return GATE_SCALAR if np.ndim(alpha) == 3 else GATE_CHANNEL
 
 
-def forward(q, k, v, beta, alpha=None, S0=None, scale=1.0, nthreads=None):
-    """Token-by-token forward.  Returns ``(o [B,T,H,dv], S_T [B,H,dk,dv])``."""
+def forward(q, k, v, beta, alpha=None, S0=None, scale=1.0, nthreads=None, want_errors=False):
+    """Token-by-token forward.  Returns ``(o [B,T,H,dv], S_T [B,H,dk,dv])``, and
+    with ``want_errors`` also the write errors
+    ``E [B,T,H,dv]``, ``e_t = v_t - (Diag(alpha_t) S_{t-1})^T k_t``."""
     q, k, v, beta, alpha, S0 = map(_f64, (q, k, v, beta, alpha, S0))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     gate = gate_kind(alpha, q)
     o = np.zeros((B, T, H, dv))
     ST = np.zeros((B, H, dk, dv))
+    if want_errors:
+        E = np.zeros((B, T, H, dv))
+        rc = _load().oracle_forward_errors(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
+                                           _p(beta), _p(alpha), _p(S0), _p(o), _p(ST), _p(E),
+                                           _threads(nthreads))
+        _check(rc, "oracle_forward_errors")
+        return o, ST, E
     rc = _load().oracle_forward(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
                                 _p(beta), _p(alpha), _p(S0), _p(o), _p(ST), _threads(nthreads))
     _check(rc, "oracle_forward")
     return o, ST
 
 
-def backward(q, k, v, beta, alpha, S0, dO, dST=None, scale=1.0, nthreads=None):
+def backward(q, k, v, beta, alpha, S0, dO, dST=None, scale=1.0, nthreads=None, dE=None):
     """Adjoint of :func:`forward`.
 
     Returns a dict with ``dq, dk, dv, dbeta, dalpha`` (None for DeltaNet) and
     ``dS0``.  ``dalpha`` is the derivative with respect to alpha itself.
+    ``dE`` [B,T,H,dv], when given, is a gradient arriving at the write errors
+    that ``forward(..., want_errors=True)`` returns.
     """
-    q, k, v, beta, alpha, S0, dO, dST = map(_f64, (q, k, v, beta, alpha, S0, dO, dST))
+    q, k, v, beta, alpha, S0, dO, dST, dE = map(_f64, (q, k, v, beta, alpha, S0, dO, dST, dE))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     gate = gate_kind(alpha, q)
@@ -124,10 +138,17 @@ def backward(q, k, v, beta, alpha, S0, dO, dST=None, scale=1.0, nthreads=None):
     dbeta = np.zeros_like(beta)
     dalpha = None if alpha is None else np.zeros_like(alpha)
     dS0 = np.zeros((B, H, dk, dv))
-    rc = _load().oracle_backward(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
-                                 _p(beta), _p(alpha), _p(S0), _p(dO), _p(dST), _p(dq), _p(dk_),
-                                 _p(dv_), _p(dbeta), _p(dalpha), _p(dS0), _threads(nthreads))
-    _check(rc, "oracle_backward")
+    if dE is not None:
+        rc = _load().oracle_backward_errors(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
+                                            _p(beta), _p(alpha), _p(S0), _p(dO), _p(dST), _p(dE),
+                                            _p(dq), _p(dk_), _p(dv_), _p(dbeta), _p(dalpha), _p(dS0),
+                                            _threads(nthreads))
+        _check(rc, "oracle_backward_errors")
+    else:
+        rc = _load().oracle_backward(B, T, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v),
+                                     _p(beta), _p(alpha), _p(S0), _p(dO), _p(dST), _p(dq), _p(dk_),
+                                     _p(dv_), _p(dbeta), _p(dalpha), _p(dS0), _threads(nthreads))
+        _check(rc, "oracle_backward")
     return {"dq": dq, "dk": dk_, "dv": dv_, "dbeta": dbeta, "dalpha": dalpha, "dS0": dS0}
 
 
@@ -165,3 +186,17 @@ def clvr_backward(dh, v, lam=None):
     rc = _load().oracle_clvr_backward(B, T, H, dv, _p(dh), _p(v), _p(lam), _p(dv_acc), _p(dlam))
     _check(rc, "oracle_clvr_backward")
     return dv_acc, dlam
+
+
+def cler_forward(h, E, lam=None):
+    """Error routing into the hidden stream (CLER-H): ``h + lam * e`` per hidden
+    channel ``h*dv + j``, with E the write errors from
+    ``forward(..., want_errors=True)``.  The routing is CLVR's with the write
+    error in place of the value."""
+    return clvr_forward(h, E, lam)
+
+
+def cler_backward(dh, E, lam=None):
+    """Returns ``(dE [B,T,H,dv], dlam [H*dv])`` for :func:`cler_forward`; dE is
+    then passed to :func:`backward`."""
+    return clvr_backward(dh, E, lam)

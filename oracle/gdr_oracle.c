@@ -34,6 +34,8 @@ typedef struct {
     double scale;
     const double *q, *k, *v, *beta, *alpha, *S0, *dO, *dST;
     double *o, *ST, *dq, *dk_out, *dv_out, *dbeta, *dalpha, *dS0;
+    double* E;        /* forward: write errors e_t, [B,T,H,dv] (NULL: not written) */
+    const double* dE; /* backward: gradient arriving at e_t, [B,T,H,dv] (NULL: zero) */
     int64_t N; /* decode: number of sequences */
     double* S; /* decode: state in/out */
     int status;
@@ -148,6 +150,7 @@ static void forward_slab(job_t* j, int64_t slab) {
         const int64_t tok = (b * T + t) * H + h;
         for (int64_t i = 0; i < dk; ++i) a[i] = gate_at(j, b, t, h, i);
         step(dk, dv, a, j->k + tok * dk, j->v + tok * dv, j->beta[tok], S, Sd, e, u, Sn);
+        if (j->E) memcpy(j->E + tok * dv, e, sizeof(double) * (size_t)dv);
         double* tmp = S;
         S = Sn;
         Sn = tmp;
@@ -184,6 +187,21 @@ int oracle_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int 
     return run_slabs(&j, nthreads, forward_slab);
 }
 
+int oracle_forward_errors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate,
+                          double scale, const double* q, const double* k, const double* v,
+                          const double* beta, const double* alpha, const double* S0, double* o,
+                          double* ST, double* E, int nthreads) {
+    if (check_common(B, T, H, dk, dv, gate)) return -1;
+    if (T > 0 && (!q || !k || !v || !beta || !o || !E)) return -1;
+    if (gate != ORACLE_GATE_NONE && T > 0 && !alpha) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.B = B; j.T = T; j.H = H; j.dk = dk; j.dv = dv; j.gate = gate; j.scale = scale;
+    j.q = q; j.k = k; j.v = v; j.beta = beta; j.alpha = alpha; j.S0 = S0; j.o = o; j.ST = ST;
+    j.E = E;
+    return run_slabs(&j, nthreads, forward_slab);
+}
+
 /* ------------------------------------------------------------------------- */
 /* backward: adjoint of the token loop                                        */
 /* ------------------------------------------------------------------------- */
@@ -193,6 +211,7 @@ int oracle_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int 
  *   dq_t   = scale S_t do_t
  *   dk_t   = dS u,  du = dS^T k_t       (S_t = S' + k u^T)
  *   dbeta  = e . du, de = beta du       (u = beta e)
+ *            (+ dE_t when the write error e_t itself is consumed downstream)
  *   dv_t   = de                         (e = v - S'^T k)
  *   dS'    = dS - k de^T,  dk_t -= S' de
  *   da_i   = sum_j dS'_ij S_{t-1,ij}    (S' = Diag(a) S_{t-1})
@@ -288,7 +307,7 @@ static void backward_slab(job_t* j, int64_t slab) {
                 for (int64_t i = 0; i < dk; ++i) acc += dS[i * dv + jj] * kt[i];
                 du[jj] = acc;
                 dbt += e[jj] * acc; /* u = beta e */
-                de[jj] = bt * acc;
+                de[jj] = bt * acc + (j->dE ? j->dE[tok * dv + jj] : 0.0);
                 dvt[jj] = de[jj]; /* e = v - S'^T k */
             }
             j->dbeta[tok] = dbt;
@@ -349,6 +368,25 @@ int oracle_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int
     j.q = q; j.k = k; j.v = v; j.beta = beta; j.alpha = alpha; j.S0 = S0;
     j.dO = dO; j.dST = dST; j.dq = dq; j.dk_out = dk_out; j.dv_out = dv_out;
     j.dbeta = dbeta; j.dalpha = dalpha; j.dS0 = dS0;
+    return run_slabs(&j, nthreads, backward_slab);
+}
+
+int oracle_backward_errors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate,
+                           double scale, const double* q, const double* k, const double* v,
+                           const double* beta, const double* alpha, const double* S0,
+                           const double* dO, const double* dST, const double* dE, double* dq,
+                           double* dk_out, double* dv_out, double* dbeta, double* dalpha,
+                           double* dS0, int nthreads) {
+    if (check_common(B, T, H, dk, dv, gate)) return -1;
+    if (T > 0 && (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta))
+        return -1;
+    if (gate != ORACLE_GATE_NONE && T > 0 && !alpha) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.B = B; j.T = T; j.H = H; j.dk = dk; j.dv = dv; j.gate = gate; j.scale = scale;
+    j.q = q; j.k = k; j.v = v; j.beta = beta; j.alpha = alpha; j.S0 = S0;
+    j.dO = dO; j.dST = dST; j.dq = dq; j.dk_out = dk_out; j.dv_out = dv_out;
+    j.dbeta = dbeta; j.dalpha = dalpha; j.dS0 = dS0; j.dE = dE;
     return run_slabs(&j, nthreads, backward_slab);
 }
 

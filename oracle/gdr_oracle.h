@@ -56,6 +56,25 @@ int oracle_backward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int
                     double* dq, double* dk_out, double* dv_out, double* dbeta,
                     double* dalpha, double* dS0, int nthreads);
 
+/* oracle_forward that also writes every token's write error
+ *     e_t = v_t - (Diag(alpha_t) S_{t-1})^T k_t        E [B, T, H, dv]
+ * the correction the delta rule writes (u_t = beta_t e_t), which the
+ * error-routing epilogue CLER-H sends into the hidden stream (popular article on
+ * the study, cross-layer section).  E must not be NULL. */
+int oracle_forward_errors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate,
+                          double scale, const double* q, const double* k, const double* v,
+                          const double* beta, const double* alpha, const double* S0, double* o,
+                          double* ST, double* E, int nthreads);
+
+/* oracle_backward with a gradient dE [B, T, H, dv] arriving at the write errors
+ * e_t as well (NULL means zero, which is oracle_backward). */
+int oracle_backward_errors(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate,
+                           double scale, const double* q, const double* k, const double* v,
+                           const double* beta, const double* alpha, const double* S0,
+                           const double* dO, const double* dST, const double* dE, double* dq,
+                           double* dk_out, double* dv_out, double* dbeta, double* dalpha,
+                           double* dS0, int nthreads);
+
 /* One recurrence step for N independent sequences (decode): S is [N,H,dk,dv]
  * and is updated in place; q,k [N,H,dk], v,o [N,H,dv], beta [N,H],
  * alpha [N,H] (SCALAR) or [N,H,dk] (CHANNEL). */

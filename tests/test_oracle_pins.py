@@ -443,3 +443,136 @@ def test_clvr_zero_init_is_a_no_op_and_unit_scale_adds_v():
     dv_acc, dlam = oracle.clvr_backward(dh, v, lam)
     assert np.abs(dv_acc.reshape(B, T, H * dv) - lam * dh).max() < 1e-15
     assert np.abs(dlam - (dh * v.reshape(B, T, H * dv)).sum((0, 1))).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# write errors (the quantity the CLER-H epilogue routes into the hidden stream)
+# --------------------------------------------------------------------------
+
+
+def _errors_from_states(case):
+    """Recovers every write error from consecutive states of the (pinned)
+    forward on prefixes: the update is S_t = D_t S_{t-1} + beta_t k_t e_t^T, so
+    k_t^T (S_t - D_t S_{t-1}) = beta_t |k_t|^2 e_t^T."""
+    q, k, v, beta, alpha, S0 = case
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    E = np.zeros((B, T, H, dv))
+    prev = np.zeros((B, H, dk, dv)) if S0 is None else S0
+    for t in range(T):
+        sl = lambda x: None if x is None else x[:, :t + 1]
+        _, St = oracle_fwd(sl(q), sl(k), sl(v), sl(beta), sl(alpha), S0)
+        for b in range(B):
+            for h in range(H):
+                D = np.diag(gate_vec(alpha, b, t, h, dk))
+                kk = k[b, t, h]
+                E[b, t, h] = kk @ (St[b, h] - D @ prev[b, h]) / (beta[b, t, h] * (kk @ kk))
+        prev = St
+    return E
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_write_errors_match_state_increments(gate):
+    case = rand_case(B=2, T=7, H=2, dk=5, dv=4, gate=gate, seed=40)
+    o, ST, E = oracle.forward(*case, want_errors=True, nthreads=2)
+    o2, ST2 = oracle_fwd(*case)
+    assert np.array_equal(o, o2) and np.array_equal(ST, ST2)
+    assert np.abs(E - _errors_from_states(case)).max() < 1e-12
+
+
+def test_write_error_pin_catches_undecayed_read():
+    """A mistake that reads the error against S_{t-1} instead of the decayed
+    D_t S_{t-1} fails the increment pin."""
+    case = rand_case(B=1, T=5, H=1, dk=4, dv=3, gate="channel", seed=41)
+    q, k, v, beta, alpha, S0 = case
+    E_ref = _errors_from_states(case)
+    S = S0[0, 0].copy()
+    bad = np.zeros_like(E_ref)
+    for t in range(5):
+        kk, a = k[0, t, 0], alpha[0, t, 0]
+        bad[0, t, 0] = v[0, t, 0] - S.T @ kk
+        Sd = np.diag(a) @ S
+        S = Sd + beta[0, t, 0] * np.outer(kk, v[0, t, 0] - Sd.T @ kk)
+    assert np.abs(bad - E_ref).max() > 1e-3
+
+
+def test_write_error_special_cases():
+    """From zero state the first error is the value itself; writing the same
+    unit-norm pair again with beta = 1 and no decay leaves no error; after a
+    write the residual at k_t shrinks to (1 - beta_t |k_t|^2) e_t."""
+    q, k, v, beta, alpha, S0 = rand_case(B=1, T=6, H=2, dk=5, dv=4, gate="scalar", s0=False, seed=42)
+    _, _, E = oracle.forward(q, k, v, beta, alpha, None, want_errors=True)
+    assert np.array_equal(E[:, 0], v[:, 0])
+    k2, v2, b2, a2 = k.copy(), v.copy(), beta.copy(), alpha.copy()
+    k2[:, 3], v2[:, 3] = k2[:, 2], v2[:, 2]
+    b2[:, 2:4], a2[:, 3] = 1.0, 1.0
+    _, _, E2 = oracle.forward(q, k2, v2, b2, a2, None, want_errors=True)
+    assert np.abs(E2[:, 3]).max() < 1e-14
+    case = rand_case(B=1, T=6, H=2, dk=5, dv=4, gate="channel", seed=43)
+    q, k, v, beta, alpha, S0 = case
+    _, _, E = oracle.forward(*case, want_errors=True)
+    for t in range(6):
+        sl = lambda x: x[:, :t + 1]
+        _, St = oracle_fwd(sl(q), sl(k), sl(v), sl(beta), sl(alpha), S0)
+        for h in range(2):
+            kk = k[0, t, h]
+            resid = v[0, t, h] - St[0, h].T @ kk
+            assert np.abs(resid - (1 - beta[0, t, h] * (kk @ kk)) * E[0, t, h]).max() < 1e-13
+
+
+def _loss_e(case, dO, dST, dE, scale):
+    o, ST, E = oracle.forward(*case, scale=scale, want_errors=True, nthreads=2)
+    return float((o * dO).sum() + (ST * dST).sum() + (E * dE).sum())
+
+
+@pytest.mark.parametrize("gate", ["none", "channel"])
+def test_backward_with_error_gradient_matches_central_differences(gate):
+    case = list(rand_case(B=1, T=5, H=2, dk=4, dv=3, gate=gate, seed=44))
+    r = np.random.default_rng(45)
+    dO = r.standard_normal((1, 5, 2, 3))
+    dST = r.standard_normal((1, 2, 4, 3))
+    dE = r.standard_normal((1, 5, 2, 3))
+    g = oracle.backward(*case, dO, dST, scale=0.6, dE=dE)
+    eps = 1e-6
+    for idx, name in enumerate(["dq", "dk", "dv", "dbeta", "dalpha", "dS0"]):
+        x = case[idx]
+        if x is None:
+            assert g[name] is None
+            continue
+        num = np.zeros_like(x)
+        for mi in np.ndindex(x.shape):
+            old = x[mi]
+            x[mi] = old + eps
+            lp = _loss_e(case, dO, dST, dE, 0.6)
+            x[mi] = old - eps
+            lm = _loss_e(case, dO, dST, dE, 0.6)
+            x[mi] = old
+            num[mi] = (lp - lm) / (2 * eps)
+        err = np.abs(num - g[name]).max() / max(1.0, np.abs(num).max())
+        assert err < 1e-7, (name, err)
+
+
+def test_zero_error_gradient_is_the_plain_backward():
+    case = rand_case(B=2, T=6, H=2, dk=4, dv=3, gate="channel", seed=46)
+    r = np.random.default_rng(47)
+    dO = r.standard_normal((2, 6, 2, 3))
+    a = oracle.backward(*case, dO)
+    b = oracle.backward(*case, dO, dE=np.zeros((2, 6, 2, 3)))
+    assert all(np.array_equal(a[n], b[n]) for n in a)
+
+
+def test_cler_routing_adds_scaled_errors():
+    """CLER-H adds lam * e_t to the hidden stream per channel h*dv + j; lam = 0
+    leaves it unchanged, and its adjoint sends lam * dh to the errors."""
+    case = rand_case(B=1, T=4, H=2, dk=4, dv=3, gate="channel", seed=48)
+    _, _, E = oracle.forward(*case, want_errors=True)
+    r = np.random.default_rng(49)
+    hid = r.standard_normal((1, 4, 6))
+    assert np.array_equal(oracle.cler_forward(hid, E, np.zeros(6)), hid)
+    lam = r.standard_normal(6)
+    out = oracle.cler_forward(hid, E, lam)
+    assert np.abs(out - hid - lam * E.reshape(1, 4, 6)).max() < 1e-15
+    dh = r.standard_normal(hid.shape)
+    dE, dlam = oracle.cler_backward(dh, E, lam)
+    assert np.abs(dE.reshape(1, 4, 6) - lam * dh).max() < 1e-15
+    assert np.abs(dlam - (dh * E.reshape(1, 4, 6)).sum((0, 1))).max() < 1e-13
