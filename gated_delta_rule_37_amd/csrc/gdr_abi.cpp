@@ -56,6 +56,8 @@ gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
         (d->out_dtype != GDR_BF16 && d->out_dtype != GDR_FP32))
         return fail(GDR_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", d->in_dtype, d->out_dtype);
     if (!std::isfinite(d->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is not finite");
+    if (d->route != GDR_ROUTE_VALUE && d->route != GDR_ROUTE_ERROR)
+        return fail(GDR_ERR_INVALID_ARG, "unknown epilogue route %d", d->route);
     if (d->dk != d->dv || (d->dk != 64 && d->dk != 128))
         return fail(GDR_ERR_UNSUPPORTED, "only dk == dv in {64, 128} is supported (got %lld, %lld)",
                     (long long)d->dk, (long long)d->dv);
@@ -76,12 +78,17 @@ gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
     return GDR_OK;
 }
 
-// CLVR scale gradient: token segments reduced in two passes
+// Epilogue scale gradient, reduced in two passes: CLVR sums token segments;
+// the error-routing epilogue leaves one partial row per chunk.
 int64_t dlam_segments(const gdr_desc* d) {
     const int64_t bt = d->B * d->T;
     return bt < 1 ? 1 : (bt < 256 ? bt : 256);
 }
 size_t dlam_partial_bytes(const gdr_desc* d) {
+    if (d->route == GDR_ROUTE_ERROR) {
+        const int64_t nc = (d->T + kChunk - 1) / kChunk;
+        return size_t(d->B) * size_t(nc) * size_t(d->H) * size_t(d->dv) * 4;
+    }
     return size_t(dlam_segments(d)) * size_t(d->H) * size_t(d->dv) * 4;
 }
 
@@ -91,7 +98,7 @@ namespace gdr {
 
 // Carves the chunk workspace; returns the bytes needed.  `base` may be NULL
 // (sizing only).
-size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* out, void* base) {
+size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, ChunkWs* out, void* base) {
     ChunkWs w;
     std::memset(&w, 0, sizeof w);
     size_t off = 0;
@@ -132,6 +139,7 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* 
         w.gA = static_cast<float*>(take(sq32));
         w.gP = static_cast<float*>(take(sq32));
         w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
+        if (cler) w.Mt = take(mat);
     }
     if (out) *out = w;
     return off;
@@ -154,7 +162,7 @@ const char* gdr_status_string(gdr_status s) {
 
 const char* gdr_last_error(void) { return g_err; }
 
-int32_t gdr_version(void) { return 100; }
+int32_t gdr_version(void) { return 200; }
 
 size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     int64_t NC = 0;
@@ -165,7 +173,8 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     }
     const int64_t nch = desc->B * desc->H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
-    size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, nullptr, nullptr);
+    size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, desc->route == GDR_ROUTE_ERROR, nullptr,
+                                   nullptr);
     if (op == 1) n += align_up(dlam_partial_bytes(desc));
     return n;
 }
@@ -220,7 +229,7 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     const int64_t nch = B * H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
     gdr::ChunkWs w;
-    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, train, &w, ws);
+    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, train, desc->route == GDR_ROUTE_ERROR, &w, ws);
     const size_t need = train ? chunk_bytes + align_up(dlam_partial_bytes(desc)) : chunk_bytes;
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
@@ -235,24 +244,34 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
+    // the value-routing epilogue runs in the intra-chunk kernel (it needs only
+    // v); the error-routing one needs U, so it follows the state pass
+    const bool cler = h_clvr && desc->route == GDR_ROUTE_ERROR;
     hipError_t e = hipSuccess;
     if (NC > 0) {
         gdr::prof_before(s);
         e = gdr::launch_intra(int(D), desc->gate, in_f32, train ? 2 : 0, B, T, int(H), NC, q, k, v, beta,
-                              alpha, h_clvr, clvr_scale, w, s);
+                              alpha, cler ? nullptr : h_clvr, cler ? nullptr : clvr_scale, w, s);
         gdr::prof_after(train ? "intra_train" : "intra_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
     }
     gdr::prof_before(s);
     e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o,
-                              train, s);
+                              train || cler, s);
     gdr::prof_after(train ? "state_train" : "state_fwd", s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     if (!in_f32 && NC > 0) {
         gdr::prof_before(s);
-        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, s);
-        gdr::prof_after("output", s);
+        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta, clvr_scale,
+                               cler ? h_clvr : nullptr, s);
+        gdr::prof_after(cler ? "output_cler" : "output", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
+    }
+    if (in_f32 && cler && NC > 0) {
+        gdr::prof_before(s);
+        e = gdr::launch_cler_fwd(int(D), in_f32, B, T, int(H), NC, w, beta, clvr_scale, h_clvr, s);
+        gdr::prof_after("cler_fwd", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "error-routing launch: %s", hipGetErrorString(e));
     }
     return GDR_OK;
 }
@@ -307,7 +326,7 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const int64_t nch = B * H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
     gdr::ChunkWs w;
-    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, true, &w, ws);
+    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, true, desc->route == GDR_ROUTE_ERROR, &w, ws);
     const size_t need = chunk_bytes + align_up(dlam_partial_bytes(desc));
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
@@ -334,16 +353,29 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
         GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
                                                          desc->scale, w, S0, nullptr, nullptr, true, s));
     }
+    // error routing: dh reaches U inside the reverse state pass and beta and the
+    // scale afterwards; value routing: dh reaches v in the gradient kernel
+    const bool cler = dh_clvr && desc->route == GDR_ROUTE_ERROR;
+    if (cler && NC > 0)
+        GDR_STEP("cler_mt", gdr::launch_cler_mt(int(D), in_f32, B, T, int(H), NC, w, clvr_scale, dh_clvr, s));
     GDR_STEP("state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
-                                                 dS0, s));
+                                                 dS0, cler ? dh_clvr : nullptr, clvr_scale, beta, s));
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
     if (NC > 0) {
+        // both routes add lam * dh to dv: the value route through v itself,
+        // the error route through e = v - ...
         GDR_STEP("grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
                                                   q, k, v, beta, alpha, dO, dh_clvr, clvr_scale, dv, dbeta, w, s));
+        if (cler)
+            GDR_STEP("cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta, clvr_scale,
+                                                        dh_clvr, dclvr_scale, partial, s));
         GDR_STEP("grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
                                                     alpha, dq, dk, dalpha, w, s));
     }
-    if (dclvr_scale) {
-        float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
+    if (cler) {
+        if (dclvr_scale && NC == 0)
+            GDR_STEP("cler_dlam", gdr::launch_dlam_final(int(H * D), 0, partial, dclvr_scale, s));
+    } else if (dclvr_scale) {
         GDR_STEP("clvr_dlam", gdr::launch_clvr_dlam(in_f32, B * T, int(H), int(D), dh_clvr, v, dclvr_scale,
                                                     partial, dlam_segments(desc), s));
     }

@@ -1033,6 +1033,10 @@ hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* d
         hipLaunchKernelGGL((clvr_dlam_partial<false>), g1, dim3(256), 0, stream, BT, HD, nseg, dh, v, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_dlam_final(HD, nseg, partial, dlam, stream);
+}
+
+hipError_t launch_dlam_final(int HD, int64_t nseg, const float* partial, float* dlam, hipStream_t stream) {
     hipLaunchKernelGGL(clvr_dlam_final, dim3((HD + 63) / 64), dim3(256), 0, stream, HD, nseg, partial, dlam);
     return hipGetLastError();
 }

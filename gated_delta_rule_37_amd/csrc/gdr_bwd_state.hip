@@ -9,6 +9,14 @@
 // slices of 16 columns exactly like the forward pass.  Per chunk it saves the
 // chunk-end gradient dS' and dU (fragment order, for the gradient kernels); the
 // gradient that reaches the initial state is dS0.
+//
+// With the error-routing epilogue (CLER-H) the write errors
+// E = (V - Kt S) - M U (M = strict_tril(P)) feed the hidden stream, and their
+// gradient dE = lam * dh adds dU -= M^T dE and dS -= Kt^T dE.  The saved dU
+// (read by the gradient kernels) is dU - M^T dE, with M^T dE formed before this
+// pass.  The state update uses the equivalent
+//   dS -= W^T (dU + dE / beta)    [W^T (dE / beta + M^T dE) = Kt^T dE]
+// which needs no Kt: only dh and beta are staged besides M^T dE.
 #include "gdr_common.hpp"
 #include "gdr_launch.hpp"
 
@@ -28,6 +36,14 @@ struct BwdCfg {
     static constexpr int SRT = D / 64;
 };
 
+// Gradient arriving at the hidden stream of the error-routing epilogue (dh NULL:
+// no epilogue) with its scale (NULL: ones) and the betas.
+struct ClerBwd {
+    const void* dh;
+    const float* lam;
+    const float* beta;
+};
+
 template <int D, bool IN_F32>
 struct BwdFrags {
     using OpT = typename BwdCfg<D, IN_F32>::OpT;
@@ -36,14 +52,17 @@ struct BwdFrags {
     Frag<OpT> at[2], kb[D / 32], qtt[SRT][2], wt[SRT][2];
     float gam[SRT][4];
     InT dO[4];
+    InT dh[4];    // error-routing epilogue only
+    float bt[4];
+    OpT mt[4];
 };
 
 // Loads the operands of chunk c (fragment order, contiguous per fragment) and
 // this lane's four dO values (rows 16*wid + 4*g4 + e, column j0 + l16).
-template <int D, bool IN_F32>
+template <int D, bool IN_F32, bool CLER>
 __device__ __forceinline__ void load_bwd(BwdFrags<D, IN_F32>& f, const ChunkWs& ws, int64_t ch, int64_t c,
                                          int64_t b, int64_t T, int H, int h, const void* dO_, int j0, int wid,
-                                         int lane) {
+                                         int lane, const ClerBwd& cl) {
     using Cfg = BwdCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
     using InT = typename Cfg::InT;
@@ -72,6 +91,12 @@ __device__ __forceinline__ void load_bwd(BwdFrags<D, IN_F32>& f, const ChunkWs& 
     for (int e = 0; e < 4; ++e) {
         const int64_t t = (tb + e < T) ? tb + e : T - 1;  // clamped; zeroed at use
         f.dO[e] = dO[((b * T + t) * H + h) * D + j0 + (lane & 15)];
+        if constexpr (CLER) {
+            f.dh[e] = reinterpret_cast<const InT*>(cl.dh)[((b * T + t) * H + h) * D + j0 + (lane & 15)];
+            f.bt[e] = cl.beta[(b * T + t) * H + h];
+            f.mt[e] = reinterpret_cast<const OpT*>(ws.Mt)[(ch * CHUNK + 16 * wid + 4 * (lane >> 4) + e) * D + j0 +
+                                                          (lane & 15)];
+        }
     }
 }
 
@@ -106,13 +131,15 @@ __device__ __forceinline__ void st8(OpT* dst, const OpT (&v)[8]) {
     }
 }
 
-template <int D, bool IN_F32>
+template <int D, bool IN_F32, bool CLER>
 __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t c, int64_t T, int64_t bh,
-                                         int64_t NC, int j0, int wid, int lane, float scale, const ChunkWs& ws,
+                                         int64_t NC, int j0, int wid, int lane, float scale, float lamj,
+                                         const ChunkWs& ws,
                                          float4v (&dS)[BwdCfg<D, IN_F32>::SRT],
                                          typename BwdCfg<D, IN_F32>::OpT* s_dS,
                                          typename BwdCfg<D, IN_F32>::OpT* s_dO,
-                                         typename BwdCfg<D, IN_F32>::OpT* s_dU) {
+                                         typename BwdCfg<D, IN_F32>::OpT* s_dU,
+                                         typename BwdCfg<D, IN_F32>::OpT* s_dUE) {
     using Cfg = BwdCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
     constexpr int SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
@@ -154,21 +181,33 @@ __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t
             mma(cur.kb[kq], fs, du);
         }
     }
+    if constexpr (CLER) {
+        // saved: dU - M^T dE; state update: dU + dE / beta
+        const int64_t tb = c * CHUNK + 16 * wid + 4 * g4;
+        float4v due;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            due[e] = du[e] - to_f32(cur.mt[e]);
+            if (tb + e < T) du[e] += lamj * to_f32(cur.dh[e]) / cur.bt[e];
+        }
+        st4b<OpT>(s_dUE + l16 * LDS_U + 16 * wid + 4 * g4, due);
+    }
     st4b<OpT>(s_dU + l16 * LDS_U + 16 * wid + 4 * g4, du);
     __syncthreads();
 
     // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
+    const OpT* s_sv = CLER ? s_dUE : s_dU;
     if (tid < 2 * CHUNK) {
         const int pos = tid >> 1, hf = tid & 1;
         OpT vals[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = s_dU[(8 * hf + e) * LDS_U + pos];
+        for (int e = 0; e < 8; ++e) vals[e] = s_sv[(8 * hf + e) * LDS_U + pos];
         st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
     } else if (tid < 2 * CHUNK + 128) {
         const int t2 = tid - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;  // column j, positions 8pg..8pg+7
         OpT vals[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = s_dU[j * LDS_U + 8 * pg + e];
+        for (int e = 0; e < 8; ++e) vals[e] = s_sv[j * LDS_U + 8 * pg + e];
         st8(reinterpret_cast<OpT*>(ws.dUsaveT) + ch * D * CHUNK + frag_off<CHUNK>(j0 + j, 8 * pg), vals);
     }
 
@@ -194,10 +233,10 @@ __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t
     __syncthreads();
 }
 
-template <int D, bool IN_F32>
+template <int D, bool IN_F32, bool CLER>
 __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                         const void* __restrict__ dO, const float* __restrict__ dST,
-                                                        float* __restrict__ dS0) {
+                                                        float* __restrict__ dS0, ClerBwd cl) {
     using Cfg = BwdCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
     constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
@@ -205,6 +244,7 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
     __shared__ __attribute__((aligned(16))) OpT s_dS[Cfg::NS * LDS_S];
     __shared__ __attribute__((aligned(16))) OpT s_dO[Cfg::NS * LDS_U];
     __shared__ __attribute__((aligned(16))) OpT s_dU[Cfg::NS * LDS_U];
+    __shared__ __attribute__((aligned(16))) OpT s_dUE[CLER ? Cfg::NS * LDS_U : 8];
 
     const int64_t nblk = gridDim.x;
     int64_t lid = blockIdx.x;
@@ -215,6 +255,7 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
     const int h = static_cast<int>(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const float lamj = (CLER && cl.lam) ? cl.lam[static_cast<int64_t>(h) * D + j0 + l16] : 1.f;
 
     float4v dS[SRT];
 #pragma unroll
@@ -227,16 +268,17 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
     __syncthreads();
 
     BwdFrags<D, IN_F32> fa, fb;
-    if (NC > 0) load_bwd<D, IN_F32>(fa, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, wid, lane);
+    if (NC > 0) load_bwd<D, IN_F32, CLER>(fa, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, wid, lane, cl);
 #pragma unroll 1
     for (int64_t c = NC - 1; c >= 0; c -= 2) {
         const int64_t n1 = c - 1 >= 0 ? c - 1 : 0;
-        load_bwd<D, IN_F32>(fb, ws, bh * NC + n1, n1, b, T, H, h, dO, j0, wid, lane);
-        bwd_step<D, IN_F32>(fa, c, T, bh, NC, j0, wid, lane, scale, ws, dS, s_dS, s_dO, s_dU);
+        load_bwd<D, IN_F32, CLER>(fb, ws, bh * NC + n1, n1, b, T, H, h, dO, j0, wid, lane, cl);
+        bwd_step<D, IN_F32, CLER>(fa, c, T, bh, NC, j0, wid, lane, scale, lamj, ws, dS, s_dS, s_dO, s_dU, s_dUE);
         if (c - 1 < 0) break;
         const int64_t n2 = c - 2 >= 0 ? c - 2 : 0;
-        load_bwd<D, IN_F32>(fa, ws, bh * NC + n2, n2, b, T, H, h, dO, j0, wid, lane);
-        bwd_step<D, IN_F32>(fb, c - 1, T, bh, NC, j0, wid, lane, scale, ws, dS, s_dS, s_dO, s_dU);
+        load_bwd<D, IN_F32, CLER>(fa, ws, bh * NC + n2, n2, b, T, H, h, dO, j0, wid, lane, cl);
+        bwd_step<D, IN_F32, CLER>(fb, c - 1, T, bh, NC, j0, wid, lane, scale, lamj, ws, dS, s_dS, s_dO, s_dU,
+                                  s_dUE);
     }
 
     if (dS0) {
@@ -258,7 +300,7 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
 // barriers (after dU, after dS).
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool CLER>
 struct BwdStage {
     static constexpr int MAT = CHUNK * D * 2;   // [64][D] or [D][64] fp16
     static constexpr int AT = 0;                // [64][64]
@@ -267,17 +309,22 @@ struct BwdStage {
     static constexpr int WT = QTT + MAT;
     static constexpr int DO = WT + MAT;         // dO rows of this slice: [64][16] in the input dtype (bf16)
     static constexpr int GAM = DO + 2048;       // D fp32 in a 1 KiB slot
-    static constexpr int BYTES = GAM + 1024;
+    static constexpr int DH = GAM + 1024;       // error routing: dh rows of this slice, like dO
+    static constexpr int BT = DH + 2048;        // error routing: the chunk's 64 betas (1 KiB slot)
+    static constexpr int MT = BT + 1024;        // error routing: M^T dE rows of this slice (fp16)
+    static constexpr int BYTES = CLER ? MT + 2048 : GAM + 1024;
     static constexpr int NSL = D / 16;
     static constexpr int NL = (CHUNK * CHUNK * 2 + 3 * MAT) / NSL / 128 + 1;  // lines touched per chunk
     static constexpr int NT = (NL + 63) / 64;
 };
 
-// PART 0: A^T, dO rows, gamma; PART 1: Kb; PART 2: Qt^T; PART 3: W^T.
-template <int D, int PART>
+// PART 0: A^T, dO rows, gamma (and the epilogue's dh rows and betas); PART 1:
+// Kb; PART 2: Qt^T; PART 3: W^T.
+template <int D, bool CLER, int PART>
 __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c, int64_t b,
-                                          int64_t T, int H, int h, const void* dO, int j0, int lane) {
-    using L = BwdStage<D>;
+                                          int64_t T, int H, int h, const void* dO, int j0, int lane,
+                                          const ClerBwd& cl) {
+    using L = BwdStage<D, CLER>;
     if constexpr (PART == 1) {
         copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
     } else if constexpr (PART == 2) {
@@ -298,22 +345,42 @@ __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int6
         }
         const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
         copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+        if constexpr (CLER) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
+                const int64_t t = t0 < T ? t0 : T - 1;
+                const char* src =
+                    static_cast<const char*>(cl.dh) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
+                copy16_to_lds(src, dst + L::DH + i * 1024);
+            }
+            const int64_t t0 = c * CHUNK + lane;
+            const int64_t t = t0 < T ? t0 : T - 1;
+            copy4_to_lds(cl.beta + (b * T + t) * H + h, dst + L::BT);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int pos = 32 * i + (lane >> 1);
+                const char* src = static_cast<const char*>(ws.Mt) + ((ch * CHUNK + pos) * D + j0 + 8 * (lane & 1)) * 2;
+                copy16_to_lds(src, dst + L::MT + i * 1024);
+            }
+        }
     }
 }
 
 // Loader wave `part` (0..3) copies its share of chunk ch.
-template <int D>
+template <int D, bool CLER>
 __device__ __forceinline__ void stage_bwd_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c,
-                                               int64_t b, int64_t T, int H, int h, const void* dO, int j0, int lane) {
-    if (part == 0) stage_bwd<D, 0>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
-    else if (part == 1) stage_bwd<D, 1>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
-    else if (part == 2) stage_bwd<D, 2>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
-    else stage_bwd<D, 3>(dst, ws, ch, c, b, T, H, h, dO, j0, lane);
+                                               int64_t b, int64_t T, int H, int h, const void* dO, int j0, int lane,
+                                               const ClerBwd& cl) {
+    if (part == 0) stage_bwd<D, CLER, 0>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else if (part == 1) stage_bwd<D, CLER, 1>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else if (part == 2) stage_bwd<D, CLER, 2>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else stage_bwd<D, CLER, 3>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
 }
 
 template <int D>
 __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
-    using L = BwdStage<D>;
+    using L = BwdStage<D, false>;
     constexpr int AL = CHUNK * CHUNK * 2 / L::NSL / 128, QL = L::MAT / L::NSL / 128;
 #pragma unroll
     for (int i = 0; i < L::NT; ++i) {
@@ -330,21 +397,23 @@ __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, in
     }
 }
 
-template <int D>
+template <int D, bool CLER>
 __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                             const void* __restrict__ dO,
                                                             const float* __restrict__ dST,
-                                                            float* __restrict__ dS0) {
+                                                            float* __restrict__ dS0, ClerBwd cl) {
     using Cfg = BwdCfg<D, false>;
     using OpT = _Float16;
-    using L = BwdStage<D>;
+    using L = BwdStage<D, CLER>;
+    using LT = BwdStage<D, false>;
     constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
     constexpr int PF = 8;
 
     __shared__ __attribute__((aligned(16))) OpT s_dS[Cfg::NS * LDS_S];
     __shared__ __attribute__((aligned(16))) OpT s_dU[Cfg::NS * LDS_U];
+    __shared__ __attribute__((aligned(16))) OpT s_dUE[CLER ? Cfg::NS * LDS_U : 8];
     __shared__ __attribute__((aligned(1024))) char stage[2][L::BYTES];
-    __shared__ __attribute__((aligned(16))) char dummy[L::NT * 256];
+    __shared__ __attribute__((aligned(16))) char dummy[LT::NT * 256];
 
     const int64_t nblk = gridDim.x;
     int64_t lid = blockIdx.x;
@@ -366,7 +435,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         // one; wave 4 also warms the L2.
         const int part = wid - 4;
         const bool w4 = part == 0;
-        if (NC > 0) stage_bwd_part<D>(part, sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane);
+        if (NC > 0) stage_bwd_part<D, CLER>(part, sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane, cl);
         if (w4) {
 #pragma unroll 1
             for (int64_t c = NC - 2; c >= 0 && c > NC - 1 - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
@@ -377,11 +446,13 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
 #pragma unroll 1
         for (int64_t c = NC - 1; c >= 0; --c) {
             const bool st = c >= 1, tpf = w4 && c - PF >= 0;
-            if (st) stage_bwd_part<D>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0, lane);
+            if (st)
+                stage_bwd_part<D, CLER>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0,
+                                        lane, cl);
             if (tpf) touch_bwd<D>(sdummy, ws, bh * NC + c - PF, slice, lane);
             __builtin_amdgcn_s_barrier();
             // chunk c-1 must have landed; only this step's touches may stay in flight
-            if (tpf) wait_vmcnt<L::NT>();
+            if (tpf) wait_vmcnt<LT::NT>();
             else wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             nb ^= 1;
@@ -389,6 +460,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         return;
     }
 
+    const float lamj = (CLER && cl.lam) ? cl.lam[static_cast<int64_t>(h) * D + j0 + l16] : 1.f;
     float4v dS[SRT];
 #pragma unroll
     for (int m = 0; m < SRT; ++m) {
@@ -451,23 +523,41 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
             fs.load(s_dS + l16 * LDS_S + 32 * kq + 8 * g4);
             mma(kb[kq], fs, du);
         }
+        if constexpr (CLER) {
+            // saved: dU - M^T dE; state update: dU + lam dh / beta (rows 16 wid + 4 g4 + e)
+            const __attribute__((address_space(3))) bf16_t* dhs =
+                reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DH);
+            const __attribute__((address_space(3))) _Float16* mts =
+                reinterpret_cast<const __attribute__((address_space(3))) _Float16*>(src + L::MT);
+            const float4v bt =
+                *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::BT + (16 * wid + 4 * g4) * 4);
+            float4v due;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = 16 * wid + 4 * g4 + e;
+                due[e] = du[e] - static_cast<float>(mts[pos * 16 + l16]);
+                if (c * CHUNK + pos < T) du[e] += lamj * bf16_to_f32(dhs[pos * 16 + l16]) / bt[e];
+            }
+            st4b<OpT>(s_dUE + l16 * LDS_U + 16 * wid + 4 * g4, due);
+        }
         st4b<OpT>(s_dU + l16 * LDS_U + 16 * wid + 4 * g4, du);
         __syncthreads();
 
         // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
         {
+            const OpT* s_sv = CLER ? s_dUE : s_dU;
             const int t = tid;
             if (t < 2 * CHUNK) {
                 const int pos = t >> 1, hf = t & 1;
                 OpT vals[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = s_dU[(8 * hf + e) * LDS_U + pos];
+                for (int e = 0; e < 8; ++e) vals[e] = s_sv[(8 * hf + e) * LDS_U + pos];
                 st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
             } else if (t < 2 * CHUNK + 128) {
                 const int t2 = t - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;
                 OpT vals[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = s_dU[j * LDS_U + 8 * pg + e];
+                for (int e = 0; e < 8; ++e) vals[e] = s_sv[j * LDS_U + 8 * pg + e];
                 st8(reinterpret_cast<OpT*>(ws.dUsaveT) + ch * D * CHUNK + frag_off<CHUNK>(j0 + j, 8 * pg), vals);
             }
         }
@@ -513,29 +603,38 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
     }
 }
 
+template <int D, bool IN_F32, bool CLER>
+static void launch_state_bwd_c(int64_t nblk, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
+                               const void* dO, const float* dST, float* dS0, const ClerBwd& cl, hipStream_t stream) {
+    if constexpr (!IN_F32)
+        hipLaunchKernelGGL((state_bwd_lds_kernel<D, CLER>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC,
+                           scale, ws, dO, dST, dS0, cl);
+    else
+        hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32, CLER>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H,
+                           NC, scale, ws, dO, dST, dS0, cl);
+}
+
 template <int D, bool IN_F32>
 static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
-                                     const void* dO, const float* dST, float* dS0, hipStream_t stream) {
+                                     const void* dO, const float* dST, float* dS0, const ClerBwd& cl,
+                                     hipStream_t stream) {
     const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    if constexpr (!IN_F32)
-        hipLaunchKernelGGL((state_bwd_lds_kernel<D>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC, scale,
-                           ws, dO, dST, dS0);
-    else
-        hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
-                           scale, ws, dO, dST, dS0);
+    if (cl.dh) launch_state_bwd_c<D, IN_F32, true>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+    else launch_state_bwd_c<D, IN_F32, false>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            hipStream_t stream) {
+                            const void* dh_cler, const float* lam, const float* beta, hipStream_t stream) {
+    const ClerBwd cl{dh_cler, lam, beta};
     if (D == 64) {
-        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
-        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
     }
-    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
-    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, stream);
+    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
 }
 
 }  // namespace gdr

@@ -29,13 +29,14 @@ struct ChunkWs {
     float *Nw, *Pw;
     void *Ssnap, *Usave, *dSsnap, *dUsave, *dUsaveT;
     float *gQt, *gKt, *gKb, *gA, *gP, *gGam;
+    void* Mt;  // error-routing backward: M^T dE [64][D] per chunk-head
 };
 
 // Per-launch event timing (gdr_profile_begin/end); no-ops unless enabled.
 void prof_before(hipStream_t stream);
 void prof_after(const char* name, hipStream_t stream);
 
-size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, ChunkWs* out, void* base);
+size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, ChunkWs* out, void* base);
 
 hipError_t launch_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, int H,
                          float scale, const void* q, const void* k, const void* v,
@@ -44,8 +45,11 @@ hipError_t launch_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nsl
 
 // O = scale (Qt S + A U) for every chunk from the saved chunk-start states and U
 // (fp16 operands only).
+// h_cler (bf16 hidden stream, NULL = none): the error-routing epilogue, applied
+// from the same read of U (fp16 operands only).
 hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
-                         const ChunkWs& ws, void* o, hipStream_t stream);
+                         const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
+                         hipStream_t stream);
 
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
@@ -56,9 +60,11 @@ hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
                             float* ST, void* o, bool save_for_backward, hipStream_t stream);
 
+// dh_cler (NULL = none): gradient at the hidden stream of the error-routing
+// epilogue, which adds lam * dh / beta to dU.
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            hipStream_t stream);
+                            const void* dh_cler, const float* lam, const float* beta, hipStream_t stream);
 
 hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                            int64_t NC, float scale, const void* q, const void* k, const void* v,
@@ -72,5 +78,20 @@ hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t 
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);
+// dlam[c] = sum over nseg rows of partial[seg][c], fixed order
+hipError_t launch_dlam_final(int HD, int64_t nseg, const float* partial, float* dlam, hipStream_t stream);
+
+// Error-routing epilogue (CLER-H).  Forward from the saved U: h += lam * U / beta.
+// Backward: launch_cler_mt forms M^T dE (dE = lam dh) before the reverse state
+// pass; launch_cler_post adds the write errors' Kt and P terms to the gradient
+// workspace before the gate kernel and, with dlam, reduces one partial row per
+// chunk ([B*NC][H*D] floats) into dlam.
+hipError_t launch_cler_fwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                           const float* beta, const float* lam, void* h, hipStream_t stream);
+hipError_t launch_cler_mt(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                          const float* lam, const void* dh, hipStream_t stream);
+hipError_t launch_cler_post(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                            const float* beta, const float* lam, const void* dh, float* dlam, float* partial,
+                            hipStream_t stream);
 
 }  // namespace gdr

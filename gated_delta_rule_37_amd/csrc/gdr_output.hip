@@ -13,6 +13,11 @@
 // as they are.  Wave w owns the value columns 32w..32w+31 of all 64 rows.  The
 // products accumulate in the same order as a fused state pass would (Qt S over
 // d, then A U), in fp32.
+//
+// With the error-routing epilogue (CLER), every thread also adds lam * u / beta
+// to the hidden-stream piece of the U piece it has just read (the write errors,
+// see gdr_cler.hpp), so U is read once for both.
+#include "gdr_cler.hpp"
 #include "gdr_common.hpp"
 #include "gdr_launch.hpp"
 
@@ -29,9 +34,10 @@ struct OutLayout {
     static constexpr int BYTES = A + CHUNK * CHUNK * 2;
 };
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool CLER>
 __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
-                                                     void* __restrict__ o_) {
+                                                     void* __restrict__ o_, const float* __restrict__ beta,
+                                                     const float* __restrict__ lam, bf16_t* __restrict__ hs) {
     using L = OutLayout<D>;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int LDT = L::LDT, LDU = L::LDU;
@@ -47,6 +53,8 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     const int h = static_cast<int>(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t nvalid64 = T - c * CHUNK;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
 
     // Qt and A: straight copies (fragment order), 1 KiB per copy
     {
@@ -80,13 +88,20 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
             const half8 v = *reinterpret_cast<const half8*>(Ug + p * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) uT[(j + e) * LDU + pos] = v[e];
+            if constexpr (CLER) {
+                if (pos < nvalid) {
+                    const int64_t t = c * CHUNK + pos;
+                    float u[8], lm[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) u[e] = static_cast<float>(v[e]);
+                    load_lam8(lam, static_cast<int64_t>(h) * D + j, lm);
+                    cler_add8(hs + ((b * T + t) * H + h) * D + j, u, lm, beta[(b * T + t) * H + h]);
+                }
+            }
         }
     }
     wait_vmcnt<0>();
     __syncthreads();
-
-    const int64_t nvalid64 = T - c * CHUNK;
-    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
     OutT* o = reinterpret_cast<OutT*>(o_);
     const int64_t tstride = static_cast<int64_t>(H) * D;
     const int64_t obase = ((b * T + c * CHUNK) * H + h) * D;
@@ -143,24 +158,29 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     }
 }
 
+template <int D, bool OUT_F32>
+static void launch_output_t(int64_t nch, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws, void* o,
+                            const float* beta, const float* lam, void* h, hipStream_t stream) {
+    bf16_t* hs = static_cast<bf16_t*>(h);
+    if (h)
+        hipLaunchKernelGGL((output_kernel<D, OUT_F32, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
+                           scale, ws, o, beta, lam, hs);
+    else
+        hipLaunchKernelGGL((output_kernel<D, OUT_F32, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
+                           scale, ws, o, beta, lam, hs);
+}
+
 hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
-                         const ChunkWs& ws, void* o, hipStream_t stream) {
+                         const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
+                         hipStream_t stream) {
     const int64_t nch = B * H * NC;
     if (nch == 0) return hipSuccess;
     if (D == 64) {
-        if (out_f32)
-            hipLaunchKernelGGL((output_kernel<64, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, scale,
-                               ws, o);
-        else
-            hipLaunchKernelGGL((output_kernel<64, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, scale,
-                               ws, o);
+        if (out_f32) launch_output_t<64, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
+        else launch_output_t<64, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
     } else {
-        if (out_f32)
-            hipLaunchKernelGGL((output_kernel<128, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                               scale, ws, o);
-        else
-            hipLaunchKernelGGL((output_kernel<128, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                               scale, ws, o);
+        if (out_f32) launch_output_t<128, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
+        else launch_output_t<128, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
     }
     return hipGetLastError();
 }

@@ -21,6 +21,15 @@
  * is added into the aligned hidden (residual) stream, with a per-channel scale
  * lam standing in for the paper's zero-initialised routing projection:
  *     h[b,t,h*dv+j] += lam[h*dv+j] * v[b,t,h,j]
+ * or, with desc->route == GDR_ROUTE_ERROR, the error-routing variant CLER-H
+ * (popular article on the study, cross-layer section), which adds the write
+ * error of the delta rule instead of the value:
+ *     h[b,t,h*dv+j] += lam[h*dv+j] * e[b,t,h,j],
+ *     e_t = v_t - (Diag(alpha_t) S_{t-1})^T k_t      (so that u_t = beta_t e_t
+ *                                                     is what the step writes)
+ * The chunked kernels obtain e_t as u_t / beta_t, so CLER-H requires every
+ * beta != 0 (beta in (0, 1], the sigmoid range the pages use); beta == 0 gives
+ * Inf/NaN in h and in the gradients, it is not checked.
  *
  * Conventions shared by every entry point
  *   - Every function is extern "C", never throws, never aborts, and never
@@ -70,6 +79,10 @@ typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gd
 
 typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
 
+/* What the hidden-stream epilogue (h_clvr) adds per token: the written value
+ * v_t (CLVR) or the write error e_t (CLER-H). */
+typedef enum { GDR_ROUTE_VALUE = 0, GDR_ROUTE_ERROR = 1 } gdr_route;
+
 typedef struct {
     int64_t B, T, H, dk, dv; /* batch, tokens, heads, key and value widths */
     int32_t gate;            /* gdr_gate */
@@ -77,6 +90,7 @@ typedef struct {
     int32_t out_dtype;       /* gdr_dtype of o, dq, dk, dv */
     float scale;             /* o = scale * S^T q ; 1.0 is the pages' equation */
     int32_t chunk;           /* 0 selects the default (64); only 64 is supported */
+    int32_t route;           /* gdr_route of the h_clvr epilogue; 0 (VALUE) when unused */
 } gdr_desc;
 
 /* Bytes of device workspace the chunked calls need for `desc`.
@@ -96,7 +110,8 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op);
  *   S0        initial state, NULL = zeros.  ST final state, NULL = not written;
  *             ST may alias S0.
  *   o         [B,T,H,dv] in out_dtype; must not alias an input.
- *   h_clvr    NULL = no CLVR; else updated in place (in_dtype).
+ *   h_clvr    NULL = no epilogue; else updated in place (in_dtype) with
+ *             lam * v (route VALUE) or lam * e (route ERROR).
  *   clvr_scale NULL = lam == 1.
  *   ws        device workspace of at least gdr_workspace_size(desc, 0) bytes;
  *             its contents on entry do not matter.
@@ -111,8 +126,9 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
  * forward's intermediates):
  *   dO        [B,T,H,dv] in_dtype, upstream gradient of o.
  *   dST       NULL = zero gradient on the final state.
- *   dh_clvr   NULL = no CLVR term; else [B,T,H*dv] in_dtype, the gradient
- *             arriving at the hidden stream after the CLVR add.
+ *   dh_clvr   NULL = no epilogue term; else [B,T,H*dv] in_dtype, the gradient
+ *             arriving at the hidden stream after the epilogue's add (for
+ *             route ERROR it reaches every input through e_t).
  *   dq, dk    [B,T,H,dk], dv [B,T,H,dv] in out_dtype.
  *   dbeta     [B,T,H] fp32.
  *   dalpha    alpha's shape, fp32, derivative w.r.t. alpha itself; must be NULL

@@ -51,9 +51,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_desc_layout_matches_header():
-    # int64 x5, int32 x3, float, int32 -> 60 bytes, padded to 64
+    # int64 x5, int32 x3, float, int32 x2 -> 64 bytes
     assert ctypes.sizeof(_lib.Desc) == 64
-    assert _lib.Desc.scale.offset == 52 and _lib.Desc.chunk.offset == 56
+    assert _lib.Desc.scale.offset == 52 and _lib.Desc.chunk.offset == 56 and _lib.Desc.route.offset == 60
 
 
 def test_status_strings_and_version(lib):
@@ -62,8 +62,8 @@ def test_status_strings_and_version(lib):
     assert lib.gdr_version() >= 100
 
 
-def desc(B=2, T=100, H=3, d=128, gate=2, in_dt=0, out_dt=1, scale=1.0, chunk=0):
-    return _lib.Desc(B, T, H, d, d, gate, in_dt, out_dt, scale, chunk)
+def desc(B=2, T=100, H=3, d=128, gate=2, in_dt=0, out_dt=1, scale=1.0, chunk=0, route=0):
+    return _lib.Desc(B, T, H, d, d, gate, in_dt, out_dt, scale, chunk, route)
 
 
 def test_workspace_size_formula(lib):
@@ -80,6 +80,15 @@ def test_workspace_size_formula(lib):
                   + al(nch * d * d * opb))
         assert lib.gdr_workspace_size(ctypes.byref(dd), 0) == expect
         assert lib.gdr_workspace_size(ctypes.byref(dd), 1) > expect
+        # the error-routing epilogue adds nothing to the forward; its backward
+        # keeps M^T dE ([64][d] per chunk-head, operand precision) and one fp32
+        # partial row of H*d scale gradients per chunk and batch
+        de = desc(B=2, T=130, H=3, d=d, in_dt=in_dt, route=1)
+        assert lib.gdr_workspace_size(ctypes.byref(de), 0) == expect
+        clvr_part = al(min(2 * 130, 256) * 3 * d * 4)
+        cler_part = al(2 * 3 * 3 * d * 4)
+        assert (lib.gdr_workspace_size(ctypes.byref(de), 1) - lib.gdr_workspace_size(ctypes.byref(dd), 1)
+                == al(nch * 64 * d * opb) + cler_part - clvr_part)
     assert lib.gdr_workspace_size(ctypes.byref(desc(T=0)), 0) == 0
 
 
@@ -101,6 +110,8 @@ def test_forward_rejects_invalid_arguments(lib):
     assert fwd(lib, desc(d=96)) == UNSUPPORTED
     assert fwd(lib, desc(chunk=32)) == UNSUPPORTED
     assert fwd(lib, desc(gate=3)) == INVALID
+    assert fwd(lib, desc(route=2)) == INVALID
+    assert fwd(lib, desc(route=-1)) == INVALID
     assert fwd(lib, desc(in_dt=5)) == INVALID
     assert fwd(lib, desc(B=-1)) == INVALID
     assert fwd(lib, desc(scale=float("nan"))) == INVALID
