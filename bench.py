@@ -87,6 +87,11 @@ PER_TH_BYTES = {
     "grad_lin": 256 + 4 + 512 + 256 + 256 + 256 + 256 + 4,  # k,beta,alpha,v,dO,dh read; dv,dbeta written
     "grad_gate": 2 * 256 + 512 + 2 * 256 + 512,        # q,k,alpha read; dq,dk,dalpha written
     "clvr_dlam": 2 * 256,                              # dh, v read
+    # error-routing epilogue (CLER-H) training step
+    "output_cler": 256 + 2 * 256 + 4,                  # o written; h read+write; beta read
+    "cler_mt": 256,                                    # dh read
+    "state_bwd_cler": 2 * 256 + 4,                     # dO, dh, beta read
+    "cler_post": 256 + 4,                              # dh, beta read
 }
 # Per (b,h) state tensors (fp32 d x d): S_T written by the forward state pass.
 PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
@@ -95,7 +100,9 @@ PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
 KERNEL_SOURCES = {
     "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"], "intra_train": ["gdr_intra.hip"],
     "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"], "state_train": ["gdr_state.hip"],
-    "output": ["gdr_output.hip"],
+    "output": ["gdr_output.hip"], "output_cler": ["gdr_output.hip", "gdr_cler.hpp"],
+    "cler_mt": ["gdr_cler.hip", "gdr_cler.hpp"], "cler_post": ["gdr_cler.hip", "gdr_cler.hpp"],
+    "state_bwd_cler": ["gdr_bwd_state.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
     "decode": ["gdr_decode.hip"],
@@ -252,6 +259,44 @@ def main():
                 "traffic": measured_traffic(dom), "alg_bytes_per_launch": kernels[dom]["alg_bytes"],
                 "avg_us": round(kernels[dom]["avg_us"], 2)}
 
+    # ---------------- the same training step with the error-routing epilogue ----------------
+    cler = None
+    if do_bwd:
+        nbc = gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf, backward=True, route="error")
+        del ws_b
+        ws_c = torch.empty(nbc, dtype=torch.uint8, device=dev)
+
+        def cler_step():
+            gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_c, output_final_state=True,
+                        save_for_backward=True, route="error")
+            gdr.backward(q, k, v, beta, alpha, None, dO, dh=h, clvr_scale=lam, want_dclvr_scale=True,
+                         saved_workspace=ws_c, route="error")
+
+        for _ in range(args.warmup):
+            cler_step()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            cler_step()
+        e1.record()
+        torch.cuda.synchronize()
+        cler_ms = e0.elapsed_time(e1) / args.steps
+        timer.begin()
+        for _ in range(args.steps):
+            cler_step()
+        torch.cuda.synchronize()
+        ck = {}
+        for n, (c, ms) in timer.end().items():
+            if n in ("output_cler", "cler_mt", "state_bwd_cler", "cler_post"):
+                us = 1e3 * ms / c
+                gbs = kbytes[n] / (us * 1e-6) / 1e9
+                ck[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        cler = {"workload": "the same step with route=error (CLER-H: h += lam * write error)",
+                "ms_per_step": round(cler_ms, 4), "tokens_per_s": round(tokens / (cler_ms * 1e-3), 1),
+                "kernels": ck}
+        log("cler step %.3f ms; kernels %s" % (cler_ms, json.dumps(ck)))
+        del ws_c
+
     # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
     dc = gdr_inputs.DECODE_CONFIG
     nsets = 3
@@ -328,6 +373,7 @@ def main():
         "kernels": {n: {"avg_us": round(kr["avg_us"], 2), "alg_GBs": kr["alg_GBs"], "hbm_frac": kr["hbm_frac"]}
                     for n, kr in kernels.items()},
         "decode": decode,
+        "cler": cler,
     }
     print(json.dumps(out), flush=True)
 

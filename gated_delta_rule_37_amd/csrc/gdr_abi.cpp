@@ -358,7 +358,7 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const bool cler = dh_clvr && desc->route == GDR_ROUTE_ERROR;
     if (cler && NC > 0)
         GDR_STEP("cler_mt", gdr::launch_cler_mt(int(D), in_f32, B, T, int(H), NC, w, clvr_scale, dh_clvr, s));
-    GDR_STEP("state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
+    GDR_STEP(cler ? "state_bwd_cler" : "state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
                                                  dS0, cler ? dh_clvr : nullptr, clvr_scale, beta, s));
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
     if (NC > 0) {
