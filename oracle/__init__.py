@@ -200,3 +200,72 @@ def cler_backward(dh, E, lam=None):
     """Returns ``(dE [B,T,H,dv], dlam [H*dv])`` for :func:`cler_forward`; dE is
     then passed to :func:`backward`."""
     return clvr_backward(dh, E, lam)
+
+
+# --------------------------------------------------------------------------
+# Prologue: L2-normalised q and k, activated gates
+# --------------------------------------------------------------------------
+# The KDA blog applies an L2 norm to q and k after their projections (section
+# 7.1, also section 2.1's remark on numerical stability) and drives the gates
+# through a sigmoid; its section 7.1 sets the forget-gate bias to -3, which
+# makes the forgotten fraction sigmoid(-3) ~ 0.05 at initialisation.  Two gate
+# readings are offered:
+#   PRO_ALPHA_SIGMOID : alpha = sigmoid(a)
+#   PRO_ALPHA_FORGET  : alpha = exp(-softplus(a)) = 1 - sigmoid(a)  (a is the
+#                       forget-gate logit; bias -3 keeps ~95 % per token)
+# and beta = sigmoid(b) in both.  The norm is x / max(|x|_2, NORM_EPS).
+PRO_NONE, PRO_ALPHA_SIGMOID, PRO_ALPHA_FORGET = 0, 1, 2
+NORM_EPS = 1e-6
+
+
+def _sigmoid(x):
+    x = np.asarray(x, np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def l2_normalise(x):
+    """Rows of the last axis divided by max(|row|, NORM_EPS)."""
+    x = np.asarray(x, np.float64)
+    n = np.sqrt((x * x).sum(-1, keepdims=True))
+    return x / np.maximum(n, NORM_EPS)
+
+
+def prologue_forward(q, k, beta_logit, alpha_logit, mode):
+    """Raw inputs -> (q_hat, k_hat, beta, alpha) as the operator consumes them."""
+    if mode not in (PRO_ALPHA_SIGMOID, PRO_ALPHA_FORGET):
+        raise ValueError("prologue mode %r" % (mode,))
+    alpha = None
+    if alpha_logit is not None:
+        a = np.asarray(alpha_logit, np.float64)
+        alpha = _sigmoid(a) if mode == PRO_ALPHA_SIGMOID else _sigmoid(-a)
+    return l2_normalise(q), l2_normalise(k), _sigmoid(beta_logit), alpha
+
+
+def _l2_normalise_backward(x, dxh):
+    x = np.asarray(x, np.float64)
+    n = np.sqrt((x * x).sum(-1, keepdims=True))
+    big = n > NORM_EPS
+    xh = x / np.maximum(n, NORM_EPS)
+    proj = dxh - xh * (xh * dxh).sum(-1, keepdims=True)
+    return np.where(big, proj / np.where(big, n, 1.0), dxh / NORM_EPS)
+
+
+def prologue_backward(q, k, beta_logit, alpha_logit, mode, g):
+    """Takes the gradients ``g`` of :func:`backward` (with respect to q_hat,
+    k_hat, beta, alpha) back to the raw inputs; returns a new dict."""
+    out = dict(g)
+    out["dq"] = _l2_normalise_backward(q, g["dq"])
+    out["dk"] = _l2_normalise_backward(k, g["dk"])
+    bt = _sigmoid(beta_logit)
+    out["dbeta"] = g["dbeta"] * bt * (1.0 - bt)
+    if alpha_logit is not None:
+        a = np.asarray(alpha_logit, np.float64)
+        s = 1.0 if mode == PRO_ALPHA_SIGMOID else -1.0
+        al = _sigmoid(s * a)
+        out["dalpha"] = g["dalpha"] * s * al * (1.0 - al)
+    return out

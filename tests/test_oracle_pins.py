@@ -576,3 +576,90 @@ def test_cler_routing_adds_scaled_errors():
     dE, dlam = oracle.cler_backward(dh, E, lam)
     assert np.abs(dE.reshape(1, 4, 6) - lam * dh).max() < 1e-15
     assert np.abs(dlam - (dh * E.reshape(1, 4, 6)).sum((0, 1))).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# prologue: L2-normalised q, k and activated gates
+# --------------------------------------------------------------------------
+
+
+def test_l2_normalise_gives_unit_rows_and_keeps_zero_rows():
+    r = np.random.default_rng(60)
+    x = r.standard_normal((4, 3, 7)) * r.uniform(0.01, 50, (4, 3, 1))
+    n = np.linalg.norm(oracle.l2_normalise(x), axis=-1)
+    assert np.abs(n - 1).max() < 1e-15
+    z = np.zeros((2, 5))
+    assert np.array_equal(oracle.l2_normalise(z), z)
+    tiny = np.full((1, 4), 1e-9)
+    assert np.allclose(oracle.l2_normalise(tiny), tiny / oracle.NORM_EPS, rtol=1e-15)
+
+
+def test_gate_activations():
+    """beta = sigmoid(b); the two alpha readings are mirror images
+    (exp(-softplus(a)) = 1 - sigmoid(a)), checked against log1p/exp directly."""
+    a = np.linspace(-30, 30, 61)
+    _, _, b0, al_s = oracle.prologue_forward(np.ones((1, 2)), np.ones((1, 2)), np.zeros(1), a,
+                                             oracle.PRO_ALPHA_SIGMOID)
+    _, _, _, al_f = oracle.prologue_forward(np.ones((1, 2)), np.ones((1, 2)), np.zeros(1), a,
+                                            oracle.PRO_ALPHA_FORGET)
+    assert b0[0] == 0.5
+    assert np.abs(al_s + al_f - 1).max() < 1e-15
+    assert np.abs(al_f - np.exp(-np.log1p(np.exp(a)))).max() < 1e-15
+    assert np.abs(al_s - 1 / (1 + np.exp(-a))).max() < 1e-15
+
+
+def test_forget_gate_bias_from_the_page():
+    with open(os.path.join(HERE, "golden", "forget_gate_bias.json")) as f:
+        g = json.load(f)
+    _, _, _, al = oracle.prologue_forward(np.ones((1, 2)), np.ones((1, 2)), np.zeros(1), np.array([g["bias"]]),
+                                          oracle.PRO_ALPHA_FORGET)
+    assert abs((1 - al[0]) - g["forget_fraction"]) < g["tolerance"]
+    assert al[0] > 0.9  # the state keeps most of itself per token at initialisation
+
+
+def test_prologue_exact_retrieval_with_unnormalised_keys():
+    """q = k = c * u for any c > 0 and beta -> 1 (logit 40 rounds to 1.0 in
+    fp64): after the prologue the read-out returns v exactly (KDA blog 2.1)."""
+    r = np.random.default_rng(61)
+    B, T, H, d = 1, 6, 2, 5
+    u = unit(r.standard_normal((B, T, H, d)))
+    c = r.uniform(0.1, 40, (B, T, H, 1))
+    v = r.standard_normal((B, T, H, d))
+    a = r.standard_normal((B, T, H, d))
+    qh, kh, bt, al = oracle.prologue_forward(c * u, c * u, np.full((B, T, H), 40.0), a, oracle.PRO_ALPHA_FORGET)
+    assert np.all(bt == 1.0)
+    o, _ = oracle.forward(qh, kh, v, bt, al, None)
+    assert np.abs(o - v).max() < 1e-12
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prologue_backward_matches_central_differences(mode):
+    r = np.random.default_rng(62 + mode)
+    B, T, H, d = 1, 5, 2, 4
+    q = r.standard_normal((B, T, H, d)) * 3
+    k = r.standard_normal((B, T, H, d)) * 0.5
+    v = r.standard_normal((B, T, H, d))
+    b = r.standard_normal((B, T, H))
+    a = r.standard_normal((B, T, H, d)) + 2
+    dO = r.standard_normal((B, T, H, d))
+
+    def loss(q_, k_, b_, a_):
+        qh, kh, bt, al = oracle.prologue_forward(q_, k_, b_, a_, mode)
+        o, _ = oracle.forward(qh, kh, v, bt, al, None)
+        return float((o * dO).sum())
+
+    qh, kh, bt, al = oracle.prologue_forward(q, k, b, a, mode)
+    g = oracle.prologue_backward(q, k, b, a, mode, oracle.backward(qh, kh, v, bt, al, None, dO))
+    eps = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dbeta", b), ("dalpha", a)):
+        num = np.zeros_like(x)
+        for mi in np.ndindex(x.shape):
+            old = x[mi]
+            x[mi] = old + eps
+            lp = loss(q, k, b, a)
+            x[mi] = old - eps
+            lm = loss(q, k, b, a)
+            x[mi] = old
+            num[mi] = (lp - lm) / (2 * eps)
+        err = np.abs(num - g[name]).max() / max(1.0, np.abs(num).max())
+        assert err < 1e-7, (name, err)
