@@ -9,6 +9,7 @@ import torch
 
 GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
 ROUTE_VALUE, ROUTE_ERROR = 0, 1
+PROLOGUE_NONE, PROLOGUE_ALPHA_SIGMOID, PROLOGUE_ALPHA_FORGET = 0, 1, 2
 _BF16, _FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("gate", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("chunk", ctypes.c_int32), ("route", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("chunk", ctypes.c_int32), ("route", ctypes.c_int32),
+                ("prologue", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -123,11 +125,24 @@ def _route(route):
     raise ValueError("route must be 'value' (CLVR) or 'error' (CLER-H), got %r" % (route,))
 
 
-def _desc(q, v, alpha, out_dtype, scale, route=ROUTE_VALUE):
+_PROLOGUES = {None: PROLOGUE_NONE, "none": PROLOGUE_NONE, "sigmoid": PROLOGUE_ALPHA_SIGMOID,
+              "forget": PROLOGUE_ALPHA_FORGET}
+
+
+def _prologue(p):
+    if p in (PROLOGUE_NONE, PROLOGUE_ALPHA_SIGMOID, PROLOGUE_ALPHA_FORGET):
+        return int(p)
+    if p in _PROLOGUES:
+        return _PROLOGUES[p]
+    raise ValueError("prologue must be None, 'sigmoid' or 'forget' (or 0, 1, 2), got %r" % (p,))
+
+
+def _desc(q, v, alpha, out_dtype, scale, route=ROUTE_VALUE, prologue=None):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     return Desc(B, T, H, dk, dv, _gate_of(alpha, q), _dt(q.dtype),
-                _dt(out_dtype if out_dtype is not None else q.dtype), float(scale), 0, _route(route))
+                _dt(out_dtype if out_dtype is not None else q.dtype), float(scale), 0, _route(route),
+                _prologue(prologue))
 
 
 def _stream(device):
@@ -135,8 +150,9 @@ def _stream(device):
 
 
 def workspace_size(B, T, H, d, gate=GATE_CHANNEL, in_dtype=torch.bfloat16, out_dtype=None,
-                   backward=False, route=ROUTE_VALUE) -> int:
-    desc = Desc(B, T, H, d, d, gate, _dt(in_dtype), _dt(out_dtype or in_dtype), 1.0, 0, _route(route))
+                   backward=False, route=ROUTE_VALUE, prologue=None) -> int:
+    desc = Desc(B, T, H, d, d, gate, _dt(in_dtype), _dt(out_dtype or in_dtype), 1.0, 0, _route(route),
+                _prologue(prologue))
     n = load_library().gdr_workspace_size(ctypes.byref(desc), 1 if backward else 0)
     if n == 0 and B * H * T > 0:
         _check(1)
@@ -163,13 +179,17 @@ def _check_inputs(q, k, v, beta, alpha, S0):
 
 def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=None,
             clvr_scale=None, output_final_state=True, workspace=None, save_for_backward=False,
-            route="value"):
+            route="value", prologue=None):
     """Chunked forward.  Returns ``(o, S_T)`` (``S_T`` None unless requested).
 
     ``h`` ([B, T, H*dv], q's dtype) is updated in place by the hidden-stream
     epilogue when given: ``h += clvr_scale * v`` (``route="value"``, CLVR) or
     ``h += clvr_scale * e`` with the write errors ``e_t = u_t / beta_t``
     (``route="error"``, CLER-H; every beta must be nonzero).
+
+    ``prologue="sigmoid"`` or ``"forget"``: q and k are passed unnormalised and
+    beta, alpha as logits; the library L2-normalises q and k and applies
+    beta = sigmoid(b) and alpha = sigmoid(a) resp. exp(-softplus(a)).
 
     ``save_for_backward=True`` runs the training forward: ``workspace`` (a uint8
     tensor of ``workspace_size(..., backward=True)`` bytes, required) then holds
@@ -178,7 +198,7 @@ def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=
     _need(h, "h", q.dtype, (B, T, H * dv))
     _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
     lib = load_library()
-    desc = _desc(q, v, alpha, out_dtype, scale, route)
+    desc = _desc(q, v, alpha, out_dtype, scale, route, prologue)
     o = torch.empty((B, T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
     ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     need = lib.gdr_workspace_size(ctypes.byref(desc), 1 if save_for_backward else 0)
@@ -198,7 +218,7 @@ def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=
 
 def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=None, dh=None,
              clvr_scale=None, want_dclvr_scale=False, workspace=None, saved_workspace=None,
-             route="value"):
+             route="value", prologue=None):
     """Gradients of :func:`forward`.  Returns a dict with ``dq, dk, dv, dbeta,
     dalpha`` (None for DeltaNet), ``dS0`` and ``dclvr_scale`` (when asked).
     ``dh`` is the gradient at the hidden stream after the epilogue of the given
@@ -213,7 +233,7 @@ def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=Non
     _need(dh, "dh", q.dtype, (B, T, H * dv))
     _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
     lib = load_library()
-    desc = _desc(q, v, alpha, out_dtype, scale, route)
+    desc = _desc(q, v, alpha, out_dtype, scale, route, prologue)
     od = out_dtype or q.dtype
     dq = torch.empty_like(q, dtype=od)
     dk_ = torch.empty_like(k, dtype=od)

@@ -58,6 +58,8 @@ gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
     if (!std::isfinite(d->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is not finite");
     if (d->route != GDR_ROUTE_VALUE && d->route != GDR_ROUTE_ERROR)
         return fail(GDR_ERR_INVALID_ARG, "unknown epilogue route %d", d->route);
+    if (d->prologue < GDR_PROLOGUE_NONE || d->prologue > GDR_PROLOGUE_ALPHA_FORGET)
+        return fail(GDR_ERR_INVALID_ARG, "unknown prologue %d", d->prologue);
     if (d->dk != d->dv || (d->dk != 64 && d->dk != 128))
         return fail(GDR_ERR_UNSUPPORTED, "only dk == dv in {64, 128} is supported (got %lld, %lld)",
                     (long long)d->dk, (long long)d->dv);
@@ -98,7 +100,8 @@ namespace gdr {
 
 // Carves the chunk workspace; returns the bytes needed.  `base` may be NULL
 // (sizing only).
-size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, ChunkWs* out, void* base) {
+size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, bool pro, ChunkWs* out,
+                      void* base) {
     ChunkWs w;
     std::memset(&w, 0, sizeof w);
     size_t off = 0;
@@ -121,6 +124,12 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
     // kernel and the gradient kernels
     w.Ssnap = take(st);
     w.Usave = take(mat);
+    if (pro) {
+        // one float per token-head each (nch * 64 covers B * T * H)
+        w.Bact = static_cast<float*>(take(size_t(nch) * kChunk * 4));
+        w.rq = static_cast<float*>(take(size_t(nch) * kChunk * 4));
+        w.rk = static_cast<float*>(take(size_t(nch) * kChunk * 4));
+    }
     if (backward) {
         const size_t sq32 = size_t(nch) * kChunk * kChunk * 4;
         const size_t mat32 = size_t(nch) * kChunk * D * 4;
@@ -173,8 +182,8 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     }
     const int64_t nch = desc->B * desc->H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
-    size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, desc->route == GDR_ROUTE_ERROR, nullptr,
-                                   nullptr);
+    size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, desc->route == GDR_ROUTE_ERROR,
+                                   desc->prologue != GDR_PROLOGUE_NONE, nullptr, nullptr);
     if (op == 1) n += align_up(dlam_partial_bytes(desc));
     return n;
 }
@@ -229,7 +238,9 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     const int64_t nch = B * H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
     gdr::ChunkWs w;
-    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, train, desc->route == GDR_ROUTE_ERROR, &w, ws);
+    const int pro = desc->prologue;
+    const size_t chunk_bytes =
+        gdr::chunk_ws_bytes(nch, int(D), opb, train, desc->route == GDR_ROUTE_ERROR, pro != 0, &w, ws);
     const size_t need = train ? chunk_bytes + align_up(dlam_partial_bytes(desc)) : chunk_bytes;
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
@@ -247,11 +258,13 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     // the value-routing epilogue runs in the intra-chunk kernel (it needs only
     // v); the error-routing one needs U, so it follows the state pass
     const bool cler = h_clvr && desc->route == GDR_ROUTE_ERROR;
+    // with the prologue the kernels after the intra-chunk one read its activated beta
+    const float* beta_eff = pro ? w.Bact : beta;
     hipError_t e = hipSuccess;
     if (NC > 0) {
         gdr::prof_before(s);
         e = gdr::launch_intra(int(D), desc->gate, in_f32, train ? 2 : 0, B, T, int(H), NC, q, k, v, beta,
-                              alpha, cler ? nullptr : h_clvr, cler ? nullptr : clvr_scale, w, s);
+                              alpha, cler ? nullptr : h_clvr, cler ? nullptr : clvr_scale, w, pro, s);
         gdr::prof_after(train ? "intra_train" : "intra_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
     }
@@ -262,14 +275,14 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     if (!in_f32 && NC > 0) {
         gdr::prof_before(s);
-        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta, clvr_scale,
+        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff, clvr_scale,
                                cler ? h_clvr : nullptr, s);
         gdr::prof_after(cler ? "output_cler" : "output", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
     }
     if (in_f32 && cler && NC > 0) {
         gdr::prof_before(s);
-        e = gdr::launch_cler_fwd(int(D), in_f32, B, T, int(H), NC, w, beta, clvr_scale, h_clvr, s);
+        e = gdr::launch_cler_fwd(int(D), in_f32, B, T, int(H), NC, w, beta_eff, clvr_scale, h_clvr, s);
         gdr::prof_after("cler_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "error-routing launch: %s", hipGetErrorString(e));
     }
@@ -326,7 +339,9 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const int64_t nch = B * H * NC;
     const int opb = desc->in_dtype == GDR_FP32 ? 4 : 2;
     gdr::ChunkWs w;
-    const size_t chunk_bytes = gdr::chunk_ws_bytes(nch, int(D), opb, true, desc->route == GDR_ROUTE_ERROR, &w, ws);
+    const int pro = desc->prologue;
+    const size_t chunk_bytes =
+        gdr::chunk_ws_bytes(nch, int(D), opb, true, desc->route == GDR_ROUTE_ERROR, pro != 0, &w, ws);
     const size_t need = chunk_bytes + align_up(dlam_partial_bytes(desc));
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
@@ -349,28 +364,31 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     } while (0)
     if (NC > 0 && recompute) {
         GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, 1, B, T, int(H), NC, q, k, v, beta,
-                                                alpha, nullptr, nullptr, w, s));
+                                                alpha, nullptr, nullptr, w, pro, s));
         GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
                                                          desc->scale, w, S0, nullptr, nullptr, true, s));
     }
     // error routing: dh reaches U inside the reverse state pass and beta and the
     // scale afterwards; value routing: dh reaches v in the gradient kernel
     const bool cler = dh_clvr && desc->route == GDR_ROUTE_ERROR;
+    // with the prologue the kernels after the intra-chunk one read its activated beta
+    const float* beta_eff = pro ? w.Bact : beta;
     if (cler && NC > 0)
         GDR_STEP("cler_mt", gdr::launch_cler_mt(int(D), in_f32, B, T, int(H), NC, w, clvr_scale, dh_clvr, s));
     GDR_STEP(cler ? "state_bwd_cler" : "state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
-                                                 dS0, cler ? dh_clvr : nullptr, clvr_scale, beta, s));
+                                                 dS0, cler ? dh_clvr : nullptr, clvr_scale, beta_eff, s));
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
     if (NC > 0) {
         // both routes add lam * dh to dv: the value route through v itself,
         // the error route through e = v - ...
         GDR_STEP("grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
-                                                  q, k, v, beta, alpha, dO, dh_clvr, clvr_scale, dv, dbeta, w, s));
+                                                  q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dv, dbeta, w,
+                                                  pro, s));
         if (cler)
-            GDR_STEP("cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta, clvr_scale,
+            GDR_STEP("cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta_eff, clvr_scale,
                                                         dh_clvr, dclvr_scale, partial, s));
         GDR_STEP("grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
-                                                    alpha, dq, dk, dalpha, w, s));
+                                                    alpha, dq, dk, dalpha, w, pro, s));
     }
     if (cler) {
         if (dclvr_scale && NC == 0)

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
                                                          const float* __restrict__ alpha,
                                                          const void* __restrict__ dO_, const void* __restrict__ dh_,
                                                          const float* __restrict__ lam, void* __restrict__ dv_,
-                                                         float* __restrict__ dbeta, ChunkWs ws) {
+                                                         float* __restrict__ dbeta, ChunkWs ws, int pro) {
     using L = GLinLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -190,11 +190,11 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     if (tid < CHUNK) {
         const bool ok = tid < nvalid;
         const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
-        const float bt = beta[tok];
+        const float bt = beta[tok];  // activated (the prologue's copy when it is on)
         s_beta[tid] = ok ? bt : 0.f;
         if constexpr (GATE == GATE_SCALAR) {
             const float at = alpha[tok];
-            float g = ok ? log2_fast(at) : 0.f;
+            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -207,7 +207,9 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     for (int j = 0; j < RPP; ++j) {
         const bool ok = r0 + j < nvalid;
         kk[j] = ok ? kk[j] : 0.f;
-        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(G[j]) : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (pro ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
+        // prologue: k divided by its row norm (kept by the intra-chunk kernel)
+        if (pro && ok) kk[j] *= fabsf(ws.rk[(b * T + t0 + r0 + j) * H + h]);
     }
     if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
@@ -481,18 +483,22 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         s_db[tid] = sdb;
     }
     __syncthreads();
-    if (tid < nvalid) dbeta[(b * T + t0 + tid) * H + h] = s_db[tid];
+    if (tid < nvalid) {
+        float db = s_db[tid];
+        if (pro) db *= s_beta[tid] * (1.f - s_beta[tid]);  // prologue: beta = sigmoid(logit)
+        dbeta[(b * T + t0 + tid) * H + h] = db;
+    }
 }
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* k,
                                     const void* v, const float* beta, const float* alpha, const void* dO,
                                     const void* dh, const float* lam, void* dv, float* dbeta, const ChunkWs& ws,
-                                    hipStream_t stream) {
+                                    int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
     hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T,
-                       H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws);
+                       H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
     return hipGetLastError();
 }
 
@@ -500,25 +506,25 @@ template <int D, int GATE>
 static hipError_t launch_grad_lin_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                                     float scale, const void* k, const void* v, const float* beta,
                                     const float* alpha, const void* dO, const void* dh, const float* lam,
-                                    void* dv, float* dbeta, const ChunkWs& ws, hipStream_t stream) {
+                                    void* dv, float* dbeta, const ChunkWs& ws, int pro, hipStream_t stream) {
     if (in_f32) {
         if constexpr (D == 64) {
-            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
-            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
+            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
         }
         return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
     }
-    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
-    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream);
+    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
+    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
 }
 
 hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                            int64_t NC, float scale, const void* q, const void* k, const void* v,
                            const float* beta, const float* alpha, const void* dO,
                            const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, hipStream_t stream) {
+                           const ChunkWs& ws, int pro, hipStream_t stream) {
     (void)q;
-#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, stream
+#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grad_lin_g<64, GATE_NONE>(GL_ARGS);
         if (gate == GATE_SCALAR) return launch_grad_lin_g<64, GATE_SCALAR>(GL_ARGS);
@@ -579,7 +585,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
                                                           const void* __restrict__ q_, const void* __restrict__ k_,
                                                           const float* __restrict__ alpha, void* __restrict__ dq_,
                                                           void* __restrict__ dk_, float* __restrict__ dalpha,
-                                                          ChunkWs ws) {
+                                                          ChunkWs ws, int pro) {
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -591,6 +597,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     __shared__ float s_gs[CHUNK];
     __shared__ float s_red[NW];
     __shared__ float s_row[CHUNK];
+    __shared__ float s_nrm[NW * 2 * RPP];  // prologue: row-dot partials
 
     OpT* dAs = reinterpret_cast<OpT*>(smem + L::DA);
     OpT* dPs = reinterpret_cast<OpT*>(smem + L::DP);
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         if (tid < CHUNK) {
             const bool ok = tid < nvalid;
             const float at = alpha[(b * T + t0 + (ok ? tid : nvalid - 1)) * H + h];
-            float g = ok ? log2_fast(at) : 0.f;
+            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
             s_row[tid] = ok ? at : 1.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -651,10 +658,17 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         kk[j] = ok ? kk[j] : 0.f;
         qq[j] = ok ? qq[j] : 0.f;
         if constexpr (GATE == GATE_CHANNEL) {
+            // prologue: al stays the logit (the final dalpha needs it)
             al[j] = ok ? al[j] : 1.f;
-            G[j] = log2_fast(al[j]);
+            G[j] = ok ? (pro ? log2_alpha_logit(al[j], pro) : log2_fast(al[j])) : 0.f;
         } else {
             G[j] = 0.f;
+        }
+        if (pro && ok) {
+            // prologue: q and k divided by their row norms
+            const int64_t tok = (b * T + t0 + r0 + j) * H + h;
+            qq[j] *= fabsf(ws.rq[tok]);
+            kk[j] *= fabsf(ws.rk[tok]);
         }
     }
     if constexpr (GATE == GATE_CHANNEL) {
@@ -860,18 +874,41 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
             pkt[j] = gKt[(r0 + j) * D + cc];
             pkb[j] = gKb[(r0 + j) * D + cc];
         }
+        float dqa[RPP], dka[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
+            const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
+            dqa[j] = gq + Aq[j];
+            dka[j] = gkt + gkb + Prow[j] + Ccol[j];
+            dG[j] = qq[j] * dqa[j] + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
+            lastsum += kk[j] * gkb;
+        }
+        if (pro) {
+            // prologue: back through x / |x|: (dx_hat - x_hat (x_hat . dx_hat)) / |x|
+            // (only dx_hat / eps where the norm was clamped)
+            float dot[2 * RPP];
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                dot[j] = qq[j] * dqa[j];
+                dot[RPP + j] = kk[j] * dka[j];
+            }
+            part_row_sums<D, 2 * RPP>(dot, s_nrm);
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                if (r0 + j >= nvalid) continue;
+                const int64_t tok = (b * T + t0 + r0 + j) * H + h;
+                const float rq = ws.rq[tok], rk = ws.rk[tok];
+                dqa[j] = (rq > 0.f) ? (dqa[j] - qq[j] * dot[j]) * rq : -dqa[j] * rq;
+                dka[j] = (rk > 0.f) ? (dka[j] - kk[j] * dot[RPP + j]) * rk : -dka[j] * rk;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = r0 + j;
-            const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
-            const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
-            const float dqv = gq + Aq[j];
-            const float dkv = gkt + gkb + Prow[j] + Ccol[j];
-            dG[j] = qq[j] * dqv + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
-            lastsum += kk[j] * gkb;
             if (r < nvalid) {
-                dq[base + r * tokstride + cc] = from_f32<OutT>(dqv);
-                dk[base + r * tokstride + cc] = from_f32<OutT>(dkv);
+                dq[base + r * tokstride + cc] = from_f32<OutT>(dqa[j]);
+                dk[base + r * tokstride + cc] = from_f32<OutT>(dka[j]);
             }
         }
     }
@@ -907,7 +944,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
 #pragma unroll
             for (int j = 0; j < RPP; ++j) {
                 const int r = r0 + j;
-                if (r < nvalid) dalpha[base + r * tokstride + cc] = dg[j] / al[j];
+                if (r < nvalid)
+                    dalpha[base + r * tokstride + cc] = pro ? dlogit_from_dlog(dg[j], al[j], pro) : dg[j] / al[j];
             }
         } else {
             // scalar gate: sum over channels
@@ -924,7 +962,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
             __syncthreads();
             if (tid < nvalid) {
                 float a1 = alpha[(b * T + t0 + tid) * H + h];
-                dalpha[(b * T + t0 + tid) * H + h] = s_row[tid] / a1;
+                dalpha[(b * T + t0 + tid) * H + h] = pro ? dlogit_from_dlog(s_row[tid], a1, pro) : s_row[tid] / a1;
             }
         }
     }
@@ -933,33 +971,33 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
                                      const float* alpha, void* dq, void* dk, float* dalpha, const ChunkWs& ws,
-                                     hipStream_t stream) {
+                                     int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
     hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream,
-                       T, H, NC, q, k, alpha, dq, dk, dalpha, ws);
+                       T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
     return hipGetLastError();
 }
 
 template <int D, int GATE>
 static hipError_t launch_grad_gate_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                                      const void* q, const void* k, const float* alpha, void* dq, void* dk,
-                                     float* dalpha, const ChunkWs& ws, hipStream_t stream) {
+                                     float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream) {
     if (in_f32) {
         if constexpr (D == 64) {
-            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
-            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
+            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
         }
         return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
     }
-    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
-    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream);
+    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
+    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
 }
 
 hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, hipStream_t stream) {
-#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, stream
+                            void* dk, float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream) {
+#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grad_gate_g<64, GATE_NONE>(GG_ARGS);
         if (gate == GATE_SCALAR) return launch_grad_gate_g<64, GATE_SCALAR>(GG_ARGS);

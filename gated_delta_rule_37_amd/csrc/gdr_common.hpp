@@ -211,4 +211,70 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// ---------------------------------------------------------------------------
+// Prologue: L2-normalised q and k, activated gates (KDA blog, sections 2.1 and
+// 7.1: an L2 norm after the q/k projections; sigmoid gates, with the forget
+// gate's logit biased to -3 so that it forgets ~5 % per token at the start).
+//   PRO 1: beta = sigmoid(b), alpha = sigmoid(a)
+//   PRO 2: beta = sigmoid(b), alpha = exp(-softplus(a)) = sigmoid(-a)
+// A row is divided by max(|row|_2, NORM_EPS).
+// ---------------------------------------------------------------------------
+constexpr float NORM_EPS = 1e-6f;
+
+__device__ __forceinline__ float sigmoid_acc(float x) {
+    if (x >= 0.f) return 1.f / (1.f + expf(-x));
+    const float e = expf(x);
+    return e / (1.f + e);
+}
+
+// s = +1 (PRO 1) or -1 (PRO 2): alpha = sigmoid(s a)
+__device__ __forceinline__ float pro_sign(int pro) { return pro == 1 ? 1.f : -1.f; }
+
+// log2(alpha) from the logit, without forming alpha: -softplus(-s a) / ln 2
+__device__ __forceinline__ float log2_alpha_logit(float a, int pro) {
+    const float y = -pro_sign(pro) * a;
+    const float sp = fmaxf(y, 0.f) + log1pf(expf(-fabsf(y)));
+    return -sp * 1.4426950408889634f;
+}
+
+// d alpha-logit from the gradient with respect to ln(alpha):
+// d ln(sigmoid(s a)) / da = s (1 - sigmoid(s a)) = s sigmoid(-s a)
+__device__ __forceinline__ float dlogit_from_dlog(float dlog, float a, int pro) {
+    const float s = pro_sign(pro);
+    return dlog * s * sigmoid_acc(-s * a);
+}
+
+// Reciprocal norm of a row, with the clamped case flagged by the sign (the
+// gradient then has no projection term).
+__device__ __forceinline__ float recip_norm(float sumsq) {
+    const float n = sqrtf(sumsq);
+    return n > NORM_EPS ? 1.f / n : -1.f / NORM_EPS;
+}
+
+// Sums x[j] over the D threads of this thread's part (threads part*D ..
+// part*D + D - 1, D / 64 whole waves) for every j, in a fixed order; every
+// thread of the part receives the totals.  red: LDS scratch of
+// (threads / 64) * N floats.  Called by every thread of the workgroup.
+template <int D, int N>
+__device__ __forceinline__ void part_row_sums(float (&x)[N], float* red) {
+    const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x[j] += __shfl_xor(x[j], off);
+    }
+    if constexpr (D > WAVE) {
+        static_assert(D == 2 * WAVE, "two waves per part");
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < N; ++j) red[wid * N + j] = x[j];
+        }
+        __syncthreads();
+        const int w0 = wid & ~1;
+#pragma unroll
+        for (int j = 0; j < N; ++j) x[j] = red[w0 * N + j] + red[(w0 + 1) * N + j];
+        __syncthreads();
+    }
+}
+
 }  // namespace gdr

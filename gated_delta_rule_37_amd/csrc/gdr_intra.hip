@@ -98,7 +98,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                                                       const float* __restrict__ beta,
                                                       const float* __restrict__ alpha,
                                                       void* __restrict__ h_, const float* __restrict__ lam,
-                                                      ChunkWs ws) {
+                                                      ChunkWs ws, int pro) {
     constexpr bool FO = MODE != 1;  // forward operands: Qt, A
     constexpr bool BWD = MODE != 0; // backward operands: Kb, Qt^T, A^T, W^T, N, P
     using L = IntraLayout<D, GATE, IN_F32>;
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     __shared__ float s_gs[CHUNK];  // scalar-gate G per row
     __shared__ float s_beta[CHUNK];
     __shared__ float s_red[NW][2];
+    __shared__ float s_nrm[NW * 2 * L::RPP];  // prologue: row-norm partials
 
     OpT* Kq = reinterpret_cast<OpT*>(smem + L::KQ);
     OpT* Qq = reinterpret_cast<OpT*>(smem + L::QQ);
@@ -168,11 +169,17 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     if (tid < CHUNK) {
         const bool ok = tid < nvalid;
         const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
-        const float bt = beta[tok];
+        float bt = beta[tok];
+        if (pro) {
+            // prologue: beta arrives as a logit; the activated value is kept for
+            // the later kernels
+            bt = sigmoid_acc(bt);
+            if (ok) ws.Bact[tok] = bt;
+        }
         s_beta[tid] = ok ? bt : 0.f;
         if constexpr (GATE == GATE_SCALAR) {
             const float at = alpha[tok];
-            float g = ok ? log2_fast(at) : 0.f;
+            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -187,7 +194,32 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         kk[j] = ok ? kk[j] : 0.f;
         qq[j] = ok ? qq[j] : 0.f;
         vv[j] = ok ? vv[j] : 0.f;
-        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? log2_fast(G[j]) : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (pro ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
+    }
+    if (pro) {
+        // prologue: q and k rows divided by their L2 norms (sums over the D
+        // threads of this part); the backward kernels get the reciprocal norms
+        float nrm[2 * RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            nrm[j] = qq[j] * qq[j];
+            nrm[RPP + j] = kk[j] * kk[j];
+        }
+        part_row_sums<D, 2 * RPP>(nrm, s_nrm);
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const float rq = recip_norm(nrm[j]), rk = recip_norm(nrm[RPP + j]);
+            qq[j] *= fabsf(rq);
+            kk[j] *= fabsf(rk);
+            if constexpr (BWD) {
+                const int r = r0 + j;
+                if (cc == 0 && r < nvalid) {
+                    const int64_t tok = (b * T + t0 + r) * H + h;
+                    ws.rq[tok] = rq;
+                    ws.rk[tok] = rk;
+                }
+            }
+        }
     }
     if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
@@ -623,18 +655,18 @@ template <int D, int GATE, bool IN_F32>
 static hipError_t launch_intra_t(int mode, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                                  const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
-                                 const ChunkWs& ws, hipStream_t stream) {
+                                 const ChunkWs& ws, int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
     if (mode == 1)
         hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 1>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
     else if (mode == 2)
         hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 2>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
     else
         hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 0>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws);
+                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
     return hipGetLastError();
 }
 
@@ -642,24 +674,24 @@ template <int D, bool IN_F32>
 static hipError_t launch_intra_d(int gate, int mode, int64_t B, int64_t T, int H, int64_t NC,
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
-                                 const ChunkWs& ws, hipStream_t stream) {
+                                 const ChunkWs& ws, int pro, hipStream_t stream) {
     switch (gate) {
-        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
     }
 }
 
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
-                        const ChunkWs& ws, hipStream_t stream) {
+                        const ChunkWs& ws, int pro, hipStream_t stream) {
     if (D == 64) {
-        if (in_f32) return launch_intra_d<64, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-        return launch_intra_d<64, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+        if (in_f32) return launch_intra_d<64, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+        return launch_intra_d<64, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
     }
-    if (in_f32) return launch_intra_d<128, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
-    return launch_intra_d<128, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, stream);
+    if (in_f32) return launch_intra_d<128, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+    return launch_intra_d<128, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
 }
 
 }  // namespace gdr

@@ -30,13 +30,17 @@ struct ChunkWs {
     void *Ssnap, *Usave, *dSsnap, *dUsave, *dUsaveT;
     float *gQt, *gKt, *gKb, *gA, *gP, *gGam;
     void* Mt;  // error-routing backward: M^T dE [64][D] per chunk-head
+    // prologue: activated beta ([B,T,H] layout) and the reciprocal row norms of
+    // q and k (negative where the norm was clamped), written by the intra kernel
+    float *Bact, *rq, *rk;
 };
 
 // Per-launch event timing (gdr_profile_begin/end); no-ops unless enabled.
 void prof_before(hipStream_t stream);
 void prof_after(const char* name, hipStream_t stream);
 
-size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, ChunkWs* out, void* base);
+size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler, bool pro, ChunkWs* out,
+                      void* base);
 
 hipError_t launch_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, int H,
                          float scale, const void* q, const void* k, const void* v,
@@ -51,10 +55,12 @@ hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64
                          const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
                          hipStream_t stream);
 
+// pro: the prologue (0 none; 1 / 2 the two alpha activations, gdr_prologue):
+// q, k arrive unnormalised and beta, alpha as logits.
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
-                        const ChunkWs& ws, hipStream_t stream);
+                        const ChunkWs& ws, int pro, hipStream_t stream);
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
@@ -70,11 +76,11 @@ hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B
                            int64_t NC, float scale, const void* q, const void* k, const void* v,
                            const float* beta, const float* alpha, const void* dO,
                            const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, hipStream_t stream);
+                           const ChunkWs& ws, int pro, hipStream_t stream);
 
 hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, hipStream_t stream);
+                            void* dk, float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream);
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);

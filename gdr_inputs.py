@@ -16,6 +16,12 @@ Recipe (fixed draw order per seed, NumPy ``default_rng``):
   S0    ~ N(0, 0.02^2) fp32 (standard deviation 0.02) where a config asks for it
   dO    ~ N(0, 1) in the input dtype (backward configs)
   h     ~ N(0, 1) in the input dtype, [B, T, H*dv] (CLVR configs)
+With ``prologue`` ("sigmoid" or "forget") the operator's own prologue is
+exercised instead: q and k ~ N(0, 1) times a per-row scale drawn from
+U(0.2, 5), not normalised; beta is a logit ~ N(0, 1); alpha a logit
+~ N(3, 1) ("sigmoid": alpha = sigmoid(a)) or ~ N(-3, 1) ("forget": alpha =
+1 - sigmoid(a), the forget-gate bias -3 of KDA blog section 7.1), so that
+alpha lands near 0.95 either way.
 All arrays come back as float32 NumPy arrays whose values are exactly
 representable in the declared dtype (bf16 values are exact in fp32).
 """
@@ -69,22 +75,35 @@ def _unit_rows(x):
 
 
 def make(B, T, H, d, gate="channel", dtype="bf16", seed=0, s0=False, bwd=False, clvr=False,
-         alpha_recipe="sigmoid(N(3,1))", beta_recipe="sigmoid(N(0,1))", **_unused):
+         alpha_recipe="sigmoid(N(3,1))", beta_recipe="sigmoid(N(0,1))", prologue=None, **_unused):
     """Draws one batch of chunked-path inputs.  Returns a dict of float32 arrays
     (``alpha`` None for DeltaNet, ``S0`` None for a zero start)."""
     if gate not in GATES:
         raise ValueError(gate)
+    if prologue not in (None, "sigmoid", "forget"):
+        raise ValueError(prologue)
     rng = np.random.default_rng(seed)
     out = {}
-    out["q"] = round_to(_unit_rows(rng.standard_normal((B, T, H, d))), dtype)
-    out["k"] = round_to(_unit_rows(rng.standard_normal((B, T, H, d))), dtype)
+    if prologue is None:
+        out["q"] = round_to(_unit_rows(rng.standard_normal((B, T, H, d))), dtype)
+        out["k"] = round_to(_unit_rows(rng.standard_normal((B, T, H, d))), dtype)
+    else:
+        out["q"] = round_to(rng.standard_normal((B, T, H, d)) * rng.uniform(0.2, 5, (B, T, H, 1)), dtype)
+        out["k"] = round_to(rng.standard_normal((B, T, H, d)) * rng.uniform(0.2, 5, (B, T, H, 1)), dtype)
     out["v"] = round_to(rng.standard_normal((B, T, H, d)), dtype)
-    out["beta"] = _beta(rng, (B, T, H), beta_recipe)
+    if prologue is None:
+        out["beta"] = _beta(rng, (B, T, H), beta_recipe)
+    else:
+        out["beta"] = rng.standard_normal((B, T, H)).astype(np.float32)
     if gate == "none":
         out["alpha"] = None
     else:
         shape = (B, T, H) if gate == "scalar" else (B, T, H, d)
-        out["alpha"] = _alpha(rng, shape, alpha_recipe)
+        if prologue is None:
+            out["alpha"] = _alpha(rng, shape, alpha_recipe)
+        else:
+            mu = 3.0 if prologue == "sigmoid" else -3.0
+            out["alpha"] = (mu + rng.standard_normal(shape)).astype(np.float32)
     out["S0"] = (0.02 * rng.standard_normal((B, H, d, d))).astype(np.float32) if s0 else None
     if bwd:
         out["dO"] = round_to(rng.standard_normal((B, T, H, d)), dtype)

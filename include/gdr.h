@@ -40,7 +40,8 @@
  *       beta        [B, T, H]    fp32
  *       alpha       NONE: NULL; SCALAR: [B, T, H] fp32; CHANNEL: [B, T, H, dk]
  *                   fp32; every value in (0, 1] (the chunked kernels work with
- *                   log2(alpha); alpha == 0 is outside the domain)
+ *                   log2(alpha); alpha == 0 is outside the domain); logits
+ *                   with a prologue (gdr_prologue)
  *       S0, ST      [B, H, dk, dv] fp32
  *       h_clvr      [B, T, H*dv] in the input dtype
  *       clvr_scale  [H*dv] fp32
@@ -83,6 +84,24 @@ typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
  * v_t (CLVR) or the write error e_t (CLER-H). */
 typedef enum { GDR_ROUTE_VALUE = 0, GDR_ROUTE_ERROR = 1 } gdr_route;
 
+/* Fused prologue of the chunked calls (KDA blog sections 2.1 and 7.1: q and k
+ * are L2-normalised after their projections; the gates come out of sigmoids,
+ * the forget gate's logit biased to -3 so that it forgets ~5 % per token at
+ * initialisation).  With a prologue, q and k are passed unnormalised and beta
+ * and alpha as logits b and a; the operator uses
+ *     q_hat = q / max(|q|_2, 1e-6)   (per token and head; k likewise)
+ *     beta  = sigmoid(b)
+ *     alpha = sigmoid(a)                       GDR_PROLOGUE_ALPHA_SIGMOID
+ *     alpha = exp(-softplus(a)) = 1 - sigmoid(a)   GDR_PROLOGUE_ALPHA_FORGET
+ * and the backward returns dq, dk, dbeta, dalpha with respect to the raw
+ * q, k and the logits.  Any finite logit is in the domain.  The decode step
+ * takes activated inputs. */
+typedef enum {
+    GDR_PROLOGUE_NONE = 0,
+    GDR_PROLOGUE_ALPHA_SIGMOID = 1,
+    GDR_PROLOGUE_ALPHA_FORGET = 2
+} gdr_prologue;
+
 typedef struct {
     int64_t B, T, H, dk, dv; /* batch, tokens, heads, key and value widths */
     int32_t gate;            /* gdr_gate */
@@ -91,6 +110,7 @@ typedef struct {
     float scale;             /* o = scale * S^T q ; 1.0 is the pages' equation */
     int32_t chunk;           /* 0 selects the default (64); only 64 is supported */
     int32_t route;           /* gdr_route of the h_clvr epilogue; 0 (VALUE) when unused */
+    int32_t prologue;        /* gdr_prologue; 0 (NONE): q, k, beta, alpha used as passed */
 } gdr_desc;
 
 /* Bytes of device workspace the chunked calls need for `desc`.

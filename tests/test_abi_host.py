@@ -51,9 +51,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_desc_layout_matches_header():
-    # int64 x5, int32 x3, float, int32 x2 -> 64 bytes
-    assert ctypes.sizeof(_lib.Desc) == 64
+    # int64 x5, int32 x3, float, int32 x3 -> 68 bytes, padded to 72
+    assert ctypes.sizeof(_lib.Desc) == 72
     assert _lib.Desc.scale.offset == 52 and _lib.Desc.chunk.offset == 56 and _lib.Desc.route.offset == 60
+    assert _lib.Desc.prologue.offset == 64
 
 
 def test_status_strings_and_version(lib):
@@ -62,8 +63,8 @@ def test_status_strings_and_version(lib):
     assert lib.gdr_version() >= 100
 
 
-def desc(B=2, T=100, H=3, d=128, gate=2, in_dt=0, out_dt=1, scale=1.0, chunk=0, route=0):
-    return _lib.Desc(B, T, H, d, d, gate, in_dt, out_dt, scale, chunk, route)
+def desc(B=2, T=100, H=3, d=128, gate=2, in_dt=0, out_dt=1, scale=1.0, chunk=0, route=0, prologue=0):
+    return _lib.Desc(B, T, H, d, d, gate, in_dt, out_dt, scale, chunk, route, prologue)
 
 
 def test_workspace_size_formula(lib):
@@ -89,6 +90,12 @@ def test_workspace_size_formula(lib):
         cler_part = al(2 * 3 * 3 * d * 4)
         assert (lib.gdr_workspace_size(ctypes.byref(de), 1) - lib.gdr_workspace_size(ctypes.byref(dd), 1)
                 == al(nch * 64 * d * opb) + cler_part - clvr_part)
+        # the prologue keeps the activated beta and the reciprocal q and k row
+        # norms: one fp32 per token slot each, in both layouts
+        dp = desc(B=2, T=130, H=3, d=d, in_dt=in_dt, prologue=2)
+        for op in (0, 1):
+            assert (lib.gdr_workspace_size(ctypes.byref(dp), op) - lib.gdr_workspace_size(ctypes.byref(dd), op)
+                    == 3 * al(nch * 64 * 4))
     assert lib.gdr_workspace_size(ctypes.byref(desc(T=0)), 0) == 0
 
 
@@ -111,6 +118,8 @@ def test_forward_rejects_invalid_arguments(lib):
     assert fwd(lib, desc(chunk=32)) == UNSUPPORTED
     assert fwd(lib, desc(gate=3)) == INVALID
     assert fwd(lib, desc(route=2)) == INVALID
+    assert fwd(lib, desc(prologue=3)) == INVALID
+    assert fwd(lib, desc(prologue=-1)) == INVALID
     assert fwd(lib, desc(route=-1)) == INVALID
     assert fwd(lib, desc(in_dt=5)) == INVALID
     assert fwd(lib, desc(B=-1)) == INVALID
