@@ -297,6 +297,60 @@ def main():
         log("cler step %.3f ms; kernels %s" % (cler_ms, json.dumps(ck)))
         del ws_c
 
+    # ---------------- the same training step with the fused prologue ----------------
+    prologue = None
+    if do_bwd:
+        pinp = gdr_inputs.make(**dict(cfg, bwd=True, prologue="forget"))
+        pq = torch.from_numpy(pinp["q"]).to(dev).to(bf)
+        pk = torch.from_numpy(pinp["k"]).to(dev).to(bf)
+        pb = torch.from_numpy(pinp["beta"]).to(dev)
+        pa = torch.from_numpy(pinp["alpha"]).to(dev)
+        del pinp
+        nbp = gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf, backward=True, prologue="forget")
+        ws_p = torch.empty(nbp, dtype=torch.uint8, device=dev)
+
+        def pro_step():
+            gdr.forward(pq, pk, v, pb, pa, None, h=h, clvr_scale=lam, workspace=ws_p, output_final_state=True,
+                        save_for_backward=True, prologue="forget")
+            gdr.backward(pq, pk, v, pb, pa, None, dO, dh=h, clvr_scale=lam, want_dclvr_scale=True,
+                         saved_workspace=ws_p, prologue="forget")
+
+        def separate_pass():
+            # what the prologue replaces: a pass that normalises q, k and
+            # activates the gates before the operator (torch ops, for comparison)
+            qn = torch.nn.functional.normalize(pq.float(), dim=-1, eps=1e-6).to(bf)
+            kn = torch.nn.functional.normalize(pk.float(), dim=-1, eps=1e-6).to(bf)
+            return qn, kn, torch.sigmoid(pb), torch.sigmoid(-pa)
+
+        for _ in range(args.warmup):
+            pro_step()
+            separate_pass()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            pro_step()
+        e1.record()
+        torch.cuda.synchronize()
+        pro_ms = e0.elapsed_time(e1) / args.steps
+        e0.record()
+        for _ in range(args.steps):
+            separate_pass()
+        e1.record()
+        torch.cuda.synchronize()
+        sep_ms = e0.elapsed_time(e1) / args.steps
+        timer.begin()
+        for _ in range(args.steps):
+            pro_step()
+        torch.cuda.synchronize()
+        pk_t = {n: round(1e3 * ms / c, 2) for n, (c, ms) in timer.end().items()}
+        prologue = {"workload": "the same step with prologue=forget: raw q, k and gate logits, normalised and "
+                                "activated inside the kernels",
+                    "ms_per_step": round(pro_ms, 4), "tokens_per_s": round(tokens / (pro_ms * 1e-3), 1),
+                    "separate_pass_ms": round(sep_ms, 4), "kernels_avg_us": pk_t}
+        log("prologue step %.3f ms (separate torch pass it replaces: %.3f ms); kernels %s" % (
+            pro_ms, sep_ms, json.dumps(pk_t)))
+        del ws_p, pq, pk, pb, pa
+
     # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
     dc = gdr_inputs.DECODE_CONFIG
     nsets = 3
@@ -374,6 +428,7 @@ def main():
                     for n, kr in kernels.items()},
         "decode": decode,
         "cler": cler,
+        "prologue": prologue,
     }
     print(json.dumps(out), flush=True)
 

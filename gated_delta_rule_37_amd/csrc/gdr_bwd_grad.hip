@@ -69,7 +69,7 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
     }
 }
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32>
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
 __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64_t NC, float scale,
                                                          const void* __restrict__ k_, const void* __restrict__ v_,
                                                          const float* __restrict__ beta,
@@ -88,6 +88,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     __shared__ float s_gs[CHUNK];
     __shared__ float s_beta[CHUNK];
     __shared__ float s_db[CHUNK];
+    __shared__ float s_rk[PRO ? CHUNK : 1];  // prologue: reciprocal k row norms
 
     OpT* KT = reinterpret_cast<OpT*>(smem + L::KT);
     float* NTF = reinterpret_cast<float*>(smem + L::KT);                    // phase 3: N^T
@@ -192,9 +193,10 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
         const float bt = beta[tok];  // activated (the prologue's copy when it is on)
         s_beta[tid] = ok ? bt : 0.f;
+        if constexpr (PRO) s_rk[tid] = fabsf(ws.rk[tok]);  // prologue: k row norms (intra kernel)
         if constexpr (GATE == GATE_SCALAR) {
             const float at = alpha[tok];
-            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
+            float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -207,9 +209,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     for (int j = 0; j < RPP; ++j) {
         const bool ok = r0 + j < nvalid;
         kk[j] = ok ? kk[j] : 0.f;
-        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (pro ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
-        // prologue: k divided by its row norm (kept by the intra-chunk kernel)
-        if (pro && ok) kk[j] *= fabsf(ws.rk[(b * T + t0 + r0 + j) * H + h]);
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (PRO ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
     }
     if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
@@ -239,7 +239,11 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         for (int j = 0; j < RPP; ++j) G[j] = s_gs[r0 + j];
     }
 #pragma unroll
-    for (int j = 0; j < RPP; ++j) KT[(r0 + j) * LDR + cc] = from_f32<OpT>(kk[j] * exp2_fast(G[j]));
+    for (int j = 0; j < RPP; ++j) {
+        // prologue: k divided by its row norm
+        const float kn = PRO ? kk[j] * s_rk[r0 + j] : kk[j];
+        KT[(r0 + j) * LDR + cc] = from_f32<OpT>(kn * exp2_fast(G[j]));
+    }
     // T^T[i][r] = N[r][i] beta_i
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
         const int r = e / CHUNK, i = e % CHUNK;
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     __syncthreads();
     if (tid < nvalid) {
         float db = s_db[tid];
-        if (pro) db *= s_beta[tid] * (1.f - s_beta[tid]);  // prologue: beta = sigmoid(logit)
+        if constexpr (PRO) db *= s_beta[tid] * (1.f - s_beta[tid]);  // prologue: beta = sigmoid(logit)
         dbeta[(b * T + t0 + tid) * H + h] = db;
     }
 }
@@ -497,8 +501,12 @@ static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, flo
                                     int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T,
-                       H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
+    if (pro)
+        hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
+    else
+        hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
     return hipGetLastError();
 }
 
@@ -580,7 +588,7 @@ struct GGateLayout {
     static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
 };
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32>
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
 __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int64_t NC,
                                                           const void* __restrict__ q_, const void* __restrict__ k_,
                                                           const float* __restrict__ alpha, void* __restrict__ dq_,
@@ -598,6 +606,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     __shared__ float s_red[NW];
     __shared__ float s_row[CHUNK];
     __shared__ float s_nrm[NW * 2 * RPP];  // prologue: row-dot partials
+    __shared__ float s_rq[PRO ? CHUNK : 1], s_rk[PRO ? CHUNK : 1];  // prologue: reciprocal row norms
 
     OpT* dAs = reinterpret_cast<OpT*>(smem + L::DA);
     OpT* dPs = reinterpret_cast<OpT*>(smem + L::DP);
@@ -642,7 +651,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         if (tid < CHUNK) {
             const bool ok = tid < nvalid;
             const float at = alpha[(b * T + t0 + (ok ? tid : nvalid - 1)) * H + h];
-            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
+            float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
             s_row[tid] = ok ? at : 1.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -660,15 +669,16 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         if constexpr (GATE == GATE_CHANNEL) {
             // prologue: al stays the logit (the final dalpha needs it)
             al[j] = ok ? al[j] : 1.f;
-            G[j] = ok ? (pro ? log2_alpha_logit(al[j], pro) : log2_fast(al[j])) : 0.f;
+            G[j] = ok ? (PRO ? log2_alpha_logit(al[j], pro) : log2_fast(al[j])) : 0.f;
         } else {
             G[j] = 0.f;
         }
-        if (pro && ok) {
-            // prologue: q and k divided by their row norms
-            const int64_t tok = (b * T + t0 + r0 + j) * H + h;
-            qq[j] *= fabsf(ws.rq[tok]);
-            kk[j] *= fabsf(ws.rk[tok]);
+    }
+    if constexpr (PRO) {
+        if (tid < CHUNK) {
+            const int64_t tok = (b * T + t0 + (tid < nvalid ? tid : nvalid - 1)) * H + h;
+            s_rq[tid] = ws.rq[tok];
+            s_rk[tid] = ws.rk[tok];
         }
     }
     if constexpr (GATE == GATE_CHANNEL) {
@@ -698,6 +708,14 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     }
     for (int e = tid; e < D * LDC; e += NT) KhT[e] = from_f32<OpT>(0.f);
     __syncthreads();
+    if constexpr (PRO) {
+        // prologue: q and k divided by their row norms
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            qq[j] *= fabsf(s_rq[r0 + j]);
+            kk[j] *= fabsf(s_rk[r0 + j]);
+        }
+    }
 
     float carry = 0.f, glast = 0.f;
     if constexpr (GATE == GATE_CHANNEL) {
@@ -874,41 +892,54 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
             pkt[j] = gKt[(r0 + j) * D + cc];
             pkb[j] = gKb[(r0 + j) * D + cc];
         }
-        float dqa[RPP], dka[RPP];
+        if constexpr (!PRO) {
 #pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
-            const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
-            dqa[j] = gq + Aq[j];
-            dka[j] = gkt + gkb + Prow[j] + Ccol[j];
-            dG[j] = qq[j] * dqa[j] + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
-            lastsum += kk[j] * gkb;
-        }
-        if (pro) {
+            for (int j = 0; j < RPP; ++j) {
+                const int r = r0 + j;
+                const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
+                const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
+                const float dqv = gq + Aq[j];
+                const float dkv = gkt + gkb + Prow[j] + Ccol[j];
+                dG[j] = qq[j] * dqv + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
+                lastsum += kk[j] * gkb;
+                if (r < nvalid) {
+                    dq[base + r * tokstride + cc] = from_f32<OutT>(dqv);
+                    dk[base + r * tokstride + cc] = from_f32<OutT>(dkv);
+                }
+            }
+        } else {
             // prologue: back through x / |x|: (dx_hat - x_hat (x_hat . dx_hat)) / |x|
-            // (only dx_hat / eps where the norm was clamped)
+            // (only dx_hat / eps where the norm was clamped).  dq_hat and dk_hat
+            // wait in LDS (the product buffers are free now) while the row dots
+            // are summed, which keeps them out of the register file.
+            float* sQ = SCf;                                     // [64][D] fp32
+            float* sK = reinterpret_cast<float*>(smem + L::DA);  // [64][D] fp32 over dA .. dP^T
+            static_assert(CHUNK * D * 4 <= L::QQT - L::DA, "dk_hat must fit over dA .. dP^T");
             float dot[2 * RPP];
 #pragma unroll
             for (int j = 0; j < RPP; ++j) {
-                dot[j] = qq[j] * dqa[j];
-                dot[RPP + j] = kk[j] * dka[j];
+                const float E = exp2_fast(G[j]), Eb = exp2_fast(glast - G[j]);
+                const float gq = pq[j] * E, gkt = pkt[j] * E, gkb = pkb[j] * Eb;
+                const float dqv = gq + Aq[j];
+                const float dkv = gkt + gkb + Prow[j] + Ccol[j];
+                dG[j] = qq[j] * dqv + kk[j] * (gkt - gkb + Prow[j] - Ccol[j]);
+                lastsum += kk[j] * gkb;
+                sQ[(r0 + j) * D + cc] = dqv;
+                sK[(r0 + j) * D + cc] = dkv;
+                dot[j] = qq[j] * dqv;
+                dot[RPP + j] = kk[j] * dkv;
             }
-            part_row_sums<D, 2 * RPP>(dot, s_nrm);
+            part_row_sums32<D>(dot, s_nrm);
 #pragma unroll
             for (int j = 0; j < RPP; ++j) {
-                if (r0 + j >= nvalid) continue;
-                const int64_t tok = (b * T + t0 + r0 + j) * H + h;
-                const float rq = ws.rq[tok], rk = ws.rk[tok];
-                dqa[j] = (rq > 0.f) ? (dqa[j] - qq[j] * dot[j]) * rq : -dqa[j] * rq;
-                dka[j] = (rk > 0.f) ? (dka[j] - kk[j] * dot[RPP + j]) * rk : -dka[j] * rk;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            const int r = r0 + j;
-            if (r < nvalid) {
-                dq[base + r * tokstride + cc] = from_f32<OutT>(dqa[j]);
-                dk[base + r * tokstride + cc] = from_f32<OutT>(dka[j]);
+                const int r = r0 + j;
+                if (r >= nvalid) continue;
+                const float rq = s_rq[r], rk = s_rk[r];
+                const float dqv = sQ[r * D + cc], dkv = sK[r * D + cc];
+                const float gq = (rq > 0.f) ? (dqv - qq[j] * dot[j]) * rq : -dqv * rq;
+                const float gk = (rk > 0.f) ? (dkv - kk[j] * dot[RPP + j]) * rk : -dkv * rk;
+                dq[base + r * tokstride + cc] = from_f32<OutT>(gq);
+                dk[base + r * tokstride + cc] = from_f32<OutT>(gk);
             }
         }
     }
@@ -945,7 +976,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
             for (int j = 0; j < RPP; ++j) {
                 const int r = r0 + j;
                 if (r < nvalid)
-                    dalpha[base + r * tokstride + cc] = pro ? dlogit_from_dlog(dg[j], al[j], pro) : dg[j] / al[j];
+                    dalpha[base + r * tokstride + cc] = PRO ? dlogit_from_dlog(dg[j], al[j], pro) : dg[j] / al[j];
             }
         } else {
             // scalar gate: sum over channels
@@ -962,7 +993,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
             __syncthreads();
             if (tid < nvalid) {
                 float a1 = alpha[(b * T + t0 + tid) * H + h];
-                dalpha[(b * T + t0 + tid) * H + h] = pro ? dlogit_from_dlog(s_row[tid], a1, pro) : s_row[tid] / a1;
+                dalpha[(b * T + t0 + tid) * H + h] = PRO ? dlogit_from_dlog(s_row[tid], a1, pro) : s_row[tid] / a1;
             }
         }
     }
@@ -974,8 +1005,12 @@ static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, co
                                      int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nblk), dim3(4 * D), 0, stream,
-                       T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
+    if (pro)
+        hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
+    else
+        hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
+                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
     return hipGetLastError();
 }
 

@@ -221,60 +221,79 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // ---------------------------------------------------------------------------
 constexpr float NORM_EPS = 1e-6f;
 
-__device__ __forceinline__ float sigmoid_acc(float x) {
-    if (x >= 0.f) return 1.f / (1.f + expf(-x));
-    const float e = expf(x);
-    return e / (1.f + e);
+// sigmoid with the hardware exp2; 1 - sigmoid(x) is sigmoid(-x), never formed
+// by subtraction
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * 1.4426950408889634f));
 }
 
 // s = +1 (PRO 1) or -1 (PRO 2): alpha = sigmoid(s a)
 __device__ __forceinline__ float pro_sign(int pro) { return pro == 1 ? 1.f : -1.f; }
 
-// log2(alpha) from the logit, without forming alpha: -softplus(-s a) / ln 2
+// log2(alpha) from the logit without forming alpha:
+//   log2 sigmoid(s a) = -log2(1 + 2^(-s a log2 e))
+//                     = -(max(y, 0) + log2(1 + 2^-|y|)),  y = -s a log2 e.
+// Where 2^-|y| is below fp32's half ulp of 1 the second term is lost: an
+// absolute error below 2^-24 in log2(alpha), i.e. alpha within an ulp of 1.
 __device__ __forceinline__ float log2_alpha_logit(float a, int pro) {
-    const float y = -pro_sign(pro) * a;
-    const float sp = fmaxf(y, 0.f) + log1pf(expf(-fabsf(y)));
-    return -sp * 1.4426950408889634f;
+    const float y = -pro_sign(pro) * a * 1.4426950408889634f;
+    return -(fmaxf(y, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(y))));
 }
 
 // d alpha-logit from the gradient with respect to ln(alpha):
 // d ln(sigmoid(s a)) / da = s (1 - sigmoid(s a)) = s sigmoid(-s a)
 __device__ __forceinline__ float dlogit_from_dlog(float dlog, float a, int pro) {
     const float s = pro_sign(pro);
-    return dlog * s * sigmoid_acc(-s * a);
+    return dlog * s * sigmoid_fast(-s * a);
 }
 
 // Reciprocal norm of a row, with the clamped case flagged by the sign (the
 // gradient then has no projection term).
 __device__ __forceinline__ float recip_norm(float sumsq) {
-    const float n = sqrtf(sumsq);
-    return n > NORM_EPS ? 1.f / n : -1.f / NORM_EPS;
+    return sumsq > NORM_EPS * NORM_EPS ? __builtin_amdgcn_rsqf(sumsq) : -1.f / NORM_EPS;
 }
 
-// Sums x[j] over the D threads of this thread's part (threads part*D ..
-// part*D + D - 1, D / 64 whole waves) for every j, in a fixed order; every
-// thread of the part receives the totals.  red: LDS scratch of
-// (threads / 64) * N floats.  Called by every thread of the workgroup.
-template <int D, int N>
-__device__ __forceinline__ void part_row_sums(float (&x)[N], float* red) {
-    const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+// Sums x[j] (32 values per thread) over the D threads of this thread's part
+// (threads part*D .. part*D + D - 1, D / 64 whole waves) for every j; every
+// thread of the part receives the 32 totals.  A butterfly that halves the
+// values each step (reduce-scatter: 16 + 8 + 4 + 2 + 1 + 1 exchanges instead of
+// 32 * 6) leaves lane l with the wave's sum of value (l >> 1) & 31; the sums
+// go through LDS.  The order of additions is fixed.  red: LDS scratch of
+// (threads / 64) * 32 floats.  Called by every thread of the workgroup.
+// One butterfly step: lanes with bit M keep the upper N/2 values, their
+// partners the lower ones; each receives the other half from its partner.
+template <int N, int M>
+__device__ __forceinline__ void butterfly_step(float (&x)[32], int lane) {
+    const bool up = (lane & M) != 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) x[j] += __shfl_xor(x[j], off);
+    for (int i = 0; i < N / 2; ++i) {
+        const float send = up ? x[i] : x[i + N / 2];
+        const float keep = up ? x[i + N / 2] : x[i];
+        x[i] = keep + __shfl_xor(send, M);
     }
-    if constexpr (D > WAVE) {
-        static_assert(D == 2 * WAVE, "two waves per part");
-        if (lane == 0) {
+}
+
+template <int D>
+__device__ __forceinline__ void part_row_sums32(float (&x)[32], float* red) {
+    const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+    butterfly_step<32, 32>(x, lane);
+    butterfly_step<16, 16>(x, lane);
+    butterfly_step<8, 8>(x, lane);
+    butterfly_step<4, 4>(x, lane);
+    butterfly_step<2, 2>(x, lane);
+    x[0] += __shfl_xor(x[0], 1);
+    if ((lane & 1) == 0) red[wid * 32 + ((lane >> 1) & 31)] = x[0];
+    __syncthreads();
+    if constexpr (D == WAVE) {
 #pragma unroll
-            for (int j = 0; j < N; ++j) red[wid * N + j] = x[j];
-        }
-        __syncthreads();
+        for (int j = 0; j < 32; ++j) x[j] = red[wid * 32 + j];
+    } else {
+        static_assert(D == 2 * WAVE, "two waves per part");
         const int w0 = wid & ~1;
 #pragma unroll
-        for (int j = 0; j < N; ++j) x[j] = red[w0 * N + j] + red[(w0 + 1) * N + j];
-        __syncthreads();
+        for (int j = 0; j < 32; ++j) x[j] = red[w0 * 32 + j] + red[(w0 + 1) * 32 + j];
     }
+    __syncthreads();
 }
 
 }  // namespace gdr

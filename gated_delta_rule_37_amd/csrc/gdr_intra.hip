@@ -90,7 +90,8 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // MODE 0: the forward's operands (and CLVR); 1: the operands of the recomputing
 // backward; 2: both, so that a training forward leaves everything its backward needs.
-template <int D, int GATE, bool IN_F32, int MODE>
+// PRO: the prologue (pro = 1 or 2 selects the alpha activation).
+template <int D, int GATE, bool IN_F32, int MODE, bool PRO>
 __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t NC,
                                                       const void* __restrict__ q_,
                                                       const void* __restrict__ k_,
@@ -170,16 +171,16 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         const bool ok = tid < nvalid;
         const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
         float bt = beta[tok];
-        if (pro) {
+        if constexpr (PRO) {
             // prologue: beta arrives as a logit; the activated value is kept for
             // the later kernels
-            bt = sigmoid_acc(bt);
+            bt = sigmoid_fast(bt);
             if (ok) ws.Bact[tok] = bt;
         }
         s_beta[tid] = ok ? bt : 0.f;
         if constexpr (GATE == GATE_SCALAR) {
             const float at = alpha[tok];
-            float g = ok ? (pro ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
+            float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -194,18 +195,19 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         kk[j] = ok ? kk[j] : 0.f;
         qq[j] = ok ? qq[j] : 0.f;
         vv[j] = ok ? vv[j] : 0.f;
-        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (pro ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
+        if constexpr (GATE == GATE_CHANNEL) G[j] = ok ? (PRO ? log2_alpha_logit(G[j], pro) : log2_fast(G[j])) : 0.f;
     }
-    if (pro) {
+    if constexpr (PRO) {
         // prologue: q and k rows divided by their L2 norms (sums over the D
         // threads of this part); the backward kernels get the reciprocal norms
+        static_assert(2 * RPP == 32, "32 row sums per thread");
         float nrm[2 * RPP];
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             nrm[j] = qq[j] * qq[j];
             nrm[RPP + j] = kk[j] * kk[j];
         }
-        part_row_sums<D, 2 * RPP>(nrm, s_nrm);
+        part_row_sums32<D>(nrm, s_nrm);
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const float rq = recip_norm(nrm[j]), rk = recip_norm(nrm[RPP + j]);
@@ -658,15 +660,19 @@ static hipError_t launch_intra_t(int mode, int64_t B, int64_t T, int H, int64_t 
                                  const ChunkWs& ws, int pro, hipStream_t stream) {
     const int64_t nblk = B * H * NC;
     if (nblk == 0) return hipSuccess;
-    if (mode == 1)
-        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 1>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
-    else if (mode == 2)
-        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 2>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
-    else
-        hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, 0>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro);
+#define GDR_INTRA(M, P)                                                                                \
+    hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, M, P>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T, H, \
+                       NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro)
+    if (pro) {
+        if (mode == 1) GDR_INTRA(1, true);
+        else if (mode == 2) GDR_INTRA(2, true);
+        else GDR_INTRA(0, true);
+    } else {
+        if (mode == 1) GDR_INTRA(1, false);
+        else if (mode == 2) GDR_INTRA(2, false);
+        else GDR_INTRA(0, false);
+    }
+#undef GDR_INTRA
     return hipGetLastError();
 }
 
