@@ -269,3 +269,41 @@ def prologue_backward(q, k, beta_logit, alpha_logit, mode, g):
         al = _sigmoid(s * a)
         out["dalpha"] = g["dalpha"] * s * al * (1.0 - al)
     return out
+
+
+# --------------------------------------------------------------------------
+# Output gate: y = sigmoid(g) * RMSNorm(o) per head (KDA blog section 4.1)
+# --------------------------------------------------------------------------
+# The page's best output gate is o_t = W_o(Sigmoid(W_up W_down x_t) * RMSNorm(KDA(...))).
+# The projections are GEMMs outside the operator; the elementwise part takes the
+# gate pre-activation g (the low-rank projection's output) from the caller.
+# RMSNorm is taken per head over dv with a weight w [H*dv]:
+#   y = sigmoid(g) * w * o / sqrt(mean_j o_j^2 + GATE_EPS)
+GATE_EPS = 1e-6
+
+
+def output_gate_forward(o, g, w=None):
+    """o, g [B,T,H,dv]; w [H*dv] or None (ones).  Returns (y, rstd [B,T,H])."""
+    o = np.asarray(o, np.float64)
+    g = np.asarray(g, np.float64)
+    B, T, H, dv = o.shape
+    w = np.ones((H, dv)) if w is None else np.asarray(w, np.float64).reshape(H, dv)
+    rstd = 1.0 / np.sqrt((o * o).mean(-1) + GATE_EPS)
+    return _sigmoid(g) * w * o * rstd[..., None], rstd
+
+
+def output_gate_backward(o, g, w, dy):
+    """Returns (do, dg, dw [H*dv]) for :func:`output_gate_forward`."""
+    o = np.asarray(o, np.float64)
+    g = np.asarray(g, np.float64)
+    dy = np.asarray(dy, np.float64)
+    B, T, H, dv = o.shape
+    w = np.ones((H, dv)) if w is None else np.asarray(w, np.float64).reshape(H, dv)
+    rstd = 1.0 / np.sqrt((o * o).mean(-1) + GATE_EPS)
+    n = o * rstd[..., None]
+    s = _sigmoid(g)
+    dn = dy * s * w
+    do = rstd[..., None] * (dn - n * (dn * n).mean(-1, keepdims=True))
+    dg = dy * w * n * s * (1.0 - s)
+    dw = (dy * s * n).sum((0, 1)).reshape(H * dv)
+    return do, dg, dw

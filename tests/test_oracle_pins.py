@@ -663,3 +663,52 @@ def test_prologue_backward_matches_central_differences(mode):
             num[mi] = (lp - lm) / (2 * eps)
         err = np.abs(num - g[name]).max() / max(1.0, np.abs(num).max())
         assert err < 1e-7, (name, err)
+
+
+# --------------------------------------------------------------------------
+# output gate: sigmoid(g) * RMSNorm(o) per head
+# --------------------------------------------------------------------------
+
+
+def test_output_gate_normalises_rows_and_gates_them():
+    """With w = 1 and a saturated gate the rows come out with unit RMS; g = 0
+    halves them; positive rescaling of o cancels; w scales channel by channel."""
+    r = np.random.default_rng(70)
+    o = r.standard_normal((2, 3, 2, 8)) * r.uniform(0.5, 20, (2, 3, 2, 1))
+    y, _ = oracle.output_gate_forward(o, np.full(o.shape, 40.0))
+    m = (o * o).mean(-1)
+    assert np.abs(np.sqrt((y * y).mean(-1)) - np.sqrt(m / (m + oracle.GATE_EPS))).max() < 1e-13
+    y0, _ = oracle.output_gate_forward(o, np.zeros(o.shape))
+    assert np.abs(2 * y0 - y).max() < 1e-12
+    g = r.standard_normal(o.shape)
+    a, _ = oracle.output_gate_forward(o, g)
+    b, _ = oracle.output_gate_forward(7.5 * o, g)
+    assert np.abs(a - b).max() < 1e-9
+    w = r.standard_normal(16)
+    c, _ = oracle.output_gate_forward(o, g, w)
+    assert np.abs(c - a * w.reshape(2, 8)).max() < 1e-12
+
+
+def test_output_gate_backward_matches_central_differences():
+    r = np.random.default_rng(71)
+    o = r.standard_normal((1, 3, 2, 5))
+    g = r.standard_normal(o.shape)
+    w = r.standard_normal(10)
+    dy = r.standard_normal(o.shape)
+    do, dg, dw = oracle.output_gate_backward(o, g, w, dy)
+
+    def loss(o_, g_, w_):
+        return float((oracle.output_gate_forward(o_, g_, w_)[0] * dy).sum())
+
+    eps = 1e-6
+    for x, ref in ((o, do), (g, dg), (w, dw)):
+        num = np.zeros_like(x)
+        for mi in np.ndindex(x.shape):
+            old = x[mi]
+            x[mi] = old + eps
+            lp = loss(o, g, w)
+            x[mi] = old - eps
+            lm = loss(o, g, w)
+            x[mi] = old
+            num[mi] = (lp - lm) / (2 * eps)
+        assert np.abs(num - ref).max() / max(1.0, np.abs(num).max()) < 1e-8
