@@ -683,7 +683,8 @@ def test_output_gate_normalises_rows_and_gates_them():
     g = r.standard_normal(o.shape)
     a, _ = oracle.output_gate_forward(o, g)
     b, _ = oracle.output_gate_forward(7.5 * o, g)
-    assert np.abs(a - b).max() < 1e-9
+    ratio = np.sqrt((m + oracle.GATE_EPS) / (m + oracle.GATE_EPS / 7.5 ** 2))[..., None]
+    assert np.abs(a * ratio - b).max() < 1e-13
     w = r.standard_normal(16)
     c, _ = oracle.output_gate_forward(o, g, w)
     assert np.abs(c - a * w.reshape(2, 8)).max() < 1e-12
