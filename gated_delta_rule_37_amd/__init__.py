@@ -16,10 +16,10 @@ from __future__ import annotations
 
 from ._lib import (GATE_CHANNEL, GATE_NONE, GATE_SCALAR, PROLOGUE_ALPHA_FORGET, PROLOGUE_ALPHA_SIGMOID,
                    PROLOGUE_NONE, ROUTE_ERROR, ROUTE_VALUE, GdrError, backward, decode_step, forward,
-                   library_path, load_library, workspace_size)
+                   library_path, load_library, output_gate, output_gate_backward, workspace_size)
 
 __all__ = [
     "GATE_NONE", "GATE_SCALAR", "GATE_CHANNEL", "ROUTE_VALUE", "ROUTE_ERROR", "PROLOGUE_NONE",
     "PROLOGUE_ALPHA_SIGMOID", "PROLOGUE_ALPHA_FORGET", "GdrError", "forward", "backward",
-    "decode_step", "workspace_size", "load_library", "library_path",
+    "decode_step", "output_gate", "output_gate_backward", "workspace_size", "load_library", "library_path",
 ]

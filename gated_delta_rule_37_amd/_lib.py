@@ -69,6 +69,12 @@ def load_library():
         lib.gdr_backward_saved.restype = ctypes.c_int
         lib.gdr_decode_step.argtypes = [I64] * 4 + [I32] * 3 + [F32] + [P] * 7 + [P]
         lib.gdr_decode_step.restype = ctypes.c_int
+        lib.gdr_output_gate_forward.argtypes = [D] + [P] * 4 + [P]
+        lib.gdr_output_gate_forward.restype = ctypes.c_int
+        lib.gdr_output_gate_workspace_size.argtypes = [D]
+        lib.gdr_output_gate_workspace_size.restype = SZ
+        lib.gdr_output_gate_backward.argtypes = [D] + [P] * 8 + [SZ, P]
+        lib.gdr_output_gate_backward.restype = ctypes.c_int
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_last_error.argtypes = []
@@ -283,3 +289,46 @@ def decode_step(q, k, v, beta, alpha, S, *, scale=1.0, out_dtype=None, out=None)
                                _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
                                _stream(q.device)))
     return o
+
+
+def _gate_desc(o, g):
+    if o.dim() != 4:
+        raise ValueError("o must be [B, T, H, dv]")
+    B, T, H, dv = o.shape
+    return Desc(B, T, H, dv, dv, GATE_NONE, _dt(g.dtype), _dt(o.dtype), 1.0, 0, ROUTE_VALUE, PROLOGUE_NONE)
+
+
+def output_gate(o, g, w=None, *, out=None):
+    """Output-gate epilogue ``y = sigmoid(g) * w * RMSNorm(o)`` per head (KDA
+    blog 4.1).  o [B,T,H,dv] (bf16 or fp32), g of o's shape (bf16 or fp32),
+    w [H*dv] fp32 or None.  ``out`` may be ``o`` itself."""
+    _need(o, "o")
+    _need(g, "g", None, tuple(o.shape))
+    B, T, H, dv = o.shape
+    _need(w, "w", torch.float32, (H * dv,))
+    y = out if out is not None else torch.empty_like(o)
+    _need(y, "out", o.dtype, tuple(o.shape))
+    lib = load_library()
+    desc = _gate_desc(o, g)
+    _check(lib.gdr_output_gate_forward(ctypes.byref(desc), _ptr(o), _ptr(g), _ptr(w), _ptr(y), _stream(o.device)))
+    return y
+
+
+def output_gate_backward(o, g, w, dy, *, want_dw=True):
+    """Returns ``(dO, dg, dw)`` for :func:`output_gate`; dO and dg have g's
+    dtype (dO is what :func:`backward` takes), dw is None unless asked."""
+    _need(o, "o")
+    _need(g, "g", None, tuple(o.shape))
+    _need(dy, "dy", o.dtype, tuple(o.shape))
+    B, T, H, dv = o.shape
+    _need(w, "w", torch.float32, (H * dv,))
+    lib = load_library()
+    desc = _gate_desc(o, g)
+    dO = torch.empty_like(g)
+    dg = torch.empty_like(g)
+    dw = torch.empty((H * dv,), dtype=torch.float32, device=o.device) if want_dw else None
+    need = lib.gdr_output_gate_workspace_size(ctypes.byref(desc)) if want_dw else 0
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device) if want_dw else None
+    _check(lib.gdr_output_gate_backward(ctypes.byref(desc), _ptr(o), _ptr(g), _ptr(w), _ptr(dy), _ptr(dO),
+                                        _ptr(dg), _ptr(dw), _ptr(ws), need, _stream(o.device)))
+    return dO, dg, dw

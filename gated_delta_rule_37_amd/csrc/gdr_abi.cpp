@@ -477,4 +477,82 @@ gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t
     return GDR_OK;
 }
 
+// Output gate: one row of dv channels per token and head
+static gdr_status gate_common(const gdr_desc* desc, int64_t* BT) {
+    gdr_status st = check_desc(desc, nullptr);
+    if (st != GDR_OK) return st;
+    *BT = desc->B * desc->T;
+    if (*BT * desc->H > 2147483647LL * 64) return fail(GDR_ERR_INVALID_ARG, "tensor too large");
+    return GDR_OK;
+}
+
+gdr_status gdr_output_gate_forward(const gdr_desc* desc, const void* o, const void* g, const float* w, void* y,
+                                   void* stream) {
+    int64_t BT = 0;
+    gdr_status st = gate_common(desc, &BT);
+    if (st != GDR_OK) return st;
+    const int64_t H = desc->H, D = desc->dv;
+    if (BT * H == 0) return GDR_OK;
+    if (!o || !g || !y) return fail(GDR_ERR_INVALID_ARG, "o, g and y are required");
+    const void* ptrs[] = {o, g, w, y};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t n = size_t(BT) * H * D;
+    const size_t ob = dtype_bytes(desc->out_dtype), ib = dtype_bytes(desc->in_dtype);
+    if (overlap(y, n * ob, g, n * ib) || overlap(y, n * ob, w, size_t(H) * D * 4))
+        return fail(GDR_ERR_INVALID_ARG, "y overlaps g or w");
+    if (y != o && overlap(y, n * ob, o, n * ob))
+        return fail(GDR_ERR_INVALID_ARG, "y partially overlaps o (it may only be o itself)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    gdr::prof_before(s);
+    hipError_t e = gdr::launch_gate(false, int(D), desc->in_dtype == GDR_FP32, desc->out_dtype == GDR_FP32, BT, int(H),
+                                    o, g, w, y, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+    gdr::prof_after("gate_fwd", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output-gate launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+size_t gdr_output_gate_workspace_size(const gdr_desc* desc) {
+    int64_t BT = 0;
+    if (gate_common(desc, &BT) != GDR_OK) return 0;
+    return align_up(size_t(gdr::gate_segments(BT)) * size_t(desc->H) * size_t(desc->dv) * 4);
+}
+
+gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const void* g, const float* w,
+                                    const void* dy, void* dO, void* dg, float* dw, void* ws, size_t ws_bytes,
+                                    void* stream) {
+    int64_t BT = 0;
+    gdr_status st = gate_common(desc, &BT);
+    if (st != GDR_OK) return st;
+    const int64_t H = desc->H, D = desc->dv;
+    if (BT * H == 0) return GDR_OK;
+    if (!o || !g || !dy || !dO || !dg) return fail(GDR_ERR_INVALID_ARG, "o, g, dy, dO and dg are required");
+    const void* ptrs[] = {o, g, w, dy, dO, dg, dw, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t n = size_t(BT) * H * D;
+    const size_t ob = dtype_bytes(desc->out_dtype), ib = dtype_bytes(desc->in_dtype);
+    const size_t need = dw ? gdr_output_gate_workspace_size(desc) : 0;
+    if (dw && (ws_bytes < need || !ws))
+        return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{o, n * ob}, {g, n * ib}, {w, size_t(H) * D * 4}, {dy, n * ob}},
+      outs[] = {{dO, n * ib}, {dg, n * ib}, {dw, size_t(H) * D * 4}, {dw ? ws : nullptr, need}};
+    for (auto& o1 : outs) {
+        for (auto& in : ins)
+            if (overlap(o1.p, o1.n, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "an output overlaps an input");
+        for (auto& o2 : outs)
+            if (&o1 != &o2 && overlap(o1.p, o1.n, o2.p, o2.n)) return fail(GDR_ERR_INVALID_ARG, "two outputs overlap");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    gdr::prof_before(s);
+    hipError_t e = gdr::launch_gate(true, int(D), desc->in_dtype == GDR_FP32, desc->out_dtype == GDR_FP32, BT, int(H),
+                                    o, g, w, nullptr, dy, dO, dg, dw, static_cast<float*>(ws), s);
+    gdr::prof_after("gate_bwd", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output-gate launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
 }  // extern "C"

@@ -23,61 +23,6 @@ __device__ __forceinline__ void frag_piece(int p, int& pos, int& j) {
     j = 32 * (f % (D / 32)) + 8 * (l >> 4);
 }
 
-// Eight consecutive values (16-byte aligned) converted to / from fp32.
-template <typename T>
-__device__ __forceinline__ void load8f(const T* p, float (&x)[8]) {
-    if constexpr (sizeof(T) == 2) {
-        const uint4 r = *reinterpret_cast<const uint4*>(p);
-        const T* v = reinterpret_cast<const T*>(&r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = to_f32(v[e]);
-    } else {
-        const float4v a = reinterpret_cast<const float4v*>(p)[0];
-        const float4v b = reinterpret_cast<const float4v*>(p)[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = a[e];
-            x[4 + e] = b[e];
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void store8f(T* p, const float (&x)[8]) {
-    if constexpr (sizeof(T) == 2) {
-        uint4 r;
-        T* v = reinterpret_cast<T*>(&r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(x[e]);
-        *reinterpret_cast<uint4*>(p) = r;
-    } else {
-        float4v a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = x[e];
-            b[e] = x[4 + e];
-        }
-        reinterpret_cast<float4v*>(p)[0] = a;
-        reinterpret_cast<float4v*>(p)[1] = b;
-    }
-}
-
-// lam[c..c+7], or ones when lam is NULL (the unit scale)
-__device__ __forceinline__ void load_lam8(const float* lam, int64_t c, float (&x)[8]) {
-    if (lam) {
-        const float4v a = *reinterpret_cast<const float4v*>(lam + c);
-        const float4v b = *reinterpret_cast<const float4v*>(lam + c + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = a[e];
-            x[4 + e] = b[e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 1.f;
-    }
-}
-
 // h[0..7] += lam[0..7] * u[0..7] / beta for one piece of a hidden row.
 template <typename InT>
 __device__ __forceinline__ void cler_add8(InT* hrow, const float (&u)[8], const float (&lm)[8], float beta) {

@@ -207,6 +207,61 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 
+// Eight consecutive values (16-byte aligned) converted to / from fp32.
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        const T* v = reinterpret_cast<const T*>(&r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = to_f32(v[e]);
+    } else {
+        const float4v a = reinterpret_cast<const float4v*>(p)[0];
+        const float4v b = reinterpret_cast<const float4v*>(p)[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8f(T* p, const float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        uint4 r;
+        T* v = reinterpret_cast<T*>(&r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(x[e]);
+        *reinterpret_cast<uint4*>(p) = r;
+    } else {
+        float4v a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = x[e];
+            b[e] = x[4 + e];
+        }
+        reinterpret_cast<float4v*>(p)[0] = a;
+        reinterpret_cast<float4v*>(p)[1] = b;
+    }
+}
+
+// lam[c..c+7], or ones when lam is NULL (the unit scale)
+__device__ __forceinline__ void load_lam8(const float* lam, int64_t c, float (&x)[8]) {
+    if (lam) {
+        const float4v a = *reinterpret_cast<const float4v*>(lam + c);
+        const float4v b = *reinterpret_cast<const float4v*>(lam + c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 1.f;
+    }
+}
+
 // Fast base-2 exponent and logarithm (v_exp_f32 / v_log_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }

@@ -100,4 +100,11 @@ hipError_t launch_cler_post(int D, bool in_f32, int64_t B, int64_t T, int H, int
                             const float* beta, const float* lam, const void* dh, float* dlam, float* partial,
                             hipStream_t stream);
 
+// Output-gate epilogue y = sigmoid(g) * w * RMSNorm(o) per head (and its
+// backward, with dw reduced from one partial row per token range).
+int64_t gate_segments(int64_t BT);
+hipError_t launch_gate(bool bwd, int D, bool in_f32, bool out_f32, int64_t BT, int H, const void* o, const void* g,
+                       const float* w, void* y, const void* dy, void* dO, void* dg, float* dw, float* partial,
+                       hipStream_t stream);
+
 }  // namespace gdr

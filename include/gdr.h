@@ -210,6 +210,32 @@ gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t
                            const void* k, const void* v, const float* beta,
                            const float* alpha, float* S, void* o, void* stream);
 
+/* Output-gate epilogue, the elementwise tail of the gated output of KDA blog
+ * section 4.1 (o_t = W_o(Sigmoid(W_up W_down x_t) * RMSNorm(KDA(...)))); the
+ * projections are GEMMs outside this library and g is the caller's low-rank
+ * projection output.  Per token and head:
+ *     y = sigmoid(g) * w * o / sqrt(mean_j o_j^2 + 1e-6)      (j over dv)
+ *   o, y      [B,T,H,dv] in out_dtype (the operator's output); y may be o itself
+ *   g         [B,T,H,dv] in in_dtype
+ *   w         [H*dv] fp32 norm weight, NULL = ones
+ * Only B, T, H, dv, in_dtype and out_dtype of desc are used (dk must equal dv).
+ * No workspace. */
+gdr_status gdr_output_gate_forward(const gdr_desc* desc, const void* o, const void* g, const float* w,
+                                   void* y, void* stream);
+
+/* Bytes of workspace gdr_output_gate_backward needs (the partial sums of dw). */
+size_t gdr_output_gate_workspace_size(const gdr_desc* desc);
+
+/* Backward of gdr_output_gate_forward, from dy [B,T,H,dv] (out_dtype):
+ *   dO   [B,T,H,dv] in in_dtype: the gradient of o, in the dtype gdr_backward
+ *        takes as its dO
+ *   dg   [B,T,H,dv] in in_dtype
+ *   dw   [H*dv] fp32, NULL = not computed (then ws may be NULL)
+ * Outputs must not overlap the inputs or each other. */
+gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const void* g, const float* w,
+                                    const void* dy, void* dO, void* dg, float* dw, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Static text for a status code. */
 const char* gdr_status_string(gdr_status status);
 

@@ -167,3 +167,19 @@ def test_backward_validates_descriptor(lib):
     P = ctypes.c_void_p
     args = [P(FAKE)] * 17
     assert lib.gdr_backward(ctypes.byref(d), *args, P(FAKE), 1 << 40, None) == UNSUPPORTED
+
+
+def test_output_gate_validation_and_workspace(lib):
+    d = desc(B=2, T=100, H=3, d=64)
+    P = fake
+    # workspace: one fp32 partial row of H*dv per token range (at most 256 ranges)
+    assert lib.gdr_output_gate_workspace_size(ctypes.byref(d)) == (min(200, 256) * 3 * 64 * 4 + 255) // 256 * 256
+    f = lib.gdr_output_gate_forward
+    assert f(ctypes.byref(d), None, P(2), None, P(3), None) == INVALID          # o missing
+    assert f(ctypes.byref(d), P(1), P(2), None, ctypes.c_void_p(FAKE + (3 << 32) + 4), None) == INVALID  # misaligned
+    assert f(ctypes.byref(d), P(1), P(2), None, ctypes.c_void_p(FAKE + (1 << 32) + 64), None) == INVALID  # y overlaps o
+    assert f(ctypes.byref(desc(d=96)), P(1), P(2), None, P(3), None) == UNSUPPORTED
+    b = lib.gdr_output_gate_backward
+    assert b(ctypes.byref(d), P(1), P(2), None, P(3), P(4), P(5), P(6), P(7), 16, None) == WORKSPACE
+    assert b(ctypes.byref(d), P(1), P(2), None, P(3), P(4), P(4), None, None, 0, None) == INVALID  # dO and dg overlap
+    assert b(ctypes.byref(d), P(1), P(2), None, P(3), P(1), P(5), None, None, 0, None) == INVALID  # dO overlaps o
