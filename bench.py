@@ -92,6 +92,9 @@ PER_TH_BYTES = {
     "cler_mt": 256,                                    # dh read
     "state_bwd_cler": 2 * 256 + 4,                     # dO, dh, beta read
     "cler_post": 256 + 4,                              # dh, beta read
+    # output-gate epilogue (bf16 o, g, y, dy, dO, dg)
+    "gate_fwd": 3 * 256,                               # o, g read; y written
+    "gate_bwd": 5 * 256,                               # o, g, dy read; dO, dg written
 }
 # Per (b,h) state tensors (fp32 d x d): S_T written by the forward state pass.
 PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
@@ -103,6 +106,8 @@ KERNEL_SOURCES = {
     "output": ["gdr_output.hip"], "output_cler": ["gdr_output.hip", "gdr_cler.hpp"],
     "cler_mt": ["gdr_cler.hip", "gdr_cler.hpp"], "cler_post": ["gdr_cler.hip", "gdr_cler.hpp"],
     "state_bwd_cler": ["gdr_bwd_state.hip"],
+    "gate_fwd": ["gdr_gate.hip"], "gate_bwd": ["gdr_gate.hip"],
+    "intra_train_pro": ["gdr_intra.hip"], "grad_lin_pro": ["gdr_bwd_grad.hip"], "grad_gate_pro": ["gdr_bwd_grad.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
     "decode": ["gdr_decode.hip"],
@@ -351,6 +356,34 @@ def main():
             pro_ms, sep_ms, json.dumps(pk_t)))
         del ws_p, pq, pk, pb, pa
 
+    # ---------------- output-gate epilogue on the step's output shape ----------------
+    og = torch.randn((B, T, H, d), device=dev).to(bf)
+    ow = torch.ones(H * d, device=dev)
+    oo = torch.randn((B, T, H, d), device=dev).to(bf)
+    ody = torch.randn((B, T, H, d), device=dev).to(bf)
+
+    def gate_pass():
+        gdr.output_gate(oo, og, ow)
+        gdr.output_gate_backward(oo, og, ow, ody)
+
+    for _ in range(args.warmup):
+        gate_pass()
+    torch.cuda.synchronize()
+    timer.begin()
+    for _ in range(args.steps):
+        gate_pass()
+    torch.cuda.synchronize()
+    gk = {}
+    for n, (c, ms) in timer.end().items():
+        if n in ("gate_fwd", "gate_bwd"):
+            us = 1e3 * ms / c
+            gbs = kbytes[n] / (us * 1e-6) / 1e9
+            gk[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    output_gate = {"workload": "sigmoid(g) * RMSNorm(o) per head on [B=%d, T=%d, H=%d, dv=%d] bf16" % (B, T, H, d),
+                   "kernels": gk}
+    log("output gate %s" % json.dumps(gk))
+    del og, oo, ody
+
     # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
     dc = gdr_inputs.DECODE_CONFIG
     nsets = 3
@@ -429,6 +462,7 @@ def main():
         "decode": decode,
         "cler": cler,
         "prologue": prologue,
+        "output_gate": output_gate,
     }
     print(json.dumps(out), flush=True)
 

@@ -45,21 +45,30 @@ __global__ __launch_bounds__(256) void gate_fwd_kernel(int64_t BT, int H, int64_
     OutT* y = reinterpret_cast<OutT*>(y_);
     float wv[8];
     load_lam8(w, static_cast<int64_t>(h) * D + c0, wv);
-#pragma unroll 2
-    for (int64_t r = r0 + rs; r < r1; r += RPI) {
-        const int64_t e = (r * H + h) * D + c0;
-        float ov[8], gv[8];
-        load8f(o + e, ov);
-        load8f(g + e, gv);
-        float ss = 0.f;
+    // NB rows per round: all their loads are issued before the first reduction
+    constexpr int NB = 4;
+    for (int64_t rb = r0 + rs; rb < r1; rb += NB * RPI) {
+        float ov[NB][8], gv[NB][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(ov[i], ov[i], ss);
-        ss = row_sum<TPR>(ss);
-        const float rstd = __builtin_amdgcn_rsqf(ss * (1.f / D) + GATE_EPS);
-        float yv[8];
+        for (int k = 0; k < NB; ++k) {
+            const int64_t r = rb + k * RPI < r1 ? rb + k * RPI : r1 - 1;  // clamped; not stored
+            const int64_t e = (r * H + h) * D + c0;
+            load8f(o + e, ov[k]);
+            load8f(g + e, gv[k]);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) yv[i] = sigmoid_fast(gv[i]) * wv[i] * (ov[i] * rstd);
-        store8f(y + e, yv);
+        for (int k = 0; k < NB; ++k) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(ov[k][i], ov[k][i], ss);
+            ss = row_sum<TPR>(ss);
+            const float rstd = __builtin_amdgcn_rsqf(ss * (1.f / D) + GATE_EPS);
+            float yv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] = sigmoid_fast(gv[k][i]) * wv[i] * (ov[k][i] * rstd);
+            const int64_t r = rb + k * RPI;
+            if (r < r1) store8f(y + (r * H + h) * D + c0, yv);
+        }
     }
 }
 
@@ -85,13 +94,25 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int64_t BT, int H, int64_
     load_lam8(w, static_cast<int64_t>(h) * D + c0, wv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 2
-    for (int64_t r = r0 + rs; r < r1; r += RPI) {
+    constexpr int NB = 2;  // rows per round, loads first
+    for (int64_t rb = r0 + rs; rb < r1; rb += NB * RPI) {
+      float ovb[NB][8], gvb[NB][8], dyb[NB][8];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+          const int64_t r = rb + k * RPI < r1 ? rb + k * RPI : r1 - 1;  // clamped; not stored or summed
+          const int64_t e = (r * H + h) * D + c0;
+          load8f(o + e, ovb[k]);
+          load8f(g + e, gvb[k]);
+          load8f(dy + e, dyb[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int64_t r = rb + k * RPI;
+        const bool live = r < r1;
         const int64_t e = (r * H + h) * D + c0;
-        float ov[8], gv[8], dyv[8];
-        load8f(o + e, ov);
-        load8f(g + e, gv);
-        load8f(dy + e, dyv);
+        float (&ov)[8] = ovb[k];
+        float (&gv)[8] = gvb[k];
+        float (&dyv)[8] = dyb[k];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(ov[i], ov[i], ss);
@@ -104,7 +125,7 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int64_t BT, int H, int64_
             sv[i] = sigmoid_fast(gv[i]);
             dn[i] = dyv[i] * sv[i] * wv[i];
             dot = __builtin_fmaf(dn[i], nv[i], dot);
-            acc[i] = __builtin_fmaf(dyv[i] * sv[i], nv[i], acc[i]);
+            if (live) acc[i] = __builtin_fmaf(dyv[i] * sv[i], nv[i], acc[i]);
         }
         dot = row_sum<TPR>(dot) * (1.f / D);
         float dov[8], dgv[8];
@@ -114,8 +135,11 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int64_t BT, int H, int64_
             // s (1 - s) = sigmoid(g) sigmoid(-g), without the subtraction
             dgv[i] = dyv[i] * wv[i] * nv[i] * sv[i] * sigmoid_fast(-gv[i]);
         }
-        store8f(dO + e, dov);
-        store8f(dg + e, dgv);
+        if (live) {
+            store8f(dO + e, dov);
+            store8f(dg + e, dgv);
+        }
+      }
     }
     if (!partial) return;
     // dw partial of this token range: the RPI row slots in a fixed order
