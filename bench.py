@@ -252,7 +252,11 @@ def main():
     fwd_flops = th * (5 * 64 * d + 6 * d * d + 64 * 64 / 3)
     kbytes = kernel_alg_bytes(B, T, H, d)
     for n, kr in kernels.items():
+        # a kernel may run as several launches per step (a state pass cut into
+        # chunk ranges and the per-chunk kernels of each range): bytes per launch
         nb = kbytes.get(n)
+        if nb:
+            nb = nb * args.steps // kr["launches"]
         kr["alg_bytes"] = nb
         kr["alg_GBs"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9, 1)
         kr["hbm_frac"] = None if not nb else round(nb / (kr["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
@@ -294,7 +298,7 @@ def main():
         for n, (c, ms) in timer.end().items():
             if n in ("output_cler", "cler_mt", "state_bwd_cler", "cler_post"):
                 us = 1e3 * ms / c
-                gbs = kbytes[n] / (us * 1e-6) / 1e9
+                gbs = kbytes[n] * args.steps / c / (us * 1e-6) / 1e9
                 ck[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         cler = {"workload": "the same step with route=error (CLER-H: h += lam * write error)",
                 "ms_per_step": round(cler_ms, 4), "tokens_per_s": round(tokens / (cler_ms * 1e-3), 1),
@@ -377,7 +381,7 @@ def main():
     for n, (c, ms) in timer.end().items():
         if n in ("gate_fwd", "gate_bwd"):
             us = 1e3 * ms / c
-            gbs = kbytes[n] / (us * 1e-6) / 1e9
+            gbs = kbytes[n] * args.steps / c / (us * 1e-6) / 1e9
             gk[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     output_gate = {"workload": "sigmoid(g) * RMSNorm(o) per head on [B=%d, T=%d, H=%d, dv=%d] bf16" % (B, T, H, d),
                    "kernels": gk}
@@ -457,7 +461,8 @@ def main():
                     "alg_TFLOPs": round(fwd_flops / (fwd_us * 1e-6) / 1e12, 2),
                     "hbm_frac": round(fwd_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "mfma_frac": round(fwd_flops / (fwd_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4)},
-        "kernels": {n: {"avg_us": round(kr["avg_us"], 2), "alg_GBs": kr["alg_GBs"], "hbm_frac": kr["hbm_frac"]}
+        "kernels": {n: {"avg_us": round(kr["avg_us"], 2), "launches_per_step": round(kr["launches"] / args.steps, 2),
+                        "alg_GBs": kr["alg_GBs"], "hbm_frac": kr["hbm_frac"]}
                     for n, kr in kernels.items()},
         "decode": decode,
         "cler": cler,

@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gdr_launch.hpp"
 
@@ -43,6 +44,55 @@ bool overlap(const void* p, size_t n, const void* q, size_t m) {
 }
 
 size_t dtype_bytes(int32_t dt) { return dt == GDR_FP32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Overlap of the sequential state passes with per-chunk work.  A state pass
+// runs one workgroup per (batch, head, 16-column slice); when that leaves CUs
+// idle, the pass is cut into chunk ranges (its state handed from one launch to
+// the next through the workspace) and the per-chunk kernels of a finished range
+// run on a second stream while the pass continues.  The second stream and the
+// events that order it against the caller's stream are created once per device
+// (default priority) and reused; enqueueing is serialised by a mutex so that
+// concurrent callers never interleave their uses of the shared events.
+// ---------------------------------------------------------------------------
+constexpr int kAuxEvents = 8;
+constexpr int kMaxDevices = 64;
+
+struct Aux {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kAuxEvents] = {};
+    int cus = 0;
+    bool ok = false, tried = false;
+};
+std::mutex g_aux_mu;
+Aux g_aux[kMaxDevices];
+
+// The current device's second stream, or nullptr if it cannot be had (then
+// everything runs on the caller's stream).  Call with g_aux_mu held.
+Aux* aux_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    Aux& a = g_aux[dev];
+    if (!a.tried) {
+        a.tried = true;
+        hipDeviceProp_t prop;
+        bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                  hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ok && i < kAuxEvents; ++i)
+            ok = hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming) == hipSuccess;
+        a.cus = ok ? prop.multiProcessorCount : 0;
+        a.ok = ok;
+    }
+    return a.ok ? &a : nullptr;
+}
+
+// Ranges to cut a state pass of `blocks` workgroups over NC chunks into: one
+// while the pass fills the chip, else up to four of at least 16 chunks.
+int state_parts(const Aux* a, int64_t blocks, int64_t NC) {
+    if (!a || blocks >= a->cus) return 1;
+    const int64_t p = NC / 16;
+    return int(p < 1 ? 1 : (p > 4 ? 4 : p));
+}
 
 // Checks a descriptor; fills derived sizes.
 gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
@@ -86,6 +136,11 @@ int64_t dlam_segments(const gdr_desc* d) {
     const int64_t bt = d->B * d->T;
     return bt < 1 ? 1 : (bt < 256 ? bt : 256);
 }
+// fp32 [B, H, dk, dv]: the state (gradient) handed between the ranges of a cut pass
+size_t carry_bytes(const gdr_desc* d) {
+    return d->T > 0 ? size_t(d->B) * size_t(d->H) * size_t(d->dk) * size_t(d->dv) * 4 : 0;
+}
+
 size_t dlam_partial_bytes(const gdr_desc* d) {
     if (d->route == GDR_ROUTE_ERROR) {
         const int64_t nc = (d->T + kChunk - 1) / kChunk;
@@ -185,7 +240,7 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
     size_t n = gdr::chunk_ws_bytes(nch, int(desc->dk), opb, op == 1, desc->route == GDR_ROUTE_ERROR,
                                    desc->prologue != GDR_PROLOGUE_NONE, nullptr, nullptr);
     if (op == 1) n += align_up(dlam_partial_bytes(desc));
-    return n;
+    return n + align_up(carry_bytes(desc));
 }
 
 }  // extern "C"
@@ -241,7 +296,8 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     const int pro = desc->prologue;
     const size_t chunk_bytes =
         gdr::chunk_ws_bytes(nch, int(D), opb, train, desc->route == GDR_ROUTE_ERROR, pro != 0, &w, ws);
-    const size_t need = train ? chunk_bytes + align_up(dlam_partial_bytes(desc)) : chunk_bytes;
+    const size_t need = (train ? chunk_bytes + align_up(dlam_partial_bytes(desc)) : chunk_bytes) +
+                        align_up(carry_bytes(desc));
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     if (B * H == 0) return GDR_OK;
@@ -268,17 +324,52 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         gdr::prof_after(train ? "intra_train" : "intra_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
     }
+    const char* st_name = train ? "state_train" : "state_fwd";
+    const char* out_name = cler ? "output_cler" : "output";
+    auto output = [&](gdr::ChunkRange cr, hipStream_t os) -> gdr_status {
+        gdr::prof_before(os);
+        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff, clvr_scale,
+                               cler ? h_clvr : nullptr, cr, os);
+        gdr::prof_after(out_name, os);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
+        return GDR_OK;
+    };
+    {
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        Aux* aux = (!in_f32 && NC > 0) ? aux_stream() : nullptr;
+        const int parts = state_parts(aux, B * H * (D / 16), NC);
+        if (parts > 1) {
+            // the chain in `parts` ranges (state handed through the workspace);
+            // the output of each finished range is computed on the second stream
+            float* carry = reinterpret_cast<float*>(static_cast<char*>(ws) + need - align_up(carry_bytes(desc)));
+            const int64_t per = (NC + parts - 1) / parts;
+            for (int p = 0; p < parts; ++p) {
+                const int64_t lo = p * per, hi = lo + per < NC ? lo + per : NC;
+                gdr::prof_before(s);
+                e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w,
+                                          p == 0 ? S0 : carry, p == parts - 1 ? ST : carry, o, true,
+                                          gdr::ChunkRange{lo, hi - lo}, s);
+                gdr::prof_after(st_name, s);
+                if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
+                if (hipEventRecord(aux->ev[p], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[p], 0) != hipSuccess)
+                    return fail(GDR_ERR_DEVICE, "stream ordering failed");
+                gdr_status g = output(gdr::ChunkRange{lo, hi - lo}, aux->s);
+                if (g != GDR_OK) return g;
+            }
+            if (hipEventRecord(aux->ev[kAuxEvents - 1], aux->s) != hipSuccess ||
+                hipStreamWaitEvent(s, aux->ev[kAuxEvents - 1], 0) != hipSuccess)
+                return fail(GDR_ERR_DEVICE, "stream ordering failed");
+            return GDR_OK;
+        }
+    }
     gdr::prof_before(s);
     e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o,
-                              train || cler, s);
-    gdr::prof_after(train ? "state_train" : "state_fwd", s);
+                              train || cler, gdr::ChunkRange{0, NC}, s);
+    gdr::prof_after(st_name, s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     if (!in_f32 && NC > 0) {
-        gdr::prof_before(s);
-        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff, clvr_scale,
-                               cler ? h_clvr : nullptr, s);
-        gdr::prof_after(cler ? "output_cler" : "output", s);
-        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
+        gdr_status g = output(gdr::ChunkRange{0, NC}, s);
+        if (g != GDR_OK) return g;
     }
     if (in_f32 && cler && NC > 0) {
         gdr::prof_before(s);
@@ -342,7 +433,7 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const int pro = desc->prologue;
     const size_t chunk_bytes =
         gdr::chunk_ws_bytes(nch, int(D), opb, true, desc->route == GDR_ROUTE_ERROR, pro != 0, &w, ws);
-    const size_t need = chunk_bytes + align_up(dlam_partial_bytes(desc));
+    const size_t need = chunk_bytes + align_up(dlam_partial_bytes(desc)) + align_up(carry_bytes(desc));
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     for (auto& o1 : outs)
@@ -355,18 +446,20 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
     const int gate = desc->gate;
     hipError_t e = hipSuccess;
-#define GDR_STEP(name, call)                                                                  \
+#define GDR_STEP_ON(st, name, call)                                                           \
     do {                                                                                      \
-        gdr::prof_before(s);                                                                  \
+        gdr::prof_before(st);                                                                 \
         e = (call);                                                                           \
-        gdr::prof_after(name, s);                                                             \
+        gdr::prof_after(name, st);                                                            \
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "%s launch: %s", name, hipGetErrorString(e)); \
     } while (0)
+#define GDR_STEP(name, call) GDR_STEP_ON(s, name, call)
     if (NC > 0 && recompute) {
         GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, 1, B, T, int(H), NC, q, k, v, beta,
                                                 alpha, nullptr, nullptr, w, pro, s));
         GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
-                                                         desc->scale, w, S0, nullptr, nullptr, true, s));
+                                                         desc->scale, w, S0, nullptr, nullptr, true,
+                                                         gdr::ChunkRange{0, NC}, s));
     }
     // error routing: dh reaches U inside the reverse state pass and beta and the
     // scale afterwards; value routing: dh reaches v in the gradient kernel
@@ -375,29 +468,73 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     const float* beta_eff = pro ? w.Bact : beta;
     if (cler && NC > 0)
         GDR_STEP("cler_mt", gdr::launch_cler_mt(int(D), in_f32, B, T, int(H), NC, w, clvr_scale, dh_clvr, s));
-    GDR_STEP(cler ? "state_bwd_cler" : "state_bwd", gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST,
-                                                 dS0, cler ? dh_clvr : nullptr, clvr_scale, beta_eff, s));
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes);
-    if (NC > 0) {
+    float* carry =
+        reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes + align_up(dlam_partial_bytes(desc)));
+    // per-chunk gradient kernels of one chunk range, on stream `gs`
+    auto grads = [&](gdr::ChunkRange cr, hipStream_t gs) -> gdr_status {
         // both routes add lam * dh to dv: the value route through v itself,
         // the error route through e = v - ...
-        GDR_STEP("grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
-                                                  q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dv, dbeta, w,
-                                                  pro, s));
+        GDR_STEP_ON(gs, "grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
+                                                         q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dv, dbeta,
+                                                         w, pro, cr, gs));
         if (cler)
-            GDR_STEP("cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta_eff, clvr_scale,
-                                                        dh_clvr, dclvr_scale, partial, s));
-        GDR_STEP("grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
-                                                    alpha, dq, dk, dalpha, w, pro, s));
+            GDR_STEP_ON(gs, "cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta_eff,
+                                                               clvr_scale, dh_clvr, dclvr_scale ? partial : nullptr,
+                                                               cr, gs));
+        GDR_STEP_ON(gs, "grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
+                                                           alpha, dq, dk, dalpha, w, pro, cr, gs));
+        return GDR_OK;
+    };
+    const char* sb_name = cler ? "state_bwd_cler" : "state_bwd";
+    const void* dh_state = cler ? dh_clvr : nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        Aux* aux = NC > 0 ? aux_stream() : nullptr;
+        const int parts = state_parts(aux, B * H * (D / 16), NC);
+        if (parts == 1) {
+            GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST, dS0,
+                                                    dh_state, clvr_scale, beta_eff, gdr::ChunkRange{0, NC}, s));
+            if (NC > 0) {
+                gdr_status g = grads(gdr::ChunkRange{0, NC}, s);
+                if (g != GDR_OK) return g;
+            }
+        } else {
+            // reverse pass in `parts` ranges, last chunks first; the gradient
+            // kernels of each finished range run on the second stream
+            const int64_t per = (NC + parts - 1) / parts;
+            for (int p = 0; p < parts; ++p) {
+                const int64_t hi = NC - p * per, lo = hi - per > 0 ? hi - per : 0;
+                GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO,
+                                                        p == 0 ? dST : carry, p == parts - 1 ? dS0 : carry,
+                                                        dh_state, clvr_scale, beta_eff, gdr::ChunkRange{lo, hi - lo},
+                                                        s));
+                if (hipEventRecord(aux->ev[p], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[p], 0) != hipSuccess)
+                    return fail(GDR_ERR_DEVICE, "stream ordering failed");
+                gdr_status g = grads(gdr::ChunkRange{lo, hi - lo}, aux->s);
+                if (g != GDR_OK) return g;
+            }
+            // the value-route scale gradient needs only dh and v: it runs on the
+            // caller's stream beside the last ranges' gradient kernels
+            if (!cler && dclvr_scale)
+                GDR_STEP("clvr_dlam", gdr::launch_clvr_dlam(in_f32, B * T, int(H), int(D), dh_clvr, v, dclvr_scale,
+                                                            partial, dlam_segments(desc), s));
+            if (hipEventRecord(aux->ev[kAuxEvents - 1], aux->s) != hipSuccess ||
+                hipStreamWaitEvent(s, aux->ev[kAuxEvents - 1], 0) != hipSuccess)
+                return fail(GDR_ERR_DEVICE, "stream ordering failed");
+            if (cler && dclvr_scale)
+                GDR_STEP("cler_dlam", gdr::launch_dlam_final(int(H * D), B * NC, partial, dclvr_scale, s));
+            return GDR_OK;
+        }
     }
     if (cler) {
-        if (dclvr_scale && NC == 0)
-            GDR_STEP("cler_dlam", gdr::launch_dlam_final(int(H * D), 0, partial, dclvr_scale, s));
+        if (dclvr_scale) GDR_STEP("cler_dlam", gdr::launch_dlam_final(int(H * D), B * NC, partial, dclvr_scale, s));
     } else if (dclvr_scale) {
         GDR_STEP("clvr_dlam", gdr::launch_clvr_dlam(in_f32, B * T, int(H), int(D), dh_clvr, v, dclvr_scale,
                                                     partial, dlam_segments(desc), s));
     }
 #undef GDR_STEP
+#undef GDR_STEP_ON
     return GDR_OK;
 }
 

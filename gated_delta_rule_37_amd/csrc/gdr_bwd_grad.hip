@@ -76,7 +76,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
                                                          const float* __restrict__ alpha,
                                                          const void* __restrict__ dO_, const void* __restrict__ dh_,
                                                          const float* __restrict__ lam, void* __restrict__ dv_,
-                                                         float* __restrict__ dbeta, ChunkWs ws, int pro) {
+                                                         float* __restrict__ dbeta, ChunkWs ws, int pro,
+                                                         ChunkRange cr) {
     using L = GLinLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -99,8 +100,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     float* NF = reinterpret_cast<float*>(smem + L::NF);
     float* DTF = reinterpret_cast<float*>(smem + L::DTF);
 
-    const int64_t ch = blockIdx.x;
-    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int64_t t0 = c * CHUNK;
@@ -498,15 +499,15 @@ template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* k,
                                     const void* v, const float* beta, const float* alpha, const void* dO,
                                     const void* dh, const float* lam, void* dv, float* dbeta, const ChunkWs& ws,
-                                    int pro, hipStream_t stream) {
-    const int64_t nblk = B * H * NC;
+                                    int pro, ChunkRange cr, hipStream_t stream) {
+    const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
     if (pro)
         hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
+                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr);
     else
         hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro);
+                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr);
     return hipGetLastError();
 }
 
@@ -514,25 +515,26 @@ template <int D, int GATE>
 static hipError_t launch_grad_lin_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                                     float scale, const void* k, const void* v, const float* beta,
                                     const float* alpha, const void* dO, const void* dh, const float* lam,
-                                    void* dv, float* dbeta, const ChunkWs& ws, int pro, hipStream_t stream) {
+                                    void* dv, float* dbeta, const ChunkWs& ws, int pro, ChunkRange cr,
+                                    hipStream_t stream) {
     if (in_f32) {
         if constexpr (D == 64) {
-            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
-            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
+            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
+            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
         }
         return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
     }
-    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
-    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream);
+    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
+    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
 }
 
 hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                            int64_t NC, float scale, const void* q, const void* k, const void* v,
                            const float* beta, const float* alpha, const void* dO,
                            const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, int pro, hipStream_t stream) {
+                           const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
     (void)q;
-#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, stream
+#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grad_lin_g<64, GATE_NONE>(GL_ARGS);
         if (gate == GATE_SCALAR) return launch_grad_lin_g<64, GATE_SCALAR>(GL_ARGS);
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
                                                           const void* __restrict__ q_, const void* __restrict__ k_,
                                                           const float* __restrict__ alpha, void* __restrict__ dq_,
                                                           void* __restrict__ dk_, float* __restrict__ dalpha,
-                                                          ChunkWs ws, int pro) {
+                                                          ChunkWs ws, int pro, ChunkRange cr) {
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -619,8 +621,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     float* SBf = reinterpret_cast<float*>(smem + L::SB);
     float* SCf = reinterpret_cast<float*>(smem + L::SC);
 
-    const int64_t ch = blockIdx.x;
-    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int64_t t0 = c * CHUNK;
@@ -1002,37 +1004,37 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
                                      const float* alpha, void* dq, void* dk, float* dalpha, const ChunkWs& ws,
-                                     int pro, hipStream_t stream) {
-    const int64_t nblk = B * H * NC;
+                                     int pro, ChunkRange cr, hipStream_t stream) {
+    const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
     if (pro)
         hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
+                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
     else
         hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro);
+                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
     return hipGetLastError();
 }
 
 template <int D, int GATE>
 static hipError_t launch_grad_gate_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                                      const void* q, const void* k, const float* alpha, void* dq, void* dk,
-                                     float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream) {
+                                     float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
     if (in_f32) {
         if constexpr (D == 64) {
-            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
-            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
+            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
+            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
         }
         return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
     }
-    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
-    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream);
+    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
+    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
 }
 
 hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream) {
-#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, stream
+                            void* dk, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
+#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grad_gate_g<64, GATE_NONE>(GG_ARGS);
         if (gate == GATE_SCALAR) return launch_grad_gate_g<64, GATE_SCALAR>(GG_ARGS);

@@ -236,7 +236,7 @@ __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t
 template <int D, bool IN_F32, bool CLER>
 __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                         const void* __restrict__ dO, const float* __restrict__ dST,
-                                                        float* __restrict__ dS0, ClerBwd cl) {
+                                                        float* __restrict__ dS0, ClerBwd cl, ChunkRange cr) {
     using Cfg = BwdCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
     constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
@@ -268,14 +268,15 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
     __syncthreads();
 
     BwdFrags<D, IN_F32> fa, fb;
-    if (NC > 0) load_bwd<D, IN_F32, CLER>(fa, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, wid, lane, cl);
+    const int64_t clo = cr.lo, chi = cr.lo + cr.n - 1;  // chunks chi down to clo
+    if (cr.n > 0) load_bwd<D, IN_F32, CLER>(fa, ws, bh * NC + chi, chi, b, T, H, h, dO, j0, wid, lane, cl);
 #pragma unroll 1
-    for (int64_t c = NC - 1; c >= 0; c -= 2) {
-        const int64_t n1 = c - 1 >= 0 ? c - 1 : 0;
+    for (int64_t c = chi; c >= clo; c -= 2) {
+        const int64_t n1 = c - 1 >= clo ? c - 1 : clo;
         load_bwd<D, IN_F32, CLER>(fb, ws, bh * NC + n1, n1, b, T, H, h, dO, j0, wid, lane, cl);
         bwd_step<D, IN_F32, CLER>(fa, c, T, bh, NC, j0, wid, lane, scale, lamj, ws, dS, s_dS, s_dO, s_dU, s_dUE);
-        if (c - 1 < 0) break;
-        const int64_t n2 = c - 2 >= 0 ? c - 2 : 0;
+        if (c - 1 < clo) break;
+        const int64_t n2 = c - 2 >= clo ? c - 2 : clo;
         load_bwd<D, IN_F32, CLER>(fa, ws, bh * NC + n2, n2, b, T, H, h, dO, j0, wid, lane, cl);
         bwd_step<D, IN_F32, CLER>(fb, c - 1, T, bh, NC, j0, wid, lane, scale, lamj, ws, dS, s_dS, s_dO, s_dU,
                                   s_dUE);
@@ -401,7 +402,7 @@ template <int D, bool CLER>
 __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                             const void* __restrict__ dO,
                                                             const float* __restrict__ dST,
-                                                            float* __restrict__ dS0, ClerBwd cl) {
+                                                            float* __restrict__ dS0, ClerBwd cl, ChunkRange cr) {
     using Cfg = BwdCfg<D, false>;
     using OpT = _Float16;
     using L = BwdStage<D, CLER>;
@@ -427,6 +428,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
     const int l16 = lane & 15, g4 = lane >> 4;
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
+    const int64_t clo = cr.lo, chi = cr.lo + cr.n - 1;  // chunks chi down to clo
 
     if (wid >= 4) {
         // Loaders: chunk c-1 goes into the buffer chunk c+1 used (free since the
@@ -435,17 +437,17 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         // one; wave 4 also warms the L2.
         const int part = wid - 4;
         const bool w4 = part == 0;
-        if (NC > 0) stage_bwd_part<D, CLER>(part, sbuf, ws, bh * NC + NC - 1, NC - 1, b, T, H, h, dO, j0, lane, cl);
+        if (cr.n > 0) stage_bwd_part<D, CLER>(part, sbuf, ws, bh * NC + chi, chi, b, T, H, h, dO, j0, lane, cl);
         if (w4) {
 #pragma unroll 1
-            for (int64_t c = NC - 2; c >= 0 && c > NC - 1 - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = chi - 1; c >= 0 && c > chi - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
         }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         int nb = 1;  // buffer of chunk c-1
 #pragma unroll 1
-        for (int64_t c = NC - 1; c >= 0; --c) {
-            const bool st = c >= 1, tpf = w4 && c - PF >= 0;
+        for (int64_t c = chi; c >= clo; --c) {
+            const bool st = c >= clo + 1, tpf = w4 && c - PF >= 0;
             if (st)
                 stage_bwd_part<D, CLER>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0,
                                         lane, cl);
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
 
     int cb = 0;
 #pragma unroll 1
-    for (int64_t c = NC - 1; c >= 0; --c) {
+    for (int64_t c = chi; c >= clo; --c) {
         const lds_char* src = sbuf + cb * L::BYTES;
         cb ^= 1;
         const int64_t ch = bh * NC + c;
@@ -605,36 +607,38 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
 
 template <int D, bool IN_F32, bool CLER>
 static void launch_state_bwd_c(int64_t nblk, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
-                               const void* dO, const float* dST, float* dS0, const ClerBwd& cl, hipStream_t stream) {
+                               const void* dO, const float* dST, float* dS0, const ClerBwd& cl, ChunkRange cr,
+                               hipStream_t stream) {
     if constexpr (!IN_F32)
         hipLaunchKernelGGL((state_bwd_lds_kernel<D, CLER>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC,
-                           scale, ws, dO, dST, dS0, cl);
+                           scale, ws, dO, dST, dS0, cl, cr);
     else
         hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32, CLER>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H,
-                           NC, scale, ws, dO, dST, dS0, cl);
+                           NC, scale, ws, dO, dST, dS0, cl, cr);
 }
 
 template <int D, bool IN_F32>
 static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
                                      const void* dO, const float* dST, float* dS0, const ClerBwd& cl,
-                                     hipStream_t stream) {
+                                     ChunkRange cr, hipStream_t stream) {
     const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    if (cl.dh) launch_state_bwd_c<D, IN_F32, true>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
-    else launch_state_bwd_c<D, IN_F32, false>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+    if (cl.dh) launch_state_bwd_c<D, IN_F32, true>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+    else launch_state_bwd_c<D, IN_F32, false>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            const void* dh_cler, const float* lam, const float* beta, hipStream_t stream) {
+                            const void* dh_cler, const float* lam, const float* beta, ChunkRange cr,
+                            hipStream_t stream) {
     const ClerBwd cl{dh_cler, lam, beta};
     if (D == 64) {
-        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
-        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
     }
-    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
-    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, stream);
+    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
 }
 
 }  // namespace gdr

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256) void cler_mt_kernel(int64_t T, int H, int64_t 
 template <int D, bool IN_F32>
 __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
                                                         const float* __restrict__ beta, const float* __restrict__ lam,
-                                                        const void* __restrict__ dh_, float* __restrict__ partial) {
+                                                        const void* __restrict__ dh_, float* __restrict__ partial,
+                                                        ChunkRange cr) {
     using Lc = ClerLayout<D, IN_F32>;
     using OpT = typename Lc::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -161,8 +162,8 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
     __shared__ __attribute__((aligned(16))) OpT sE[CHUNK * LDE];
     __shared__ float colred[4][32];
 
-    const int64_t ch = blockIdx.x;
-    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -273,8 +274,8 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
 template <int D, bool IN_F32>
 static hipError_t launch_cler_t(int which, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                                 const float* beta, const float* lam, void* h, const void* dh, float* partial,
-                                hipStream_t stream) {
-    const int64_t nch = B * H * NC;
+                                ChunkRange cr, hipStream_t stream) {
+    const int64_t nch = B * H * (which == 2 ? cr.n : NC);
     if (nch == 0) return hipSuccess;
     if (which == 0)
         hipLaunchKernelGGL((cler_fwd_kernel<D, IN_F32>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, ws,
@@ -284,37 +285,34 @@ static hipError_t launch_cler_t(int which, int64_t B, int64_t T, int H, int64_t 
                            dh);
     else
         hipLaunchKernelGGL((cler_post_kernel<D, IN_F32>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC, ws,
-                           beta, lam, dh, partial);
+                           beta, lam, dh, partial, cr);
     return hipGetLastError();
 }
 
 static hipError_t launch_cler(int which, int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC,
                               const ChunkWs& ws, const float* beta, const float* lam, void* h, const void* dh,
-                              float* partial, hipStream_t stream) {
+                              float* partial, ChunkRange cr, hipStream_t stream) {
     if (D == 64)
-        return in_f32 ? launch_cler_t<64, true>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, stream)
-                      : launch_cler_t<64, false>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, stream);
-    return in_f32 ? launch_cler_t<128, true>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, stream)
-                  : launch_cler_t<128, false>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, stream);
+        return in_f32 ? launch_cler_t<64, true>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, cr, stream)
+                      : launch_cler_t<64, false>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, cr, stream);
+    return in_f32 ? launch_cler_t<128, true>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, cr, stream)
+                  : launch_cler_t<128, false>(which, B, T, H, NC, ws, beta, lam, h, dh, partial, cr, stream);
 }
 
 hipError_t launch_cler_fwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                            const float* beta, const float* lam, void* h, hipStream_t stream) {
-    return launch_cler(0, D, in_f32, B, T, H, NC, ws, beta, lam, h, nullptr, nullptr, stream);
+    return launch_cler(0, D, in_f32, B, T, H, NC, ws, beta, lam, h, nullptr, nullptr, ChunkRange{0, NC}, stream);
 }
 
 hipError_t launch_cler_mt(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                           const float* lam, const void* dh, hipStream_t stream) {
-    return launch_cler(1, D, in_f32, B, T, H, NC, ws, nullptr, lam, nullptr, dh, nullptr, stream);
+    return launch_cler(1, D, in_f32, B, T, H, NC, ws, nullptr, lam, nullptr, dh, nullptr, ChunkRange{0, NC}, stream);
 }
 
 hipError_t launch_cler_post(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
-                            const float* beta, const float* lam, const void* dh, float* dlam, float* partial,
+                            const float* beta, const float* lam, const void* dh, float* partial, ChunkRange cr,
                             hipStream_t stream) {
-    hipError_t e = launch_cler(2, D, in_f32, B, T, H, NC, ws, beta, lam, nullptr, dh, dlam ? partial : nullptr,
-                               stream);
-    if (e != hipSuccess || !dlam) return e;
-    return launch_dlam_final(H * D, B * NC, partial, dlam, stream);
+    return launch_cler(2, D, in_f32, B, T, H, NC, ws, beta, lam, nullptr, dh, partial, cr, stream);
 }
 
 }  // namespace gdr

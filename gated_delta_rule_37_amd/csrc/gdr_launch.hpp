@@ -22,6 +22,12 @@ namespace gdr {
 //     dUsaveT [D][64] (op)                                      reverse pass
 //     gQt, gKt, gKb [64][D], gA, gP [64][64], gGam [D] (fp32)  gradients w.r.t.
 //       Qt, Kt, Kb, A, P and gamma, passed to the gate-gradient kernel
+// A range of chunks [lo, lo + n) of every (batch, head): the per-chunk kernels
+// run one workgroup per chunk-head of the range.
+struct ChunkRange {
+    int64_t lo, n;
+};
+
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;
     float* gam;
@@ -53,7 +59,7 @@ hipError_t launch_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nsl
 // from the same read of U (fp16 operands only).
 hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                          const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
-                         hipStream_t stream);
+                         ChunkRange cr, hipStream_t stream);
 
 // pro: the prologue (0 none; 1 / 2 the two alpha activations, gdr_prologue):
 // q, k arrive unnormalised and beta, alpha as logits.
@@ -62,25 +68,31 @@ hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
                         const ChunkWs& ws, int pro, hipStream_t stream);
 
+// cr: the chunks this launch carries the state through (fp16 operands only; the
+// fp32-operand pass always runs the whole sequence and ignores it).
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
-                            float* ST, void* o, bool save_for_backward, hipStream_t stream);
+                            float* ST, void* o, bool save_for_backward, ChunkRange cr, hipStream_t stream);
 
 // dh_cler (NULL = none): gradient at the hidden stream of the error-routing
 // epilogue, which adds lam * dh / beta to dU.
+// cr: the chunks this launch carries dS through, from lo + n - 1 down to lo; dST
+// is the gradient arriving at the end of the range, dS0 the one leaving its start.
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            const void* dh_cler, const float* lam, const float* beta, hipStream_t stream);
+                            const void* dh_cler, const float* lam, const float* beta, ChunkRange cr,
+                            hipStream_t stream);
 
 hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                            int64_t NC, float scale, const void* q, const void* k, const void* v,
                            const float* beta, const float* alpha, const void* dO,
                            const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, int pro, hipStream_t stream);
+                           const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream);
 
 hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, int pro, hipStream_t stream);
+                            void* dk, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
+                            hipStream_t stream);
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);
@@ -97,7 +109,7 @@ hipError_t launch_cler_fwd(int D, bool in_f32, int64_t B, int64_t T, int H, int6
 hipError_t launch_cler_mt(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                           const float* lam, const void* dh, hipStream_t stream);
 hipError_t launch_cler_post(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
-                            const float* beta, const float* lam, const void* dh, float* dlam, float* partial,
+                            const float* beta, const float* lam, const void* dh, float* partial, ChunkRange cr,
                             hipStream_t stream);
 
 // Output-gate epilogue y = sigmoid(g) * w * RMSNorm(o) per head (and its

@@ -37,7 +37,8 @@ struct OutLayout {
 template <int D, bool OUT_F32, bool CLER>
 __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                      void* __restrict__ o_, const float* __restrict__ beta,
-                                                     const float* __restrict__ lam, bf16_t* __restrict__ hs) {
+                                                     const float* __restrict__ lam, bf16_t* __restrict__ hs,
+                                                     ChunkRange cr) {
     using L = OutLayout<D>;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int LDT = L::LDT, LDU = L::LDU;
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     _Float16* sT = reinterpret_cast<_Float16*>(smem + L::ST);
     _Float16* uT = reinterpret_cast<_Float16*>(smem + L::UT);
 
-    const int64_t ch = blockIdx.x;
-    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -160,27 +161,27 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
 
 template <int D, bool OUT_F32>
 static void launch_output_t(int64_t nch, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws, void* o,
-                            const float* beta, const float* lam, void* h, hipStream_t stream) {
+                            const float* beta, const float* lam, void* h, ChunkRange cr, hipStream_t stream) {
     bf16_t* hs = static_cast<bf16_t*>(h);
     if (h)
         hipLaunchKernelGGL((output_kernel<D, OUT_F32, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                           scale, ws, o, beta, lam, hs);
+                           scale, ws, o, beta, lam, hs, cr);
     else
         hipLaunchKernelGGL((output_kernel<D, OUT_F32, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                           scale, ws, o, beta, lam, hs);
+                           scale, ws, o, beta, lam, hs, cr);
 }
 
 hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                          const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
-                         hipStream_t stream) {
-    const int64_t nch = B * H * NC;
+                         ChunkRange cr, hipStream_t stream) {
+    const int64_t nch = B * H * cr.n;
     if (nch == 0) return hipSuccess;
     if (D == 64) {
-        if (out_f32) launch_output_t<64, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
-        else launch_output_t<64, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
+        if (out_f32) launch_output_t<64, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
+        else launch_output_t<64, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
     } else {
-        if (out_f32) launch_output_t<128, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
-        else launch_output_t<128, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, stream);
+        if (out_f32) launch_output_t<128, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
+        else launch_output_t<128, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
     }
     return hipGetLastError();
 }

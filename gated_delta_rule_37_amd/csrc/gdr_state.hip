@@ -460,7 +460,7 @@ __device__ __forceinline__ void wait_outstanding(int n) {
 
 template <int D>
 __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
-                                                          const float* S0, float* ST) {
+                                                          const float* S0, float* ST, ChunkRange cr) {
     using Cfg = StateCfg<D, false>;
     using OpT = _Float16;
     using L = ChainStage<D>;
@@ -484,32 +484,35 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
     const int l16 = lane & 15, g4 = lane >> 4;
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
+    const int64_t lo = cr.lo, hi = cr.lo + cr.n;  // chunks lo .. hi-1 (the state enters at lo)
 
     if (wid >= 4) {
         // Loaders (waves 4-7, one part each).  Two barriers per step, like the
         // compute waves; they never fence, so their copies stay in flight
-        // across the first one.  Wave 4 also warms the L2.
+        // across the first one.  Wave 4 also warms the L2 (also past the range:
+        // the next range's first chunks).
         const int part = wid - 4;
         const bool w4 = part == 0;
-        if (NC > 0) stage_chain_part<D>(part, sbuf, ws, bh * NC, slice, lane);
-        if (NC > 1) stage_chain_part<D>(part, sbuf + L::BYTES, ws, bh * NC + 1, slice, lane);
+        if (cr.n > 0) stage_chain_part<D>(part, sbuf, ws, bh * NC + lo, slice, lane);
+        if (cr.n > 1) stage_chain_part<D>(part, sbuf + L::BYTES, ws, bh * NC + lo + 1, slice, lane);
         if (w4) {
 #pragma unroll 1
-            for (int64_t c = 2; c < PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = lo + 2; c < lo + PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
         }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         int nb = 2;  // buffer of chunk c + 2
 #pragma unroll 1
-        for (int64_t c = 0; c < NC; ++c) {
-            const bool st2 = c + 2 < NC, tpf = w4 && c + PF < NC;
+        for (int64_t c = lo; c < hi; ++c) {
+            const bool st2 = c + 2 < hi, tpf = w4 && c + PF < NC;
             if (st2) stage_chain_part<D>(part, sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
             if (tpf) touch_chain<D>(sdummy, ws, bh * NC + c + PF, slice, lane);
             nb = nb == 2 ? 0 : nb + 1;
             __builtin_amdgcn_s_barrier();
             // this wave's copies of chunk c+1 must have landed; later ones may stay in flight
             if (w4) {
-                const int n = ((c >= 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND0 : 0) + (tpf ? L::NT : 0);
+                // the previous step's touches (issued iff it ran and touched), then this step's copies and touches
+                const int n = ((c >= lo + 1 && c - 1 + PF < NC) ? L::NT : 0) + (st2 ? L::ND0 : 0) + (tpf ? L::NT : 0);
                 wait_outstanding<L::ND0, L::NT>(n);
             } else if (st2) {
                 wait_vmcnt<L::NDP>();
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
 
     int cb = 0;  // buffer of chunk c
 #pragma unroll 1
-    for (int64_t c = 0; c < NC; ++c) {
+    for (int64_t c = lo; c < hi; ++c) {
         ChunkFrags<D, false> f;
         chain_frags<D>(f, sbuf + cb * L::BYTES, wid, lane);
         cb = cb == 2 ? 0 : cb + 1;
@@ -554,14 +557,14 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
 template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float scale,
                                  const ChunkWs& ws, const float* S0, float* ST, void* o, bool save,
-                                 hipStream_t stream) {
+                                 ChunkRange cr, hipStream_t stream) {
     const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
     if constexpr (!IN_F32) {
         // fp16 operands: the chain pass always saves the chunk-start states and U;
         // the output is produced by output_kernel
         hipLaunchKernelGGL((state_chain_kernel<D>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC, ws, S0,
-                           ST);
+                           ST, cr);
         return hipGetLastError();
     }
     if (save && o)
@@ -578,21 +581,21 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
-                            float* ST, void* o, bool save_for_backward, hipStream_t stream) {
+                            float* ST, void* o, bool save_for_backward, ChunkRange cr, hipStream_t stream) {
     if (D == 64) {
         if (in_f32) {
-            if (out_f32) return launch_state_t<64, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
-            return launch_state_t<64, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
+            if (out_f32) return launch_state_t<64, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+            return launch_state_t<64, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
         }
-        if (out_f32) return launch_state_t<64, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
-        return launch_state_t<64, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
+        if (out_f32) return launch_state_t<64, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+        return launch_state_t<64, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
     }
     if (in_f32) {
-        if (out_f32) return launch_state_t<128, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
-        return launch_state_t<128, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
+        if (out_f32) return launch_state_t<128, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+        return launch_state_t<128, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
     }
-    if (out_f32) return launch_state_t<128, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
-    return launch_state_t<128, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, stream);
+    if (out_f32) return launch_state_t<128, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+    return launch_state_t<128, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
 }
 
 }  // namespace gdr
