@@ -55,7 +55,7 @@ size_t dtype_bytes(int32_t dt) { return dt == GDR_FP32 ? 4 : 2; }
 // (default priority) and reused; enqueueing is serialised by a mutex so that
 // concurrent callers never interleave their uses of the shared events.
 // ---------------------------------------------------------------------------
-constexpr int kAuxEvents = 8;
+constexpr int kAuxEvents = 16;
 constexpr int kMaxDevices = 64;
 
 struct Aux {
@@ -87,11 +87,15 @@ Aux* aux_stream() {
 }
 
 // Ranges to cut a state pass of `blocks` workgroups over NC chunks into: one
-// while the pass fills the chip, else up to four of at least 16 chunks.
+// while the pass fills the chip, else up to kMaxParts of at least 16 chunks.
+// (At the 32K-token KDA shape the training step took 3.37, 3.34, 3.41 and
+// 3.55 ms with at most 2, 4, 8 and 16 ranges: more ranges add relaunch and
+// pipeline-fill costs and shrink the grids of the overlapped kernels.)
+constexpr int kMaxParts = 4;
 int state_parts(const Aux* a, int64_t blocks, int64_t NC) {
     if (!a || blocks >= a->cus) return 1;
     const int64_t p = NC / 16;
-    return int(p < 1 ? 1 : (p > 4 ? 4 : p));
+    return int(p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p));
 }
 
 // Checks a descriptor; fills derived sizes.
