@@ -191,7 +191,6 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
     }
     if (backward) {
         const size_t sq32 = size_t(nch) * kChunk * kChunk * 4;
-        const size_t mat32 = size_t(nch) * kChunk * D * 4;
         w.AT = take(sq);
         w.Kb = take(mat);
         w.QtT = take(mat);
@@ -201,11 +200,11 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
         w.dSsnap = take(st);
         w.dUsave = take(mat);
         w.dUsaveT = take(mat);
-        w.gQt = static_cast<float*>(take(mat32));
-        w.gKt = static_cast<float*>(take(mat32));
-        w.gKb = static_cast<float*>(take(mat32));
-        w.gA = static_cast<float*>(take(sq32));
-        w.gP = static_cast<float*>(take(sq32));
+        w.gQt = take(mat);
+        w.gKt = take(mat);
+        w.gKb = take(mat);
+        w.gA = take(sq);
+        w.gP = take(sq);
         w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
         if (cler) w.Mt = take(mat);
     }

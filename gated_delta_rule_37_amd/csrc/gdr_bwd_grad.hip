@@ -335,8 +335,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         for (int r4 = 0; r4 < 4; ++r4) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ws.gQt[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = rq[r4][e];
-                ws.gKb[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = rk[r4][e];
+                static_cast<OpT*>(ws.gQt)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = from_f32<OpT>(rq[r4][e]);
+                static_cast<OpT*>(ws.gKb)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = from_f32<OpT>(rk[r4][e]);
             }
         }
 #pragma unroll
@@ -344,7 +344,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
             const int r4 = (wid >> 2) + k * NHALF;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                ws.gA[ch * CHUNK * CHUNK + (16 * r4 + 4 * g4 + e) * CHUNK + 16 * itp + l16] = ra[k][e];
+                static_cast<OpT*>(ws.gA)[ch * CHUNK * CHUNK + (16 * r4 + 4 * g4 + e) * CHUNK + 16 * itp + l16] =
+                    from_f32<OpT>(ra[k][e]);
         }
         if (g4 == 0) ws.gGam[ch * D + col] = sg;
     }
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
             const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ws.gKt[ch * CHUNK * D + (r_ + e) * D + col] = rkt[ii][e];
+                static_cast<OpT*>(ws.gKt)[ch * CHUNK * D + (r_ + e) * D + col] = from_f32<OpT>(rkt[ii][e]);
                 const int r = r_ + e;
                 if (r < nvalid) dv[base + r * tokstride + col] = from_f32<OutT>(rdv[ii][e]);
             }
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
             for (int e = 0; e < 4; ++e) {
                 const int a = 16 * at + 4 * g4 + e;
                 const float dl = (x < a) ? -acc[e] : 0.f;
-                ws.gP[ch * CHUNK * CHUNK + a * CHUNK + x] = s_beta[a] * dl;
+                static_cast<OpT*>(ws.gP)[ch * CHUNK * CHUNK + a * CHUNK + x] = from_f32<OpT>(s_beta[a] * dl);
                 CB[a * LDF + x] = dl * pwv[t][e];
             }
         }
@@ -635,8 +636,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
     const InT* q = reinterpret_cast<const InT*>(q_);
     const InT* k = reinterpret_cast<const InT*>(k_);
-    const float* gA = ws.gA + ch * CHUNK * CHUNK;
-    const float* gP = ws.gP + ch * CHUNK * CHUNK;
+    const OpT* gA = static_cast<const OpT*>(ws.gA) + ch * CHUNK * CHUNK;
+    const OpT* gP = static_cast<const OpT*>(ws.gP) + ch * CHUNK * CHUNK;
 
     // ---------------- phase 0: G, block references, row operands, dA/dP ----------------
     float G[RPP], kk[RPP], qq[RPP], al[RPP];
@@ -695,8 +696,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         float av[NE], pv[NE];
 #pragma unroll
         for (int k2 = 0; k2 < NE; ++k2) {
-            av[k2] = gA[k2 * NT + tid];
-            pv[k2] = gP[k2 * NT + tid];
+            av[k2] = to_f32(gA[k2 * NT + tid]);
+            pv[k2] = to_f32(gP[k2 * NT + tid]);
         }
 #pragma unroll
         for (int k2 = 0; k2 < NE; ++k2) {
@@ -861,14 +862,14 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     }
     // exact diagonal blocks (fp32, pair factors 2^(G_r - G_i) <= 1)
     if ((flags >> part) & 1) {
-        const float* gAr = gA + r0 * CHUNK + r0;
-        const float* gPr = gP + r0 * CHUNK + r0;
+        const OpT* gAr = gA + r0 * CHUNK + r0;
+        const OpT* gPr = gP + r0 * CHUNK + r0;
 #pragma unroll
         for (int jr = 0; jr < RPP; ++jr) {
 #pragma unroll
             for (int ji = 0; ji <= jr; ++ji) {
                 const float E = exp2_fast(G[jr] - G[ji]);
-                const float da = gAr[jr * CHUNK + ji], dp = (ji < jr) ? gPr[jr * CHUNK + ji] : 0.f;
+                const float da = to_f32(gAr[jr * CHUNK + ji]), dp = (ji < jr) ? to_f32(gPr[jr * CHUNK + ji]) : 0.f;
                 Aq[jr] += da * kk[ji] * E;
                 Prow[jr] += dp * kk[ji] * E;
                 Ccol[ji] += (da * qq[jr] + dp * kk[jr]) * E;
@@ -882,17 +883,17 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     {
         OutT* dq = reinterpret_cast<OutT*>(dq_);
         OutT* dk = reinterpret_cast<OutT*>(dk_);
-        const float* gQt = ws.gQt + ch * CHUNK * D;
-        const float* gKt = ws.gKt + ch * CHUNK * D;
-        const float* gKb = ws.gKb + ch * CHUNK * D;
+        const OpT* gQt = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * D;
+        const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * D;
+        const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * D;
         // every partial is loaded before the first store (the stores could
         // alias them as far as the compiler knows)
         float pq[RPP], pkt[RPP], pkb[RPP];
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
-            pq[j] = gQt[(r0 + j) * D + cc];
-            pkt[j] = gKt[(r0 + j) * D + cc];
-            pkb[j] = gKb[(r0 + j) * D + cc];
+            pq[j] = to_f32(gQt[(r0 + j) * D + cc]);
+            pkt[j] = to_f32(gKt[(r0 + j) * D + cc]);
+            pkb[j] = to_f32(gKb[(r0 + j) * D + cc]);
         }
         if constexpr (!PRO) {
 #pragma unroll

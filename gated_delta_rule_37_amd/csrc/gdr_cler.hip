@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
 
     // dKt -= dE S^T: wave w takes the state-row tiles dt = w, w + 4, ... for all
     // four position tiles (S fragments read once)
-    float* gKt = ws.gKt + ch * CHUNK * D;
+    OpT* gKt = static_cast<OpT*>(ws.gKt) + ch * CHUNK * D;
 #pragma unroll
     for (int dt = wid; dt < D / 16; dt += 4) {
         Frag<OpT> fs[KQ];
@@ -244,13 +244,16 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
                 mma(fe, fs[kq], acc);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16] -= acc[e];
+            for (int e = 0; e < 4; ++e) {
+                OpT& gk = gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16];
+                gk = from_f32<OpT>(to_f32(gk) - acc[e]);
+            }
         }
     }
     // dP -= strict_tril(dE U^T): wave w takes position-row tile w and the
     // column tiles up to it
     {
-        float* gP = ws.gP + ch * CHUNK * CHUNK;
+        OpT* gP = static_cast<OpT*>(ws.gP) + ch * CHUNK * CHUNK;
         const int at = wid;
         for (int xt = 0; xt <= at; ++xt) {
             float4v acc = zero4();
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 16 * at + 4 * g4 + e;
-                if (x < a) gP[a * CHUNK + x] -= acc[e];
+                if (x < a) gP[a * CHUNK + x] = from_f32<OpT>(to_f32(gP[a * CHUNK + x]) - acc[e]);
             }
         }
     }

@@ -34,7 +34,9 @@ struct ChunkWs {
     void *AT, *Kb, *QtT, *WT;
     float *Nw, *Pw;
     void *Ssnap, *Usave, *dSsnap, *dUsave, *dUsaveT;
-    float *gQt, *gKt, *gKb, *gA, *gP, *gGam;
+    // per-chunk gradient partials, in operand precision (fp16 for bf16 inputs)
+    void *gQt, *gKt, *gKb, *gA, *gP;
+    float* gGam;
     void* Mt;  // error-routing backward: M^T dE [64][D] per chunk-head
     // prologue: activated beta ([B,T,H] layout) and the reciprocal row norms of
     // q and k (negative where the norm was clamped), written by the intra kernel
