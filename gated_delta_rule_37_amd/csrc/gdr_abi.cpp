@@ -98,6 +98,43 @@ int state_parts(const Aux* a, int64_t blocks, int64_t NC) {
     return int(p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p));
 }
 
+// Bounds of range p of a pass cut into `parts`, in the order the pass runs.
+// Range sizes grow geometrically (weights 1 : 2 : 4 : ...) away from the range
+// whose per-chunk work cannot overlap anything: the first range of the reverse
+// pass (its gradient kernels wait for it, and each later range must be ready
+// before the gradient kernels of the one before finish, which run about twice
+// as long per chunk) and the last range of the forward (its output kernel runs
+// after the chain).  A range keeps at least 16 chunks where the sizes allow.
+void cut_range(int64_t NC, int parts, int p, bool reverse, int64_t* lo, int64_t* hi) {
+    if (parts < 2) {
+        *lo = 0;
+        *hi = NC;
+        return;
+    }
+    // sizes in processing order for the reverse pass: w_i = 2^i
+    int64_t size[kMaxParts];
+    const int64_t wsum = (int64_t(1) << parts) - 1;
+    int64_t used = 0;
+    for (int i = 0; i < parts; ++i) {
+        int64_t n = NC * (int64_t(1) << i) / wsum;
+        if (n < 16) n = 16;
+        size[i] = n;
+        used += n;
+    }
+    size[parts - 1] += NC - used;  // the largest range absorbs the remainder
+    if (size[parts - 1] < 1) {
+        // the minimums left nothing for it: equal ranges instead
+        for (int i = 0; i < parts; ++i) size[i] = NC / parts + (i < NC % parts ? 1 : 0);
+    }
+    // range i of the reverse order covers the chunks from the top down; the
+    // forward uses the same sizes from chunk 0 up, largest first
+    const int i = reverse ? p : parts - 1 - p;
+    int64_t top = NC;
+    for (int j = 0; j < i; ++j) top -= size[j];
+    *hi = top;
+    *lo = top - size[i];
+}
+
 // Checks a descriptor; fills derived sizes.
 gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
     if (!d) return fail(GDR_ERR_INVALID_ARG, "desc is NULL");
@@ -345,9 +382,9 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
             // the chain in `parts` ranges (state handed through the workspace);
             // the output of each finished range is computed on the second stream
             float* carry = reinterpret_cast<float*>(static_cast<char*>(ws) + need - align_up(carry_bytes(desc)));
-            const int64_t per = (NC + parts - 1) / parts;
             for (int p = 0; p < parts; ++p) {
-                const int64_t lo = p * per, hi = lo + per < NC ? lo + per : NC;
+                int64_t lo, hi;
+                cut_range(NC, parts, p, false, &lo, &hi);
                 gdr::prof_before(s);
                 e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w,
                                           p == 0 ? S0 : carry, p == parts - 1 ? ST : carry, o, true,
@@ -505,9 +542,9 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
         } else {
             // reverse pass in `parts` ranges, last chunks first; the gradient
             // kernels of each finished range run on the second stream
-            const int64_t per = (NC + parts - 1) / parts;
             for (int p = 0; p < parts; ++p) {
-                const int64_t hi = NC - p * per, lo = hi - per > 0 ? hi - per : 0;
+                int64_t lo, hi;
+                cut_range(NC, parts, p, true, &lo, &hi);
                 GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO,
                                                         p == 0 ? dST : carry, p == parts - 1 ? dS0 : carry,
                                                         dh_state, clvr_scale, beta_eff, gdr::ChunkRange{lo, hi - lo},
