@@ -95,3 +95,48 @@ def test_cut_forward_chain_matches_oracle(route):
     errs = {"o": rel(o, o_ref), "S": rel(ST, ST_ref), "h": rel(h, h_ref)}
     report(**errs)
     assert errs["o"] < 2e-3 and errs["S"] < 2e-3 and errs["h"] < 2e-3 + 2.0 ** -8, errs
+
+
+def test_training_pair_replays_from_a_hip_graph():
+    """The cut passes fork work onto the library's second stream and join it
+    back with events, which a graph capture on the caller's stream records as
+    well.  The captured training pair is replayed three times, with eager work
+    and synchronisations in between, and every replay must equal the eager
+    results bit for bit."""
+    announce("graph replay of the training pair")
+    inp = gdr_inputs.make(B=1, T=4096, H=1, d=128, gate="channel", dtype="bf16", seed=830, bwd=True, clvr=True)
+    t = inputs_to_dev({n: a for n, a in inp.items() if n not in ("h", "lam")}, "bf16")
+    lam = to_dev(inp["lam"])
+    h0 = to_dev(inp["h"], torch.bfloat16)
+    dh = to_dev(gdr_inputs.round_bf16(np.random.default_rng(831).standard_normal((1, 4096, 128))), torch.bfloat16)
+    ws = torch.empty(gdr.workspace_size(1, 4096, 1, 128, gdr.GATE_CHANNEL, torch.bfloat16, torch.bfloat16,
+                                        backward=True), dtype=torch.uint8, device="cuda")
+    h = h0.clone()
+
+    def pair():
+        h.copy_(h0)
+        o, ST = gdr.forward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], None, h=h, clvr_scale=lam,
+                            workspace=ws, save_for_backward=True)
+        g = gdr.backward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], None, t["dO"], dh=dh, clvr_scale=lam,
+                         want_dclvr_scale=True, saved_workspace=ws)
+        return [o, ST, h] + [g[n] for n in ("dq", "dk", "dv", "dbeta", "dalpha", "dclvr_scale")]
+
+    eager = [x.clone() for x in pair()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pair()  # warm the caching allocator on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = pair()
+    for rep in range(3):
+        scratch = torch.randn(1 << 20, device="cuda") * 2  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (rep, i)
+        del scratch
