@@ -100,7 +100,8 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     float* NF = reinterpret_cast<float*>(smem + L::NF);
     float* DTF = reinterpret_cast<float*>(smem + L::DTF);
 
-    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    int64_t bh, c;
+    range_block(cr, bh, c);
     const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
@@ -116,70 +117,18 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     const InT* v = reinterpret_cast<const InT*>(v_);
     const InT* dO = reinterpret_cast<const InT*>(dO_);
 
-    // ---------------- phase 1 operands, fetched first so that their latency
-    // overlaps phase 0: dU and U copied to LDS, dO converted into LDS, and this
-    // wave's S, dS' and V fragments into registers
-    constexpr int KQ1 = D / 32;
-    OpT* sDO = reinterpret_cast<OpT*>(smem + L::RDO);
-    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
-    const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
-    Frag<OpT> bS[KQ1], bD[KQ1], bV[KQ1];
-    const int itp = wid & 3;
-    {
-        constexpr int KQ = KQ1;
-        // stage dU and U (straight copies) and dO (converted; rows past the end zero)
-        {
-            constexpr int NCP = CHUNK * D * L::OPB / 1024;  // 1 KiB copies per array
-            const char* gdu = static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB;
-            const char* gu = static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB;
-            lds_char* sm = (lds_char*)&smem[0];
-            for (int i = wid; i < 2 * NCP; i += NW) {
-                if (i < NCP) copy16_to_lds(gdu + i * 1024 + lane * 16, sm + L::RDU + i * 1024);
-                else copy16_to_lds(gu + (i - NCP) * 1024 + lane * 16, sm + L::RU + (i - NCP) * 1024);
-            }
-            constexpr int NP = CHUNK * D / 8 / NT;  // 8-element pieces per thread
-#pragma unroll
-            for (int k2 = 0; k2 < NP; ++k2) {
-                const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
-                const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
-                Frag<OpT> x;
-                load_frag_in<InT, OpT>(x, dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
-                if (pos >= nvalid) x.zero();
-                if constexpr (sizeof(OpT) == 2) {
-                    *reinterpret_cast<half8*>(sDO + p * 8) = x.v;
-                } else {
-                    float4v lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = x.v[e];
-                        hi[e] = x.v[4 + e];
-                    }
-                    reinterpret_cast<float4v*>(sDO + p * 8)[0] = lo;
-                    reinterpret_cast<float4v*>(sDO + p * 8)[1] = hi;
-                }
-            }
-        }
-        // this wave's column tile of S and dS' (B operands, k = value column)
-        const int nt = wid;
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-            bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
-            bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
-        }
-        // V rows of this wave's position tiles (it = wid % 4)
-        {
-            const int brow = 16 * itp + l16;
-            const bool bok = brow < nvalid;
-            const int64_t brow_g = base + (bok ? brow : nvalid - 1) * tokstride;
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
-                if (!bok) bV[kq].zero();
-            }
-        }
+    // ---------------- loads.  Phase 0's operands (beta, alpha, k, N) are issued
+    // first, so that phase 0 waits only for them; phase 1's (dU and U copied to
+    // LDS, dO, and this wave's S, dS' and V fragments) follow and land while
+    // phase 0 computes.
+    float bt0 = 0.f, rk0 = 0.f, at0 = 1.f;
+    const bool tok_ok = tid < nvalid;
+    if (tid < CHUNK) {
+        const int64_t tok = (b * T + t0 + (tok_ok ? tid : nvalid - 1)) * H + h;
+        bt0 = beta[tok];  // activated (the prologue's copy when it is on)
+        if constexpr (PRO) rk0 = ws.rk[tok];
+        if constexpr (GATE == GATE_SCALAR) at0 = alpha[tok];
     }
-
-    // ---------------- phase 0: Kt = K 2^G, N, T^T ----------------
     float G[RPP], kk[RPP];
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
@@ -189,15 +138,66 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         if constexpr (GATE == GATE_CHANNEL) G[j] = alpha[e];
         else G[j] = 0.f;
     }
+    constexpr int NE = CHUNK * CHUNK / NT;
+    float nv[NE];
+#pragma unroll
+    for (int k2 = 0; k2 < NE; ++k2) nv[k2] = ws.Nw[ch * CHUNK * CHUNK + k2 * NT + tid];
+
+    constexpr int KQ1 = D / 32;
+    OpT* sDO = reinterpret_cast<OpT*>(smem + L::RDO);
+    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
+    const OpT* dSs = reinterpret_cast<const OpT*>(ws.dSsnap) + ch * D * D;
+    Frag<OpT> bS[KQ1], bV[KQ1];
+    Frag<OpT> bD[KQ1];
+    const int itp = wid & 3;
+    constexpr int NP = CHUNK * D / 8 / NT;  // dO: 8-element pieces per thread
+    Frag<OpT> xdo[NP];
+    constexpr int NCPT = CHUNK * D * L::OPB / 16 / NT;  // dU, U: 16-byte pieces per thread
+    uint4v xdu[NCPT], xu[NCPT];
+    {
+        constexpr int KQ = KQ1;
+        // dU and U: 16-byte pieces into registers, written to LDS at the start of
+        // phase 1.  (Not direct-to-LDS copies: while one of those is pending the
+        // compiler makes every LDS access wait for all loads, phase 0's included.)
+        {
+            const uint4v* gdu = reinterpret_cast<const uint4v*>(static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB);
+            const uint4v* gu = reinterpret_cast<const uint4v*>(static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB);
+#pragma unroll
+            for (int it = 0; it < NCPT; ++it) {
+                xdu[it] = gdu[it * NT + tid];
+                xu[it] = gu[it * NT + tid];
+            }
+        }
+        // this wave's column tile of S and dS' (B operands, k = value column)
+        const int nt = wid;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+            bS[kq].load(Ss + ((nt * KQ + kq) * 64 + lane) * 8);
+            bD[kq].load(dSs + ((nt * KQ + kq) * 64 + lane) * 8);
+        }
+        // V rows of this wave's position tiles (it = wid % 4); rows past the end
+        // read the last row and are zeroed at use
+        {
+            const int brow = 16 * itp + l16;
+            const int64_t brow_g = base + (brow < nvalid ? brow : nvalid - 1) * tokstride;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
+        }
+        // dO pieces, converted into LDS at the start of phase 1
+#pragma unroll
+        for (int k2 = 0; k2 < NP; ++k2) {
+            const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
+            const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
+            load_frag_in<InT, OpT>(xdo[k2], dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
+        }
+    }
+
+    // ---------------- phase 0: Kt = K 2^G, N, T^T ----------------
     if (tid < CHUNK) {
-        const bool ok = tid < nvalid;
-        const int64_t tok = (b * T + t0 + (ok ? tid : nvalid - 1)) * H + h;
-        const float bt = beta[tok];  // activated (the prologue's copy when it is on)
-        s_beta[tid] = ok ? bt : 0.f;
-        if constexpr (PRO) s_rk[tid] = fabsf(ws.rk[tok]);  // prologue: k row norms (intra kernel)
+        s_beta[tid] = tok_ok ? bt0 : 0.f;
+        if constexpr (PRO) s_rk[tid] = rk0;  // prologue: k row norms (intra kernel; negative if clamped)
         if constexpr (GATE == GATE_SCALAR) {
-            const float at = alpha[tok];
-            float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
+            float g = tok_ok ? (PRO ? log2_alpha_logit(at0, pro) : log2_fast(at0)) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -217,16 +217,10 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    {
-        constexpr int NE = CHUNK * CHUNK / NT;
-        float nv[NE];
 #pragma unroll
-        for (int k2 = 0; k2 < NE; ++k2) nv[k2] = ws.Nw[ch * CHUNK * CHUNK + k2 * NT + tid];
-#pragma unroll
-        for (int k2 = 0; k2 < NE; ++k2) {
-            const int e = k2 * NT + tid;
-            NF[(e / CHUNK) * LDF + e % CHUNK] = nv[k2];
-        }
+    for (int k2 = 0; k2 < NE; ++k2) {
+        const int e = k2 * NT + tid;
+        NF[(e / CHUNK) * LDF + e % CHUNK] = nv[k2];
     }
     __syncthreads();
     if constexpr (GATE == GATE_CHANNEL) {
@@ -242,7 +236,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
         // prologue: k divided by its row norm
-        const float kn = PRO ? kk[j] * s_rk[r0 + j] : kk[j];
+        const float kn = PRO ? kk[j] * fabsf(s_rk[r0 + j]) : kk[j];
         KT[(r0 + j) * LDR + cc] = from_f32<OpT>(kn * exp2_fast(G[j]));
     }
     // T^T[i][r] = N[r][i] beta_i
@@ -267,7 +261,38 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         const OpT* sU = reinterpret_cast<const OpT*>(smem + L::RU);
         constexpr int NPW = 4 / NHALF;  // position tiles per wave
         const int nt = wid;             // this wave's value-column tile
-        wait_vmcnt<0>();                // the copies into LDS have landed
+        // dU and U into LDS; dO converted (rows past the end zero); V rows past
+        // the end zeroed
+        {
+            uint4v* sdu = reinterpret_cast<uint4v*>(smem + L::RDU);
+            uint4v* su = reinterpret_cast<uint4v*>(smem + L::RU);
+#pragma unroll
+            for (int it = 0; it < NCPT; ++it) {
+                sdu[it * NT + tid] = xdu[it];
+                su[it * NT + tid] = xu[it];
+            }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NP; ++k2) {
+            const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
+            if (16 * (f / KQ) + (l & 15) >= nvalid) xdo[k2].zero();
+            if constexpr (sizeof(OpT) == 2) {
+                *reinterpret_cast<half8*>(sDO + p * 8) = xdo[k2].v;
+            } else {
+                float4v lo, hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo[e] = xdo[k2].v[e];
+                    hi[e] = xdo[k2].v[4 + e];
+                }
+                reinterpret_cast<float4v*>(sDO + p * 8)[0] = lo;
+                reinterpret_cast<float4v*>(sDO + p * 8)[1] = hi;
+            }
+        }
+        if (16 * itp + l16 >= nvalid) {
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) bV[kq].zero();
+        }
         __syncthreads();
 
         // dgamma_d = sum_j dS'[d][j] S[d][j], d = 16 nt + l16: this lane's 8 KQ
@@ -366,14 +391,27 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
         float dhv[NIT][4], lmv[NIT];
 #pragma unroll
         for (int ct = half; ct < D / 16; ct += NHALF) {
-            const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
+            const int ii = (ct - half) / NHALF;
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) bU[ii][kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
-            lmv[ii] = (dh && lam) ? lam[h * D + col] : 1.f;
+        }
+        if (dh) {  // CLVR: the four dh rows of each tile, all issued before any is used
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = r_ + e < nvalid ? r_ + e : nvalid - 1;  // clamped; not stored past the end
-                dhv[ii][e] = dh ? to_f32(dh[base + r * tokstride + col]) : 0.f;
+            for (int ct = half; ct < D / 16; ct += NHALF) {
+                const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
+                lmv[ii] = lam ? lam[h * D + col] : 1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r_ + e < nvalid ? r_ + e : nvalid - 1;  // clamped; not stored past the end
+                    dhv[ii][e] = to_f32(dh[base + r * tokstride + col]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ii = 0; ii < NIT; ++ii) {
+                lmv[ii] = 1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dhv[ii][e] = 0.f;
             }
         }
         float rkt[NIT][4], rdv[NIT][4];
@@ -622,7 +660,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     float* SBf = reinterpret_cast<float*>(smem + L::SB);
     float* SCf = reinterpret_cast<float*>(smem + L::SC);
 
-    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    int64_t bh, c;
+    range_block(cr, bh, c);
     const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
@@ -640,6 +679,21 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     const OpT* gP = static_cast<const OpT*>(ws.gP) + ch * CHUNK * CHUNK;
 
     // ---------------- phase 0: G, block references, row operands, dA/dP ----------------
+    // Every load of the phase is issued before any value is used, the token
+    // values first (the scalar-gate scan needs only them).  Rows past the end
+    // read the last row and are masked after the empty asm statement below: a
+    // masking select on a loaded value may otherwise turn into a branch around
+    // the load, which then waits for every load issued before it.
+    const bool tok_ok = tid < nvalid;
+    float at0 = 1.f, rq0 = 0.f, rk0 = 0.f;
+    if (tid < CHUNK) {
+        const int64_t tok = (b * T + t0 + (tok_ok ? tid : nvalid - 1)) * H + h;
+        if constexpr (GATE == GATE_SCALAR) at0 = alpha[tok];
+        if constexpr (PRO) {
+            rq0 = ws.rq[tok];
+            rk0 = ws.rk[tok];
+        }
+    }
     float G[RPP], kk[RPP], qq[RPP], al[RPP];
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
@@ -650,12 +704,11 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         if constexpr (GATE == GATE_CHANNEL) al[j] = alpha[e];
         else al[j] = 1.f;
     }
+    asm volatile("" ::: "memory");
     if constexpr (GATE == GATE_SCALAR) {
         if (tid < CHUNK) {
-            const bool ok = tid < nvalid;
-            const float at = alpha[(b * T + t0 + (ok ? tid : nvalid - 1)) * H + h];
-            float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
-            s_row[tid] = ok ? at : 1.f;
+            float g = tok_ok ? (PRO ? log2_alpha_logit(at0, pro) : log2_fast(at0)) : 0.f;
+            s_row[tid] = tok_ok ? at0 : 1.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(g, off);
@@ -679,9 +732,8 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     }
     if constexpr (PRO) {
         if (tid < CHUNK) {
-            const int64_t tok = (b * T + t0 + (tid < nvalid ? tid : nvalid - 1)) * H + h;
-            s_rq[tid] = ws.rq[tok];
-            s_rk[tid] = ws.rk[tok];
+            s_rq[tid] = rq0;
+            s_rk[tid] = rk0;
         }
     }
     if constexpr (GATE == GATE_CHANNEL) {
@@ -690,7 +742,6 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         s_tot[part][cc] = G[RPP - 1];
     }
     // dA, dP into operand precision, both orientations; Kh^T starts at zero.
-    // All loads are issued before the first LDS write.
     {
         constexpr int NE = CHUNK * CHUNK / NT;
         float av[NE], pv[NE];

@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256) void cler_post_kernel(int64_t T, int H, int64_
     __shared__ __attribute__((aligned(16))) OpT sE[CHUNK * LDE];
     __shared__ float colred[4][32];
 
-    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    int64_t bh, c;
+    range_block(cr, bh, c);
     const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);

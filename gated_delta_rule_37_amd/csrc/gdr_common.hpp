@@ -24,6 +24,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float8v __attribute__((ext_vector_type(8)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 enum Gate { GATE_NONE = 0, GATE_SCALAR = 1, GATE_CHANNEL = 2 };

@@ -28,6 +28,16 @@ struct ChunkRange {
     int64_t lo, n;
 };
 
+#ifdef __HIPCC__
+// Workgroup -> (batch * heads + head, chunk) of a launch over a range.  Grids
+// have fewer than 2^31 workgroups, so 32-bit division suffices.
+__device__ __forceinline__ void range_block(const ChunkRange& cr, int64_t& bh, int64_t& c) {
+    const uint32_t n = static_cast<uint32_t>(cr.n), bid = blockIdx.x;
+    bh = bid / n;
+    c = cr.lo + bid % n;
+}
+#endif
+
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;
     float* gam;

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     _Float16* sT = reinterpret_cast<_Float16*>(smem + L::ST);
     _Float16* uT = reinterpret_cast<_Float16*>(smem + L::UT);
 
-    const int64_t bh = blockIdx.x / cr.n, c = cr.lo + blockIdx.x % cr.n;
+    int64_t bh, c;
+    range_block(cr, bh, c);
     const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
