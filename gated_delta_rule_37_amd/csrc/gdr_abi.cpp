@@ -532,9 +532,12 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
         std::lock_guard<std::mutex> lock(g_aux_mu);
         Aux* aux = NC > 0 ? aux_stream() : nullptr;
         const int parts = state_parts(aux, B * H * (D / 16), NC);
+        // two state slices per workgroup when the pass shares the chip with the
+        // gradient kernels or has more slices than there are CUs
+        const bool wide = parts > 1 || (aux && B * H * (D / 16) > aux->cus);
         if (parts == 1) {
             GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO, dST, dS0,
-                                                    dh_state, clvr_scale, beta_eff, gdr::ChunkRange{0, NC}, s));
+                                                    dh_state, clvr_scale, beta_eff, wide, gdr::ChunkRange{0, NC}, s));
             if (NC > 0) {
                 gdr_status g = grads(gdr::ChunkRange{0, NC}, s);
                 if (g != GDR_OK) return g;
@@ -547,8 +550,8 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
                 cut_range(NC, parts, p, true, &lo, &hi);
                 GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO,
                                                         p == 0 ? dST : carry, p == parts - 1 ? dS0 : carry,
-                                                        dh_state, clvr_scale, beta_eff, gdr::ChunkRange{lo, hi - lo},
-                                                        s));
+                                                        dh_state, clvr_scale, beta_eff, wide,
+                                                        gdr::ChunkRange{lo, hi - lo}, s));
                 if (hipEventRecord(aux->ev[p], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[p], 0) != hipSuccess)
                     return fail(GDR_ERR_DEVICE, "stream ordering failed");
                 gdr_status g = grads(gdr::ChunkRange{lo, hi - lo}, aux->s);

@@ -293,39 +293,44 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant for fp16 operands.  Wave 4 copies chunk c-1's operands
-// (A^T, Kb, Qt^T, W^T, gamma and this slice's dO rows) from global memory
-// straight into the LDS buffer that chunk c+1 used, while waves 0-3 run chunk
-// c from the other buffer; it also pulls chunk c-PF into the L2.  The dO
+// LDS-staged variant for fp16 operands.  A workgroup carries NSW slices of one
+// head: waves 4 s .. 4 s + 3 run slice s, and the last four waves copy chunk
+// c-1's operands (A^T, Kb, Qt^T, W^T, gamma and the slices' dO rows) from
+// global memory straight into the LDS buffer that chunk c+1 used, while the
+// compute waves run chunk c from the other buffer; they also pull chunk c-PF
+// into the L2.  The slices share the staged operands, so each chunk is staged
+// D / (16 NSW) times instead of D / 16, and the pass occupies that many CUs per
+// head, which leaves the rest to the gradient kernels that run beside it (a
+// wave that ran several slices would lengthen the serial step).  The dO
 // fragments are built directly from the staged rows, so a step needs only two
 // barriers (after dU, after dS).
 // ---------------------------------------------------------------------------
 
-template <int D, bool CLER>
+template <int D, bool CLER, int NSW>
 struct BwdStage {
     static constexpr int MAT = CHUNK * D * 2;   // [64][D] or [D][64] fp16
     static constexpr int AT = 0;                // [64][64]
     static constexpr int KB = AT + CHUNK * CHUNK * 2;
     static constexpr int QTT = KB + MAT;
     static constexpr int WT = QTT + MAT;
-    static constexpr int DO = WT + MAT;         // dO rows of this slice: [64][16] in the input dtype (bf16)
-    static constexpr int GAM = DO + 2048;       // D fp32 in a 1 KiB slot
-    static constexpr int DH = GAM + 1024;       // error routing: dh rows of this slice, like dO
-    static constexpr int BT = DH + 2048;        // error routing: the chunk's 64 betas (1 KiB slot)
-    static constexpr int MT = BT + 1024;        // error routing: M^T dE rows of this slice (fp16)
-    static constexpr int BYTES = CLER ? MT + 2048 : GAM + 1024;
+    static constexpr int DO = WT + MAT;         // dO rows of each slice: NSW x [64][16] in the input dtype (bf16)
+    static constexpr int GAM = DO + NSW * 2048; // D fp32 in a 1 KiB slot
+    static constexpr int DH = GAM + 1024;       // error routing: dh rows of each slice, like dO
+    static constexpr int BT = DH + NSW * 2048;  // error routing: the chunk's 64 betas (1 KiB slot)
+    static constexpr int MT = BT + 1024;        // error routing: M^T dE rows of each slice (fp16)
+    static constexpr int BYTES = CLER ? MT + NSW * 2048 : GAM + 1024;
     static constexpr int NSL = D / 16;
-    static constexpr int NL = (CHUNK * CHUNK * 2 + 3 * MAT) / NSL / 128 + 1;  // lines touched per chunk
+    static constexpr int NL = (CHUNK * CHUNK * 2 + 3 * MAT) / NSL / 128 + 1;  // lines touched per chunk and slice
     static constexpr int NT = (NL + 63) / 64;
 };
 
-// PART 0: A^T, dO rows, gamma (and the epilogue's dh rows and betas); PART 1:
-// Kb; PART 2: Qt^T; PART 3: W^T.
-template <int D, bool CLER, int PART>
+// PART 0: A^T, the dO rows of the NSW slices from column j0 on, gamma (and the
+// epilogue's dh rows and betas); PART 1: Kb; PART 2: Qt^T; PART 3: W^T.
+template <int D, bool CLER, int NSW, int PART>
 __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c, int64_t b,
                                           int64_t T, int H, int h, const void* dO, int j0, int lane,
                                           const ClerBwd& cl) {
-    using L = BwdStage<D, CLER>;
+    using L = BwdStage<D, CLER, NSW>;
     if constexpr (PART == 1) {
         copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
     } else if constexpr (PART == 2) {
@@ -335,53 +340,64 @@ __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int6
     } else {
         copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2,
                                                     dst + L::AT, lane);
-        // dO rows: position pos = 32 i + lane / 2, half lane % 2 of its 16 columns
-        // (rows past the end re-read the last token; they are zeroed at use)
+        // dO rows: position pos = 32 i + lane / 2, half lane % 2 of the slice's 16
+        // columns (rows past the end re-read the last token; they are zeroed at use)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
-            const int64_t t = t0 < T ? t0 : T - 1;
-            const char* src = static_cast<const char*>(dO) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
-            copy16_to_lds(src, dst + L::DO + i * 1024);
-        }
-        const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
-        copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
-        if constexpr (CLER) {
+        for (int sl = 0; sl < NSW; ++sl) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
                 const int64_t t = t0 < T ? t0 : T - 1;
                 const char* src =
-                    static_cast<const char*>(cl.dh) + (((b * T + t) * H + h) * D + j0 + 8 * (lane & 1)) * 2;
-                copy16_to_lds(src, dst + L::DH + i * 1024);
+                    static_cast<const char*>(dO) + (((b * T + t) * H + h) * D + j0 + 16 * sl + 8 * (lane & 1)) * 2;
+                copy16_to_lds(src, dst + L::DO + sl * 2048 + i * 1024);
+            }
+        }
+        const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
+        copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
+        if constexpr (CLER) {
+#pragma unroll
+            for (int sl = 0; sl < NSW; ++sl) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int64_t t0 = c * CHUNK + 32 * i + (lane >> 1);
+                    const int64_t t = t0 < T ? t0 : T - 1;
+                    const char* src = static_cast<const char*>(cl.dh) +
+                                      (((b * T + t) * H + h) * D + j0 + 16 * sl + 8 * (lane & 1)) * 2;
+                    copy16_to_lds(src, dst + L::DH + sl * 2048 + i * 1024);
+                }
             }
             const int64_t t0 = c * CHUNK + lane;
             const int64_t t = t0 < T ? t0 : T - 1;
             copy4_to_lds(cl.beta + (b * T + t) * H + h, dst + L::BT);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int pos = 32 * i + (lane >> 1);
-                const char* src = static_cast<const char*>(ws.Mt) + ((ch * CHUNK + pos) * D + j0 + 8 * (lane & 1)) * 2;
-                copy16_to_lds(src, dst + L::MT + i * 1024);
+            for (int sl = 0; sl < NSW; ++sl) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int pos = 32 * i + (lane >> 1);
+                    const char* src = static_cast<const char*>(ws.Mt) +
+                                      ((ch * CHUNK + pos) * D + j0 + 16 * sl + 8 * (lane & 1)) * 2;
+                    copy16_to_lds(src, dst + L::MT + sl * 2048 + i * 1024);
+                }
             }
         }
     }
 }
 
 // Loader wave `part` (0..3) copies its share of chunk ch.
-template <int D, bool CLER>
+template <int D, bool CLER, int NSW>
 __device__ __forceinline__ void stage_bwd_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c,
                                                int64_t b, int64_t T, int H, int h, const void* dO, int j0, int lane,
                                                const ClerBwd& cl) {
-    if (part == 0) stage_bwd<D, CLER, 0>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
-    else if (part == 1) stage_bwd<D, CLER, 1>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
-    else if (part == 2) stage_bwd<D, CLER, 2>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
-    else stage_bwd<D, CLER, 3>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    if (part == 0) stage_bwd<D, CLER, NSW, 0>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else if (part == 1) stage_bwd<D, CLER, NSW, 1>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else if (part == 2) stage_bwd<D, CLER, NSW, 2>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
+    else stage_bwd<D, CLER, NSW, 3>(dst, ws, ch, c, b, T, H, h, dO, j0, lane, cl);
 }
 
 template <int D>
 __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
-    using L = BwdStage<D, false>;
+    using L = BwdStage<D, false, 1>;
     constexpr int AL = CHUNK * CHUNK * 2 / L::NSL / 128, QL = L::MAT / L::NSL / 128;
 #pragma unroll
     for (int i = 0; i < L::NT; ++i) {
@@ -398,49 +414,54 @@ __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, in
     }
 }
 
-template <int D, bool CLER>
-__global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
-                                                            const void* __restrict__ dO,
-                                                            const float* __restrict__ dST,
-                                                            float* __restrict__ dS0, ClerBwd cl, ChunkRange cr) {
+template <int D, bool CLER, int NSW>
+__global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64_t T, int H, int64_t NC, float scale,
+                                                                           ChunkWs ws, const void* __restrict__ dO,
+                                                                           const float* __restrict__ dST,
+                                                                           float* __restrict__ dS0, ClerBwd cl,
+                                                                           ChunkRange cr) {
     using Cfg = BwdCfg<D, false>;
     using OpT = _Float16;
-    using L = BwdStage<D, CLER>;
-    using LT = BwdStage<D, false>;
+    using L = BwdStage<D, CLER, NSW>;
+    using LT = BwdStage<D, false, 1>;
     constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S, LDS_U = Cfg::LDS_U;
+    constexpr int NG = NSL / NSW;  // workgroups per head
     constexpr int PF = 8;
+    static_assert(NSL % NSW == 0, "slices per workgroup");
 
-    __shared__ __attribute__((aligned(16))) OpT s_dS[Cfg::NS * LDS_S];
-    __shared__ __attribute__((aligned(16))) OpT s_dU[Cfg::NS * LDS_U];
-    __shared__ __attribute__((aligned(16))) OpT s_dUE[CLER ? Cfg::NS * LDS_U : 8];
+    __shared__ __attribute__((aligned(16))) OpT s_dS[NSW][Cfg::NS * LDS_S];
+    __shared__ __attribute__((aligned(16))) OpT s_dU[NSW][Cfg::NS * LDS_U];
+    __shared__ __attribute__((aligned(16))) OpT s_dUE[NSW][CLER ? Cfg::NS * LDS_U : 8];
     __shared__ __attribute__((aligned(1024))) char stage[2][L::BYTES];
     __shared__ __attribute__((aligned(16))) char dummy[LT::NT * 256];
 
     const int64_t nblk = gridDim.x;
     int64_t lid = blockIdx.x;
     if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-    const int64_t bh = lid / NSL;
-    const int slice = static_cast<int>(lid % NSL);
-    const int j0 = slice * Cfg::NS;
+    const int64_t bh = lid / NG;
+    const int grp = static_cast<int>(lid % NG);
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
     const int64_t clo = cr.lo, chi = cr.lo + cr.n - 1;  // chunks chi down to clo
 
-    if (wid >= 4) {
+    if (tid >= 256 * NSW) {
         // Loaders: chunk c-1 goes into the buffer chunk c+1 used (free since the
         // end of that step).  Four waves each copy one part (A^T, dO and gamma;
         // Kb; Qt^T; W^T), so four times as many copies are in flight as with
-        // one; wave 4 also warms the L2.
-        const int part = wid - 4;
+        // one; the first also warms the L2 (the lines of this group's slices).
+        const int part = (tid >> 6) - 4 * NSW;
         const bool w4 = part == 0;
-        if (cr.n > 0) stage_bwd_part<D, CLER>(part, sbuf, ws, bh * NC + chi, chi, b, T, H, h, dO, j0, lane, cl);
+        const int jg = grp * NSW * 16;
+        if (cr.n > 0) stage_bwd_part<D, CLER, NSW>(part, sbuf, ws, bh * NC + chi, chi, b, T, H, h, dO, jg, lane, cl);
         if (w4) {
 #pragma unroll 1
-            for (int64_t c = chi - 1; c >= 0 && c > chi - PF; --c) touch_bwd<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = chi - 1; c >= 0 && c > chi - PF; --c)
+#pragma unroll
+                for (int sl = 0; sl < NSW; ++sl) touch_bwd<D>(sdummy, ws, bh * NC + c, grp * NSW + sl, lane);
         }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
@@ -449,12 +470,15 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         for (int64_t c = chi; c >= clo; --c) {
             const bool st = c >= clo + 1, tpf = w4 && c - PF >= 0;
             if (st)
-                stage_bwd_part<D, CLER>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO, j0,
-                                        lane, cl);
-            if (tpf) touch_bwd<D>(sdummy, ws, bh * NC + c - PF, slice, lane);
+                stage_bwd_part<D, CLER, NSW>(part, sbuf + nb * L::BYTES, ws, bh * NC + c - 1, c - 1, b, T, H, h, dO,
+                                             jg, lane, cl);
+            if (tpf) {
+#pragma unroll
+                for (int sl = 0; sl < NSW; ++sl) touch_bwd<D>(sdummy, ws, bh * NC + c - PF, grp * NSW + sl, lane);
+            }
             __builtin_amdgcn_s_barrier();
             // chunk c-1 must have landed; only this step's touches may stay in flight
-            if (tpf) wait_vmcnt<LT::NT>();
+            if (tpf) wait_vmcnt<NSW * LT::NT>();
             else wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             nb ^= 1;
@@ -462,6 +486,12 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         return;
     }
 
+    // compute waves: slice sl of the group, wave wid (0..3) within the slice
+    const int sl = tid >> 8, wid = (tid >> 6) & 3, stid = tid & 255;
+    const int j0 = (grp * NSW + sl) * Cfg::NS;
+    OpT* const sdS = s_dS[sl];
+    OpT* const sdU = s_dU[sl];
+    OpT* const sdUE = s_dUE[sl];
     const float lamj = (CLER && cl.lam) ? cl.lam[static_cast<int64_t>(h) * D + j0 + l16] : 1.f;
     float4v dS[SRT];
 #pragma unroll
@@ -469,7 +499,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dS[m][e] = dST ? dST[(bh * D + d0 + e) * D + j0 + l16] : 0.f;
-        st4b<OpT>(s_dS + l16 * LDS_S + d0, dS[m]);
+        st4b<OpT>(sdS + l16 * LDS_S + d0, dS[m]);
     }
     __syncthreads();
 
@@ -503,7 +533,8 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
         // 32 kq + 8 g4 + e, scaled; rows past the end are zero
         Frag<OpT> fo[2];
         {
-            const __attribute__((address_space(3))) bf16_t* dos = reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DO);
+            const __attribute__((address_space(3))) bf16_t* dos =
+                reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DO + sl * 2048);
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
 #pragma unroll
@@ -522,15 +553,15 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
 #pragma unroll
         for (int kq = 0; kq < D / 32; ++kq) {
             Frag<OpT> fs;
-            fs.load(s_dS + l16 * LDS_S + 32 * kq + 8 * g4);
+            fs.load(sdS + l16 * LDS_S + 32 * kq + 8 * g4);
             mma(kb[kq], fs, du);
         }
         if constexpr (CLER) {
             // saved: dU - M^T dE; state update: dU + lam dh / beta (rows 16 wid + 4 g4 + e)
             const __attribute__((address_space(3))) bf16_t* dhs =
-                reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DH);
+                reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DH + sl * 2048);
             const __attribute__((address_space(3))) _Float16* mts =
-                reinterpret_cast<const __attribute__((address_space(3))) _Float16*>(src + L::MT);
+                reinterpret_cast<const __attribute__((address_space(3))) _Float16*>(src + L::MT + sl * 2048);
             const float4v bt =
                 *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::BT + (16 * wid + 4 * g4) * 4);
             float4v due;
@@ -540,15 +571,15 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
                 due[e] = du[e] - static_cast<float>(mts[pos * 16 + l16]);
                 if (c * CHUNK + pos < T) du[e] += lamj * bf16_to_f32(dhs[pos * 16 + l16]) / bt[e];
             }
-            st4b<OpT>(s_dUE + l16 * LDS_U + 16 * wid + 4 * g4, due);
+            st4b<OpT>(sdUE + l16 * LDS_U + 16 * wid + 4 * g4, due);
         }
-        st4b<OpT>(s_dU + l16 * LDS_U + 16 * wid + 4 * g4, du);
+        st4b<OpT>(sdU + l16 * LDS_U + 16 * wid + 4 * g4, du);
         __syncthreads();
 
         // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
         {
-            const OpT* s_sv = CLER ? s_dUE : s_dU;
-            const int t = tid;
+            const OpT* s_sv = CLER ? sdUE : sdU;
+            const int t = stid;
             if (t < 2 * CHUNK) {
                 const int pos = t >> 1, hf = t & 1;
                 OpT vals[8];
@@ -571,15 +602,15 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
                 const int d = RW * wid + (lane >> 1), hf = lane & 1;
                 OpT vals[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = s_dS[(8 * hf + e) * LDS_S + d];
+                for (int e = 0; e < 8; ++e) vals[e] = sdS[(8 * hf + e) * LDS_S + d];
                 st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf), vals);
             }
         }
 
         // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
         Frag<OpT> fu0, fu1;
-        fu0.load(s_dU + l16 * LDS_U + 8 * g4);
-        fu1.load(s_dU + l16 * LDS_U + 32 + 8 * g4);
+        fu0.load(sdU + l16 * LDS_U + 8 * g4);
+        fu1.load(sdU + l16 * LDS_U + 32 + 8 * g4);
 #pragma unroll
         for (int m = 0; m < SRT; ++m) {
 #pragma unroll
@@ -590,7 +621,7 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
             mma(wt[m][0], fu0, wdu);
             mma(wt[m][1], fu1, wdu);
             dS[m] -= wdu;
-            st4b<OpT>(s_dS + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, dS[m]);
+            st4b<OpT>(sdS + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, dS[m]);
         }
         __syncthreads();
     }
@@ -607,38 +638,45 @@ __global__ __launch_bounds__(512) void state_bwd_lds_kernel(int64_t T, int H, in
 
 template <int D, bool IN_F32, bool CLER>
 static void launch_state_bwd_c(int64_t nblk, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
-                               const void* dO, const float* dST, float* dS0, const ClerBwd& cl, ChunkRange cr,
-                               hipStream_t stream) {
-    if constexpr (!IN_F32)
-        hipLaunchKernelGGL((state_bwd_lds_kernel<D, CLER>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC,
-                           scale, ws, dO, dST, dS0, cl, cr);
-    else
+                               const void* dO, const float* dST, float* dS0, const ClerBwd& cl, bool wide,
+                               ChunkRange cr, hipStream_t stream) {
+    if constexpr (!IN_F32) {
+        if (wide)
+            hipLaunchKernelGGL((state_bwd_lds_kernel<D, CLER, 2>), dim3((unsigned)(nblk / 2)), dim3(64 * 12), 0,
+                               stream, T, H, NC, scale, ws, dO, dST, dS0, cl, cr);
+        else
+            hipLaunchKernelGGL((state_bwd_lds_kernel<D, CLER, 1>), dim3((unsigned)nblk), dim3(64 * 8), 0, stream,
+                               T, H, NC, scale, ws, dO, dST, dS0, cl, cr);
+    } else {
         hipLaunchKernelGGL((state_bwd_kernel<D, IN_F32, CLER>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H,
                            NC, scale, ws, dO, dST, dS0, cl, cr);
+    }
 }
 
 template <int D, bool IN_F32>
 static hipError_t launch_state_bwd_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
-                                     const void* dO, const float* dST, float* dS0, const ClerBwd& cl,
+                                     const void* dO, const float* dST, float* dS0, const ClerBwd& cl, bool wide,
                                      ChunkRange cr, hipStream_t stream) {
     const int64_t nblk = B * H * BwdCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    if (cl.dh) launch_state_bwd_c<D, IN_F32, true>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
-    else launch_state_bwd_c<D, IN_F32, false>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+    if (cl.dh) launch_state_bwd_c<D, IN_F32, true>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, wide, cr, stream);
+    else launch_state_bwd_c<D, IN_F32, false>(nblk, T, H, NC, scale, ws, dO, dST, dS0, cl, wide, cr, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            const void* dh_cler, const float* lam, const float* beta, ChunkRange cr,
+                            const void* dh_cler, const float* lam, const float* beta, bool wide, ChunkRange cr,
                             hipStream_t stream) {
     const ClerBwd cl{dh_cler, lam, beta};
+#define GDR_SB_ARGS B, T, H, NC, scale, ws, dO, dST, dS0, cl, wide, cr, stream
     if (D == 64) {
-        if (in_f32) return launch_state_bwd_t<64, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
-        return launch_state_bwd_t<64, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+        if (in_f32) return launch_state_bwd_t<64, true>(GDR_SB_ARGS);
+        return launch_state_bwd_t<64, false>(GDR_SB_ARGS);
     }
-    if (in_f32) return launch_state_bwd_t<128, true>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
-    return launch_state_bwd_t<128, false>(B, T, H, NC, scale, ws, dO, dST, dS0, cl, cr, stream);
+    if (in_f32) return launch_state_bwd_t<128, true>(GDR_SB_ARGS);
+    return launch_state_bwd_t<128, false>(GDR_SB_ARGS);
+#undef GDR_SB_ARGS
 }
 
 }  // namespace gdr

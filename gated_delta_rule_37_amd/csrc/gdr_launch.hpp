@@ -90,9 +90,11 @@ hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t
 // epilogue, which adds lam * dh / beta to dU.
 // cr: the chunks this launch carries dS through, from lo + n - 1 down to lo; dST
 // is the gradient arriving at the end of the range, dS0 the one leaving its start.
+// wide: two 16-column state slices per workgroup (half the workgroups, a longer
+// step) for fp16 operands.
 hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                             const ChunkWs& ws, const void* dO, const float* dST, float* dS0,
-                            const void* dh_cler, const float* lam, const float* beta, ChunkRange cr,
+                            const void* dh_cler, const float* lam, const float* beta, bool wide, ChunkRange cr,
                             hipStream_t stream);
 
 hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
