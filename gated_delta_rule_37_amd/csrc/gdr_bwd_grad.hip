@@ -345,7 +345,7 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
                 Frag<OpT> fo_, fdu;
                 fo_.load(sDO + fo);
                 fdu.load(sDU + fo);
-                if (itp <= r4) mma(fo_, bU[kq], aa);
+                mma(fo_, bU[kq], aa);  // tiles above the diagonal are masked below (no branch here)
                 mma(fdu, bV[kq], at);
             }
             const int r0_ = 16 * r4 + 4 * g4, pc = 16 * itp + l16;

@@ -509,7 +509,8 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
         const lds_char* src = sbuf + cb * L::BYTES;
         cb ^= 1;
         const int64_t ch = bh * NC + c;
-        // operand fragments of this wave
+        // operand fragments of this wave for dU (those for dS are read once the
+        // dU products are issued)
         Frag<OpT> at[2], kb[D / 32], qtt[SRT][2], wt[SRT][2];
         float gam[SRT][4];
         at[0].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::AT + ((wid * 2 + 0) * 64 + lane) * 16);
@@ -517,31 +518,27 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
 #pragma unroll
         for (int kq = 0; kq < D / 32; ++kq)
             kb[kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::KB + ((wid * (D / 32) + kq) * 64 + lane) * 16);
-#pragma unroll
-        for (int m = 0; m < SRT; ++m) {
-            const int rt = wid * (D / 64) + m;
-#pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
-                qtt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::QTT + ((rt * 2 + kq) * 64 + lane) * 16);
-                wt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::WT + ((rt * 2 + kq) * 64 + lane) * 16);
-            }
-            const float4v g = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::GAM + (16 * rt + 4 * g4) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gam[m][e] = g[e];
-        }
         // dO fragments (B operand, k = position): column j0 + l16, positions
         // 32 kq + 8 g4 + e, scaled; rows past the end are zero
+        // (all sixteen values are read before any is masked: a select on each
+        // read would become a branch that waits for every LDS read before it)
+        const int64_t nvc = T - c * CHUNK;  // positions of this chunk inside the sequence
         Frag<OpT> fo[2];
         {
             const __attribute__((address_space(3))) bf16_t* dos =
                 reinterpret_cast<const __attribute__((address_space(3))) bf16_t*>(src + L::DO + sl * 2048);
+            bf16_t raw[2][8];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) raw[kq][e] = dos[(32 * kq + 8 * g4 + e) * 16 + l16];
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int pos = 32 * kq + 8 * g4 + e;
-                    const float x = (c * CHUNK + pos < T) ? scale * bf16_to_f32(dos[pos * 16 + l16]) : 0.f;
-                    fo[kq].v[e] = from_f32<_Float16>(x);
+                    const float x = scale * bf16_to_f32(raw[kq][e]);
+                    fo[kq].v[e] = from_f32<_Float16>(32 * kq + 8 * g4 + e < nvc ? x : 0.f);
                 }
             }
         }
@@ -565,13 +562,30 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
             const float4v bt =
                 *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::BT + (16 * wid + 4 * g4) * 4);
             float4v due;
+            bf16_t dhr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dhr[e] = dhs[(16 * wid + 4 * g4 + e) * 16 + l16];
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int pos = 16 * wid + 4 * g4 + e;
                 due[e] = du[e] - static_cast<float>(mts[pos * 16 + l16]);
-                if (c * CHUNK + pos < T) du[e] += lamj * bf16_to_f32(dhs[pos * 16 + l16]) / bt[e];
+                if (pos < nvc) du[e] += lamj * bf16_to_f32(dhr[e]) / bt[e];
             }
             st4b<OpT>(sdUE + l16 * LDS_U + 16 * wid + 4 * g4, due);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int m = 0; m < SRT; ++m) {
+            const int rt = wid * (D / 64) + m;
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                qtt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::QTT + ((rt * 2 + kq) * 64 + lane) * 16);
+                wt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::WT + ((rt * 2 + kq) * 64 + lane) * 16);
+            }
+            const float4v g = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::GAM + (16 * rt + 4 * g4) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gam[m][e] = g[e];
         }
         st4b<OpT>(sdU + l16 * LDS_U + 16 * wid + 4 * g4, du);
         __syncthreads();
