@@ -858,34 +858,51 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         __syncthreads();
         // (a) dA_R Kh, (b) dP_R Kh: 16 x D each, k over 16(R+1) columns
         // (c) [dA_R^T | dP_R^T] [Qq_R ; Kq_R]: 16(R+1) x D, one 32-wide k step
-        constexpr int NDT = D / 16;
-        const int nj = 2 * NDT + (R + 1) * NDT;
-        for (int job = wid; job < nj; job += NW) {
-            float4v acc = zero4();
-            if (job < 2 * NDT) {
-                const int isP = job / NDT, ct = job % NDT;
+        // Wave w takes column tile w of all of them (D / 16 tiles, one per wave):
+        // a fixed set of products, so every read is issued before the first one
+        // is used.
+        static_assert(D / 16 == NW, "one column tile per wave");
+        {
+            const int ct = wid;
+            const int nkq = (16 * (R + 1) + 31) / 32;  // a constant once the R loop is unrolled
+            float4v acc[2];
+#pragma unroll
+            for (int isP = 0; isP < 2; ++isP) {
                 const OpT* arow = (isP ? dPs : dAs) + (16 * R + l16) * LDC + 8 * g4;
                 const OpT* brow = KhT + (16 * ct + l16) * LDC + 8 * g4;
-                const int nkq = (16 * (R + 1) + 31) / 32;
-                for (int kq = 0; kq < nkq; ++kq) {
-                    Frag<OpT> fa, fb;
-                    fa.load(arow + 32 * kq);
-                    fb.load(brow + 32 * kq);
-                    mma(fa, fb, acc);
-                }
-                float* dst = isP ? SBf : SAf;
+                acc[isP] = zero4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(4 * g4 + e) * D + 16 * ct + l16] = acc[e];
-            } else {
-                const int t = job - 2 * NDT, it = t / NDT, ct = t % NDT;
+                for (int kq = 0; kq < 2; ++kq) {
+                    if (kq < nkq) {
+                        Frag<OpT> fa, fb;
+                        fa.load(arow + 32 * kq);
+                        fb.load(brow + 32 * kq);
+                        mma(fa, fb, acc[isP]);
+                    }
+                }
+            }
+            float4v accc[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                if (it > R) continue;
                 Frag<OpT> fa, fb;
                 // k < 16: dA^T and Qq; k >= 16: dP^T and Kq (lane groups 0,1 vs 2,3)
                 const int i = 16 * it + l16, kr = 16 * R + 8 * (g4 & 1);
                 fa.load((g4 < 2 ? dAT : dPT) + i * LDC + kr);
                 fb.load((g4 < 2 ? QqT : KqT) + (16 * ct + l16) * LDC + kr);
-                mma(fa, fb, acc);
+                accc[it] = zero4();
+                mma(fa, fb, accc[it]);
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) SCf[(16 * it + 4 * g4 + e) * D + 16 * ct + l16] = acc[e];
+            for (int e = 0; e < 4; ++e) {
+                SAf[(4 * g4 + e) * D + 16 * ct + l16] = acc[0][e];
+                SBf[(4 * g4 + e) * D + 16 * ct + l16] = acc[1][e];
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                if (it > R) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) SCf[(16 * it + 4 * g4 + e) * D + 16 * ct + l16] = accc[it][e];
             }
         }
         __syncthreads();
