@@ -55,11 +55,17 @@ struct IntraLayout {
     static constexpr int NT = 4 * D;         // threads
     static constexpr int NW = NT / WAVE;     // waves
     static constexpr int RPP = 16;           // rows per thread (one 16-row block)
-    // phase 1-2: Kq, Qq, Kh  (each [64][LDR])
+    // phase 1-2: Kq, Qq ([64][LDR]) and Kh: [64][LDR], or for the channel gate
+    // with fp16 operands at d = 128 (KH4) the column operands of all four block
+    // rows, R = 0..3 holding rows 0 .. 16R+15 from row 8R(R+1) on (160 rows).
+    // (At d = 64 the larger buffer would stop two workgroups sharing a CU; with
+    // fp32 operands it does not fit.)
+    static constexpr bool KH4 = GATE == GATE_CHANNEL && !IN_F32 && D == 128;
     static constexpr int KQ = 0;
     static constexpr int QQ = KQ + CHUNK * LDR * OPB;
     static constexpr int KH = QQ + CHUNK * LDR * OPB;
-    static constexpr int END12 = KH + CHUNK * LDR * OPB;
+    static constexpr int KH_ROWS = KH4 ? 160 : CHUNK;
+    static constexpr int END12 = KH + KH_ROWS * LDR * OPB;
     // phase 3-4: Kt^T, V^T ([D][LDC]), P/L/T, N
     static constexpr int KTT = 0;
     static constexpr int VT = KTT + D * LDC * OPB;
@@ -379,12 +385,71 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     float* Ps = Nm;  // fp32 P staging, outside the phase 1-2 buffers
     OpT* A_g = reinterpret_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
     OpT* AT_g = reinterpret_cast<OpT*>(ws.AT) + ch * CHUNK * CHUNK;
-    constexpr int NPH = (GATE == GATE_CHANNEL) ? 4 : 1;
+    // One tile job: rows 16R.. of Kq (P) or Qq (A) against the column operand
+    // rows kh (16 of them), masked to the lower triangle and stored.
+    auto pa_tile = [&](int R, int I, int isA, const OpT* kh) {
+        float4v acc = zero4();
+        const OpT* arow = kh + l16 * LDR + 8 * g4;
+        const OpT* brow = (isA ? Qq : Kq) + (16 * R + l16) * LDR + 8 * g4;
 #pragma unroll
-    for (int ph = 0; ph < NPH; ++ph) {
-        if constexpr (GATE == GATE_CHANNEL) {
-            // column operand for block row R = ph: rows 0 .. 16R+15 with reference ref(R)
-            const int R = ph;
+        for (int kq = 0; kq < D / 32; ++kq) {
+            Frag<OpT> fa, fb;
+            fa.load(arow + 32 * kq);
+            fb.load(brow + 32 * kq);
+            mma(fa, fb, acc);
+        }
+        const int r = 16 * R + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g4 + e;
+            float f = (i <= r) ? 1.f : 0.f;
+            if constexpr (GATE == GATE_SCALAR) f = (i <= r) ? exp2_fast(s_gs[r] - s_gs[i]) : 0.f;
+            acc[e] *= f;
+        }
+        if (isA) {
+            if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
+            if constexpr (BWD) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) AT_g[frag_off<CHUNK>(16 * I + 4 * g4 + e, r)] = from_f32<OpT>(acc[e]);
+            }
+        } else {
+            *reinterpret_cast<float4v*>(Ps + r * CHUNK + 16 * I + 4 * g4) = acc;
+        }
+    };
+    if constexpr (L::KH4) {
+        // the column operands of all four block rows (reference ref(R)), built
+        // in one pass, so that the 20 tiles need a single barrier
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            if (part <= R) {
+                const float ref = R ? s_tot[R - 1][cc] : 0.f;
+                const float eref = exp2_fast(ref);
+                const bool zero = (part == R) && ((flags >> R) & 1);  // redone exactly below
+                OpT* khr = Kh + (8 * R * (R + 1) + r0) * LDR + cc;
+#pragma unroll
+                for (int j = 0; j < RPP; ++j) {
+                    float val = wide ? kk[j] * exp2_fast(ref - G[j]) : kk[j] * (Ei[j] * eref);
+                    khr[j * LDR] = from_f32<OpT>(zero ? 0.f : val);
+                }
+            }
+        }
+        __syncthreads();
+        // tiles (R, I <= R, P or A) in the order R, I, A/P, dealt to the waves in turn
+        constexpr int NJOB = 20, JPW = (NJOB + NW - 1) / NW;
+#pragma unroll
+        for (int k = 0; k < JPW; ++k) {
+            const int job = wid + NW * k;
+            if (job < NJOB) {
+                const int R = job < 2 ? 0 : (job < 6 ? 1 : (job < 12 ? 2 : 3));
+                const int I = (job - R * (R + 1)) >> 1, isA = job & 1;
+                if (!(I == R && ((flags >> R) & 1))) pa_tile(R, I, isA, Kh + (8 * R * (R + 1) + 16 * I) * LDR);
+            }
+        }
+    } else if constexpr (GATE == GATE_CHANNEL) {
+        // fp32 operands: one block row at a time through a single Kh buffer
+        int ti = 0;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
             if (part <= R) {
                 const float ref = R ? s_tot[R - 1][cc] : 0.f;
                 const float eref = exp2_fast(ref);
@@ -396,46 +461,17 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 }
             }
             __syncthreads();
+            for (int I = 0; I <= R; ++I)
+                for (int isA = 0; isA < 2; ++isA, ++ti)
+                    if ((ti % NW) == wid && !(I == R && ((flags >> R) & 1))) pa_tile(R, I, isA, Kh + (16 * I) * LDR);
+            if (R < 3) __syncthreads();  // Kh is rebuilt for the next block row
         }
-        const int Rlo = (GATE == GATE_CHANNEL) ? ph : 0;
-        const int Rhi = (GATE == GATE_CHANNEL) ? ph : 3;
+    } else {
         int ti = 0;
-        for (int R = Rlo; R <= Rhi; ++R) {
-            for (int I = 0; I <= R; ++I) {
-                for (int isA = 0; isA < 2; ++isA, ++ti) {
-                    if ((ti % NW) != wid) continue;
-                    if (GATE == GATE_CHANNEL && I == R && ((flags >> R) & 1)) continue;
-                    float4v acc = zero4();
-                    const OpT* arow = Kh + (16 * I + l16) * LDR + 8 * g4;
-                    const OpT* brow = (isA ? Qq : Kq) + (16 * R + l16) * LDR + 8 * g4;
-#pragma unroll
-                    for (int kq = 0; kq < D / 32; ++kq) {
-                        Frag<OpT> fa, fb;
-                        fa.load(arow + 32 * kq);
-                        fb.load(brow + 32 * kq);
-                        mma(fa, fb, acc);
-                    }
-                    const int r = 16 * R + l16;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * I + 4 * g4 + e;
-                        float f = (i <= r) ? 1.f : 0.f;
-                        if constexpr (GATE == GATE_SCALAR) f = (i <= r) ? exp2_fast(s_gs[r] - s_gs[i]) : 0.f;
-                        acc[e] *= f;
-                    }
-                    if (isA) {
-                        if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
-                        if constexpr (BWD) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) AT_g[frag_off<CHUNK>(16 * I + 4 * g4 + e, r)] = from_f32<OpT>(acc[e]);
-                        }
-                    } else {
-                        *reinterpret_cast<float4v*>(Ps + r * CHUNK + 16 * I + 4 * g4) = acc;
-                    }
-                }
-            }
-        }
-        if (GATE == GATE_CHANNEL && ph < NPH - 1) __syncthreads();  // Kh is rebuilt next phase
+        for (int R = 0; R <= 3; ++R)
+            for (int I = 0; I <= R; ++I)
+                for (int isA = 0; isA < 2; ++isA, ++ti)
+                    if ((ti % NW) == wid) pa_tile(R, I, isA, Kh + (16 * I) * LDR);
     }
     // zero the strictly upper tiles of A (never computed)
     for (int e = tid; e < 6 * 64; e += NT) {
