@@ -105,7 +105,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                                                       const float* __restrict__ beta,
                                                       const float* __restrict__ alpha,
                                                       void* __restrict__ h_, const float* __restrict__ lam,
-                                                      ChunkWs ws, int pro) {
+                                                      ChunkWs ws, int pro, ChunkRange cr) {
     constexpr bool FO = MODE != 1;  // forward operands: Qt, A
     constexpr bool BWD = MODE != 0; // backward operands: Kb, Qt^T, A^T, W^T, N, P
     using L = IntraLayout<D, GATE, IN_F32>;
@@ -131,8 +131,9 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     OpT* Tm = reinterpret_cast<OpT*>(smem + L::PL);
     float* Nm = reinterpret_cast<float*>(smem + L::NM);
 
-    const int64_t ch = blockIdx.x;  // (b*H + h)*NC + c
-    const int64_t bh = ch / NC, c = ch % NC;
+    int64_t bh, c;
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int64_t t0 = c * CHUNK;
@@ -693,12 +694,12 @@ template <int D, int GATE, bool IN_F32>
 static hipError_t launch_intra_t(int mode, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                                  const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
-                                 const ChunkWs& ws, int pro, hipStream_t stream) {
-    const int64_t nblk = B * H * NC;
+                                 const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
+    const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
 #define GDR_INTRA(M, P)                                                                                \
     hipLaunchKernelGGL((intra_kernel<D, GATE, IN_F32, M, P>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T, H, \
-                       NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro)
+                       NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr)
     if (pro) {
         if (mode == 1) GDR_INTRA(1, true);
         else if (mode == 2) GDR_INTRA(2, true);
@@ -716,24 +717,24 @@ template <int D, bool IN_F32>
 static hipError_t launch_intra_d(int gate, int mode, int64_t B, int64_t T, int H, int64_t NC,
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, void* h_clvr, const float* lam,
-                                 const ChunkWs& ws, int pro, hipStream_t stream) {
+                                 const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
     switch (gate) {
-        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
-        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
-        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+        case GATE_NONE: return launch_intra_t<D, GATE_NONE, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
+        case GATE_SCALAR: return launch_intra_t<D, GATE_SCALAR, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
+        default: return launch_intra_t<D, GATE_CHANNEL, IN_F32>(mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
     }
 }
 
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
-                        const ChunkWs& ws, int pro, hipStream_t stream) {
+                        const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
     if (D == 64) {
-        if (in_f32) return launch_intra_d<64, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
-        return launch_intra_d<64, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+        if (in_f32) return launch_intra_d<64, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
+        return launch_intra_d<64, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
     }
-    if (in_f32) return launch_intra_d<128, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
-    return launch_intra_d<128, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, stream);
+    if (in_f32) return launch_intra_d<128, true>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
+    return launch_intra_d<128, false>(gate, mode, B, T, H, NC, q, k, v, beta, alpha, h_clvr, lam, ws, pro, cr, stream);
 }
 
 }  // namespace gdr

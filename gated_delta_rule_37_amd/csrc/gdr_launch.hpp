@@ -74,11 +74,12 @@ hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64
                          ChunkRange cr, hipStream_t stream);
 
 // pro: the prologue (0 none; 1 / 2 the two alpha activations, gdr_prologue):
-// q, k arrive unnormalised and beta, alpha as logits.
+// q, k arrive unnormalised and beta, alpha as logits.  cr: the chunks of every
+// (batch, head) this launch transforms.
 hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64_t T, int H,
                         int64_t NC, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, void* h_clvr, const float* lam,
-                        const ChunkWs& ws, int pro, hipStream_t stream);
+                        const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream);
 
 // cr: the chunks this launch carries the state through (fp16 operands only; the
 // fp32-operand pass always runs the whole sequence and ignores it).
