@@ -86,6 +86,8 @@ PER_TH_BYTES = {
     "state_bwd": 256,                                  # dO read
     "grad_lin": 256 + 4 + 512 + 256 + 256 + 256 + 256 + 4,  # k,beta,alpha,v,dO,dh read; dv,dbeta written
     "grad_gate": 2 * 256 + 512 + 2 * 256 + 512,        # q,k,alpha read; dq,dk,dalpha written
+    # both gradient kernels in one launch (value route): the two rows above
+    "grads": (256 + 4 + 512 + 256 + 256 + 256 + 256 + 4) + (2 * 256 + 512 + 2 * 256 + 512),
     "clvr_dlam": 2 * 256,                              # dh, v read
     # error-routing epilogue (CLER-H) training step
     "output_cler": 256 + 2 * 256 + 4,                  # o written; h read+write; beta read
@@ -110,6 +112,7 @@ KERNEL_SOURCES = {
     "intra_train_pro": ["gdr_intra.hip"], "grad_lin_pro": ["gdr_bwd_grad.hip"], "grad_gate_pro": ["gdr_bwd_grad.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
+    "grads": ["gdr_bwd_grad.hip"], "grads_pro": ["gdr_bwd_grad.hip"],
     "decode": ["gdr_decode.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kda_t32k.txt")

@@ -550,6 +550,12 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     auto grads = [&](gdr::ChunkRange cr, hipStream_t gs) -> gdr_status {
         // both routes add lam * dh to dv: the value route through v itself,
         // the error route through e = v - ...
+        if (!cler) {  // nothing between the two: one kernel runs both per chunk
+            GDR_STEP_ON(gs, "grads", gdr::launch_grads(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
+                                                       q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dq, dk, dv,
+                                                       dbeta, dalpha, w, pro, cr, gs));
+            return GDR_OK;
+        }
         GDR_STEP_ON(gs, "grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
                                                          q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dv, dbeta,
                                                          w, pro, cr, gs));

@@ -69,22 +69,22 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
     }
 }
 
+// The bodies of the two gradient kernels are device functions on a caller-
+// provided LDS buffer, so that one kernel can run both for a chunk.
 template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
-__global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64_t NC, float scale,
-                                                         const void* __restrict__ k_, const void* __restrict__ v_,
-                                                         const float* __restrict__ beta,
-                                                         const float* __restrict__ alpha,
-                                                         const void* __restrict__ dO_, const void* __restrict__ dh_,
-                                                         const float* __restrict__ lam, void* __restrict__ dv_,
-                                                         float* __restrict__ dbeta, ChunkWs ws, int pro,
-                                                         ChunkRange cr) {
+__device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, float scale,
+                                              const void* __restrict__ k_, const void* __restrict__ v_,
+                                              const float* __restrict__ beta, const float* __restrict__ alpha,
+                                              const void* __restrict__ dO_, const void* __restrict__ dh_,
+                                              const float* __restrict__ lam, void* __restrict__ dv_,
+                                              float* __restrict__ dbeta, ChunkWs ws, int pro,
+                                              ChunkRange cr, char* smem) {
     using L = GLinLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int NT = L::NT, NW = L::NW, LDR = L::LDR, LDC = L::LDC, LDF = L::LDF, RPP = 16;
 
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __shared__ float s_tot[4][D];
     __shared__ float s_gs[CHUNK];
     __shared__ float s_beta[CHUNK];
@@ -534,6 +534,20 @@ __global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64
     }
 }
 
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+__global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64_t NC, float scale,
+                                                         const void* __restrict__ k_, const void* __restrict__ v_,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ alpha,
+                                                         const void* __restrict__ dO_, const void* __restrict__ dh_,
+                                                         const float* __restrict__ lam, void* __restrict__ dv_,
+                                                         float* __restrict__ dbeta, ChunkWs ws, int pro,
+                                                         ChunkRange cr) {
+    __shared__ __attribute__((aligned(16))) char smem[GLinLayout<D, IN_F32>::BYTES];
+    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_, dbeta,
+                                                 ws, pro, cr, smem);
+}
+
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* k,
                                     const void* v, const float* beta, const float* alpha, const void* dO,
@@ -607,6 +621,22 @@ namespace gdr {
 // the block's rows (pair factors from G differences, always <= 1).
 // ---------------------------------------------------------------------------
 
+// N values of one thread in operand precision, read one by one; fp16 values
+// are kept two to a register (the loads fill the low and high halves).
+template <typename OpT, int N>
+struct PairRows {
+    OpT v[N];
+    __device__ __forceinline__ void set(int j, OpT x) { v[j] = x; }
+    __device__ __forceinline__ float operator[](int j) const { return to_f32(v[j]); }
+};
+template <int N>
+struct PairRows<_Float16, N> {
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    half2v v[N / 2];
+    __device__ __forceinline__ void set(int j, _Float16 x) { v[j >> 1][j & 1] = x; }
+    __device__ __forceinline__ float operator[](int j) const { return static_cast<float>(v[j >> 1][j & 1]); }
+};
+
 template <int D, bool IN_F32>
 struct GGateLayout {
     using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
@@ -630,18 +660,17 @@ struct GGateLayout {
 };
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
-__global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int64_t NC,
-                                                          const void* __restrict__ q_, const void* __restrict__ k_,
-                                                          const float* __restrict__ alpha, void* __restrict__ dq_,
-                                                          void* __restrict__ dk_, float* __restrict__ dalpha,
-                                                          ChunkWs ws, int pro, ChunkRange cr) {
+__device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
+                                               const void* __restrict__ k_, const float* __restrict__ alpha,
+                                               void* __restrict__ dq_, void* __restrict__ dk_,
+                                               float* __restrict__ dalpha, ChunkWs ws, int pro, ChunkRange cr,
+                                               char* smem) {
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int NT = L::NT, NW = L::NW, LDC = L::LDC, RPP = 16;
 
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __shared__ float s_tot[4][D];
     __shared__ float s_gs[CHUNK];
     __shared__ float s_red[NW];
@@ -955,13 +984,14 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
         const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * D;
         const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * D;
         // every partial is loaded before the first store (the stores could
-        // alias them as far as the compiler knows)
-        float pq[RPP], pkt[RPP], pkb[RPP];
+        // alias them as far as the compiler knows); fp16 partials two rows to a
+        // register, which keeps this phase within the register file
+        PairRows<OpT, RPP> pq, pkt, pkb;
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
-            pq[j] = to_f32(gQt[(r0 + j) * D + cc]);
-            pkt[j] = to_f32(gKt[(r0 + j) * D + cc]);
-            pkb[j] = to_f32(gKb[(r0 + j) * D + cc]);
+            pq.set(j, gQt[(r0 + j) * D + cc]);
+            pkt.set(j, gKt[(r0 + j) * D + cc]);
+            pkb.set(j, gKb[(r0 + j) * D + cc]);
         }
         if constexpr (!PRO) {
 #pragma unroll
@@ -1070,6 +1100,38 @@ __global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int6
     }
 }
 
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+__global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int64_t NC,
+                                                          const void* __restrict__ q_, const void* __restrict__ k_,
+                                                          const float* __restrict__ alpha, void* __restrict__ dq_,
+                                                          void* __restrict__ dk_, float* __restrict__ dalpha,
+                                                          ChunkWs ws, int pro, ChunkRange cr) {
+    __shared__ __attribute__((aligned(16))) char smem[GGateLayout<D, IN_F32>::BYTES];
+    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr, smem);
+}
+
+// Both gradient kernels for one chunk in one workgroup (no epilogue between
+// them): the partials grad_lin writes are read back by the same workgroup,
+// from the L2, after a barrier that makes them visible; the LDS buffer is
+// shared.
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+__global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t NC, float scale,
+                                                      const void* __restrict__ q_, const void* __restrict__ k_,
+                                                      const void* __restrict__ v_, const float* __restrict__ beta,
+                                                      const float* __restrict__ alpha, const void* __restrict__ dO_,
+                                                      const void* __restrict__ dh_, const float* __restrict__ lam,
+                                                      void* __restrict__ dq_, void* __restrict__ dk_,
+                                                      void* __restrict__ dv_, float* __restrict__ dbeta,
+                                                      float* __restrict__ dalpha, ChunkWs ws, int pro,
+                                                      ChunkRange cr) {
+    constexpr int LB = GLinLayout<D, IN_F32>::BYTES, GB = GGateLayout<D, IN_F32>::BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[LB > GB ? LB : GB];
+    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_, dbeta,
+                                                 ws, pro, cr, smem);
+    __syncthreads();
+    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr, smem);
+}
+
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
                                      const float* alpha, void* dq, void* dk, float* dalpha, const ChunkWs& ws,
@@ -1113,6 +1175,59 @@ hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t 
     if (gate == GATE_SCALAR) return launch_grad_gate_g<128, GATE_SCALAR>(GG_ARGS);
     return launch_grad_gate_g<128, GATE_CHANNEL>(GG_ARGS);
 #undef GG_ARGS
+}
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+static hipError_t launch_grads_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* q,
+                                 const void* k, const void* v, const float* beta, const float* alpha,
+                                 const void* dO, const void* dh, const float* lam, void* dq, void* dk, void* dv,
+                                 float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
+                                 hipStream_t stream) {
+    const int64_t nblk = B * H * cr.n;
+    if (nblk == 0) return hipSuccess;
+#define GDR_GRADS(P)                                                                                              \
+    hipLaunchKernelGGL((grads_kernel<D, GATE, IN_F32, OUT_F32, P>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T, \
+                       H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr)
+    if (pro) GDR_GRADS(true);
+    else GDR_GRADS(false);
+#undef GDR_GRADS
+    return hipGetLastError();
+}
+
+template <int D, int GATE>
+static hipError_t launch_grads_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                                 const void* q, const void* k, const void* v, const float* beta,
+                                 const float* alpha, const void* dO, const void* dh, const float* lam, void* dq,
+                                 void* dk, void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro,
+                                 ChunkRange cr, hipStream_t stream) {
+#define GDR_GR_ARGS B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, stream
+    if (in_f32) {
+        if constexpr (D == 64) {
+            if (out_f32) return launch_grads_t<D, GATE, true, true>(GDR_GR_ARGS);
+            return launch_grads_t<D, GATE, true, false>(GDR_GR_ARGS);
+        }
+        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
+    }
+    if (out_f32) return launch_grads_t<D, GATE, false, true>(GDR_GR_ARGS);
+    return launch_grads_t<D, GATE, false, false>(GDR_GR_ARGS);
+#undef GDR_GR_ARGS
+}
+
+hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
+                        float scale, const void* q, const void* k, const void* v, const float* beta,
+                        const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
+                        void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
+                        hipStream_t stream) {
+#define GDR_GR_ARGS in_f32, out_f32, B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, stream
+    if (D == 64) {
+        if (gate == GATE_NONE) return launch_grads_g<64, GATE_NONE>(GDR_GR_ARGS);
+        if (gate == GATE_SCALAR) return launch_grads_g<64, GATE_SCALAR>(GDR_GR_ARGS);
+        return launch_grads_g<64, GATE_CHANNEL>(GDR_GR_ARGS);
+    }
+    if (gate == GATE_NONE) return launch_grads_g<128, GATE_NONE>(GDR_GR_ARGS);
+    if (gate == GATE_SCALAR) return launch_grads_g<128, GATE_SCALAR>(GDR_GR_ARGS);
+    return launch_grads_g<128, GATE_CHANNEL>(GDR_GR_ARGS);
+#undef GDR_GR_ARGS
 }
 
 // ---------------------------------------------------------------------------

@@ -109,6 +109,14 @@ hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t 
                             void* dk, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
                             hipStream_t stream);
 
+// Both gradient kernels of a chunk range in one launch, when no epilogue runs
+// between them: the arguments of launch_grad_lin and launch_grad_gate together.
+hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
+                        float scale, const void* q, const void* k, const void* v, const float* beta,
+                        const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
+                        void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
+                        hipStream_t stream);
+
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);
 // dlam[c] = sum over nseg rows of partial[seg][c], fixed order
