@@ -580,66 +580,32 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         for (int r = 0; r < 16; ++r) Nm[(16 * R + r) * CHUNK + 16 * R + lane] = x[r];
     }
     __syncthreads();
-    // off-diagonal blocks: N[R, <R] = -N_RR (L[R, <R] N[<R, <R])
-    {
-        constexpr int RSTEP = NT / 32;            // rows of block R handled per pass
-        constexpr int RPT = 16 / RSTEP;           // rows per thread (1 or 2)
-        const int r0t = tid >> 5, cl = tid & 31;  // first row in block R, column lane
-        float* X = Pm;  // rows 0..15 of L are no longer needed
+    // off-diagonal blocks, one block row at a time on fp32 matrix cores:
+    // N[R, J] = -N_RR (sum_{K=J}^{R-1} L[R, K] N[K, J]), wave J taking tile J.
+    // One v_mfma_f32_16x16x4 per 4-wide k slice; lane (l16, g4) supplies k =
+    // 4 g4 + m of instruction m, so A rows are read as float4 and the product's
+    // accumulator (rows 4 g4 .. +3, column l16) is directly the B operand of
+    // the next product.
 #pragma unroll
-        for (int R = 1; R < 4; ++R) {
-            float xs[RPT][2];
+    for (int R = 1; R < 4; ++R) {
+        if (wid < R) {
+            const int J = wid;
+            float4v x = zero4();
+            for (int K = J; K < R; ++K) {
+                const float4v a = *reinterpret_cast<const float4v*>(Pm + (16 * R + l16) * CHUNK + 16 * K + 4 * g4);
 #pragma unroll
-            for (int a = 0; a < RPT; ++a) {
-                const int r = r0t + a * RSTEP;
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const int col = cl + 32 * mm;
-                    float s = 0.f;
-                    if (col < 16 * R) {
-                        const float* Lr = Pm + (16 * R + r) * CHUNK;
-                        for (int j = 16 * (col >> 4); j < 16 * R; ++j) s += Lr[j] * Nm[j * CHUNK + col];
-                    }
-                    xs[a][mm] = s;
-                }
+                for (int m = 0; m < 4; ++m)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], Nm[(16 * K + 4 * g4 + m) * CHUNK + 16 * J + l16], x,
+                                                             0, 0, 0);
             }
-            __syncthreads();
+            const float4v nrr = *reinterpret_cast<const float4v*>(Nm + (16 * R + l16) * CHUNK + 16 * R + 4 * g4);
+            float4v y = zero4();
 #pragma unroll
-            for (int a = 0; a < RPT; ++a) {
-                const int r = r0t + a * RSTEP;
+            for (int m = 0; m < 4; ++m) y = __builtin_amdgcn_mfma_f32_16x16x4f32(nrr[m], x[m], y, 0, 0, 0);
 #pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const int col = cl + 32 * mm;
-                    if (col < 16 * R) X[r * CHUNK + col] = xs[a][mm];
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int a = 0; a < RPT; ++a) {
-                const int r = r0t + a * RSTEP;
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const int col = cl + 32 * mm;
-                    if (col < 16 * R) {
-                        float s = 0.f;
-                        const float* Nr = Nm + (16 * R + r) * CHUNK + 16 * R;
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) s += Nr[j] * X[j * CHUNK + col];
-                        xs[a][mm] = -s;
-                    }
-                }
-            }
-#pragma unroll
-            for (int a = 0; a < RPT; ++a) {
-                const int r = r0t + a * RSTEP;
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const int col = cl + 32 * mm;
-                    if (col < 16 * R) Nm[(16 * R + r) * CHUNK + col] = xs[a][mm];
-                }
-            }
-            __syncthreads();
+            for (int e = 0; e < 4; ++e) Nm[(16 * R + 4 * g4 + e) * CHUNK + 16 * J + l16] = -y[e];
         }
+        __syncthreads();
     }
     // T = N diag(beta) in operand precision (row-major, padded), in the L region
     for (int e = tid; e < CHUNK * CHUNK; e += NT) {
