@@ -387,16 +387,24 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
         return GDR_OK;
     };
+    // two state slices per workgroup when the chain has more slices than there are CUs
+    bool wide = false;
     {
         std::lock_guard<std::mutex> lock(g_aux_mu);
         Aux* aux = (!in_f32 && NC > 0) ? aux_stream() : nullptr;
         const int parts = state_parts(aux, B * H * (D / 16), NC);
+        wide = aux && B * H * (D / 16) > aux->cus;
         if (parts > 1) {
             // The chain in `parts` ranges (state handed through the workspace).
             // Range p's intra-chunk transform runs on the second stream while
             // the chain carries range p-1 (the chain holds only part of the chip),
             // and the output of each finished range on the third.  Events: ev[p]
-            // intra range p done, ev[parts + p] chain range p done.
+            // intra range p done, ev[parts + p] chain range p done.  The first
+            // chain range, beside most of the intra-chunk work, carries two
+            // slices per workgroup to leave that work more CUs; the later ones
+            // one (at the 32K-token KDA shape: inference forward 0.951 ms,
+            // against 0.960 with one slice and 0.985 with two throughout; the
+            // two-slice chain steps slower beside the intra-chunk kernel).
             float* carry = reinterpret_cast<float*>(static_cast<char*>(ws) + need - align_up(carry_bytes(desc)));
             int64_t lo[kMaxParts], hi[kMaxParts];
             for (int p = 0; p < parts; ++p) cut_range(NC, parts, p, false, &lo[p], &hi[p]);
@@ -416,7 +424,7 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
                 gdr::prof_before(s);
                 e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w,
                                           p == 0 ? S0 : carry, p == parts - 1 ? ST : carry, o, true,
-                                          gdr::ChunkRange{lo[p], hi[p] - lo[p]}, s);
+                                          p == 0, gdr::ChunkRange{lo[p], hi[p] - lo[p]}, s);
                 gdr::prof_after(st_name, s);
                 if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
                 if (hipEventRecord(aux->ev[parts + p], s) != hipSuccess ||
@@ -439,7 +447,7 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     }
     gdr::prof_before(s);
     e = gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o,
-                              train || cler, gdr::ChunkRange{0, NC}, s);
+                              train || cler, wide, gdr::ChunkRange{0, NC}, s);
     gdr::prof_after(st_name, s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     if (!in_f32 && NC > 0) {
@@ -532,8 +540,14 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     if (NC > 0 && recompute) {
         GDR_STEP("intra_bwd", gdr::launch_intra(int(D), gate, in_f32, 1, B, T, int(H), NC, q, k, v, beta,
                                                 alpha, nullptr, nullptr, w, pro, gdr::ChunkRange{0, NC}, s));
+        bool wide = false;
+        if (!in_f32) {
+            std::lock_guard<std::mutex> lock(g_aux_mu);
+            const Aux* aux = aux_stream();
+            wide = aux && B * H * (D / 16) > aux->cus;
+        }
         GDR_STEP("state_fwd_save", gdr::launch_state_fwd(int(D), in_f32, out_f32, B, T, int(H), NC,
-                                                         desc->scale, w, S0, nullptr, nullptr, true,
+                                                         desc->scale, w, S0, nullptr, nullptr, true, wide,
                                                          gdr::ChunkRange{0, NC}, s));
     }
     // error routing: dh reaches U inside the reverse state pass and beta and the

@@ -82,10 +82,13 @@ hipError_t launch_intra(int D, int gate, bool in_f32, int mode, int64_t B, int64
                         const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream);
 
 // cr: the chunks this launch carries the state through (fp16 operands only; the
-// fp32-operand pass always runs the whole sequence and ignores it).
+// fp32-operand pass always runs the whole sequence and ignores it).  wide: two
+// state slices per workgroup (fp16 operands only), for a pass that shares the
+// chip with other kernels or has more slices than there are CUs.
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
-                            float* ST, void* o, bool save_for_backward, ChunkRange cr, hipStream_t stream);
+                            float* ST, void* o, bool save_for_backward, bool wide, ChunkRange cr,
+                            hipStream_t stream);
 
 // dh_cler (NULL = none): gradient at the hidden stream of the error-routing
 // epilogue, which adds lam * dh / beta to dU.

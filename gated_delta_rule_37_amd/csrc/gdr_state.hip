@@ -355,27 +355,28 @@ __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_
 // c from its buffer with conflict-free 16-byte LDS reads.
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, int NSW>
 struct ChainStage {
     static constexpr int MAT = CHUNK * D * 2;  // [64][D] fp16
     static constexpr int W = 0;
     static constexpr int KBT = MAT;
-    static constexpr int UT = 2 * MAT;          // this slice's four 16x16 tiles of Ut
-    static constexpr int GAM = UT + 2048;       // D fp32 in a 1 KiB slot
+    static constexpr int UT = 2 * MAT;          // per slice, its four 16x16 tiles of Ut (2 KiB)
+    static constexpr int GAM = UT + 2048 * NSW; // D fp32 in a 1 KiB slot
     static constexpr int BYTES = GAM + 1024;
-    static constexpr int ND0 = MAT / 2048 + 2 + 1;     // copies per chunk of loader wave 0
-    static constexpr int NDP = MAT / 2048;             // copies per chunk of loader waves 1-3
-    static constexpr int NSL = D / 16;
-    static constexpr int QL = MAT / NSL / 128;         // 128-byte lines per slice of one array
-    static constexpr int NT = (3 * QL + 1 + 63) / 64;  // touch copies per chunk
+    static constexpr int ND0 = MAT / 2048 + 2 * NSW + 1;  // copies per chunk of loader wave 0
+    static constexpr int NDP = MAT / 2048;                // copies per chunk of loader waves 1-3
+    static constexpr int NWH = D / 16 / NSW;              // workgroups per head
+    static constexpr int QL = MAT / NWH / 128;            // 128-byte lines per workgroup of one array
+    static constexpr int NT = (3 * QL + 1 + 63) / 64;     // touch copies per chunk
 };
 
-// Chunk ch's operands for slice `slice` into `dst`, in four parts, one per
-// loader wave: PART 0 the first half of W, Ut and gamma; PART 1 the second half
+// Chunk ch's operands for the NSW slices of workgroup `member` of its head
+// (slices member*NSW ..) into `dst`, in four parts, one per loader wave: PART 0
+// the first half of W, the slices' Ut tiles and gamma; PART 1 the second half
 // of W; PARTs 2 and 3 the halves of Kb^T.
-template <int D, int PART>
-__device__ __forceinline__ void stage_chain(lds_char* dst, const ChunkWs& ws, int64_t ch, int slice, int lane) {
-    using L = ChainStage<D>;
+template <int D, int NSW, int PART>
+__device__ __forceinline__ void stage_chain(lds_char* dst, const ChunkWs& ws, int64_t ch, int member, int lane) {
+    using L = ChainStage<D, NSW>;
     constexpr int HALF = L::MAT / 2;
     if constexpr (PART == 1) {
         copy_block_to_lds<HALF / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT + HALF, dst + L::W + HALF, lane);
@@ -389,29 +390,32 @@ __device__ __forceinline__ void stage_chain(lds_char* dst, const ChunkWs& ws, in
         // Ut tiles (rt, slice), rt = 0..3, 512 bytes each: two tiles per copy
         const char* U = static_cast<const char*>(ws.Ut) + ch * L::MAT;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rt = 2 * i + (lane >> 5);
-            copy16_to_lds(U + (rt * (D / 16) + slice) * 512 + (lane & 31) * 16, dst + L::UT + i * 1024);
-        }
+        for (int sl = 0; sl < NSW; ++sl)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rt = 2 * i + (lane >> 5);
+                copy16_to_lds(U + (rt * (D / 16) + member * NSW + sl) * 512 + (lane & 31) * 16,
+                              dst + L::UT + sl * 2048 + i * 1024);
+            }
         // gamma: D floats; lanes past the end re-read the first piece into the slot's tail
         const char* G = reinterpret_cast<const char*>(ws.gam + ch * D);
         copy16_to_lds(G + (lane < D / 4 ? lane : 0) * 16, dst + L::GAM);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void stage_chain_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int slice,
+template <int D, int NSW>
+__device__ __forceinline__ void stage_chain_part(int part, lds_char* dst, const ChunkWs& ws, int64_t ch, int member,
                                                  int lane) {
-    if (part == 0) stage_chain<D, 0>(dst, ws, ch, slice, lane);
-    else if (part == 1) stage_chain<D, 1>(dst, ws, ch, slice, lane);
-    else if (part == 2) stage_chain<D, 2>(dst, ws, ch, slice, lane);
-    else stage_chain<D, 3>(dst, ws, ch, slice, lane);
+    if (part == 0) stage_chain<D, NSW, 0>(dst, ws, ch, member, lane);
+    else if (part == 1) stage_chain<D, NSW, 1>(dst, ws, ch, member, lane);
+    else if (part == 2) stage_chain<D, NSW, 2>(dst, ws, ch, member, lane);
+    else stage_chain<D, NSW, 3>(dst, ws, ch, member, lane);
 }
 
-// One dword of each 128-byte line of this slice's share of chunk ch.
-template <int D>
+// One dword of each 128-byte line of this workgroup's share of chunk ch.
+template <int D, int NSW>
 __device__ __forceinline__ void touch_chain(lds_char* dummy, const ChunkWs& ws, int64_t ch, int slice, int lane) {
-    using L = ChainStage<D>;
+    using L = ChainStage<D, NSW>;
     constexpr int QL = L::QL;
 #pragma unroll
     for (int i = 0; i < L::NT; ++i) {
@@ -425,9 +429,9 @@ __device__ __forceinline__ void touch_chain(lds_char* dummy, const ChunkWs& ws, 
     }
 }
 
-template <int D>
-__device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const lds_char* src, int wid, int lane) {
-    using L = ChainStage<D>;
+template <int D, int NSW>
+__device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const lds_char* src, int sl, int wid, int lane) {
+    using L = ChainStage<D, NSW>;
     constexpr int SRT = StateCfg<D, false>::SRT;
 #pragma unroll
     for (int kq = 0; kq < D / 32; ++kq)
@@ -441,7 +445,7 @@ __device__ __forceinline__ void chain_frags(ChunkFrags<D, false>& f, const lds_c
 #pragma unroll
         for (int e = 0; e < 4; ++e) f.gam[m][e] = g[e];
     }
-    const half4 u = *reinterpret_cast<const __attribute__((address_space(3))) half4*>(src + L::UT + (wid * 256 + lane * 4) * 2);
+    const half4 u = *reinterpret_cast<const __attribute__((address_space(3))) half4*>(src + L::UT + sl * 2048 + (wid * 256 + lane * 4) * 2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) f.ut[e] = u[e];
 }
@@ -458,46 +462,50 @@ __device__ __forceinline__ void wait_outstanding(int n) {
     else wait_vmcnt<0>();
 }
 
-template <int D>
-__global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
-                                                          const float* S0, float* ST, ChunkRange cr) {
+// NSW slices per workgroup: 4*NSW compute waves (four per slice, slice sl =
+// wave / 4) and four loader waves that stage each chunk's W, Kb^T and gamma once
+// for all of them.  With two slices a head's state pass holds half as many CUs,
+// which the intra-chunk kernels running beside it use.
+template <int D, int NSW>
+__global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_chain_kernel(int64_t T, int H, int64_t NC, ChunkWs ws,
+                                                                         const float* S0, float* ST, ChunkRange cr) {
     using Cfg = StateCfg<D, false>;
     using OpT = _Float16;
-    using L = ChainStage<D>;
-    constexpr int NSL = Cfg::NSL, SRT = Cfg::SRT, LDS_S = Cfg::LDS_S;
+    using L = ChainStage<D, NSW>;
+    constexpr int SRT = Cfg::SRT, LDS_S = Cfg::LDS_S;
     constexpr int PF = 8;
 
-    __shared__ __attribute__((aligned(16))) OpT s_S[Cfg::NS * LDS_S];
-    __shared__ __attribute__((aligned(16))) OpT s_U[Cfg::NS * Cfg::LDS_U];
+    __shared__ __attribute__((aligned(16))) OpT s_S[NSW][Cfg::NS * LDS_S];
+    __shared__ __attribute__((aligned(16))) OpT s_U[NSW][Cfg::NS * Cfg::LDS_U];
     __shared__ __attribute__((aligned(1024))) char stage[3][L::BYTES];
     __shared__ __attribute__((aligned(16))) char dummy[L::NT * 256];
 
     const int64_t nblk = gridDim.x;
     int64_t lid = blockIdx.x;
     if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-    const int64_t bh = lid / NSL;
-    const int slice = static_cast<int>(lid % NSL);
-    const int j0 = slice * Cfg::NS;
+    const int64_t bh = lid / L::NWH;
+    const int member = static_cast<int>(lid % L::NWH);
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     lds_char* const sbuf = (lds_char*)&stage[0][0];
     lds_char* const sdummy = (lds_char*)&dummy[0];
     const int64_t lo = cr.lo, hi = cr.lo + cr.n;  // chunks lo .. hi-1 (the state enters at lo)
 
-    if (wid >= 4) {
-        // Loaders (waves 4-7, one part each).  Two barriers per step, like the
-        // compute waves; they never fence, so their copies stay in flight
-        // across the first one.  Wave 4 also warms the L2 (also past the range:
-        // the next range's first chunks).
-        const int part = wid - 4;
+    if (wave >= 4 * NSW) {
+        // Loaders (the last four waves, one part each).  Two barriers per step,
+        // like the compute waves; they never fence, so their copies stay in
+        // flight across the first one.  The first loader also warms the L2
+        // (also past the range: the next range's first chunks).
+        const int part = wave - 4 * NSW;
         const bool w4 = part == 0;
-        if (cr.n > 0) stage_chain_part<D>(part, sbuf, ws, bh * NC + lo, slice, lane);
-        if (cr.n > 1) stage_chain_part<D>(part, sbuf + L::BYTES, ws, bh * NC + lo + 1, slice, lane);
+        if (cr.n > 0) stage_chain_part<D, NSW>(part, sbuf, ws, bh * NC + lo, member, lane);
+        if (cr.n > 1) stage_chain_part<D, NSW>(part, sbuf + L::BYTES, ws, bh * NC + lo + 1, member, lane);
         if (w4) {
 #pragma unroll 1
-            for (int64_t c = lo + 2; c < lo + PF && c < NC; ++c) touch_chain<D>(sdummy, ws, bh * NC + c, slice, lane);
+            for (int64_t c = lo + 2; c < lo + PF && c < NC; ++c)
+                touch_chain<D, NSW>(sdummy, ws, bh * NC + c, member, lane);
         }
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
@@ -505,8 +513,8 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
 #pragma unroll 1
         for (int64_t c = lo; c < hi; ++c) {
             const bool st2 = c + 2 < hi, tpf = w4 && c + PF < NC;
-            if (st2) stage_chain_part<D>(part, sbuf + nb * L::BYTES, ws, bh * NC + c + 2, slice, lane);
-            if (tpf) touch_chain<D>(sdummy, ws, bh * NC + c + PF, slice, lane);
+            if (st2) stage_chain_part<D, NSW>(part, sbuf + nb * L::BYTES, ws, bh * NC + c + 2, member, lane);
+            if (tpf) touch_chain<D, NSW>(sdummy, ws, bh * NC + c + PF, member, lane);
             nb = nb == 2 ? 0 : nb + 1;
             __builtin_amdgcn_s_barrier();
             // this wave's copies of chunk c+1 must have landed; later ones may stay in flight
@@ -524,13 +532,17 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
         return;
     }
 
+    const int sl = wave >> 2, wid = wave & 3;
+    const int j0 = (member * NSW + sl) * Cfg::NS;
+    OpT* const sS = &s_S[sl][0];
+    OpT* const sU = &s_U[sl][0];
     float4v S[SRT];
 #pragma unroll
     for (int m = 0; m < SRT; ++m) {
         const int d0 = wid * (D / 4) + 16 * m + 4 * g4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[m][e] = S0 ? S0[(bh * D + d0 + e) * D + j0 + l16] : 0.f;
-        st4<OpT>(s_S + l16 * LDS_S + d0, S[m]);
+        st4<OpT>(sS + l16 * LDS_S + d0, S[m]);
     }
     __syncthreads();
 
@@ -538,10 +550,10 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
 #pragma unroll 1
     for (int64_t c = lo; c < hi; ++c) {
         ChunkFrags<D, false> f;
-        chain_frags<D>(f, sbuf + cb * L::BYTES, wid, lane);
+        chain_frags<D, NSW>(f, sbuf + cb * L::BYTES, sl, wid, lane);
         cb = cb == 2 ? 0 : cb + 1;
-        state_step<D, false, false, true, false>(f, c, T, H, b, h, bh, NC, j0, wid, l16, g4, 1.f, ws, S, s_S,
-                                                 s_U, nullptr);
+        state_step<D, false, false, true, false>(f, c, T, H, b, h, bh, NC, j0, wid, l16, g4, 1.f, ws, S, sS, sU,
+                                                 nullptr);
     }
 
     if (ST) {
@@ -557,14 +569,18 @@ __global__ __launch_bounds__(512) void state_chain_kernel(int64_t T, int H, int6
 template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float scale,
                                  const ChunkWs& ws, const float* S0, float* ST, void* o, bool save,
-                                 ChunkRange cr, hipStream_t stream) {
+                                 bool wide, ChunkRange cr, hipStream_t stream) {
     const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
     if constexpr (!IN_F32) {
         // fp16 operands: the chain pass always saves the chunk-start states and U;
         // the output is produced by output_kernel
-        hipLaunchKernelGGL((state_chain_kernel<D>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC, ws, S0,
-                           ST, cr);
+        if (wide)
+            hipLaunchKernelGGL((state_chain_kernel<D, 2>), dim3((unsigned)(nblk / 2)), dim3(768), 0, stream, T, H,
+                               NC, ws, S0, ST, cr);
+        else
+            hipLaunchKernelGGL((state_chain_kernel<D, 1>), dim3((unsigned)nblk), dim3(512), 0, stream, T, H, NC,
+                               ws, S0, ST, cr);
         return hipGetLastError();
     }
     if (save && o)
@@ -581,21 +597,21 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
-                            float* ST, void* o, bool save_for_backward, ChunkRange cr, hipStream_t stream) {
+                            float* ST, void* o, bool save_for_backward, bool wide, ChunkRange cr, hipStream_t stream) {
     if (D == 64) {
         if (in_f32) {
-            if (out_f32) return launch_state_t<64, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
-            return launch_state_t<64, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+            if (out_f32) return launch_state_t<64, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
+            return launch_state_t<64, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
         }
-        if (out_f32) return launch_state_t<64, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
-        return launch_state_t<64, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+        if (out_f32) return launch_state_t<64, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
+        return launch_state_t<64, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
     }
     if (in_f32) {
-        if (out_f32) return launch_state_t<128, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
-        return launch_state_t<128, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+        if (out_f32) return launch_state_t<128, true, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
+        return launch_state_t<128, true, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
     }
-    if (out_f32) return launch_state_t<128, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
-    return launch_state_t<128, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, cr, stream);
+    if (out_f32) return launch_state_t<128, false, true>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
+    return launch_state_t<128, false, false>(B, T, H, NC, scale, ws, S0, ST, o, save_for_backward, wide, cr, stream);
 }
 
 }  // namespace gdr

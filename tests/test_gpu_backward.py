@@ -96,6 +96,21 @@ def test_backward_ragged_lengths(T):
     assert max(errs.values()) < 2e-3, errs
 
 
+@pytest.mark.parametrize("d,B,H", [(64, 5, 14), (128, 3, 11)])
+def test_backward_more_state_slices_than_cus(d, B, H):
+    """The recomputing backward where the forward chain it re-runs has more
+    16-column state slices than the chip has CUs (two slices per workgroup);
+    ragged T = 130, initial state and final-state gradient."""
+    announce("backward two-slice chain d=%d B=%d H=%d" % (d, B, H))
+    inp = gdr_inputs.make(B=B, T=130, H=H, d=d, gate="channel", dtype="bf16", seed=350 + d, s0=True, bwd=True)
+    dST = (0.1 * np.random.default_rng(351).standard_normal((B, H, d, d))).astype(np.float32)
+    t = inputs_to_dev(inp, "bf16")
+    g = gpu_backward(t, to_dev(dST))
+    errs = compare(inp, g, dST)
+    report(**errs)
+    assert max(errs.values()) < 2e-3, errs
+
+
 def test_backward_empty_sequence_passes_state_gradient():
     announce("backward T=0")
     inp = gdr_inputs.make(B=1, T=0, H=2, d=64, gate="channel", dtype="bf16", seed=330, s0=True, bwd=True)

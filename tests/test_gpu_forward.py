@@ -61,6 +61,18 @@ def test_forward_ragged_lengths(T):
     assert eo < 2e-3 and es < 2e-3, (eo, es)
 
 
+@pytest.mark.parametrize("d,B,H", [(64, 5, 14), (128, 3, 11)])
+def test_forward_more_state_slices_than_cus(d, B, H):
+    """More 16-column state slices (B*H*d/16 = 280 and 264) than the chip has
+    CUs (256): the chain pass then carries two slices per workgroup.  Ragged
+    T = 130, with an initial state."""
+    announce("forward two-slice chain d=%d B=%d H=%d" % (d, B, H))
+    inp = gdr_inputs.make(B=B, T=130, H=H, d=d, gate="channel", dtype="bf16", seed=250 + d, s0=True)
+    eo, es = check(inp, "bf16")
+    report(o=eo, S=es)
+    assert eo < 2e-3 and es < 2e-3, (eo, es)
+
+
 def test_forward_empty_sequence_copies_state():
     announce("forward T=0")
     inp = gdr_inputs.make(B=2, T=0, H=2, d=64, gate="channel", dtype="bf16", seed=210, s0=True)
