@@ -1253,14 +1253,28 @@ __global__ __launch_bounds__(256) void clvr_dlam_partial(int64_t BT, int HD, int
     float s[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) s[e] = 0.f;
-#pragma unroll 4
-    for (int64_t t = t0; t < t1; ++t) {
-        const float4v rd = *reinterpret_cast<const float4v*>(dh + t * HD + c0);
-        const float4v rv = *reinterpret_cast<const float4v*>(v + t * HD + c0);
-        const InT* pd = reinterpret_cast<const InT*>(&rd);
-        const InT* pv = reinterpret_cast<const InT*>(&rv);
+    // rows in groups of RB: every load of a group is issued before the first
+    // product (rows past the end re-read the last row and are masked after),
+    // and the products are added in row order
+    constexpr int RB = 8;
+#pragma unroll 1
+    for (int64_t t = t0; t < t1; t += RB) {
+        float4v rd[RB], rv[RB];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s[e] = __builtin_fmaf(to_f32(pd[e]), to_f32(pv[e]), s[e]);
+        for (int r = 0; r < RB; ++r) {
+            const int64_t tr = t + r < t1 ? t + r : t1 - 1;
+            rd[r] = *reinterpret_cast<const float4v*>(dh + tr * HD + c0);
+            rv[r] = *reinterpret_cast<const float4v*>(v + tr * HD + c0);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const InT* pd = reinterpret_cast<const InT*>(&rd[r]);
+            const InT* pv = reinterpret_cast<const InT*>(&rv[r]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                s[e] = t + r < t1 ? __builtin_fmaf(to_f32(pd[e]), to_f32(pv[e]), s[e]) : s[e];
+        }
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) partial[seg * HD + c0 + e] = s[e];
@@ -1274,8 +1288,23 @@ __global__ __launch_bounds__(256) void clvr_dlam_final(int HD, int64_t nseg, con
     const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
     const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
     float s = 0.f;
-    if (c < HD)
-        for (int64_t seg = g; seg < nseg; seg += 4) s += partial[seg * HD + c];
+    if (c < HD) {
+        // segments g, g + 4, ... added in that order, eight loads in flight at a
+        // time (indices past the end re-read the last segment and are masked)
+        constexpr int SB = 8;
+#pragma unroll 1
+        for (int64_t seg = g; seg < nseg; seg += 4 * SB) {
+            float x[SB];
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int64_t sg = seg + 4 * u < nseg ? seg + 4 * u : nseg - 1;
+                x[u] = partial[sg * HD + c];
+            }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < SB; ++u) s = seg + 4 * u < nseg ? s + x[u] : s;
+        }
+    }
     red[g][cl] = s;
     __syncthreads();
     if (g == 0 && c < HD) dlam[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
