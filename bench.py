@@ -84,16 +84,17 @@ PER_TH_BYTES = {
     "intra_bwd": 3 * 256 + 4 + 512,                    # q,k,v,beta,alpha read
     "state_fwd_save": 0,                               # intermediates only
     "state_bwd": 256,                                  # dO read
-    "grad_lin": 256 + 4 + 512 + 256 + 256 + 256 + 256 + 4,  # k,beta,alpha,v,dO,dh read; dv,dbeta written
-    "grad_gate": 2 * 256 + 512 + 2 * 256 + 512,        # q,k,alpha read; dq,dk,dalpha written
-    # both gradient kernels in one launch (value route): the two rows above
+    # both gradient stages in one launch: first k,beta,alpha,v,dO,dh read and dv,dbeta
+    # written; then q,k,alpha read and dq,dk,dalpha written
     "grads": (256 + 4 + 512 + 256 + 256 + 256 + 256 + 4) + (2 * 256 + 512 + 2 * 256 + 512),
     "clvr_dlam": 2 * 256,                              # dh, v read
     # error-routing epilogue (CLER-H) training step
     "output_cler": 256 + 2 * 256 + 4,                  # o written; h read+write; beta read
     "cler_mt": 256,                                    # dh read
     "state_bwd_cler": 2 * 256 + 4,                     # dO, dh, beta read
-    "cler_post": 256 + 4,                              # dh, beta read
+    # the error route's gradient kernel: both gradient stages and the write errors' terms
+    # (dh, beta read once more)
+    "grads_cler": (256 + 4 + 512 + 256 + 256 + 256 + 256 + 4) + (2 * 256 + 512 + 2 * 256 + 512) + 256 + 4,
     # output-gate epilogue (bf16 o, g, y, dy, dO, dg)
     "gate_fwd": 3 * 256,                               # o, g read; y written
     "gate_bwd": 5 * 256,                               # o, g, dy read; dO, dg written
@@ -106,13 +107,14 @@ KERNEL_SOURCES = {
     "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"], "intra_train": ["gdr_intra.hip"],
     "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"], "state_train": ["gdr_state.hip"],
     "output": ["gdr_output.hip"], "output_cler": ["gdr_output.hip", "gdr_cler.hpp"],
-    "cler_mt": ["gdr_cler.hip", "gdr_cler.hpp"], "cler_post": ["gdr_cler.hip", "gdr_cler.hpp"],
+    "cler_mt": ["gdr_cler.hip", "gdr_cler.hpp"],
     "state_bwd_cler": ["gdr_bwd_state.hip"],
     "gate_fwd": ["gdr_gate.hip"], "gate_bwd": ["gdr_gate.hip"],
-    "intra_train_pro": ["gdr_intra.hip"], "grad_lin_pro": ["gdr_bwd_grad.hip"], "grad_gate_pro": ["gdr_bwd_grad.hip"],
+    "intra_train_pro": ["gdr_intra.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
-    "grad_lin": ["gdr_bwd_grad.hip"], "grad_gate": ["gdr_bwd_grad.hip"], "clvr_dlam": ["gdr_bwd_grad.hip"],
+    "clvr_dlam": ["gdr_bwd_grad.hip"],
     "grads": ["gdr_bwd_grad.hip"], "grads_pro": ["gdr_bwd_grad.hip"],
+    "grads_cler": ["gdr_bwd_grad.hip", "gdr_cler.hpp"],
     "decode": ["gdr_decode.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kda_t32k.txt")
@@ -299,7 +301,7 @@ def main():
         torch.cuda.synchronize()
         ck = {}
         for n, (c, ms) in timer.end().items():
-            if n in ("output_cler", "cler_mt", "state_bwd_cler", "cler_post"):
+            if n in ("output_cler", "cler_mt", "state_bwd_cler", "grads_cler"):
                 us = 1e3 * ms / c
                 gbs = kbytes[n] * args.steps / c / (us * 1e-6) / 1e9
                 ck[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}

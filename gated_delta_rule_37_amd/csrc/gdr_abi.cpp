@@ -562,23 +562,13 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
         reinterpret_cast<float*>(static_cast<char*>(ws) + chunk_bytes + align_up(dlam_partial_bytes(desc)));
     // per-chunk gradient kernels of one chunk range, on stream `gs`
     auto grads = [&](gdr::ChunkRange cr, hipStream_t gs) -> gdr_status {
-        // both routes add lam * dh to dv: the value route through v itself,
-        // the error route through e = v - ...
-        if (!cler) {  // nothing between the two: one kernel runs both per chunk
-            GDR_STEP_ON(gs, "grads", gdr::launch_grads(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
-                                                       q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dq, dk, dv,
-                                                       dbeta, dalpha, w, pro, cr, gs));
-            return GDR_OK;
-        }
-        GDR_STEP_ON(gs, "grad_lin", gdr::launch_grad_lin(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale,
-                                                         q, k, v, beta_eff, alpha, dO, dh_clvr, clvr_scale, dv, dbeta,
-                                                         w, pro, cr, gs));
-        if (cler)
-            GDR_STEP_ON(gs, "cler_post", gdr::launch_cler_post(int(D), in_f32, B, T, int(H), NC, w, beta_eff,
-                                                               clvr_scale, dh_clvr, dclvr_scale ? partial : nullptr,
-                                                               cr, gs));
-        GDR_STEP_ON(gs, "grad_gate", gdr::launch_grad_gate(int(D), gate, in_f32, out_f32, B, T, int(H), NC, q, k,
-                                                           alpha, dq, dk, dalpha, w, pro, cr, gs));
+        // both routes add lam * dh to dv: the value route through v itself, the
+        // error route through e = v - ...; the error route's own terms run
+        // between the two gradient stages, in the same kernel
+        GDR_STEP_ON(gs, cler ? "grads_cler" : "grads",
+                    gdr::launch_grads(int(D), gate, in_f32, out_f32, B, T, int(H), NC, desc->scale, q, k, v, beta_eff,
+                                      alpha, dO, dh_clvr, clvr_scale, dq, dk, dv, dbeta, dalpha, w, pro, cr, cler,
+                                      cler && dclvr_scale ? partial : nullptr, gs));
         return GDR_OK;
     };
     const char* sb_name = cler ? "state_bwd_cler" : "state_bwd";

@@ -11,10 +11,12 @@
 //   dT  = dU V^T + dW Kt^T     dV = T^T dU              dKt = T^T dW
 //   Y   = N^T dT               dbeta = diag(Y) + rowsum(dL . P)
 //   dL  = -strict_tril(Y T^T)  dP = diag(beta) dL
-// grad_lin_kernel computes all of that.  grad_gate_kernel then takes dA and dP
-// back through the decay-factored products (the same block references as the
-// forward), adds the Qt, Kt, Kb and gamma terms, and turns the gradient with
-// respect to the in-chunk log-decay cumsum into dalpha by a reverse cumsum.
+// The first stage (grad_lin_body) computes all of that.  The second
+// (grad_gate_body) takes dA and dP back through the decay-factored products
+// (the same block references as the forward), adds the Qt, Kt, Kb and gamma
+// terms, and turns the gradient with respect to the in-chunk log-decay cumsum
+// into dalpha by a reverse cumsum.  One workgroup runs both for a chunk.
+#include "gdr_cler.hpp"
 #include "gdr_common.hpp"
 #include "gdr_launch.hpp"
 
@@ -69,8 +71,8 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
     }
 }
 
-// The bodies of the two gradient kernels are device functions on a caller-
-// provided LDS buffer, so that one kernel can run both for a chunk.
+// The two gradient stages are device functions on a caller-provided LDS
+// buffer, which grads_kernel runs one after the other for a chunk.
 template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
 __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, float scale,
                                               const void* __restrict__ k_, const void* __restrict__ v_,
@@ -534,70 +536,6 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
     }
 }
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
-__global__ __launch_bounds__(4 * D) void grad_lin_kernel(int64_t T, int H, int64_t NC, float scale,
-                                                         const void* __restrict__ k_, const void* __restrict__ v_,
-                                                         const float* __restrict__ beta,
-                                                         const float* __restrict__ alpha,
-                                                         const void* __restrict__ dO_, const void* __restrict__ dh_,
-                                                         const float* __restrict__ lam, void* __restrict__ dv_,
-                                                         float* __restrict__ dbeta, ChunkWs ws, int pro,
-                                                         ChunkRange cr) {
-    __shared__ __attribute__((aligned(16))) char smem[GLinLayout<D, IN_F32>::BYTES];
-    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_, dbeta,
-                                                 ws, pro, cr, smem);
-}
-
-template <int D, int GATE, bool IN_F32, bool OUT_F32>
-static hipError_t launch_grad_lin_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* k,
-                                    const void* v, const float* beta, const float* alpha, const void* dO,
-                                    const void* dh, const float* lam, void* dv, float* dbeta, const ChunkWs& ws,
-                                    int pro, ChunkRange cr, hipStream_t stream) {
-    const int64_t nblk = B * H * cr.n;
-    if (nblk == 0) return hipSuccess;
-    if (pro)
-        hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr);
-    else
-        hipLaunchKernelGGL((grad_lin_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr);
-    return hipGetLastError();
-}
-
-template <int D, int GATE>
-static hipError_t launch_grad_lin_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
-                                    float scale, const void* k, const void* v, const float* beta,
-                                    const float* alpha, const void* dO, const void* dh, const float* lam,
-                                    void* dv, float* dbeta, const ChunkWs& ws, int pro, ChunkRange cr,
-                                    hipStream_t stream) {
-    if (in_f32) {
-        if constexpr (D == 64) {
-            if (out_f32) return launch_grad_lin_t<D, GATE, true, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
-            return launch_grad_lin_t<D, GATE, true, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
-        }
-        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
-    }
-    if (out_f32) return launch_grad_lin_t<D, GATE, false, true>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
-    return launch_grad_lin_t<D, GATE, false, false>(B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream);
-}
-
-hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
-                           int64_t NC, float scale, const void* q, const void* k, const void* v,
-                           const float* beta, const float* alpha, const void* dO,
-                           const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
-    (void)q;
-#define GL_ARGS in_f32, out_f32, B, T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, stream
-    if (D == 64) {
-        if (gate == GATE_NONE) return launch_grad_lin_g<64, GATE_NONE>(GL_ARGS);
-        if (gate == GATE_SCALAR) return launch_grad_lin_g<64, GATE_SCALAR>(GL_ARGS);
-        return launch_grad_lin_g<64, GATE_CHANNEL>(GL_ARGS);
-    }
-    if (gate == GATE_NONE) return launch_grad_lin_g<128, GATE_NONE>(GL_ARGS);
-    if (gate == GATE_SCALAR) return launch_grad_lin_g<128, GATE_SCALAR>(GL_ARGS);
-    return launch_grad_lin_g<128, GATE_CHANNEL>(GL_ARGS);
-#undef GL_ARGS
-}
 
 }  // namespace gdr
 
@@ -1100,21 +1038,13 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     }
 }
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
-__global__ __launch_bounds__(4 * D) void grad_gate_kernel(int64_t T, int H, int64_t NC,
-                                                          const void* __restrict__ q_, const void* __restrict__ k_,
-                                                          const float* __restrict__ alpha, void* __restrict__ dq_,
-                                                          void* __restrict__ dk_, float* __restrict__ dalpha,
-                                                          ChunkWs ws, int pro, ChunkRange cr) {
-    __shared__ __attribute__((aligned(16))) char smem[GGateLayout<D, IN_F32>::BYTES];
-    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr, smem);
-}
-
-// Both gradient kernels for one chunk in one workgroup (no epilogue between
-// them): the partials grad_lin writes are read back by the same workgroup,
-// from the L2, after a barrier that makes them visible; the LDS buffer is
-// shared.
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+// Both gradient stages for one chunk in one workgroup: the partials grad_lin
+// writes are read back by the same workgroup, from the L2, after a barrier that
+// makes them visible; the LDS buffer is shared.  With the error-routing
+// epilogue (CLER) the write errors' own terms (cler_post_body, which edits the
+// dKt and dP partials and writes the chunk's scale-gradient partial row) run
+// between the two, behind barriers of their own.
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool CLER>
 __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t NC, float scale,
                                                       const void* __restrict__ q_, const void* __restrict__ k_,
                                                       const void* __restrict__ v_, const float* __restrict__ beta,
@@ -1123,73 +1053,40 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
                                                       void* __restrict__ dq_, void* __restrict__ dk_,
                                                       void* __restrict__ dv_, float* __restrict__ dbeta,
                                                       float* __restrict__ dalpha, ChunkWs ws, int pro,
-                                                      ChunkRange cr) {
+                                                      ChunkRange cr, float* __restrict__ partial) {
     constexpr int LB = GLinLayout<D, IN_F32>::BYTES, GB = GGateLayout<D, IN_F32>::BYTES;
+    static_assert(!CLER || ClerLayout<D, IN_F32>::POST_BYTES <= (LB > GB ? LB : GB), "LDS of the CLER terms");
     __shared__ __attribute__((aligned(16))) char smem[LB > GB ? LB : GB];
     grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_, dbeta,
                                                  ws, pro, cr, smem);
     __syncthreads();
+    if constexpr (CLER) {
+        cler_post_body<D, IN_F32, 4 * D>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
+        __syncthreads();
+    }
     grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr, smem);
 }
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32>
-static hipError_t launch_grad_gate_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
-                                     const float* alpha, void* dq, void* dk, float* dalpha, const ChunkWs& ws,
-                                     int pro, ChunkRange cr, hipStream_t stream) {
-    const int64_t nblk = B * H * cr.n;
-    if (nblk == 0) return hipSuccess;
-    if (pro)
-        hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, true>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
-    else
-        hipLaunchKernelGGL((grad_gate_kernel<D, GATE, IN_F32, OUT_F32, false>), dim3((unsigned)nblk), dim3(4 * D), 0,
-                           stream, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
-    return hipGetLastError();
-}
-
-template <int D, int GATE>
-static hipError_t launch_grad_gate_g(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
-                                     const void* q, const void* k, const float* alpha, void* dq, void* dk,
-                                     float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
-    if (in_f32) {
-        if constexpr (D == 64) {
-            if (out_f32) return launch_grad_gate_t<D, GATE, true, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
-            return launch_grad_gate_t<D, GATE, true, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
-        }
-        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
-    }
-    if (out_f32) return launch_grad_gate_t<D, GATE, false, true>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
-    return launch_grad_gate_t<D, GATE, false, false>(B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream);
-}
-
-hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
-                            int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream) {
-#define GG_ARGS in_f32, out_f32, B, T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr, stream
-    if (D == 64) {
-        if (gate == GATE_NONE) return launch_grad_gate_g<64, GATE_NONE>(GG_ARGS);
-        if (gate == GATE_SCALAR) return launch_grad_gate_g<64, GATE_SCALAR>(GG_ARGS);
-        return launch_grad_gate_g<64, GATE_CHANNEL>(GG_ARGS);
-    }
-    if (gate == GATE_NONE) return launch_grad_gate_g<128, GATE_NONE>(GG_ARGS);
-    if (gate == GATE_SCALAR) return launch_grad_gate_g<128, GATE_SCALAR>(GG_ARGS);
-    return launch_grad_gate_g<128, GATE_CHANNEL>(GG_ARGS);
-#undef GG_ARGS
-}
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grads_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* q,
                                  const void* k, const void* v, const float* beta, const float* alpha,
                                  const void* dO, const void* dh, const float* lam, void* dq, void* dk, void* dv,
                                  float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                                 hipStream_t stream) {
+                                 bool cler, float* partial, hipStream_t stream) {
     const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
-#define GDR_GRADS(P)                                                                                              \
-    hipLaunchKernelGGL((grads_kernel<D, GATE, IN_F32, OUT_F32, P>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, T, \
-                       H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr)
-    if (pro) GDR_GRADS(true);
-    else GDR_GRADS(false);
+#define GDR_GRADS(P, C)                                                                                              \
+    hipLaunchKernelGGL((grads_kernel<D, GATE, IN_F32, OUT_F32, P, C>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, \
+                       T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr,    \
+                       partial)
+    if (cler) {
+        if (pro) GDR_GRADS(true, true);
+        else GDR_GRADS(false, true);
+    } else {
+        if (pro) GDR_GRADS(true, false);
+        else GDR_GRADS(false, false);
+    }
 #undef GDR_GRADS
     return hipGetLastError();
 }
@@ -1199,8 +1096,9 @@ static hipError_t launch_grads_g(bool in_f32, bool out_f32, int64_t B, int64_t T
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, const void* dO, const void* dh, const float* lam, void* dq,
                                  void* dk, void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro,
-                                 ChunkRange cr, hipStream_t stream) {
-#define GDR_GR_ARGS B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, stream
+                                 ChunkRange cr, bool cler, float* partial, hipStream_t stream) {
+#define GDR_GR_ARGS B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, \
+                    cler, partial, stream
     if (in_f32) {
         if constexpr (D == 64) {
             if (out_f32) return launch_grads_t<D, GATE, true, true>(GDR_GR_ARGS);
@@ -1217,8 +1115,9 @@ hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, i
                         float scale, const void* q, const void* k, const void* v, const float* beta,
                         const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
                         void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                        hipStream_t stream) {
-#define GDR_GR_ARGS in_f32, out_f32, B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, stream
+                        bool cler, float* partial, hipStream_t stream) {
+#define GDR_GR_ARGS in_f32, out_f32, B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, \
+                    dalpha, ws, pro, cr, cler, partial, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grads_g<64, GATE_NONE>(GDR_GR_ARGS);
         if (gate == GATE_SCALAR) return launch_grads_g<64, GATE_SCALAR>(GDR_GR_ARGS);

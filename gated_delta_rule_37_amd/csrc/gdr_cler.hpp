@@ -13,6 +13,9 @@
 #pragma once
 
 #include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+#include <type_traits>
 
 namespace gdr {
 
@@ -32,6 +35,149 @@ __device__ __forceinline__ void cler_add8(InT* hrow, const float (&u)[8], const 
 #pragma unroll
     for (int e = 0; e < 8; ++e) hv[e] = __builtin_fmaf(lm[e], u[e] * ib, hv[e]);
     store8f(hrow, hv);
+}
+
+template <int D, bool IN_F32>
+struct ClerLayout {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    static constexpr int PAD = 16 / sizeof(OpT);
+    static constexpr int LDE = D + PAD;       // dE [64][D] row stride
+    static constexpr int LDT = CHUNK + PAD;   // [x][64] row stride (M^T, dE^T)
+    // the post-gradient terms: dE [64][LDE], then one [32] column-sum row per wave
+    static constexpr int COLRED = CHUNK * LDE * (int)sizeof(OpT);
+    static constexpr int POST_BYTES = COLRED + 8 * 32 * 4;  // up to eight waves
+};
+
+// Between the two gradient stages of a chunk (NT threads of its workgroup, on
+// an LDS buffer of ClerLayout::POST_BYTES): the write errors' own terms,
+// e = (V - Kt S) - M U:
+//   dKt -= dE S^T,   dP -= strict_tril(dE U^T),
+// and the scale gradient's partial row of this chunk, sum_t dh_t e_t, with
+// e = U / beta.
+template <int D, bool IN_F32, int NT>
+__device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                                               const float* __restrict__ beta, const float* __restrict__ lam,
+                                               const void* __restrict__ dh_, float* __restrict__ partial,
+                                               ChunkRange cr, char* smem) {
+    using Lc = ClerLayout<D, IN_F32>;
+    using OpT = typename Lc::OpT;
+    using InT = typename InType<IN_F32>::T;
+    constexpr int LDE = Lc::LDE, KQ = D / 32, NW = NT / 64, NPT = CHUNK * D / 8 / NT;
+    static_assert(NT % 256 == 0 && NW % KQ == 0 && CHUNK * D / 8 % NT == 0, "thread count");
+    OpT* sE = reinterpret_cast<OpT*>(smem);
+    float (*colred)[32] = reinterpret_cast<float (*)[32]>(smem + Lc::COLRED);
+
+    int64_t bh, c;
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int64_t nvalid64 = T - c * CHUNK;
+    const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
+    const OpT* U = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
+    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
+    const InT* dh = reinterpret_cast<const InT*>(dh_);
+
+    // pieces of U (fragment order) with the matching dh: dE rows into LDS and
+    // the per-column sums of dh . e.  A thread's columns are the same in every
+    // piece it takes (the fragment index advances by NW, a multiple of the
+    // 32-column steps per row).
+    float col[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) col[e] = 0.f;
+    int jcol = 0;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int p = i * NT + tid;
+        int pos, j;
+        frag_piece<D>(p, pos, j);
+        jcol = j;
+        float g[8], lm[8], u[8];
+        load_lam8(lam, static_cast<int64_t>(h) * D + j, lm);
+        if (pos < nvalid) {
+            const int64_t t = c * CHUNK + pos;
+            load8f(dh + ((b * T + t) * H + h) * D + j, g);
+            load8f(U + p * 8, u);
+            const float ib = 1.f / beta[(b * T + t) * H + h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) col[e] = __builtin_fmaf(g[e], u[e] * ib, col[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sE[pos * LDE + j + e] = static_cast<OpT>(lm[e] * g[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        col[e] += __shfl_xor(col[e], 1);
+        col[e] += __shfl_xor(col[e], 2);
+        col[e] += __shfl_xor(col[e], 4);
+        col[e] += __shfl_xor(col[e], 8);
+    }
+    if (l16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) colred[wid][(jcol & 31) + e] = col[e];
+    }
+    __syncthreads();
+    if (partial && tid < D) {
+        // column tid lies in 32-column step tid / 32, held by the waves w with w % KQ == step
+        const int step = tid >> 5;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            if (w % KQ == step) s += colred[w][tid & 31];
+        partial[(b * NC + c) * (static_cast<int64_t>(H) * D) + static_cast<int64_t>(h) * D + tid] = s;
+    }
+
+    // dKt -= dE S^T: wave w takes the state-row tiles dt = w, w + NW, ... for all
+    // four position tiles (S fragments read once)
+    OpT* gKt = static_cast<OpT*>(ws.gKt) + ch * CHUNK * D;
+#pragma unroll
+    for (int dt = wid; dt < D / 16; dt += NW) {
+        Frag<OpT> fs[KQ];
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) fs[kq].load(Ss + ((dt * KQ + kq) * 64 + lane) * 8);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                Frag<OpT> fe;
+                fe.load(sE + (16 * rt + l16) * LDE + 32 * kq + 8 * g4);
+                mma(fe, fs[kq], acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                OpT& gk = gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16];
+                gk = from_f32<OpT>(to_f32(gk) - acc[e]);
+            }
+        }
+    }
+    // dP -= strict_tril(dE U^T): wave w < 4 takes position-row tile w and the
+    // column tiles up to it
+    if (wid < 4) {
+        OpT* gP = static_cast<OpT*>(ws.gP) + ch * CHUNK * CHUNK;
+        const int at = wid;
+        for (int xt = 0; xt <= at; ++xt) {
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                Frag<OpT> fe, fu;
+                fe.load(sE + (16 * at + l16) * LDE + 32 * kq + 8 * g4);
+                fu.load(U + ((xt * KQ + kq) * 64 + lane) * 8);
+                mma(fe, fu, acc);
+            }
+            const int x = 16 * xt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = 16 * at + 4 * g4 + e;
+                if (x < a) gP[a * CHUNK + x] = from_f32<OpT>(to_f32(gP[a * CHUNK + x]) - acc[e]);
+            }
+        }
+    }
 }
 
 }  // namespace gdr

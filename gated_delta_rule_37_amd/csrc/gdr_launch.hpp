@@ -101,24 +101,16 @@ hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int
                             const void* dh_cler, const float* lam, const float* beta, bool wide, ChunkRange cr,
                             hipStream_t stream);
 
-hipError_t launch_grad_lin(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
-                           int64_t NC, float scale, const void* q, const void* k, const void* v,
-                           const float* beta, const float* alpha, const void* dO,
-                           const void* dh, const float* lam, void* dv, float* dbeta,
-                           const ChunkWs& ws, int pro, ChunkRange cr, hipStream_t stream);
-
-hipError_t launch_grad_gate(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,
-                            int64_t NC, const void* q, const void* k, const float* alpha, void* dq,
-                            void* dk, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                            hipStream_t stream);
-
-// Both gradient kernels of a chunk range in one launch, when no epilogue runs
-// between them: the arguments of launch_grad_lin and launch_grad_gate together.
+// The per-chunk gradients of a chunk range, both stages in one launch (one
+// workgroup per chunk-head).  cler: the error-routing epilogue's terms run
+// between the stages (dh, lam and beta as for the epilogue; partial, if not
+// NULL, receives one scale-gradient row per chunk, [B*NC][H*D] floats, for
+// launch_dlam_final).
 hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                         float scale, const void* q, const void* k, const void* v, const float* beta,
                         const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
                         void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                        hipStream_t stream);
+                        bool cler, float* partial, hipStream_t stream);
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);
@@ -127,16 +119,12 @@ hipError_t launch_dlam_final(int HD, int64_t nseg, const float* partial, float* 
 
 // Error-routing epilogue (CLER-H).  Forward from the saved U: h += lam * U / beta.
 // Backward: launch_cler_mt forms M^T dE (dE = lam dh) before the reverse state
-// pass; launch_cler_post adds the write errors' Kt and P terms to the gradient
-// workspace before the gate kernel and, with dlam, reduces one partial row per
-// chunk ([B*NC][H*D] floats) into dlam.
+// pass; the write errors' Kt and P terms and the scale-gradient rows are added
+// inside launch_grads (cler).
 hipError_t launch_cler_fwd(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                            const float* beta, const float* lam, void* h, hipStream_t stream);
 hipError_t launch_cler_mt(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                           const float* lam, const void* dh, hipStream_t stream);
-hipError_t launch_cler_post(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
-                            const float* beta, const float* lam, const void* dh, float* partial, ChunkRange cr,
-                            hipStream_t stream);
 
 // Output-gate epilogue y = sigmoid(g) * w * RMSNorm(o) per head (and its
 // backward, with dw reduced from one partial row per token range).
