@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int64_t BT, int H, int64_
     load_lam8(w, static_cast<int64_t>(h) * D + c0, wv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    constexpr int NB = 2;  // rows per round, loads first
+    constexpr int NB = 4;  // rows per round, loads first
     for (int64_t rb = r0 + rs; rb < r1; rb += NB * RPI) {
       float ovb[NB][8], gvb[NB][8], dyb[NB][8];
 #pragma unroll
@@ -161,13 +161,19 @@ template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_gate_t(bool bwd, int64_t BT, int H, const void* o, const void* g, const float* w,
                                 void* y, const void* dy, void* dO, void* dg, float* dw, float* partial,
                                 hipStream_t stream) {
+    if (!bwd) {
+        // the forward has no partial rows: finer token segments (shorter
+        // workgroups, a shorter tail) measured 84 against 87 us at 1024 against
+        // 256 segments on 32K tokens x 16 heads
+        const int64_t fseg = BT < 1024 ? (BT < 1 ? 1 : BT) : 1024;
+        const int64_t fper = (BT + fseg - 1) / fseg;
+        hipLaunchKernelGGL((gate_fwd_kernel<D, IN_F32, OUT_F32>), dim3((unsigned)H, (unsigned)fseg), dim3(256), 0,
+                           stream, BT, H, fper, o, g, w, y);
+        return hipGetLastError();
+    }
     const int64_t nseg = gate_segments(BT);
     const int64_t per = (BT + nseg - 1) / nseg;
     const dim3 grid((unsigned)H, (unsigned)nseg);
-    if (!bwd) {
-        hipLaunchKernelGGL((gate_fwd_kernel<D, IN_F32, OUT_F32>), grid, dim3(256), 0, stream, BT, H, per, o, g, w, y);
-        return hipGetLastError();
-    }
     hipLaunchKernelGGL((gate_bwd_kernel<D, IN_F32, OUT_F32>), grid, dim3(256), 0, stream, BT, H, per, o, g, w, dy,
                        dO, dg, dw ? partial : nullptr);
     hipError_t e = hipGetLastError();
