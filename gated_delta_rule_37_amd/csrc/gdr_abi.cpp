@@ -589,13 +589,16 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
             }
         } else {
             // reverse pass in `parts` ranges, last chunks first; the gradient
-            // kernels of each finished range run on the second stream
+            // kernels of each finished range run on the second stream.  Nothing
+            // runs beside the first range, so it keeps one slice per workgroup
+            // (its faster step; 2.63 against 2.645 ms per training step at the
+            // 32K-token KDA shape)
             for (int p = 0; p < parts; ++p) {
                 int64_t lo, hi;
                 cut_range(NC, parts, p, true, &lo, &hi);
                 GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO,
                                                         p == 0 ? dST : carry, p == parts - 1 ? dS0 : carry,
-                                                        dh_state, clvr_scale, beta_eff, wide,
+                                                        dh_state, clvr_scale, beta_eff, wide && p > 0,
                                                         gdr::ChunkRange{lo, hi - lo}, s));
                 if (hipEventRecord(aux->ev[p], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[p], 0) != hipSuccess)
                     return fail(GDR_ERR_DEVICE, "stream ordering failed");
