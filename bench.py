@@ -8,7 +8,11 @@ HBM before the timed region starts.  The decode step (256 sequences x 16 heads,
 256 MiB fp32 state, rotating over independent state sets so the 256 MB
 Infinity Cache cannot serve it) is timed in the same run and reported beside.
 
-Prints ONE JSON line (see the design doc for every field's definition).
+Prints ONE JSON line: metric, value (tokens/s), timing, config, plus `roofline`
+(the dominant kernel's algorithmic GB/s against the 8 TB/s HBM peak, with its
+measured traffic from the stored counter summary), `cpu_baseline` (the fp64
+oracle on a bounded sample), and per-kernel, forward, decode, error-route,
+prologue and output-gate figures.
 """
 from __future__ import annotations
 
@@ -156,8 +160,8 @@ def measured_traffic(name):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the operator shards "
-              "over batch and heads with no communication; see DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: there is no multi-GPU path (the operator shards over "
+              "batch and heads with no communication between GPUs). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
