@@ -64,6 +64,7 @@ __device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, con
     using InT = typename InType<IN_F32>::T;
     constexpr int LDE = Lc::LDE, KQ = D / 32, NW = NT / 64, NPT = CHUNK * D / 8 / NT;
     static_assert(NT % 256 == 0 && NW % KQ == 0 && CHUNK * D / 8 % NT == 0, "thread count");
+    static_assert(NW <= 8, "the column-sum table holds eight waves");
     OpT* sE = reinterpret_cast<OpT*>(smem);
     float (*colred)[32] = reinterpret_cast<float (*)[32]>(smem + Lc::COLRED);
 
