@@ -708,26 +708,39 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    // dA, dP into operand precision, both orientations; Kh^T starts at zero.
+    // dA, dP (stored in operand precision) into LDS, both orientations, in
+    // 16-byte pieces of one row; Kh^T starts at zero.
     {
-        constexpr int NE = CHUNK * CHUNK / NT;
-        float av[NE], pv[NE];
+        constexpr int EPV = 16 / static_cast<int>(sizeof(OpT));  // elements per piece
+        constexpr int NV = CHUNK * CHUNK / EPV / NT;              // pieces per thread
+        static_assert(CHUNK * CHUNK % (EPV * NT) == 0 && CHUNK % EPV == 0, "dA/dP pieces");
+        uint4v ra[NV], rp[NV];
 #pragma unroll
-        for (int k2 = 0; k2 < NE; ++k2) {
-            av[k2] = to_f32(gA[k2 * NT + tid]);
-            pv[k2] = to_f32(gP[k2 * NT + tid]);
+        for (int v = 0; v < NV; ++v) {
+            ra[v] = *reinterpret_cast<const uint4v*>(gA + (v * NT + tid) * EPV);
+            rp[v] = *reinterpret_cast<const uint4v*>(gP + (v * NT + tid) * EPV);
         }
 #pragma unroll
-        for (int k2 = 0; k2 < NE; ++k2) {
-            const int e = k2 * NT + tid, r = e / CHUNK, i = e % CHUNK;
-            const OpT a = from_f32<OpT>(av[k2]), p = from_f32<OpT>(pv[k2]);
-            dAs[r * LDC + i] = a;
-            dPs[r * LDC + i] = p;
-            dAT[i * LDC + r] = a;
-            dPT[i * LDC + r] = p;
+        for (int v = 0; v < NV; ++v) {
+            const int e0 = (v * NT + tid) * EPV, r = e0 / CHUNK, i0 = e0 % CHUNK;
+            *reinterpret_cast<uint4v*>(dAs + r * LDC + i0) = ra[v];
+            *reinterpret_cast<uint4v*>(dPs + r * LDC + i0) = rp[v];
+            const OpT* a = reinterpret_cast<const OpT*>(&ra[v]);
+            const OpT* p = reinterpret_cast<const OpT*>(&rp[v]);
+#pragma unroll
+            for (int u = 0; u < EPV; ++u) {
+                dAT[(i0 + u) * LDC + r] = a[u];
+                dPT[(i0 + u) * LDC + r] = p[u];
+            }
         }
     }
-    for (int e = tid; e < D * LDC; e += NT) KhT[e] = from_f32<OpT>(0.f);
+    {
+        constexpr int NZ = D * LDC * static_cast<int>(sizeof(OpT)) / 16;
+        static_assert(D * LDC * sizeof(OpT) % 16 == 0, "Kh^T in 16-byte pieces");
+        uint4v* kz = reinterpret_cast<uint4v*>(KhT);
+        const uint4v z = {0u, 0u, 0u, 0u};
+        for (int e = tid; e < NZ; e += NT) kz[e] = z;
+    }
     __syncthreads();
     if constexpr (PRO) {
         // prologue: q and k divided by their row norms
