@@ -553,12 +553,20 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     __syncthreads();
 
     // ---------------- phase 3: T = (I + L)^-1 diag(beta), L = strict_tril(diag(beta) P) ----------------
-    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
-        const int r = e / CHUNK, i = e % CHUNK;
-        const float pv = Ps[e];
-        if constexpr (BWD) ws.Pw[ch * CHUNK * CHUNK + e] = (i < r) ? pv : 0.f;
-        Pm[e] = (i < r) ? s_beta[r] * pv : 0.f;  // Ps aliases Nm: read before the zero
-        Nm[e] = 0.f;
+    // four consecutive elements of one row per thread and step (16-byte accesses)
+    for (int e4 = tid; e4 < CHUNK * CHUNK / 4; e4 += NT) {
+        const int e = 4 * e4, r = e / CHUNK, i0 = e % CHUNK;
+        const float4v pv = *reinterpret_cast<const float4v*>(Ps + e);
+        const float br = s_beta[r];
+        float4v pw, pm;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pw[c] = (i0 + c < r) ? pv[c] : 0.f;
+            pm[c] = (i0 + c < r) ? br * pv[c] : 0.f;
+        }
+        if constexpr (BWD) *reinterpret_cast<float4v*>(ws.Pw + ch * CHUNK * CHUNK + e) = pw;
+        *reinterpret_cast<float4v*>(Pm + e) = pm;
+        *reinterpret_cast<float4v*>(Nm + e) = zero4();  // Ps aliases Nm: read above, before the zero
     }
     __syncthreads();
     // diagonal 16x16 blocks, one wave per block, lane j solves column j of
@@ -608,11 +616,21 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         __syncthreads();
     }
     // T = N diag(beta) in operand precision (row-major, padded), in the L region
-    for (int e = tid; e < CHUNK * CHUNK; e += NT) {
-        const int r = e / CHUNK, i = e % CHUNK;
-        const float n = Nm[e];
-        Tm[r * LDC + i] = from_f32<OpT>(n * s_beta[i]);
-        if constexpr (BWD) ws.Nw[ch * CHUNK * CHUNK + e] = n;
+    for (int e4 = tid; e4 < CHUNK * CHUNK / 4; e4 += NT) {
+        const int e = 4 * e4, r = e / CHUNK, i0 = e % CHUNK;
+        const float4v n = *reinterpret_cast<const float4v*>(Nm + e);
+        if constexpr (sizeof(OpT) == 2) {
+            half4 t;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = from_f32<OpT>(n[c] * s_beta[i0 + c]);
+            *reinterpret_cast<half4*>(Tm + r * LDC + i0) = t;
+        } else {
+            float4v t;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = n[c] * s_beta[i0 + c];
+            *reinterpret_cast<float4v*>(Tm + r * LDC + i0) = t;
+        }
+        if constexpr (BWD) *reinterpret_cast<float4v*>(ws.Nw + ch * CHUNK * CHUNK + e) = n;
     }
     __syncthreads();
 
