@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the GDN forward, KDA-with-S0, 350M-layer and sequence-length-sweep workloads")
+    p.add_argument("--no-peaks", action="store_true", help="skip the measured copy and matrix peaks")
     p.add_argument("--copy-calibration", action="store_true",
                    help="end with three 1 GiB device copies (reference kernel for HBM counters)")
     return p.parse_args()
@@ -77,32 +80,39 @@ class KernelTimer:
 
 
 # Path tensors each kernel must touch at least once (bytes per token-head, KDA,
-# bf16 q/k/v/dO/h and bf16 outputs, fp32 beta/alpha and their gradients).  A
-# tensor read by two kernels counts for both; workspace intermediates never count.
+# bf16 q/k/v/dO/h and bf16 outputs, fp32 beta/alpha and their gradients).  Each
+# distinct tensor counts once per launch, however many times the kernel reads
+# it; a tensor read by two kernels counts for both; workspace intermediates
+# never count.
+BT16, F32, AK = 256, 4, 512        # a bf16 row of d = 128, one fp32 scalar, an fp32 alpha row
 PER_TH_BYTES = {
-    "intra_fwd": 3 * 256 + 4 + 512 + 2 * 256,          # q,k,v,beta,alpha read; h read+write (CLVR)
-    "intra_train": 3 * 256 + 4 + 512 + 2 * 256,        # the same, training forward
-    "state_fwd": 0,                                    # intermediates only (+ S_T)
-    "state_train": 0,                                  # intermediates only (+ S_T)
-    "output": 256,                                     # o written
-    "intra_bwd": 3 * 256 + 4 + 512,                    # q,k,v,beta,alpha read
-    "state_fwd_save": 0,                               # intermediates only
-    "state_bwd": 256,                                  # dO read
-    # both gradient stages in one launch: first k,beta,alpha,v,dO,dh read and dv,dbeta
-    # written; then q,k,alpha read and dq,dk,dalpha written
-    "grads": (256 + 4 + 512 + 256 + 256 + 256 + 256 + 4) + (2 * 256 + 512 + 2 * 256 + 512),
-    "clvr_dlam": 2 * 256,                              # dh, v read
+    "intra_fwd": 3 * BT16 + F32 + AK + 2 * BT16,   # q,k,v,beta,alpha read; h read+write (CLVR)
+    "intra_train": 3 * BT16 + F32 + AK + 2 * BT16,  # the same, training forward
+    "state_fwd": 0,                                 # intermediates only (+ S_T)
+    "state_train": 0,                               # intermediates only (+ S_T)
+    "output": BT16,                                 # o written
+    "intra_bwd": 3 * BT16 + F32 + AK,               # q,k,v,beta,alpha read
+    "state_fwd_save": 0,                            # intermediates only
+    "state_bwd": BT16,                              # dO read
+    # both gradient stages in one launch: q,k,v,beta,alpha,dO,dh read; dq,dk,dv,dbeta,dalpha
+    # written (the backward's 2824 B of the path tensors plus dh's 256)
+    "grads": (5 * BT16 + F32 + AK) + (3 * BT16 + F32 + AK),
+    "clvr_dlam": 2 * BT16,                          # dh, v read
     # error-routing epilogue (CLER-H) training step
-    "output_cler": 256 + 2 * 256 + 4,                  # o written; h read+write; beta read
-    "cler_mt": 256,                                    # dh read
-    "state_bwd_cler": 2 * 256 + 4,                     # dO, dh, beta read
-    # the error route's gradient kernel: both gradient stages and the write errors' terms
-    # (dh, beta read once more)
-    "grads_cler": (256 + 4 + 512 + 256 + 256 + 256 + 256 + 4) + (2 * 256 + 512 + 2 * 256 + 512) + 256 + 4,
+    "output_cler": BT16 + 2 * BT16 + F32,           # o written; h read+write; beta read
+    "cler_mt": BT16,                                # dh read
+    "state_bwd_cler": 2 * BT16 + F32,               # dO, dh, beta read
+    # the error route's gradient kernel touches the same tensors as "grads"
+    "grads_cler": (5 * BT16 + F32 + AK) + (3 * BT16 + F32 + AK),
     # output-gate epilogue (bf16 o, g, y, dy, dO, dg)
-    "gate_fwd": 3 * 256,                               # o, g read; y written
-    "gate_bwd": 5 * 256,                               # o, g, dy read; dO, dg written
+    "gate_fwd": 3 * BT16,                           # o, g read; y written
+    "gate_bwd": 5 * BT16,                           # o, g, dy read; dO, dg written
 }
+# The whole training step's compulsory bytes per token-head: the forward's
+# q,k,v,beta,alpha reads and o write (1540) with CLVR's h read+write (512), and
+# the backward's reads of q,k,v,beta,alpha,dO,dh and writes of dq,dk,dv,dbeta,
+# dalpha (3080); plus S_T once per (b,h).
+STEP_TH_BYTES = 1540 + 512 + 3080
 # Per (b,h) state tensors (fp32 d x d): S_T written by the forward state pass.
 PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
 
@@ -157,6 +167,45 @@ def measured_traffic(name):
     return None
 
 
+def cuda_time_ms(fn, steps, warmup=1):
+    """Average milliseconds of fn() over `steps` calls between events on the
+    current stream, after `warmup` untimed calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def host_cpu():
+    """(cores available to this process, cores on the host, CPU model name)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return avail, os.cpu_count() or avail, model
+
+
+def fwd_flops_per_th(d, C=64):
+    # five triangular C x C x d products, three d x d state products, the solve
+    return 5 * C * d + 6 * d * d + C * C / 3
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,21 +222,18 @@ def main():
     dev = torch.device("cuda:0")
     lib = gdr.load_library()
     timer = KernelTimer(lib)
+    bf = torch.bfloat16
+
+    def to_dev(a, dt=torch.float32):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
 
     # ---------------- chunked workload: KDA prefill at 32K tokens ----------------
     cfg = dict(gdr_inputs.CONFIGS["c5b"])
     B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
     log("generating inputs B=%d T=%d H=%d d=%d" % (B, T, H, d))
     inp = gdr_inputs.make(**dict(cfg, bwd=True, clvr=True))
-    bf = torch.bfloat16
-    q = torch.from_numpy(inp["q"]).to(dev).to(bf)
-    k = torch.from_numpy(inp["k"]).to(dev).to(bf)
-    v = torch.from_numpy(inp["v"]).to(dev).to(bf)
-    beta = torch.from_numpy(inp["beta"]).to(dev)
-    alpha = torch.from_numpy(inp["alpha"]).to(dev)
-    dO = torch.from_numpy(inp["dO"]).to(dev).to(bf)
-    h = torch.from_numpy(inp["h"]).to(dev).to(bf)
-    lam = torch.from_numpy(inp["lam"]).to(dev)
+    q, k, v, dO, h = (to_dev(inp[n], bf) for n in ("q", "k", "v", "dO", "h"))
+    beta, alpha, lam = (to_dev(inp[n]) for n in ("beta", "alpha", "lam"))
     ws_f = torch.empty(gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf), dtype=torch.uint8,
                        device=dev)
     do_bwd = not args.no_backward
@@ -213,14 +259,7 @@ def main():
         step()
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = cuda_time_ms(step, args.steps, warmup=0)
     tokens = B * T
     value = tokens / (ms_step / 1e3)
 
@@ -237,14 +276,7 @@ def main():
     def fwd():
         gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f, output_final_state=True)
 
-    fwd()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        fwd()
-    e1.record()
-    torch.cuda.synchronize()
-    fwd_us = 1e3 * e0.elapsed_time(e1) / args.steps
+    fwd_us = 1e3 * cuda_time_ms(fwd, args.steps)
     timer.begin()
     for _ in range(args.steps):
         fwd()
@@ -253,12 +285,9 @@ def main():
         kernels.setdefault(n, {"launches": c, "avg_us": 1e3 * ms / c})
     log("forward %.1f us" % fwd_us)
 
-    # Algorithmic bytes per token-head (KDA, bf16 q/k/v/dO/outputs, fp32 beta/alpha):
-    # q,k,v 3*256 + beta 4 + alpha 512 read, o 256 written -> 1540; CLVR reads and
-    # writes h (2*256).
     th = B * T * H
-    fwd_bytes = th * (1540 + 512)  # the whole forward: intra + state + output
-    fwd_flops = th * (5 * 64 * d + 6 * d * d + 64 * 64 / 3)
+    fwd_bytes = th * (1540 + 512)  # the whole forward: intra + state + output, CLVR's h read+write
+    fwd_flops = th * fwd_flops_per_th(d)
     kbytes = kernel_alg_bytes(B, T, H, d)
     for n, kr in kernels.items():
         # a kernel may run as several launches per step (a state pass cut into
@@ -276,6 +305,17 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom), "alg_bytes_per_launch": kernels[dom]["alg_bytes"],
                 "avg_us": round(kernels[dom]["avg_us"], 2)}
+    # the whole step against both roofs, in algorithmic bytes and flops
+    step_bytes = th * (STEP_TH_BYTES if do_bwd else 1540 + 512) + B * H * d * d * 4
+    step_flops = th * fwd_flops_per_th(d) * (3 if do_bwd else 1)
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    step_tfs = step_flops / (ms_step * 1e-3) / 1e12
+    step_roof = {"alg_bytes": step_bytes, "alg_GBs": round(step_gbs, 1), "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                 "alg_flops": int(step_flops), "alg_TFLOPs": round(step_tfs, 2),
+                 "mfma_frac": round(step_tfs / MFMA_F16_PEAK_TFS, 4),
+                 "note": "algorithmic bytes (%d B per token-head + S_T) and flops (3 x %.0f per token-head) of the "
+                         "training step over its measured time" % (STEP_TH_BYTES, fwd_flops_per_th(d))}
+    log("step roofline %s" % json.dumps(step_roof))
 
     # ---------------- the same training step with the error-routing epilogue ----------------
     cler = None
@@ -290,15 +330,7 @@ def main():
             gdr.backward(q, k, v, beta, alpha, None, dO, dh=h, clvr_scale=lam, want_dclvr_scale=True,
                          saved_workspace=ws_c, route="error")
 
-        for _ in range(args.warmup):
-            cler_step()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            cler_step()
-        e1.record()
-        torch.cuda.synchronize()
-        cler_ms = e0.elapsed_time(e1) / args.steps
+        cler_ms = cuda_time_ms(cler_step, args.steps, args.warmup)
         timer.begin()
         for _ in range(args.steps):
             cler_step()
@@ -319,10 +351,8 @@ def main():
     prologue = None
     if do_bwd:
         pinp = gdr_inputs.make(**dict(cfg, bwd=True, prologue="forget"))
-        pq = torch.from_numpy(pinp["q"]).to(dev).to(bf)
-        pk = torch.from_numpy(pinp["k"]).to(dev).to(bf)
-        pb = torch.from_numpy(pinp["beta"]).to(dev)
-        pa = torch.from_numpy(pinp["alpha"]).to(dev)
+        pq, pk = to_dev(pinp["q"], bf), to_dev(pinp["k"], bf)
+        pb, pa = to_dev(pinp["beta"]), to_dev(pinp["alpha"])
         del pinp
         nbp = gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf, backward=True, prologue="forget")
         ws_p = torch.empty(nbp, dtype=torch.uint8, device=dev)
@@ -340,22 +370,8 @@ def main():
             kn = torch.nn.functional.normalize(pk.float(), dim=-1, eps=1e-6).to(bf)
             return qn, kn, torch.sigmoid(pb), torch.sigmoid(-pa)
 
-        for _ in range(args.warmup):
-            pro_step()
-            separate_pass()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            pro_step()
-        e1.record()
-        torch.cuda.synchronize()
-        pro_ms = e0.elapsed_time(e1) / args.steps
-        e0.record()
-        for _ in range(args.steps):
-            separate_pass()
-        e1.record()
-        torch.cuda.synchronize()
-        sep_ms = e0.elapsed_time(e1) / args.steps
+        pro_ms = cuda_time_ms(pro_step, args.steps, args.warmup)
+        sep_ms = cuda_time_ms(separate_pass, args.steps, args.warmup)
         timer.begin()
         for _ in range(args.steps):
             pro_step()
@@ -395,46 +411,163 @@ def main():
     output_gate = {"workload": "sigmoid(g) * RMSNorm(o) per head on [B=%d, T=%d, H=%d, dv=%d] bf16" % (B, T, H, d),
                    "kernels": gk}
     log("output gate %s" % json.dumps(gk))
-    del og, oo, ody
+    del og, oo, ody, q, k, v, dO, h, beta, alpha, ws_f
 
-    # ---------------- decode: 256 sequences x 16 heads, rotating state sets ----------------
+    # ---------------- the other workloads: one set of 262,144 token-heads per gate ----------------
+    # GDN forward (B=4 H=16 T=4096), KDA forward with S0 (B=1 H=16 T=16384), the
+    # 350M training layer (B=8 H=8 T=4096, KDA fwd+bwd+CLVR) and the sequence-length
+    # sweep of the 350M layer (B*T = 32768, H = 8) all hold 262,144 token-heads:
+    # one draw per gate kind, viewed in each shape (rows stay unit-norm and iid).
+    others = {}
+    if not args.no_other_configs:
+        n_th, dd = 262144, 128
+        sets = {}
+        for gname, seed in (("channel", 4), ("scalar", 2)):
+            gi = gdr_inputs.make(B=1, T=n_th // 8, H=8, d=dd, gate=gname, dtype="bf16", seed=seed, bwd=True)
+            sets[gname] = {n: (to_dev(a, bf) if n in ("q", "k", "v", "dO") else to_dev(a))
+                           for n, a in gi.items() if a is not None}
+            del gi
+        S0c3 = to_dev((0.02 * np.random.default_rng(3).standard_normal((1, 16, dd, dd))).astype(np.float32))
+
+        def view(gname, Bv, Tv, Hv):
+            src = sets[gname]
+            out = {n: t.view(Bv, Tv, Hv, *t.shape[3:]) for n, t in src.items()}
+            return out
+
+        def run_fwd(x, S0=None):
+            gdr.forward(x["q"], x["k"], x["v"], x["beta"], x.get("alpha"), S0, output_final_state=True)
+
+        def fwd_entry(name, gname, Bv, Tv, Hv, S0=None, desc=""):
+            x = view(gname, Bv, Tv, Hv)
+            wsz = gdr.workspace_size(Bv, Tv, Hv, dd, gdr.GATE_CHANNEL if gname == "channel" else gdr.GATE_SCALAR,
+                                     bf, bf)
+            ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+            def f():
+                gdr.forward(x["q"], x["k"], x["v"], x["beta"], x["alpha"], S0, workspace=ws, output_final_state=True)
+
+            us = 1e3 * cuda_time_ms(f, args.steps, args.warmup)
+            nth = Bv * Tv * Hv
+            nbytes = nth * (1540 if gname == "channel" else 1032) + Bv * Hv * dd * dd * 4 * (2 if S0 is not None else 1)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            tfs = nth * fwd_flops_per_th(dd) / (us * 1e-6) / 1e12
+            return {"workload": desc, "us": round(us, 2), "tokens_per_s": round(Bv * Tv / (us * 1e-6), 1),
+                    "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "alg_TFLOPs": round(tfs, 2), "mfma_frac": round(tfs / MFMA_F16_PEAK_TFS, 4)}
+
+        def train_entry(gname, Bv, Tv, Hv, clvr, desc=""):
+            x = view(gname, Bv, Tv, Hv)
+            gate = gdr.GATE_CHANNEL if gname == "channel" else gdr.GATE_SCALAR
+            ws = torch.empty(gdr.workspace_size(Bv, Tv, Hv, dd, gate, bf, bf, backward=True), dtype=torch.uint8,
+                             device=dev)
+            hh = torch.randn((Bv, Tv, Hv * dd), device=dev).to(bf) if clvr else None
+            ll = torch.ones(Hv * dd, device=dev) if clvr else None
+
+            def f():
+                gdr.forward(x["q"], x["k"], x["v"], x["beta"], x["alpha"], None, h=hh, clvr_scale=ll, workspace=ws,
+                            output_final_state=True, save_for_backward=True)
+                gdr.backward(x["q"], x["k"], x["v"], x["beta"], x["alpha"], None, x["dO"], dh=hh, clvr_scale=ll,
+                             want_dclvr_scale=clvr, saved_workspace=ws)
+
+            ms = cuda_time_ms(f, args.steps, args.warmup)
+            nth = Bv * Tv * Hv
+            per = (1540 + 2824) if gname == "channel" else (1032 + 2824 - 2 * 508)
+            if clvr:
+                per += 512 + 256
+            nbytes = nth * per + Bv * Hv * dd * dd * 4
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            tfs = 3 * nth * fwd_flops_per_th(dd) / (ms * 1e-3) / 1e12
+            return {"workload": desc, "ms_per_step": round(ms, 4), "tokens_per_s": round(Bv * Tv / (ms * 1e-3), 1),
+                    "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "alg_TFLOPs": round(tfs, 2), "mfma_frac": round(tfs / MFMA_F16_PEAK_TFS, 4)}
+
+        others["gdn_fwd_B4_H16_T4096"] = fwd_entry("c2", "scalar", 4, 4096, 16,
+                                                   desc="Gated DeltaNet forward, B=4 H=16 T=4096 d=128 bf16")
+        others["kda_fwd_s0_B1_H16_T16384"] = fwd_entry("c3", "channel", 1, 16384, 16, S0=S0c3,
+                                                       desc="KDA forward with initial state, B=1 H=16 T=16384")
+        if do_bwd:
+            others["kda_train_350m_layer_B8_H8_T4096"] = train_entry(
+                "channel", 8, 4096, 8, True, desc="KDA fwd+bwd+CLVR (h [8,4096,1024]), B=8 H=8 T=4096")
+        sweep = []
+        for gname in ("channel", "scalar"):
+            for Tv in (4096, 16384, 32768):
+                Bv = 32768 // Tv
+                e = {"gate": "KDA" if gname == "channel" else "GDN", "B": Bv, "T": Tv, "H": 8}
+                e["fwd_us"] = fwd_entry("", gname, Bv, Tv, 8)["us"]
+                if do_bwd:
+                    e["train_ms"] = train_entry(gname, Bv, Tv, 8, False)["ms_per_step"]
+                sweep.append(e)
+        for gname in ("KDA", "GDN"):
+            pts = [e for e in sweep if e["gate"] == gname]
+            key = "train_ms" if do_bwd else "fwd_us"
+            growth = pts[-1][key] / pts[0][key] - 1.0
+            for e in pts:
+                e["growth_vs_T4096"] = round(e[key] / pts[0][key] - 1.0, 4)
+            log("T-sweep %s: %s (4K -> 32K growth %+.1f %%)" % (gname, json.dumps(pts), 100 * growth))
+        others["t_sweep_350m_layer"] = {"workload": "B*T = 32768 tokens, H=8, d=128, bf16; forward (fwd_us) and "
+                                                    "training step (train_ms) per sequence length",
+                                        "points": sweep}
+        log("other workloads %s" % json.dumps({n: e for n, e in others.items() if n != "t_sweep_350m_layer"}))
+        del sets
+
+    # ---------------- decode: 256 sequences x 16 heads ----------------
     dc = gdr_inputs.DECODE_CONFIG
     nsets = 3
     dinp = gdr_inputs.make_decode(N=dc["N"], H=dc["H"], d=dc["d"], seed=dc["seed"], nstates=nsets)
-    dq = torch.from_numpy(dinp["q"]).to(dev).to(bf)
-    dk_ = torch.from_numpy(dinp["k"]).to(dev).to(bf)
-    dv_ = torch.from_numpy(dinp["v"]).to(dev).to(bf)
-    db = torch.from_numpy(dinp["beta"]).to(dev)
-    da = torch.from_numpy(dinp["alpha"]).to(dev)
-    states = [torch.from_numpy(s).to(dev) for s in dinp["S"]]
+    dq, dk_, dv_ = (to_dev(dinp[n], bf) for n in ("q", "k", "v"))
+    db, da = to_dev(dinp["beta"]), to_dev(dinp["alpha"])
+    states = [to_dev(s) for s in dinp["S"]]
     del dinp
     od = torch.empty((dc["N"], dc["H"], dc["d"]), dtype=bf, device=dev)
-    for i in range(3):
-        gdr.decode_step(dq, dk_, dv_, db, da, states[i % nsets], out=od)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.decode_steps):
-        gdr.decode_step(dq, dk_, dv_, db, da, states[i % nsets], out=od)
-    e1.record()
-    torch.cuda.synchronize()
-    dec_us = 1e3 * e0.elapsed_time(e1) / args.decode_steps
+    rot = [0]
+
+    def dec_rot():
+        # rotating over independent state sets (768 MiB) so the Infinity Cache cannot serve it
+        gdr.decode_step(dq, dk_, dv_, db, da, states[rot[0] % nsets], out=od)
+        rot[0] += 1
+
+    def dec_inplace():
+        gdr.decode_step(dq, dk_, dv_, db, da, states[0], out=od)
+
+    dec_us = 1e3 * cuda_time_ms(dec_rot, args.decode_steps, 3)
+    dec_ip_us = 1e3 * cuda_time_ms(dec_inplace, args.decode_steps, 3)
     slabs = dc["N"] * dc["H"]
     dec_bytes = slabs * (2 * dc["d"] * dc["d"] * 4 + 3 * dc["d"] * 2 + dc["d"] * 4 + 4 + dc["d"] * 2)
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
     decode = {"workload": "KDA decode step, N=256 H=16 d=128, fp32 state 256 MiB, %d rotating sets" % nsets,
               "us_per_step": round(dec_us, 2), "tokens_per_s": round(dc["N"] / (dec_us * 1e-6), 1),
-              "achieved_GBs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+              "achieved_GBs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+              "in_place_us_per_step": round(dec_ip_us, 2),
+              "in_place_GBs": round(dec_bytes / (dec_ip_us * 1e-6) / 1e9, 1),
+              "in_place_note": "one state set updated in place: 256 MiB fits the 256 MB Infinity Cache in part, "
+                               "so this rate is not a DRAM rate"}
+    del states, dq, dk_, dv_, db, da, od
+
+    # ---------------- measured peaks on this GPU ----------------
+    peaks = {}
+    if not args.no_peaks:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        cp_ms = cuda_time_ms(lambda: dst.copy_(src), 10, 2)
+        peaks["copy_GBs"] = round(2 * src.numel() * 4 / (cp_ms * 1e-3) / 1e9, 1)
+        del src, dst
+        n = 8192
+        a16 = torch.randn((n, n), device=dev, dtype=torch.float16)
+        b16 = torch.randn((n, n), device=dev, dtype=torch.float16)
+        mm_ms = cuda_time_ms(lambda: torch.mm(a16, b16), 10, 3)
+        peaks["fp16_gemm_TFLOPs"] = round(2 * n ** 3 / (mm_ms * 1e-3) / 1e12, 1)
+        peaks["note"] = ("copy: a 1 GiB device-to-device copy (read + write); matrix: an 8192^3 fp16 torch.mm "
+                         "(hipBLASLt), as the attainable rates beside the published 8 TB/s and 2.5 PFLOP/s")
+        del a16, b16
+        log("measured peaks %s" % json.dumps(peaks))
 
     # ---------------- CPU baseline: the fp64 oracle on a bounded sample ----------------
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         ts = min(args.cpu_sample_tokens, T)
-        try:
-            cores = len(os.sched_getaffinity(0))
-        except AttributeError:
-            cores = os.cpu_count() or 1
-        threads = min(cores, B * H)
+        avail, host_cores, model = host_cpu()
+        threads = min(avail, B * H)
         sl = lambda a: np.ascontiguousarray(a[:, :ts])  # noqa: E731
         t0 = time.perf_counter()
         oracle.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["alpha"]),
@@ -444,8 +577,9 @@ def main():
                             sl(inp["alpha"]), None, sl(inp["dO"]), nthreads=threads)
         cpu_s = time.perf_counter() - t0
         cpu = {"value": round(B * ts / cpu_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": "first %d of %d tokens, all %d heads, %s, fp64 token-by-token" % (
-                   ts, T, H, "forward+backward" if do_bwd else "forward")}
+               "sample": "first %d of %d tokens, all %d heads, %s, fp64 token-by-token, one thread per head" % (
+                   ts, T, H, "forward+backward" if do_bwd else "forward"),
+               "host_cores_available": avail, "host_cores": host_cores, "cpu_model": model}
 
     out = {
         "metric": METRIC,
@@ -464,6 +598,7 @@ def main():
             "fwd+bwd" if do_bwd else "fwd", B, H, T, d), "global_batch": B, "seq_len": T,
             "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "step_roofline": step_roof,
         "cpu_baseline": cpu,
         "forward": {"us": round(fwd_us, 2), "tokens_per_s": round(tokens / (fwd_us * 1e-6), 1),
                     "alg_GBs": round(fwd_bytes / (fwd_us * 1e-6) / 1e9, 1),
@@ -474,6 +609,8 @@ def main():
                         "alg_GBs": kr["alg_GBs"], "hbm_frac": kr["hbm_frac"]}
                     for n, kr in kernels.items()},
         "decode": decode,
+        "other_workloads": others,
+        "measured_peaks": peaks,
         "cler": cler,
         "prologue": prologue,
         "output_gate": output_gate,

@@ -3,7 +3,8 @@
 // Host code only: argument validation (pure functions of sizes and pointer
 // values, so it runs and is tested without a GPU), workspace sizing and carving,
 // and kernel launches on the caller's stream.  No function here allocates
-// device memory, throws, aborts or synchronises.
+// device memory, throws or aborts; none synchronises except in the debug mode
+// (GDR_VALIDATE=1), which checks the inputs on the device first.
 #include "../../include/gdr.h"
 
 #include <hip/hip_runtime.h>
@@ -12,6 +13,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -180,6 +182,67 @@ gdr_status check_desc(const gdr_desc* d, int64_t* NC) {
     if (blocks > 2147483647.0 || state_blocks > 2147483647.0)
         return fail(GDR_ERR_INVALID_ARG, "too many chunks for one launch");
     if (NC) *NC = nc;
+    return GDR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Debug mode (GDR_VALIDATE=1 in the environment, read at every call): after
+// the host checks, every input tensor is checked on the device against the
+// domain of the kernels (finite values; alpha in (0, 1]; for bf16 inputs the
+// fp16 operand range) and the call synchronises the stream to read the result.
+// A violation returns GDR_ERR_INVALID_ARG before any compute kernel is launched.
+// ---------------------------------------------------------------------------
+bool validate_on() {
+    const char* e = std::getenv("GDR_VALIDATE");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+struct Check {
+    const void* p;
+    int64_t n;
+    bool bf16;
+    uint32_t rules;
+    const char* name;
+};
+
+std::mutex g_check_mu;
+unsigned long long* g_check_res[kMaxDevices] = {};
+
+const char* rule_text(unsigned long long bits) {
+    if (bits & gdr::CHECK_FINITE) return "is not finite (NaN or Inf)";
+    if (bits & gdr::CHECK_ALPHA_OPEN) return "is outside (0, 1] (the chunked kernels take its logarithm)";
+    if (bits & gdr::CHECK_ALPHA_CLOSED) return "is outside [0, 1]";
+    if (bits & gdr::CHECK_NONZERO) return "is 0 (the error route divides the written update by beta)";
+    if (bits & gdr::CHECK_FP16_RANGE)
+        return "has magnitude >= 65504, beyond the fp16 operands that bf16 inputs are computed with";
+    return "breaks an input rule";
+}
+
+gdr_status run_checks(const Check* c, int count, hipStream_t s) {
+    if (!validate_on()) return GDR_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess)
+        return fail(GDR_ERR_DEVICE, "GDR_VALIDATE: cannot query the stream");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(GDR_ERR_INVALID_ARG, "GDR_VALIDATE=1 synchronises the stream; it cannot run under graph capture");
+    std::lock_guard<std::mutex> lock(g_check_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(GDR_ERR_DEVICE, "GDR_VALIDATE: no current device");
+    if (!g_check_res[dev] && gdr::check_result_address(&g_check_res[dev]) != hipSuccess) {
+        g_check_res[dev] = nullptr;
+        return fail(GDR_ERR_DEVICE, "GDR_VALIDATE: check buffer unavailable");
+    }
+    for (int i = 0; i < count; ++i) {
+        if (!c[i].p || c[i].n <= 0) continue;
+        unsigned long long res[2] = {0, 0};
+        if (gdr::launch_check(c[i].p, c[i].n, c[i].bf16, c[i].rules, g_check_res[dev], s) != hipSuccess ||
+            hipMemcpyAsync(res, g_check_res[dev], sizeof res, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return fail(GDR_ERR_DEVICE, "GDR_VALIDATE: check of %s failed to run", c[i].name);
+        if (res[0])
+            return fail(GDR_ERR_INVALID_ARG, "GDR_VALIDATE: %s[%llu] %s", c[i].name, res[1], rule_text(res[0]));
+    }
     return GDR_OK;
 }
 
@@ -363,6 +426,25 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
+    {
+        const bool bf = !in_f32;
+        const int pro_ = desc->prologue;
+        const uint32_t F = gdr::CHECK_FINITE, R = bf ? gdr::CHECK_FP16_RANGE : 0u;
+        const uint32_t beta_rules =
+            F | ((h_clvr && desc->route == GDR_ROUTE_ERROR && !pro_) ? gdr::CHECK_NONZERO : 0u);
+        const Check checks[] = {
+            {q, int64_t(n_in), bf, F | (pro_ ? 0u : R), "q"},
+            {k, int64_t(n_in), bf, F | (pro_ ? 0u : R), "k"},
+            {v, int64_t(n_in), bf, F | R, "v"},
+            {beta, ntok, false, beta_rules, "beta"},
+            {alpha, int64_t(a_bytes / 4), false, pro_ ? F : gdr::CHECK_ALPHA_OPEN, "alpha"},
+            {S0, int64_t(s_bytes / 4), false, F | R, "S0"},
+            {h_clvr, int64_t(n_in), bf, F, "h_clvr"},
+            {clvr_scale, H * D, false, F, "clvr_scale"},
+        };
+        gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
+        if (g != GDR_OK) return g;
+    }
     // the value-routing epilogue runs in the intra-chunk kernel (it needs only
     // v); the error-routing one needs U, so it follows the state pass
     const bool cler = h_clvr && desc->route == GDR_ROUTE_ERROR;
@@ -528,6 +610,26 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
     const int gate = desc->gate;
+    {
+        const bool bf = !in_f32;
+        const uint32_t F = gdr::CHECK_FINITE, R = bf ? gdr::CHECK_FP16_RANGE : 0u;
+        const uint32_t beta_rules =
+            F | ((dh_clvr && desc->route == GDR_ROUTE_ERROR && !pro) ? gdr::CHECK_NONZERO : 0u);
+        const Check checks[] = {
+            {q, int64_t(n_in), bf, F | (pro ? 0u : R), "q"},
+            {k, int64_t(n_in), bf, F | (pro ? 0u : R), "k"},
+            {v, int64_t(n_in), bf, F | R, "v"},
+            {beta, ntok, false, beta_rules, "beta"},
+            {alpha, int64_t(a_bytes / 4), false, pro ? F : gdr::CHECK_ALPHA_OPEN, "alpha"},
+            {S0, int64_t(s_bytes / 4), false, F | R, "S0"},
+            {dO, int64_t(n_in), bf, F | R, "dO"},
+            {dST, int64_t(s_bytes / 4), false, F | R, "dST"},
+            {dh_clvr, int64_t(n_in), bf, F | R, "dh_clvr"},
+            {clvr_scale, H * D, false, F, "clvr_scale"},
+        };
+        gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
+        if (g != GDR_OK) return g;
+    }
     hipError_t e = hipSuccess;
 #define GDR_STEP_ON(st, name, call)                                                           \
     do {                                                                                      \
@@ -700,6 +802,17 @@ gdr_status gdr_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t
     }
     if (overlap(S, s_bytes, o, n * ob)) return fail(GDR_ERR_INVALID_ARG, "o overlaps S");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const bool bf = in_dtype != GDR_FP32;
+        const uint32_t F = gdr::CHECK_FINITE;
+        const Check checks[] = {
+            {q, int64_t(n), bf, F, "q"}, {k, int64_t(n), bf, F, "k"}, {v, int64_t(n), bf, F, "v"},
+            {beta, nslab, false, F, "beta"}, {alpha, int64_t(a_bytes / 4), false, gdr::CHECK_ALPHA_CLOSED, "alpha"},
+            {S, int64_t(s_bytes / 4), false, F, "S"},
+        };
+        gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
+        if (g != GDR_OK) return g;
+    }
     gdr::prof_before(s);
     hipError_t e = gdr::launch_decode(int(dk), gate, in_dtype == GDR_FP32, out_dtype == GDR_FP32, nslab,
                                       int(H), scale, q, k, v, beta, alpha, S, o, s);
@@ -735,6 +848,14 @@ gdr_status gdr_output_gate_forward(const gdr_desc* desc, const void* o, const vo
     if (y != o && overlap(y, n * ob, o, n * ob))
         return fail(GDR_ERR_INVALID_ARG, "y partially overlaps o (it may only be o itself)");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const uint32_t F = gdr::CHECK_FINITE;
+        const Check checks[] = {{o, int64_t(n), desc->out_dtype != GDR_FP32, F, "o"},
+                                {g, int64_t(n), desc->in_dtype != GDR_FP32, F, "g"},
+                                {w, H * D, false, F, "w"}};
+        gdr_status gs = run_checks(checks, 3, s);
+        if (gs != GDR_OK) return gs;
+    }
     gdr::prof_before(s);
     hipError_t e = gdr::launch_gate(false, int(D), desc->in_dtype == GDR_FP32, desc->out_dtype == GDR_FP32, BT, int(H),
                                     o, g, w, y, nullptr, nullptr, nullptr, nullptr, nullptr, s);
@@ -778,6 +899,15 @@ gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const v
             if (&o1 != &o2 && overlap(o1.p, o1.n, o2.p, o2.n)) return fail(GDR_ERR_INVALID_ARG, "two outputs overlap");
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const uint32_t F = gdr::CHECK_FINITE;
+        const Check checks[] = {{o, int64_t(n), desc->out_dtype != GDR_FP32, F, "o"},
+                                {g, int64_t(n), desc->in_dtype != GDR_FP32, F, "g"},
+                                {w, H * D, false, F, "w"},
+                                {dy, int64_t(n), desc->out_dtype != GDR_FP32, F, "dy"}};
+        gdr_status gs = run_checks(checks, 4, s);
+        if (gs != GDR_OK) return gs;
+    }
     gdr::prof_before(s);
     hipError_t e = gdr::launch_gate(true, int(D), desc->in_dtype == GDR_FP32, desc->out_dtype == GDR_FP32, BT, int(H),
                                     o, g, w, nullptr, dy, dO, dg, dw, static_cast<float*>(ws), s);

@@ -1031,21 +1031,26 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                     dalpha[base + r * tokstride + cc] = PRO ? dlogit_from_dlog(dg[j], al[j], pro) : dg[j] / al[j];
             }
         } else {
-            // scalar gate: sum over channels
-            __syncthreads();
-            for (int e = tid; e < CHUNK; e += NT) s_row[e] = 0.f;
+            // scalar gate: sum over channels, in a fixed order: each wave sums
+            // its 64 channels of a row, then the D / 64 wave sums of the row
+            // are added in channel order (s_tot is free again after ltot)
+            float* s_wsum = &s_tot[0][0];  // [D / 64][CHUNK]
+            static_assert((D / 64) * CHUNK <= 4 * D, "wave sums fit s_tot");
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < RPP; ++j) {
                 float x = dg[j];
 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-                if (lane == 0) atomicAdd(&s_row[r0 + j], x);
+                if (lane == 0) s_wsum[(cc >> 6) * CHUNK + r0 + j] = x;
             }
             __syncthreads();
             if (tid < nvalid) {
+                float srow = s_wsum[tid];
+#pragma unroll
+                for (int w = 1; w < D / 64; ++w) srow += s_wsum[w * CHUNK + tid];
                 float a1 = alpha[(b * T + t0 + tid) * H + h];
-                dalpha[(b * T + t0 + tid) * H + h] = PRO ? dlogit_from_dlog(s_row[tid], a1, pro) : s_row[tid] / a1;
+                dalpha[(b * T + t0 + tid) * H + h] = PRO ? dlogit_from_dlog(srow, a1, pro) : srow / a1;
             }
         }
     }

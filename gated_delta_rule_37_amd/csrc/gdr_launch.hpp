@@ -126,6 +126,21 @@ hipError_t launch_cler_fwd(int D, bool in_f32, int64_t B, int64_t T, int H, int6
 hipError_t launch_cler_mt(int D, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const ChunkWs& ws,
                           const float* lam, const void* dh, hipStream_t stream);
 
+// Input checks of the debug mode (GDR_VALIDATE=1).  Rules, OR-ed:
+enum CheckRule : uint32_t {
+    CHECK_FINITE = 1u,        // no NaN or Inf
+    CHECK_FP16_RANGE = 2u,    // |x| < 65504 (becomes an fp16 operand or snapshot)
+    CHECK_ALPHA_OPEN = 4u,    // 0 < x <= 1 (the chunked kernels take log2 x)
+    CHECK_ALPHA_CLOSED = 8u,  // 0 <= x <= 1 (the decode step)
+    CHECK_NONZERO = 16u       // x != 0 (beta of the error route, e = u / beta)
+};
+// Clears res (two words), then ORs into res[0] the rules element i of p ([n],
+// bf16 or fp32) breaks and lowers res[1] to the smallest such i.
+hipError_t launch_check(const void* p, int64_t n, bool bf16, uint32_t rules, unsigned long long* res,
+                        hipStream_t stream);
+// Device address of the check result on the current device.
+hipError_t check_result_address(unsigned long long** out);
+
 // Output-gate epilogue y = sigmoid(g) * w * RMSNorm(o) per head (and its
 // backward, with dw reduced from one partial row per token range).
 int64_t gate_segments(int64_t BT);

@@ -29,7 +29,7 @@
  *                                                     is what the step writes)
  * The chunked kernels obtain e_t as u_t / beta_t, so CLER-H requires every
  * beta != 0 (beta in (0, 1], the sigmoid range the pages use); beta == 0 gives
- * Inf/NaN in h and in the gradients, it is not checked.
+ * Inf/NaN in h and in the gradients (rejected in the debug mode below).
  *
  * Conventions shared by every entry point
  *   - Every function is extern "C", never throws, never aborts, and never
@@ -53,10 +53,31 @@
  *     surface at the caller's next synchronisation.
  *   - Precision: fp32 state and fp32 accumulation throughout.  For bf16 inputs
  *     the matrix-core operands of the chunked path are rounded to fp16 (one
- *     pass), which requires every intermediate (|v|, |S|, the entries of the
- *     in-chunk transform) to stay below 65504 in magnitude.  For fp32 inputs
- *     the operands stay fp32.
- *   - NaN and Inf propagate; they are not checked.
+ *     pass), and so are the chunk-start states and state gradients the
+ *     backward keeps.  Every such value must stay below 65504 in magnitude:
+ *     q, k, v, S0, dO, dST, dh themselves, and what grows from them -- the
+ *     state (about |v| times a few for unit-norm keys) and the state gradient
+ *     (a sum of scale * q do^T over the decay horizon).  Measured on MI355X
+ *     at d = 128 with unit-norm q, k: v scaled to N(0, 1000^2) and dO scaled
+ *     by 256 (a loss scale) at T = 2048 without decay stay within the 2e-3
+ *     bar; a larger loss scale on long sequences without decay can overflow
+ *     the fp16 state-gradient snapshots (Inf in the gradients).  Unscale the
+ *     loss scale into dO beforehand, or use fp32 inputs, whose operands stay
+ *     fp32.
+ *   - NaN and Inf propagate; in the normal mode no input is checked.
+ *   - Debug mode: with the environment variable GDR_VALIDATE=1 (read at every
+ *     call) each entry point, after its host checks, checks its inputs on the
+ *     device and synchronises `stream` to read the result; a violation
+ *     returns GDR_ERR_INVALID_ARG, names the tensor and the first offending
+ *     element in gdr_last_error(), and launches nothing else, so every output
+ *     is untouched.  Rules: every float input finite; alpha in (0, 1] for
+ *     the chunked calls (with a prologue: finite logits) and in [0, 1] for the
+ *     decode step; beta != 0 on the error route (without a prologue); for
+ *     bf16 inputs, |x| < 65504 for q, k (without a prologue), v, S0, dO, dST
+ *     and dh.  Valid inputs give the same results bit for bit as the normal
+ *     mode.  The check cannot run under stream capture (it synchronises):
+ *     there it returns GDR_ERR_INVALID_ARG.  Concurrent validated calls on one
+ *     device are serialised by a lock.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -152,7 +173,12 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
  *   dq, dk    [B,T,H,dk], dv [B,T,H,dv] in out_dtype.
  *   dbeta     [B,T,H] fp32.
  *   dalpha    alpha's shape, fp32, derivative w.r.t. alpha itself; must be NULL
- *             iff the gate is NONE.
+ *             iff the gate is NONE.  The kernels form the gradient with
+ *             respect to ln(alpha) (the decay enters through its cumulative
+ *             logarithm) and divide by alpha: alpha * dalpha is held to the
+ *             same relative bar as every other output, and the absolute error
+ *             of dalpha grows like 1 / alpha where alpha is small (measured
+ *             raw relative errors are listed with the parity results).
  *   dS0       [B,H,dk,dv] fp32, NULL = not written.
  *   dclvr_scale [H*dv] fp32, NULL = not written (requires dh_clvr).
  *   ws        at least gdr_workspace_size(desc, 1) bytes.

@@ -115,3 +115,52 @@ def test_training_pair_full_layer_equals_separate_calls():
                 torch.bfloat16)
     assert_same(run_pair(t, torch.bfloat16, torch.bfloat16, lam, dh, h),
                 run_separate(t, torch.bfloat16, lam, dh, h))
+
+
+@pytest.mark.parametrize("out_dt", ["fp32", "bf16"])
+def test_training_pair_32k_prefill_sampled_heads(out_dt):
+    """The timed training step itself: KDA, B=1 H=16 T=32768 d=128, bf16 inputs,
+    CLVR with its scale gradient, through gdr_forward_train + gdr_backward_saved
+    (the forward chain and the reverse pass cut into chunk ranges, the per-chunk
+    kernels of each range on the second stream).  o, S_T and every gradient of
+    heads 0 and 11 are compared with the oracle, element by element; h and
+    dlam over the whole hidden stream.  fp32 outputs are held to 2e-3, bf16
+    outputs (the timed configuration) to 2e-3 + 2^-8."""
+    announce("training pair 32K prefill sampled heads, %s outputs" % out_dt)
+    inp, cfg = gdr_inputs.make_config("c5b", bwd=True, clvr=True)
+    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
+    r = np.random.default_rng(430)
+    lam = r.standard_normal(H * d).astype(np.float32)
+    dh = gdr_inputs.round_bf16(r.standard_normal((B, T, H * d)))
+    t = inputs_to_dev({n: a for n, a in inp.items() if n not in ("h", "lam")}, "bf16")
+    od = torch.float32 if out_dt == "fp32" else torch.bfloat16
+    h = to_dev(inp["h"], torch.bfloat16)
+    ws = torch.empty(gdr.workspace_size(B, T, H, d, gdr.GATE_CHANNEL, torch.bfloat16, od, backward=True),
+                     dtype=torch.uint8, device="cuda")
+    o, ST = gdr.forward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], None, out_dtype=od, h=h,
+                        clvr_scale=to_dev(lam), workspace=ws, output_final_state=True, save_for_backward=True)
+    g = gdr.backward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], None, t["dO"], out_dtype=od,
+                     dh=to_dev(dh, torch.bfloat16), clvr_scale=to_dev(lam), want_dclvr_scale=True,
+                     saved_workspace=ws)
+    torch.cuda.synchronize()
+    heads = [0, 11]
+    sl = lambda a: np.ascontiguousarray(a[:, :, heads])  # noqa: E731
+    o_ref, ST_ref = oracle.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["alpha"]),
+                                   None, nthreads=len(heads))
+    ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["alpha"]), None,
+                          sl(inp["dO"]), nthreads=len(heads))
+    dvc, dlam = oracle.clvr_backward(dh, inp["v"], lam)
+    h_ref = oracle.clvr_forward(inp["h"], inp["v"], lam)
+    ref["dv"] = ref["dv"] + sl(dvc.reshape(B, T, H, d))
+    errs = {"o": rel(o[:, :, heads], o_ref), "S_T": rel(ST[:, heads], ST_ref)}
+    for n in ("dq", "dk", "dv", "dbeta", "dalpha"):
+        errs[n] = rel(g[n][:, :, heads], ref[n])
+    errs["dlam"] = rel(g["dclvr_scale"], dlam)
+    errs["h"] = rel(h, h_ref)
+    report(**errs)
+    bar = 2e-3 if out_dt == "fp32" else 2e-3 + 2.0 ** -8
+    # o, dq, dk, dv are stored in the output dtype; S_T, dbeta, dalpha, dlam are
+    # always fp32; h is the bf16 hidden stream
+    for n, e in errs.items():
+        b = bar if n in ("o", "dq", "dk", "dv") else (2e-3 + 2.0 ** -8 if n == "h" else 2e-3)
+        assert e < b, (n, e, b)
