@@ -54,13 +54,16 @@ def _load():
             lib.oracle_forward.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 8 + [cint]
             lib.oracle_backward.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 14 + [cint]
             lib.oracle_decode.argtypes = [i64] * 4 + [cint, dbl] + [ptr] * 7 + [cint]
+            lib.oracle_gdn2_forward.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 9 + [cint]
+            lib.oracle_gdn2_decode.argtypes = [i64] * 4 + [cint, dbl] + [ptr] * 8 + [cint]
             lib.oracle_clvr_forward.argtypes = [i64] * 4 + [ptr] * 4
             lib.oracle_clvr_backward.argtypes = [i64] * 4 + [ptr] * 5
             lib.oracle_forward_errors.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 9 + [cint]
             lib.oracle_backward_errors.argtypes = [i64] * 5 + [cint, dbl] + [ptr] * 15 + [cint]
             for f in (lib.oracle_forward, lib.oracle_backward, lib.oracle_decode,
                       lib.oracle_clvr_forward, lib.oracle_clvr_backward,
-                      lib.oracle_forward_errors, lib.oracle_backward_errors):
+                      lib.oracle_forward_errors, lib.oracle_backward_errors,
+                      lib.oracle_gdn2_forward, lib.oracle_gdn2_decode):
                 f.restype = cint
             _lib = lib
     return _lib
@@ -164,6 +167,36 @@ def decode(q, k, v, beta, alpha, S, scale=1.0, nthreads=None):
     rc = _load().oracle_decode(N, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v), _p(beta),
                                _p(alpha), _p(S), _p(o), _threads(nthreads))
     _check(rc, "oracle_decode")
+    return o, S
+
+
+def gdn2_forward(q, k, v, erase, write, alpha=None, S0=None, scale=1.0, nthreads=None):
+    """Gated DeltaNet-2, token by token (erase and write gates [B,T,H,dk]):
+    ``S_t = (I - (e_t*k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t*k_t) v_t^T``,
+    ``o_t = scale S_t^T q_t``.  Returns ``(o, S_T)``."""
+    q, k, v, erase, write, alpha, S0 = map(_f64, (q, k, v, erase, write, alpha, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    rc = _load().oracle_gdn2_forward(B, T, H, dk, dv, gate_kind(alpha, q), float(scale), _p(q), _p(k), _p(v),
+                                     _p(erase), _p(write), _p(alpha), _p(S0), _p(o), _p(ST), _threads(nthreads))
+    _check(rc, "oracle_gdn2_forward")
+    return o, ST
+
+
+def gdn2_decode(q, k, v, erase, write, alpha, S, scale=1.0, nthreads=None):
+    """One Gated DeltaNet-2 step for N sequences (erase, write [N,H,dk]).
+    Returns ``(o [N,H,dv], S_new)``; the input state is not modified."""
+    q, k, v, erase, write, alpha = map(_f64, (q, k, v, erase, write, alpha))
+    S = np.array(S, dtype=np.float64, order="C", copy=True)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    gate = GATE_NONE if alpha is None else (GATE_SCALAR if alpha.ndim == 2 else GATE_CHANNEL)
+    o = np.zeros((N, H, dv))
+    rc = _load().oracle_gdn2_decode(N, H, dk, dv, gate, float(scale), _p(q), _p(k), _p(v), _p(erase), _p(write),
+                                    _p(alpha), _p(S), _p(o), _threads(nthreads))
+    _check(rc, "oracle_gdn2_decode")
     return o, S
 
 

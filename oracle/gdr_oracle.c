@@ -36,6 +36,7 @@ typedef struct {
     double *o, *ST, *dq, *dk_out, *dv_out, *dbeta, *dalpha, *dS0;
     double* E;        /* forward: write errors e_t, [B,T,H,dv] (NULL: not written) */
     const double* dE; /* backward: gradient arriving at e_t, [B,T,H,dv] (NULL: zero) */
+    const double *erase, *write; /* Gated DeltaNet-2: erase and write gates, [B,T,H,dk] */
     int64_t N; /* decode: number of sequences */
     double* S; /* decode: state in/out */
     int status;
@@ -473,4 +474,128 @@ int oracle_clvr_backward(int64_t B, int64_t T, int64_t H, int64_t dv, const doub
                 if (dlam) dlam[c] += g * v[(bt * H + h) * dv + jj];
             }
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Gated DeltaNet-2: separate erase and write gates                           */
+/* ------------------------------------------------------------------------- */
+/*
+ * The popular article on the study (its Gated DeltaNet-2 paragraph) describes
+ * this member only in words: erasing old content and writing new content are
+ * decoupled and steered by two gates computed independently from the current
+ * token, an erase gate choosing the regions of the memory to clear and a write
+ * gate the regions to write; with the two gates equal the mechanism falls back
+ * to Kimi Delta Attention, and further to Gated DeltaNet.  Reading taken (the
+ * plainest one that keeps both reductions): the memory's regions are its key
+ * channels (rows of S), the gates are dk-vectors e_t, w_t per token and head,
+ * and one step is
+ *   S'  = Diag(a) S                      decay first, as for the family
+ *   p   = S'^T k_t                       what the memory predicts for k_t
+ *   S_t = S' - (e_t * k_t) p^T + (w_t * k_t) v_t^T
+ *       = (I - (e_t * k_t) k_t^T) Diag(a) S + (w_t * k_t) v_t^T
+ *   o_t = scale * S_t^T q_t
+ * (* elementwise).  e_t = w_t = beta_t 1 gives the step of oracle_forward.
+ */
+static void gdn2_step(int64_t dk, int64_t dv, const double* a, const double* kt, const double* vt,
+                      const double* et, const double* wt, const double* S_prev, double* Sd, double* p,
+                      double* S_new) {
+    for (int64_t i = 0; i < dk; ++i)
+        for (int64_t j = 0; j < dv; ++j) Sd[i * dv + j] = a[i] * S_prev[i * dv + j];
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0; /* (S'^T k)_j */
+        for (int64_t i = 0; i < dk; ++i) acc += Sd[i * dv + j] * kt[i];
+        p[j] = acc;
+    }
+    for (int64_t i = 0; i < dk; ++i) {
+        const double ek = et[i] * kt[i], wk = wt[i] * kt[i];
+        for (int64_t j = 0; j < dv; ++j) S_new[i * dv + j] = Sd[i * dv + j] - ek * p[j] + wk * vt[j];
+    }
+}
+
+static void gdn2_forward_slab(job_t* j, int64_t slab) {
+    const int64_t b = slab / j->H, h = slab % j->H, dk = j->dk, dv = j->dv, T = j->T, H = j->H;
+    const size_t nS = (size_t)(dk * dv);
+    double* S = (double*)malloc(sizeof(double) * nS);
+    double* Sn = (double*)malloc(sizeof(double) * nS);
+    double* Sd = (double*)malloc(sizeof(double) * nS);
+    double* a = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !Sn || !Sd || !a || !p) {
+        j->status = -2;
+        goto done;
+    }
+    if (j->S0)
+        memcpy(S, j->S0 + (size_t)slab * nS, sizeof(double) * nS);
+    else
+        memset(S, 0, sizeof(double) * nS);
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t tok = (b * T + t) * H + h;
+        for (int64_t i = 0; i < dk; ++i) a[i] = gate_at(j, b, t, h, i);
+        gdn2_step(dk, dv, a, j->k + tok * dk, j->v + tok * dv, j->erase + tok * dk, j->write + tok * dk, S, Sd,
+                  p, Sn);
+        double* tmp = S;
+        S = Sn;
+        Sn = tmp;
+        readout(dk, dv, j->scale, S, j->q + tok * dk, j->o + tok * dv);
+    }
+    if (j->ST) memcpy(j->ST + (size_t)slab * nS, S, sizeof(double) * nS);
+done:
+    free(S);
+    free(Sn);
+    free(Sd);
+    free(a);
+    free(p);
+}
+
+int oracle_gdn2_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate, double scale,
+                        const double* q, const double* k, const double* v, const double* erase,
+                        const double* write, const double* alpha, const double* S0, double* o, double* ST,
+                        int nthreads) {
+    if (check_common(B, T, H, dk, dv, gate)) return -1;
+    if (T > 0 && (!q || !k || !v || !erase || !write || !o)) return -1;
+    if (gate != ORACLE_GATE_NONE && T > 0 && !alpha) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.B = B; j.T = T; j.H = H; j.dk = dk; j.dv = dv; j.gate = gate; j.scale = scale;
+    j.q = q; j.k = k; j.v = v; j.erase = erase; j.write = write; j.alpha = alpha; j.S0 = S0; j.o = o;
+    j.ST = ST;
+    return run_slabs(&j, nthreads, gdn2_forward_slab);
+}
+
+static void gdn2_decode_slab(job_t* j, int64_t slab) {
+    const int64_t n = slab / j->H, h = slab % j->H, dk = j->dk, dv = j->dv;
+    const size_t nS = (size_t)(dk * dv);
+    double* S = j->S + (size_t)slab * nS;
+    double* Sn = (double*)malloc(sizeof(double) * nS);
+    double* Sd = (double*)malloc(sizeof(double) * nS);
+    double* a = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!Sn || !Sd || !a || !p) {
+        j->status = -2;
+        goto done;
+    }
+    for (int64_t i = 0; i < dk; ++i) a[i] = gate_at(j, n, 0, h, i);
+    gdn2_step(dk, dv, a, j->k + slab * dk, j->v + slab * dv, j->erase + slab * dk, j->write + slab * dk, S, Sd,
+              p, Sn);
+    memcpy(S, Sn, sizeof(double) * nS);
+    readout(dk, dv, j->scale, S, j->q + slab * dk, j->o + slab * dv);
+done:
+    free(Sn);
+    free(Sd);
+    free(a);
+    free(p);
+}
+
+int oracle_gdn2_decode(int64_t N, int64_t H, int64_t dk, int64_t dv, int gate, double scale, const double* q,
+                       const double* k, const double* v, const double* erase, const double* write,
+                       const double* alpha, double* S, double* o, int nthreads) {
+    if (check_common(N, 1, H, dk, dv, gate)) return -1;
+    if (N * H > 0 && (!q || !k || !v || !erase || !write || !S || !o)) return -1;
+    if (gate != ORACLE_GATE_NONE && N * H > 0 && !alpha) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.B = N; j.T = 1; j.H = H; j.dk = dk; j.dv = dv; j.gate = gate; j.scale = scale;
+    j.q = q; j.k = k; j.v = v; j.erase = erase; j.write = write; j.alpha = alpha; j.S = S; j.o = o;
+    j.N = N;
+    return run_slabs(&j, nthreads, gdn2_decode_slab);
 }

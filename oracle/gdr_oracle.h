@@ -95,6 +95,24 @@ int oracle_clvr_forward(int64_t B, int64_t T, int64_t H, int64_t dv, const doubl
 int oracle_clvr_backward(int64_t B, int64_t T, int64_t H, int64_t dv, const double* dh,
                          const double* v, const double* lam, double* dv_acc, double* dlam);
 
+/* Gated DeltaNet-2 (popular article on the study, its Gated DeltaNet-2
+ * paragraph: separate erase and write gates).  Reading (see the C file):
+ *     S_t = (I - (e_t * k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t * k_t) v_t^T
+ *     o_t = scale * S_t^T q_t
+ * with the erase gate e and the write gate w [B, T, H, dk] (elementwise *);
+ * alpha, S0, ST as for oracle_forward.  e = w = beta (broadcast over dk) is
+ * oracle_forward's recurrence. */
+int oracle_gdn2_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int gate, double scale,
+                        const double* q, const double* k, const double* v, const double* erase,
+                        const double* write, const double* alpha, const double* S0, double* o, double* ST,
+                        int nthreads);
+
+/* One Gated DeltaNet-2 step for N sequences, S [N,H,dk,dv] updated in place;
+ * erase, write [N,H,dk]. */
+int oracle_gdn2_decode(int64_t N, int64_t H, int64_t dk, int64_t dv, int gate, double scale, const double* q,
+                       const double* k, const double* v, const double* erase, const double* write,
+                       const double* alpha, double* S, double* o, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
