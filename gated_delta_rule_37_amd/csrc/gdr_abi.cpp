@@ -734,6 +734,19 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     return GDR_OK;
 }
 
+namespace gdr {
+
+// Entry points defined in other sources share the forward and the error text.
+gdr_status forward_entry(const gdr_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                         const float* alpha, const float* S0, void* o, float* ST, void* h_clvr,
+                         const float* clvr_scale, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(desc, q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws, ws_bytes, stream, false);
+}
+
+gdr_status set_error(gdr_status s, const char* msg) { return fail(s, "%s", msg); }
+
+}  // namespace gdr
+
 extern "C" {
 
 gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,

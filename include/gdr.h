@@ -222,6 +222,25 @@ gdr_status gdr_backward_saved(const gdr_desc* desc, const void* q, const void* k
                               void* dk, void* dv, float* dbeta, float* dalpha, float* dS0,
                               float* dclvr_scale, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free chunked forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, checks and results (bit for bit) as
+ * gdr_forward_chunked, without ws / ws_bytes: the workspace is a fixed device
+ * array inside the library of GDR_NOALLOC_SCRATCH_BYTES (256 MiB), one per
+ * GPU, held until the process ends.  A descriptor whose
+ * gdr_workspace_size(desc, 0) exceeds it returns GDR_ERR_WORKSPACE (at
+ * d = 128 with bf16 inputs the limit is about 2,100 chunk-heads, e.g. B = 1,
+ * H = 16, T = 8192).  The call allocates nothing.  Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different streams,
+ * or threads without ordering) race and give wrong results; order them on one
+ * stream or with events. */
+#define GDR_NOALLOC_SCRATCH_BYTES (256ull * 1024ull * 1024ull)
+size_t gdr_noalloc_scratch_bytes(void);
+gdr_status gdr_forward_chunked_noalloc(const gdr_desc* desc, const void* q, const void* k,
+                                       const void* v, const float* beta, const float* alpha,
+                                       const float* S0, void* o, float* ST, void* h_clvr,
+                                       const float* clvr_scale, void* stream);
+
 /* One decode step for N independent sequences, state updated in place
  * (inference with a fixed-size state, KDA blog section 6.1):
  *   p = S^T (alpha*k), r = S^T (alpha*q), u = beta (v - p),
