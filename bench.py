@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the GDN forward, KDA-with-S0, 350M-layer and sequence-length-sweep workloads")
     p.add_argument("--no-peaks", action="store_true", help="skip the measured copy and matrix peaks")
+    p.add_argument("--no-gdn2", action="store_true", help="skip the Gated DeltaNet-2 forward and decode")
     p.add_argument("--copy-calibration", action="store_true",
                    help="end with three 1 GiB device copies (reference kernel for HBM counters)")
     return p.parse_args()
@@ -510,6 +511,65 @@ def main():
         log("other workloads %s" % json.dumps({n: e for n, e in others.items() if n != "t_sweep_350m_layer"}))
         del sets
 
+    # ---------------- Gated DeltaNet-2 (separate erase and write gates) ----------------
+    gdn2 = None
+    if not args.no_gdn2:
+        g = gdr_inputs.make(**dict(cfg))  # the 32K-token KDA prefill inputs
+        gq, gk, gv = (to_dev(g[n], bf) for n in ("q", "k", "v"))
+        ga = to_dev(g["alpha"])
+        del g
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        ge = torch.rand((B, T, H, d), generator=gen, device=dev)
+        gw = torch.rand((B, T, H, d), generator=gen, device=dev)
+        gws = torch.empty(gdr.gdn2_workspace_size(B, T, H, d, gdr.GATE_CHANNEL, bf, bf), dtype=torch.uint8, device=dev)
+
+        def gdn2_fwd():
+            gdr.gdn2_forward(gq, gk, gv, ge, gw, ga, None, workspace=gws)
+
+        g_ms = cuda_time_ms(gdn2_fwd, args.steps, args.warmup)
+        timer.begin()
+        for _ in range(args.steps):
+            gdn2_fwd()
+        torch.cuda.synchronize()
+        g_k = {n: {"avg_us": round(1e3 * ms / c, 2)} for n, (c, ms) in timer.end().items()}
+        g_bytes = th * (3 * 256 + 2 * 512 + 512 + 256) + B * H * d * d * 4  # q,k,v, e,w, alpha, o; S_T
+        g_flops = th * (9 * 64 * d + 8 * d * d)
+        g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
+        g_tfs = g_flops / (g_ms * 1e-3) / 1e12
+        del gq, gk, gv, ga, ge, gw, gws
+        # decode step at the decode shape (256 sequences x 16 heads), rotating state sets
+        dc2 = gdr_inputs.DECODE_CONFIG
+        di = gdr_inputs.make_decode(N=dc2["N"], H=dc2["H"], d=dc2["d"], seed=dc2["seed"], nstates=3)
+        xq, xk, xv = (to_dev(di[n], bf) for n in ("q", "k", "v"))
+        xa = to_dev(di["alpha"])
+        xst = [to_dev(sx) for sx in di["S"]]
+        del di
+        xe = torch.rand((dc2["N"], dc2["H"], dc2["d"]), generator=gen, device=dev)
+        xw = torch.rand((dc2["N"], dc2["H"], dc2["d"]), generator=gen, device=dev)
+        xo = torch.empty((dc2["N"], dc2["H"], dc2["d"]), dtype=bf, device=dev)
+        rot2 = [0]
+
+        def gdn2_dec():
+            gdr.gdn2_decode_step(xq, xk, xv, xe, xw, xa, xst[rot2[0] % 3], out=xo)
+            rot2[0] += 1
+
+        gd_us = 1e3 * cuda_time_ms(gdn2_dec, args.decode_steps, 3)
+        nsl = dc2["N"] * dc2["H"]
+        gd_bytes = nsl * (2 * dc2["d"] * dc2["d"] * 4 + 3 * dc2["d"] * 2 + 3 * dc2["d"] * 4 + dc2["d"] * 2)
+        del xq, xk, xv, xa, xst, xe, xw, xo
+        gdn2 = {"workload": "Gated DeltaNet-2 forward (erase, write gates U(0,1) per channel; KDA gates), "
+                            "B=%d H=%d T=%d d=%d bf16" % (B, H, T, d),
+                "us": round(g_ms * 1e3, 2), "tokens_per_s": round(tokens / (g_ms * 1e-3), 1),
+                "alg_GBs": round(g_gbs, 1), "hbm_frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                "alg_TFLOPs": round(g_tfs, 2), "mfma_frac": round(g_tfs / MFMA_F16_PEAK_TFS, 4),
+                "kernels": g_k,
+                "decode": {"workload": "one step, N=256 H=16 d=128, 3 rotating fp32 state sets",
+                           "us_per_step": round(gd_us, 2),
+                           "achieved_GBs": round(gd_bytes / (gd_us * 1e-6) / 1e9, 1),
+                           "hbm_frac": round(gd_bytes / (gd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+        log("gdn2 %s" % json.dumps(gdn2))
+
     # ---------------- decode: 256 sequences x 16 heads ----------------
     dc = gdr_inputs.DECODE_CONFIG
     nsets = 3
@@ -614,6 +674,7 @@ def main():
         "cler": cler,
         "prologue": prologue,
         "output_gate": output_gate,
+        "gdn2": gdn2,
     }
     print(json.dumps(out), flush=True)
 

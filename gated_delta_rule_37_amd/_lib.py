@@ -81,6 +81,12 @@ def load_library():
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_version.argtypes = []
         lib.gdr_version.restype = I32
+        lib.gdr_gdn2_workspace_size.argtypes = [D]
+        lib.gdr_gdn2_workspace_size.restype = SZ
+        lib.gdr_gdn2_forward_chunked.argtypes = [D] + [P] * 9 + [P, SZ, P]
+        lib.gdr_gdn2_forward_chunked.restype = ctypes.c_int
+        lib.gdr_gdn2_decode_step.argtypes = [I64] * 4 + [I32] * 3 + [F32] + [P] * 8 + [P]
+        lib.gdr_gdn2_decode_step.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -288,6 +294,73 @@ def decode_step(q, k, v, beta, alpha, S, *, scale=1.0, out_dtype=None, out=None)
     _check(lib.gdr_decode_step(N, H, dk, dv, gate, _dt(q.dtype), _dt(od), float(scale), _ptr(q),
                                _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S), _ptr(o),
                                _stream(q.device)))
+    return o
+
+
+def gdn2_workspace_size(B, T, H, d, gate=GATE_CHANNEL, in_dtype=torch.bfloat16, out_dtype=None) -> int:
+    desc = Desc(B, T, H, d, d, gate, _dt(in_dtype), _dt(out_dtype or in_dtype), 1.0, 0, ROUTE_VALUE, PROLOGUE_NONE)
+    n = load_library().gdr_gdn2_workspace_size(ctypes.byref(desc))
+    if n == 0 and B * H * T > 0:
+        _check(1)
+    return int(n)
+
+
+def gdn2_forward(q, k, v, erase, write, alpha=None, S0=None, *, scale=1.0, out_dtype=None,
+                 output_final_state=True, workspace=None):
+    """Gated DeltaNet-2 chunked forward: separate erase and write gates
+    ``erase``, ``write`` [B, T, H, dk] fp32,
+    ``S_t = (I - (e_t*k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t*k_t) v_t^T``,
+    ``o_t = scale S_t^T q_t``.  Returns ``(o, S_T)``."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, dk))
+    _need(v, "v", q.dtype, (B, T, H, dv))
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32, (B, T, H) if alpha.dim() == 3 else (B, T, H, dk))
+    _need(S0, "S0", torch.float32, (B, H, dk, dv))
+    _need(erase, "erase", torch.float32, (B, T, H, dk))
+    _need(write, "write", torch.float32, (B, T, H, dk))
+    lib = load_library()
+    desc = _desc(q, v, alpha, out_dtype, scale)
+    o = torch.empty((B, T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    need = lib.gdr_gdn2_workspace_size(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib.gdr_gdn2_forward_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(erase), _ptr(write),
+                                        _ptr(alpha), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), need,
+                                        _stream(q.device)))
+    return o, ST
+
+
+def gdn2_decode_step(q, k, v, erase, write, alpha, S, *, scale=1.0, out_dtype=None, out=None):
+    """One Gated DeltaNet-2 step for N sequences (``erase``, ``write`` [N, H, dk]
+    fp32); ``S`` [N, H, dk, dv] fp32 is updated in place.  Returns ``o``."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (N, H, dk))
+    _need(v, "v", q.dtype, (N, H, dv))
+    _need(erase, "erase", torch.float32, (N, H, dk))
+    _need(write, "write", torch.float32, (N, H, dk))
+    gate = GATE_NONE
+    if alpha is not None:
+        gate = GATE_SCALAR if alpha.dim() == 2 else GATE_CHANNEL
+        _need(alpha, "alpha", torch.float32, (N, H) if gate == GATE_SCALAR else (N, H, dk))
+    _need(S, "S", torch.float32, (N, H, dk, dv))
+    od = out_dtype or q.dtype
+    o = out if out is not None else torch.empty((N, H, dv), dtype=od, device=q.device)
+    _need(o, "out", od, (N, H, dv))
+    lib = load_library()
+    _check(lib.gdr_gdn2_decode_step(N, H, dk, dv, gate, _dt(q.dtype), _dt(od), float(scale), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(erase), _ptr(write), _ptr(alpha), _ptr(S), _ptr(o),
+                                    _stream(q.device)))
     return o
 
 

@@ -734,6 +734,174 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     return GDR_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Gated DeltaNet-2 (separate erase and write gates): fp32 chunk operands and the
+// two additive terms X, Y per chunk-head.
+// ---------------------------------------------------------------------------
+static size_t gdn2_ws_bytes(int64_t nch, int D, gdr::ChunkWs* out, void* base) {
+    gdr::ChunkWs w;
+    std::memset(&w, 0, sizeof w);
+    size_t off = 0;
+    char* p = static_cast<char*>(base);
+    auto take = [&](size_t bytes) -> void* {
+        void* r = p ? p + off : nullptr;
+        off += align_up(bytes);
+        return r;
+    };
+    const size_t mat = size_t(nch) * kChunk * D * 4;
+    w.W = take(mat);
+    w.Ut = take(mat);
+    w.Qt = take(mat);
+    w.KbT = take(mat);
+    w.A = take(size_t(nch) * kChunk * kChunk * 4);
+    w.gam = static_cast<float*>(take(size_t(nch) * D * 4));
+    w.X = static_cast<float*>(take(size_t(nch) * D * D * 4));
+    w.Y = static_cast<float*>(take(mat));
+    if (out) *out = w;
+    return off;
+}
+
+static gdr_status gdn2_check_desc(const gdr_desc* desc, int64_t* NC) {
+    gdr_status st = check_desc(desc, NC);
+    if (st != GDR_OK) return st;
+    if (desc->route != GDR_ROUTE_VALUE || desc->prologue != GDR_PROLOGUE_NONE)
+        return fail(GDR_ERR_UNSUPPORTED, "the separate-gate variant takes no hidden-stream route and no prologue");
+    return GDR_OK;
+}
+
+extern "C" size_t gdr_gdn2_workspace_size(const gdr_desc* desc) {
+    int64_t NC = 0;
+    if (gdn2_check_desc(desc, &NC) != GDR_OK) return 0;
+    return gdn2_ws_bytes(desc->B * desc->H * NC, int(desc->dk), nullptr, nullptr);
+}
+
+extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                                               const float* erase, const float* write, const float* alpha,
+                                               const float* S0, void* o, float* ST, void* ws, size_t ws_bytes,
+                                               void* stream) {
+    int64_t NC = 0;
+    gdr_status st = gdn2_check_desc(desc, &NC);
+    if (st != GDR_OK) return st;
+    const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
+    const int64_t ntok = B * T * H;
+    const bool any = ntok > 0;
+    if (any && (!q || !k || !v || !erase || !write || !o))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, erase, write and o are required");
+    if ((desc->gate == GDR_GATE_NONE) != (alpha == nullptr) && any)
+        return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
+    const void* ptrs[] = {q, k, v, erase, write, alpha, S0, o, ST, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t ib = dtype_bytes(desc->in_dtype), ob = dtype_bytes(desc->out_dtype);
+    const size_t n_in = size_t(ntok) * D;
+    const size_t o_bytes = n_in * ob;
+    const size_t a_bytes = desc->gate == GDR_GATE_CHANNEL ? n_in * 4 : size_t(ntok) * 4;
+    const size_t s_bytes = size_t(B * H) * D * D * 4;
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{q, n_in * ib}, {k, n_in * ib}, {v, n_in * ib}, {erase, n_in * 4}, {write, n_in * 4},
+               {alpha, a_bytes}, {S0, s_bytes}};
+    for (auto& in : ins) {
+        if (overlap(o, o_bytes, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "o overlaps an input");
+        if (ST && in.p != S0 && overlap(ST, s_bytes, in.p, in.n))
+            return fail(GDR_ERR_INVALID_ARG, "ST overlaps an input other than S0");
+    }
+    if (ST && overlap(ST, s_bytes, o, o_bytes)) return fail(GDR_ERR_INVALID_ARG, "ST overlaps o");
+    if (S0 && ST && S0 != ST && overlap(S0, s_bytes, ST, s_bytes))
+        return fail(GDR_ERR_INVALID_ARG, "ST partially overlaps S0 (it may only alias it exactly)");
+    gdr::ChunkWs w;
+    const size_t need = gdn2_ws_bytes(B * H * NC, int(D), &w, ws);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+    if (B * H == 0) return GDR_OK;
+    if (ws) {
+        for (auto& in : ins)
+            if (overlap(ws, need, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an input");
+        if (overlap(ws, need, o, o_bytes) || (ST && overlap(ws, need, ST, s_bytes)))
+            return fail(GDR_ERR_INVALID_ARG, "workspace overlaps an output");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool in_f32 = desc->in_dtype == GDR_FP32, out_f32 = desc->out_dtype == GDR_FP32;
+    {
+        const uint32_t F = gdr::CHECK_FINITE, R = in_f32 ? 0u : gdr::CHECK_FP16_RANGE;
+        const Check checks[] = {
+            {q, int64_t(n_in), !in_f32, F, "q"},         {k, int64_t(n_in), !in_f32, F, "k"},
+            {v, int64_t(n_in), !in_f32, F | R, "v"},     {erase, int64_t(n_in), false, F, "erase"},
+            {write, int64_t(n_in), false, F, "write"},   {alpha, int64_t(a_bytes / 4), false, gdr::CHECK_ALPHA_OPEN, "alpha"},
+            {S0, int64_t(s_bytes / 4), false, F, "S0"},
+        };
+        gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
+        if (g != GDR_OK) return g;
+    }
+    hipError_t e = hipSuccess;
+    if (NC > 0) {
+        gdr::prof_before(s);
+        e = gdr::launch_gdn2_intra(int(D), desc->gate, in_f32, B, T, int(H), NC, q, k, v, erase, write, alpha, w, s);
+        gdr::prof_after("gdn2_intra", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
+    }
+    gdr::prof_before(s);
+    e = gdr::launch_state_fwd_xy(int(D), out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o, s);
+    gdr::prof_after("gdn2_state", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+extern "C" gdr_status gdr_gdn2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,
+                                           int32_t in_dtype, int32_t out_dtype, float scale, const void* q,
+                                           const void* k, const void* v, const float* erase, const float* write,
+                                           const float* alpha, float* S, void* o, void* stream) {
+    gdr_desc d;
+    std::memset(&d, 0, sizeof d);
+    d.B = N; d.T = 1; d.H = H; d.dk = dk; d.dv = dv; d.gate = gate; d.in_dtype = in_dtype;
+    d.out_dtype = out_dtype; d.scale = scale; d.chunk = 0;
+    gdr_status st = check_desc(&d, nullptr);
+    if (st != GDR_OK) return st;
+    const int64_t nslab = N * H;
+    if (nslab == 0) return GDR_OK;
+    if (nslab > 2147483647LL) return fail(GDR_ERR_INVALID_ARG, "N*H too large for one launch");
+    if (!q || !k || !v || !erase || !write || !S || !o)
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, erase, write, S and o are required");
+    if ((gate == GDR_GATE_NONE) != (alpha == nullptr))
+        return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
+    const void* ptrs[] = {q, k, v, erase, write, alpha, S, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+    const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const size_t n = size_t(nslab) * dk;
+    const size_t s_bytes = size_t(nslab) * dk * dv * 4;
+    const size_t a_bytes = gate == GDR_GATE_CHANNEL ? n * 4 : size_t(nslab) * 4;
+    struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{q, n * ib}, {k, n * ib}, {v, n * ib}, {erase, n * 4}, {write, n * 4}, {alpha, a_bytes}};
+    for (auto& in : ins) {
+        if (overlap(o, n * ob, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "o overlaps an input");
+        if (overlap(S, s_bytes, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "S overlaps an input");
+    }
+    if (overlap(S, s_bytes, o, n * ob)) return fail(GDR_ERR_INVALID_ARG, "o overlaps S");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const bool bf = in_dtype != GDR_FP32;
+        const uint32_t F = gdr::CHECK_FINITE;
+        const Check checks[] = {
+            {q, int64_t(n), bf, F, "q"},         {k, int64_t(n), bf, F, "k"},         {v, int64_t(n), bf, F, "v"},
+            {erase, int64_t(n), false, F, "erase"}, {write, int64_t(n), false, F, "write"},
+            {alpha, int64_t(a_bytes / 4), false, gdr::CHECK_ALPHA_CLOSED, "alpha"},
+            {S, int64_t(s_bytes / 4), false, F, "S"},
+        };
+        gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
+        if (g != GDR_OK) return g;
+    }
+    gdr::prof_before(s);
+    hipError_t e = gdr::launch_gdn2_decode(int(dk), gate, in_dtype == GDR_FP32, out_dtype == GDR_FP32, nslab, scale,
+                                           q, k, v, erase, write, alpha, S, o, s);
+    gdr::prof_after("gdn2_decode", s);
+    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
 namespace gdr {
 
 // Entry points defined in other sources share the forward and the error text.

@@ -1,0 +1,571 @@
+// gdr_gdn2.hip -- Gated DeltaNet-2: separate erase and write gates.
+//
+// The popular article on the study (its Gated DeltaNet-2 paragraph) describes
+// this member in words only: erasing old content and writing new content are
+// decoupled and steered by two gates computed independently from the token, an
+// erase gate choosing the regions of the memory to clear and a write gate the
+// regions to write; equal gates fall back to Kimi Delta Attention.  The regions
+// are read as key channels (rows of S), the gates as dk-vectors e_t, w_t:
+//     S_t = (I - (e_t*k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t*k_t) v_t^T
+//     o_t = scale * S_t^T q_t
+// With e = w = beta 1 this is the KDA step.
+//
+// Chunked form (chunk start state S, G_r the in-chunk cumulative log2 decay,
+// Kt = K*2^G, Qt = Q*2^G, Eh = (e*K)*2^-G, Wh = (w*K)*2^-G, Eb = (e*K)*2^(G_last-G),
+// Wb = (w*K)*2^(G_last-G), all row-wise; P the rows of the predictions S'^T k):
+//     M_e = strict_tril(Kt Eh^T)   M_w = strict_tril(Kt Wh^T)
+//     A_e = tril(Qt Eh^T)          A_w = tril(Qt Wh^T)
+//     P   = N (Kt S + M_w V),      N = (I + M_e)^-1
+//     O   = Qt S + A_w V - A_e P
+//     S'  = Diag(2^G_last) S + Wb^T V - Eb^T P
+// Only P depends on S, through W = N Kt.  The intra-chunk kernel writes the
+// operands of the fp32 state pass, with U = -P = Ut - W S:
+//     W = N Kt, Ut = -N M_w V, Qt, KbT = Eb^T, A = A_e, gam, X = Wb^T V, Y = A_w V
+// and the pass runs U = Ut - W S, O = scale (Qt S + A U + Y),
+// S <- Diag(gam) S + KbT U + X.
+//
+// Range of the decay factors: every product of a row factor 2^(G_r - ref) and a
+// column factor 2^(ref - G_j) uses a reference between the two (the end of the
+// column block for blocks below the diagonal, so both factors are at most 1;
+// the start of the block on the diagonal, where the column factor is at most
+// 2^rho for the block's decay range rho).  A diagonal block whose range exceeds
+// 60 (in log2) is computed pair by pair with 2^(G_r - G_j) formed directly.
+// All chunk products run on fp32 matrix cores, except the three with V as an
+// operand (X, Y, M_w V), which take fp16 operands for bf16 inputs.
+#include <type_traits>
+
+#include "gdr_common.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+namespace {
+
+constexpr int NT2 = 256;  // threads of the intra-chunk kernel
+
+// wave-wide maximum
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+template <typename OpT>
+__device__ __forceinline__ void set_frag(Frag<OpT>& f, const float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = from_f32<OpT>(x[i]);
+}
+
+template <int D, int GATE, bool IN_F32>
+__global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
+                                                         const void* __restrict__ k_, const void* __restrict__ v_,
+                                                         const float* __restrict__ erase,
+                                                         const float* __restrict__ write,
+                                                         const float* __restrict__ alpha, ChunkWs ws) {
+    using InT = typename InType<IN_F32>::T;
+    // operand type of the products with V: fp16 for bf16 inputs, fp32 for fp32 inputs
+    using VOpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    constexpr int P = NT2 / D;       // row parts of the channel-per-thread layout
+    constexpr int RPP = CHUNK / P;   // rows per part
+    constexpr int NCT = D / 16;      // 16-column tiles of a [..][D] matrix
+
+    // sM: M_e, M_w, A_e, A_w [64][64]; sA: G, then V, then M_w V [64][D];
+    // sB: Wb, then Kt [64][D]
+    __shared__ __attribute__((aligned(16))) float sM[4][CHUNK * CHUNK];
+    __shared__ __attribute__((aligned(16))) float sA[CHUNK * D];
+    __shared__ __attribute__((aligned(16))) float sB[CHUNK * D];
+    __shared__ float s_tot[P][D];
+
+    const int64_t ch = blockIdx.x;  // chunk-head: (b * H + h) * NC + c
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t t0 = c * CHUNK;
+    const int nvalid = static_cast<int>(T - t0 < CHUNK ? T - t0 : CHUNK);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const InT* q = reinterpret_cast<const InT*>(q_);
+    const InT* k = reinterpret_cast<const InT*>(k_);
+    const InT* v = reinterpret_cast<const InT*>(v_);
+    auto tok = [&](int r) -> int64_t { return (b * T + t0 + r) * H + h; };
+
+    // ---- phase 1: G, the in-chunk inclusive cumulative log2 decay, per channel
+    for (int i = tid; i < CHUNK * CHUNK; i += NT2) {
+        sM[0][i] = 0.f;
+        sM[1][i] = 0.f;
+        sM[2][i] = 0.f;
+        sM[3][i] = 0.f;
+    }
+    const int cc = tid % D, part = tid / D;
+    {
+        float g = 0.f, G[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = part * RPP + j;
+            float la = 0.f;  // rows past the sequence decay by nothing
+            if (GATE != GATE_NONE && r < nvalid) {
+                const float a = GATE == GATE_SCALAR ? alpha[tok(r)] : alpha[tok(r) * D + cc];
+                la = log2_fast(a);
+            }
+            g += la;
+            G[j] = g;
+        }
+        s_tot[part][cc] = g;
+        __syncthreads();
+        float carry = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) carry += (p < part) ? s_tot[p][cc] : 0.f;
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) sA[(part * RPP + j) * D + cc] = G[j] + carry;
+    }
+    __syncthreads();
+    const float* sG = sA;
+
+    // ---- phase 2: the four C x C matrices, 16 x 16 block pairs (R, J), J <= R
+    {
+        const int pairR[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+        const int pairJ[10] = {0, 1, 2, 3, 0, 1, 2, 0, 1, 0};
+        for (int pi = wid; pi < 10; pi += 4) {
+            const int R = pairR[pi], J = pairJ[pi];
+            bool exact = false;
+            if (R == J) {
+                float rho = 0.f;
+                for (int c2 = lane; c2 < D; c2 += WAVE)
+                    rho = fmaxf(rho, sG[(16 * R) * D + c2] - sG[(16 * R + 15) * D + c2]);
+                exact = wave_max(rho) > 60.f;
+            }
+            const int refrow = R == J ? 16 * R : 16 * J + 15;
+            if (!exact) {
+                float4v aMe = zero4(), aMw = zero4(), aAe = zero4(), aAw = zero4();
+                const int rr = 16 * R + (lane & 15), jj = 16 * J + (lane & 15), kg = 8 * (lane >> 4);
+#pragma unroll
+                for (int kq = 0; kq < D / 32; ++kq) {
+                    const int c0 = 32 * kq + kg;
+                    float xk[8], xq[8], ye[8], yw[8];
+                    if (rr < nvalid) {
+                        load8f(k + tok(rr) * D + c0, xk);
+                        load8f(q + tok(rr) * D + c0, xq);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) xk[i] = xq[i] = 0.f;
+                    }
+                    if (jj < nvalid) {
+                        float kj[8];
+                        load8f(k + tok(jj) * D + c0, kj);
+                        load8f(erase + tok(jj) * D + c0, ye);
+                        load8f(write + tok(jj) * D + c0, yw);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            ye[i] *= kj[i];
+                            yw[i] *= kj[i];
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ye[i] = yw[i] = 0.f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float ref = sG[refrow * D + c0 + i];
+                        const float fr = exp2_fast(sG[rr * D + c0 + i] - ref);
+                        const float fc = exp2_fast(ref - sG[jj * D + c0 + i]);
+                        xk[i] *= fr;
+                        xq[i] *= fr;
+                        ye[i] *= fc;
+                        yw[i] *= fc;
+                    }
+                    Frag<float> Ak, Aq, Be, Bw;
+                    set_frag(Ak, xk);
+                    set_frag(Aq, xq);
+                    set_frag(Be, ye);
+                    set_frag(Bw, yw);
+                    mma(Ak, Be, aMe);
+                    mma(Ak, Bw, aMw);
+                    mma(Aq, Be, aAe);
+                    mma(Aq, Bw, aAw);
+                }
+                // lane: column jj, rows 16R + 4(lane / 16) + e
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * R + 4 * (lane >> 4) + e;
+                    const bool keepM = J < R || jj < r, keepA = J < R || jj <= r;
+                    sM[0][r * CHUNK + jj] = keepM ? aMe[e] : 0.f;
+                    sM[1][r * CHUNK + jj] = keepM ? aMw[e] : 0.f;
+                    sM[2][r * CHUNK + jj] = keepA ? aAe[e] : 0.f;
+                    sM[3][r * CHUNK + jj] = keepA ? aAw[e] : 0.f;
+                }
+            } else {
+                // diagonal block with a large decay range: 2^(G_r - G_j) per pair.
+                // lane: row rr, columns 16R + 4(lane / 16) + i, i < 4
+                const int rr = 16 * R + (lane & 15), jb = 16 * R + 4 * (lane >> 4);
+                float me[4] = {0.f, 0.f, 0.f, 0.f}, mw[4] = {0.f, 0.f, 0.f, 0.f};
+                float ae[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
+                if (rr < nvalid) {
+                    for (int c2 = 0; c2 < D; ++c2) {
+                        const float gr = sG[rr * D + c2];
+                        const float kr = to_f32(k[tok(rr) * D + c2]), qr = to_f32(q[tok(rr) * D + c2]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = jb + i;
+                            if (j <= rr) {
+                                const float f = exp2_fast(gr - sG[j * D + c2]);
+                                const float kj = to_f32(k[tok(j) * D + c2]);
+                                const float ej = erase[tok(j) * D + c2] * kj * f;
+                                const float wj = write[tok(j) * D + c2] * kj * f;
+                                me[i] += kr * ej;
+                                mw[i] += kr * wj;
+                                ae[i] += qr * ej;
+                                aw[i] += qr * wj;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jb + i;
+                    sM[0][rr * CHUNK + j] = j < rr ? me[i] : 0.f;
+                    sM[1][rr * CHUNK + j] = j < rr ? mw[i] : 0.f;
+                    sM[2][rr * CHUNK + j] = j <= rr ? ae[i] : 0.f;
+                    sM[3][rr * CHUNK + j] = j <= rr ? aw[i] : 0.f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: row-wise operands; Wb into sB; Kt kept in registers
+    float* Qt = static_cast<float*>(ws.Qt) + ch * CHUNK * D;
+    float* KbT = static_cast<float*>(ws.KbT) + ch * D * CHUNK;
+    float kt[RPP];
+    {
+        const float gl = sG[(CHUNK - 1) * D + cc];  // rows past the sequence carry the last decay
+        if (part == 0) ws.gam[ch * D + cc] = exp2_fast(gl);
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = part * RPP + j;
+            float kv = 0.f, qv = 0.f, ev = 0.f, wv = 0.f;
+            if (r < nvalid) {
+                kv = to_f32(k[tok(r) * D + cc]);
+                qv = to_f32(q[tok(r) * D + cc]);
+                ev = erase[tok(r) * D + cc];
+                wv = write[tok(r) * D + cc];
+            }
+            const float gr = sG[r * D + cc];
+            const float f0 = exp2_fast(gr), fl = exp2_fast(gl - gr);
+            kt[j] = kv * f0;
+            Qt[frag_off<D>(r, cc)] = qv * f0;
+            KbT[frag_off<CHUNK>(cc, r)] = ev * kv * fl;
+            sB[r * D + cc] = wv * kv * fl;
+        }
+        // A = A_e in fragment order, eight consecutive columns per store pair
+        float* A = static_cast<float*>(ws.A) + ch * CHUNK * CHUNK;
+        for (int run = tid; run < CHUNK * CHUNK / 8; run += NT2) {
+            const int r = run / (CHUNK / 8), j0 = 8 * (run % (CHUNK / 8));
+            float4v lo, hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = sM[2][r * CHUNK + j0 + e];
+                hi[e] = sM[2][r * CHUNK + j0 + 4 + e];
+            }
+            float* dst = A + frag_off<CHUNK>(r, j0);
+            reinterpret_cast<float4v*>(dst)[0] = lo;
+            reinterpret_cast<float4v*>(dst)[1] = hi;
+        }
+    }
+    __syncthreads();
+    // V (fp32) over G
+    for (int i = tid; i < CHUNK * D / 8; i += NT2) {
+        const int r = i / (D / 8), c0 = 8 * (i % (D / 8));
+        float x[8];
+        if (r < nvalid) {
+            load8f(v + tok(r) * D + c0, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        float4v lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo[e] = x[e];
+            hi[e] = x[4 + e];
+        }
+        reinterpret_cast<float4v*>(sA + r * D + c0)[0] = lo;
+        reinterpret_cast<float4v*>(sA + r * D + c0)[1] = hi;
+    }
+    __syncthreads();
+
+    // ---- X = Wb^T V [D][D] (contraction over the 64 rows), accumulator order
+    const int l16 = lane & 15, kg = 8 * (lane >> 4);
+    {
+        float* X = ws.X + ch * D * D;
+        for (int tile = wid; tile < NCT * NCT; tile += 4) {
+            const int mt = tile / NCT, nt = tile % NCT;
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < CHUNK / 32; ++kq) {
+                float xa[8], xb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 32 * kq + kg + i;
+                    xa[i] = sB[r * D + 16 * mt + l16];
+                    xb[i] = sA[r * D + 16 * nt + l16];
+                }
+                Frag<VOpT> fa, fb;
+                set_frag(fa, xa);
+                set_frag(fb, xb);
+                mma(fa, fb, acc);
+            }
+            *reinterpret_cast<float4v*>(X + ((mt * NCT + nt) * WAVE + lane) * 4) = acc;
+        }
+    }
+
+    // ---- Y = A_w V and M_w V [64][D] (contraction over the 64 columns)
+    constexpr int MT = CHUNK / 16 * NCT;  // 16 x 16 tiles of a [64][D] result
+    constexpr int MPW = MT / 4;           // per wave
+    float4v mwv[MPW];
+    {
+        float* Y = ws.Y + ch * CHUNK * D;
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int tile = wid + 4 * i;
+            const int mt = tile / NCT, nt = tile % NCT;
+            float4v ay = zero4(), am = zero4();
+#pragma unroll
+            for (int kq = 0; kq < CHUNK / 32; ++kq) {
+                float xw[8], xm[8], xb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * kq + kg + e;
+                    xw[e] = sM[3][(16 * mt + l16) * CHUNK + j];
+                    xm[e] = sM[1][(16 * mt + l16) * CHUNK + j];
+                    xb[e] = sA[j * D + 16 * nt + l16];
+                }
+                Frag<VOpT> fw, fm, fb;
+                set_frag(fw, xw);
+                set_frag(fm, xm);
+                set_frag(fb, xb);
+                mma(fw, fb, ay);
+                mma(fm, fb, am);
+            }
+            *reinterpret_cast<float4v*>(Y + ((mt * NCT + nt) * WAVE + lane) * 4) = ay;
+            mwv[i] = am;
+        }
+    }
+    __syncthreads();  // every read of Wb (sB) and V (sA) is done
+    // right-hand sides of the solve: Kt into sB, M_w V into sA (row-major)
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) sB[(part * RPP + j) * D + cc] = kt[j];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int tile = wid + 4 * i;
+        const int mt = tile / NCT, nt = tile % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sA[(16 * mt + 4 * (lane >> 4) + e) * D + 16 * nt + l16] = mwv[i][e];
+    }
+    __syncthreads();
+
+    // ---- phase 5: (I + M_e) [W | Vt] = [Kt | M_w V] by forward substitution;
+    // thread t owns right-hand-side column t (2D columns)
+    if (tid < 2 * D) {
+        const bool left = tid < D;
+        const int col = left ? tid : tid - D;
+        const float* src = left ? sB : sA;
+        float z[CHUNK];
+#pragma unroll
+        for (int r = 0; r < CHUNK; ++r) z[r] = src[r * D + col];
+#pragma unroll
+        for (int r = 1; r < CHUNK; ++r) {
+            float acc = z[r];
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= sM[0][r * CHUNK + j] * z[j];
+            z[r] = acc;
+        }
+        if (left) {
+            float* W = static_cast<float*>(ws.W) + ch * CHUNK * D;
+#pragma unroll
+            for (int r = 0; r < CHUNK; ++r) W[frag_off<D>(r, col)] = z[r];
+        } else {
+            // Ut = -Vt, accumulator order: four consecutive rows per 16-byte store
+            float* Ut = static_cast<float*>(ws.Ut) + ch * CHUNK * D;
+#pragma unroll
+            for (int r = 0; r < CHUNK; r += 4) {
+                float4v u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[e] = -z[r + e];
+                *reinterpret_cast<float4v*>(Ut + cfrag_off<D>(r, col)) = u;
+            }
+        }
+    }
+}
+
+// One Gated DeltaNet-2 step per (sequence, head) slab, the state read once and
+// written once (the structure of the KDA decode step):
+//     p = S^T (alpha*k), r = S^T (alpha*q),
+//     S <- Diag(alpha) S - (e*k) p^T + (w*k) v^T,
+//     o = scale (r - (q.(e*k)) p + (q.(w*k)) v)   (= scale S_new^T q)
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void gdn2_decode_kernel(int64_t nslab, float scale, const void* __restrict__ q_,
+                                                          const void* __restrict__ k_, const void* __restrict__ v_,
+                                                          const float* __restrict__ erase,
+                                                          const float* __restrict__ write,
+                                                          const float* __restrict__ alpha, float* __restrict__ S,
+                                                          void* __restrict__ o_) {
+    using InT = typename InType<IN_F32>::T;
+    using OutT = typename InType<OUT_F32>::T;
+    constexpr int TPR = D / 4;     // threads per state row (float4 each)
+    constexpr int RG = 256 / TPR;  // row groups
+    constexpr int RPT = D / RG;    // rows per thread
+
+    const int64_t slab = blockIdx.x;
+    if (slab >= nslab) return;
+    const int tid = threadIdx.x;
+    const int rg = tid / TPR, cg = tid % TPR;
+    const InT* q = reinterpret_cast<const InT*>(q_) + slab * D;
+    const InT* k = reinterpret_cast<const InT*>(k_) + slab * D;
+    const InT* v = reinterpret_cast<const InT*>(v_) + slab * D;
+    OutT* o = reinterpret_cast<OutT*>(o_) + slab * D;
+    float4v* Sv = reinterpret_cast<float4v*>(S + slab * (int64_t)D * D);
+
+    __shared__ float s_ak[D], s_aq[D], s_ek[D], s_wk[D], s_a[D];
+    __shared__ float s_p[RG][D], s_r[RG][D];
+    __shared__ float s_dot[2][2];
+
+    float4v st[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) st[m] = __builtin_nontemporal_load(&Sv[(rg + m * RG) * TPR + cg]);
+
+    if (tid < D) {
+        float a = 1.f;
+        if constexpr (GATE == GATE_SCALAR) a = alpha[slab];
+        if constexpr (GATE == GATE_CHANNEL) a = alpha[slab * D + tid];
+        const float kk = to_f32(k[tid]), qq = to_f32(q[tid]);
+        const float ek = erase[slab * D + tid] * kk, wk = write[slab * D + tid] * kk;
+        s_a[tid] = a;
+        s_ak[tid] = a * kk;
+        s_aq[tid] = a * qq;
+        s_ek[tid] = ek;
+        s_wk[tid] = wk;
+        float qe = qq * ek, qw = qq * wk;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            qe += __shfl_xor(qe, off);
+            qw += __shfl_xor(qw, off);
+        }
+        if ((tid & 63) == 0) {
+            s_dot[tid >> 6][0] = qe;
+            s_dot[tid >> 6][1] = qw;
+        }
+    }
+    __syncthreads();
+    const float qe = D == 128 ? s_dot[0][0] + s_dot[1][0] : s_dot[0][0];
+    const float qw = D == 128 ? s_dot[0][1] + s_dot[1][1] : s_dot[0][1];
+
+    float4v p = zero4(), r = zero4();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        p += st[m] * s_ak[i];
+        r += st[m] * s_aq[i];
+    }
+    *reinterpret_cast<float4v*>(&s_p[rg][4 * cg]) = p;
+    *reinterpret_cast<float4v*>(&s_r[rg][4 * cg]) = r;
+    __syncthreads();
+    float4v pt = zero4(), rt = zero4();
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        pt += *reinterpret_cast<const float4v*>(&s_p[g][4 * cg]);
+        rt += *reinterpret_cast<const float4v*>(&s_r[g][4 * cg]);
+    }
+    float vv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[4 * cg + e]);
+    if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * cg + e] = from_f32<OutT>(scale * (rt[e] - qe * pt[e] + qw * vv[e]));
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const float a = s_a[i], ek = s_ek[i], wk = s_wk[i];
+        float4v sn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sn[e] = __builtin_fmaf(a, st[m][e], wk * vv[e] - ek * pt[e]);
+        __builtin_nontemporal_store(sn, &Sv[i * TPR + cg]);
+    }
+}
+
+template <int D, int GATE, bool IN_F32>
+hipError_t intra_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k, const void* v,
+                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
+                   hipStream_t stream) {
+    const int64_t nch = B * H * NC;
+    if (nch == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdn2_intra_kernel<D, GATE, IN_F32>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q,
+                       k, v, erase, write, alpha, ws);
+    return hipGetLastError();
+}
+
+template <int D, int GATE>
+hipError_t intra_g(bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k, const void* v,
+                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
+                   hipStream_t stream) {
+    return in_f32 ? intra_t<D, GATE, true>(B, T, H, NC, q, k, v, erase, write, alpha, ws, stream)
+                  : intra_t<D, GATE, false>(B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+}
+
+template <int D>
+hipError_t intra_d(int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
+                   const void* v, const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
+                   hipStream_t stream) {
+    if (gate == GATE_NONE) return intra_g<D, GATE_NONE>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+    if (gate == GATE_SCALAR)
+        return intra_g<D, GATE_SCALAR>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+    return intra_g<D, GATE_CHANNEL>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+}
+
+template <int D, int GATE, bool IN_F32, bool OUT_F32>
+hipError_t decode_t(int64_t nslab, float scale, const void* q, const void* k, const void* v, const float* erase,
+                    const float* write, const float* alpha, float* S, void* o, hipStream_t stream) {
+    hipLaunchKernelGGL((gdn2_decode_kernel<D, GATE, IN_F32, OUT_F32>), dim3((unsigned)nslab), dim3(256), 0, stream,
+                       nslab, scale, q, k, v, erase, write, alpha, S, o);
+    return hipGetLastError();
+}
+
+template <int D, int GATE>
+hipError_t decode_g(bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q, const void* k,
+                    const void* v, const float* erase, const float* write, const float* alpha, float* S, void* o,
+                    hipStream_t stream) {
+    if (in_f32)
+        return out_f32 ? decode_t<D, GATE, true, true>(nslab, scale, q, k, v, erase, write, alpha, S, o, stream)
+                       : decode_t<D, GATE, true, false>(nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+    return out_f32 ? decode_t<D, GATE, false, true>(nslab, scale, q, k, v, erase, write, alpha, S, o, stream)
+                   : decode_t<D, GATE, false, false>(nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+}
+
+template <int D>
+hipError_t decode_d(int gate, bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q, const void* k,
+                    const void* v, const float* erase, const float* write, const float* alpha, float* S, void* o,
+                    hipStream_t stream) {
+    if (gate == GATE_NONE)
+        return decode_g<D, GATE_NONE>(in_f32, out_f32, nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+    if (gate == GATE_SCALAR)
+        return decode_g<D, GATE_SCALAR>(in_f32, out_f32, nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+    return decode_g<D, GATE_CHANNEL>(in_f32, out_f32, nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gdn2_intra(int D, int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q,
+                             const void* k, const void* v, const float* erase, const float* write,
+                             const float* alpha, const ChunkWs& ws, hipStream_t stream) {
+    if (D == 64) return intra_d<64>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+    return intra_d<128>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+}
+
+hipError_t launch_gdn2_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q,
+                              const void* k, const void* v, const float* erase, const float* write,
+                              const float* alpha, float* S, void* o, hipStream_t stream) {
+    if (nslab == 0) return hipSuccess;
+    if (D == 64) return decode_d<64>(gate, in_f32, out_f32, nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+    return decode_d<128>(gate, in_f32, out_f32, nslab, scale, q, k, v, erase, write, alpha, S, o, stream);
+}
+
+}  // namespace gdr

@@ -51,6 +51,9 @@ struct ChunkWs {
     // prologue: activated beta ([B,T,H] layout) and the reciprocal row norms of
     // q and k (negative where the norm was clamped), written by the intra kernel
     float *Bact, *rq, *rk;
+    // separate erase and write gates (Gated DeltaNet-2), fp32 accumulator order:
+    // X [D][D] added to the state after each chunk, Y [64][D] added to its output
+    float *X, *Y;
 };
 
 // Per-launch event timing (gdr_profile_begin/end); no-ops unless enabled.
@@ -89,6 +92,23 @@ hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t
                             int64_t NC, float scale, const ChunkWs& ws, const float* S0,
                             float* ST, void* o, bool save_for_backward, bool wide, ChunkRange cr,
                             hipStream_t stream);
+
+// The pass of the separate-gate variant (Gated DeltaNet-2): fp32 operands of ws
+// (W, Ut, Qt, KbT, A, gam, X, Y) over whole sequences, o computed in the pass.
+hipError_t launch_state_fwd_xy(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                               const ChunkWs& ws, const float* S0, float* ST, void* o, hipStream_t stream);
+
+// Gated DeltaNet-2 (separate erase and write gates e, w [B,T,H,D] fp32): the
+// intra-chunk kernel writes the pass's operands into ws (fp32): W = N Kt,
+// Ut = -N M_w V, Qt, KbT = (e*K*2^(G_last - G))^T, A = tril(Qt (e*Kh)^T), gam,
+// X = ((w*K)*2^(G_last - G))^T V and Y = tril(Qt (w*Kh)^T) V, with
+// N = (I + strict_tril(Kt (e*Kh)^T))^-1.
+hipError_t launch_gdn2_intra(int D, int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q,
+                             const void* k, const void* v, const float* erase, const float* write,
+                             const float* alpha, const ChunkWs& ws, hipStream_t stream);
+hipError_t launch_gdn2_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q,
+                              const void* k, const void* v, const float* erase, const float* write,
+                              const float* alpha, float* S, void* o, hipStream_t stream);
 
 // dh_cler (NULL = none): gradient at the hidden stream of the error-routing
 // epilogue, which adds lam * dh / beta to dU.

@@ -36,19 +36,23 @@ struct StateCfg {
 
 // Operand fragments of one chunk, held in registers exactly as loaded (no
 // conversion at load time, so issuing a prefetch never waits for it).
-template <int D, bool IN_F32>
+// XY: the chunk also carries the additive terms of the separate-gate variant
+// (Gated DeltaNet-2): x, this lane's part of the state term X added after the
+// chunk's update, and y, its part of the output term Y (fp32, accumulator order).
+template <int D, bool IN_F32, bool XY = false>
 struct ChunkFrags {
     using OpT = typename StateCfg<D, IN_F32>::OpT;
     static constexpr int SRT = StateCfg<D, IN_F32>::SRT;
     Frag<OpT> w[D / 32], q[D / 32], a[2], kb[SRT][2];
     OpT ut[4];
     float gam[SRT][4];
+    float x[XY ? SRT : 1][4], y[4];
 };
 
 // All chunk operands are stored in fragment order by the intra-chunk kernel:
 // every fragment below is one contiguous, fully coalesced 1 KiB (fp16) load.
-template <int D, bool IN_F32>
-__device__ __forceinline__ void load_chunk(ChunkFrags<D, IN_F32>& f, const ChunkWs& ws, int64_t ch,
+template <int D, bool IN_F32, bool XY = false>
+__device__ __forceinline__ void load_chunk(ChunkFrags<D, IN_F32, XY>& f, const ChunkWs& ws, int64_t ch,
                                            int j0, int wid, int lane) {
     using Cfg = StateCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
@@ -75,6 +79,22 @@ __device__ __forceinline__ void load_chunk(ChunkFrags<D, IN_F32>& f, const Chunk
     const OpT* Ut = reinterpret_cast<const OpT*>(ws.Ut) + ch * CHUNK * D + ((wid * (D / 16) + j0 / 16) * 64 + lane) * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) f.ut[e] = Ut[e];
+    if constexpr (XY) {
+        // X [D][D] and Y [64][D], accumulator order: this lane's four rows of
+        // column j0 + lane % 16 of the wave's state tiles and output rows
+#pragma unroll
+        for (int m = 0; m < Cfg::SRT; ++m) {
+            const int rt = wid * (D / 64) + m;
+            const float4v xv = *reinterpret_cast<const float4v*>(
+                ws.X + ch * D * D + ((rt * (D / 16) + j0 / 16) * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f.x[m][e] = xv[e];
+        }
+        const float4v yv = *reinterpret_cast<const float4v*>(
+            ws.Y + ch * CHUNK * D + ((wid * (D / 16) + j0 / 16) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.y[e] = yv[e];
+    }
 }
 
 template <typename OpT>
@@ -108,8 +128,8 @@ __device__ __forceinline__ void st4(OpT* dst, const float4v& v) {
     }
 }
 
-template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O>
-__device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int64_t c, int64_t T, int H,
+template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O, bool XY = false>
+__device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32, XY>& cur, int64_t c, int64_t T, int H,
                                            int64_t b, int h, int64_t bh, int64_t NC, int j0, int wid,
                                            int l16, int g4, float scale, const ChunkWs& ws,
                                            float4v (&S)[StateCfg<D, IN_F32>::SRT],
@@ -155,6 +175,10 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
     if constexpr (HAS_O) {
         mma(cur.a[0], fu0, oacc);
         mma(cur.a[1], fu1, oacc);  // zero block for waves 0 and 1
+        if constexpr (XY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[e] += cur.y[e];
+        }
         const int64_t tbase = c * CHUNK + 16 * wid + 4 * g4;
         OutT* op = o + ((b * T + tbase) * H + h) * D + j0 + l16;
         const int64_t tstride = static_cast<int64_t>(H) * D;
@@ -192,6 +216,10 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32>& cur, int
         for (int e = 0; e < 4; ++e) S[m][e] *= cur.gam[m][e];
         mma(cur.kb[m][0], fu0, S[m]);
         mma(cur.kb[m][1], fu1, S[m]);
+        if constexpr (XY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[m][e] += cur.x[m][e];
+        }
         st4<OpT>(s_S + l16 * LDS_S + wid * (D / 4) + 16 * m + 4 * g4, S[m]);
     }
     __syncthreads();
@@ -244,7 +272,7 @@ __device__ __forceinline__ void touch_chunk(uint32_t (&out)[NPF], const ChunkWs&
     }
 }
 
-template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O>
+template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O, bool XY = false>
 __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_t NC, float scale,
                                                         ChunkWs ws, const float* S0,
                                                         float* ST, void* __restrict__ o_) {
@@ -318,18 +346,18 @@ __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_
     // The prefetch is unconditional (the chunk index is clamped to the last
     // chunk) so that the compiler can count outstanding loads exactly and wait
     // only for the chunk about to be used.
-    ChunkFrags<D, IN_F32> fa, fb;
+    ChunkFrags<D, IN_F32, XY> fa, fb;
     const int64_t last = NC - 1;
-    if (NC > 0) load_chunk<D, IN_F32>(fa, ws, bh * NC, j0, wid, lane);
+    if (NC > 0) load_chunk<D, IN_F32, XY>(fa, ws, bh * NC, j0, wid, lane);
 #pragma unroll 1
     for (int64_t c = 0; c < NC; c += 2) {
-        load_chunk<D, IN_F32>(fb, ws, bh * NC + (c + 1 < NC ? c + 1 : last), j0, wid, lane);
-        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O>(fa, c, T, H, b, h, bh, NC, j0, wid, l16, g4, scale, ws,
-                                                    S, s_S, s_U, o);
+        load_chunk<D, IN_F32, XY>(fb, ws, bh * NC + (c + 1 < NC ? c + 1 : last), j0, wid, lane);
+        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O, XY>(fa, c, T, H, b, h, bh, NC, j0, wid, l16, g4, scale, ws,
+                                                        S, s_S, s_U, o);
         if (c + 1 >= NC) break;
-        load_chunk<D, IN_F32>(fa, ws, bh * NC + (c + 2 < NC ? c + 2 : last), j0, wid, lane);
-        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O>(fb, c + 1, T, H, b, h, bh, NC, j0, wid, l16, g4, scale,
-                                                    ws, S, s_S, s_U, o);
+        load_chunk<D, IN_F32, XY>(fa, ws, bh * NC + (c + 2 < NC ? c + 2 : last), j0, wid, lane);
+        state_step<D, IN_F32, OUT_F32, SAVE, HAS_O, XY>(fb, c + 1, T, H, b, h, bh, NC, j0, wid, l16, g4, scale,
+                                                        ws, S, s_S, s_U, o);
     }
 
     if (ST) {
@@ -593,6 +621,27 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
         hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false, true>), dim3((unsigned)nblk), dim3(320),
                            0, stream, T, H, NC, scale, ws, S0, ST, o);
     return hipGetLastError();
+}
+
+// The separate-gate variant's pass: fp32 operands, output computed in the pass,
+// plus the per-chunk terms X (state) and Y (output) of ws.
+template <int D, bool OUT_F32>
+static hipError_t launch_state_xy_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
+                                    const float* S0, float* ST, void* o, hipStream_t stream) {
+    const int64_t nblk = B * H * StateCfg<D, true>::NSL;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((state_fwd_kernel<D, true, OUT_F32, false, true, true>), dim3((unsigned)nblk), dim3(320), 0,
+                       stream, T, H, NC, scale, ws, S0, ST, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_fwd_xy(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                               const ChunkWs& ws, const float* S0, float* ST, void* o, hipStream_t stream) {
+    if (D == 64)
+        return out_f32 ? launch_state_xy_t<64, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
+                       : launch_state_xy_t<64, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
+    return out_f32 ? launch_state_xy_t<128, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
+                   : launch_state_xy_t<128, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
 }
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,

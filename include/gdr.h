@@ -281,6 +281,41 @@ gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const v
                                     const void* dy, void* dO, void* dg, float* dw, void* ws, size_t ws_bytes,
                                     void* stream);
 
+/* Gated DeltaNet-2: separate erase and write gates (popular article on the
+ * study, its Gated DeltaNet-2 paragraph, which describes the mechanism in words
+ * only: erasing and writing decoupled, each steered by its own gate computed
+ * from the token, the erase gate choosing the regions of the memory to clear,
+ * the write gate the regions to write; equal gates fall back to Kimi Delta
+ * Attention).  Reading implemented, with the regions taken as key channels:
+ *     S_t = (I - (e_t*k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t*k_t) v_t^T
+ *     o_t = scale * S_t^T q_t                          (* elementwise)
+ *   erase, write  [B, T, H, dk] fp32 (any finite values; gates in [0, 1])
+ *   q, k, v, alpha, S0, ST, o as for gdr_forward_chunked; e = w = beta 1
+ *   computes what gdr_forward_chunked computes.
+ * desc->route and desc->prologue must be 0 (no hidden-stream epilogue: the
+ * article leaves open what routing the written value means here), else
+ * GDR_ERR_UNSUPPORTED.  The chunk products run with fp32 operands (fp16 for
+ * the three products with v when v is bf16) and the state pass with fp32
+ * operands; forward only (no backward in this version).
+ * ws: at least gdr_gdn2_workspace_size(desc) bytes (240.5 KiB per chunk-head
+ * of 64 tokens at dk = dv = 128). */
+size_t gdr_gdn2_workspace_size(const gdr_desc* desc);
+gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* erase, const float* write, const float* alpha,
+                                    const float* S0, void* o, float* ST, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* One Gated DeltaNet-2 step for N sequences, S [N,H,dk,dv] fp32 in place:
+ *   p = S^T (alpha*k), r = S^T (alpha*q),
+ *   S <- Diag(alpha) S - (e*k) p^T + (w*k) v^T,
+ *   o = scale (r - (q.(e*k)) p + (q.(w*k)) v),
+ * exactly one step of the recurrence above; erase, write [N,H,dk] fp32, the
+ * other arguments as for gdr_decode_step.  No workspace. */
+gdr_status gdr_gdn2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,
+                                int32_t in_dtype, int32_t out_dtype, float scale, const void* q,
+                                const void* k, const void* v, const float* erase, const float* write,
+                                const float* alpha, float* S, void* o, void* stream);
+
 /* Static text for a status code. */
 const char* gdr_status_string(gdr_status status);
 

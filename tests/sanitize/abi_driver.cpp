@@ -127,6 +127,41 @@ int main() {
                         }
     run_pair(desc(1, 200, 2, 128, 2, GDR_FP32, GDR_FP32), false);  // fp32 at d = 128: backward unsupported
 
+    // the separate-gate variant (Gated DeltaNet-2): forward and decode
+    for (int gate = 0; gate < 3; ++gate)
+        for (int in = 0; in < 2; ++in)
+            for (int64_t T : {int64_t(0), int64_t(1), int64_t(130)}) {
+                const int64_t d = in == GDR_FP32 ? 64 : 128;
+                gdr_desc x = desc(2, T, 3, d, gate, in, GDR_FP32);
+                const size_t n = size_t(2 * T * 3 * d), ns = size_t(2 * 3 * d * d), ib = in == GDR_FP32 ? 4 : 2;
+                const size_t na = gate == GDR_GATE_CHANNEL ? n : size_t(2 * T * 3);
+                Buf q(n * ib), k(n * ib), v(n * ib), e(n * 4), w(n * 4), a(na * 4), S0(ns * 4), o(n * 4), ST(ns * 4);
+                const size_t need = gdr_gdn2_workspace_size(&x);
+                EXPECT(T == 0 || need > 0, "gdn2 workspace size 0");
+                Buf ws(need);
+                stub::ws_lo = ws.p;
+                stub::ws_hi = ws.p + need;
+                auto F = [](char* p) { return reinterpret_cast<float*>(p); };
+                const float* al = gate == GDR_GATE_NONE ? nullptr : F(a.p);
+                EXPECT(gdr_gdn2_forward_chunked(&x, q.p, k.p, v.p, F(e.p), F(w.p), al, F(S0.p), o.p, F(ST.p), ws.p,
+                                                need, nullptr) == GDR_OK, "gdn2 forward");
+                if (need > 0)
+                    EXPECT(gdr_gdn2_forward_chunked(&x, q.p, k.p, v.p, F(e.p), F(w.p), al, F(S0.p), o.p, F(ST.p),
+                                                    ws.p, need - 1, nullptr) == GDR_ERR_WORKSPACE,
+                           "gdn2 short workspace");
+                if (T > 0)
+                    EXPECT(gdr_gdn2_forward_chunked(&x, q.p, k.p, v.p, F(e.p), F(w.p), al, F(S0.p), e.p, F(ST.p),
+                                                    ws.p, need, nullptr) == GDR_ERR_INVALID_ARG,
+                           "gdn2 o aliasing erase");
+                gdr_desc xr = x;
+                xr.route = GDR_ROUTE_ERROR;
+                EXPECT(gdr_gdn2_workspace_size(&xr) == 0, "gdn2 with a route accepted");
+                stub::ws_lo = stub::ws_hi = nullptr;
+                if (T == 1)
+                    EXPECT(gdr_gdn2_decode_step(2, 3, d, d, gate, in, GDR_FP32, 1.f, q.p, k.p, v.p, F(e.p), F(w.p), al,
+                                                F(S0.p), o.p, nullptr) == GDR_OK, "gdn2 decode");
+            }
+
     // decode and the output gate
     {
         const int64_t N = 3, H = 2, d = 64;

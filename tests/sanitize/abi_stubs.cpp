@@ -19,7 +19,8 @@ long launches = 0;
 namespace {
 
 void in_ws(const void* p, const char* what) {
-    if (!p || !stub::ws_lo) return;
+    // an empty workspace (no chunks) carves pointers that are never read
+    if (!p || !stub::ws_lo || stub::ws_lo == stub::ws_hi) return;
     const char* c = static_cast<const char*>(p);
     if (c < stub::ws_lo || c >= stub::ws_hi) {
         std::fprintf(stderr, "workspace pointer %s outside the workspace\n", what);
@@ -113,6 +114,25 @@ hipError_t launch_cler_fwd(int, bool, int64_t, int64_t, int, int64_t, const Chun
 hipError_t launch_cler_mt(int, bool, int64_t, int64_t, int, int64_t, const ChunkWs& ws, const float*, const void*,
                           hipStream_t) {
     check_ws(ws);
+    ++stub::launches;
+    return hipSuccess;
+}
+hipError_t launch_state_fwd_xy(int, bool, int64_t, int64_t, int, int64_t, float, const ChunkWs& ws, const float*,
+                               float*, void*, hipStream_t) {
+    check_ws(ws);
+    in_ws(ws.X, "X");
+    in_ws(ws.Y, "Y");
+    ++stub::launches;
+    return hipSuccess;
+}
+hipError_t launch_gdn2_intra(int, int, bool, int64_t, int64_t, int, int64_t, const void*, const void*, const void*,
+                             const float*, const float*, const float*, const ChunkWs& ws, hipStream_t) {
+    check_ws(ws);
+    ++stub::launches;
+    return hipSuccess;
+}
+hipError_t launch_gdn2_decode(int, int, bool, bool, int64_t, float, const void*, const void*, const void*,
+                              const float*, const float*, const float*, float*, void*, hipStream_t) {
     ++stub::launches;
     return hipSuccess;
 }

@@ -92,6 +92,22 @@ static void one(int64_t B, int64_t T, int64_t H, int64_t d, int gate, int s0) {
         CHECK(maxdiff < 1e-12, "decode steps differ from the forward");
         free(S); free(qt); free(kt); free(vt); free(bt); free(at); free(ot);
     }
+    /* Gated DeltaNet-2 with equal gates reproduces the forward above */
+    {
+        double *g = arr(n, 0, 0), *og = arr(n, 0, 0), *STg = arr(ns, 0, 0);
+        for (size_t i = 0; i < n; ++i) g[i] = beta[i / (size_t)d];
+        CHECK(oracle_gdn2_forward(B, T, H, d, d, gate, 0.7, q, k, v, g, g, al, S0, og, STg, 3) == 0, "gdn2 forward");
+        double md = 0;
+        for (size_t i = 0; i < n; ++i) md = fmax(md, fabs(og[i] - o[i]));
+        for (size_t i = 0; i < ns; ++i) md = fmax(md, fabs(STg[i] - ST[i]));
+        CHECK(md < 1e-12, "gdn2 with equal gates differs from the forward");
+        if (T > 0) {
+            double* S = arr(ns, 0, 0);
+            CHECK(oracle_gdn2_decode(B, H, d, d, gate, 0.7, q, k, v, g, g, al, S, og, 2) == 0, "gdn2 decode");
+            free(S);
+        }
+        free(g); free(og); free(STg);
+    }
     double* hin = arr(n, -1, 1), *hout = arr(n, 0, 0), *lam = arr((size_t)(H * d), -1, 1), *dlam = arr((size_t)(H * d), 0, 0);
     CHECK(oracle_clvr_forward(B, T, H, d, hin, v, lam, hout) == 0, "clvr forward");
     CHECK(oracle_clvr_forward(B, T, H, d, hin, v, NULL, hin) == 0, "clvr in place");
