@@ -738,7 +738,7 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
 // Gated DeltaNet-2 (separate erase and write gates): fp32 chunk operands and the
 // two additive terms X, Y per chunk-head.
 // ---------------------------------------------------------------------------
-static size_t gdn2_ws_bytes(int64_t nch, int D, gdr::ChunkWs* out, void* base) {
+static size_t gdn2_ws_bytes(int64_t nch, int D, int op_bytes, gdr::ChunkWs* out, void* base) {
     gdr::ChunkWs w;
     std::memset(&w, 0, sizeof w);
     size_t off = 0;
@@ -748,15 +748,15 @@ static size_t gdn2_ws_bytes(int64_t nch, int D, gdr::ChunkWs* out, void* base) {
         off += align_up(bytes);
         return r;
     };
-    const size_t mat = size_t(nch) * kChunk * D * 4;
+    const size_t mat = size_t(nch) * kChunk * D * op_bytes;  // [64][D] in operand precision
     w.W = take(mat);
     w.Ut = take(mat);
     w.Qt = take(mat);
     w.KbT = take(mat);
-    w.A = take(size_t(nch) * kChunk * kChunk * 4);
+    w.A = take(size_t(nch) * kChunk * kChunk * op_bytes);
     w.gam = static_cast<float*>(take(size_t(nch) * D * 4));
-    w.X = static_cast<float*>(take(size_t(nch) * D * D * 4));
-    w.Y = static_cast<float*>(take(mat));
+    w.X = static_cast<float*>(take(size_t(nch) * D * D * 4));       // fp32
+    w.Y = static_cast<float*>(take(size_t(nch) * kChunk * D * 4));  // fp32
     if (out) *out = w;
     return off;
 }
@@ -772,7 +772,8 @@ static gdr_status gdn2_check_desc(const gdr_desc* desc, int64_t* NC) {
 extern "C" size_t gdr_gdn2_workspace_size(const gdr_desc* desc) {
     int64_t NC = 0;
     if (gdn2_check_desc(desc, &NC) != GDR_OK) return 0;
-    return gdn2_ws_bytes(desc->B * desc->H * NC, int(desc->dk), nullptr, nullptr);
+    return gdn2_ws_bytes(desc->B * desc->H * NC, int(desc->dk), desc->in_dtype == GDR_FP32 ? 4 : 2, nullptr,
+                         nullptr);
 }
 
 extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
@@ -811,7 +812,7 @@ extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void*
     if (S0 && ST && S0 != ST && overlap(S0, s_bytes, ST, s_bytes))
         return fail(GDR_ERR_INVALID_ARG, "ST partially overlaps S0 (it may only alias it exactly)");
     gdr::ChunkWs w;
-    const size_t need = gdn2_ws_bytes(B * H * NC, int(D), &w, ws);
+    const size_t need = gdn2_ws_bytes(B * H * NC, int(D), desc->in_dtype == GDR_FP32 ? 4 : 2, &w, ws);
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     if (B * H == 0) return GDR_OK;
@@ -842,7 +843,7 @@ extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void*
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
     }
     gdr::prof_before(s);
-    e = gdr::launch_state_fwd_xy(int(D), out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o, s);
+    e = gdr::launch_state_fwd_xy(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o, s);
     gdr::prof_after("gdn2_state", s);
     if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
     return GDR_OK;

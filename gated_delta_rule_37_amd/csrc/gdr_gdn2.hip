@@ -30,8 +30,10 @@
 // the start of the block on the diagonal, where the column factor is at most
 // 2^rho for the block's decay range rho).  A diagonal block whose range exceeds
 // 60 (in log2) is computed pair by pair with 2^(G_r - G_j) formed directly.
-// All chunk products run on fp32 matrix cores, except the three with V as an
-// operand (X, Y, M_w V), which take fp16 operands for bf16 inputs.
+// The four C x C matrices are formed with fp32 operands on matrix cores.  For
+// bf16 inputs the three products with V (X, Y, M_w V) take fp16 operands and
+// the pass's operands W, Ut, Qt, KbT, A are stored in fp16 (the operand
+// precision of the KDA path); X and Y stay fp32.  fp32 inputs keep fp32 throughout.
 #include <type_traits>
 
 #include "gdr_common.hpp"
@@ -63,8 +65,11 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
                                                          const float* __restrict__ write,
                                                          const float* __restrict__ alpha, ChunkWs ws) {
     using InT = typename InType<IN_F32>::T;
-    // operand type of the products with V: fp16 for bf16 inputs, fp32 for fp32 inputs
-    using VOpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    // operand precision (as in the KDA path): fp16 for bf16 inputs, fp32 for
+    // fp32 inputs -- of the products with V and of the operands the state pass
+    // reads (W, Ut, Qt, KbT, A); the four C x C matrices take fp32 operands
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    using VOpT = OpT;
     constexpr int P = NT2 / D;       // row parts of the channel-per-thread layout
     constexpr int RPP = CHUNK / P;   // rows per part
     constexpr int NCT = D / 16;      // 16-column tiles of a [..][D] matrix
@@ -137,46 +142,39 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
             if (!exact) {
                 float4v aMe = zero4(), aMw = zero4(), aAe = zero4(), aAw = zero4();
                 const int rr = 16 * R + (lane & 15), jj = 16 * J + (lane & 15), kg = 8 * (lane >> 4);
+                // rows past the sequence read row 0 and are zeroed by a factor, so
+                // every load of the pair is issued before the first product
+                const float mr = rr < nvalid ? 1.f : 0.f, mj = jj < nvalid ? 1.f : 0.f;
+                const int64_t tr = tok(rr < nvalid ? rr : 0) * D, tj = tok(jj < nvalid ? jj : 0) * D;
+                constexpr int NKQ = D / 32;
+                float xk[NKQ][8], xq[NKQ][8], kj[NKQ][8], ye[NKQ][8], yw[NKQ][8];
 #pragma unroll
-                for (int kq = 0; kq < D / 32; ++kq) {
+                for (int kq = 0; kq < NKQ; ++kq) {
                     const int c0 = 32 * kq + kg;
-                    float xk[8], xq[8], ye[8], yw[8];
-                    if (rr < nvalid) {
-                        load8f(k + tok(rr) * D + c0, xk);
-                        load8f(q + tok(rr) * D + c0, xq);
-                    } else {
+                    load8f(k + tr + c0, xk[kq]);
+                    load8f(q + tr + c0, xq[kq]);
+                    load8f(k + tj + c0, kj[kq]);
+                    load8f(erase + tj + c0, ye[kq]);
+                    load8f(write + tj + c0, yw[kq]);
+                }
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) xk[i] = xq[i] = 0.f;
-                    }
-                    if (jj < nvalid) {
-                        float kj[8];
-                        load8f(k + tok(jj) * D + c0, kj);
-                        load8f(erase + tok(jj) * D + c0, ye);
-                        load8f(write + tok(jj) * D + c0, yw);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            ye[i] *= kj[i];
-                            yw[i] *= kj[i];
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) ye[i] = yw[i] = 0.f;
-                    }
+                for (int kq = 0; kq < NKQ; ++kq) {
+                    const int c0 = 32 * kq + kg;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const float ref = sG[refrow * D + c0 + i];
-                        const float fr = exp2_fast(sG[rr * D + c0 + i] - ref);
-                        const float fc = exp2_fast(ref - sG[jj * D + c0 + i]);
-                        xk[i] *= fr;
-                        xq[i] *= fr;
-                        ye[i] *= fc;
-                        yw[i] *= fc;
+                        const float fr = mr * exp2_fast(sG[rr * D + c0 + i] - ref);
+                        const float fc = mj * exp2_fast(ref - sG[jj * D + c0 + i]);
+                        xk[kq][i] *= fr;
+                        xq[kq][i] *= fr;
+                        ye[kq][i] *= kj[kq][i] * fc;
+                        yw[kq][i] *= kj[kq][i] * fc;
                     }
                     Frag<float> Ak, Aq, Be, Bw;
-                    set_frag(Ak, xk);
-                    set_frag(Aq, xq);
-                    set_frag(Be, ye);
-                    set_frag(Bw, yw);
+                    set_frag(Ak, xk[kq]);
+                    set_frag(Aq, xq[kq]);
+                    set_frag(Be, ye[kq]);
+                    set_frag(Bw, yw[kq]);
                     mma(Ak, Be, aMe);
                     mma(Ak, Bw, aMw);
                     mma(Aq, Be, aAe);
@@ -232,8 +230,8 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     __syncthreads();
 
     // ---- phase 3: row-wise operands; Wb into sB; Kt kept in registers
-    float* Qt = static_cast<float*>(ws.Qt) + ch * CHUNK * D;
-    float* KbT = static_cast<float*>(ws.KbT) + ch * D * CHUNK;
+    OpT* Qt = static_cast<OpT*>(ws.Qt) + ch * CHUNK * D;
+    OpT* KbT = static_cast<OpT*>(ws.KbT) + ch * D * CHUNK;
     float kt[RPP];
     {
         const float gl = sG[(CHUNK - 1) * D + cc];  // rows past the sequence carry the last decay
@@ -241,33 +239,45 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = part * RPP + j;
-            float kv = 0.f, qv = 0.f, ev = 0.f, wv = 0.f;
-            if (r < nvalid) {
-                kv = to_f32(k[tok(r) * D + cc]);
-                qv = to_f32(q[tok(r) * D + cc]);
-                ev = erase[tok(r) * D + cc];
-                wv = write[tok(r) * D + cc];
-            }
+            const float m = r < nvalid ? 1.f : 0.f;
+            const int64_t tr = tok(r < nvalid ? r : 0) * D + cc;
+            const float kv = m * to_f32(k[tr]), wv = write[tr];
             const float gr = sG[r * D + cc];
-            const float f0 = exp2_fast(gr), fl = exp2_fast(gl - gr);
-            kt[j] = kv * f0;
-            Qt[frag_off<D>(r, cc)] = qv * f0;
-            KbT[frag_off<CHUNK>(cc, r)] = ev * kv * fl;
-            sB[r * D + cc] = wv * kv * fl;
+            kt[j] = kv * exp2_fast(gr);
+            sB[r * D + cc] = wv * kv * exp2_fast(gl - gr);
         }
-        // A = A_e in fragment order, eight consecutive columns per store pair
-        float* A = static_cast<float*>(ws.A) + ch * CHUNK * CHUNK;
+        // Qt: one run of eight channels of one row per task (fragment order)
+        for (int task = tid; task < CHUNK * D / 8; task += NT2) {
+            const int r = task / (D / 8), c0 = 8 * (task % (D / 8));
+            float x[8];
+            load8f(q + tok(r < nvalid ? r : 0) * D + c0, x);
+            const float m = r < nvalid ? 1.f : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= m * exp2_fast(sG[r * D + c0 + e]);
+            store_run<OpT, 8>(Qt + frag_off<D>(r, c0), x);
+        }
+        // KbT = (e*K*2^(G_last - G))^T: one run of eight tokens of one channel per task
+        for (int task = tid; task < D * CHUNK / 8; task += NT2) {
+            const int c2 = task / (CHUNK / 8), r0 = 8 * (task % (CHUNK / 8));
+            const float gl2 = sG[(CHUNK - 1) * D + c2];
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = r0 + e;
+                const int64_t tr = tok(r < nvalid ? r : 0) * D + c2;
+                const float m = r < nvalid ? 1.f : 0.f;
+                x[e] = m * erase[tr] * to_f32(k[tr]) * exp2_fast(gl2 - sG[r * D + c2]);
+            }
+            store_run<OpT, 8>(KbT + frag_off<CHUNK>(c2, r0), x);
+        }
+        // A = A_e in fragment order
+        OpT* A = static_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
         for (int run = tid; run < CHUNK * CHUNK / 8; run += NT2) {
             const int r = run / (CHUNK / 8), j0 = 8 * (run % (CHUNK / 8));
-            float4v lo, hi;
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lo[e] = sM[2][r * CHUNK + j0 + e];
-                hi[e] = sM[2][r * CHUNK + j0 + 4 + e];
-            }
-            float* dst = A + frag_off<CHUNK>(r, j0);
-            reinterpret_cast<float4v*>(dst)[0] = lo;
-            reinterpret_cast<float4v*>(dst)[1] = hi;
+            for (int e = 0; e < 8; ++e) x[e] = sM[2][r * CHUNK + j0 + e];
+            store_run<OpT, 8>(A + frag_off<CHUNK>(r, j0), x);
         }
     }
     __syncthreads();
@@ -364,11 +374,12 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
 
     // ---- phase 5: (I + M_e) [W | Vt] = [Kt | M_w V] by forward substitution;
     // thread t owns right-hand-side column t (2D columns)
-    if (tid < 2 * D) {
-        const bool left = tid < D;
-        const int col = left ? tid : tid - D;
+    const bool solver = tid < 2 * D;
+    const bool left = tid < D;
+    const int col = left ? tid : tid - D;
+    float z[CHUNK];
+    if (solver) {
         const float* src = left ? sB : sA;
-        float z[CHUNK];
 #pragma unroll
         for (int r = 0; r < CHUNK; ++r) z[r] = src[r * D + col];
 #pragma unroll
@@ -378,21 +389,33 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
             for (int j = 0; j < r; ++j) acc -= sM[0][r * CHUNK + j] * z[j];
             z[r] = acc;
         }
+    }
+    __syncthreads();  // every column is read before W is staged over Kt
+    if (solver) {
         if (left) {
-            float* W = static_cast<float*>(ws.W) + ch * CHUNK * D;
 #pragma unroll
-            for (int r = 0; r < CHUNK; ++r) W[frag_off<D>(r, col)] = z[r];
+            for (int r = 0; r < CHUNK; ++r) sB[r * D + col] = z[r];
         } else {
-            // Ut = -Vt, accumulator order: four consecutive rows per 16-byte store
-            float* Ut = static_cast<float*>(ws.Ut) + ch * CHUNK * D;
+            // Ut = -Vt, accumulator order: four consecutive rows per store
+            OpT* Ut = static_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
 #pragma unroll
             for (int r = 0; r < CHUNK; r += 4) {
                 float4v u;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) u[e] = -z[r + e];
-                *reinterpret_cast<float4v*>(Ut + cfrag_off<D>(r, col)) = u;
+                store4<OpT>(Ut + cfrag_off<D>(r, col), u);
             }
         }
+    }
+    __syncthreads();
+    // W in fragment order, one run of eight channels of one row per task
+    OpT* W = static_cast<OpT*>(ws.W) + ch * CHUNK * D;
+    for (int task = tid; task < CHUNK * D / 8; task += NT2) {
+        const int r = task / (D / 8), c0 = 8 * (task % (D / 8));
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sB[r * D + c0 + e];
+        store_run<OpT, 8>(W + frag_off<D>(r, c0), x);
     }
 }
 

@@ -623,25 +623,33 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
     return hipGetLastError();
 }
 
-// The separate-gate variant's pass: fp32 operands, output computed in the pass,
-// plus the per-chunk terms X (state) and Y (output) of ws.
-template <int D, bool OUT_F32>
+// The separate-gate variant's pass: the register-prefetch pass with the output
+// computed in it, plus the per-chunk terms X (state) and Y (output) of ws.
+template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_state_xy_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
                                     const float* S0, float* ST, void* o, hipStream_t stream) {
-    const int64_t nblk = B * H * StateCfg<D, true>::NSL;
+    const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((state_fwd_kernel<D, true, OUT_F32, false, true, true>), dim3((unsigned)nblk), dim3(320), 0,
-                       stream, T, H, NC, scale, ws, S0, ST, o);
+    hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false, true, true>), dim3((unsigned)nblk), dim3(320),
+                       0, stream, T, H, NC, scale, ws, S0, ST, o);
     return hipGetLastError();
 }
 
-hipError_t launch_state_fwd_xy(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
-                               const ChunkWs& ws, const float* S0, float* ST, void* o, hipStream_t stream) {
-    if (D == 64)
-        return out_f32 ? launch_state_xy_t<64, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
-                       : launch_state_xy_t<64, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
-    return out_f32 ? launch_state_xy_t<128, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
-                   : launch_state_xy_t<128, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
+template <int D>
+static hipError_t launch_state_xy_d(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                                    const ChunkWs& ws, const float* S0, float* ST, void* o, hipStream_t stream) {
+    if (in_f32)
+        return out_f32 ? launch_state_xy_t<D, true, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
+                       : launch_state_xy_t<D, true, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
+    return out_f32 ? launch_state_xy_t<D, false, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
+                   : launch_state_xy_t<D, false, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
+}
+
+hipError_t launch_state_fwd_xy(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
+                               float scale, const ChunkWs& ws, const float* S0, float* ST, void* o,
+                               hipStream_t stream) {
+    if (D == 64) return launch_state_xy_d<64>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, stream);
+    return launch_state_xy_d<128>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, stream);
 }
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,

@@ -117,8 +117,8 @@ hipError_t launch_cler_mt(int, bool, int64_t, int64_t, int, int64_t, const Chunk
     ++stub::launches;
     return hipSuccess;
 }
-hipError_t launch_state_fwd_xy(int, bool, int64_t, int64_t, int, int64_t, float, const ChunkWs& ws, const float*,
-                               float*, void*, hipStream_t) {
+hipError_t launch_state_fwd_xy(int, bool, bool, int64_t, int64_t, int, int64_t, float, const ChunkWs& ws,
+                               const float*, float*, void*, hipStream_t) {
     check_ws(ws);
     in_ws(ws.X, "X");
     in_ws(ws.Y, "Y");
