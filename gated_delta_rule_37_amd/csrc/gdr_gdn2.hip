@@ -43,7 +43,7 @@ namespace gdr {
 
 namespace {
 
-constexpr int NT2 = 256;  // threads of the intra-chunk kernel
+constexpr int NT2 = 512;  // threads of the intra-chunk kernel
 
 // wave-wide maximum
 __device__ __forceinline__ float wave_max(float x) {
@@ -51,6 +51,26 @@ __device__ __forceinline__ float wave_max(float x) {
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
     return x;
 }
+
+// Eight consecutive input elements held as loaded (bf16: four registers), so
+// that many loads can be in flight at once; converted at use.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    uint4 r;
+    __device__ __forceinline__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ float at(int i) const {
+        const uint32_t word = (i >> 1) == 0 ? r.x : (i >> 1) == 1 ? r.y : (i >> 1) == 2 ? r.z : r.w;
+        return __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+    }
+};
+template <> struct Raw8<float> {
+    float4v a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4v*>(p)[0];
+        b = reinterpret_cast<const float4v*>(p)[1];
+    }
+    __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
 
 template <typename OpT>
 __device__ __forceinline__ void set_frag(Frag<OpT>& f, const float (&x)[8]) {
@@ -66,19 +86,23 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
                                                          const float* __restrict__ alpha, ChunkWs ws) {
     using InT = typename InType<IN_F32>::T;
     // operand precision (as in the KDA path): fp16 for bf16 inputs, fp32 for
-    // fp32 inputs -- of the products with V and of the operands the state pass
-    // reads (W, Ut, Qt, KbT, A); the four C x C matrices take fp32 operands
+    // fp32 inputs -- of the C x C blocks (a diagonal block whose decay range is
+    // too wide for fp16 is computed pair by pair), the products with V, and the
+    // operands the state pass reads (W, Ut, Qt, KbT, A); the solve's block
+    // updates take fp32 operands
     using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
-    using VOpT = OpT;
+    constexpr int NW = NT2 / WAVE;   // waves
     constexpr int P = NT2 / D;       // row parts of the channel-per-thread layout
     constexpr int RPP = CHUNK / P;   // rows per part
     constexpr int NCT = D / 16;      // 16-column tiles of a [..][D] matrix
+    constexpr int LT = CHUNK + 4;    // row stride of the transposed [D][64] arrays (conflict-free columns)
+    constexpr int BUF = CHUNK * D > D * LT ? CHUNK * D : D * LT;
 
-    // sM: M_e, M_w, A_e, A_w [64][64]; sA: G, then V, then M_w V [64][D];
-    // sB: Wb, then Kt [64][D]
+    // sM: M_e, M_w, A_e, A_w [64][64]; sA: G [64][D], then Eb^T and V^T [D][64],
+    // then M_w V and Vt [64][D]; sB: Wb^T [D][64], then Kt and W [64][D]
     __shared__ __attribute__((aligned(16))) float sM[4][CHUNK * CHUNK];
-    __shared__ __attribute__((aligned(16))) float sA[CHUNK * D];
-    __shared__ __attribute__((aligned(16))) float sB[CHUNK * D];
+    __shared__ __attribute__((aligned(16))) float sA[BUF];
+    __shared__ __attribute__((aligned(16))) float sB[BUF];
     __shared__ float s_tot[P][D];
 
     const int64_t ch = blockIdx.x;  // chunk-head: (b * H + h) * NC + c
@@ -88,30 +112,34 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     const int64_t t0 = c * CHUNK;
     const int nvalid = static_cast<int>(T - t0 < CHUNK ? T - t0 : CHUNK);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, kg = 8 * (lane >> 4);
     const InT* q = reinterpret_cast<const InT*>(q_);
     const InT* k = reinterpret_cast<const InT*>(k_);
     const InT* v = reinterpret_cast<const InT*>(v_);
-    auto tok = [&](int r) -> int64_t { return (b * T + t0 + r) * H + h; };
+    // element offset of row r (rows past the sequence read the first row; their
+    // values are zeroed by a factor, so loads need no branch)
+    auto rowoff = [&](int r) -> int64_t { return ((b * T + t0 + (r < nvalid ? r : 0)) * H + h) * D; };
 
     // ---- phase 1: G, the in-chunk inclusive cumulative log2 decay, per channel
-    for (int i = tid; i < CHUNK * CHUNK; i += NT2) {
-        sM[0][i] = 0.f;
-        sM[1][i] = 0.f;
-        sM[2][i] = 0.f;
-        sM[3][i] = 0.f;
+    {
+        float4v* z4 = reinterpret_cast<float4v*>(&sM[0][0]);
+        for (int i = tid; i < 4 * CHUNK * CHUNK / 4; i += NT2) z4[i] = zero4();
     }
     const int cc = tid % D, part = tid / D;
     {
+        float av[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int64_t e = rowoff(part * RPP + j) + cc;
+            if constexpr (GATE == GATE_CHANNEL) av[j] = alpha[e];
+            else if constexpr (GATE == GATE_SCALAR) av[j] = alpha[e / D];
+            else av[j] = 1.f;
+        }
         float g = 0.f, G[RPP];
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
-            const int r = part * RPP + j;
-            float la = 0.f;  // rows past the sequence decay by nothing
-            if (GATE != GATE_NONE && r < nvalid) {
-                const float a = GATE == GATE_SCALAR ? alpha[tok(r)] : alpha[tok(r) * D + cc];
-                la = log2_fast(a);
-            }
-            g += la;
+            const bool ok = part * RPP + j < nvalid;  // rows past the sequence decay by nothing
+            g += (GATE != GATE_NONE && ok) ? log2_fast(av[j]) : 0.f;
             G[j] = g;
         }
         s_tot[part][cc] = g;
@@ -125,56 +153,59 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     __syncthreads();
     const float* sG = sA;
 
-    // ---- phase 2: the four C x C matrices, 16 x 16 block pairs (R, J), J <= R
+    // ---- phase 2: the four C x C matrices, 16 x 16 block pairs (R, J), J <= R:
+    // the diagonal blocks first (waves 0-3), the six below the diagonal after
     {
         const int pairR[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
         const int pairJ[10] = {0, 1, 2, 3, 0, 1, 2, 0, 1, 0};
-        for (int pi = wid; pi < 10; pi += 4) {
+        for (int pi = wid; pi < 10; pi += NW) {
             const int R = pairR[pi], J = pairJ[pi];
             bool exact = false;
             if (R == J) {
                 float rho = 0.f;
                 for (int c2 = lane; c2 < D; c2 += WAVE)
                     rho = fmaxf(rho, sG[(16 * R) * D + c2] - sG[(16 * R + 15) * D + c2]);
-                exact = wave_max(rho) > 60.f;
+                // fp16 operands carry a column factor up to 2^8 (as in the KDA
+                // kernel), fp32 ones up to 2^60
+                exact = wave_max(rho) > (sizeof(OpT) == 2 ? 8.f : 60.f);
             }
             const int refrow = R == J ? 16 * R : 16 * J + 15;
+            const int rr = 16 * R + l16, jj = 16 * J + l16;
             if (!exact) {
                 float4v aMe = zero4(), aMw = zero4(), aAe = zero4(), aAw = zero4();
-                const int rr = 16 * R + (lane & 15), jj = 16 * J + (lane & 15), kg = 8 * (lane >> 4);
-                // rows past the sequence read row 0 and are zeroed by a factor, so
-                // every load of the pair is issued before the first product
                 const float mr = rr < nvalid ? 1.f : 0.f, mj = jj < nvalid ? 1.f : 0.f;
-                const int64_t tr = tok(rr < nvalid ? rr : 0) * D, tj = tok(jj < nvalid ? jj : 0) * D;
+                const int64_t tr = rowoff(rr), tj = rowoff(jj);
                 constexpr int NKQ = D / 32;
-                float xk[NKQ][8], xq[NKQ][8], kj[NKQ][8], ye[NKQ][8], yw[NKQ][8];
+                Raw8<InT> rk[NKQ], rq[NKQ], rkj[NKQ];
+                Raw8<float> re[NKQ], rw[NKQ];
 #pragma unroll
                 for (int kq = 0; kq < NKQ; ++kq) {
                     const int c0 = 32 * kq + kg;
-                    load8f(k + tr + c0, xk[kq]);
-                    load8f(q + tr + c0, xq[kq]);
-                    load8f(k + tj + c0, kj[kq]);
-                    load8f(erase + tj + c0, ye[kq]);
-                    load8f(write + tj + c0, yw[kq]);
+                    rk[kq].load(k + tr + c0);
+                    rq[kq].load(q + tr + c0);
+                    rkj[kq].load(k + tj + c0);
+                    re[kq].load(erase + tj + c0);
+                    rw[kq].load(write + tj + c0);
                 }
 #pragma unroll
                 for (int kq = 0; kq < NKQ; ++kq) {
                     const int c0 = 32 * kq + kg;
+                    float xk[8], xq[8], ye[8], yw[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const float ref = sG[refrow * D + c0 + i];
                         const float fr = mr * exp2_fast(sG[rr * D + c0 + i] - ref);
-                        const float fc = mj * exp2_fast(ref - sG[jj * D + c0 + i]);
-                        xk[kq][i] *= fr;
-                        xq[kq][i] *= fr;
-                        ye[kq][i] *= kj[kq][i] * fc;
-                        yw[kq][i] *= kj[kq][i] * fc;
+                        const float fc = mj * exp2_fast(ref - sG[jj * D + c0 + i]) * rkj[kq].at(i);
+                        xk[i] = rk[kq].at(i) * fr;
+                        xq[i] = rq[kq].at(i) * fr;
+                        ye[i] = re[kq].at(i) * fc;
+                        yw[i] = rw[kq].at(i) * fc;
                     }
-                    Frag<float> Ak, Aq, Be, Bw;
-                    set_frag(Ak, xk[kq]);
-                    set_frag(Aq, xq[kq]);
-                    set_frag(Be, ye[kq]);
-                    set_frag(Bw, yw[kq]);
+                    Frag<OpT> Ak, Aq, Be, Bw;
+                    set_frag(Ak, xk);
+                    set_frag(Aq, xq);
+                    set_frag(Be, ye);
+                    set_frag(Bw, yw);
                     mma(Ak, Be, aMe);
                     mma(Ak, Bw, aMw);
                     mma(Aq, Be, aAe);
@@ -193,21 +224,23 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
             } else {
                 // diagonal block with a large decay range: 2^(G_r - G_j) per pair.
                 // lane: row rr, columns 16R + 4(lane / 16) + i, i < 4
-                const int rr = 16 * R + (lane & 15), jb = 16 * R + 4 * (lane >> 4);
+                const int jb = 16 * R + 4 * (lane >> 4);
                 float me[4] = {0.f, 0.f, 0.f, 0.f}, mw[4] = {0.f, 0.f, 0.f, 0.f};
                 float ae[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
                 if (rr < nvalid) {
+                    const int64_t tr = rowoff(rr);
                     for (int c2 = 0; c2 < D; ++c2) {
                         const float gr = sG[rr * D + c2];
-                        const float kr = to_f32(k[tok(rr) * D + c2]), qr = to_f32(q[tok(rr) * D + c2]);
+                        const float kr = to_f32(k[tr + c2]), qr = to_f32(q[tr + c2]);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int j = jb + i;
                             if (j <= rr) {
+                                const int64_t tj = rowoff(j) + c2;
                                 const float f = exp2_fast(gr - sG[j * D + c2]);
-                                const float kj = to_f32(k[tok(j) * D + c2]);
-                                const float ej = erase[tok(j) * D + c2] * kj * f;
-                                const float wj = write[tok(j) * D + c2] * kj * f;
+                                const float kj = to_f32(k[tj]);
+                                const float ej = erase[tj] * kj * f;
+                                const float wj = write[tj] * kj * f;
                                 me[i] += kr * ej;
                                 mw[i] += kr * wj;
                                 ae[i] += qr * ej;
@@ -229,46 +262,47 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     }
     __syncthreads();
 
-    // ---- phase 3: row-wise operands; Wb into sB; Kt kept in registers
+    // ---- phase 3: row-wise operands.  Wb into sB; Kt and Eb in registers
     OpT* Qt = static_cast<OpT*>(ws.Qt) + ch * CHUNK * D;
     OpT* KbT = static_cast<OpT*>(ws.KbT) + ch * D * CHUNK;
-    float kt[RPP];
+    float kt[RPP], eb[RPP];
     {
+        float kv[RPP], ev[RPP], wv[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int64_t e = rowoff(part * RPP + j) + cc;
+            kv[j] = to_f32(k[e]);
+            ev[j] = erase[e];
+            wv[j] = write[e];
+        }
         const float gl = sG[(CHUNK - 1) * D + cc];  // rows past the sequence carry the last decay
         if (part == 0) ws.gam[ch * D + cc] = exp2_fast(gl);
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
             const int r = part * RPP + j;
             const float m = r < nvalid ? 1.f : 0.f;
-            const int64_t tr = tok(r < nvalid ? r : 0) * D + cc;
-            const float kv = m * to_f32(k[tr]), wv = write[tr];
+            kv[j] *= m;
             const float gr = sG[r * D + cc];
-            kt[j] = kv * exp2_fast(gr);
-            sB[r * D + cc] = wv * kv * exp2_fast(gl - gr);
+            const float fl = exp2_fast(gl - gr);
+            kt[j] = kv[j] * exp2_fast(gr);
+            eb[j] = ev[j] * kv[j] * fl;
+            sB[cc * LT + r] = wv[j] * kv[j] * fl;  // Wb^T [D][64], row stride LT
         }
-        // Qt: one run of eight channels of one row per task (fragment order)
-        for (int task = tid; task < CHUNK * D / 8; task += NT2) {
-            const int r = task / (D / 8), c0 = 8 * (task % (D / 8));
-            float x[8];
-            load8f(q + tok(r < nvalid ? r : 0) * D + c0, x);
+        // Qt in fragment order: runs of eight channels of one row
+        constexpr int NQ = CHUNK * D / 8 / NT2;
+        float xq[NQ][8];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int task = tid + i * NT2, r = task / (D / 8), c0 = 8 * (task % (D / 8));
+            load8f(q + rowoff(r) + c0, xq[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int task = tid + i * NT2, r = task / (D / 8), c0 = 8 * (task % (D / 8));
             const float m = r < nvalid ? 1.f : 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= m * exp2_fast(sG[r * D + c0 + e]);
-            store_run<OpT, 8>(Qt + frag_off<D>(r, c0), x);
-        }
-        // KbT = (e*K*2^(G_last - G))^T: one run of eight tokens of one channel per task
-        for (int task = tid; task < D * CHUNK / 8; task += NT2) {
-            const int c2 = task / (CHUNK / 8), r0 = 8 * (task % (CHUNK / 8));
-            const float gl2 = sG[(CHUNK - 1) * D + c2];
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = r0 + e;
-                const int64_t tr = tok(r < nvalid ? r : 0) * D + c2;
-                const float m = r < nvalid ? 1.f : 0.f;
-                x[e] = m * erase[tr] * to_f32(k[tr]) * exp2_fast(gl2 - sG[r * D + c2]);
-            }
-            store_run<OpT, 8>(KbT + frag_off<CHUNK>(c2, r0), x);
+            for (int e = 0; e < 8; ++e) xq[i][e] *= m * exp2_fast(sG[r * D + c0 + e]);
+            store_run<OpT, 8>(Qt + frag_off<D>(r, c0), xq[i]);
         }
         // A = A_e in fragment order
         OpT* A = static_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
@@ -280,33 +314,42 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
             store_run<OpT, 8>(A + frag_off<CHUNK>(r, j0), x);
         }
     }
+    __syncthreads();  // G is read for the last time
+    // KbT = Eb^T in fragment order: Eb staged transposed over G, runs of eight tokens
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) sA[cc * LT + part * RPP + j] = eb[j];
     __syncthreads();
-    // V (fp32) over G
-    for (int i = tid; i < CHUNK * D / 8; i += NT2) {
-        const int r = i / (D / 8), c0 = 8 * (i % (D / 8));
+    for (int task = tid; task < D * CHUNK / 8; task += NT2) {
+        const int c2 = task / (CHUNK / 8), r0 = 8 * (task % (CHUNK / 8));
         float x[8];
-        if (r < nvalid) {
-            load8f(v + tok(r) * D + c0, x);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-        float4v lo, hi;
+        for (int e = 0; e < 8; ++e) x[e] = sA[c2 * LT + r0 + e];
+        store_run<OpT, 8>(KbT + frag_off<CHUNK>(c2, r0), x);
+    }
+    __syncthreads();
+    // V (fp32) over Eb^T
+    {
+        constexpr int NV = CHUNK * D / 8 / NT2;
+        float x[NV][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            lo[e] = x[e];
-            hi[e] = x[4 + e];
+        for (int i = 0; i < NV; ++i) {
+            const int p = tid + i * NT2, r = p / (D / 8), c0 = 8 * (p % (D / 8));
+            load8f(v + rowoff(r) + c0, x[i]);
         }
-        reinterpret_cast<float4v*>(sA + r * D + c0)[0] = lo;
-        reinterpret_cast<float4v*>(sA + r * D + c0)[1] = hi;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int p = tid + i * NT2, r = p / (D / 8), c0 = 8 * (p % (D / 8));
+            const float m = r < nvalid ? 1.f : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sA[(c0 + e) * LT + r] = m * x[i][e];  // V^T [D][64], row stride LT
+        }
     }
     __syncthreads();
 
     // ---- X = Wb^T V [D][D] (contraction over the 64 rows), accumulator order
-    const int l16 = lane & 15, kg = 8 * (lane >> 4);
     {
         float* X = ws.X + ch * D * D;
-        for (int tile = wid; tile < NCT * NCT; tile += 4) {
+        for (int tile = wid; tile < NCT * NCT; tile += NW) {
             const int mt = tile / NCT, nt = tile % NCT;
             float4v acc = zero4();
 #pragma unroll
@@ -315,10 +358,10 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 32 * kq + kg + i;
-                    xa[i] = sB[r * D + 16 * mt + l16];
-                    xb[i] = sA[r * D + 16 * nt + l16];
+                    xa[i] = sB[(16 * mt + l16) * LT + r];
+                    xb[i] = sA[(16 * nt + l16) * LT + r];
                 }
-                Frag<VOpT> fa, fb;
+                Frag<OpT> fa, fb;
                 set_frag(fa, xa);
                 set_frag(fb, xb);
                 mma(fa, fb, acc);
@@ -329,13 +372,14 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
 
     // ---- Y = A_w V and M_w V [64][D] (contraction over the 64 columns)
     constexpr int MT = CHUNK / 16 * NCT;  // 16 x 16 tiles of a [64][D] result
-    constexpr int MPW = MT / 4;           // per wave
+    constexpr int MPW = MT / NW;          // per wave
+    static_assert(MT % NW == 0, "tiles per wave");
     float4v mwv[MPW];
     {
         float* Y = ws.Y + ch * CHUNK * D;
 #pragma unroll
         for (int i = 0; i < MPW; ++i) {
-            const int tile = wid + 4 * i;
+            const int tile = wid + NW * i;
             const int mt = tile / NCT, nt = tile % NCT;
             float4v ay = zero4(), am = zero4();
 #pragma unroll
@@ -346,9 +390,9 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
                     const int j = 32 * kq + kg + e;
                     xw[e] = sM[3][(16 * mt + l16) * CHUNK + j];
                     xm[e] = sM[1][(16 * mt + l16) * CHUNK + j];
-                    xb[e] = sA[j * D + 16 * nt + l16];
+                    xb[e] = sA[(16 * nt + l16) * LT + j];
                 }
-                Frag<VOpT> fw, fm, fb;
+                Frag<OpT> fw, fm, fb;
                 set_frag(fw, xw);
                 set_frag(fm, xm);
                 set_frag(fb, xb);
@@ -365,50 +409,70 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     for (int j = 0; j < RPP; ++j) sB[(part * RPP + j) * D + cc] = kt[j];
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-        const int tile = wid + 4 * i;
+        const int tile = wid + NW * i;
         const int mt = tile / NCT, nt = tile % NCT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sA[(16 * mt + 4 * (lane >> 4) + e) * D + 16 * nt + l16] = mwv[i][e];
     }
     __syncthreads();
 
-    // ---- phase 5: (I + M_e) [W | Vt] = [Kt | M_w V] by forward substitution;
-    // thread t owns right-hand-side column t (2D columns)
-    const bool solver = tid < 2 * D;
-    const bool left = tid < D;
-    const int col = left ? tid : tid - D;
-    float z[CHUNK];
-    if (solver) {
-        const float* src = left ? sB : sA;
+    // ---- phase 5: (I + M_e) Z = [Kt | M_w V] for Z = [W | Vt], in place, by
+    // 16-row blocks: block R first takes the products of the solved rows above
+    // it, M_e[R, <16R] Z[<16R] (fp32 matrix cores, one 16-column tile per wave),
+    // then is solved by forward substitution inside the block (one column per
+    // thread).  Column t < D lives in sB, the others in sA.
+    auto zat = [&](int r, int col) -> float& { return col < D ? sB[r * D + col] : sA[r * D + col - D]; };
 #pragma unroll
-        for (int r = 0; r < CHUNK; ++r) z[r] = src[r * D + col];
+    for (int R = 0; R < CHUNK / 16; ++R) {
+        if (R > 0) {
+            for (int ct = wid; ct < 2 * NCT; ct += NW) {
+                float4v acc = zero4();
+                const int col = 16 * ct + l16;
 #pragma unroll
-        for (int r = 1; r < CHUNK; ++r) {
-            float acc = z[r];
+                for (int kq = 0; kq < (16 * R + 31) / 32; ++kq) {
+                    float xa[8], xb[8];
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc -= sM[0][r * CHUNK + j] * z[j];
-            z[r] = acc;
-        }
-    }
-    __syncthreads();  // every column is read before W is staged over Kt
-    if (solver) {
-        if (left) {
+                    for (int i = 0; i < 8; ++i) {
+                        const int j = 32 * kq + kg + i;
+                        xa[i] = j < 16 * R ? sM[0][(16 * R + l16) * CHUNK + j] : 0.f;
+                        xb[i] = j < 16 * R ? zat(j, col) : 0.f;
+                    }
+                    Frag<float> fa, fb;
+                    set_frag(fa, xa);
+                    set_frag(fb, xb);
+                    mma(fa, fb, acc);
+                }
 #pragma unroll
-            for (int r = 0; r < CHUNK; ++r) sB[r * D + col] = z[r];
-        } else {
-            // Ut = -Vt, accumulator order: four consecutive rows per store
-            OpT* Ut = static_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
-#pragma unroll
-            for (int r = 0; r < CHUNK; r += 4) {
-                float4v u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) u[e] = -z[r + e];
-                store4<OpT>(Ut + cfrag_off<D>(r, col), u);
+                for (int e = 0; e < 4; ++e) zat(16 * R + 4 * (lane >> 4) + e, col) -= acc[e];
             }
+            __syncthreads();
         }
+        if (tid < 2 * D) {
+            float z[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[i] = zat(16 * R + i, tid);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) {
+                const int r = 16 * R + i;
+                float m[16];
+#pragma unroll
+                for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
+                    const float4v x = *reinterpret_cast<const float4v*>(&sM[0][r * CHUNK + 16 * R + 4 * j4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m[4 * j4 + e] = x[e];
+                }
+                float acc = z[i];
+#pragma unroll
+                for (int j = 0; j < i; ++j) acc -= m[j] * z[j];
+                z[i] = acc;
+            }
+#pragma unroll
+            for (int i = 1; i < 16; ++i) zat(16 * R + i, tid) = z[i];
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    // W in fragment order, one run of eight channels of one row per task
+
+    // ---- outputs: W (sB) in fragment order, Ut = -Vt (sA) in accumulator order
     OpT* W = static_cast<OpT*>(ws.W) + ch * CHUNK * D;
     for (int task = tid; task < CHUNK * D / 8; task += NT2) {
         const int r = task / (D / 8), c0 = 8 * (task % (D / 8));
@@ -416,6 +480,14 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = sB[r * D + c0 + e];
         store_run<OpT, 8>(W + frag_off<D>(r, c0), x);
+    }
+    OpT* Ut = static_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
+    for (int task = tid; task < CHUNK / 4 * D; task += NT2) {
+        const int r = 4 * (task / D), n = task % D;
+        float4v u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = -sA[(r + e) * D + n];
+        store4<OpT>(Ut + cfrag_off<D>(r, n), u);
     }
 }
 
