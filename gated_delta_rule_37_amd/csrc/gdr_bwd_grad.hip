@@ -200,12 +200,7 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
         if constexpr (PRO) s_rk[tid] = rk0;  // prologue: k row norms (intra kernel; negative if clamped)
         if constexpr (GATE == GATE_SCALAR) {
             float g = tok_ok ? (PRO ? log2_alpha_logit(at0, pro) : log2_fast(at0)) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(g, off);
-                if (lane >= off) g += y;
-            }
-            s_gs[tid] = g;
+            s_gs[tid] = chunk_prefix_sum(g);
         }
     }
 #pragma unroll
@@ -676,12 +671,7 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         if (tid < CHUNK) {
             float g = tok_ok ? (PRO ? log2_alpha_logit(at0, pro) : log2_fast(at0)) : 0.f;
             s_row[tid] = tok_ok ? at0 : 1.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(g, off);
-                if (lane >= off) g += y;
-            }
-            s_gs[tid] = g;
+            s_gs[tid] = chunk_prefix_sum(g);
         }
     }
 #pragma unroll

@@ -267,6 +267,29 @@ __device__ __forceinline__ void load_lam8(const float* lam, int64_t c, float (&x
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Prefix sums over a chunk of one value per row (row = lane of one 64-lane
+// wave), associated the way the per-channel path sums a column: a running sum
+// inside each 16-row block, then the totals of the earlier blocks added in
+// order.  The difference of two prefixes then carries the rounding of the terms
+// between them only (not that of the whole prefix), and rows that add 0 repeat
+// the previous prefix exactly, so a chunk's last prefix equals that of its last
+// valid row.  All 64 lanes must call it.
+__device__ __forceinline__ float chunk_prefix_sum(float x) {
+    const int lane = threadIdx.x & 63, li = lane & 15, blk = lane >> 4;
+    float s = x;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        const float prev = __shfl_up(s, 1);
+        s = (li == i) ? prev + x : s;
+    }
+    const float t0 = __shfl(s, 15), t1 = __shfl(s, 31), t2 = __shfl(s, 47);
+    float carry = 0.f;
+    carry += blk > 0 ? t0 : 0.f;
+    carry += blk > 1 ? t1 : 0.f;
+    carry += blk > 2 ? t2 : 0.f;
+    return s + carry;
+}
+
 // ---------------------------------------------------------------------------
 // Prologue: L2-normalised q and k, activated gates (KDA blog, sections 2.1 and
 // 7.1: an L2 norm after the q/k projections; sigmoid gates, with the forget

@@ -188,12 +188,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         if constexpr (GATE == GATE_SCALAR) {
             const float at = alpha[tok];
             float g = ok ? (PRO ? log2_alpha_logit(at, pro) : log2_fast(at)) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(g, off);
-                if (lane >= off) g += y;
-            }
-            s_gs[tid] = g;
+            s_gs[tid] = chunk_prefix_sum(g);
         }
     }
 #pragma unroll
@@ -257,6 +252,9 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     }
     int flags = 0;      // bit R: diagonal block R needs the exact path
     bool wide = false;  // 2^G or 2^-G would leave the fp32 range somewhere in the chunk
+    // (scalar gate: one decay for every channel, so the chunk's own total decides;
+    // its in-chunk pair factors are formed from G differences and never overflow)
+    if constexpr (GATE == GATE_SCALAR) wide = !(-glast <= L::WIDE_MAX);  // NaN-safe
     if constexpr (GATE == GATE_CHANNEL) {
         // each wave holds one block (part) for 64 channels
         const float rho = wave_max(carry - G[RPP - 1]);

@@ -120,10 +120,11 @@ def test_backward_empty_sequence_passes_state_gradient():
     assert torch.equal(g["dS0"].cpu(), torch.from_numpy(dST))
 
 
+@pytest.mark.parametrize("gate", ["channel", "scalar"])
 @pytest.mark.parametrize("recipe", ["sigmoid(N(-1,1))", "uniform[1e-6,1e-3]"])
-def test_backward_strong_gates(recipe):
-    announce("backward strong gates %s" % recipe)
-    inp = gdr_inputs.make(B=1, T=512, H=2, d=128, gate="channel", dtype="bf16", seed=340, s0=True, bwd=True,
+def test_backward_strong_gates(recipe, gate):
+    announce("backward strong gates %s %s" % (gate, recipe))
+    inp = gdr_inputs.make(B=1, T=512, H=2, d=128, gate=gate, dtype="bf16", seed=340, s0=True, bwd=True,
                           alpha_recipe=recipe)
     t = inputs_to_dev(inp, "bf16")
     g = gpu_backward(t)

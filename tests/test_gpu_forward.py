@@ -99,21 +99,25 @@ def test_forward_bf16_output():
     assert eo < tol("bf16", "bf16") and es < 2e-3, (eo, es)
 
 
+@pytest.mark.parametrize("gate", ["channel", "scalar"])
 @pytest.mark.parametrize("recipe", ["sigmoid(N(-1,1))", "uniform[1e-6,1e-3]"])
-def test_forward_strong_gates(recipe):
+def test_forward_strong_gates(recipe, gate):
     """Gates far stronger than the workloads': the in-block decay range exceeds
-    what fp16 operands can carry, so the exact diagonal-block path runs."""
-    announce("forward strong gates %s" % recipe)
-    inp = gdr_inputs.make(B=1, T=2048, H=2, d=128, gate="channel", dtype="bf16", seed=230,
+    what fp16 operands can carry, so the exact diagonal-block path runs; with
+    alpha <= 1e-3 a chunk's total decay (below 2^-600) leaves the fp32 range, for
+    the scalar gate as for the channel gate."""
+    announce("forward strong gates %s %s" % (gate, recipe))
+    inp = gdr_inputs.make(B=1, T=2048, H=2, d=128, gate=gate, dtype="bf16", seed=230,
                           s0=True, alpha_recipe=recipe)
     eo, es = check(inp, "bf16")
     report(o=eo, S=es)
     assert eo < 2e-3 and es < 2e-3, (eo, es)
 
 
-def test_forward_strong_gates_fp32():
-    announce("forward strong gates fp32")
-    inp = gdr_inputs.make(B=1, T=300, H=2, d=64, gate="channel", dtype="fp32", seed=231,
+@pytest.mark.parametrize("gate", ["channel", "scalar"])
+def test_forward_strong_gates_fp32(gate):
+    announce("forward strong gates fp32 %s" % gate)
+    inp = gdr_inputs.make(B=1, T=300, H=2, d=64, gate=gate, dtype="fp32", seed=231,
                           s0=True, alpha_recipe="uniform[1e-6,1e-3]")
     eo, es = check(inp, "fp32")
     report(o=eo, S=es)

@@ -88,12 +88,13 @@ def test_gdn2_forward_ragged(T):
     assert max(errs.values()) < 2e-3, errs
 
 
+@pytest.mark.parametrize("gate", ["channel", "scalar"])
 @pytest.mark.parametrize("recipe", ["sigmoid(N(-1,1))", "uniform[1e-6,1e-3]"])
-def test_gdn2_forward_strong_gates(recipe):
+def test_gdn2_forward_strong_gates(recipe, gate):
     """Decay ranges above 60 (log2) inside a 16-token block take the pair-by-pair
     path of the diagonal blocks."""
-    announce("gdn2 forward strong gates %s" % recipe)
-    inp = make(1, 300, 2, 128, "channel", "bf16", 1030, alpha_recipe=recipe)
+    announce("gdn2 forward strong gates %s %s" % (gate, recipe))
+    inp = make(1, 300, 2, 128, gate, "bf16", 1030, alpha_recipe=recipe)
     o, ST = run(inp, "bf16")
     o_ref, S_ref = ref(inp)
     errs = {"o": rel(o, o_ref), "S_T": rel(ST, S_ref)}
