@@ -312,13 +312,18 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
         w.dSsnap = take(st);
         w.dUsave = take(mat);
         w.dUsaveT = take(mat);
-        w.gQt = take(mat);
-        w.gKt = take(mat);
-        w.gKb = take(mat);
-        w.gA = take(sq);
-        w.gP = take(sq);
-        w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
-        if (cler) w.Mt = take(mat);
+        // the gradient partials the stages do not hand on chip
+        if (cler || !grad_qkb_on_chip(D)) {
+            w.gQt = take(mat);
+            w.gKb = take(mat);
+        }
+        if (cler) {
+            w.gKt = take(mat);
+            w.gA = take(sq);
+            w.gP = take(sq);
+            w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
+            w.Mt = take(mat);
+        }
     }
     if (out) *out = w;
     return off;

@@ -49,6 +49,75 @@ struct GLinLayout {
     static_assert(2 * CHUNK * LDF * 4 <= NF, "N^T and dT^T must fit below N");
 };
 
+// LDS layout of the second stage (defined here: the first stage writes into it).
+template <int D, bool IN_F32>
+struct GGateLayout {
+    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
+    static constexpr int OPB = sizeof(OpT);
+    static constexpr int PAD = 16 / OPB;
+    static constexpr int LDC = CHUNK + PAD;
+    static constexpr int NT = 4 * D;
+    static constexpr int NW = NT / WAVE;
+    static constexpr int DA = 0;                            // dA  [64][LDC]
+    static constexpr int DP = DA + CHUNK * LDC * OPB;       // dP  [64][LDC]
+    static constexpr int DAT = DP + CHUNK * LDC * OPB;      // dA^T
+    static constexpr int DPT = DAT + CHUNK * LDC * OPB;     // dP^T
+    static constexpr int QQT = DPT + CHUNK * LDC * OPB;     // Qq^T [D][LDC]
+    static constexpr int KQT = QQT + D * LDC * OPB;         // Kq^T
+    static constexpr int KHT = KQT + D * LDC * OPB;         // Kh^T
+    static constexpr int SA = KHT + D * LDC * OPB;          // fp32 [16][D]  dA_R Kh
+    static constexpr int SB = SA + 16 * D * 4;              // fp32 [16][D]  dP_R Kh
+    static constexpr int SC = SB + 16 * D * 4;              // fp32 [64][D]  dA_R^T Qq + dP_R^T Kq
+    static constexpr int BYTES = SC + CHUNK * D * 4;
+    static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
+    // on-chip partials: dQt, dKt, dKb handed to the combine through LDS that is
+    // free by then (SA .. the end, else dA .. dP^T), [D][64] each with the
+    // 16-byte pieces of a column XOR-swizzled by the column
+    static constexpr int XPART = 3 * CHUNK * D * OPB;
+    static constexpr int XR = (BYTES - SA >= XPART) ? SA : DA;
+    static_assert(XR == SA || QQT - DA >= XPART, "partials exchange fits");
+    static constexpr int EPC = 16 / OPB;       // elements per 16-byte piece
+    static constexpr int NPC = CHUNK / EPC;    // pieces per column
+};
+
+// Offset of (row r, column c) in one [D][64] array of the partials exchange.
+template <int EPC, int NPC>
+__device__ __forceinline__ int xoff(int c, int r) {
+    return c * CHUNK + (((r / EPC) ^ (c % NPC)) * EPC) + r % EPC;
+}
+
+// The first stage's partials (dQt, dKb, dKt, dA, dP) as the second stage takes
+// them when they stay on chip: this thread's values in the accumulator layout
+// they were computed in (four consecutive rows of one column per tile), in
+// operand precision, so they are rounded exactly as the workspace copies are.
+template <int D, bool IN_F32>
+struct GradPartials {
+    using V4 = typename std::conditional<IN_F32, float4v, half4>::type;
+    static constexpr int NW = 4 * D / WAVE;
+    static constexpr int NHALF = NW / 4;
+    static constexpr int NIT = D / 16 / NHALF;  // dKt column tiles per wave
+    static constexpr int NPW = 4 / NHALF;       // dA position tiles per wave
+    static constexpr int NTL = 16 / NW;         // dP tiles per wave
+    // Where each stays: at d = 64 (one wave per SIMD, registers to spare) all in
+    // registers; at d = 128 dKt goes to LDS past the second stage's buffers and
+    // dQt, dKb still through the workspace (holding them too would spill).
+    static constexpr bool QREG = grad_qkb_on_chip(D);
+    static constexpr bool TLDS = D == 128;
+    V4 q[4], kb[4];  // dQt, dKb: row tile r4, value-column tile = wave
+    V4 kt[NIT];      // dKt: row tile wave % 4, value-column tiles wave / 4 + NHALF i
+    V4 a[NPW];       // dA: row tiles wave / 4 + NHALF k, column tile wave % 4
+    V4 p[NTL];       // dP: tile wave + NW t
+};
+
+template <typename V4>
+__device__ __forceinline__ V4 to_v4(const float (&x)[4]) {
+    V4 r;
+    using E = typename std::remove_reference<decltype(r[0])>::type;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = from_f32<E>(x[e]);
+    return r;
+}
+
 template <typename InT, typename OpT>
 __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
     // eight consecutive input elements -> operand precision
@@ -73,21 +142,23 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
 
 // The two gradient stages are device functions on a caller-provided LDS
 // buffer, which grads_kernel runs one after the other for a chunk.
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+// KEEP: the partials stay on chip (pk, and dgamma in s_gam) instead of going
+// through the workspace.
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP>
 __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, float scale,
                                               const void* __restrict__ k_, const void* __restrict__ v_,
                                               const float* __restrict__ beta, const float* __restrict__ alpha,
                                               const void* __restrict__ dO_, const void* __restrict__ dh_,
                                               const float* __restrict__ lam, void* __restrict__ dv_,
                                               float* __restrict__ dbeta, ChunkWs ws, int pro,
-                                              ChunkRange cr, char* smem) {
+                                              ChunkRange cr, char* smem, GradPartials<D, IN_F32>& pk,
+                                              float* s_gam, float (&s_tot)[4][D]) {
     using L = GLinLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int NT = L::NT, NW = L::NW, LDR = L::LDR, LDC = L::LDC, LDF = L::LDF, RPP = 16;
 
-    __shared__ float s_tot[4][D];
     __shared__ float s_gs[CHUNK];
     __shared__ float s_beta[CHUNK];
     __shared__ float s_db[CHUNK];
@@ -352,24 +423,44 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
                 DTF[(r0_ + e) * LDF + pc] = at[e];
             }
         }
-        // stores
+        // stores (or the on-chip copies)
+        using P = GradPartials<D, IN_F32>;
+        if constexpr (KEEP) {
+            using V4 = typename P::V4;
+            if constexpr (P::QREG) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    pk.q[r4] = to_v4<V4>(rq[r4]);
+                    pk.kb[r4] = to_v4<V4>(rk[r4]);
+                }
+            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                static_cast<OpT*>(ws.gQt)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = from_f32<OpT>(rq[r4][e]);
-                static_cast<OpT*>(ws.gKb)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] = from_f32<OpT>(rk[r4][e]);
+            for (int k = 0; k < NPW; ++k) pk.a[k] = to_v4<V4>(ra[k]);
+            if (g4 == 0) s_gam[col] = sg;
+        }
+        if constexpr (!KEEP || !P::QREG) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    static_cast<OpT*>(ws.gQt)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] =
+                        from_f32<OpT>(rq[r4][e]);
+                    static_cast<OpT*>(ws.gKb)[ch * CHUNK * D + (16 * r4 + 4 * g4 + e) * D + col] =
+                        from_f32<OpT>(rk[r4][e]);
+                }
             }
         }
+        if constexpr (!KEEP) {
 #pragma unroll
-        for (int k = 0; k < NPW; ++k) {
-            const int r4 = (wid >> 2) + k * NHALF;
+            for (int k = 0; k < NPW; ++k) {
+                const int r4 = (wid >> 2) + k * NHALF;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                static_cast<OpT*>(ws.gA)[ch * CHUNK * CHUNK + (16 * r4 + 4 * g4 + e) * CHUNK + 16 * itp + l16] =
-                    from_f32<OpT>(ra[k][e]);
+                for (int e = 0; e < 4; ++e)
+                    static_cast<OpT*>(ws.gA)[ch * CHUNK * CHUNK + (16 * r4 + 4 * g4 + e) * CHUNK + 16 * itp + l16] =
+                        from_f32<OpT>(ra[k][e]);
+            }
+            if (g4 == 0) ws.gGam[ch * D + col] = sg;
         }
-        if (g4 == 0) ws.gGam[ch * D + col] = sg;
     }
     __syncthreads();
 
@@ -433,9 +524,21 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
 #pragma unroll
         for (int ct = half; ct < D / 16; ct += NHALF) {
             const int ii = (ct - half) / NHALF, col = 16 * ct + l16;
+            using P = GradPartials<D, IN_F32>;
+            if constexpr (KEEP && P::TLDS) {
+                // past the second stage's buffers, in its exchange layout (that
+                // region lies in the row-operand staging, dead since phase 1)
+                using GL = GGateLayout<D, IN_F32>;
+                *reinterpret_cast<typename P::V4*>(reinterpret_cast<OpT*>(smem + GL::BYTES) +
+                                                   xoff<GL::EPC, GL::NPC>(col, r_)) =
+                    to_v4<typename P::V4>(rkt[ii]);
+            } else if constexpr (KEEP) {
+                pk.kt[ii] = to_v4<typename P::V4>(rkt[ii]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                static_cast<OpT*>(ws.gKt)[ch * CHUNK * D + (r_ + e) * D + col] = from_f32<OpT>(rkt[ii][e]);
+                if constexpr (!KEEP)
+                    static_cast<OpT*>(ws.gKt)[ch * CHUNK * D + (r_ + e) * D + col] = from_f32<OpT>(rkt[ii][e]);
                 const int r = r_ + e;
                 if (r < nvalid) dv[base + r * tokstride + col] = from_f32<OutT>(rdv[ii][e]);
             }
@@ -508,13 +611,17 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
                 mma(fa, fb, acc);
             }
             const int x = 16 * xt + l16;
+            float dpv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 16 * at + 4 * g4 + e;
                 const float dl = (x < a) ? -acc[e] : 0.f;
-                static_cast<OpT*>(ws.gP)[ch * CHUNK * CHUNK + a * CHUNK + x] = from_f32<OpT>(s_beta[a] * dl);
+                dpv[e] = s_beta[a] * dl;
+                if constexpr (!KEEP)
+                    static_cast<OpT*>(ws.gP)[ch * CHUNK * CHUNK + a * CHUNK + x] = from_f32<OpT>(dpv[e]);
                 CB[a * LDF + x] = dl * pwv[t][e];
             }
+            if constexpr (KEEP) pk.p[t] = to_v4<typename GradPartials<D, IN_F32>::V4>(dpv);
         }
     }
     __syncthreads();
@@ -570,41 +677,20 @@ struct PairRows<_Float16, N> {
     __device__ __forceinline__ float operator[](int j) const { return static_cast<float>(v[j >> 1][j & 1]); }
 };
 
-template <int D, bool IN_F32>
-struct GGateLayout {
-    using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
-    static constexpr int OPB = sizeof(OpT);
-    static constexpr int PAD = 16 / OPB;
-    static constexpr int LDC = CHUNK + PAD;
-    static constexpr int NT = 4 * D;
-    static constexpr int NW = NT / WAVE;
-    static constexpr int DA = 0;                            // dA  [64][LDC]
-    static constexpr int DP = DA + CHUNK * LDC * OPB;       // dP  [64][LDC]
-    static constexpr int DAT = DP + CHUNK * LDC * OPB;      // dA^T
-    static constexpr int DPT = DAT + CHUNK * LDC * OPB;     // dP^T
-    static constexpr int QQT = DPT + CHUNK * LDC * OPB;     // Qq^T [D][LDC]
-    static constexpr int KQT = QQT + D * LDC * OPB;         // Kq^T
-    static constexpr int KHT = KQT + D * LDC * OPB;         // Kh^T
-    static constexpr int SA = KHT + D * LDC * OPB;          // fp32 [16][D]  dA_R Kh
-    static constexpr int SB = SA + 16 * D * 4;              // fp32 [16][D]  dP_R Kh
-    static constexpr int SC = SB + 16 * D * 4;              // fp32 [64][D]  dA_R^T Qq + dP_R^T Kq
-    static constexpr int BYTES = SC + CHUNK * D * 4;
-    static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
-};
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO>
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP>
 __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                const void* __restrict__ k_, const float* __restrict__ alpha,
                                                void* __restrict__ dq_, void* __restrict__ dk_,
                                                float* __restrict__ dalpha, ChunkWs ws, int pro, ChunkRange cr,
-                                               char* smem) {
+                                               char* smem, const GradPartials<D, IN_F32>& pk,
+                                               const float* s_gam, float (&s_tot)[4][D]) {
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
     constexpr int NT = L::NT, NW = L::NW, LDC = L::LDC, RPP = 16;
 
-    __shared__ float s_tot[4][D];
     __shared__ float s_gs[CHUNK];
     __shared__ float s_red[NW];
     __shared__ float s_row[CHUNK];
@@ -637,8 +723,8 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
     const InT* q = reinterpret_cast<const InT*>(q_);
     const InT* k = reinterpret_cast<const InT*>(k_);
-    const OpT* gA = static_cast<const OpT*>(ws.gA) + ch * CHUNK * CHUNK;
-    const OpT* gP = static_cast<const OpT*>(ws.gP) + ch * CHUNK * CHUNK;
+    const OpT* gA = KEEP ? nullptr : static_cast<const OpT*>(ws.gA) + ch * CHUNK * CHUNK;
+    const OpT* gP = KEEP ? nullptr : static_cast<const OpT*>(ws.gP) + ch * CHUNK * CHUNK;
 
     // ---------------- phase 0: G, block references, row operands, dA/dP ----------------
     // Every load of the phase is issued before any value is used, the token
@@ -698,9 +784,27 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
         s_tot[part][cc] = G[RPP - 1];
     }
-    // dA, dP (stored in operand precision) into LDS, both orientations, in
-    // 16-byte pieces of one row; Kh^T starts at zero.
-    {
+    // dA, dP (operand precision) into LDS, both orientations; Kh^T starts at
+    // zero.  On chip: from this thread's accumulator-layout values (four rows of
+    // a column), else from the workspace in 16-byte pieces of one row.
+    if constexpr (KEEP) {
+        using P = GradPartials<D, IN_F32>;
+        const int itp = wid & 3;
+#pragma unroll
+        for (int k2 = 0; k2 < P::NPW; ++k2) {
+            const int r = 16 * ((wid >> 2) + k2 * P::NHALF) + 4 * g4, i = 16 * itp + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dAs[(r + e) * LDC + i] = pk.a[k2][e];
+            *reinterpret_cast<typename P::V4*>(dAT + i * LDC + r) = pk.a[k2];
+        }
+#pragma unroll
+        for (int t = 0; t < P::NTL; ++t) {
+            const int tile = wid + t * NW, r = 16 * (tile / 4) + 4 * g4, i = 16 * (tile % 4) + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dPs[(r + e) * LDC + i] = pk.p[t][e];
+            *reinterpret_cast<typename P::V4*>(dPT + i * LDC + r) = pk.p[t];
+        }
+    } else {
         constexpr int EPV = 16 / static_cast<int>(sizeof(OpT));  // elements per piece
         constexpr int NV = CHUNK * CHUNK / EPV / NT;              // pieces per thread
         static_assert(CHUNK * CHUNK % (EPV * NT) == 0 && CHUNK % EPV == 0, "dA/dP pieces");
@@ -792,15 +896,16 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         store_run<OpT, RPP>(QqT + cc * LDC + r0, fq);
         store_run<OpT, RPP>(KqT + cc * LDC + r0, kq_);
     }
-    // flagged diagonal blocks are excluded from the matrix-core products
+    // flagged diagonal blocks are excluded from the matrix-core products: their
+    // Kh rows are zero in the row-side products (below), and their transposed
+    // dA and dP blocks are zeroed for the column side; dA and dP themselves
+    // keep the values the exact path reads
     if (flags) {
         for (int e = tid; e < 4 * 256; e += NT) {
             const int R = e / 256;
             if (!((flags >> R) & 1)) continue;
             const int r = 16 * R + (e % 256) / 16, i = 16 * R + e % 16;
             const OpT z = from_f32<OpT>(0.f);
-            dAs[r * LDC + i] = z;
-            dPs[r * LDC + i] = z;
             dAT[i * LDC + r] = z;
             dPT[i * LDC + r] = z;
         }
@@ -900,14 +1005,14 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     }
     // exact diagonal blocks (fp32, pair factors 2^(G_r - G_i) <= 1)
     if ((flags >> part) & 1) {
-        const OpT* gAr = gA + r0 * CHUNK + r0;
-        const OpT* gPr = gP + r0 * CHUNK + r0;
+        const OpT* sAr = dAs + r0 * LDC + r0;
+        const OpT* sPr = dPs + r0 * LDC + r0;
 #pragma unroll
         for (int jr = 0; jr < RPP; ++jr) {
 #pragma unroll
             for (int ji = 0; ji <= jr; ++ji) {
                 const float E = exp2_fast(G[jr] - G[ji]);
-                const float da = to_f32(gAr[jr * CHUNK + ji]), dp = (ji < jr) ? to_f32(gPr[jr * CHUNK + ji]) : 0.f;
+                const float da = to_f32(sAr[jr * LDC + ji]), dp = (ji < jr) ? to_f32(sPr[jr * LDC + ji]) : 0.f;
                 Aq[jr] += da * kk[ji] * E;
                 Prow[jr] += dp * kk[ji] * E;
                 Ccol[ji] += (da * qq[jr] + dp * kk[jr]) * E;
@@ -921,18 +1026,75 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     {
         OutT* dq = reinterpret_cast<OutT*>(dq_);
         OutT* dk = reinterpret_cast<OutT*>(dk_);
-        const OpT* gQt = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * D;
-        const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * D;
-        const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * D;
         // every partial is loaded before the first store (the stores could
         // alias them as far as the compiler knows); fp16 partials two rows to a
         // register, which keeps this phase within the register file
         PairRows<OpT, RPP> pq, pkt, pkb;
+        using P = GradPartials<D, IN_F32>;
+        if constexpr (KEEP && P::QREG) {
+            // on chip: this thread's accumulator-layout values into the exchange,
+            // then its 16 rows of column cc out of it, in 16-byte pieces
+            using V4 = typename P::V4;
+            constexpr int EPC = L::EPC, NPC = L::NPC;
+            OpT* X = reinterpret_cast<OpT*>(smem + L::XR);  // [3][D][64]: dQt, dKt, dKb
+            __syncthreads();  // the R loop's reads of SA..SC and the exact path's of dA, dP are done
+            {
+                const int col = 16 * wid + l16;
 #pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-            pq.set(j, gQt[(r0 + j) * D + cc]);
-            pkt.set(j, gKt[(r0 + j) * D + cc]);
-            pkb.set(j, gKb[(r0 + j) * D + cc]);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int o = xoff<EPC, NPC>(col, 16 * r4 + 4 * g4);
+                    *reinterpret_cast<V4*>(X + o) = pk.q[r4];
+                    *reinterpret_cast<V4*>(X + 2 * CHUNK * D + o) = pk.kb[r4];
+                }
+                const int rt = wid & 3, half = wid >> 2;
+#pragma unroll
+                for (int ii = 0; ii < P::NIT; ++ii) {
+                    const int c2 = 16 * (half + P::NHALF * ii) + l16;
+                    *reinterpret_cast<V4*>(X + CHUNK * D + xoff<EPC, NPC>(c2, 16 * rt + 4 * g4)) = pk.kt[ii];
+                }
+            }
+            __syncthreads();
+            static_assert(RPP % EPC == 0, "whole pieces per thread");
+#pragma unroll
+            for (int pc = 0; pc < RPP / EPC; ++pc) {
+                const int o = xoff<EPC, NPC>(cc, r0 + pc * EPC);
+                const uint4v vq = *reinterpret_cast<const uint4v*>(X + o);
+                const uint4v vt = *reinterpret_cast<const uint4v*>(X + CHUNK * D + o);
+                const uint4v vb = *reinterpret_cast<const uint4v*>(X + 2 * CHUNK * D + o);
+                const OpT* eq = reinterpret_cast<const OpT*>(&vq);
+                const OpT* et = reinterpret_cast<const OpT*>(&vt);
+                const OpT* eb = reinterpret_cast<const OpT*>(&vb);
+#pragma unroll
+                for (int u = 0; u < EPC; ++u) {
+                    pq.set(pc * EPC + u, eq[u]);
+                    pkt.set(pc * EPC + u, et[u]);
+                    pkb.set(pc * EPC + u, eb[u]);
+                }
+            }
+            if constexpr (PRO) __syncthreads();  // the prologue's dq_hat / dk_hat below overlap the exchange
+        } else {
+            const OpT* gQt = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * D;
+            const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * D;
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) {
+                pq.set(j, gQt[(r0 + j) * D + cc]);
+                pkb.set(j, gKb[(r0 + j) * D + cc]);
+            }
+            if constexpr (KEEP && P::TLDS) {
+                // dKt from LDS past this stage's buffers (written in the first stage)
+                const OpT* X = reinterpret_cast<const OpT*>(smem + L::BYTES);
+#pragma unroll
+                for (int pc = 0; pc < RPP / L::EPC; ++pc) {
+                    const uint4v vt = *reinterpret_cast<const uint4v*>(X + xoff<L::EPC, L::NPC>(cc, r0 + pc * L::EPC));
+                    const OpT* et = reinterpret_cast<const OpT*>(&vt);
+#pragma unroll
+                    for (int u = 0; u < L::EPC; ++u) pkt.set(pc * L::EPC + u, et[u]);
+                }
+            } else {
+                const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * D;
+#pragma unroll
+                for (int j = 0; j < RPP; ++j) pkt.set(j, gKt[(r0 + j) * D + cc]);
+            }
         }
         if constexpr (!PRO) {
 #pragma unroll
@@ -1005,7 +1167,7 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         for (int p = 0; p < 4; ++p) ltot += s_tot[p][cc];
         // the last row (and so every row, through the reverse cumsum) also gets
         // d/dG_last of Kb's 2^G_last and of gamma: sum_r k.dKb.2^(Gl-G) + gamma.dgamma
-        const float gl_term = ltot + exp2_fast(glast) * ws.gGam[ch * D + cc];
+        const float gl_term = ltot + exp2_fast(glast) * (KEEP ? s_gam[cc] : ws.gGam[ch * D + cc]);
         float run = later + gl_term;
         float dg[RPP];
 #pragma unroll
@@ -1064,15 +1226,24 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
                                                       ChunkRange cr, float* __restrict__ partial) {
     constexpr int LB = GLinLayout<D, IN_F32>::BYTES, GB = GGateLayout<D, IN_F32>::BYTES;
     static_assert(!CLER || ClerLayout<D, IN_F32>::POST_BYTES <= (LB > GB ? LB : GB), "LDS of the CLER terms");
-    __shared__ __attribute__((aligned(16))) char smem[LB > GB ? LB : GB];
-    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_, dbeta,
-                                                 ws, pro, cr, smem);
+    // On the value route the partials stay on chip; the error route's terms
+    // edit them in the workspace between the stages.
+    constexpr bool KEEP = !CLER;
+    // d = 128: dKt waits past the second stage's buffers
+    constexpr int GBX = GB + ((KEEP && GradPartials<D, IN_F32>::TLDS) ? CHUNK * D * (IN_F32 ? 4 : 2) : 0);
+    __shared__ __attribute__((aligned(16))) char smem[LB > GBX ? LB : GBX];
+    __shared__ float s_gam[KEEP ? D : 1];
+    __shared__ float s_tot[4][D];  // per-part column sums, used by both stages in turn
+    GradPartials<D, IN_F32> pk;
+    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_,
+                                                       dbeta, ws, pro, cr, smem, pk, s_gam, s_tot);
     __syncthreads();
     if constexpr (CLER) {
         cler_post_body<D, IN_F32, 4 * D>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
         __syncthreads();
     }
-    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr, smem);
+    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr,
+                                                        smem, pk, s_gam, s_tot);
 }
 
 

@@ -38,6 +38,12 @@ __device__ __forceinline__ void range_block(const ChunkRange& cr, int64_t& bh, i
 }
 #endif
 
+// The gradient stages hand their partials (dQt, dKb, dKt, dA, dP, dgamma) on
+// chip on the value route; on the error route, whose terms edit dKt and dP
+// between the stages, all go through the workspace.  At d = 128 dQt and dKb
+// still do on the value route (holding them on chip too would spill).
+constexpr bool grad_qkb_on_chip(int D) { return D == 64; }
+
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;
     float* gam;

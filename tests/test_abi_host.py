@@ -90,8 +90,13 @@ def test_workspace_size_formula(lib):
         assert lib.gdr_workspace_size(ctypes.byref(de), 0) == expect
         clvr_part = al(min(2 * 130, 256) * 3 * d * 4)
         cler_part = al(2 * 3 * 3 * d * 4)
+        # ... and the gradient partials that the value route hands between its
+        # two gradient stages on chip: dKt [64][d], dA, dP [64][64] and dgamma
+        # [d] always, dQt and dKb [64][d] at d = 64 only
+        on_chip = (al(nch * 64 * d * opb) + 2 * al(nch * 64 * 64 * opb) + al(nch * d * 4)
+                   + (2 * al(nch * 64 * d * opb) if d == 64 else 0))
         assert (lib.gdr_workspace_size(ctypes.byref(de), 1) - lib.gdr_workspace_size(ctypes.byref(dd), 1)
-                == al(nch * 64 * d * opb) + cler_part - clvr_part)
+                == al(nch * 64 * d * opb) + cler_part - clvr_part + on_chip)
         # the prologue keeps the activated beta and the reciprocal q and k row
         # norms: one fp32 per token slot each, in both layouts
         dp = desc(B=2, T=130, H=3, d=d, in_dt=in_dt, prologue=2)
