@@ -313,17 +313,18 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
         w.dUsave = take(mat);
         w.dUsaveT = take(mat);
         // the gradient partials the stages do not hand on chip
-        if (cler || !grad_qkb_on_chip(D)) {
+        const bool all = cler || grad_split(D, op_bytes == 4);
+        if (all || !grad_qkb_on_chip(D)) {
             w.gQt = take(mat);
             w.gKb = take(mat);
         }
-        if (cler) {
+        if (all) {
             w.gKt = take(mat);
             w.gA = take(sq);
             w.gP = take(sq);
             w.gGam = static_cast<float*>(take(size_t(nch) * D * 4));
-            w.Mt = take(mat);
         }
+        if (cler) w.Mt = take(mat);
     }
     if (out) *out = w;
     return off;
@@ -376,8 +377,8 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
     const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
-    if (train && desc->in_dtype == GDR_FP32 && D == 128)
-        return fail(GDR_ERR_UNSUPPORTED, "the backward supports fp32 inputs only at dk = dv = 64");
+    if (train && desc->in_dtype == GDR_FP32 && D == 128 && desc->prologue != GDR_PROLOGUE_NONE)
+        return fail(GDR_ERR_UNSUPPORTED, "the backward with the prologue supports fp32 inputs only at dk = dv = 64");
     const int64_t ntok = B * T * H;
     const bool any = ntok > 0;
     if (any && (!q || !k || !v || !beta || !o))
@@ -562,8 +563,8 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
     const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
-    if (desc->in_dtype == GDR_FP32 && D == 128)
-        return fail(GDR_ERR_UNSUPPORTED, "the backward supports fp32 inputs only at dk = dv = 64");
+    if (desc->in_dtype == GDR_FP32 && D == 128 && desc->prologue != GDR_PROLOGUE_NONE)
+        return fail(GDR_ERR_UNSUPPORTED, "the backward with the prologue supports fp32 inputs only at dk = dv = 64");
     const int64_t ntok = B * T * H;
     const bool any = ntok > 0;
     if (any && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))

@@ -24,7 +24,10 @@
 
 namespace gdr {
 
-template <int D, bool IN_F32>
+// NORO: the row operands dO, dU and U are read from global memory where they
+// are used instead of being staged in LDS (fp32 operands at d = 128, where the
+// staging does not fit).
+template <int D, bool IN_F32, bool NORO = false>
 struct GLinLayout {
     using OpT = typename std::conditional<IN_F32, float, _Float16>::type;
     static constexpr int OPB = sizeof(OpT);
@@ -44,7 +47,7 @@ struct GLinLayout {
     static constexpr int RDO = RO;                         //   scaled-free dO [64][D]
     static constexpr int RDU = RDO + CHUNK * D * OPB;      //   dU [64][D]
     static constexpr int RU = RDU + CHUNK * D * OPB;       //   U [64][D]
-    static constexpr int BYTES = RU + CHUNK * D * OPB;
+    static constexpr int BYTES = NORO ? RO : RU + CHUNK * D * OPB;
     // phase 3 reuses the Kt..T^T region (dead by then) for N^T and dT^T (fp32)
     static_assert(2 * CHUNK * LDF * 4 <= NF, "N^T and dT^T must fit below N");
 };
@@ -144,7 +147,7 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
 // buffer, which grads_kernel runs one after the other for a chunk.
 // KEEP: the partials stay on chip (pk, and dgamma in s_gam) instead of going
 // through the workspace.
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP>
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, bool NORO = false>
 __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, float scale,
                                               const void* __restrict__ k_, const void* __restrict__ v_,
                                               const float* __restrict__ beta, const float* __restrict__ alpha,
@@ -153,7 +156,7 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
                                               float* __restrict__ dbeta, ChunkWs ws, int pro,
                                               ChunkRange cr, char* smem, GradPartials<D, IN_F32>& pk,
                                               float* s_gam, float (&s_tot)[4][D]) {
-    using L = GLinLayout<D, IN_F32>;
+    using L = GLinLayout<D, IN_F32, NORO>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
     using OutT = typename InType<OUT_F32>::T;
@@ -232,7 +235,7 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
         // dU and U: 16-byte pieces into registers, written to LDS at the start of
         // phase 1.  (Not direct-to-LDS copies: while one of those is pending the
         // compiler makes every LDS access wait for all loads, phase 0's included.)
-        {
+        if constexpr (!NORO) {
             const uint4v* gdu = reinterpret_cast<const uint4v*>(static_cast<const char*>(ws.dUsave) + ch * CHUNK * D * L::OPB);
             const uint4v* gu = reinterpret_cast<const uint4v*>(static_cast<const char*>(ws.Usave) + ch * CHUNK * D * L::OPB);
 #pragma unroll
@@ -257,11 +260,13 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
             for (int kq = 0; kq < KQ; ++kq) load_frag_in<InT, OpT>(bV[kq], v + brow_g + 32 * kq + 8 * g4);
         }
         // dO pieces, converted into LDS at the start of phase 1
+        if constexpr (!NORO) {
 #pragma unroll
-        for (int k2 = 0; k2 < NP; ++k2) {
-            const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
-            const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
-            load_frag_in<InT, OpT>(xdo[k2], dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
+            for (int k2 = 0; k2 < NP; ++k2) {
+                const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
+                const int pos = 16 * (f / KQ) + (l & 15), j = 32 * (f % KQ) + 8 * (l >> 4);
+                load_frag_in<InT, OpT>(xdo[k2], dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + j);
+            }
         }
     }
 
@@ -331,7 +336,7 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
         const int nt = wid;             // this wave's value-column tile
         // dU and U into LDS; dO converted (rows past the end zero); V rows past
         // the end zeroed
-        {
+        if constexpr (!NORO) {
             uint4v* sdu = reinterpret_cast<uint4v*>(smem + L::RDU);
             uint4v* su = reinterpret_cast<uint4v*>(smem + L::RU);
 #pragma unroll
@@ -341,7 +346,7 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
             }
         }
 #pragma unroll
-        for (int k2 = 0; k2 < NP; ++k2) {
+        for (int k2 = 0; k2 < (NORO ? 0 : NP); ++k2) {
             const int p = k2 * NT + tid, f = p >> 6, l = p & 63;
             if (16 * (f / KQ) + (l & 15) >= nvalid) xdo[k2].zero();
             if constexpr (sizeof(OpT) == 2) {
@@ -373,6 +378,24 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
         sg += __shfl_xor(sg, 16);
         sg += __shfl_xor(sg, 32);
 
+        // fragment (row tile r4, 32-column step kq) of dO, dU or U
+        const OpT* gDU = reinterpret_cast<const OpT*>(ws.dUsave) + ch * CHUNK * D;
+        const OpT* gU = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
+        auto ld_do = [&](Frag<OpT>& f, int r4, int kq) {
+            if constexpr (NORO) {
+                const int pos = 16 * r4 + l16;
+                load_frag_in<InT, OpT>(f, dO + base + (pos < nvalid ? pos : nvalid - 1) * tokstride + 32 * kq + 8 * g4);
+                if (pos >= nvalid) f.zero();
+            } else {
+                f.load(sDO + ((r4 * KQ + kq) * 64 + lane) * 8);
+            }
+        };
+        auto ld_du = [&](Frag<OpT>& f, int r4, int kq) {
+            f.load((NORO ? gDU : sDU) + ((r4 * KQ + kq) * 64 + lane) * 8);
+        };
+        auto ld_u = [&](Frag<OpT>& f, int r4, int kq) {
+            f.load((NORO ? gU : sU) + ((r4 * KQ + kq) * 64 + lane) * 8);
+        };
         float rq[4][4], rk[4][4], ra[NPW][4];
         const int col = 16 * nt + l16;
 #pragma unroll
@@ -380,11 +403,10 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
             float4v aq = zero4(), aw = zero4(), ak = zero4();
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
-                const int fo = ((r4 * KQ + kq) * 64 + lane) * 8;
                 Frag<OpT> fo_, fdu, fu;
-                fo_.load(sDO + fo);
-                fdu.load(sDU + fo);
-                fu.load(sU + fo);
+                ld_do(fo_, r4, kq);
+                ld_du(fdu, r4, kq);
+                ld_u(fu, r4, kq);
                 mma(fo_, bS[kq], aq);
                 mma(fdu, bS[kq], aw);
                 mma(fu, bD[kq], ak);
@@ -402,17 +424,16 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
         // position tiles: dA = tril(dO U^T) (scaled), dT1 = dU V^T
         Frag<OpT> bU[KQ];
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) bU[kq].load(sU + ((itp * KQ + kq) * 64 + lane) * 8);
+        for (int kq = 0; kq < KQ; ++kq) ld_u(bU[kq], itp, kq);
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
             const int r4 = (wid >> 2) + k * NHALF;
             float4v aa = zero4(), at = zero4();
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
-                const int fo = ((r4 * KQ + kq) * 64 + lane) * 8;
                 Frag<OpT> fo_, fdu;
-                fo_.load(sDO + fo);
-                fdu.load(sDU + fo);
+                ld_do(fo_, r4, kq);
+                ld_du(fdu, r4, kq);
                 mma(fo_, bU[kq], aa);  // tiles above the diagonal are masked below (no branch here)
                 mma(fdu, bV[kq], at);
             }
@@ -678,13 +699,19 @@ struct PairRows<_Float16, N> {
 };
 
 
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP>
+// DS: the channels of a row (D is the number this call handles, channels
+// coff .. coff + D - 1).  With DS > D the channels are taken in npass calls
+// (pass = 0, 1, ..), and the scalar gate's per-row channel sums are carried
+// from one call to the next in s_acc.
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, int DS = D>
 __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                const void* __restrict__ k_, const float* __restrict__ alpha,
                                                void* __restrict__ dq_, void* __restrict__ dk_,
                                                float* __restrict__ dalpha, ChunkWs ws, int pro, ChunkRange cr,
                                                char* smem, const GradPartials<D, IN_F32>& pk,
-                                               const float* s_gam, float (&s_tot)[4][D]) {
+                                               const float* s_gam, float (&s_tot)[4][D], int coff = 0,
+                                               int npass = 1, int pass = 0, float* s_acc = nullptr) {
+    static_assert(DS == D || (!PRO && !KEEP), "channel passes: no prologue, partials in the workspace");
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -717,8 +744,8 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int cc = tid % D, part = tid / D, r0 = part * RPP;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int64_t tokstride = static_cast<int64_t>(H) * D;
-    const int64_t base = ((b * T + t0) * H + h) * D;
+    const int64_t tokstride = static_cast<int64_t>(H) * DS;
+    const int64_t base = ((b * T + t0) * H + h) * DS + coff;
     const int64_t nvalid64 = T - t0;
     const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
     const InT* q = reinterpret_cast<const InT*>(q_);
@@ -1073,12 +1100,12 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
             }
             if constexpr (PRO) __syncthreads();  // the prologue's dq_hat / dk_hat below overlap the exchange
         } else {
-            const OpT* gQt = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * D;
-            const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * D;
+            const OpT* gQt = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * DS + coff;
+            const OpT* gKb = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * DS + coff;
 #pragma unroll
             for (int j = 0; j < RPP; ++j) {
-                pq.set(j, gQt[(r0 + j) * D + cc]);
-                pkb.set(j, gKb[(r0 + j) * D + cc]);
+                pq.set(j, gQt[(r0 + j) * DS + cc]);
+                pkb.set(j, gKb[(r0 + j) * DS + cc]);
             }
             if constexpr (KEEP && P::TLDS) {
                 // dKt from LDS past this stage's buffers (written in the first stage)
@@ -1091,9 +1118,9 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                     for (int u = 0; u < L::EPC; ++u) pkt.set(pc * L::EPC + u, et[u]);
                 }
             } else {
-                const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * D;
+                const OpT* gKt = static_cast<const OpT*>(ws.gKt) + ch * CHUNK * DS + coff;
 #pragma unroll
-                for (int j = 0; j < RPP; ++j) pkt.set(j, gKt[(r0 + j) * D + cc]);
+                for (int j = 0; j < RPP; ++j) pkt.set(j, gKt[(r0 + j) * DS + cc]);
             }
         }
         if constexpr (!PRO) {
@@ -1167,7 +1194,7 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         for (int p = 0; p < 4; ++p) ltot += s_tot[p][cc];
         // the last row (and so every row, through the reverse cumsum) also gets
         // d/dG_last of Kb's 2^G_last and of gamma: sum_r k.dKb.2^(Gl-G) + gamma.dgamma
-        const float gl_term = ltot + exp2_fast(glast) * (KEEP ? s_gam[cc] : ws.gGam[ch * D + cc]);
+        const float gl_term = ltot + exp2_fast(glast) * (KEEP ? s_gam[cc] : ws.gGam[ch * DS + coff + cc]);
         float run = later + gl_term;
         float dg[RPP];
 #pragma unroll
@@ -1197,12 +1224,18 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                 if (lane == 0) s_wsum[(cc >> 6) * CHUNK + r0 + j] = x;
             }
             __syncthreads();
-            if (tid < nvalid) {
+            if (tid < CHUNK) {
                 float srow = s_wsum[tid];
 #pragma unroll
                 for (int w = 1; w < D / 64; ++w) srow += s_wsum[w * CHUNK + tid];
-                float a1 = alpha[(b * T + t0 + tid) * H + h];
-                dalpha[(b * T + t0 + tid) * H + h] = PRO ? dlogit_from_dlog(srow, a1, pro) : srow / a1;
+                if (npass > 1) {  // channel passes: the earlier passes' sum first
+                    if (pass > 0) srow = s_acc[tid] + srow;
+                    if (pass + 1 < npass) s_acc[tid] = srow;
+                }
+                if (pass + 1 == npass && tid < nvalid) {
+                    float a1 = alpha[(b * T + t0 + tid) * H + h];
+                    dalpha[(b * T + t0 + tid) * H + h] = PRO ? dlogit_from_dlog(srow, a1, pro) : srow / a1;
+                }
             }
         }
     }
@@ -1246,6 +1279,72 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
                                                         smem, pk, s_gam, s_tot);
 }
 
+// fp32 operands at d = 128, where one workgroup's LDS cannot hold either stage:
+// the stages as two kernels with every partial in the workspace.  The first
+// reads its row operands from global memory; the second takes the channels in
+// two passes of 64 (its block products are independent per channel).
+template <int GATE, bool OUT_F32, bool CLER>
+__global__ __launch_bounds__(512) void grad_lin_split_kernel(int64_t T, int H, int64_t NC, float scale,
+                                                             const void* __restrict__ k_, const void* __restrict__ v_,
+                                                             const float* __restrict__ beta,
+                                                             const float* __restrict__ alpha,
+                                                             const void* __restrict__ dO_, const void* __restrict__ dh_,
+                                                             const float* __restrict__ lam, void* __restrict__ dv_,
+                                                             float* __restrict__ dbeta, ChunkWs ws, ChunkRange cr,
+                                                             float* __restrict__ partial) {
+    constexpr int LB = GLinLayout<128, true, true>::BYTES;
+    static_assert(!CLER || ClerLayout<128, true>::POST_BYTES <= LB, "LDS of the CLER terms");
+    __shared__ __attribute__((aligned(16))) char smem[LB];
+    __shared__ float s_tot[4][128];
+    GradPartials<128, true> pk;
+    grad_lin_body<128, GATE, true, OUT_F32, false, false, true>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam,
+                                                                dv_, dbeta, ws, 0, cr, smem, pk, nullptr, s_tot);
+    if constexpr (CLER) {
+        __syncthreads();
+        cler_post_body<128, true, 512>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
+    }
+}
+
+template <int GATE, bool OUT_F32>
+__global__ __launch_bounds__(256) void grad_gate_split_kernel(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
+                                                              const void* __restrict__ k_,
+                                                              const float* __restrict__ alpha, void* __restrict__ dq_,
+                                                              void* __restrict__ dk_, float* __restrict__ dalpha,
+                                                              ChunkWs ws, ChunkRange cr) {
+    __shared__ __attribute__((aligned(16))) char smem[GGateLayout<64, true>::BYTES];
+    __shared__ float s_tot[4][64];
+    __shared__ float s_acc[CHUNK];
+    GradPartials<64, true> pk;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass) __syncthreads();
+        grad_gate_body<64, GATE, true, OUT_F32, false, false, 128>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, 0,
+                                                                   cr, smem, pk, nullptr, s_tot, 64 * pass, 2, pass,
+                                                                   s_acc);
+    }
+}
+
+template <int GATE, bool OUT_F32>
+static hipError_t launch_grads_split(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* q,
+                                     const void* k, const void* v, const float* beta, const float* alpha,
+                                     const void* dO, const void* dh, const float* lam, void* dq, void* dk, void* dv,
+                                     float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
+                                     bool cler, float* partial, hipStream_t stream) {
+    const int64_t nblk = B * H * cr.n;
+    if (nblk == 0) return hipSuccess;
+    if (pro) return hipErrorInvalidValue;  // rejected by the ABI
+    if (cler)
+        hipLaunchKernelGGL((grad_lin_split_kernel<GATE, OUT_F32, true>), dim3((unsigned)nblk), dim3(512), 0, stream, T,
+                           H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, cr, partial);
+    else
+        hipLaunchKernelGGL((grad_lin_split_kernel<GATE, OUT_F32, false>), dim3((unsigned)nblk), dim3(512), 0, stream,
+                           T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, cr, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((grad_gate_split_kernel<GATE, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
+                       q, k, alpha, dq, dk, dalpha, ws, cr);
+    return hipGetLastError();
+}
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
 static hipError_t launch_grads_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const void* q,
@@ -1283,7 +1382,10 @@ static hipError_t launch_grads_g(bool in_f32, bool out_f32, int64_t B, int64_t T
             if (out_f32) return launch_grads_t<D, GATE, true, true>(GDR_GR_ARGS);
             return launch_grads_t<D, GATE, true, false>(GDR_GR_ARGS);
         }
-        return hipErrorInvalidValue;  // fp32 operands at d = 128 exceed the LDS budget (rejected by the ABI)
+        if constexpr (D == 128) {
+            if (out_f32) return launch_grads_split<GATE, true>(GDR_GR_ARGS);
+            return launch_grads_split<GATE, false>(GDR_GR_ARGS);
+        }
     }
     if (out_f32) return launch_grads_t<D, GATE, false, true>(GDR_GR_ARGS);
     return launch_grads_t<D, GATE, false, false>(GDR_GR_ARGS);

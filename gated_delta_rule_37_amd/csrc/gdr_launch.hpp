@@ -43,6 +43,9 @@ __device__ __forceinline__ void range_block(const ChunkRange& cr, int64_t& bh, i
 // between the stages, all go through the workspace.  At d = 128 dQt and dKb
 // still do on the value route (holding them on chip too would spill).
 constexpr bool grad_qkb_on_chip(int D) { return D == 64; }
+// fp32 operands at d = 128 run the two stages as two kernels, every partial in
+// the workspace.
+constexpr bool grad_split(int D, bool in_f32) { return in_f32 && D == 128; }
 
 struct ChunkWs {
     void *W, *Ut, *Qt, *KbT, *A;

@@ -64,9 +64,12 @@ def test_backward_parity_bf16(gate, d, s0):
 
 
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
-def test_backward_parity_fp32(gate):
-    announce("backward fp32 gate=%s" % gate)
-    inp = gdr_inputs.make(B=1, T=150, H=2, d=64, gate=gate, dtype="fp32", seed=310, s0=True, bwd=True)
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_parity_fp32(gate, d):
+    """fp32 inputs; at d = 128 the two gradient stages run as two kernels, the
+    second in two passes of 64 channels."""
+    announce("backward fp32 gate=%s d=%d" % (gate, d))
+    inp = gdr_inputs.make(B=1, T=150, H=2, d=d, gate=gate, dtype="fp32", seed=310, s0=True, bwd=True)
     t = inputs_to_dev(inp, "fp32")
     g = gpu_backward(t, scale=0.8)
     errs = compare(inp, g, scale=0.8)
@@ -122,11 +125,12 @@ def test_backward_empty_sequence_passes_state_gradient():
 
 @pytest.mark.parametrize("gate", ["channel", "scalar"])
 @pytest.mark.parametrize("recipe", ["sigmoid(N(-1,1))", "uniform[1e-6,1e-3]"])
-def test_backward_strong_gates(recipe, gate):
-    announce("backward strong gates %s %s" % (gate, recipe))
-    inp = gdr_inputs.make(B=1, T=512, H=2, d=128, gate=gate, dtype="bf16", seed=340, s0=True, bwd=True,
-                          alpha_recipe=recipe)
-    t = inputs_to_dev(inp, "bf16")
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_backward_strong_gates(recipe, gate, dt):
+    announce("backward strong gates %s %s %s" % (gate, recipe, dt))
+    inp = gdr_inputs.make(B=1, T=512 if dt == "bf16" else 200, H=2, d=128, gate=gate, dtype=dt, seed=340, s0=True,
+                          bwd=True, alpha_recipe=recipe)
+    t = inputs_to_dev(inp, dt)
     g = gpu_backward(t)
     errs = compare(inp, g)
     # The chunked backward reaches dalpha through the gradient with respect to
@@ -140,10 +144,18 @@ def test_backward_strong_gates(recipe, gate):
     errs["alpha*dalpha"] = rel(dlog, ref["dalpha"] * inp["alpha"])
     raw = errs.pop("dalpha")
     report(raw_dalpha=raw, min_alpha=float(inp["alpha"].min()), **errs)
-    assert max(errs.values()) < 2e-3, errs
-    # the absolute error of d/dlog(alpha) is at most 2e-3 * max|d/dlog(alpha)|
+    bar = 2e-3 if dt == "bf16" else 1e-5
+    # fp32 inputs with alpha <= 1e-3: alpha * dalpha measures 1.2e-4 .. 7.7e-4 (d 64
+    # and 128, both gates), every other gradient <= 1e-6.  The in-chunk cumulative
+    # log2-decay G reaches about -1300 there, where the fp32 spacing is 1.2e-4, and
+    # alpha * dalpha sums many decay-weighted terms with cancellation, the likely
+    # cause.  It is held to the bf16 bar; with sigmoid(N(-1, 1)) gates it meets 1e-5.
+    gbar = 2e-3 if (dt == "fp32" and recipe == "uniform[1e-6,1e-3]") else bar
+    adal = errs.pop("alpha*dalpha")
+    assert max(errs.values()) < bar and adal < gbar, (adal, errs)
+    # the absolute error of d/dlog(alpha) is at most gbar * max|d/dlog(alpha)|
     # (asserted above); dividing by alpha >= min(alpha) bounds the raw error
-    bound = 2e-3 * np.abs(ref["dalpha"] * inp["alpha"]).max() / float(inp["alpha"].min())
+    bound = gbar * np.abs(ref["dalpha"] * inp["alpha"]).max() / float(inp["alpha"].min())
     assert raw * np.abs(ref["dalpha"]).max() <= bound, (raw, bound)
 
 
@@ -163,13 +175,14 @@ def test_backward_clvr_terms():
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
-@pytest.mark.parametrize("d", [64, 128])
-def test_backward_is_deterministic(gate, d):
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (128, "bf16"), (128, "fp32")])
+def test_backward_is_deterministic(gate, d, dt):
     """Two runs give the same bits (every reduction, the scalar gate's sum of
-    dalpha over channels included, runs in a fixed order)."""
-    announce("backward determinism gate=%s d=%d" % (gate, d))
-    inp = gdr_inputs.make(B=1, T=300, H=2, d=d, gate=gate, dtype="bf16", seed=360, s0=True, bwd=True)
-    t = inputs_to_dev(inp, "bf16")
+    dalpha over channels included, runs in a fixed order; at fp32 d = 128 that
+    sum is carried from the first channel pass to the second)."""
+    announce("backward determinism gate=%s d=%d %s" % (gate, d, dt))
+    inp = gdr_inputs.make(B=1, T=300, H=2, d=d, gate=gate, dtype=dt, seed=360, s0=True, bwd=True)
+    t = inputs_to_dev(inp, dt)
     g1 = gpu_backward(t)
     g2 = gpu_backward(t)
     for n in NAMES:

@@ -62,7 +62,8 @@ def dev_inputs(inp, in_dt):
 
 @pytest.mark.parametrize("gate,d,in_dt", [("none", 128, "bf16"), ("scalar", 128, "bf16"),
                                           ("channel", 128, "bf16"), ("channel", 64, "bf16"),
-                                          ("scalar", 64, "fp32"), ("channel", 64, "fp32")])
+                                          ("scalar", 64, "fp32"), ("channel", 64, "fp32"),
+                                          ("scalar", 128, "fp32"), ("channel", 128, "fp32")])
 def test_cler_forward_and_backward_match_oracle(gate, d, in_dt):
     announce("cler gate=%s d=%d in=%s" % (gate, d, in_dt))
     inp, lam, dh, dST = case(gate, d, in_dt, seed=500 + d + (7 if in_dt == "fp32" else 0))
