@@ -377,8 +377,6 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
     const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
-    if (train && desc->in_dtype == GDR_FP32 && D == 128 && desc->prologue != GDR_PROLOGUE_NONE)
-        return fail(GDR_ERR_UNSUPPORTED, "the backward with the prologue supports fp32 inputs only at dk = dv = 64");
     const int64_t ntok = B * T * H;
     const bool any = ntok > 0;
     if (any && (!q || !k || !v || !beta || !o))
@@ -563,8 +561,6 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
     const int64_t B = desc->B, T = desc->T, H = desc->H, D = desc->dk;
-    if (desc->in_dtype == GDR_FP32 && D == 128 && desc->prologue != GDR_PROLOGUE_NONE)
-        return fail(GDR_ERR_UNSUPPORTED, "the backward with the prologue supports fp32 inputs only at dk = dv = 64");
     const int64_t ntok = B * T * H;
     const bool any = ntok > 0;
     if (any && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))

@@ -701,8 +701,10 @@ struct PairRows<_Float16, N> {
 
 // DS: the channels of a row (D is the number this call handles, channels
 // coff .. coff + D - 1).  With DS > D the channels are taken in npass calls
-// (pass = 0, 1, ..), and the scalar gate's per-row channel sums are carried
-// from one call to the next in s_acc.
+// (pass = 0, 1, ..); s_acc ([3][64] floats) carries the scalar gate's per-row
+// channel sums and the prologue's row dots from one call to the next, and the
+// prologue's earlier passes leave dq_hat, dk_hat in their workspace partial
+// slots for the last pass to finish.
 template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, int DS = D>
 __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                const void* __restrict__ k_, const float* __restrict__ alpha,
@@ -711,7 +713,7 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                                                char* smem, const GradPartials<D, IN_F32>& pk,
                                                const float* s_gam, float (&s_tot)[4][D], int coff = 0,
                                                int npass = 1, int pass = 0, float* s_acc = nullptr) {
-    static_assert(DS == D || (!PRO && !KEEP), "channel passes: no prologue, partials in the workspace");
+    static_assert(DS == D || !KEEP, "channel passes keep the partials in the workspace");
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -1161,16 +1163,71 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                 dot[RPP + j] = kk[j] * dkv;
             }
             part_row_sums32<D>(dot, s_nrm);
+            if (npass > 1) {
+                // channel passes: a row's dots run over every pass (the earlier
+                // passes' sums first)
+                float* pdot = s_acc + CHUNK;  // [2][64]
+                if (pass > 0) {
 #pragma unroll
-            for (int j = 0; j < RPP; ++j) {
-                const int r = r0 + j;
-                if (r >= nvalid) continue;
-                const float rq = s_rq[r], rk = s_rk[r];
-                const float dqv = sQ[r * D + cc], dkv = sK[r * D + cc];
-                const float gq = (rq > 0.f) ? (dqv - qq[j] * dot[j]) * rq : -dqv * rq;
-                const float gk = (rk > 0.f) ? (dkv - kk[j] * dot[RPP + j]) * rk : -dkv * rk;
-                dq[base + r * tokstride + cc] = from_f32<OutT>(gq);
-                dk[base + r * tokstride + cc] = from_f32<OutT>(gk);
+                    for (int j = 0; j < RPP; ++j) {
+                        dot[j] = pdot[r0 + j] + dot[j];
+                        dot[RPP + j] = pdot[CHUNK + r0 + j] + dot[RPP + j];
+                    }
+                }
+                __syncthreads();
+                if (cc == 0) {
+#pragma unroll
+                    for (int j = 0; j < RPP; ++j) {
+                        pdot[r0 + j] = dot[j];
+                        pdot[CHUNK + r0 + j] = dot[RPP + j];
+                    }
+                }
+                if (pass + 1 < npass) {
+                    // dq_hat, dk_hat wait in this pass's dQt, dKb slots (read above)
+                    OpT* hq = static_cast<OpT*>(ws.gQt) + ch * CHUNK * DS + coff;
+                    OpT* hk = static_cast<OpT*>(ws.gKb) + ch * CHUNK * DS + coff;
+#pragma unroll
+                    for (int j = 0; j < RPP; ++j) {
+                        hq[(r0 + j) * DS + cc] = from_f32<OpT>(sQ[(r0 + j) * D + cc]);
+                        hk[(r0 + j) * DS + cc] = from_f32<OpT>(sK[(r0 + j) * D + cc]);
+                    }
+                }
+            }
+            if (npass == 1 || pass + 1 == npass) {
+#pragma unroll
+                for (int j = 0; j < RPP; ++j) {
+                    const int r = r0 + j;
+                    if (r >= nvalid) continue;
+                    const float rq = s_rq[r], rk = s_rk[r];
+                    const float dqv = sQ[r * D + cc], dkv = sK[r * D + cc];
+                    const float gq = (rq > 0.f) ? (dqv - qq[j] * dot[j]) * rq : -dqv * rq;
+                    const float gk = (rk > 0.f) ? (dkv - kk[j] * dot[RPP + j]) * rk : -dkv * rk;
+                    dq[base + r * tokstride + cc] = from_f32<OutT>(gq);
+                    dk[base + r * tokstride + cc] = from_f32<OutT>(gk);
+                }
+            }
+            if (npass > 1 && pass + 1 == npass) {
+                // the earlier passes' channels, from their waiting dq_hat, dk_hat and
+                // their q and k rows normalised again
+#pragma unroll 1
+                for (int pp = 0; pp + 1 < npass; ++pp) {
+                    const int64_t bp = base - coff + D * pp;
+                    const OpT* hq = static_cast<const OpT*>(ws.gQt) + ch * CHUNK * DS + D * pp;
+                    const OpT* hk = static_cast<const OpT*>(ws.gKb) + ch * CHUNK * DS + D * pp;
+#pragma unroll 2
+                    for (int j = 0; j < RPP; ++j) {
+                        const int r = r0 + j;
+                        if (r >= nvalid) continue;
+                        const float rq = s_rq[r], rk = s_rk[r];
+                        const float qh = to_f32(q[bp + r * tokstride + cc]) * fabsf(rq);
+                        const float kh = to_f32(k[bp + r * tokstride + cc]) * fabsf(rk);
+                        const float dqv = to_f32(hq[r * DS + cc]), dkv = to_f32(hk[r * DS + cc]);
+                        const float gq = (rq > 0.f) ? (dqv - qh * dot[j]) * rq : -dqv * rq;
+                        const float gk = (rk > 0.f) ? (dkv - kh * dot[RPP + j]) * rk : -dkv * rk;
+                        dq[bp + r * tokstride + cc] = from_f32<OutT>(gq);
+                        dk[bp + r * tokstride + cc] = from_f32<OutT>(gk);
+                    }
+                }
             }
         }
     }
@@ -1283,44 +1340,44 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
 // the stages as two kernels with every partial in the workspace.  The first
 // reads its row operands from global memory; the second takes the channels in
 // two passes of 64 (its block products are independent per channel).
-template <int GATE, bool OUT_F32, bool CLER>
+template <int GATE, bool OUT_F32, bool CLER, bool PRO>
 __global__ __launch_bounds__(512) void grad_lin_split_kernel(int64_t T, int H, int64_t NC, float scale,
                                                              const void* __restrict__ k_, const void* __restrict__ v_,
                                                              const float* __restrict__ beta,
                                                              const float* __restrict__ alpha,
                                                              const void* __restrict__ dO_, const void* __restrict__ dh_,
                                                              const float* __restrict__ lam, void* __restrict__ dv_,
-                                                             float* __restrict__ dbeta, ChunkWs ws, ChunkRange cr,
-                                                             float* __restrict__ partial) {
+                                                             float* __restrict__ dbeta, ChunkWs ws, int pro,
+                                                             ChunkRange cr, float* __restrict__ partial) {
     constexpr int LB = GLinLayout<128, true, true>::BYTES;
     static_assert(!CLER || ClerLayout<128, true>::POST_BYTES <= LB, "LDS of the CLER terms");
     __shared__ __attribute__((aligned(16))) char smem[LB];
     __shared__ float s_tot[4][128];
     GradPartials<128, true> pk;
-    grad_lin_body<128, GATE, true, OUT_F32, false, false, true>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam,
-                                                                dv_, dbeta, ws, 0, cr, smem, pk, nullptr, s_tot);
+    grad_lin_body<128, GATE, true, OUT_F32, PRO, false, true>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam,
+                                                              dv_, dbeta, ws, pro, cr, smem, pk, nullptr, s_tot);
     if constexpr (CLER) {
         __syncthreads();
         cler_post_body<128, true, 512>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
     }
 }
 
-template <int GATE, bool OUT_F32>
+template <int GATE, bool OUT_F32, bool PRO>
 __global__ __launch_bounds__(256) void grad_gate_split_kernel(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                               const void* __restrict__ k_,
                                                               const float* __restrict__ alpha, void* __restrict__ dq_,
                                                               void* __restrict__ dk_, float* __restrict__ dalpha,
-                                                              ChunkWs ws, ChunkRange cr) {
+                                                              ChunkWs ws, int pro, ChunkRange cr) {
     __shared__ __attribute__((aligned(16))) char smem[GGateLayout<64, true>::BYTES];
     __shared__ float s_tot[4][64];
-    __shared__ float s_acc[CHUNK];
+    __shared__ float s_acc[3 * CHUNK];
     GradPartials<64, true> pk;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
         if (pass) __syncthreads();
-        grad_gate_body<64, GATE, true, OUT_F32, false, false, 128>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, 0,
-                                                                   cr, smem, pk, nullptr, s_tot, 64 * pass, 2, pass,
-                                                                   s_acc);
+        grad_gate_body<64, GATE, true, OUT_F32, PRO, false, 128>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro,
+                                                                 cr, smem, pk, nullptr, s_tot, 64 * pass, 2, pass,
+                                                                 s_acc);
     }
 }
 
@@ -1332,17 +1389,25 @@ static hipError_t launch_grads_split(int64_t B, int64_t T, int H, int64_t NC, fl
                                      bool cler, float* partial, hipStream_t stream) {
     const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
-    if (pro) return hipErrorInvalidValue;  // rejected by the ABI
-    if (cler)
-        hipLaunchKernelGGL((grad_lin_split_kernel<GATE, OUT_F32, true>), dim3((unsigned)nblk), dim3(512), 0, stream, T,
-                           H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, cr, partial);
-    else
-        hipLaunchKernelGGL((grad_lin_split_kernel<GATE, OUT_F32, false>), dim3((unsigned)nblk), dim3(512), 0, stream,
-                           T, H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, cr, partial);
+#define GDR_LIN_SPLIT(C, P)                                                                                      \
+    hipLaunchKernelGGL((grad_lin_split_kernel<GATE, OUT_F32, C, P>), dim3((unsigned)nblk), dim3(512), 0, stream, T, \
+                       H, NC, scale, k, v, beta, alpha, dO, dh, lam, dv, dbeta, ws, pro, cr, partial)
+    if (cler) {
+        if (pro) GDR_LIN_SPLIT(true, true);
+        else GDR_LIN_SPLIT(true, false);
+    } else {
+        if (pro) GDR_LIN_SPLIT(false, true);
+        else GDR_LIN_SPLIT(false, false);
+    }
+#undef GDR_LIN_SPLIT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grad_gate_split_kernel<GATE, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, stream, T, H, NC,
-                       q, k, alpha, dq, dk, dalpha, ws, cr);
+    if (pro)
+        hipLaunchKernelGGL((grad_gate_split_kernel<GATE, OUT_F32, true>), dim3((unsigned)nblk), dim3(256), 0, stream, T,
+                           H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
+    else
+        hipLaunchKernelGGL((grad_gate_split_kernel<GATE, OUT_F32, false>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                           T, H, NC, q, k, alpha, dq, dk, dalpha, ws, pro, cr);
     return hipGetLastError();
 }
 

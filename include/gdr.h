@@ -183,9 +183,7 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
  *   dclvr_scale [H*dv] fp32, NULL = not written (requires dh_clvr).
  *   ws        at least gdr_workspace_size(desc, 1) bytes.
  * fp32 inputs at dk = dv = 128 run the two gradient stages as two kernels
- * (neither fits one workgroup's LDS with fp32 operands); with the prologue
- * they return GDR_ERR_UNSUPPORTED (its normalisation backward needs whole-row
- * sums that the second stage, taken in channel passes, does not form).
+ * (neither fits one workgroup's LDS with fp32 operands).
  */
 gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, const void* v,
                         const float* beta, const float* alpha, const float* S0,
@@ -208,8 +206,6 @@ gdr_status gdr_backward(const gdr_desc* desc, const void* q, const void* k, cons
  * gdr_forward_train call on the same stream, with the same desc, q, k, v, beta,
  * alpha and S0, none of them modified in between (the library cannot check
  * this; other contents give wrong gradients, never an out-of-bounds access).
- * fp32 inputs with the prologue at dk = dv = 128 return GDR_ERR_UNSUPPORTED,
- * as for gdr_backward.
  */
 gdr_status gdr_forward_train(const gdr_desc* desc, const void* q, const void* k,
                              const void* v, const float* beta, const float* alpha,

@@ -63,13 +63,11 @@ static void run_pair(const gdr_desc& d, bool train) {
     auto F = [](char* p) { return reinterpret_cast<float*>(p); };
     gdr_status s = (train ? gdr_forward_train : gdr_forward_chunked)(
         &d, q.p, k.p, v.p, F(beta.p), al, F(S0.p), o.p, F(ST.p), h.p, F(lam.p), ws.p, wf, nullptr);
-    // fp32 inputs with the prologue have no backward at d = 128 (nor a training forward)
-    const bool bwd_ok = !(d.in_dtype == GDR_FP32 && d.dk == 128 && d.prologue != GDR_PROLOGUE_NONE);
-    EXPECT(s == ((train && !bwd_ok) ? GDR_ERR_UNSUPPORTED : GDR_OK), "forward status %d", int(s));
+    EXPECT(s == GDR_OK, "forward status %d", int(s));
     s = (train ? gdr_backward_saved : gdr_backward)(&d, q.p, k.p, v.p, F(beta.p), al, F(S0.p), dO.p, F(dST.p),
                                                     dh.p, F(lam.p), dq.p, dk.p, dv.p, F(dbeta.p), dal, F(dS0.p),
                                                     F(dlam.p), ws.p, wb, nullptr);
-    EXPECT(s == (bwd_ok ? GDR_OK : GDR_ERR_UNSUPPORTED), "backward status %d", int(s));
+    EXPECT(s == GDR_OK, "backward status %d", int(s));
     // a workspace one byte short is refused before anything runs
     const long before = stub::launches;
     if (wf > 0) {
@@ -126,8 +124,8 @@ int main() {
                             const int d = in == GDR_FP32 ? 64 : 128;
                             run_pair(desc(2, T, 2, d, gate, in, GDR_FP32, route, pro), train != 0);
                         }
-    // fp32 at d = 128: the two-kernel gradient path, all routes; with the prologue
-    // no backward
+    // fp32 at d = 128: the two-kernel gradient path, every route, with and without
+    // the prologue
     for (int train = 0; train < 2; ++train)
         for (int route = 0; route < 2; ++route)
             for (int pro = 0; pro < 3; pro += 2)

@@ -50,8 +50,12 @@ def errors(o, ST, g, o_ref, ST_ref, ref):
 @pytest.mark.parametrize("gate,d,in_dt,mode", [
     ("none", 128, "bf16", "forget"), ("scalar", 128, "bf16", "sigmoid"), ("scalar", 128, "bf16", "forget"),
     ("channel", 128, "bf16", "forget"), ("channel", 128, "bf16", "sigmoid"), ("channel", 64, "bf16", "forget"),
-    ("scalar", 64, "fp32", "forget"), ("channel", 64, "fp32", "sigmoid"), ("channel", 64, "fp32", "forget")])
+    ("scalar", 64, "fp32", "forget"), ("channel", 64, "fp32", "sigmoid"), ("channel", 64, "fp32", "forget"),
+    ("scalar", 128, "fp32", "forget"), ("channel", 128, "fp32", "sigmoid"), ("none", 128, "fp32", "forget")])
 def test_prologue_matches_oracle(gate, d, in_dt, mode):
+    """At fp32 d = 128 the second gradient stage runs in two channel passes: the
+    row-norm backward's row dots are carried across them and the first pass's
+    channels are finished by the second."""
     announce("prologue gate=%s d=%d in=%s mode=%s" % (gate, d, in_dt, mode))
     inp = gdr_inputs.make(B=2, T=200, H=2, d=d, gate=gate, dtype=in_dt, seed=600 + d, s0=True, bwd=True,
                           prologue=mode)
@@ -73,11 +77,12 @@ def test_prologue_ragged_lengths(T):
     assert max(errs.values()) < 2e-3, errs
 
 
-def test_prologue_zero_rows_take_the_clamped_norm():
+@pytest.mark.parametrize("d", [64, 128])
+def test_prologue_zero_rows_take_the_clamped_norm(d):
     """A zero q row and a zero k row: their norms are clamped, the normalised
     rows are zero and the gradients are dx_hat / eps (no projection term)."""
-    announce("prologue zero rows")
-    inp = gdr_inputs.make(B=1, T=70, H=2, d=64, gate="channel", dtype="fp32", seed=620, bwd=True,
+    announce("prologue zero rows d=%d" % d)
+    inp = gdr_inputs.make(B=1, T=70, H=2, d=d, gate="channel", dtype="fp32", seed=620, bwd=True,
                           prologue="forget")
     inp["q"][0, 5, 1] = 0.0
     inp["k"][0, 66, 0] = 0.0

@@ -95,21 +95,6 @@ def test_training_pair_fp32_equals_separate_calls(d):
     assert max(errs.values()) < 1e-5, errs
 
 
-def test_training_forward_rejects_fp32_d128_with_prologue():
-    """fp32 inputs at d = 128 with the prologue have no backward (its row-norm
-    backward needs whole rows, which the channel passes of that shape do not
-    form): the training forward refuses them up front."""
-    inp = gdr_inputs.make(B=1, T=64, H=1, d=128, gate="channel", dtype="fp32", seed=411, prologue="sigmoid")
-    t = inputs_to_dev(inp, "fp32")
-    nb = gdr.workspace_size(1, 64, 1, 128, gdr.GATE_CHANNEL, torch.float32, torch.float32, backward=True,
-                            prologue="sigmoid")
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    with pytest.raises(gdr.GdrError) as e:
-        gdr.forward(t["q"], t["k"], t["v"], t["beta"], t["alpha"], None, workspace=ws, save_for_backward=True,
-                    prologue="sigmoid")
-    assert e.value.code == 2
-
-
 def test_training_pair_full_layer_equals_separate_calls():
     """350M-layer shape (B=8, T=4096, H=8, d=128, KDA, bf16, CLVR)."""
     announce("training pair full c4")
