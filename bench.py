@@ -184,6 +184,19 @@ def cuda_time_ms(fn, steps, warmup=1):
     return e0.elapsed_time(e1) / steps
 
 
+def per_call_ms(fn, n):
+    """Milliseconds of each of n calls of fn(), each between its own pair of
+    events on the current stream (the calls run back to back)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def host_cpu():
     """(cores available to this process, cores on the host, CPU model name)."""
     try:
@@ -272,12 +285,15 @@ def main():
     kt = timer.end()
     kernels = {n: {"launches": c, "avg_us": 1e3 * ms / c} for n, (c, ms) in kt.items()}
     log("step %.3f ms; kernels %s" % (ms_step, json.dumps(kernels)))
+    # the spread of single steps (each between its own events), beside the mean above
+    per_step = per_call_ms(step, args.steps)
 
     # the inference forward alone (no intermediates kept), timed the same way
     def fwd():
         gdr.forward(q, k, v, beta, alpha, None, h=h, clvr_scale=lam, workspace=ws_f, output_final_state=True)
 
     fwd_us = 1e3 * cuda_time_ms(fwd, args.steps)
+    per_fwd = per_call_ms(fwd, args.steps)
     timer.begin()
     for _ in range(args.steps):
         fwd()
@@ -649,6 +665,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_min": round(float(np.min(per_step)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -660,7 +678,9 @@ def main():
         "roofline": roofline,
         "step_roofline": step_roof,
         "cpu_baseline": cpu,
-        "forward": {"us": round(fwd_us, 2), "tokens_per_s": round(tokens / (fwd_us * 1e-6), 1),
+        "forward": {"us": round(fwd_us, 2), "us_median": round(1e3 * float(np.median(per_fwd)), 2),
+                    "us_min": round(1e3 * float(np.min(per_fwd)), 2),
+                    "tokens_per_s": round(tokens / (fwd_us * 1e-6), 1),
                     "alg_GBs": round(fwd_bytes / (fwd_us * 1e-6) / 1e9, 1),
                     "alg_TFLOPs": round(fwd_flops / (fwd_us * 1e-6) / 1e12, 2),
                     "hbm_frac": round(fwd_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
