@@ -24,16 +24,15 @@
 // and the pass runs U = Ut - W S, O = scale (Qt S + A U + Y),
 // S <- Diag(gam) S + KbT U + X.
 //
-// Range of the decay factors: every product of a row factor 2^(G_r - ref) and a
-// column factor 2^(ref - G_j) uses a reference between the two (the end of the
-// column block for blocks below the diagonal, so both factors are at most 1;
-// the start of the block on the diagonal, where the column factor is at most
-// 2^rho for the block's decay range rho).  A diagonal block whose range exceeds
-// 60 (in log2) is computed pair by pair with 2^(G_r - G_j) formed directly.
-// The four C x C matrices are formed with fp32 operands on matrix cores.  For
-// bf16 inputs the three products with V (X, Y, M_w V) take fp16 operands and
-// the pass's operands W, Ut, Qt, KbT, A are stored in fp16 (the operand
-// precision of the KDA path); X and Y stay fp32.  fp32 inputs keep fp32 throughout.
+// Two intra-chunk kernels compute these operands.  For bf16 inputs
+// (gdn2_intra_h_kernel) every product takes fp16 operands with fp32
+// accumulation, the operands are staged once in LDS, and the stored W, Ut, Qt,
+// KbT, A are fp16 (the operand precision of the KDA path); X and Y stay fp32.
+// For fp32 inputs (gdn2_intra_kernel) everything is fp32 and the block pairs
+// are formed pair by pair from the inputs: its LDS budget has no room for fp32
+// staging.  In both, a diagonal block whose decay range exceeds what the
+// operands carry (2^8 for fp16, 2^60 for fp32) is computed without the split
+// into row and column factors.
 #include <type_traits>
 
 #include "gdr_common.hpp"
@@ -78,6 +77,13 @@ __device__ __forceinline__ void set_frag(Frag<OpT>& f, const float (&x)[8]) {
     for (int i = 0; i < 8; ++i) f.v[i] = from_f32<OpT>(x[i]);
 }
 
+// fp32 inputs.  Range of the decay factors: every product of a row factor
+// 2^(G_r - ref) and a column factor 2^(ref - G_j) uses a reference between the
+// two (the end of the column block for blocks below the diagonal, so both
+// factors are at most 1; the start of the block on the diagonal, where the
+// column factor is at most 2^rho for the block's decay range rho).  A diagonal
+// block whose range exceeds 60 (in log2) is computed pair by pair with
+// 2^(G_r - G_j) formed directly.
 template <int D, int GATE, bool IN_F32>
 __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                          const void* __restrict__ k_, const void* __restrict__ v_,
@@ -491,6 +497,503 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     }
 }
 
+// The intra-chunk transform for fp16 operands (bf16 inputs), staged once in LDS.
+//
+// Decay factors.  With ref(R) = G at the last row before block R (0 for R = 0)
+// and end(J) = G at the last row of block J, every pair factor 2^(G_r - G_j)
+// (j <= r) splits into per-element factors of at most 1 and one per-channel
+// scale per block pair:
+//     2^(G_r - G_j) = a_r * c_RJ * b_j,   a_r = 2^(G_r - ref(R)),
+//     b_j = 2^(end(J) - G_j),             c_RJ = 2^(ref(R) - end(J)).
+// c_RJ = 1 for J = R - 1, <= 1 further below the diagonal, and on the diagonal
+// it is 2^rho_R (rho_R the block's whole decay), the only factor above 1: a
+// block with rho_R > 8 is computed exactly instead, from running products of
+// alpha.  The row operands k a and q a are staged in fp32 and the column
+// operands (e k) b and (w k) b in fp16, so each block pair only scales its row
+// operands by c_RJ before the single rounding to fp16.  All exponents are <= 0
+// apart from the diagonal scale, so no chunk is too wide for the fp32 range.
+//
+// Solve.  N_RR = (I + M_e[R,R])^-1 for the four diagonal blocks, one lane per
+// column, then for each block row R (in order)
+//     Z_R = N_RR (rhs_R - sum_{K<R} M_e[R,K] Z_K),  rhs = [Kt | M_w V],
+// on fp32 matrix cores.  Each wave owns whole 16-column tiles of Z and keeps
+// its Z_K in registers: the lane layout of the 16x16x4 fp32 product gives lane
+// group g the reduction indices 4g .. 4g+3, the rows of the accumulator it
+// holds, so Z_K feeds the next product directly and block rows need no barrier.
+template <int D, int GATE>
+struct Gdn2HLayout {
+    static constexpr int P = NT2 / D;       // row parts (one channel per thread)
+    static constexpr int RPP = CHUNK / P;   // rows per part: 8 or 16, inside one block
+    static constexpr int NCT = D / 16;      // 16-column tiles of a [..][D] matrix
+    static constexpr int LKR = D + 4;       // fp32 rows of the staged row operands
+    static constexpr int LEH = D + 8;       // fp16 rows of the staged column operands
+    static constexpr int LT32 = CHUNK + 4;  // fp32 rows of [D][64] Kt^T
+    static constexpr int LT16 = CHUNK + 8;  // fp16 rows of [D][64] V^T and Wb^T
+    static constexpr int LM32 = CHUNK + 4;  // fp32 rows of M_e
+    static constexpr int LM16 = CHUNK + 8;  // fp16 rows of A_e, M_w, A_w
+    static constexpr int LN = 20;           // fp32 rows of the diagonal inverses
+    // region A, block pairs: k a and q a (fp32), (e k) b and (w k) b (fp16)
+    static constexpr int KR = 0;
+    static constexpr int QR = KR + CHUNK * LKR * 4;
+    static constexpr int EH = QR + CHUNK * LKR * 4;
+    static constexpr int WH = EH + CHUNK * LEH * 2;
+    static constexpr int PAIRS_END = WH + CHUNK * LEH * 2;
+    // region A, after the block pairs: Kt^T (fp32), V^T and Wb^T (fp16; Wb^T's
+    // space then stages W in fragment order), Qt in fragment order
+    static constexpr int KTT = 0;
+    static constexpr int VT = KTT + D * LT32 * 4;
+    static constexpr int WBT = VT + D * LT16 * 2;
+    static constexpr int QTS = WBT + D * LT16 * 2;
+    static constexpr int SOLVE_END = QTS + CHUNK * D * 2;
+    static constexpr int AREG = PAIRS_END > SOLVE_END ? PAIRS_END : SOLVE_END;
+    // the four C x C matrices and the diagonal inverses
+    static constexpr int ME = AREG;
+    static constexpr int AE = ME + CHUNK * LM32 * 4;
+    static constexpr int MW = AE + CHUNK * LM16 * 2;
+    static constexpr int AW = MW + CHUNK * LM16 * 2;
+    static constexpr int NINV = AW + CHUNK * LM16 * 2;
+    static constexpr int BYTES = NINV + 4 * 16 * LN * 4;
+    static_assert(CHUNK * D * 2 <= D * LT16 * 2, "W staging fits in Wb^T's space");
+    static_assert(RPP == 8 || RPP == 16, "a part lies inside one 16-row block");
+};
+
+template <int D, int GATE>
+__global__ __launch_bounds__(NT2) void gdn2_intra_h_kernel(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
+                                                           const void* __restrict__ k_, const void* __restrict__ v_,
+                                                           const float* __restrict__ erase,
+                                                           const float* __restrict__ write,
+                                                           const float* __restrict__ alpha, ChunkWs ws) {
+    using L = Gdn2HLayout<D, GATE>;
+    using OpT = _Float16;
+    constexpr int NW = NT2 / WAVE, P = L::P, RPP = L::RPP, NCT = L::NCT;
+    constexpr int LKR = L::LKR, LEH = L::LEH, LT32 = L::LT32, LT16 = L::LT16;
+    constexpr int LM32 = L::LM32, LM16 = L::LM16, LN = L::LN;
+    constexpr float RHO_MAX = 8.f;  // in-block decay (log2) that fp16 row operands carry
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ float s_tot[P][D];
+    __shared__ __attribute__((aligned(16))) float s_c[7][D];  // block-pair scales
+    __shared__ float s_red[NW][4];
+
+    float* sKR = reinterpret_cast<float*>(smem + L::KR);
+    float* sQR = reinterpret_cast<float*>(smem + L::QR);
+    OpT* sEH = reinterpret_cast<OpT*>(smem + L::EH);
+    OpT* sWH = reinterpret_cast<OpT*>(smem + L::WH);
+    float* sKTT = reinterpret_cast<float*>(smem + L::KTT);
+    OpT* sVT = reinterpret_cast<OpT*>(smem + L::VT);
+    OpT* sWBT = reinterpret_cast<OpT*>(smem + L::WBT);
+    OpT* sWS = reinterpret_cast<OpT*>(smem + L::WBT);
+    OpT* sQTS = reinterpret_cast<OpT*>(smem + L::QTS);
+    float* sME = reinterpret_cast<float*>(smem + L::ME);
+    OpT* sAE = reinterpret_cast<OpT*>(smem + L::AE);
+    OpT* sMW = reinterpret_cast<OpT*>(smem + L::MW);
+    OpT* sAW = reinterpret_cast<OpT*>(smem + L::AW);
+    float* sN = reinterpret_cast<float*>(smem + L::NINV);
+
+    const int64_t ch = blockIdx.x;  // chunk-head: (b * H + h) * NC + c
+    const int64_t bh = ch / NC, c = ch % NC;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh % H);
+    const int64_t t0 = c * CHUNK;
+    const int nvalid = static_cast<int>(T - t0 < CHUNK ? T - t0 : CHUNK);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4, kg = 8 * g4;
+    const int cc = tid % D, part = tid / D, r0 = part * RPP, R0 = r0 / 16;
+    const bf16_t* q = reinterpret_cast<const bf16_t*>(q_);
+    const bf16_t* k = reinterpret_cast<const bf16_t*>(k_);
+    const bf16_t* v = reinterpret_cast<const bf16_t*>(v_);
+    const int64_t tokstride = static_cast<int64_t>(H) * D;
+    const int64_t base = ((b * T + t0) * H + h) * D;  // element (row 0, channel 0) of this chunk
+    // rows past the sequence read the last valid row (in bounds) and are zeroed
+    auto rowoff = [&](int r) -> int64_t { return base + (r < nvalid ? r : nvalid - 1) * tokstride; };
+
+    // ---- loads: every input of this thread's rows, issued back to back
+    float kk[RPP], qq[RPP], vv[RPP], ee[RPP], ww[RPP], G[RPP];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const int64_t e = rowoff(r0 + j) + cc;
+        kk[j] = to_f32(k[e]);
+        qq[j] = to_f32(q[e]);
+        vv[j] = to_f32(v[e]);
+        ee[j] = erase[e];
+        ww[j] = write[e];
+        if constexpr (GATE == GATE_CHANNEL) G[j] = alpha[e];
+        else if constexpr (GATE == GATE_SCALAR) G[j] = alpha[e / D];
+        else G[j] = 1.f;
+    }
+    // G: inclusive cumulative log2 decay inside the chunk; rows past the
+    // sequence decay by nothing
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+        const bool ok = r0 + j < nvalid;
+        kk[j] = ok ? kk[j] : 0.f;
+        qq[j] = ok ? qq[j] : 0.f;
+        vv[j] = ok ? vv[j] : 0.f;
+        ee[j] = ok ? ee[j] : 0.f;
+        ww[j] = ok ? ww[j] : 0.f;
+        G[j] = (GATE != GATE_NONE && ok) ? log2_fast(G[j]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
+    s_tot[part][cc] = G[RPP - 1];
+    __syncthreads();
+    // bend[R] = G at the last row of block R (this thread's channel)
+    float carry = 0.f, bend[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const float t = s_tot[p][cc];
+        carry += p < part ? t : 0.f;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) bend[R] += (p * RPP < 16 * (R + 1)) ? t : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) G[j] += carry;
+    const float refm = R0 > 0 ? bend[R0 - 1] : 0.f, refp = bend[R0], glast = bend[3];
+
+    // ---- element-wise operands
+    float kt[RPP], qt[RPP], wb[RPP];
+    {
+        const float eref = exp2_fast(refm), efl = exp2_fast(glast - refp);
+        float eb[RPP];
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+            const int r = r0 + j;
+            const float a = exp2_fast(G[j] - refm), bj = exp2_fast(refp - G[j]);
+            sKR[r * LKR + cc] = kk[j] * a;
+            sQR[r * LKR + cc] = qq[j] * a;
+            const float ek = ee[j] * kk[j], wk = ww[j] * kk[j];
+            sEH[r * LEH + cc] = from_f32<OpT>(ek * bj);
+            sWH[r * LEH + cc] = from_f32<OpT>(wk * bj);
+            const float E = a * eref, fl = bj * efl;  // 2^G, 2^(G_last - G)
+            kt[j] = kk[j] * E;
+            qt[j] = qq[j] * E;
+            eb[j] = ek * fl;
+            wb[j] = wk * fl;
+        }
+        // Kb^T = Eb^T (A operand of Kb^T U: rows channel, k = position), runs of 8
+        OpT* KbT = static_cast<OpT*>(ws.KbT) + ch * D * CHUNK;
+#pragma unroll
+        for (int j = 0; j < RPP; j += 8) store_run<OpT, 8>(KbT + frag_off<CHUNK>(cc, r0 + j), eb + j);
+        if (part == 0) {
+            ws.gam[ch * D + cc] = exp2_fast(glast);
+            // block-pair scales: (2,0), (3,0), (3,1) below the diagonal, then the
+            // four diagonal blocks
+            s_c[0][cc] = exp2_fast(bend[1] - bend[0]);
+            s_c[1][cc] = exp2_fast(bend[2] - bend[0]);
+            s_c[2][cc] = exp2_fast(bend[2] - bend[1]);
+            s_c[3][cc] = exp2_fast(-bend[0]);
+            s_c[4][cc] = exp2_fast(bend[0] - bend[1]);
+            s_c[5][cc] = exp2_fast(bend[1] - bend[2]);
+            s_c[6][cc] = exp2_fast(bend[2] - bend[3]);
+        }
+        // widest in-block decay of the wave's channels, per block
+        float rho[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) rho[R] = wave_max((R > 0 ? bend[R - 1] : 0.f) - bend[R]);
+        if (lane == 0) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) s_red[wid][R] = rho[R];
+        }
+    }
+    __syncthreads();
+    int flags = 0;  // bit R: diagonal block R is computed exactly
+    if constexpr (GATE != GATE_NONE) {
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            float rho = s_red[0][R];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) rho = fmaxf(rho, s_red[w][R]);
+            if (!(rho <= RHO_MAX)) flags |= 1 << R;  // NaN-safe
+        }
+    }
+
+    // ---- the four C x C matrices by 16 x 16 block pairs (R, J), J <= R.
+    // Pairs 0-3 are the diagonal, 4-6 need a scale below the diagonal, 7-9 not.
+    {
+#pragma unroll 1
+        for (int pi = wid; pi < 10; pi += NW) {
+            // (R, J, scale row): 0-3 (p, p, 3 + p); 4-6 (2, 0, 0), (3, 0, 1),
+            // (3, 1, 2); 7-9 (p - 6, p - 7, none)
+            const int R = pi < 4 ? pi : pi < 7 ? (pi == 4 ? 2 : 3) : pi - 6;
+            const int J = pi < 4 ? pi : pi < 7 ? (pi == 6 ? 1 : 0) : pi - 7;
+            const int si = pi < 4 ? 3 + pi : pi < 7 ? pi - 4 : -1;
+            if (R == J && ((flags >> R) & 1)) continue;  // exact path below
+            float4v aMe = zero4(), aMw = zero4(), aAe = zero4(), aAw = zero4();
+            const int rr = 16 * R + l16, jj = 16 * J + l16;
+#pragma unroll
+            for (int kq = 0; kq < D / 32; ++kq) {
+                const int c0 = 32 * kq + kg;
+                const float4v k0 = *reinterpret_cast<const float4v*>(sKR + rr * LKR + c0);
+                const float4v k1 = *reinterpret_cast<const float4v*>(sKR + rr * LKR + c0 + 4);
+                const float4v q0 = *reinterpret_cast<const float4v*>(sQR + rr * LKR + c0);
+                const float4v q1 = *reinterpret_cast<const float4v*>(sQR + rr * LKR + c0 + 4);
+                float xk[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+                float xq[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+                if (si >= 0) {
+                    const float4v s0 = *reinterpret_cast<const float4v*>(&s_c[si][c0]);
+                    const float4v s1 = *reinterpret_cast<const float4v*>(&s_c[si][c0 + 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xk[e] *= s0[e];
+                        xq[e] *= s0[e];
+                        xk[4 + e] *= s1[e];
+                        xq[4 + e] *= s1[e];
+                    }
+                }
+                Frag<OpT> Ak, Aq, Be, Bw;
+                set_frag(Ak, xk);
+                set_frag(Aq, xq);
+                Be.load(sEH + jj * LEH + c0);
+                Bw.load(sWH + jj * LEH + c0);
+                mma(Ak, Be, aMe);
+                mma(Ak, Bw, aMw);
+                mma(Aq, Be, aAe);
+                mma(Aq, Bw, aAw);
+            }
+            // lane: column 16J + l16, rows 16R + 4 g4 + e; a block below the
+            // diagonal also clears its mirror above it
+            const int j = 16 * J + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * g4 + e;
+                const bool keepM = J < R || j < r, keepA = J < R || j <= r;
+                sME[r * LM32 + j] = keepM ? aMe[e] : 0.f;
+                sMW[r * LM16 + j] = from_f32<OpT>(keepM ? aMw[e] : 0.f);
+                sAE[r * LM16 + j] = from_f32<OpT>(keepA ? aAe[e] : 0.f);
+                sAW[r * LM16 + j] = from_f32<OpT>(keepA ? aAw[e] : 0.f);
+                if (J < R) {
+                    const int ru = 16 * J + 4 * g4 + e, ju = 16 * R + l16;
+                    sME[ru * LM32 + ju] = 0.f;
+                    sMW[ru * LM16 + ju] = from_f32<OpT>(0.f);
+                    sAE[ru * LM16 + ju] = from_f32<OpT>(0.f);
+                    sAW[ru * LM16 + ju] = from_f32<OpT>(0.f);
+                }
+            }
+        }
+    }
+    // diagonal blocks with a decay range beyond fp16 operands:
+    // 2^(G_r - G_i) = prod_{s=i+1..r} alpha_s, accumulated as a running product
+    if constexpr (GATE != GATE_NONE) {
+        if (flags && tid < 256) {
+            constexpr int CPG = D / 16;  // channels per lane
+            const int rr = tid >> 4, cg = tid & 15;
+#pragma unroll 1
+            for (int R = 0; R < 4; ++R) {
+                if (!((flags >> R) & 1)) continue;
+                const int r = 16 * R + rr;
+                const bool okr = r < nvalid;
+                float kr[CPG], qr[CPG], f[CPG];
+#pragma unroll
+                for (int m = 0; m < CPG; ++m) {
+                    const int64_t e = base + (okr ? r : 0) * tokstride + cg * CPG + m;
+                    kr[m] = okr ? to_f32(k[e]) : 0.f;
+                    qr[m] = okr ? to_f32(q[e]) : 0.f;
+                    f[m] = 1.f;
+                }
+#pragma unroll 1
+                for (int i = 15; i >= 0; --i) {
+                    const int ii = 16 * R + i;
+                    float me = 0.f, mw = 0.f, ae = 0.f, aw = 0.f;
+                    if (ii <= r) {
+                        if (ii < r) {  // include alpha_{ii+1}
+                            const int s = ii + 1;
+                            const bool oks = s < nvalid;
+#pragma unroll
+                            for (int m = 0; m < CPG; ++m) {
+                                const int64_t e = base + (oks ? s : 0) * tokstride + cg * CPG + m;
+                                const float a = GATE == GATE_CHANNEL ? alpha[e] : alpha[e / D];
+                                f[m] *= oks ? a : 1.f;
+                            }
+                        }
+                        const bool oki = ii < nvalid;
+#pragma unroll
+                        for (int m = 0; m < CPG; ++m) {
+                            const int64_t e = base + (oki ? ii : 0) * tokstride + cg * CPG + m;
+                            const float ki = oki ? to_f32(k[e]) : 0.f;
+                            const float ek = erase[e] * ki * f[m], wk = write[e] * ki * f[m];
+                            me += kr[m] * ek;
+                            mw += kr[m] * wk;
+                            ae += qr[m] * ek;
+                            aw += qr[m] * wk;
+                        }
+                    }
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) {
+                        me += __shfl_xor(me, off);
+                        mw += __shfl_xor(mw, off);
+                        ae += __shfl_xor(ae, off);
+                        aw += __shfl_xor(aw, off);
+                    }
+                    if (cg == 0) {
+                        sME[r * LM32 + ii] = ii < r ? me : 0.f;
+                        sMW[r * LM16 + ii] = from_f32<OpT>(ii < r ? mw : 0.f);
+                        sAE[r * LM16 + ii] = from_f32<OpT>(ii <= r ? ae : 0.f);
+                        sAW[r * LM16 + ii] = from_f32<OpT>(ii <= r ? aw : 0.f);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // the matrices are complete; region A is free
+
+    // ---- operands of the products below: Kt^T, V^T, Wb^T ([D][64]), Qt
+#pragma unroll
+    for (int j = 0; j < RPP; j += 4) {
+        float4v x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = kt[j + e];
+        *reinterpret_cast<float4v*>(sKTT + cc * LT32 + r0 + j) = x;
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; j += 8) {
+        store_run<OpT, 8>(sVT + cc * LT16 + r0 + j, vv + j);
+        store_run<OpT, 8>(sWBT + cc * LT16 + r0 + j, wb + j);
+    }
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) sQTS[frag_off<D>(r0 + j, cc)] = from_f32<OpT>(qt[j]);
+    __syncthreads();
+
+    // ---- X = Wb^T V [D][D] (accumulator order): wave's column tile nt, TX row tiles
+    {
+        constexpr int TX = NCT * NCT / NW;
+        const int nt = wid % NCT, mt0 = (wid / NCT) * TX;
+        Frag<OpT> fv[2];
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) fv[kq].load(sVT + (16 * nt + l16) * LT16 + 32 * kq + kg);
+        float* X = ws.X + ch * D * D;
+#pragma unroll
+        for (int i = 0; i < TX; ++i) {
+            const int mt = mt0 + i;
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                Frag<OpT> fw;
+                fw.load(sWBT + (16 * mt + l16) * LT16 + 32 * kq + kg);
+                mma(fw, fv[kq], acc);
+            }
+            *reinterpret_cast<float4v*>(X + ((mt * NCT + nt) * WAVE + lane) * 4) = acc;
+        }
+    }
+    // A = A_e and Qt, fragment order, 16-byte pieces
+    {
+        OpT* A = static_cast<OpT*>(ws.A) + ch * CHUNK * CHUNK;
+        const int r = tid / (CHUNK / 8), j0 = 8 * (tid % (CHUNK / 8));
+        *reinterpret_cast<half8*>(A + frag_off<CHUNK>(r, j0)) = *reinterpret_cast<const half8*>(sAE + r * LM16 + j0);
+        OpT* Qt = static_cast<OpT*>(ws.Qt) + ch * CHUNK * D;
+#pragma unroll
+        for (int i = tid; i < CHUNK * D / 8; i += NT2)
+            *reinterpret_cast<half8*>(Qt + 8 * i) = *reinterpret_cast<const half8*>(sQTS + 8 * i);
+    }
+    // diagonal inverses N_RR = (I + M_e[R,R])^-1: wave R, lane j solves column j
+    if (wid < 4 && lane < 16) {
+        const int R = wid;
+        const float* Mb = sME + (16 * R) * LM32 + 16 * R;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = r == lane ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float m[16];
+#pragma unroll
+            for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
+                const float4v t = *reinterpret_cast<const float4v*>(Mb + r * LM32 + 4 * j4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[4 * j4 + e] = t[e];
+            }
+            float acc = x[r];
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= m[j] * x[j];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sN[(R * 16 + r) * LN + lane] = x[r];
+    }
+    __syncthreads();  // N_RR ready; Wb^T is dead (its space stages W)
+
+    // ---- solve, M_w V and Y = A_w V, by 16-column tiles: tile t < NCT is
+    // column tile t of Kt (giving W), t >= NCT column tile t - NCT of V
+    // (giving Vt = N M_w V, stored as Ut = -Vt, and Y)
+    {
+        constexpr int TS = 2 * NCT / NW;  // tiles per wave
+        float4v Z[TS][4];
+#pragma unroll
+        for (int s = 0; s < TS; ++s) {
+            const int t = wid + NW * s;
+            if (t < NCT) {
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+                    Z[s][R] = *reinterpret_cast<const float4v*>(sKTT + (16 * t + l16) * LT32 + 16 * R + 4 * g4);
+            } else {
+                const int u = t - NCT;
+                Frag<OpT> fv[2];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) fv[kq].load(sVT + (16 * u + l16) * LT16 + 32 * kq + kg);
+                float* Y = ws.Y + ch * CHUNK * D;
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+                    float4v am = zero4(), ay = zero4();
+#pragma unroll
+                    for (int kq = 0; kq < 2; ++kq) {
+                        Frag<OpT> fm, fa;
+                        fm.load(sMW + (16 * R + l16) * LM16 + 32 * kq + kg);
+                        fa.load(sAW + (16 * R + l16) * LM16 + 32 * kq + kg);
+                        mma(fm, fv[kq], am);
+                        mma(fa, fv[kq], ay);
+                    }
+                    Z[s][R] = am;
+                    *reinterpret_cast<float4v*>(Y + ((R * NCT + u) * WAVE + lane) * 4) = ay;
+                }
+            }
+        }
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+#pragma unroll
+            for (int K = 0; K < R; ++K) {
+                float4v m = *reinterpret_cast<const float4v*>(sME + (16 * R + l16) * LM32 + 16 * K + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int s = 0; s < TS; ++s)
+                        Z[s][R] = __builtin_amdgcn_mfma_f32_16x16x4f32(-m[i], Z[s][K][i], Z[s][R], 0, 0, 0);
+                }
+            }
+            const float4v n = *reinterpret_cast<const float4v*>(sN + (R * 16 + l16) * LN + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < TS; ++s) {
+                float4v z = zero4();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z = __builtin_amdgcn_mfma_f32_16x16x4f32(n[i], Z[s][R][i], z, 0, 0, 0);
+                Z[s][R] = z;
+            }
+        }
+        OpT* Ut = static_cast<OpT*>(ws.Ut) + ch * CHUNK * D;
+#pragma unroll
+        for (int s = 0; s < TS; ++s) {
+            const int t = wid + NW * s;
+            if (t < NCT) {
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sWS[frag_off<D>(16 * R + 4 * g4 + e, 16 * t + l16)] = from_f32<OpT>(Z[s][R][e]);
+                }
+            } else {
+                const int u = t - NCT;
+#pragma unroll
+                for (int R = 0; R < 4; ++R) store4<OpT>(Ut + cfrag_off<D>(16 * R + 4 * g4, 16 * u + l16), -Z[s][R]);
+            }
+        }
+    }
+    __syncthreads();
+    // W in fragment order, 16-byte pieces
+    {
+        OpT* W = static_cast<OpT*>(ws.W) + ch * CHUNK * D;
+#pragma unroll
+        for (int i = tid; i < CHUNK * D / 8; i += NT2)
+            *reinterpret_cast<half8*>(W + 8 * i) = *reinterpret_cast<const half8*>(sWS + 8 * i);
+    }
+}
+
 // One Gated DeltaNet-2 step per (sequence, head) slab, the state read once and
 // written once (the structure of the KDA decode step):
 //     p = S^T (alpha*k), r = S^T (alpha*q),
@@ -593,8 +1096,12 @@ hipError_t intra_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const
                    hipStream_t stream) {
     const int64_t nch = B * H * NC;
     if (nch == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdn2_intra_kernel<D, GATE, IN_F32>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q,
-                       k, v, erase, write, alpha, ws);
+    if constexpr (IN_F32)
+        hipLaunchKernelGGL((gdn2_intra_kernel<D, GATE, true>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q,
+                           k, v, erase, write, alpha, ws);
+    else
+        hipLaunchKernelGGL((gdn2_intra_h_kernel<D, GATE>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q, k,
+                           v, erase, write, alpha, ws);
     return hipGetLastError();
 }
 

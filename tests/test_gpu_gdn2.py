@@ -4,7 +4,8 @@ DeltaNet-2 paragraph; the reading implemented is
 S_t = (I - (e_t*k_t) k_t^T) Diag(alpha_t) S_{t-1} + (w_t*k_t) v_t^T).
 
 Chunked forward and decode step, every gate kind, d = 64 and 128, bf16 inputs
-(fp32 outputs, bar 2e-3) and fp32 inputs (bar 1e-5), ragged and empty
+(fp32 outputs, bar 2e-3) and fp32 inputs (bar 1e-5; the two input types run
+different intra-chunk kernels), ragged and empty
 sequences, strong gates (the exact diagonal-block path), the equal-gate
 reduction to the KDA path, T decode steps against the chunked forward, and a
 16-head 16K-token run checked on sampled heads."""
@@ -64,9 +65,10 @@ def test_gdn2_forward_bf16(gate, d):
 
 
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
-def test_gdn2_forward_fp32(gate):
-    announce("gdn2 forward fp32 gate=%s" % gate)
-    inp = make(1, 150, 2, 64, gate, "fp32", 1010)
+@pytest.mark.parametrize("d", [64, 128])
+def test_gdn2_forward_fp32(gate, d):
+    announce("gdn2 forward fp32 gate=%s d=%d" % (gate, d))
+    inp = make(1, 150, 2, d, gate, "fp32", 1010)
     o, ST = run(inp, "fp32")
     o_ref, S_ref = ref(inp)
     errs = {"o": rel(o, o_ref), "S_T": rel(ST, S_ref)}
