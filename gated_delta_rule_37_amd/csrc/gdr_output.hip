@@ -9,10 +9,12 @@
 //
 // The saved S and U are in the fragment order the gradient kernels read (rows
 // d resp. position, k = value column).  Here the contraction runs over d resp.
-// position, so both are transposed through LDS once; Qt and A are copied to LDS
-// as they are.  Wave w owns the value columns 32w..32w+31 of all 64 rows.  The
-// products accumulate in the same order as a fused state pass would (Qt S over
-// d, then A U), in fp32.
+// position: both are laid out row-major in LDS (one 16-byte store per saved
+// piece) and read back as B fragments with the transposed LDS read, so no
+// element is moved on its own; Qt and A are copied to LDS as they are.  Wave w
+// owns the value columns 32w..32w+31 of all 64 rows.  The products accumulate
+// in the same order as a fused state pass would (Qt S over d, then A U), in
+// fp32.
 //
 // With the error-routing epilogue (CLER), every thread also adds lam * u / beta
 // to the hidden-stream piece of the U piece it has just read (the write errors,
@@ -25,14 +27,35 @@ namespace gdr {
 
 template <int D>
 struct OutLayout {
-    static constexpr int LDT = D + 8;       // row stride of S^T [D][D]  (fp16)
-    static constexpr int LDU = CHUNK + 8;   // row stride of U^T [D][64] (fp16)
+    static constexpr int LDR = D + 8;       // row stride of S [D][D] and U [64][D] (fp16)
     static constexpr int ST = 0;
-    static constexpr int UT = ST + D * LDT * 2;
-    static constexpr int QT = UT + D * LDU * 2;  // Qt, fragment order copy
-    static constexpr int A = QT + CHUNK * D * 2;  // A, fragment order copy
+    static constexpr int UT = ST + D * LDR * 2;
+    static constexpr int QT = UT + CHUNK * LDR * 2;  // Qt, fragment order copy
+    static constexpr int A = QT + CHUNK * D * 2;     // A, fragment order copy
     static constexpr int BYTES = A + CHUNK * CHUNK * 2;
 };
+
+// B fragment (k = row, n = column) of a row-major fp16 tile in LDS: lane l gets
+// rows k0 + 8(l/16) .. +7 of column n0 + l%16.  The transposed read hands lane
+// 4a+i of each 16-lane group element i of the 8-byte pieces that lanes a, a+4,
+// a+8 and a+12 of the group address; so lane c of group g addresses row
+// k0 + 8g + c/4 (+4 for the second read), columns n0 + 4(c%4) .. +3.
+template <int LD>
+__device__ __forceinline__ Frag<_Float16> frag_tr(const _Float16* t, int k0, int n0, int lane) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const int g = lane >> 4, c = lane & 15;
+    const _Float16* p = t + (k0 + 8 * g + (c >> 2)) * LD + n0 + 4 * (c & 3);
+    const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
+    const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * LD)));
+    Frag<_Float16> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.v[e] = lo[e];
+        f.v[4 + e] = hi[e];
+    }
+    return f;
+}
 
 template <int D, bool OUT_F32, bool CLER>
 __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
@@ -41,12 +64,12 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
                                                      ChunkRange cr) {
     using L = OutLayout<D>;
     using OutT = typename InType<OUT_F32>::T;
-    constexpr int LDT = L::LDT, LDU = L::LDU;
+    constexpr int LDR = L::LDR;
     constexpr int CPW = D / 4 / 16;  // column tiles per wave
 
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
-    _Float16* sT = reinterpret_cast<_Float16*>(smem + L::ST);
-    _Float16* uT = reinterpret_cast<_Float16*>(smem + L::UT);
+    _Float16* sS = reinterpret_cast<_Float16*>(smem + L::ST);
+    _Float16* sU = reinterpret_cast<_Float16*>(smem + L::UT);
 
     int64_t bh, c;
     range_block(cr, bh, c);
@@ -69,7 +92,7 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
             else copy16_to_lds(Ag + (i - NQ) * 1024 + lane * 16, sm + L::A + (i - NQ) * 1024);
         }
     }
-    // S and U transposed: piece p of a fragment-ordered [M][D] array is lane
+    // S and U row-major: piece p of a fragment-ordered [M][D] array is lane
     // (p % 64) of fragment p / 64 = (row tile, 32-column step), eight
     // consecutive columns of one row
     {
@@ -79,17 +102,14 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
         for (int i = 0; i < D * D / 8 / 256; ++i) {
             const int p = i * 256 + tid, f = p >> 6, l = p & 63;
             const int d = 16 * (f / (D / 32)) + (l & 15), j = 32 * (f % (D / 32)) + 8 * (l >> 4);
-            const half8 v = *reinterpret_cast<const half8*>(Sg + p * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sT[(j + e) * LDT + d] = v[e];
+            *reinterpret_cast<half8*>(sS + d * LDR + j) = *reinterpret_cast<const half8*>(Sg + p * 8);
         }
 #pragma unroll
         for (int i = 0; i < CHUNK * D / 8 / 256; ++i) {
             const int p = i * 256 + tid, f = p >> 6, l = p & 63;
             const int pos = 16 * (f / (D / 32)) + (l & 15), j = 32 * (f % (D / 32)) + 8 * (l >> 4);
             const half8 v = *reinterpret_cast<const half8*>(Ug + p * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) uT[(j + e) * LDU + pos] = v[e];
+            *reinterpret_cast<half8*>(sU + pos * LDR + j) = v;
             if constexpr (CLER) {
                 if (pos < nvalid) {
                     const int64_t t = c * CHUNK + pos;
@@ -122,24 +142,20 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
             float4v acc = zero4();
 #pragma unroll
             for (int kq = 0; kq < D / 32; ++kq) {
-                Frag<_Float16> fs;
-                fs.v = *reinterpret_cast<const half8*>(sT + (16 * ct + l16) * LDT + 32 * kq + 8 * g4);
-                mma(fq[kq], fs, acc);
+                mma(fq[kq], frag_tr<LDR>(sS, 32 * kq, 16 * ct, lane), acc);
             }
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
-                Frag<_Float16> fu;
-                fu.v = *reinterpret_cast<const half8*>(uT + (16 * ct + l16) * LDU + 32 * kq + 8 * g4);
-                mma(fa[kq], fu, acc);  // the upper blocks of A are zero
+                mma(fa[kq], frag_tr<LDR>(sU, 32 * kq, 16 * ct, lane), acc);  // the upper blocks of A are zero
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) res[rt][ci][e] = scale * acc[e];
         }
     }
-    // assemble the output rows in LDS (over S^T, no longer read) and write them
+    // assemble the output rows in LDS (over S, no longer read) and write them
     // with 16-byte stores; rows past the end are not written
     __syncthreads();
-    static_assert(CHUNK * D * sizeof(OutT) <= L::QT, "output rows must fit over S^T and U^T");
+    static_assert(CHUNK * D * sizeof(OutT) <= L::QT, "output rows must fit over S and U");
     OutT* so = reinterpret_cast<OutT*>(smem + L::ST);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
