@@ -146,13 +146,13 @@ __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t
     const int l16 = lane & 15, g4 = lane >> 4, tid = wid * WAVE + lane;
     const int64_t ch = bh * NC + c;
 
-    // chunk-end gradient dS' of this chunk, fragment order (rows d, k = column)
+    // chunk-end gradient dS' of this chunk, fragment order (rows d, k = column):
+    // each 16-lane group 16 rows and 8 of the columns
     if (tid < 2 * D) {
-        const int d = tid >> 1, hf = tid & 1;
+        const int grp = tid >> 4, d0 = 16 * (grp % (D / 16)), hf = grp / (D / 16);
         OpT vals[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = s_dS[(8 * hf + e) * LDS_S + d];
-        st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf), vals);
+        lds_column8<LDS_S>(s_dS, 8 * hf, d0, lane, vals);
+        st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d0 + l16, j0 + 8 * hf), vals);
     }
     // scaled dO slice, transposed into LDS (rows past the end are zero)
     {
@@ -198,11 +198,10 @@ __device__ __forceinline__ void bwd_step(const BwdFrags<D, IN_F32>& cur, int64_t
     // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
     const OpT* s_sv = CLER ? s_dUE : s_dU;
     if (tid < 2 * CHUNK) {
-        const int pos = tid >> 1, hf = tid & 1;
+        const int grp = tid >> 4, pos0 = 16 * (grp & 3), hf = grp >> 2;
         OpT vals[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = s_sv[(8 * hf + e) * LDS_U + pos];
-        st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
+        lds_column8<LDS_U>(s_sv, 8 * hf, pos0, lane, vals);
+        st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos0 + l16, j0 + 8 * hf), vals);
     } else if (tid < 2 * CHUNK + 128) {
         const int t2 = tid - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;  // column j, positions 8pg..8pg+7
         OpT vals[8];
@@ -595,11 +594,11 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
             const OpT* s_sv = CLER ? sdUE : sdU;
             const int t = stid;
             if (t < 2 * CHUNK) {
-                const int pos = t >> 1, hf = t & 1;
+                // each 16-lane group 16 positions and 8 of the columns
+                const int grp = t >> 4, pos0 = 16 * (grp & 3), hf = grp >> 2;
                 OpT vals[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = s_sv[(8 * hf + e) * LDS_U + pos];
-                st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf), vals);
+                lds_column8<LDS_U>(s_sv, 8 * hf, pos0, lane, vals);
+                st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos0 + l16, j0 + 8 * hf), vals);
             } else if (t < 2 * CHUNK + 128) {
                 const int t2 = t - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;
                 OpT vals[8];
@@ -611,13 +610,12 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
         // chunk-end gradient dS' (rows d, k = column): each wave saves the rows
         // it owns before it overwrites them below
         {
-            constexpr int RW = D / 4;
-            if (lane < 2 * RW) {
-                const int d = RW * wid + (lane >> 1), hf = lane & 1;
+            constexpr int RW = D / 4, RG = RW / 16;
+            if (g4 < 2 * RG) {  // each 16-lane group 16 rows and 8 of the columns
+                const int d0 = RW * wid + 16 * (g4 % RG), hf = g4 / RG;
                 OpT vals[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = sdS[(8 * hf + e) * LDS_S + d];
-                st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf), vals);
+                lds_column8<LDS_S>(sdS, 8 * hf, d0, lane, vals);
+                st8(reinterpret_cast<OpT*>(ws.dSsnap) + ch * D * D + frag_off<D>(d0 + l16, j0 + 8 * hf), vals);
             }
         }
 

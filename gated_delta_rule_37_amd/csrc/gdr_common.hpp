@@ -165,6 +165,35 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
 }
 
 
+// Column piece of a row-major LDS array (row stride LD elements): out[e] =
+// t[(r0 + e) * LD + c0 + lane % 16], e = 0..7, where the 16 lanes of a group
+// share r0 and c0 (so a group reads 16 consecutive columns) and all 16 take
+// part.  fp16: two gfx950 transposed reads (ds_read_b64_tr_b16), which hand
+// lane 4a+i of a 16-lane group element i of the 8-byte pieces that lanes a,
+// a+4, a+8 and a+12 of the group address; so lane c addresses row r0 + c/4
+// (+4 in the second read), columns c0 + 4(c%4) .. +3 (8-byte aligned when LD
+// and c0 are multiples of 4).  fp32: eight plain reads.
+template <int LD, typename OpT>
+__device__ __forceinline__ void lds_column8(const OpT* t, int r0, int c0, int lane, OpT (&out)[8]) {
+    if constexpr (sizeof(OpT) == 2) {
+        static_assert(LD % 4 == 0, "8-byte aligned pieces");
+        typedef short short4v __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) short4v lds_short4;
+        const int c = lane & 15;
+        const OpT* p = t + (r0 + (c >> 2)) * LD + c0 + 4 * (c & 3);
+        const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
+        const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * LD)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[e] = lo[e];
+            out[4 + e] = hi[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = t[(r0 + e) * LD + c0 + (lane & 15)];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // direct global -> LDS copies (global_load_lds) and explicit vmcnt waits
 // ---------------------------------------------------------------------------

@@ -36,24 +36,14 @@ struct OutLayout {
 };
 
 // B fragment (k = row, n = column) of a row-major fp16 tile in LDS: lane l gets
-// rows k0 + 8(l/16) .. +7 of column n0 + l%16.  The transposed read hands lane
-// 4a+i of each 16-lane group element i of the 8-byte pieces that lanes a, a+4,
-// a+8 and a+12 of the group address; so lane c of group g addresses row
-// k0 + 8g + c/4 (+4 for the second read), columns n0 + 4(c%4) .. +3.
+// rows k0 + 8(l/16) .. +7 of column n0 + l%16.
 template <int LD>
 __device__ __forceinline__ Frag<_Float16> frag_tr(const _Float16* t, int k0, int n0, int lane) {
-    typedef short short4v __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) short4v lds_short4;
-    const int g = lane >> 4, c = lane & 15;
-    const _Float16* p = t + (k0 + 8 * g + (c >> 2)) * LD + n0 + 4 * (c & 3);
-    const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
-    const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * LD)));
+    _Float16 x[8];
+    lds_column8<LD>(t, k0 + 8 * (lane >> 4), n0, lane, x);
     Frag<_Float16> f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f.v[e] = lo[e];
-        f.v[4 + e] = hi[e];
-    }
+    for (int e = 0; e < 8; ++e) f.v[e] = x[e];
     return f;
 }
 

@@ -156,15 +156,13 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32, XY>& cur,
     st4<OpT>(s_U + l16 * LDS_U + 16 * wid + 4 * g4, u);
     __syncthreads();
     if constexpr (SAVE) {
-        // U of this chunk, fragment order (rows position, k = value column)
-        const int t = wid * WAVE + (l16 + 16 * g4);
-        if (t < 2 * CHUNK) {
-            const int pos = t >> 1, hf = t & 1;
-            OpT* us = reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + frag_off<D>(pos, j0 + 8 * hf);
+        // U of this chunk, fragment order (rows position, k = value column):
+        // waves 0 and 1, each 16-lane group 16 positions and 8 of the columns
+        if (wid < 2) {
+            const int grp = 4 * wid + g4, pos0 = 16 * (grp & 3), hf = grp >> 2;
             OpT vals[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = s_U[(8 * hf + e) * LDS_U + pos];
-            store8(us, vals);
+            lds_column8<LDS_U>(s_U, 8 * hf, pos0, l16, vals);
+            store8(reinterpret_cast<OpT*>(ws.Usave) + ch * CHUNK * D + frag_off<D>(pos0 + l16, j0 + 8 * hf), vals);
         }
     }
 
@@ -194,18 +192,16 @@ __device__ __forceinline__ void state_step(const ChunkFrags<D, IN_F32, XY>& cur,
 
     if constexpr (SAVE) {
         // chunk-start state snapshot [D][D] in operand precision, fragment order
-        // (rows d, k = value column): eight consecutive columns per lane,
-        // gathered from the transposed LDS copy.  Each wave saves the rows it
-        // owns, which no other wave writes, before it overwrites them below.
-        constexpr int RW = D / 4;
-        const int lane = 16 * g4 + l16;
-        if (lane < 2 * RW) {
-            const int d = RW * wid + (lane >> 1), hf = lane & 1;
-            OpT* snap = reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D + frag_off<D>(d, j0 + 8 * hf);
+        // (rows d, k = value column): eight consecutive columns per lane, read
+        // as columns of the transposed LDS copy.  Each wave saves the rows it
+        // owns (each 16-lane group 16 rows and 8 of the columns), which no
+        // other wave writes, before it overwrites them below.
+        constexpr int RW = D / 4, RG = RW / 16;
+        if (g4 < 2 * RG) {
+            const int d0 = RW * wid + 16 * (g4 % RG), hf = g4 / RG;
             OpT vals[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = s_S[(8 * hf + e) * LDS_S + d];
-            store8(snap, vals);
+            lds_column8<LDS_S>(s_S, 8 * hf, d0, l16, vals);
+            store8(reinterpret_cast<OpT*>(ws.Ssnap) + ch * D * D + frag_off<D>(d0 + l16, j0 + 8 * hf), vals);
         }
     }
 
