@@ -311,7 +311,9 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
         w.Pw = static_cast<float*>(take(sq32));
         w.dSsnap = take(st);
         w.dUsave = take(mat);
-        w.dUsaveT = take(mat);
+        // fp16 operands: the gradient kernel reads dU's transpose from its LDS
+        // copy of dU; fp32 operands keep the transposed copy
+        if (op_bytes == 4) w.dUsaveT = take(mat);
         // the gradient partials the stages do not hand on chip
         const bool all = cler || grad_split(D, op_bytes == 4);
         if (all || !grad_qkb_on_chip(D)) {

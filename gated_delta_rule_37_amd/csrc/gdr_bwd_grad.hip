@@ -487,22 +487,40 @@ __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, floa
 
     // ---------------- phase 2: dT += dW Kt^T, dKt = T^T dW, dV = T^T dU ----------------
     {
-        const OpT* dUT = reinterpret_cast<const OpT*>(ws.dUsaveT) + ch * D * CHUNK;
         OutT* dv = reinterpret_cast<OutT*>(dv_);
         const InT* dh = reinterpret_cast<const InT*>(dh_);
         const int r_ = 16 * rt + 4 * g4;
         Frag<OpT> aT[2];
         aT[0].load(TT + (16 * rt + l16) * LDC + 8 * g4);
         aT[1].load(TT + (16 * rt + l16) * LDC + 32 + 8 * g4);
-        // global loads first (dU^T fragments, the CLVR terms), stores last
+        // global loads first (the CLVR terms, fp32: dU^T fragments), stores last.
+        // fp16: dU^T's fragments (k = position, n = value column) are column
+        // pieces of dU's fragment-order LDS copy, read with transposed reads
         constexpr int NIT = D / 16 / NHALF;
         Frag<OpT> bU[NIT][2];
         float dhv[NIT][4], lmv[NIT];
+        if constexpr (sizeof(OpT) == 2 && !NORO) {
+            const OpT* sDU = reinterpret_cast<const OpT*>(smem + L::RDU);
 #pragma unroll
-        for (int ct = half; ct < D / 16; ct += NHALF) {
-            const int ii = (ct - half) / NHALF;
+            for (int ct = half; ct < D / 16; ct += NHALF) {
+                const int ii = (ct - half) / NHALF;
 #pragma unroll
-            for (int kq = 0; kq < 2; ++kq) bU[ii][kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
+                for (int kq = 0; kq < 2; ++kq) {
+                    OpT x[8];
+                    lds_column8_at(sDU, 32 * kq + 8 * g4, 16 * ct, lane, [](int r, int c) { return frag_off<D>(r, c); },
+                                   x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bU[ii][kq].v[e] = x[e];
+                }
+            }
+        } else {
+            const OpT* dUT = reinterpret_cast<const OpT*>(ws.dUsaveT) + ch * D * CHUNK;
+#pragma unroll
+            for (int ct = half; ct < D / 16; ct += NHALF) {
+                const int ii = (ct - half) / NHALF;
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) bU[ii][kq].load(dUT + ((ct * 2 + kq) * 64 + lane) * 8);
+            }
         }
         if (dh) {  // CLVR: the four dh rows of each tile, all issued before any is used
 #pragma unroll

@@ -589,7 +589,8 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
         st4b<OpT>(sdU + l16 * LDS_U + 16 * wid + 4 * g4, du);
         __syncthreads();
 
-        // dU saves: [64][D] rows position (k = column) and [D][64] rows column (k = position)
+        // dU save: [64][D] rows position (k = column); the gradient kernel reads
+        // its transpose from the same copy
         {
             const OpT* s_sv = CLER ? sdUE : sdU;
             const int t = stid;
@@ -599,12 +600,6 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
                 OpT vals[8];
                 lds_column8<LDS_U>(s_sv, 8 * hf, pos0, lane, vals);
                 st8(reinterpret_cast<OpT*>(ws.dUsave) + ch * CHUNK * D + frag_off<D>(pos0 + l16, j0 + 8 * hf), vals);
-            } else if (t < 2 * CHUNK + 128) {
-                const int t2 = t - 2 * CHUNK, j = t2 >> 3, pg = t2 & 7;
-                OpT vals[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = s_sv[j * LDS_U + 8 * pg + e];
-                st8(reinterpret_cast<OpT*>(ws.dUsaveT) + ch * D * CHUNK + frag_off<CHUNK>(j0 + j, 8 * pg), vals);
             }
         }
         // chunk-end gradient dS' (rows d, k = column): each wave saves the rows

@@ -165,24 +165,25 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
 }
 
 
-// Column piece of a row-major LDS array (row stride LD elements): out[e] =
-// t[(r0 + e) * LD + c0 + lane % 16], e = 0..7, where the 16 lanes of a group
-// share r0 and c0 (so a group reads 16 consecutive columns) and all 16 take
-// part.  fp16: two gfx950 transposed reads (ds_read_b64_tr_b16), which hand
-// lane 4a+i of a 16-lane group element i of the 8-byte pieces that lanes a,
-// a+4, a+8 and a+12 of the group address; so lane c addresses row r0 + c/4
-// (+4 in the second read), columns c0 + 4(c%4) .. +3 (8-byte aligned when LD
-// and c0 are multiples of 4).  fp32: eight plain reads.
-template <int LD, typename OpT>
-__device__ __forceinline__ void lds_column8(const OpT* t, int r0, int c0, int lane, OpT (&out)[8]) {
+// Column piece of an LDS array: out[e] = t[off(r0 + e, c0 + lane % 16)],
+// e = 0..7, where off(r, c) is the element offset of row r, column c, the 16
+// lanes of a group share r0 and c0 (so a group reads 16 consecutive columns)
+// and all 16 take part.  fp16: two gfx950 transposed reads (ds_read_b64_tr_b16),
+// which hand lane 4a+i of a 16-lane group element i of the 8-byte pieces that
+// lanes a, a+4, a+8 and a+12 of the group address; so lane c addresses row
+// r0 + c/4 (+4 in the second read), columns c0 + 4(c%4) .. +3, which must be
+// four consecutive, 8-byte aligned elements (c0 a multiple of 16; true of a
+// row-major array with a row stride that is a multiple of 4, and of the
+// fragment order).  fp32: eight plain reads.
+template <typename OpT, typename Off>
+__device__ __forceinline__ void lds_column8_at(const OpT* t, int r0, int c0, int lane, Off off, OpT (&out)[8]) {
     if constexpr (sizeof(OpT) == 2) {
-        static_assert(LD % 4 == 0, "8-byte aligned pieces");
         typedef short short4v __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) short4v lds_short4;
-        const int c = lane & 15;
-        const OpT* p = t + (r0 + (c >> 2)) * LD + c0 + 4 * (c & 3);
-        const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
-        const half4 hi = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * LD)));
+        const int c = lane & 15, r = r0 + (c >> 2), cc = c0 + 4 * (c & 3);
+        const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r, cc))));
+        const half4 hi =
+            __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r + 4, cc))));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             out[e] = lo[e];
@@ -190,8 +191,15 @@ __device__ __forceinline__ void lds_column8(const OpT* t, int r0, int c0, int la
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = t[(r0 + e) * LD + c0 + (lane & 15)];
+        for (int e = 0; e < 8; ++e) out[e] = t[off(r0 + e, c0 + (lane & 15))];
     }
+}
+
+// The same for a row-major array with row stride LD elements.
+template <int LD, typename OpT>
+__device__ __forceinline__ void lds_column8(const OpT* t, int r0, int c0, int lane, OpT (&out)[8]) {
+    static_assert(LD % 4 == 0, "8-byte aligned pieces");
+    lds_column8_at(t, r0, c0, lane, [](int r, int c) { return r * LD + c; }, out);
 }
 
 // ---------------------------------------------------------------------------

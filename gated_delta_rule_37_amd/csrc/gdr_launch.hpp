@@ -19,7 +19,7 @@ namespace gdr {
 //     Nw, Pw [64][64] fp32: N = (I + L)^-1 and P = Kt Kh^T     gradient kernels
 //     Ssnap [D][D] chunk-start state, Usave [64][D] (op)        state pass (save)
 //     dSsnap [D][D] chunk-end state gradient, dUsave [64][D],
-//     dUsaveT [D][64] (op)                                      reverse pass
+//     dUsaveT [D][64] (op; fp32 operands only)                  reverse pass
 //     gQt, gKt, gKb [64][D], gA, gP [64][64], gGam [D] (fp32)  gradients w.r.t.
 //       Qt, Kt, Kb, A, P and gamma, passed to the gate-gradient kernel
 // A range of chunks [lo, lo + n) of every (batch, head): the per-chunk kernels

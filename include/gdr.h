@@ -292,9 +292,10 @@ gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const v
  *   computes what gdr_forward_chunked computes.
  * desc->route and desc->prologue must be 0 (no hidden-stream epilogue: the
  * article leaves open what routing the written value means here), else
- * GDR_ERR_UNSUPPORTED.  The chunk products run with fp32 operands (fp16 for
- * the three products with v when v is bf16) and the state pass with fp32
- * operands; forward only (no backward in this version).
+ * GDR_ERR_UNSUPPORTED.  For bf16 inputs the chunk products and the state
+ * pass take fp16 operands with fp32 accumulation and an fp32 state (as
+ * gdr_forward_chunked); fp32 inputs run in fp32 throughout.  Forward only (no
+ * backward in this version).
  * ws: at least gdr_gdn2_workspace_size(desc) bytes (240.5 KiB per chunk-head
  * of 64 tokens at dk = dv = 128). */
 size_t gdr_gdn2_workspace_size(const gdr_desc* desc);
