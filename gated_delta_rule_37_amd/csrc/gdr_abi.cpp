@@ -303,10 +303,14 @@ size_t chunk_ws_bytes(int64_t nch, int D, int op_bytes, bool backward, bool cler
     }
     if (backward) {
         const size_t sq32 = size_t(nch) * kChunk * kChunk * 4;
-        w.AT = take(sq);
-        w.Kb = take(mat);
-        w.QtT = take(mat);
-        w.WT = take(mat);
+        // fp32 operands: the transposes the reverse pass reads (with fp16 operands
+        // it reads them from Qt, A, Kb^T and W with transposed LDS reads)
+        if (op_bytes == 4) {
+            w.AT = take(sq);
+            w.Kb = take(mat);
+            w.QtT = take(mat);
+            w.WT = take(mat);
+        }
         w.Nw = static_cast<float*>(take(sq32));
         w.Pw = static_cast<float*>(take(sq32));
         w.dSsnap = take(st);

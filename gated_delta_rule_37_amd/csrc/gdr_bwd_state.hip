@@ -305,14 +305,17 @@ __global__ __launch_bounds__(256) void state_bwd_kernel(int64_t T, int H, int64_
 // barriers (after dU, after dS).
 // ---------------------------------------------------------------------------
 
+// The forward's operands A, Kb^T, Qt and W are staged as stored (fragment
+// order); the step reads the fragments of their transposes A^T, Kb, Qt^T and
+// W^T as column pieces with transposed LDS reads.
 template <int D, bool CLER, int NSW>
 struct BwdStage {
     static constexpr int MAT = CHUNK * D * 2;   // [64][D] or [D][64] fp16
-    static constexpr int AT = 0;                // [64][64]
-    static constexpr int KB = AT + CHUNK * CHUNK * 2;
-    static constexpr int QTT = KB + MAT;
-    static constexpr int WT = QTT + MAT;
-    static constexpr int DO = WT + MAT;         // dO rows of each slice: NSW x [64][16] in the input dtype (bf16)
+    static constexpr int A = 0;                 // A [64][64]
+    static constexpr int KBT = A + CHUNK * CHUNK * 2;  // Kb^T [D][64]
+    static constexpr int QT = KBT + MAT;        // Qt [64][D]
+    static constexpr int W = QT + MAT;          // W [64][D]
+    static constexpr int DO = W + MAT;          // dO rows of each slice: NSW x [64][16] in the input dtype (bf16)
     static constexpr int GAM = DO + NSW * 2048; // D fp32 in a 1 KiB slot
     static constexpr int DH = GAM + 1024;       // error routing: dh rows of each slice, like dO
     static constexpr int BT = DH + NSW * 2048;  // error routing: the chunk's 64 betas (1 KiB slot)
@@ -323,22 +326,22 @@ struct BwdStage {
     static constexpr int NT = (NL + 63) / 64;
 };
 
-// PART 0: A^T, the dO rows of the NSW slices from column j0 on, gamma (and the
-// epilogue's dh rows and betas); PART 1: Kb; PART 2: Qt^T; PART 3: W^T.
+// PART 0: A, the dO rows of the NSW slices from column j0 on, gamma (and the
+// epilogue's dh rows and betas); PART 1: Kb^T; PART 2: Qt; PART 3: W.
 template <int D, bool CLER, int NSW, int PART>
 __device__ __forceinline__ void stage_bwd(lds_char* dst, const ChunkWs& ws, int64_t ch, int64_t c, int64_t b,
                                           int64_t T, int H, int h, const void* dO, int j0, int lane,
                                           const ClerBwd& cl) {
     using L = BwdStage<D, CLER, NSW>;
     if constexpr (PART == 1) {
-        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Kb) + ch * L::MAT, dst + L::KB, lane);
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.KbT) + ch * L::MAT, dst + L::KBT, lane);
     } else if constexpr (PART == 2) {
-        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.QtT) + ch * L::MAT, dst + L::QTT, lane);
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.Qt) + ch * L::MAT, dst + L::QT, lane);
     } else if constexpr (PART == 3) {
-        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.WT) + ch * L::MAT, dst + L::WT, lane);
+        copy_block_to_lds<L::MAT / 1024>(static_cast<const char*>(ws.W) + ch * L::MAT, dst + L::W, lane);
     } else {
-        copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2,
-                                                    dst + L::AT, lane);
+        copy_block_to_lds<CHUNK * CHUNK * 2 / 1024>(static_cast<const char*>(ws.A) + ch * CHUNK * CHUNK * 2,
+                                                    dst + L::A, lane);
         // dO rows: position pos = 32 i + lane / 2, half lane % 2 of the slice's 16
         // columns (rows past the end re-read the last token; they are zeroed at use)
 #pragma unroll
@@ -402,12 +405,12 @@ __device__ __forceinline__ void touch_bwd(lds_char* dummy, const ChunkWs& ws, in
     for (int i = 0; i < L::NT; ++i) {
         const int Lr = lane + 64 * i;
         const char* addr;
-        if (Lr < AL) addr = static_cast<const char*>(ws.AT) + ch * CHUNK * CHUNK * 2 + (slice * AL + Lr) * 128;
-        else if (Lr < AL + QL) addr = static_cast<const char*>(ws.Kb) + ch * L::MAT + (slice * QL + Lr - AL) * 128;
+        if (Lr < AL) addr = static_cast<const char*>(ws.A) + ch * CHUNK * CHUNK * 2 + (slice * AL + Lr) * 128;
+        else if (Lr < AL + QL) addr = static_cast<const char*>(ws.KbT) + ch * L::MAT + (slice * QL + Lr - AL) * 128;
         else if (Lr < AL + 2 * QL)
-            addr = static_cast<const char*>(ws.QtT) + ch * L::MAT + (slice * QL + Lr - AL - QL) * 128;
+            addr = static_cast<const char*>(ws.Qt) + ch * L::MAT + (slice * QL + Lr - AL - QL) * 128;
         else if (Lr < AL + 3 * QL)
-            addr = static_cast<const char*>(ws.WT) + ch * L::MAT + (slice * QL + Lr - AL - 2 * QL) * 128;
+            addr = static_cast<const char*>(ws.W) + ch * L::MAT + (slice * QL + Lr - AL - 2 * QL) * 128;
         else addr = reinterpret_cast<const char*>(ws.gam + ch * D) + (slice % (D * 4 / 128)) * 128;
         copy4_to_lds(addr, dummy + i * 256);
     }
@@ -449,8 +452,8 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
 
     if (tid >= 256 * NSW) {
         // Loaders: chunk c-1 goes into the buffer chunk c+1 used (free since the
-        // end of that step).  Four waves each copy one part (A^T, dO and gamma;
-        // Kb; Qt^T; W^T), so four times as many copies are in flight as with
+        // end of that step).  Four waves each copy one part (A, dO and gamma;
+        // Kb^T; Qt; W), so four times as many copies are in flight as with
         // one; the first also warms the L2 (the lines of this group's slices).
         const int part = (tid >> 6) - 4 * NSW;
         const bool w4 = part == 0;
@@ -510,13 +513,30 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
         const int64_t ch = bh * NC + c;
         // operand fragments of this wave for dU (those for dS are read once the
         // dU products are issued)
+        // fragment whose lane holds rows r0 + 8 g4 .. +7 of column c0 + l16 of a
+        // fragment-order array staged at byte offset `at_` (K its row length)
+        const auto colfrag = [&](int at_, int K, int r0, int c0) {
+            typedef const __attribute__((address_space(3))) _Float16* lds_f16;
+            _Float16 x[8];
+            if (K == CHUNK)
+                lds_column8_at(reinterpret_cast<lds_f16>(src + at_), r0 + 8 * g4, c0, lane,
+                               [](int r, int c) { return frag_off<CHUNK>(r, c); }, x);
+            else
+                lds_column8_at(reinterpret_cast<lds_f16>(src + at_), r0 + 8 * g4, c0, lane,
+                               [](int r, int c) { return frag_off<D>(r, c); }, x);
+            Frag<OpT> f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+            return f;
+        };
         Frag<OpT> at[2], kb[D / 32], qtt[SRT][2], wt[SRT][2];
         float gam[SRT][4];
-        at[0].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::AT + ((wid * 2 + 0) * 64 + lane) * 16);
-        at[1].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::AT + ((wid * 2 + 1) * 64 + lane) * 16);
+        // A^T (rows 16 wid + l16, k = position) and Kb (rows position, k = d):
+        // column pieces of A and Kb^T
+        at[0] = colfrag(L::A, CHUNK, 0, 16 * wid);
+        at[1] = colfrag(L::A, CHUNK, 32, 16 * wid);
 #pragma unroll
-        for (int kq = 0; kq < D / 32; ++kq)
-            kb[kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::KB + ((wid * (D / 32) + kq) * 64 + lane) * 16);
+        for (int kq = 0; kq < D / 32; ++kq) kb[kq] = colfrag(L::KBT, CHUNK, 32 * kq, 16 * wid);
         // dO fragments (B operand, k = position): column j0 + l16, positions
         // 32 kq + 8 g4 + e, scaled; rows past the end are zero
         // (all sixteen values are read before any is masked: a select on each
@@ -529,8 +549,7 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
             bf16_t raw[2][8];
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) raw[kq][e] = dos[(32 * kq + 8 * g4 + e) * 16 + l16];
+                lds_column8_at(dos, 32 * kq + 8 * g4, 0, lane, [](int r, int c) { return r * 16 + c; }, raw[kq]);
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
@@ -577,10 +596,11 @@ __global__ __launch_bounds__(64 * (4 * NSW + 4)) void state_bwd_lds_kernel(int64
 #pragma unroll
         for (int m = 0; m < SRT; ++m) {
             const int rt = wid * (D / 64) + m;
+            // Qt^T and W^T (rows d = 16 rt + l16, k = position): column pieces of Qt and W
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
-                qtt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::QTT + ((rt * 2 + kq) * 64 + lane) * 16);
-                wt[m][kq].v = *reinterpret_cast<const __attribute__((address_space(3))) half8*>(src + L::WT + ((rt * 2 + kq) * 64 + lane) * 16);
+                qtt[m][kq] = colfrag(L::QT, D, 32 * kq, 16 * rt);
+                wt[m][kq] = colfrag(L::W, D, 32 * kq, 16 * rt);
             }
             const float4v g = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(src + L::GAM + (16 * rt + 4 * g4) * 4);
 #pragma unroll

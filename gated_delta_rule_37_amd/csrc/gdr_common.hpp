@@ -168,26 +168,26 @@ __device__ __forceinline__ void store4(OpT* dst, const float4v& v) {
 // Column piece of an LDS array: out[e] = t[off(r0 + e, c0 + lane % 16)],
 // e = 0..7, where off(r, c) is the element offset of row r, column c, the 16
 // lanes of a group share r0 and c0 (so a group reads 16 consecutive columns)
-// and all 16 take part.  fp16: two gfx950 transposed reads (ds_read_b64_tr_b16),
-// which hand lane 4a+i of a 16-lane group element i of the 8-byte pieces that
-// lanes a, a+4, a+8 and a+12 of the group address; so lane c addresses row
-// r0 + c/4 (+4 in the second read), columns c0 + 4(c%4) .. +3, which must be
-// four consecutive, 8-byte aligned elements (c0 a multiple of 16; true of a
-// row-major array with a row stride that is a multiple of 4, and of the
-// fragment order).  fp32: eight plain reads.
-template <typename OpT, typename Off>
-__device__ __forceinline__ void lds_column8_at(const OpT* t, int r0, int c0, int lane, Off off, OpT (&out)[8]) {
-    if constexpr (sizeof(OpT) == 2) {
+// and all 16 take part.  16-bit elements (moved as raw bits): two gfx950
+// transposed reads (ds_read_b64_tr_b16), which hand lane 4a+i of a 16-lane
+// group element i of the 8-byte pieces that lanes a, a+4, a+8 and a+12 of the
+// group address; so lane c addresses row r0 + c/4 (+4 in the second read),
+// columns c0 + 4(c%4) .. +3, which must be four consecutive, 8-byte aligned
+// elements (c0 a multiple of 16; true of a row-major array with a row stride
+// that is a multiple of 4, and of the fragment order).  fp32: eight plain reads.
+// t may point to LDS generically or in the LDS address space.
+template <typename Ptr, typename T, typename Off>
+__device__ __forceinline__ void lds_column8_at(Ptr t, int r0, int c0, int lane, Off off, T (&out)[8]) {
+    if constexpr (sizeof(T) == 2) {
         typedef short short4v __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) short4v lds_short4;
         const int c = lane & 15, r = r0 + (c >> 2), cc = c0 + 4 * (c & 3);
-        const half4 lo = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r, cc))));
-        const half4 hi =
-            __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r + 4, cc))));
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r, cc)));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(t + off(r + 4, cc)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            out[e] = lo[e];
-            out[4 + e] = hi[e];
+            out[e] = __builtin_bit_cast(T, static_cast<short>(lo[e]));
+            out[4 + e] = __builtin_bit_cast(T, static_cast<short>(hi[e]));
         }
     } else {
 #pragma unroll

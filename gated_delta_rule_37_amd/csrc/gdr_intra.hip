@@ -18,7 +18,9 @@
 // pass is written in fragment order (see gdr_common.hpp) so that the
 // sequential kernel reads it with fully coalesced loads.  In backward mode it writes
 // instead the operands the reverse state pass and the gradient kernel need:
-// W, Ut, Kb^T, gamma, A^T, Kb, Qt^T, W^T and N = (I + L)^-1 in fp32.
+// W, Ut, Kb^T, gamma, Qt, A, N = (I + L)^-1 and P in fp32; the reverse pass
+// reads the transposes of Qt, A, Kb^T and W with transposed LDS reads (fp32
+// operands: A^T, Kb, Qt^T and W^T are stored instead of Qt and A).
 //
 // Thread layout: 4*D threads; thread (channel c, part p) owns rows 16p..16p+15
 // of channel c for the element-wise work, i.e. exactly the 16-row block p.
@@ -75,12 +77,11 @@ struct IntraLayout {
     static constexpr int NM = (PL + PL_BYTES > END12) ? PL + PL_BYTES : END12;
     static constexpr int END34 = NM + CHUNK * CHUNK * 4;
     static constexpr int BASE_BYTES = END12 > END34 ? END12 : END34;
-    // fp16 operands: Qt and Kb (fragment order) and the updated h rows are
-    // assembled in LDS and written out with full 16-byte stores
+    // fp16 operands: Qt (fragment order) and the updated h rows are assembled
+    // in LDS and written out with full 16-byte stores
     static constexpr bool STAGE = !IN_F32;
     static constexpr int QTS = BASE_BYTES;
-    static constexpr int KBS = QTS + (STAGE ? CHUNK * D * OPB : 0);
-    static constexpr int HS = KBS + (STAGE ? CHUNK * D * OPB : 0);
+    static constexpr int HS = QTS + (STAGE ? CHUNK * D * OPB : 0);
     static constexpr int BYTES = HS + (STAGE ? CHUNK * D * 2 : 0);
     // operand-precision limit on the in-block decay range (log2 units)
     static constexpr float RHO_MAX = IN_F32 ? 100.f : 8.f;
@@ -107,7 +108,12 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                                                       void* __restrict__ h_, const float* __restrict__ lam,
                                                       ChunkWs ws, int pro, ChunkRange cr) {
     constexpr bool FO = MODE != 1;  // forward operands: Qt, A
-    constexpr bool BWD = MODE != 0; // backward operands: Kb, Qt^T, A^T, W^T, N, P
+    constexpr bool BWD = MODE != 0; // backward operands: N, P (and the prologue's norms)
+    // Qt and A: the forward's operands, and with fp16 operands also the reverse
+    // pass's, which reads their transposes (and Kb, W^T) with transposed LDS
+    // reads; fp32 operands store those transposes (TR) for the reverse pass
+    constexpr bool QA = FO || (BWD && !IN_F32);
+    constexpr bool TR = BWD && IN_F32;
     using L = IntraLayout<D, GATE, IN_F32>;
     using OpT = typename L::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -123,8 +129,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
     OpT* Kq = reinterpret_cast<OpT*>(smem + L::KQ);
     OpT* Qq = reinterpret_cast<OpT*>(smem + L::QQ);
     OpT* Kh = reinterpret_cast<OpT*>(smem + L::KH);
-    OpT* QtS = reinterpret_cast<OpT*>(smem + L::QTS);  // staged outputs (fp16 operands only)
-    OpT* KbS = reinterpret_cast<OpT*>(smem + L::KBS);
+    OpT* QtS = reinterpret_cast<OpT*>(smem + L::QTS);  // staged output (fp16 operands only)
     OpT* KtT = reinterpret_cast<OpT*>(smem + L::KTT);
     OpT* VT = reinterpret_cast<OpT*>(smem + L::VT);
     float* Pm = reinterpret_cast<float*>(smem + L::PL);
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 kb[j] = kk[j] * exp2_fast(glast - G[j]);
                 fq = exp2_fast(G[j] - carry);
             }
-            if constexpr (FO) {
+            if constexpr (QA) {
                 if constexpr (L::STAGE) QtS[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
                 else Qt_g[frag_off<D>(r, cc)] = from_f32<OpT>(qq[j] * E[j]);
             }
@@ -317,19 +322,15 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                 Qq[r * LDR + cc] = from_f32<OpT>(qq[j]);
                 Kh[r * LDR + cc] = from_f32<OpT>(kk[j]);
             }
-            if constexpr (BWD) {
-                if constexpr (L::STAGE) {
-                    KbS[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
-                } else {
-                    OpT* Kb_g = reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D;
-                    Kb_g[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
-                }
+            if constexpr (TR) {
+                OpT* Kb_g = reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D;
+                Kb_g[frag_off<D>(r, cc)] = from_f32<OpT>(kb[j]);
             }
         }
         // Kb^T is the A operand of Kb^T U (rows d, k = position): two runs of 8
         store_run<OpT, 8>(KbT_g + frag_off<CHUNK>(cc, r0), kb);
         store_run<OpT, 8>(KbT_g + frag_off<CHUNK>(cc, r0 + 8), kb + 8);
-        if constexpr (BWD) {
+        if constexpr (TR) {
             float qt[RPP];
 #pragma unroll
             for (int j = 0; j < RPP; ++j) qt[j] = qq[j] * E[j];
@@ -356,15 +357,10 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         // staged outputs: fragment-order blocks are straight copies; h rows go
         // back to their tokens (rows past the end are not written)
         constexpr int NPC = CHUNK * D * 2 / 16 / NT;  // 16-byte pieces per thread
-        if constexpr (FO) {
+        if constexpr (QA) {
             uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<OpT*>(ws.Qt) + ch * CHUNK * D);
 #pragma unroll
             for (int k2 = 0; k2 < NPC; ++k2) dst[k2 * NT + tid] = reinterpret_cast<const uint4*>(QtS)[k2 * NT + tid];
-        }
-        if constexpr (BWD) {
-            uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<OpT*>(ws.Kb) + ch * CHUNK * D);
-#pragma unroll
-            for (int k2 = 0; k2 < NPC; ++k2) dst[k2 * NT + tid] = reinterpret_cast<const uint4*>(KbS)[k2 * NT + tid];
         }
         if (hh) {
             constexpr int PPR = D * 2 / 16;  // pieces per row
@@ -406,8 +402,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
             acc[e] *= f;
         }
         if (isA) {
-            if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
-            if constexpr (BWD) {
+            if constexpr (QA) store4<OpT>(A_g + frag_off<CHUNK>(r, 16 * I + 4 * g4), acc);
+            if constexpr (TR) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) AT_g[frag_off<CHUNK>(16 * I + 4 * g4 + e, r)] = from_f32<OpT>(acc[e]);
             }
@@ -478,8 +474,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
         const int R = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
         const int I = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
         const int r = 16 * R + w / 4, i0 = 16 * I + 4 * (w % 4);
-        if constexpr (FO) store4<OpT>(A_g + frag_off<CHUNK>(r, i0), zero4());
-        if constexpr (BWD) {
+        if constexpr (QA) store4<OpT>(A_g + frag_off<CHUNK>(r, i0), zero4());
+        if constexpr (TR) {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) AT_g[frag_off<CHUNK>(i0 + e2, r)] = from_f32<OpT>(0.f);
         }
@@ -541,8 +537,8 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                     }
                     if (cg == 0) {
                         Ps[r * CHUNK + ii] = ps;
-                        if constexpr (FO) A_g[frag_off<CHUNK>(r, ii)] = from_f32<OpT>(as);
-                        if constexpr (BWD) AT_g[frag_off<CHUNK>(ii, r)] = from_f32<OpT>(as);
+                        if constexpr (QA) A_g[frag_off<CHUNK>(r, ii)] = from_f32<OpT>(as);
+                        if constexpr (TR) AT_g[frag_off<CHUNK>(ii, r)] = from_f32<OpT>(as);
                     }
                 }
             }
@@ -658,7 +654,7 @@ __global__ __launch_bounds__(4 * D) void intra_kernel(int64_t T, int H, int64_t 
                     const int pos = 16 * n + l16, d0 = 16 * m + 4 * g4;
                     if (mat == 0) {
                         store4<OpT>(W_g + frag_off<D>(pos, d0), acc);  // A operand of W S
-                        if constexpr (BWD) {
+                        if constexpr (TR) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e) WT_g[frag_off<CHUNK>(d0 + e, pos)] = from_f32<OpT>(acc[e]);
                         }

@@ -15,7 +15,9 @@ namespace gdr {
 //     W [64][D], Ut [64][D] (accumulator order), Qt [64][D], KbT [D][64],
 //     A [64][64] (op); gam [D] fp32
 //   backward, additionally:
-//     AT [64][64], Kb [64][D], QtT [D][64], WT [D][64] (op)   reverse pass
+//     AT [64][64], Kb [64][D], QtT [D][64], WT [D][64]        reverse pass
+//       (fp32 operands only: with fp16 operands the reverse pass reads these
+//       transposes from Qt, A, KbT and W, which every mode then writes)
 //     Nw, Pw [64][64] fp32: N = (I + L)^-1 and P = Kt Kh^T     gradient kernels
 //     Ssnap [D][D] chunk-start state, Usave [64][D] (op)        state pass (save)
 //     dSsnap [D][D] chunk-end state gradient, dUsave [64][D],

@@ -168,3 +168,25 @@ def test_gdn2_decode_steps_equal_chunked_forward():
     errs = {"o": rel(od, o.cpu().double().numpy()), "S": rel(S, ST.cpu().double().numpy())}
     report(**errs)
     assert max(errs.values()) < 2e-3, errs
+
+
+@pytest.mark.parametrize("which", ["no erase", "no write", "neither"])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_gdn2_degenerate_gates(which, dt):
+    """Gates at zero: e = 0 writes without erasing, w = 0 erases without writing,
+    and with both zero the state only decays (S_T = prod Diag(alpha) S0)."""
+    announce("gdn2 degenerate gates %s %s" % (which, dt))
+    inp = make(1, 150, 2, 128, "channel", dt, 1080)
+    if which in ("no erase", "neither"):
+        inp["erase"] = np.zeros_like(inp["erase"])
+    if which in ("no write", "neither"):
+        inp["write"] = np.zeros_like(inp["write"])
+    o, ST = run(inp, dt)
+    o_ref, S_ref = ref(inp)
+    if which == "neither":
+        # pure decay of the initial state, independent of k and v
+        decay = np.prod(inp["alpha"][0].astype(np.float64), axis=0)  # [H, dk]
+        np.testing.assert_allclose(S_ref[0], decay[:, :, None] * inp["S0"][0], rtol=1e-12, atol=1e-14)
+    errs = {"o": rel(o, o_ref), "S_T": rel(ST, S_ref)}
+    report(**errs)
+    assert max(errs.values()) < (2e-3 if dt == "bf16" else 1e-5), errs
