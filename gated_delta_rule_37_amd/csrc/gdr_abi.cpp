@@ -103,7 +103,7 @@ int state_parts(const Aux* a, int64_t blocks, int64_t NC) {
 }
 
 // Bounds of range p of a pass cut into `parts`, in the order the pass runs.
-// Range sizes grow geometrically (weights 1 : 3/2 : 9/4 : ...) away from the
+// Range sizes grow geometrically (weights 1 : r : r^2 : ..., r = ra / rb) away from the
 // range whose per-chunk work cannot overlap anything: the first range of the
 // reverse pass (its gradient kernels wait for it, and each later range should
 // be ready about when the gradient kernels of the one before finish, which run
@@ -113,19 +113,22 @@ int state_parts(const Aux* a, int64_t blocks, int64_t NC) {
 // 2, 3/2 and 1.3 between neighbours gave 2.90, 2.89 and 2.92 ms per training
 // step, equal ranges 3.04 ms.  With the forward's intra-chunk ranges overlapping
 // the chain, its largest-first order still measured best: inference forward
-// 1.01 ms against 1.07 smallest first and 1.06 with equal ranges.)
-void cut_range(int64_t NC, int parts, int p, bool reverse, int64_t* lo, int64_t* hi) {
+// 1.01 ms against 1.07 smallest first and 1.06 with equal ranges.  Measured
+// again at 2.48 ms per step: 3, 5 or 6 ranges and ratios 4/3 and 5/3 all
+// slower for the training step, by 0.3-2.7 %; the inference forward alone is
+// 2.5 % faster with r = 4/3, which it uses: 0.869 against 0.892 ms.)
+void cut_range(int64_t NC, int parts, int p, bool reverse, int64_t* lo, int64_t* hi, int ra, int rb) {
     if (parts < 2) {
         *lo = 0;
         *hi = NC;
         return;
     }
-    // sizes in processing order for the reverse pass: w_i = 3^i 2^(parts-1-i)
+    // sizes in processing order for the reverse pass: w_i = ra^i rb^(parts-1-i)
     int64_t size[kMaxParts], w[kMaxParts];
     int64_t wsum = 0;
     for (int i = 0; i < parts; ++i) {
         w[i] = 1;
-        for (int j = 0; j < parts - 1; ++j) w[i] *= j < i ? 3 : 2;
+        for (int j = 0; j < parts - 1; ++j) w[i] *= j < i ? ra : rb;
         wsum += w[i];
     }
     int64_t used = 0;
@@ -499,7 +502,7 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
             // two-slice chain steps slower beside the intra-chunk kernel).
             float* carry = reinterpret_cast<float*>(static_cast<char*>(ws) + need - align_up(carry_bytes(desc)));
             int64_t lo[kMaxParts], hi[kMaxParts];
-            for (int p = 0; p < parts; ++p) cut_range(NC, parts, p, false, &lo[p], &hi[p]);
+            for (int p = 0; p < parts; ++p) cut_range(NC, parts, p, false, &lo[p], &hi[p], train ? 3 : 4, train ? 2 : 3);
             gdr_status g = intra(gdr::ChunkRange{lo[0], hi[0] - lo[0]}, s);
             if (g != GDR_OK) return g;
             if (hipEventRecord(aux->ev[0], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[0], 0) != hipSuccess)
@@ -705,7 +708,7 @@ static gdr_status backward_impl(const gdr_desc* desc, const void* q, const void*
             // 32K-token KDA shape)
             for (int p = 0; p < parts; ++p) {
                 int64_t lo, hi;
-                cut_range(NC, parts, p, true, &lo, &hi);
+                cut_range(NC, parts, p, true, &lo, &hi, 3, 2);
                 GDR_STEP(sb_name, gdr::launch_state_bwd(int(D), in_f32, B, T, int(H), NC, desc->scale, w, dO,
                                                         p == 0 ? dST : carry, p == parts - 1 ? dS0 : carry,
                                                         dh_state, clvr_scale, beta_eff, wide && p > 0,
