@@ -772,6 +772,13 @@ static size_t gdn2_ws_bytes(int64_t nch, int D, int op_bytes, gdr::ChunkWs* out,
     return off;
 }
 
+// The separate-gate workspace plus the fp32 state handed between the ranges of
+// a cut pass (at the end, as in the chunked forward's).
+static size_t gdn2_ws_total(const gdr_desc* d, int64_t NC) {
+    return gdn2_ws_bytes(d->B * d->H * NC, int(d->dk), d->in_dtype == GDR_FP32 ? 4 : 2, nullptr, nullptr) +
+           align_up(carry_bytes(d));
+}
+
 static gdr_status gdn2_check_desc(const gdr_desc* desc, int64_t* NC) {
     gdr_status st = check_desc(desc, NC);
     if (st != GDR_OK) return st;
@@ -783,8 +790,7 @@ static gdr_status gdn2_check_desc(const gdr_desc* desc, int64_t* NC) {
 extern "C" size_t gdr_gdn2_workspace_size(const gdr_desc* desc) {
     int64_t NC = 0;
     if (gdn2_check_desc(desc, &NC) != GDR_OK) return 0;
-    return gdn2_ws_bytes(desc->B * desc->H * NC, int(desc->dk), desc->in_dtype == GDR_FP32 ? 4 : 2, nullptr,
-                         nullptr);
+    return gdn2_ws_total(desc, NC);
 }
 
 extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
@@ -823,7 +829,8 @@ extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void*
     if (S0 && ST && S0 != ST && overlap(S0, s_bytes, ST, s_bytes))
         return fail(GDR_ERR_INVALID_ARG, "ST partially overlaps S0 (it may only alias it exactly)");
     gdr::ChunkWs w;
-    const size_t need = gdn2_ws_bytes(B * H * NC, int(D), desc->in_dtype == GDR_FP32 ? 4 : 2, &w, ws);
+    gdn2_ws_bytes(B * H * NC, int(D), desc->in_dtype == GDR_FP32 ? 4 : 2, &w, ws);
+    const size_t need = gdn2_ws_total(desc, NC);
     if (ws_bytes < need || (need > 0 && !ws))
         return fail(GDR_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
     if (B * H == 0) return GDR_OK;
@@ -847,17 +854,60 @@ extern "C" gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void*
         if (g != GDR_OK) return g;
     }
     hipError_t e = hipSuccess;
-    if (NC > 0) {
-        gdr::prof_before(s);
-        e = gdr::launch_gdn2_intra(int(D), desc->gate, in_f32, B, T, int(H), NC, q, k, v, erase, write, alpha, w, s);
-        gdr::prof_after("gdn2_intra", s);
+    auto intra = [&](gdr::ChunkRange cr, hipStream_t is) -> gdr_status {
+        gdr::prof_before(is);
+        e = gdr::launch_gdn2_intra(int(D), desc->gate, in_f32, B, T, int(H), NC, q, k, v, erase, write, alpha, w,
+                                   cr, is);
+        gdr::prof_after("gdn2_intra", is);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "intra-chunk launch: %s", hipGetErrorString(e));
+        return GDR_OK;
+    };
+    auto pass = [&](gdr::ChunkRange cr, const float* sin, float* sout) -> gdr_status {
+        gdr::prof_before(s);
+        e = gdr::launch_state_fwd_xy(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, sin, sout, o, cr, s);
+        gdr::prof_after("gdn2_state", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
+        return GDR_OK;
+    };
+    {
+        // As in the chunked forward: when the pass (one workgroup per 16-column
+        // slice) leaves CUs idle, it is cut into chunk ranges, largest first, and
+        // the intra-chunk transform of range p runs on the second stream while
+        // the pass carries range p-1 (the output is computed in the pass).  At
+        // B=1 H=16 T=32768 d=128: forward 1.29 ms uncut.
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        Aux* aux = (!in_f32 && NC > 0) ? aux_stream() : nullptr;
+        const int parts = state_parts(aux, B * H * (D / 16), NC);
+        if (parts > 1) {
+            float* carry = reinterpret_cast<float*>(static_cast<char*>(ws) + need - align_up(carry_bytes(desc)));
+            int64_t lo[kMaxParts], hi[kMaxParts];
+            for (int p = 0; p < parts; ++p) cut_range(NC, parts, p, false, &lo[p], &hi[p], 3, 2);
+            gdr_status g = intra(gdr::ChunkRange{lo[0], hi[0] - lo[0]}, s);
+            if (g != GDR_OK) return g;
+            if (hipEventRecord(aux->ev[0], s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->ev[0], 0) != hipSuccess)
+                return fail(GDR_ERR_DEVICE, "stream ordering failed");
+            for (int p = 1; p < parts; ++p) {
+                g = intra(gdr::ChunkRange{lo[p], hi[p] - lo[p]}, aux->s);
+                if (g != GDR_OK) return g;
+                if (hipEventRecord(aux->ev[p], aux->s) != hipSuccess)
+                    return fail(GDR_ERR_DEVICE, "stream ordering failed");
+            }
+            // range p's pass waits for its intra-chunk range; the last wait also
+            // orders all of the second stream's work before the caller's stream
+            for (int p = 0; p < parts; ++p) {
+                if (p > 0 && hipStreamWaitEvent(s, aux->ev[p], 0) != hipSuccess)
+                    return fail(GDR_ERR_DEVICE, "stream ordering failed");
+                g = pass(gdr::ChunkRange{lo[p], hi[p] - lo[p]}, p == 0 ? S0 : carry, p == parts - 1 ? ST : carry);
+                if (g != GDR_OK) return g;
+            }
+            return GDR_OK;
+        }
     }
-    gdr::prof_before(s);
-    e = gdr::launch_state_fwd_xy(int(D), in_f32, out_f32, B, T, int(H), NC, desc->scale, w, S0, ST, o, s);
-    gdr::prof_after("gdn2_state", s);
-    if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "state-pass launch: %s", hipGetErrorString(e));
-    return GDR_OK;
+    if (NC > 0) {
+        gdr_status g = intra(gdr::ChunkRange{0, NC}, s);
+        if (g != GDR_OK) return g;
+    }
+    return pass(gdr::ChunkRange{0, NC}, S0, ST);
 }
 
 extern "C" gdr_status gdr_gdn2_decode_step(int64_t N, int64_t H, int64_t dk, int64_t dv, int32_t gate,

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
                                                          const void* __restrict__ k_, const void* __restrict__ v_,
                                                          const float* __restrict__ erase,
                                                          const float* __restrict__ write,
-                                                         const float* __restrict__ alpha, ChunkWs ws) {
+                                                         const float* __restrict__ alpha, ChunkWs ws,
+                                                         ChunkRange cr) {
     using InT = typename InType<IN_F32>::T;
     // operand precision (as in the KDA path): fp16 for bf16 inputs, fp32 for
     // fp32 inputs -- of the C x C blocks (a diagonal block whose decay range is
@@ -111,8 +112,9 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_kernel(int64_t T, int H, int64
     __shared__ __attribute__((aligned(16))) float sB[BUF];
     __shared__ float s_tot[P][D];
 
-    const int64_t ch = blockIdx.x;  // chunk-head: (b * H + h) * NC + c
-    const int64_t bh = ch / NC, c = ch % NC;
+    int64_t bh, c;  // the chunks of the range cr of every (batch, head)
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int64_t t0 = c * CHUNK;
@@ -562,7 +564,8 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_h_kernel(int64_t T, int H, int
                                                            const void* __restrict__ k_, const void* __restrict__ v_,
                                                            const float* __restrict__ erase,
                                                            const float* __restrict__ write,
-                                                           const float* __restrict__ alpha, ChunkWs ws) {
+                                                           const float* __restrict__ alpha, ChunkWs ws,
+                                                           ChunkRange cr) {
     using L = Gdn2HLayout<D, GATE>;
     using OpT = _Float16;
     constexpr int NW = NT2 / WAVE, P = L::P, RPP = L::RPP, NCT = L::NCT;
@@ -590,8 +593,9 @@ __global__ __launch_bounds__(NT2) void gdn2_intra_h_kernel(int64_t T, int H, int
     OpT* sAW = reinterpret_cast<OpT*>(smem + L::AW);
     float* sN = reinterpret_cast<float*>(smem + L::NINV);
 
-    const int64_t ch = blockIdx.x;  // chunk-head: (b * H + h) * NC + c
-    const int64_t bh = ch / NC, c = ch % NC;
+    int64_t bh, c;  // the chunks of the range cr of every (batch, head)
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
     const int64_t t0 = c * CHUNK;
@@ -1092,35 +1096,36 @@ __global__ __launch_bounds__(256) void gdn2_decode_kernel(int64_t nslab, float s
 
 template <int D, int GATE, bool IN_F32>
 hipError_t intra_t(int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k, const void* v,
-                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
+                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws, ChunkRange cr,
                    hipStream_t stream) {
-    const int64_t nch = B * H * NC;
+    const int64_t nch = B * H * cr.n;
     if (nch == 0) return hipSuccess;
     if constexpr (IN_F32)
         hipLaunchKernelGGL((gdn2_intra_kernel<D, GATE, true>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q,
-                           k, v, erase, write, alpha, ws);
+                           k, v, erase, write, alpha, ws, cr);
     else
         hipLaunchKernelGGL((gdn2_intra_h_kernel<D, GATE>), dim3((unsigned)nch), dim3(NT2), 0, stream, T, H, NC, q, k,
-                           v, erase, write, alpha, ws);
+                           v, erase, write, alpha, ws, cr);
     return hipGetLastError();
 }
 
 template <int D, int GATE>
 hipError_t intra_g(bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k, const void* v,
-                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
+                   const float* erase, const float* write, const float* alpha, const ChunkWs& ws, ChunkRange cr,
                    hipStream_t stream) {
-    return in_f32 ? intra_t<D, GATE, true>(B, T, H, NC, q, k, v, erase, write, alpha, ws, stream)
-                  : intra_t<D, GATE, false>(B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+    return in_f32 ? intra_t<D, GATE, true>(B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream)
+                  : intra_t<D, GATE, false>(B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
 }
 
 template <int D>
 hipError_t intra_d(int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q, const void* k,
                    const void* v, const float* erase, const float* write, const float* alpha, const ChunkWs& ws,
-                   hipStream_t stream) {
-    if (gate == GATE_NONE) return intra_g<D, GATE_NONE>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+                   ChunkRange cr, hipStream_t stream) {
+    if (gate == GATE_NONE)
+        return intra_g<D, GATE_NONE>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
     if (gate == GATE_SCALAR)
-        return intra_g<D, GATE_SCALAR>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
-    return intra_g<D, GATE_CHANNEL>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+        return intra_g<D, GATE_SCALAR>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
+    return intra_g<D, GATE_CHANNEL>(in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
 }
 
 template <int D, int GATE, bool IN_F32, bool OUT_F32>
@@ -1157,9 +1162,9 @@ hipError_t decode_d(int gate, bool in_f32, bool out_f32, int64_t nslab, float sc
 
 hipError_t launch_gdn2_intra(int D, int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                              const void* k, const void* v, const float* erase, const float* write,
-                             const float* alpha, const ChunkWs& ws, hipStream_t stream) {
-    if (D == 64) return intra_d<64>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
-    return intra_d<128>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, stream);
+                             const float* alpha, const ChunkWs& ws, ChunkRange cr, hipStream_t stream) {
+    if (D == 64) return intra_d<64>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
+    return intra_d<128>(gate, in_f32, B, T, H, NC, q, k, v, erase, write, alpha, ws, cr, stream);
 }
 
 hipError_t launch_gdn2_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q,

@@ -104,21 +104,22 @@ hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t
                             float* ST, void* o, bool save_for_backward, bool wide, ChunkRange cr,
                             hipStream_t stream);
 
-// The pass of the separate-gate variant (Gated DeltaNet-2) over whole sequences,
-// o computed in the pass: operands W, Ut, Qt, KbT, A of ws in operand precision
+// The pass of the separate-gate variant (Gated DeltaNet-2) over the chunks cr
+// of every sequence (the state enters from S0, leaves into ST), o computed in
+// the pass: operands W, Ut, Qt, KbT, A of ws in operand precision
 // (fp16 for bf16 inputs, fp32 for fp32 inputs), gam, X, Y fp32.
 hipError_t launch_state_fwd_xy(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
-                               float scale, const ChunkWs& ws, const float* S0, float* ST, void* o,
+                               float scale, const ChunkWs& ws, const float* S0, float* ST, void* o, ChunkRange cr,
                                hipStream_t stream);
 
 // Gated DeltaNet-2 (separate erase and write gates e, w [B,T,H,D] fp32): the
-// intra-chunk kernel writes the pass's operands into ws: W = N Kt,
+// intra-chunk kernel writes the pass's operands of the chunks cr into ws: W = N Kt,
 // Ut = -N M_w V, Qt, KbT = (e*K*2^(G_last - G))^T, A = tril(Qt (e*Kh)^T), gam,
 // X = ((w*K)*2^(G_last - G))^T V and Y = tril(Qt (w*Kh)^T) V, with
 // N = (I + strict_tril(Kt (e*Kh)^T))^-1.
 hipError_t launch_gdn2_intra(int D, int gate, bool in_f32, int64_t B, int64_t T, int H, int64_t NC, const void* q,
                              const void* k, const void* v, const float* erase, const float* write,
-                             const float* alpha, const ChunkWs& ws, hipStream_t stream);
+                             const float* alpha, const ChunkWs& ws, ChunkRange cr, hipStream_t stream);
 hipError_t launch_gdn2_decode(int D, int gate, bool in_f32, bool out_f32, int64_t nslab, float scale, const void* q,
                               const void* k, const void* v, const float* erase, const float* write,
                               const float* alpha, float* S, void* o, hipStream_t stream);

@@ -271,9 +271,11 @@ __device__ __forceinline__ void touch_chunk(uint32_t (&out)[NPF], const ChunkWs&
 template <int D, bool IN_F32, bool OUT_F32, bool SAVE, bool HAS_O, bool XY = false>
 __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_t NC, float scale,
                                                         ChunkWs ws, const float* S0,
-                                                        float* ST, void* __restrict__ o_) {
-    // S0 and ST may alias: each workgroup reads its slice of S0 before it
-    // writes the same slice of ST, and slices of different workgroups are disjoint.
+                                                        float* ST, void* __restrict__ o_, ChunkRange cr) {
+    // Chunks cr.lo .. cr.lo + cr.n - 1 of every (batch, head); the state enters
+    // from S0 (NULL: zero) and leaves into ST.  S0 and ST may alias: each
+    // workgroup reads its slice of S0 before it writes the same slice of ST, and
+    // slices of different workgroups are disjoint.
     using Cfg = StateCfg<D, IN_F32>;
     using OpT = typename Cfg::OpT;
     using OutT = typename InType<OUT_F32>::T;
@@ -300,18 +302,22 @@ __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_
         constexpr int PF = 8;
         constexpr int NPF = L2Touch<D, IN_F32>::NPF;
         const int slice = j0 / Cfg::NS;
+        const int64_t lo = cr.lo, hi = cr.lo + cr.n;
         uint32_t ring[PF][NPF];
         uint32_t acc = 0;
+        // (an empty range touches nothing: its workspace may be empty)
+        if (cr.n > 0) {
 #pragma unroll
-        for (int s2 = 0; s2 < PF; ++s2)
-            touch_chunk<D, IN_F32, NPF>(ring[s2], ws, bh * NC + (s2 < NC ? s2 : 0), slice, lane);
+            for (int s2 = 0; s2 < PF; ++s2)
+                touch_chunk<D, IN_F32, NPF>(ring[s2], ws, bh * NC + (lo + s2 < NC ? lo + s2 : lo), slice, lane);
+        }
         __syncthreads();
 #pragma unroll 1
-        for (int64_t c0 = 0; c0 < NC; c0 += PF) {
+        for (int64_t c0 = lo; c0 < hi; c0 += PF) {
 #pragma unroll
             for (int s2 = 0; s2 < PF; ++s2) {
                 const int64_t c = c0 + s2;
-                if (c < NC) {
+                if (c < hi) {
 #pragma unroll
                     for (int i = 0; i < NPF; ++i) acc ^= ring[s2][i];  // chunk c is in L2 by now
                     // unconditional (clamped) so every slot is refilled: no register copies
@@ -343,15 +349,15 @@ __global__ __launch_bounds__(320) void state_fwd_kernel(int64_t T, int H, int64_
     // chunk) so that the compiler can count outstanding loads exactly and wait
     // only for the chunk about to be used.
     ChunkFrags<D, IN_F32, XY> fa, fb;
-    const int64_t last = NC - 1;
-    if (NC > 0) load_chunk<D, IN_F32, XY>(fa, ws, bh * NC, j0, wid, lane);
+    const int64_t lo = cr.lo, hi = cr.lo + cr.n, last = hi - 1;
+    if (cr.n > 0) load_chunk<D, IN_F32, XY>(fa, ws, bh * NC + lo, j0, wid, lane);
 #pragma unroll 1
-    for (int64_t c = 0; c < NC; c += 2) {
-        load_chunk<D, IN_F32, XY>(fb, ws, bh * NC + (c + 1 < NC ? c + 1 : last), j0, wid, lane);
+    for (int64_t c = lo; c < hi; c += 2) {
+        load_chunk<D, IN_F32, XY>(fb, ws, bh * NC + (c + 1 < hi ? c + 1 : last), j0, wid, lane);
         state_step<D, IN_F32, OUT_F32, SAVE, HAS_O, XY>(fa, c, T, H, b, h, bh, NC, j0, wid, l16, g4, scale, ws,
                                                         S, s_S, s_U, o);
-        if (c + 1 >= NC) break;
-        load_chunk<D, IN_F32, XY>(fa, ws, bh * NC + (c + 2 < NC ? c + 2 : last), j0, wid, lane);
+        if (c + 1 >= hi) break;
+        load_chunk<D, IN_F32, XY>(fa, ws, bh * NC + (c + 2 < hi ? c + 2 : last), j0, wid, lane);
         state_step<D, IN_F32, OUT_F32, SAVE, HAS_O, XY>(fb, c + 1, T, H, b, h, bh, NC, j0, wid, l16, g4, scale,
                                                         ws, S, s_S, s_U, o);
     }
@@ -609,13 +615,13 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
     }
     if (save && o)
         hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true, true>), dim3((unsigned)nblk), dim3(320),
-                           0, stream, T, H, NC, scale, ws, S0, ST, o);
+                           0, stream, T, H, NC, scale, ws, S0, ST, o, cr);
     else if (save)
         hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, true, false>), dim3((unsigned)nblk), dim3(320),
-                           0, stream, T, H, NC, scale, ws, S0, ST, o);
+                           0, stream, T, H, NC, scale, ws, S0, ST, o, cr);
     else
         hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false, true>), dim3((unsigned)nblk), dim3(320),
-                           0, stream, T, H, NC, scale, ws, S0, ST, o);
+                           0, stream, T, H, NC, scale, ws, S0, ST, o, cr);
     return hipGetLastError();
 }
 
@@ -623,29 +629,30 @@ static hipError_t launch_state_t(int64_t B, int64_t T, int H, int64_t NC, float 
 // computed in it, plus the per-chunk terms X (state) and Y (output) of ws.
 template <int D, bool IN_F32, bool OUT_F32>
 static hipError_t launch_state_xy_t(int64_t B, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws,
-                                    const float* S0, float* ST, void* o, hipStream_t stream) {
+                                    const float* S0, float* ST, void* o, ChunkRange cr, hipStream_t stream) {
     const int64_t nblk = B * H * StateCfg<D, IN_F32>::NSL;
     if (nblk == 0) return hipSuccess;
     hipLaunchKernelGGL((state_fwd_kernel<D, IN_F32, OUT_F32, false, true, true>), dim3((unsigned)nblk), dim3(320),
-                       0, stream, T, H, NC, scale, ws, S0, ST, o);
+                       0, stream, T, H, NC, scale, ws, S0, ST, o, cr);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_state_xy_d(bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
-                                    const ChunkWs& ws, const float* S0, float* ST, void* o, hipStream_t stream) {
+                                    const ChunkWs& ws, const float* S0, float* ST, void* o, ChunkRange cr,
+                                    hipStream_t stream) {
     if (in_f32)
-        return out_f32 ? launch_state_xy_t<D, true, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
-                       : launch_state_xy_t<D, true, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
-    return out_f32 ? launch_state_xy_t<D, false, true>(B, T, H, NC, scale, ws, S0, ST, o, stream)
-                   : launch_state_xy_t<D, false, false>(B, T, H, NC, scale, ws, S0, ST, o, stream);
+        return out_f32 ? launch_state_xy_t<D, true, true>(B, T, H, NC, scale, ws, S0, ST, o, cr, stream)
+                       : launch_state_xy_t<D, true, false>(B, T, H, NC, scale, ws, S0, ST, o, cr, stream);
+    return out_f32 ? launch_state_xy_t<D, false, true>(B, T, H, NC, scale, ws, S0, ST, o, cr, stream)
+                   : launch_state_xy_t<D, false, false>(B, T, H, NC, scale, ws, S0, ST, o, cr, stream);
 }
 
 hipError_t launch_state_fwd_xy(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
-                               float scale, const ChunkWs& ws, const float* S0, float* ST, void* o,
+                               float scale, const ChunkWs& ws, const float* S0, float* ST, void* o, ChunkRange cr,
                                hipStream_t stream) {
-    if (D == 64) return launch_state_xy_d<64>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, stream);
-    return launch_state_xy_d<128>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, stream);
+    if (D == 64) return launch_state_xy_d<64>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, cr, stream);
+    return launch_state_xy_d<128>(in_f32, out_f32, B, T, H, NC, scale, ws, S0, ST, o, cr, stream);
 }
 
 hipError_t launch_state_fwd(int D, bool in_f32, bool out_f32, int64_t B, int64_t T, int H,

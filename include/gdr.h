@@ -297,7 +297,8 @@ gdr_status gdr_output_gate_backward(const gdr_desc* desc, const void* o, const v
  * gdr_forward_chunked); fp32 inputs run in fp32 throughout.  Forward only (no
  * backward in this version).
  * ws: at least gdr_gdn2_workspace_size(desc) bytes (240.5 KiB per chunk-head
- * of 64 tokens at dk = dv = 128). */
+ * of 64 tokens at dk = dv = 128, plus one fp32 [dk][dv] state per (batch,
+ * head) handed between the chunk ranges of a cut state pass). */
 size_t gdr_gdn2_workspace_size(const gdr_desc* desc);
 gdr_status gdr_gdn2_forward_chunked(const gdr_desc* desc, const void* q, const void* k, const void* v,
                                     const float* erase, const float* write, const float* alpha,

@@ -117,16 +117,19 @@ hipError_t launch_cler_mt(int, bool, int64_t, int64_t, int, int64_t, const Chunk
     ++stub::launches;
     return hipSuccess;
 }
-hipError_t launch_state_fwd_xy(int, bool, bool, int64_t, int64_t, int, int64_t, float, const ChunkWs& ws,
-                               const float*, float*, void*, hipStream_t) {
+hipError_t launch_state_fwd_xy(int, bool, bool, int64_t, int64_t, int, int64_t NC, float, const ChunkWs& ws,
+                               const float*, float*, void*, ChunkRange cr, hipStream_t) {
+    if (NC > 0) check_range(cr, NC);
     check_ws(ws);
     in_ws(ws.X, "X");
     in_ws(ws.Y, "Y");
     ++stub::launches;
     return hipSuccess;
 }
-hipError_t launch_gdn2_intra(int, int, bool, int64_t, int64_t, int, int64_t, const void*, const void*, const void*,
-                             const float*, const float*, const float*, const ChunkWs& ws, hipStream_t) {
+hipError_t launch_gdn2_intra(int, int, bool, int64_t, int64_t, int, int64_t NC, const void*, const void*,
+                             const void*, const float*, const float*, const float*, const ChunkWs& ws, ChunkRange cr,
+                             hipStream_t) {
+    check_range(cr, NC);
     check_ws(ws);
     ++stub::launches;
     return hipSuccess;
