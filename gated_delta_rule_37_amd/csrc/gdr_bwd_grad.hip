@@ -730,7 +730,8 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
                                                float* __restrict__ dalpha, ChunkWs ws, int pro, ChunkRange cr,
                                                char* smem, const GradPartials<D, IN_F32>& pk,
                                                const float* s_gam, float (&s_tot)[4][D], int coff = 0,
-                                               int npass = 1, int pass = 0, float* s_acc = nullptr) {
+                                               int npass = 1, int pass = 0, float* s_acc = nullptr,
+                                               int ahead = 0) {
     static_assert(DS == D || !KEEP, "channel passes keep the partials in the workspace");
     using L = GGateLayout<D, IN_F32>;
     using OpT = typename L::OpT;
@@ -798,6 +799,43 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
         qq[j] = to_f32(q[e]);
         if constexpr (GATE == GATE_CHANNEL) al[j] = alpha[e];
         else al[j] = 1.f;
+    }
+    // L2 prefetch for the workgroup `ahead` places later in the launch (on the
+    // same XCD, as ahead is a multiple of 8): one dword per 128-byte line of
+    // its first operands, k, alpha and N, issued after this stage's own loads.
+    // The values are folded into tx, which is kept alive to the end, so the
+    // loads are issued here and waited for only there.
+    uint32_t tx = 0;
+    if constexpr (!IN_F32 && DS == D) {
+        const int64_t tb = static_cast<int64_t>(blockIdx.x) + ahead;
+        if (ahead > 0 && tb < static_cast<int64_t>(gridDim.x)) {
+            const uint32_t n = static_cast<uint32_t>(cr.n);
+            const int64_t bh_t = tb / n, c_t = cr.lo + tb % n;
+            const int64_t t0_t = c_t * CHUNK;
+            const int64_t nv64 = T - t0_t;
+            const int nv_t = nv64 < CHUNK ? static_cast<int>(nv64) : CHUNK;
+            const int64_t base_t = (((bh_t / H) * T + t0_t) * H + bh_t % H) * D;
+            const char* nw = reinterpret_cast<const char*>(ws.Nw) + (bh_t * NC + c_t) * CHUNK * CHUNK * 4;
+            // lines: k rows (D/64 each), alpha rows (D/32 each; channel gate), N (128)
+            constexpr int KL = D / 64, AL = GATE == GATE_CHANNEL ? D / 32 : 0, NL = CHUNK * (KL + AL) + 128;
+#pragma unroll
+            for (int l0 = 0; l0 < NL; l0 += NT) {
+                const int line = l0 + tid;
+                if (NL % NT == 0 || line < NL) {
+                    const char* addr;
+                    if (line < CHUNK * KL) {
+                        const int r = line / KL < nv_t ? line / KL : nv_t - 1;
+                        addr = reinterpret_cast<const char*>(k + base_t + r * tokstride) + (line % KL) * 128;
+                    } else if (line < CHUNK * (KL + AL)) {
+                        const int la = line - CHUNK * KL, r = la / AL < nv_t ? la / AL : nv_t - 1;
+                        addr = reinterpret_cast<const char*>(alpha + base_t + r * tokstride) + (la % AL) * 128;
+                    } else {
+                        addr = nw + (line - CHUNK * (KL + AL)) * 128;
+                    }
+                    tx ^= *reinterpret_cast<const uint32_t*>(addr);
+                }
+            }
+        }
     }
     asm volatile("" ::: "memory");
     if constexpr (GATE == GATE_SCALAR) {
@@ -1314,6 +1352,7 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
             }
         }
     }
+    asm volatile("" ::"v"(tx));  // the prefetch loads end here at the latest
 }
 
 // Both gradient stages for one chunk in one workgroup: the partials grad_lin
@@ -1331,7 +1370,7 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
                                                       void* __restrict__ dq_, void* __restrict__ dk_,
                                                       void* __restrict__ dv_, float* __restrict__ dbeta,
                                                       float* __restrict__ dalpha, ChunkWs ws, int pro,
-                                                      ChunkRange cr, float* __restrict__ partial) {
+                                                      ChunkRange cr, float* __restrict__ partial, int ahead) {
     constexpr int LB = GLinLayout<D, IN_F32>::BYTES, GB = GGateLayout<D, IN_F32>::BYTES;
     static_assert(!CLER || ClerLayout<D, IN_F32>::POST_BYTES <= (LB > GB ? LB : GB), "LDS of the CLER terms");
     // On the value route the partials stay on chip; the error route's terms
@@ -1351,7 +1390,7 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
         __syncthreads();
     }
     grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr,
-                                                        smem, pk, s_gam, s_tot);
+                                                        smem, pk, s_gam, s_tot, 0, 1, 0, nullptr, ahead);
 }
 
 // fp32 operands at d = 128, where one workgroup's LDS cannot hold either stage:
@@ -1404,7 +1443,7 @@ static hipError_t launch_grads_split(int64_t B, int64_t T, int H, int64_t NC, fl
                                      const void* k, const void* v, const float* beta, const float* alpha,
                                      const void* dO, const void* dh, const float* lam, void* dq, void* dk, void* dv,
                                      float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                                     bool cler, float* partial, hipStream_t stream) {
+                                     bool cler, float* partial, int, hipStream_t stream) {
     const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
 #define GDR_LIN_SPLIT(C, P)                                                                                      \
@@ -1434,13 +1473,13 @@ static hipError_t launch_grads_t(int64_t B, int64_t T, int H, int64_t NC, float 
                                  const void* k, const void* v, const float* beta, const float* alpha,
                                  const void* dO, const void* dh, const float* lam, void* dq, void* dk, void* dv,
                                  float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                                 bool cler, float* partial, hipStream_t stream) {
+                                 bool cler, float* partial, int ahead, hipStream_t stream) {
     const int64_t nblk = B * H * cr.n;
     if (nblk == 0) return hipSuccess;
 #define GDR_GRADS(P, C)                                                                                              \
     hipLaunchKernelGGL((grads_kernel<D, GATE, IN_F32, OUT_F32, P, C>), dim3((unsigned)nblk), dim3(4 * D), 0, stream, \
                        T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr,    \
-                       partial)
+                       partial, ahead)
     if (cler) {
         if (pro) GDR_GRADS(true, true);
         else GDR_GRADS(false, true);
@@ -1457,9 +1496,9 @@ static hipError_t launch_grads_g(bool in_f32, bool out_f32, int64_t B, int64_t T
                                  const void* q, const void* k, const void* v, const float* beta,
                                  const float* alpha, const void* dO, const void* dh, const float* lam, void* dq,
                                  void* dk, void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro,
-                                 ChunkRange cr, bool cler, float* partial, hipStream_t stream) {
+                                 ChunkRange cr, bool cler, float* partial, int ahead, hipStream_t stream) {
 #define GDR_GR_ARGS B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, dalpha, ws, pro, cr, \
-                    cler, partial, stream
+                    cler, partial, ahead, stream
     if (in_f32) {
         if constexpr (D == 64) {
             if (out_f32) return launch_grads_t<D, GATE, true, true>(GDR_GR_ARGS);
@@ -1479,9 +1518,9 @@ hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, i
                         float scale, const void* q, const void* k, const void* v, const float* beta,
                         const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
                         void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                        bool cler, float* partial, hipStream_t stream) {
+                        bool cler, float* partial, int ahead, hipStream_t stream) {
 #define GDR_GR_ARGS in_f32, out_f32, B, T, H, NC, scale, q, k, v, beta, alpha, dO, dh, lam, dq, dk, dv, dbeta, \
-                    dalpha, ws, pro, cr, cler, partial, stream
+                    dalpha, ws, pro, cr, cler, partial, ahead, stream
     if (D == 64) {
         if (gate == GATE_NONE) return launch_grads_g<64, GATE_NONE>(GDR_GR_ARGS);
         if (gate == GATE_SCALAR) return launch_grads_g<64, GATE_SCALAR>(GDR_GR_ARGS);

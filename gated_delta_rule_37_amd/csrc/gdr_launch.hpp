@@ -139,12 +139,15 @@ hipError_t launch_state_bwd(int D, bool in_f32, int64_t B, int64_t T, int H, int
 // workgroup per chunk-head).  cler: the error-routing epilogue's terms run
 // between the stages (dh, lam and beta as for the epilogue; partial, if not
 // NULL, receives one scale-gradient row per chunk, [B*NC][H*D] floats, for
-// launch_dlam_final).
+// launch_dlam_final).  ahead (a multiple of 8, 0 = none): each workgroup pulls
+// into the L2 the first operands of the workgroup `ahead` places after it in
+// the launch (bf16 inputs), which starts on the same XCD about when they are
+// needed if `ahead` is somewhat less than the number of CUs the launch gets.
 hipError_t launch_grads(int D, int gate, bool in_f32, bool out_f32, int64_t B, int64_t T, int H, int64_t NC,
                         float scale, const void* q, const void* k, const void* v, const float* beta,
                         const float* alpha, const void* dO, const void* dh, const float* lam, void* dq, void* dk,
                         void* dv, float* dbeta, float* dalpha, const ChunkWs& ws, int pro, ChunkRange cr,
-                        bool cler, float* partial, hipStream_t stream);
+                        bool cler, float* partial, int ahead, hipStream_t stream);
 
 hipError_t launch_clvr_dlam(bool in_f32, int64_t BT, int H, int D, const void* dh, const void* v,
                             float* dlam, float* partial, int64_t nseg, hipStream_t stream);

@@ -87,7 +87,11 @@ hipError_t launch_state_bwd(int, bool, int64_t, int64_t, int, int64_t NC, float,
 hipError_t launch_grads(int, int, bool, bool, int64_t, int64_t, int, int64_t NC, float, const void*, const void*,
                         const void*, const float*, const float*, const void*, const void*, const float*, void*,
                         void*, void*, float*, float*, const ChunkWs& ws, int, ChunkRange cr, bool, float* partial,
-                        hipStream_t) {
+                        int ahead, hipStream_t) {
+    if (ahead < 0 || ahead % 8) {
+        std::fprintf(stderr, "launch_grads: prefetch distance %d\n", ahead);
+        std::abort();
+    }
     check_ws(ws);
     check_range(cr, NC);
     in_ws(partial, "partial");
