@@ -147,7 +147,8 @@ __device__ __forceinline__ void load_frag_in(Frag<OpT>& f, const InT* p) {
 // buffer, which grads_kernel runs one after the other for a chunk.
 // KEEP: the partials stay on chip (pk, and dgamma in s_gam) instead of going
 // through the workspace.
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, bool NORO = false>
+// ROUTE only tells the value route's and the error route's instances apart.
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, bool NORO = false, int ROUTE = 0>
 __device__ __forceinline__ void grad_lin_body(int64_t T, int H, int64_t NC, float scale,
                                               const void* __restrict__ k_, const void* __restrict__ v_,
                                               const float* __restrict__ beta, const float* __restrict__ alpha,
@@ -723,7 +724,7 @@ struct PairRows<_Float16, N> {
 // channel sums and the prologue's row dots from one call to the next, and the
 // prologue's earlier passes leave dq_hat, dk_hat in their workspace partial
 // slots for the last pass to finish.
-template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, int DS = D>
+template <int D, int GATE, bool IN_F32, bool OUT_F32, bool PRO, bool KEEP, int DS = D, int ROUTE = 0>
 __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, const void* __restrict__ q_,
                                                const void* __restrict__ k_, const float* __restrict__ alpha,
                                                void* __restrict__ dq_, void* __restrict__ dk_,
@@ -1355,6 +1356,88 @@ __device__ __forceinline__ void grad_gate_body(int64_t T, int H, int64_t NC, con
     asm volatile("" ::"v"(tx));  // the prefetch loads end here at the latest
 }
 
+// The error route's terms between the stages when the first stage's partials
+// stay on chip (d = 128, fp16 operands): dKt -= dE S^T on its LDS copy past the
+// second stage's buffers, dP -= strict_tril(dE U^T) on the dP tiles this wave
+// holds in pk, each rounded to operand precision exactly as the workspace
+// route's read-modify-writes round them; dE and the scale gradient's partial
+// row as in cler_post_body.
+template <int D, bool IN_F32>
+__device__ __forceinline__ void cler_post_onchip(int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                                                 const float* __restrict__ beta, const float* __restrict__ lam,
+                                                 const void* __restrict__ dh_, float* __restrict__ partial,
+                                                 ChunkRange cr, char* smem, GradPartials<D, IN_F32>& pk) {
+    using P = GradPartials<D, IN_F32>;
+    using GL = GGateLayout<D, IN_F32>;
+    using Lc = ClerLayout<D, IN_F32>;
+    using OpT = typename Lc::OpT;
+    using V4 = typename P::V4;
+    constexpr int NT = 4 * D, NW = NT / 64, KQ = D / 32, LDE = Lc::LDE;
+    static_assert(P::TLDS && !IN_F32, "dKt on chip in LDS");
+    static_assert(D / 16 == NW, "one state-row tile of dKt per wave");
+    static_assert(Lc::POST_BYTES <= GL::BYTES, "dE below the dKt copy");
+    const OpT* sE = reinterpret_cast<const OpT*>(smem);
+    OpT* X = reinterpret_cast<OpT*>(smem + GL::BYTES);  // dKt, the second stage's exchange layout
+
+    int64_t bh, c;
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const OpT* U = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
+    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
+    const int dt = wid;
+    Frag<OpT> fs[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) fs[kq].load(Ss + ((dt * KQ + kq) * 64 + lane) * 8);
+
+    cler_build_dE<D, IN_F32, NT>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
+
+    // dKt -= dE S^T: state-row tile dt = wid, four position tiles
+    {
+        float4v acc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            acc[rt] = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                Frag<OpT> fe;
+                fe.load(sE + (16 * rt + l16) * LDE + 32 * kq + 8 * g4);
+                mma(fe, fs[kq], acc[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            V4* piece = reinterpret_cast<V4*>(X + xoff<GL::EPC, GL::NPC>(16 * dt + l16, 16 * rt + 4 * g4));
+            V4 v = *piece;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = from_f32<OpT>(to_f32(v[e]) - acc[rt][e]);
+            *piece = v;
+        }
+    }
+    // dP -= strict_tril(dE U^T) on this wave's tiles wid + NW t of pk.p
+#pragma unroll
+    for (int t = 0; t < P::NTL; ++t) {
+        const int tile = wid + NW * t, at = tile / 4, xt = tile % 4;
+        if (xt <= at) {
+            float4v acc = zero4();
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                Frag<OpT> fe, fu;
+                fe.load(sE + (16 * at + l16) * LDE + 32 * kq + 8 * g4);
+                fu.load(U + ((xt * KQ + kq) * 64 + lane) * 8);
+                mma(fe, fu, acc);
+            }
+            const int x = 16 * xt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = 16 * at + 4 * g4 + e;
+                if (x < a) pk.p[t][e] = from_f32<OpT>(to_f32(pk.p[t][e]) - acc[e]);
+            }
+        }
+    }
+}
+
 // Both gradient stages for one chunk in one workgroup: the partials grad_lin
 // writes are read back by the same workgroup, from the L2, after a barrier that
 // makes them visible; the LDS buffer is shared.  With the error-routing
@@ -1373,24 +1456,27 @@ __global__ __launch_bounds__(4 * D) void grads_kernel(int64_t T, int H, int64_t 
                                                       ChunkRange cr, float* __restrict__ partial, int ahead) {
     constexpr int LB = GLinLayout<D, IN_F32>::BYTES, GB = GGateLayout<D, IN_F32>::BYTES;
     static_assert(!CLER || ClerLayout<D, IN_F32>::POST_BYTES <= (LB > GB ? LB : GB), "LDS of the CLER terms");
-    // On the value route the partials stay on chip; the error route's terms
-    // edit them in the workspace between the stages.
-    constexpr bool KEEP = !CLER;
+    // The partials stay on chip on the value route, and on the error route at
+    // d = 128 with fp16 operands, whose terms then edit them there; otherwise
+    // the error route's terms edit them in the workspace between the stages.
+    constexpr bool KEEP = !CLER || (GradPartials<D, IN_F32>::TLDS && !IN_F32);
     // d = 128: dKt waits past the second stage's buffers
     constexpr int GBX = GB + ((KEEP && GradPartials<D, IN_F32>::TLDS) ? CHUNK * D * (IN_F32 ? 4 : 2) : 0);
     __shared__ __attribute__((aligned(16))) char smem[LB > GBX ? LB : GBX];
     __shared__ float s_gam[KEEP ? D : 1];
     __shared__ float s_tot[4][D];  // per-part column sums, used by both stages in turn
     GradPartials<D, IN_F32> pk;
-    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_, lam, dv_,
-                                                       dbeta, ws, pro, cr, smem, pk, s_gam, s_tot);
+    grad_lin_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP, false, CLER>(T, H, NC, scale, k_, v_, beta, alpha, dO_, dh_,
+                                                                     lam, dv_, dbeta, ws, pro, cr, smem, pk, s_gam,
+                                                                     s_tot);
     __syncthreads();
     if constexpr (CLER) {
-        cler_post_body<D, IN_F32, 4 * D>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
+        if constexpr (KEEP) cler_post_onchip<D, IN_F32>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem, pk);
+        else cler_post_body<D, IN_F32, 4 * D>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
         __syncthreads();
     }
-    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro, cr,
-                                                        smem, pk, s_gam, s_tot, 0, 1, 0, nullptr, ahead);
+    grad_gate_body<D, GATE, IN_F32, OUT_F32, PRO, KEEP, D, CLER>(T, H, NC, q_, k_, alpha, dq_, dk_, dalpha, ws, pro,
+                                                                  cr, smem, pk, s_gam, s_tot, 0, 1, 0, nullptr, ahead);
 }
 
 // fp32 operands at d = 128, where one workgroup's LDS cannot hold either stage:

@@ -48,17 +48,16 @@ struct ClerLayout {
     static constexpr int POST_BYTES = COLRED + 8 * 32 * 4;  // up to eight waves
 };
 
-// Between the two gradient stages of a chunk (NT threads of its workgroup, on
-// an LDS buffer of ClerLayout::POST_BYTES): the write errors' own terms,
-// e = (V - Kt S) - M U:
-//   dKt -= dE S^T,   dP -= strict_tril(dE U^T),
-// and the scale gradient's partial row of this chunk, sum_t dh_t e_t, with
-// e = U / beta.
+// The first half of the write errors' terms between the two gradient stages
+// (NT threads of the chunk's workgroup): dE = lam * dh into LDS (smem, [64][LDE]
+// in operand precision, rows past the end zero) and the scale gradient's
+// partial row of this chunk, sum_t dh_t e_t with e = U / beta (if partial is not
+// NULL).  Ends with a barrier: dE is visible to every wave.
 template <int D, bool IN_F32, int NT>
-__device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, const ChunkWs& ws,
-                                               const float* __restrict__ beta, const float* __restrict__ lam,
-                                               const void* __restrict__ dh_, float* __restrict__ partial,
-                                               ChunkRange cr, char* smem) {
+__device__ __forceinline__ void cler_build_dE(int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                                              const float* __restrict__ beta, const float* __restrict__ lam,
+                                              const void* __restrict__ dh_, float* __restrict__ partial,
+                                              ChunkRange cr, char* smem) {
     using Lc = ClerLayout<D, IN_F32>;
     using OpT = typename Lc::OpT;
     using InT = typename InType<IN_F32>::T;
@@ -73,12 +72,10 @@ __device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, con
     const int64_t ch = bh * NC + c;
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh % H);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int tid = threadIdx.x, wid = tid >> 6, l16 = tid & 15;
     const int64_t nvalid64 = T - c * CHUNK;
     const int nvalid = nvalid64 < CHUNK ? static_cast<int>(nvalid64) : CHUNK;
     const OpT* U = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
-    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
     const InT* dh = reinterpret_cast<const InT*>(dh_);
 
     // pieces of U (fragment order) with the matching dh: dE rows into LDS and
@@ -132,50 +129,99 @@ __device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, con
             if (w % KQ == step) s += colred[w][tid & 31];
         partial[(b * NC + c) * (static_cast<int64_t>(H) * D) + static_cast<int64_t>(h) * D + tid] = s;
     }
+}
 
-    // dKt -= dE S^T: wave w takes the state-row tiles dt = w, w + NW, ... for all
-    // four position tiles (S fragments read once)
+// Between the two gradient stages of a chunk (NT threads of its workgroup, on
+// an LDS buffer of ClerLayout::POST_BYTES), with the first stage's dKt and dP
+// in the workspace: the write errors' own terms, e = (V - Kt S) - M U:
+//   dKt -= dE S^T,   dP -= strict_tril(dE U^T),
+// and the scale gradient's partial row of this chunk (cler_build_dE).
+template <int D, bool IN_F32, int NT>
+__device__ __forceinline__ void cler_post_body(int64_t T, int H, int64_t NC, const ChunkWs& ws,
+                                               const float* __restrict__ beta, const float* __restrict__ lam,
+                                               const void* __restrict__ dh_, float* __restrict__ partial,
+                                               ChunkRange cr, char* smem) {
+    using Lc = ClerLayout<D, IN_F32>;
+    using OpT = typename Lc::OpT;
+    constexpr int LDE = Lc::LDE, KQ = D / 32, NW = NT / 64;
+    const OpT* sE = reinterpret_cast<const OpT*>(smem);
+
+    int64_t bh, c;
+    range_block(cr, bh, c);
+    const int64_t ch = bh * NC + c;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const OpT* U = reinterpret_cast<const OpT*>(ws.Usave) + ch * CHUNK * D;
+    const OpT* Ss = reinterpret_cast<const OpT*>(ws.Ssnap) + ch * D * D;
     OpT* gKt = static_cast<OpT*>(ws.gKt) + ch * CHUNK * D;
+    // this wave's state-row tile of dKt (see below): its sixteen dKt values and
+    // its S fragments are loaded first, so that they arrive while dE is built
+    static_assert(D / 16 == NW, "one state-row tile of dKt per wave");
+    const int dt = wid;
+    OpT cur[4][4];
 #pragma unroll
-    for (int dt = wid; dt < D / 16; dt += NW) {
-        Frag<OpT> fs[KQ];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) fs[kq].load(Ss + ((dt * KQ + kq) * 64 + lane) * 8);
+        for (int e = 0; e < 4; ++e) cur[rt][e] = gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16];
+    Frag<OpT> fs[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) fs[kq].load(Ss + ((dt * KQ + kq) * 64 + lane) * 8);
+
+    cler_build_dE<D, IN_F32, NT>(T, H, NC, ws, beta, lam, dh_, partial, cr, smem);
+
+    // dKt -= dE S^T: wave w takes the state-row tile dt = w for all four position
+    // tiles (S fragments read once).  Its dKt values were loaded at the start and
+    // are stored after all four products, so the read-modify-writes do not wait
+    // on one another.
+    {
+        float4v acc[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            float4v acc = zero4();
+            acc[rt] = zero4();
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
                 Frag<OpT> fe;
                 fe.load(sE + (16 * rt + l16) * LDE + 32 * kq + 8 * g4);
-                mma(fe, fs[kq], acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                OpT& gk = gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16];
-                gk = from_f32<OpT>(to_f32(gk) - acc[e]);
+                mma(fe, fs[kq], acc[rt]);
             }
         }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gKt[(16 * rt + 4 * g4 + e) * D + 16 * dt + l16] = from_f32<OpT>(to_f32(cur[rt][e]) - acc[rt][e]);
     }
     // dP -= strict_tril(dE U^T): wave w < 4 takes position-row tile w and the
-    // column tiles up to it
+    // column tiles up to it, its dP values loaded first in the same way
     if (wid < 4) {
         OpT* gP = static_cast<OpT*>(ws.gP) + ch * CHUNK * CHUNK;
         const int at = wid;
-        for (int xt = 0; xt <= at; ++xt) {
-            float4v acc = zero4();
+        OpT cp[4][4];
 #pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                Frag<OpT> fe, fu;
-                fe.load(sE + (16 * at + l16) * LDE + 32 * kq + 8 * g4);
-                fu.load(U + ((xt * KQ + kq) * 64 + lane) * 8);
-                mma(fe, fu, acc);
+        for (int xt = 0; xt < 4; ++xt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cp[xt][e] = gP[(16 * at + 4 * g4 + e) * CHUNK + 16 * xt + l16];
+        float4v acc[4];
+#pragma unroll
+        for (int xt = 0; xt < 4; ++xt) {
+            acc[xt] = zero4();
+            if (xt <= at) {
+#pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) {
+                    Frag<OpT> fe, fu;
+                    fe.load(sE + (16 * at + l16) * LDE + 32 * kq + 8 * g4);
+                    fu.load(U + ((xt * KQ + kq) * 64 + lane) * 8);
+                    mma(fe, fu, acc[xt]);
+                }
             }
+        }
+#pragma unroll
+        for (int xt = 0; xt < 4; ++xt) {
             const int x = 16 * xt + l16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 16 * at + 4 * g4 + e;
-                if (x < a) gP[a * CHUNK + x] = from_f32<OpT>(to_f32(gP[a * CHUNK + x]) - acc[e]);
+                if (xt <= at && x < a) gP[a * CHUNK + x] = from_f32<OpT>(to_f32(cp[xt][e]) - acc[xt][e]);
             }
         }
     }
