@@ -62,9 +62,12 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return
 // The empty asm pins x as an fp32 value: without it the compiler may fuse a
 // product feeding the conversion into one mixed-precision FMA (one rounding
 // instead of two), and whether it does depends on the surrounding code, so two
-// kernels computing the same value could round it differently.
+// kernels computing the same value could round it differently.  The asm is not
+// volatile: it has no side effects, so memory accesses may still be scheduled
+// across it (a volatile one kept every load after a conversion from being
+// issued before it).
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) {
-    asm volatile("" : "+v"(x));
+    asm("" : "+v"(x));
     return static_cast<_Float16>(x);
 }
 
