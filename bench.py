@@ -121,10 +121,10 @@ PER_BH_STATE = {"state_fwd": 1, "state_train": 1}
 KERNEL_SOURCES = {
     "intra_fwd": ["gdr_intra.hip"], "intra_bwd": ["gdr_intra.hip"], "intra_train": ["gdr_intra.hip"],
     "state_fwd": ["gdr_state.hip"], "state_fwd_save": ["gdr_state.hip"], "state_train": ["gdr_state.hip"],
-    "output": ["gdr_output.hip"], "output_cler": ["gdr_output.hip", "gdr_cler.hpp"],
+    "output": ["gdr_output.hip", "gdr_gate.hpp", "gdr_gate_rows.hpp"], "output_cler": ["gdr_output.hip", "gdr_cler.hpp", "gdr_gate.hpp", "gdr_gate_rows.hpp"],
     "cler_mt": ["gdr_cler.hip", "gdr_cler.hpp"],
     "state_bwd_cler": ["gdr_bwd_state.hip"],
-    "gate_fwd": ["gdr_gate.hip"], "gate_bwd": ["gdr_gate.hip"],
+    "gate_fwd": ["gdr_gate.hip", "gdr_gate.hpp", "gdr_gate_rows.hpp"], "gate_bwd": ["gdr_gate.hip", "gdr_gate.hpp", "gdr_gate_rows.hpp"],
     "intra_train_pro": ["gdr_intra.hip"],
     "state_bwd": ["gdr_bwd_state.hip"],
     "clvr_dlam": ["gdr_bwd_grad.hip"],
@@ -425,6 +425,22 @@ def main():
             us = 1e3 * ms / c
             gbs = kbytes[n] * args.steps / c / (us * 1e-6) / 1e9
             gk[n] = {"avg_us": round(us, 2), "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # the inference forward with the gate fused into its output kernel
+    # (gdr_forward_chunked_gated), against the forward and then the gate launch
+    yg = torch.empty((B, T, H, d), device=dev, dtype=bf)
+
+    def fwd_gated():
+        gdr.forward_gated(q, k, v, beta, alpha, og, ow, workspace=ws_f, output_final_state=True)
+
+    def fwd_then_gate():
+        o_, _ = gdr.forward(q, k, v, beta, alpha, None, workspace=ws_f, output_final_state=True)
+        gdr.output_gate(o_, og, ow, out=yg)
+
+    fused_ms = cuda_time_ms(fwd_gated, args.steps, args.warmup)
+    sep_ms = cuda_time_ms(fwd_then_gate, args.steps, args.warmup)
+    gk["forward_gated"] = {"us": round(1e3 * fused_ms, 2), "separate_us": round(1e3 * sep_ms, 2),
+                           "tokens_per_s": round(tokens / (fused_ms * 1e-3), 1)}
+    del yg
     output_gate = {"workload": "sigmoid(g) * RMSNorm(o) per head on [B=%d, T=%d, H=%d, dv=%d] bf16" % (B, T, H, d),
                    "kernels": gk}
     log("output gate %s" % json.dumps(gk))

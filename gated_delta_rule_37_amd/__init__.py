@@ -18,12 +18,13 @@ from __future__ import annotations
 
 from ._lib import (GATE_CHANNEL, GATE_NONE, GATE_SCALAR, PROLOGUE_ALPHA_FORGET, PROLOGUE_ALPHA_SIGMOID,
                    PROLOGUE_NONE, ROUTE_ERROR, ROUTE_VALUE, GdrError, backward, decode_step, forward,
+                   forward_gated,
                    gdn2_decode_step, gdn2_forward, gdn2_workspace_size, library_path, load_library, output_gate,
                    output_gate_backward, workspace_size)
 
 __all__ = [
     "GATE_NONE", "GATE_SCALAR", "GATE_CHANNEL", "ROUTE_VALUE", "ROUTE_ERROR", "PROLOGUE_NONE",
-    "PROLOGUE_ALPHA_SIGMOID", "PROLOGUE_ALPHA_FORGET", "GdrError", "forward", "backward",
+    "PROLOGUE_ALPHA_SIGMOID", "PROLOGUE_ALPHA_FORGET", "GdrError", "forward", "forward_gated", "backward",
     "decode_step", "output_gate", "output_gate_backward", "workspace_size", "load_library", "library_path",
     "gdn2_forward", "gdn2_decode_step", "gdn2_workspace_size",
 ]

@@ -61,6 +61,8 @@ def load_library():
         lib.gdr_workspace_size.restype = SZ
         lib.gdr_forward_chunked.argtypes = [D] + [P] * 10 + [P, SZ, P]
         lib.gdr_forward_chunked.restype = ctypes.c_int
+        lib.gdr_forward_chunked_gated.argtypes = [D] + [P] * 12 + [P, SZ, P]
+        lib.gdr_forward_chunked_gated.restype = ctypes.c_int
         lib.gdr_backward.argtypes = [D] + [P] * 17 + [P, SZ, P]
         lib.gdr_backward.restype = ctypes.c_int
         lib.gdr_forward_train.argtypes = [D] + [P] * 10 + [P, SZ, P]
@@ -226,6 +228,31 @@ def forward(q, k, v, beta, alpha=None, S0=None, *, scale=1.0, out_dtype=None, h=
     _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o),
               _ptr(ST), _ptr(h), _ptr(clvr_scale), _ptr(workspace), need, _stream(q.device)))
     return o, ST
+
+
+def forward_gated(q, k, v, beta, alpha, g, w=None, S0=None, *, scale=1.0, out_dtype=None, h=None,
+                  clvr_scale=None, output_final_state=True, workspace=None, route="value", prologue=None):
+    """Inference forward with the output-gate epilogue (``gdr_forward_chunked_gated``).
+    Returns ``(y, S_T)`` with ``y = sigmoid(g) * w * RMSNorm(o)`` per head, equal
+    to :func:`output_gate` applied to :func:`forward`'s ``o``; ``o`` itself is
+    not kept.  ``g`` is [B, T, H, dv] in q's dtype, ``w`` [H*dv] fp32 or None
+    (ones).  The other arguments are those of :func:`forward`."""
+    B, T, H, dk, dv = _check_inputs(q, k, v, beta, alpha, S0)
+    _need(g, "g", q.dtype, (B, T, H, dv))
+    _need(w, "w", torch.float32, (H * dv,))
+    _need(h, "h", q.dtype, (B, T, H * dv))
+    _need(clvr_scale, "clvr_scale", torch.float32, (H * dv,))
+    lib = load_library()
+    desc = _desc(q, v, alpha, out_dtype, scale, route, prologue)
+    y = torch.empty((B, T, H, dv), dtype=out_dtype or q.dtype, device=q.device)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    need = lib.gdr_workspace_size(ctypes.byref(desc), 0)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.gdr_forward_chunked_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                         _ptr(S0), _ptr(g), _ptr(w), _ptr(y), _ptr(ST), _ptr(h), _ptr(clvr_scale),
+                                         _ptr(workspace), need, _stream(q.device)))
+    return y, ST
 
 
 def backward(q, k, v, beta, alpha, S0, dO, dST=None, *, scale=1.0, out_dtype=None, dh=None,

@@ -17,6 +17,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "gdr_gate.hpp"
 #include "gdr_launch.hpp"
 
 namespace {
@@ -393,7 +394,8 @@ size_t gdr_workspace_size(const gdr_desc* desc, int op) {
 static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* k, const void* v,
                                const float* beta, const float* alpha, const float* S0, void* o,
                                float* ST, void* h_clvr, const float* clvr_scale, void* ws,
-                               size_t ws_bytes, void* stream, bool train) {
+                               size_t ws_bytes, void* stream, bool train, const void* gate_g = nullptr,
+                               const float* gate_w = nullptr) {
     int64_t NC = 0;
     gdr_status st = check_desc(desc, &NC);
     if (st != GDR_OK) return st;
@@ -404,7 +406,8 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         return fail(GDR_ERR_INVALID_ARG, "q, k, v, beta and o are required");
     if ((desc->gate == GDR_GATE_NONE) != (alpha == nullptr) && any)
         return fail(GDR_ERR_INVALID_ARG, "alpha must be NULL iff the gate is NONE");
-    const void* ptrs[] = {q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws};
+    if (any && gate_w && !gate_g) return fail(GDR_ERR_INVALID_ARG, "the output gate's w given without g");
+    const void* ptrs[] = {q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws, gate_g, gate_w};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
     if (clvr_scale && !h_clvr) return fail(GDR_ERR_INVALID_ARG, "clvr_scale given without h_clvr");
@@ -417,7 +420,8 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         const void* p;
         size_t n;
     } ins[] = {{q, n_in * ib}, {k, n_in * ib}, {v, n_in * ib}, {beta, size_t(ntok) * 4},
-               {alpha, a_bytes}, {S0, s_bytes}, {clvr_scale, size_t(H) * D * 4}};
+               {alpha, a_bytes}, {S0, s_bytes}, {clvr_scale, size_t(H) * D * 4},
+               {gate_g, n_in * ib}, {gate_w, size_t(H) * D * 4}};
     for (auto& in : ins) {
         if (overlap(o, o_bytes, in.p, in.n)) return fail(GDR_ERR_INVALID_ARG, "o overlaps an input");
         if (ST && in.p != S0 && overlap(ST, s_bytes, in.p, in.n))
@@ -466,6 +470,8 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
             {S0, int64_t(s_bytes / 4), false, F | R, "S0"},
             {h_clvr, int64_t(n_in), bf, F, "h_clvr"},
             {clvr_scale, H * D, false, F, "clvr_scale"},
+            {gate_g, int64_t(n_in), bf, F, "g"},
+            {gate_w, H * D, false, F, "w"},
         };
         gdr_status g = run_checks(checks, int(sizeof checks / sizeof checks[0]), s);
         if (g != GDR_OK) return g;
@@ -485,11 +491,14 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         return GDR_OK;
     };
     const char* st_name = train ? "state_train" : "state_fwd";
-    const char* out_name = cler ? "output_cler" : "output";
+    const char* out_name = gate_g ? "output_gated" : cler ? "output_cler" : "output";
+    const gdr::OutGate og{gate_g, gate_w};
     auto output = [&](gdr::ChunkRange cr, hipStream_t os) -> gdr_status {
         gdr::prof_before(os);
-        e = gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff, clvr_scale,
-                               cler ? h_clvr : nullptr, cr, os);
+        e = gate_g ? gdr::launch_output_gated(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff,
+                                              clvr_scale, cler ? h_clvr : nullptr, og, cr, os)
+                   : gdr::launch_output(int(D), out_f32, B, T, int(H), NC, desc->scale, w, o, beta_eff, clvr_scale,
+                                        cler ? h_clvr : nullptr, cr, os);
         gdr::prof_after(out_name, os);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output launch: %s", hipGetErrorString(e));
         return GDR_OK;
@@ -566,6 +575,14 @@ static gdr_status forward_impl(const gdr_desc* desc, const void* q, const void* 
         e = gdr::launch_cler_fwd(int(D), in_f32, B, T, int(H), NC, w, beta_eff, clvr_scale, h_clvr, s);
         gdr::prof_after("cler_fwd", s);
         if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "error-routing launch: %s", hipGetErrorString(e));
+    }
+    if (in_f32 && gate_g) {
+        // fp32 operands: the state pass writes o, and the gate runs over it in place
+        gdr::prof_before(s);
+        e = gdr::launch_gate(false, int(D), true, out_f32, B * T, int(H), o, gate_g, gate_w, o, nullptr, nullptr,
+                             nullptr, nullptr, nullptr, s);
+        gdr::prof_after("gate_fwd", s);
+        if (e != hipSuccess) return fail(GDR_ERR_DEVICE, "output-gate launch: %s", hipGetErrorString(e));
     }
     return GDR_OK;
 }
@@ -1000,6 +1017,15 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
                                float* ST, void* h_clvr, const float* clvr_scale, void* ws,
                                size_t ws_bytes, void* stream) {
     return forward_impl(desc, q, k, v, beta, alpha, S0, o, ST, h_clvr, clvr_scale, ws, ws_bytes, stream, false);
+}
+
+gdr_status gdr_forward_chunked_gated(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                                     const float* beta, const float* alpha, const float* S0, const void* g,
+                                     const float* w, void* y, float* ST, void* h_clvr, const float* clvr_scale,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    if (desc && desc->B * desc->T * desc->H > 0 && !g) return fail(GDR_ERR_INVALID_ARG, "g is required");
+    return forward_impl(desc, q, k, v, beta, alpha, S0, y, ST, h_clvr, clvr_scale, ws, ws_bytes, stream, false, g,
+                        w);
 }
 
 gdr_status gdr_forward_train(const gdr_desc* desc, const void* q, const void* k, const void* v,

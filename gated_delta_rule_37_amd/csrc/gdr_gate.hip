@@ -15,19 +15,10 @@
 // thread keeps the same eight channels of w and of the dw sums for the whole
 // range; the per-range dw rows are reduced afterwards in a fixed order.
 #include "gdr_common.hpp"
+#include "gdr_gate_rows.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
-
-constexpr float GATE_EPS = 1e-6f;
-
-// sum over the TPR consecutive lanes of a row (TPR a power of two <= 16)
-template <int TPR>
-__device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-}
 
 template <int D, bool IN_F32, bool OUT_F32>
 __global__ __launch_bounds__(256) void gate_fwd_kernel(int64_t BT, int H, int64_t per, const void* __restrict__ o_,

@@ -19,8 +19,17 @@
 // With the error-routing epilogue (CLER), every thread also adds lam * u / beta
 // to the hidden-stream piece of the U piece it has just read (the write errors,
 // see gdr_cler.hpp), so U is read once for both.
+//
+// With the output-gate epilogue (GATE, KDA blog section 4.1), the rows
+// assembled in LDS are not written as o: each is normalised over its dv
+// channels, scaled by w and by sigmoid(g), and written as y.  The lanes own the
+// same eight channels of a row, and the norm reduces in the same order, as in
+// gate_fwd_kernel, so y equals that kernel run on o, bit for bit, without o
+// being written and read back.  g is loaded before the products, so its reads
+// overlap them.
 #include "gdr_cler.hpp"
 #include "gdr_common.hpp"
+#include "gdr_gate_rows.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
@@ -47,10 +56,11 @@ __device__ __forceinline__ Frag<_Float16> frag_tr(const _Float16* t, int k0, int
     return f;
 }
 
-template <int D, bool OUT_F32, bool CLER>
+template <int D, bool OUT_F32, bool CLER, bool GATE>
 __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t NC, float scale, ChunkWs ws,
                                                      void* __restrict__ o_, const float* __restrict__ beta,
                                                      const float* __restrict__ lam, bf16_t* __restrict__ hs,
+                                                     const bf16_t* __restrict__ gg, const float* __restrict__ gw,
                                                      ChunkRange cr) {
     using L = OutLayout<D>;
     using OutT = typename InType<OUT_F32>::T;
@@ -112,11 +122,23 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
             }
         }
     }
+    const int64_t tstride = static_cast<int64_t>(H) * D;
+    const int64_t obase = ((b * T + c * CHUNK) * H + h) * D;
+    // output gate: TPR lanes per row, eight channels each; rows past the end
+    // are neither read nor written
+    constexpr int TPR = D / 8, RPI = 256 / TPR, GR = GATE ? CHUNK / RPI : 1;
+    const int grs = tid / TPR, gc0 = (tid % TPR) * 8;
+    uint4 graw[GR];
+    if constexpr (GATE) {
+#pragma unroll
+        for (int k = 0; k < GR; ++k) {
+            const int r = k * RPI + grs;
+            graw[k] = r < nvalid ? *reinterpret_cast<const uint4*>(gg + obase + r * tstride + gc0) : make_uint4(0, 0, 0, 0);
+        }
+    }
     wait_vmcnt<0>();
     __syncthreads();
     OutT* o = reinterpret_cast<OutT*>(o_);
-    const int64_t tstride = static_cast<int64_t>(H) * D;
-    const int64_t obase = ((b * T + c * CHUNK) * H + h) * D;
     float res[4][CPW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -155,6 +177,29 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
             for (int e = 0; e < 4; ++e)
                 so[(16 * rt + 4 * g4 + e) * D + 16 * (wid * CPW + ci) + l16] = from_f32<OutT>(res[rt][ci][e]);
     __syncthreads();
+    if constexpr (GATE) {
+        float wv[8];
+        load_lam8(gw, static_cast<int64_t>(h) * D + gc0, wv);
+#pragma unroll
+        for (int k = 0; k < GR; ++k) {
+            const int r = k * RPI + grs;
+            float ov[8], gv[8];
+            load8f(so + r * D + gc0, ov);
+            const bf16_t* gb = reinterpret_cast<const bf16_t*>(&graw[k]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gv[i] = to_f32(gb[i]);
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(ov[i], ov[i], ss);
+            ss = row_sum<TPR>(ss);
+            const float rstd = __builtin_amdgcn_rsqf(ss * (1.f / D) + GATE_EPS);
+            float yv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] = sigmoid_fast(gv[i]) * wv[i] * (ov[i] * rstd);
+            if (r < nvalid) store8f(o + obase + r * tstride + gc0, yv);
+        }
+        return;
+    }
     constexpr int EPP = 16 / sizeof(OutT);      // elements per 16-byte piece
     constexpr int PPR = D / EPP;                // pieces per row
     constexpr int NPC = CHUNK * PPR / 256;      // pieces per thread
@@ -166,31 +211,54 @@ __global__ __launch_bounds__(256) void output_kernel(int64_t T, int H, int64_t N
     }
 }
 
+template <int D, bool OUT_F32, bool CLER>
+static void launch_output_g(int64_t nch, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws, void* o,
+                            const float* beta, const float* lam, bf16_t* hs, const OutGate& og, ChunkRange cr,
+                            hipStream_t stream) {
+    const bf16_t* gg = static_cast<const bf16_t*>(og.g);
+    if (gg)
+        hipLaunchKernelGGL((output_kernel<D, OUT_F32, CLER, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H,
+                           NC, scale, ws, o, beta, lam, hs, gg, og.w, cr);
+    else
+        hipLaunchKernelGGL((output_kernel<D, OUT_F32, CLER, false>), dim3((unsigned)nch), dim3(256), 0, stream, T,
+                           H, NC, scale, ws, o, beta, lam, hs, gg, og.w, cr);
+}
+
 template <int D, bool OUT_F32>
 static void launch_output_t(int64_t nch, int64_t T, int H, int64_t NC, float scale, const ChunkWs& ws, void* o,
-                            const float* beta, const float* lam, void* h, ChunkRange cr, hipStream_t stream) {
+                            const float* beta, const float* lam, void* h, const OutGate& og, ChunkRange cr,
+                            hipStream_t stream) {
     bf16_t* hs = static_cast<bf16_t*>(h);
-    if (h)
-        hipLaunchKernelGGL((output_kernel<D, OUT_F32, true>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                           scale, ws, o, beta, lam, hs, cr);
-    else
-        hipLaunchKernelGGL((output_kernel<D, OUT_F32, false>), dim3((unsigned)nch), dim3(256), 0, stream, T, H, NC,
-                           scale, ws, o, beta, lam, hs, cr);
+    if (h) launch_output_g<D, OUT_F32, true>(nch, T, H, NC, scale, ws, o, beta, lam, hs, og, cr, stream);
+    else launch_output_g<D, OUT_F32, false>(nch, T, H, NC, scale, ws, o, beta, lam, hs, og, cr, stream);
+}
+
+static hipError_t launch_output_any(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                                    const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
+                                    const OutGate& og, ChunkRange cr, hipStream_t stream) {
+    const int64_t nch = B * H * cr.n;
+    if (nch == 0) return hipSuccess;
+    if (D == 64) {
+        if (out_f32) launch_output_t<64, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, og, cr, stream);
+        else launch_output_t<64, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, og, cr, stream);
+    } else {
+        if (out_f32) launch_output_t<128, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, og, cr, stream);
+        else launch_output_t<128, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, og, cr, stream);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_output(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
                          const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
                          ChunkRange cr, hipStream_t stream) {
-    const int64_t nch = B * H * cr.n;
-    if (nch == 0) return hipSuccess;
-    if (D == 64) {
-        if (out_f32) launch_output_t<64, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
-        else launch_output_t<64, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
-    } else {
-        if (out_f32) launch_output_t<128, true>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
-        else launch_output_t<128, false>(nch, T, H, NC, scale, ws, o, beta, lam, h_cler, cr, stream);
-    }
-    return hipGetLastError();
+    return launch_output_any(D, out_f32, B, T, H, NC, scale, ws, o, beta, lam, h_cler, OutGate{nullptr, nullptr},
+                             cr, stream);
+}
+
+hipError_t launch_output_gated(int D, bool out_f32, int64_t B, int64_t T, int H, int64_t NC, float scale,
+                               const ChunkWs& ws, void* o, const float* beta, const float* lam, void* h_cler,
+                               const OutGate& og, ChunkRange cr, hipStream_t stream) {
+    return launch_output_any(D, out_f32, B, T, H, NC, scale, ws, o, beta, lam, h_cler, og, cr, stream);
 }
 
 }  // namespace gdr

@@ -163,6 +163,26 @@ gdr_status gdr_forward_chunked(const gdr_desc* desc, const void* q, const void* 
                                const float* clvr_scale, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* gdr_forward_chunked with the output-gate epilogue of KDA blog section 4.1
+ * applied to o before it leaves the chip (the inference form of
+ * gdr_forward_chunked followed by gdr_output_gate_forward on its o):
+ *     y = sigmoid(g) * w * o / sqrt(mean_j o_j^2 + 1e-6)      (j over dv)
+ *   g   [B,T,H,dv] in_dtype, the caller's low-rank projection output (required)
+ *   w   [H*dv] fp32 norm weight, NULL = ones
+ *   y   [B,T,H,dv] out_dtype, written in place of o (o itself is not kept); it
+ *       must not overlap any input
+ * Every other argument, the workspace size (gdr_workspace_size(desc, 0)) and
+ * the error behaviour are those of gdr_forward_chunked; in the debug mode g and
+ * w are checked to be finite.  y equals the two separate calls bit for bit.
+ * bf16 inputs: the output kernel normalises and gates the rows it assembles on
+ * chip, so o is neither written nor read back.  fp32 inputs: the state pass
+ * writes o into y and the gate runs over y in place. */
+gdr_status gdr_forward_chunked_gated(const gdr_desc* desc, const void* q, const void* k,
+                                     const void* v, const float* beta, const float* alpha,
+                                     const float* S0, const void* g, const float* w, void* y,
+                                     float* ST, void* h_clvr, const float* clvr_scale, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 /* Gradients of gdr_forward_chunked (reverse mode, chunked, recomputing the
  * forward's intermediates):
  *   dO        [B,T,H,dv] in_dtype, upstream gradient of o.

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "../../gated_delta_rule_37_amd/csrc/gdr_gate.hpp"
 #include "../../gated_delta_rule_37_amd/csrc/gdr_launch.hpp"
 
 namespace stub {
@@ -52,6 +53,15 @@ hipError_t launch_decode(int, int, bool, bool, int64_t, int, float, const void*,
     ++stub::launches;
     return hipSuccess;
 }
+hipError_t launch_output_gated(int, bool, int64_t, int64_t, int, int64_t NC, float, const ChunkWs& ws, void*,
+                               const float*, const float*, void*, const OutGate& og, ChunkRange cr, hipStream_t) {
+    if (!og.g) std::abort();
+    check_ws(ws);
+    check_range(cr, NC);
+    ++stub::launches;
+    return hipSuccess;
+}
+
 hipError_t launch_output(int, bool, int64_t, int64_t, int, int64_t NC, float, const ChunkWs& ws, void*,
                          const float*, const float*, void*, ChunkRange cr, hipStream_t) {
     check_ws(ws);

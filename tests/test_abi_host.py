@@ -142,6 +142,23 @@ def test_forward_rejects_invalid_arguments(lib):
     assert "not 16-byte aligned" not in lib.gdr_last_error().decode() or True
 
 
+def fwd_gated(lib, d, g=8, w=9, y=6, ws_bytes=1 << 40):
+    P = lambda i: None if i is None else fake(i)  # noqa: E731
+    return lib.gdr_forward_chunked_gated(ctypes.byref(d), P(1), P(2), P(3), P(4), P(5), None, P(g), P(w), P(y),
+                                         None, None, None, P(7), ws_bytes, None)
+
+
+def test_gated_forward_rejects_invalid_arguments(lib):
+    assert fwd_gated(lib, desc(), g=None) == INVALID  # g is required
+    assert b"g is required" in lib.gdr_last_error()
+    assert fwd_gated(lib, desc(), g=None, w=None) == INVALID
+    assert fwd_gated(lib, desc(), y=8) == INVALID  # y aliases g
+    assert fwd_gated(lib, desc(), y=3) == INVALID  # y aliases v
+    assert fwd_gated(lib, desc(), ws_bytes=16) == WORKSPACE
+    assert fwd_gated(lib, desc(d=96)) == UNSUPPORTED
+    assert fwd_gated(lib, desc(B=0), g=None) == OK  # nothing to compute
+
+
 def test_forward_error_message_is_thread_local_detail(lib):
     assert fwd(lib, desc(d=96)) == UNSUPPORTED
     assert b"dk == dv" in lib.gdr_last_error()
